@@ -1,0 +1,384 @@
+"""CPU oracle of the Stable LatentMoE layer forward pass and its
+quantile-balancing (QB) bias update.
+
+TEST INFRASTRUCTURE.  Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no code
+with the HIP path and imports nothing from it.
+
+Every step is the plain definition written out in numpy, floating point in
+fp64 unless stated.  In bf16 mode the values the GPU stores in bf16 are rounded
+to bf16 here at the same points (h, z, shared hidden G, expert hidden H, expert
+output Y, combined latent y_lat, out); in f32 mode nothing is rounded and the
+result is the fp64 value of the layer.
+
+Sources (page title + place on the page):
+  [P1] "Pretraining a Mini Kimi K3" (e-book review), capsule 16 (collapse and
+       the noaux_tc bias rule), capsule 20 (3 batched expert matmuls),
+       capsule 25 (dispatch buffer that silently fell back).
+  [P3] Attention->K3 course, Day 28, design survival table (RMSNorm inside
+       LatentMoE; 896-choose-16 Stable LatentMoE; AttnRes replaces x+f(x)).
+  [P4] "Kimi K3 MoE lightweight replica demo" article: width separation and
+       the shared/routed dual path (architecture paragraph); Tab 1 data flow;
+       Tab 2 Fig. 2(a)/(b) (QB balance, histogram vs exact quantile);
+       Tab 8-10 (QB reroutes only, weight normalisation, delayed update,
+       mean centring, frozen at inference).
+  [P5] "K3 tops open source" blog, idle-experts section (hot windows raise
+       the threshold, cold ones lower it).
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes): sigmoid scores; router on the d-wide normalised h; SiLU GLU for
+all experts; no residual inside the layer; dropless routing; ties in the
+biased top-k go to the lower expert index; histogram of the raw score s on
+[0,1]; QB target quantile = the (k/E)-upper quantile (every expert's target
+load is T*k/E); bias set outright to mean(q) - q_e.
+
+Parity pins: every function here is checked in ``tests/test_oracle_*.py``
+against closed forms, library routines, brute force or invariants.  The
+layer-level equation the demo checks against ("Eq. 11" on [P4], Tab 3) is
+not reproduced on the pages: parity with it is unpinned.
+"""
+from __future__ import annotations
+
+from decimal import Decimal, getcontext
+from typing import Dict, Optional
+
+import numpy as np
+
+F32 = np.float32
+
+# --------------------------------------------------------------------------
+# bf16 rounding (storage precision of the bf16 mode)
+# --------------------------------------------------------------------------
+
+
+def bf16_round(a) -> np.ndarray:
+    """Round to the nearest bf16 value (8 significant bits, ties to even).
+
+    Written from the definition: with a = m * 2**e, 0.5 <= |m| < 1, keep
+    rint(m * 2**8) * 2**(e-8).  Exact in fp64 for finite normal-range values
+    (the only ones the layer produces).  Returns fp64.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def _store(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Value after a store in the layer's storage dtype."""
+    return bf16_round(a) if dtype == "bf16" else np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# S1: RMSNorm   ([P3] survival table: RMSNorm without mean subtraction;
+#                [P4] Tab 5: RMSNorm stability)
+# --------------------------------------------------------------------------
+
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """h = gamma * x / sqrt(mean(x^2) + eps), per token row (fp64)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return np.asarray(gamma, dtype=np.float64) * x / np.sqrt(ms + eps)
+
+
+def silu(a: np.ndarray) -> np.ndarray:
+    """silu(a) = a * sigmoid(a) = a / (1 + exp(-a)) in fp64 (SiLU-gated GLU)."""
+    return a / (1.0 + np.exp(-a))
+
+
+def glu(h: np.ndarray, Wg: np.ndarray, Wu: np.ndarray) -> np.ndarray:
+    """silu(h Wg^T) * (h Wu^T), the gated hidden of a GLU expert."""
+    return silu(h @ np.asarray(Wg, np.float64).T) * (h @ np.asarray(Wu, np.float64).T)
+
+
+# --------------------------------------------------------------------------
+# S3: scores.  The router score is a sigmoid (reading of the noaux_tc rule,
+# [P1] capsule 16).  To make routing decisions bit-reproducible from fp32
+# logits, the sigmoid is fixed down to each fp32 operation:
+#   y = -clamp(l, -30, 30);  n = rint(y * LOG2E)
+#   r = (y - n*LN2_HI) - n*LN2_LO            (Cody & Waite argument reduction)
+#   p = degree-7 Taylor polynomial of exp(r), Horner, separate mul and add
+#   e = p * 2**n;  s = 1 / (1 + e)           (IEEE fp32 divide)
+# --------------------------------------------------------------------------
+
+
+def _sigmoid_constants():
+    """Derive the fp32 constants from ln 2 (50 significant digits)."""
+    getcontext().prec = 60
+    ln2 = Decimal(2).ln()
+    log2e = F32(float(1 / ln2))
+    # ln 2 truncated to 16 significant bits: n*LN2_HI is exact for |n| < 2**8
+    hi = (ln2 * (1 << 16)).to_integral_value(rounding="ROUND_FLOOR") / (1 << 16)
+    ln2_hi = F32(float(hi))
+    ln2_lo = F32(float(ln2 - hi))
+    taylor = [F32(1.0 / float(np.prod(np.arange(1, i + 1, dtype=np.float64)))) for i in range(8)]
+    return log2e, ln2_hi, ln2_lo, taylor
+
+
+LOG2E, LN2_HI, LN2_LO, _TAYLOR = _sigmoid_constants()
+LOGIT_CLAMP = F32(30.0)
+
+
+def sigmoid_r(logits: np.ndarray) -> np.ndarray:
+    """Router score s = 1/(1+exp(-l)) with every step an fp32 op (see above)."""
+    l = np.asarray(logits, dtype=F32)
+    y = -np.minimum(np.maximum(l, -LOGIT_CLAMP), LOGIT_CLAMP)
+    n = np.rint(y * LOG2E).astype(F32)
+    r = (y - n * LN2_HI) - n * LN2_LO
+    p = _TAYLOR[7]
+    for i in range(6, -1, -1):
+        p = (p * r).astype(F32) + _TAYLOR[i]
+    p = p.astype(F32)
+    e = np.ldexp(p, n.astype(np.int32)).astype(F32)
+    return (F32(1.0) / (F32(1.0) + e)).astype(F32)
+
+
+# --------------------------------------------------------------------------
+# S5-S6: biased top-k and unbiased gates  ([P4] Tab 8-10: the bias reroutes
+# only, gate values are the renormalised scores of the chosen experts)
+# --------------------------------------------------------------------------
+
+
+def topk_select(s: np.ndarray, bias: np.ndarray, k: int) -> np.ndarray:
+    """idx[T,k]: the k experts with the largest v = s + b (fp32 add), ordered
+    by v descending, equal v by expert index ascending."""
+    s = np.asarray(s, dtype=F32)
+    assert np.all(np.isfinite(s))
+    v = (s + np.asarray(bias, dtype=F32)[None, :]).astype(F32)
+    e_idx = np.broadcast_to(np.arange(v.shape[1]), v.shape)
+    order = np.lexsort((e_idx, -v), axis=1)      # primary: -v asc; then e asc
+    return order[:, :k].astype(np.int32)
+
+
+def gates_from(s: np.ndarray, idx: np.ndarray, routed_scale: float = 1.0) -> np.ndarray:
+    """g_j = s_{idx_j} / S * routed_scale, S the fp32 sum of the selected
+    scores in slot order (fp32 throughout)."""
+    s_sel = np.take_along_axis(np.asarray(s, dtype=F32), idx.astype(np.int64), axis=1)
+    S = s_sel[:, 0].copy()
+    for j in range(1, s_sel.shape[1]):
+        S = (S + s_sel[:, j]).astype(F32)
+    g = (s_sel / S[:, None]).astype(F32)
+    return (g * F32(routed_scale)).astype(F32)
+
+
+# --------------------------------------------------------------------------
+# S7-S9: counts, offsets and the stable permutation ([P1] capsule 25 dispatch
+# buffer; dropless: every (token, slot) pair gets a row)
+# --------------------------------------------------------------------------
+
+
+def permutation(idx: np.ndarray, E: int):
+    """Group the (t, j) pairs by expert, keeping (t, j) order inside a group.
+
+    Returns counts[E], offsets[E+1] (exclusive prefix sum), perm_src[T*k]
+    (token of each row) and inv[T,k] (row of each (t, j)).
+    """
+    T, k = idx.shape
+    flat = idx.reshape(-1).astype(np.int64)
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    order = np.argsort(flat, kind="stable")          # rows in expert order
+    perm_src = (order // k).astype(np.int32)
+    inv = np.empty(T * k, dtype=np.int32)
+    inv[order] = np.arange(T * k, dtype=np.int32)
+    return counts, offsets, perm_src, inv.reshape(T, k)
+
+
+# --------------------------------------------------------------------------
+# S4 + S18: QB histogram and update ([P4] Tab 2 Fig. 2(b) histogram quantile;
+# Tab 8-10 delayed, mean-centred, frozen at inference; [P5] hot experts
+# raise their threshold)
+# --------------------------------------------------------------------------
+
+
+def score_bins(s: np.ndarray, B: int) -> np.ndarray:
+    """bin = min(B-1, floor(s*B)), s*B an fp32 product."""
+    sb = (np.asarray(s, dtype=F32) * F32(B)).astype(F32)
+    return np.minimum(np.floor(sb).astype(np.int64), B - 1)
+
+
+def histogram(s: np.ndarray, B: int) -> np.ndarray:
+    """hist[E,B] (int64): per expert, the number of tokens whose score falls
+    in each of B equal bins of [0, 1]."""
+    T, E = s.shape
+    bins = score_bins(s, B)
+    flat = (np.arange(E)[None, :] * B + bins).reshape(-1)
+    return np.bincount(flat, minlength=E * B).reshape(E, B).astype(np.int64)
+
+
+def qb_quantiles(hist: np.ndarray, N: int, k: int) -> np.ndarray:
+    """Histogram estimate q_e of the score each expert must exceed to receive
+    its target load m = N*k/E.
+
+    Scanning bins from the top, j is the bin with A_j*E < N*k <= (A_j+c_j)*E
+    (A_j = count above bin j, integer comparisons); inside it the estimate is
+    linear: q = (j+1)/B - ((N*k - A_j*E) / (E*c_j)) / B   (fp64).
+    """
+    E, B = hist.shape
+    target = N * k
+    q = np.zeros(E, dtype=np.float64)
+    for e in range(E):
+        above = 0
+        for j in range(B - 1, -1, -1):
+            c = int(hist[e, j])
+            if above * E < target <= (above + c) * E:
+                frac = float(target - above * E) / float(E * c)
+                q[e] = (j + 1) / B - frac / B
+                break
+            above += c
+        else:                                   # unreachable for N > 0
+            raise AssertionError("no quantile bin")
+    return q
+
+
+def qb_bias(q: np.ndarray) -> np.ndarray:
+    """b_e = fp32(mu - q_e), mu the fp64 mean of q summed in expert order."""
+    mu = 0.0
+    for v in q:
+        mu += float(v)
+    mu = mu / len(q)
+    return np.array([mu - float(v) for v in q], dtype=np.float64).astype(F32)
+
+
+def qb_update(hist: np.ndarray, N: int, k: int, bias: np.ndarray) -> np.ndarray:
+    """New bias from the accumulated histogram; the old bias is kept when no
+    token was seen.  The caller applies it to the next forward (one step late)."""
+    if N == 0:
+        return np.asarray(bias, dtype=F32).copy()
+    return qb_bias(qb_quantiles(hist, N, k))
+
+
+def exact_quantile(s_col: np.ndarray, N: int, k: int, E: int) -> float:
+    """Sort-based counterpart of ``qb_quantiles``: the ceil(N*k/E)-th largest
+    score of one expert."""
+    m = -(-(N * k) // E)
+    return float(np.sort(np.asarray(s_col, dtype=np.float64))[::-1][m - 1])
+
+
+# --------------------------------------------------------------------------
+# The whole layer
+# --------------------------------------------------------------------------
+
+
+def router_logits(h: np.ndarray, W_r: np.ndarray, c: Optional[np.ndarray] = None) -> np.ndarray:
+    """l = h W_r^T (+ c) in fp64, stored as fp32 ([P4] Tab 1 routing branch)."""
+    l = h @ np.asarray(W_r, np.float64).T
+    if c is not None:
+        l = l + np.asarray(c, np.float64)[None, :]
+    return l.astype(F32)
+
+
+def expert_outputs(X: np.ndarray, offsets: np.ndarray, W: Dict[str, np.ndarray], dtype: str):
+    """Per expert e on its rows X[off_e:off_e+1]: H = silu(X Wg^T) * (X Wu^T),
+    Y = H Wd^T  ([P1] capsule 20: three batched matmuls per expert group)."""
+    E = len(offsets) - 1
+    f = W["W_g"].shape[1]
+    lat = W["W_d"].shape[1]
+    H = np.zeros((X.shape[0], f), dtype=np.float64)
+    Y = np.zeros((X.shape[0], lat), dtype=np.float64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        He = _store(glu(X[a:b], W["W_g"][e], W["W_u"][e]), dtype)
+        H[a:b] = He
+        Y[a:b] = _store(He @ np.asarray(W["W_d"][e], np.float64).T, dtype)
+    return H, Y
+
+
+def forward(x: np.ndarray, W: Dict[str, np.ndarray], bias: np.ndarray, *, k: int, dtype: str,
+            eps: float = 1e-6, B: int = 256, routed_scale: float = 1.0,
+            logits: Optional[np.ndarray] = None, with_hist: bool = True) -> Dict[str, np.ndarray]:
+    """One training (or frozen) forward of the layer on x[T,d].
+
+    ``logits`` (fp32 [T,E]) replaces the router output when given, so that the
+    routing decisions can be checked bit for bit against a given set of
+    logits; everything else is computed here.
+
+    Returns every intermediate: h, logits, s, idx, gates, counts, offsets,
+    perm_src, inv, z, G, H, Y, y_lat, sh, y_r, out, and hist (if with_hist).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T = x.shape[0]
+    E = W["W_r"].shape[0]
+    r: Dict[str, np.ndarray] = {}
+    h = _store(rmsnorm(x, W["gamma"], eps), dtype)                    # S1
+    r["h"] = h
+    lg = router_logits(h, W["W_r"], W.get("c")) if logits is None else np.asarray(logits, F32)
+    r["logits"] = lg                                                   # S2
+    s = sigmoid_r(lg)                                                  # S3
+    r["s"] = s
+    if with_hist:
+        r["hist"] = histogram(s, B)                                    # S4
+    idx = topk_select(s, bias, k)                                      # S5
+    g = gates_from(s, idx, routed_scale)                               # S6
+    r["idx"], r["gates"] = idx, g
+    counts, offsets, perm_src, inv = permutation(idx, E)               # S7-S9
+    r.update(counts=counts, offsets=offsets, perm_src=perm_src, inv=inv)
+    if W.get("W_sg") is not None and W["W_sg"].shape[0] > 0:           # S10
+        G = _store(glu(h, W["W_sg"], W["W_su"]), dtype)
+        sh = G @ np.asarray(W["W_sd"], np.float64).T
+    else:
+        G = np.zeros((T, 0))
+        sh = np.zeros((T, x.shape[1]))
+    r["G"], r["sh"] = G, sh
+    z = _store(h @ np.asarray(W["W_dn"], np.float64).T, dtype)        # S11
+    r["z"] = z
+    X = z[perm_src]                                                    # S12
+    H, Y = expert_outputs(X, offsets, W, dtype)                        # S13-S14
+    r["H"], r["Y"] = H, Y
+    y_lat = np.zeros((T, z.shape[1]), dtype=np.float64)                # S15
+    for j in range(k):
+        y_lat += g[:, j].astype(np.float64)[:, None] * Y[inv[:, j]]
+    y_lat = _store(y_lat, dtype)
+    r["y_lat"] = y_lat
+    y_r = y_lat @ np.asarray(W["W_up"], np.float64).T                 # S16
+    r["y_r"] = y_r
+    r["out"] = _store(sh + y_r, dtype)                                 # S17
+    return r
+
+
+def forward_tokens(x_rows: np.ndarray, W: Dict[str, np.ndarray], idx_rows: np.ndarray,
+                   gates_rows: np.ndarray, *, dtype: str, eps: float = 1e-6) -> np.ndarray:
+    """Layer output for a few tokens given their routing (idx, gates).
+
+    Every token is independent of the others once its routing is fixed, so
+    this evaluates, per token, the same rounding points as ``forward`` without
+    any permutation: out = sh(h) + W_up bf(sum_j g_j bf(W_d[e_j] bf(GLU_e_j(z)))).
+    Used to check outputs of large batches on sampled tokens.
+    """
+    x_rows = np.asarray(x_rows, dtype=np.float64)
+    h = _store(rmsnorm(x_rows, W["gamma"], eps), dtype)
+    z = _store(h @ np.asarray(W["W_dn"], np.float64).T, dtype)
+    out = np.zeros_like(x_rows)
+    for t in range(x_rows.shape[0]):
+        y_lat = np.zeros(z.shape[1])
+        for j in range(idx_rows.shape[1]):
+            e = int(idx_rows[t, j])
+            He = _store(glu(z[t:t + 1], W["W_g"][e], W["W_u"][e]), dtype)
+            Ye = _store(He @ np.asarray(W["W_d"][e], np.float64).T, dtype)
+            y_lat += float(gates_rows[t, j]) * Ye[0]
+        y_lat = _store(y_lat, dtype)
+        y_r = y_lat @ np.asarray(W["W_up"], np.float64).T
+        if W["W_sg"].shape[0] > 0:
+            G = _store(glu(h[t:t + 1], W["W_sg"], W["W_su"]), dtype)
+            sh = (G @ np.asarray(W["W_sd"], np.float64).T)[0]
+        else:
+            sh = 0.0
+        out[t] = _store(sh + y_r, dtype)
+    return out
+
+
+def load_stats(counts: np.ndarray) -> Dict[str, float]:
+    """Balance statistics that do not hide dead experts ([P1] capsule 16: the
+    router entropy read 0.9999 while 94.5% of experts were dead)."""
+    c = np.asarray(counts, dtype=np.float64)
+    live = c[c > 0]
+    return {
+        "max_over_min": float(c.max() / c.min()) if c.min() > 0 else float("inf"),
+        "max_over_mean": float(c.max() / c.mean()),
+        "dead": int((c == 0).sum()),
+        "cv": float(c.std() / c.mean()),
+        "min_live": float(live.min()) if live.size else 0.0,
+    }

@@ -1,0 +1,123 @@
+"""Pins of the oracle's whole-layer forward: the dispatch path against a
+dense-masked brute force that never permutes, special cases that reduce to a
+plain GLU, routing-independence with identical experts, the per-token path used
+for sampled checks, and the parameter count of the replica-shaped layer
+(the self-check of the e-book's capsule 8)."""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as o
+from sparse_moe_layer_rmsnorm_amd import workloads as wl
+
+F32 = np.float32
+
+
+def _small(dtype="f32", T=48, d=64, l=32, E=8, k=3, f=32, f_s=64, wid=1):
+    return wl.LayerShape("t", wid, dtype, T=T, d=d, l=l, E=E, k=k, f=f, f_s=f_s)
+
+
+def _dense_masked_ylat(z, idx, g, W):
+    """Every expert on every token, weighted by a dense gate matrix that is
+    zero for experts the token did not pick."""
+    T = z.shape[0]
+    E = W["W_g"].shape[0]
+    G = np.zeros((T, E))
+    for j in range(idx.shape[1]):
+        G[np.arange(T), idx[:, j]] += g[:, j].astype(np.float64)
+    y = np.zeros((T, W["W_d"].shape[1]))
+    for e in range(E):
+        He = o.silu(z @ W["W_g"][e].astype(np.float64).T) * (z @ W["W_u"][e].astype(np.float64).T)
+        y += G[:, e:e + 1] * (He @ W["W_d"][e].astype(np.float64).T)
+    return y
+
+
+def test_dispatch_equals_dense_masked():
+    s = _small()
+    W = wl.make_weights(s)
+    x = wl.make_x(s)
+    b = (np.random.default_rng(0).standard_normal(s.E) * 0.05).astype(F32)
+    r = o.forward(x, W, b, k=s.k, dtype="f32")
+    want = _dense_masked_ylat(r["z"], r["idx"], r["gates"], W)
+    np.testing.assert_allclose(r["y_lat"], want, rtol=1e-12, atol=1e-12)
+    out = want @ W["W_up"].astype(np.float64).T + r["sh"]
+    np.testing.assert_allclose(r["out"], out, rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_is_a_dense_glu():
+    s = _small(E=1, k=1)
+    W = wl.make_weights(s)
+    x = wl.make_x(s)
+    r = o.forward(x, W, np.zeros(1, F32), k=1, dtype="f32")
+    assert np.all(r["gates"] == 1.0)
+    h = o.rmsnorm(x, W["gamma"], 1e-6)
+    z = h @ W["W_dn"].astype(np.float64).T
+    y = o.glu(z, W["W_g"][0], W["W_u"][0]) @ W["W_d"][0].astype(np.float64).T
+    sh = o.glu(h, W["W_sg"], W["W_su"]) @ W["W_sd"].astype(np.float64).T
+    np.testing.assert_allclose(r["out"], sh + y @ W["W_up"].astype(np.float64).T, rtol=1e-12, atol=1e-12)
+
+
+def test_identical_experts_make_routing_irrelevant():
+    s = _small()
+    W = wl.make_weights(s)
+    for name in ("W_g", "W_u", "W_d"):
+        W[name] = np.repeat(W[name][:1], s.E, axis=0)
+    x = wl.make_x(s)
+    r0 = o.forward(x, W, np.zeros(s.E, F32), k=s.k, dtype="f32")
+    rb = o.forward(x, W, np.linspace(-1, 1, s.E).astype(F32), k=s.k, dtype="f32")
+    assert np.any(r0["idx"] != rb["idx"])
+    y0 = o.glu(r0["z"], W["W_g"][0], W["W_u"][0]) @ W["W_d"][0].astype(np.float64).T
+    for r in (r0, rb):   # y_lat = (sum of the gates) * the one expert's output
+        gsum = r["gates"].astype(np.float64).sum(1, keepdims=True)
+        np.testing.assert_allclose(r["y_lat"], gsum * y0, rtol=1e-12, atol=1e-12)
+
+
+def test_no_shared_expert():
+    s = _small(f_s=0)
+    W = wl.make_weights(s)
+    r = o.forward(wl.make_x(s), W, np.zeros(s.E, F32), k=s.k, dtype="f32")
+    np.testing.assert_allclose(r["out"], r["y_r"], rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_per_token_path_equals_forward(dtype):
+    s = _small(dtype=dtype, T=40)
+    W = wl.make_weights(s)
+    x = wl.make_x(s)
+    r = o.forward(x, W, np.zeros(s.E, F32), k=s.k, dtype=dtype)
+    pick = np.array([0, 3, 17, 39])
+    got = o.forward_tokens(x[pick], W, r["idx"][pick], r["gates"][pick], dtype=dtype)
+    if dtype == "f32":
+        np.testing.assert_allclose(got, r["out"][pick], rtol=1e-12, atol=1e-12)
+    else:   # same rounding points; a summation-order difference can flip one bf16 ulp
+        rel = np.abs(got - r["out"][pick]).max() / np.abs(r["out"][pick]).max()
+        assert rel <= 2.0 ** -6
+
+
+def test_bf16_mode_rounds_stored_values():
+    s = _small(dtype="bf16")
+    W = wl.make_weights(s)
+    r = o.forward(wl.make_x(s), W, np.zeros(s.E, F32), k=s.k, dtype="bf16")
+    for key in ("h", "z", "G", "H", "Y", "y_lat", "out"):
+        np.testing.assert_array_equal(o.bf16_round(r[key]), r[key])
+
+
+def test_injected_logits_drive_routing():
+    s = _small()
+    W = wl.make_weights(s)
+    x = wl.make_x(s)
+    lg = np.random.default_rng(3).standard_normal((s.T, s.E)).astype(F32)
+    r = o.forward(x, W, np.zeros(s.E, F32), k=s.k, dtype="f32", logits=lg)
+    np.testing.assert_array_equal(r["idx"], o.topk_select(o.sigmoid_r(lg), np.zeros(s.E, F32), s.k))
+
+
+def test_replica_parameter_count():
+    """Hand count of the replica-shaped layer: gamma + router + shared GLU +
+    down/up projections + routed experts (107.74M total, 9.44M per token)."""
+    s = wl.workload("replica")
+    total = s.d + s.E * s.d + 3 * s.d * s.f_s + 2 * s.d * s.l + 3 * s.E * s.f * s.l
+    active = s.d + s.E * s.d + 3 * s.d * s.f_s + 2 * s.d * s.l + 3 * s.k * s.f * s.l
+    assert total == 107_742_208 and active == 9_438_208
+    W = wl.make_weights(wl.workload("tiny"))   # same formula on materialised tensors
+    t = wl.workload("tiny")
+    assert sum(v.size for v in W.values()) == (t.d + t.E * t.d + 3 * t.d * t.f_s + 2 * t.d * t.l
+                                               + 3 * t.E * t.f * t.l)

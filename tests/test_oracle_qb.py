@@ -1,0 +1,118 @@
+"""Pins of the oracle's quantile balancing: histogram against numpy's
+histogram, histogram quantiles against sort-based exact quantiles (within one
+bin), a hand-worked example, sum-zero centring, monotonicity and the load
+trend the demo shows (Tab 2, Fig. 2(a))."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as o
+from sparse_moe_layer_rmsnorm_amd import workloads as wl
+
+F32 = np.float32
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.mark.parametrize("B", [256, 64, 4])
+def test_histogram_matches_numpy_histogram(B):
+    rng = np.random.default_rng(B)
+    s = o.sigmoid_r((rng.standard_normal((3000, 12)) * 4).astype(F32))
+    s[:5] = F32(1.0)
+    s[5:9] = F32(0.5)
+    h = o.histogram(s, B)
+    for e in range(12):
+        want, _ = np.histogram(s[:, e].astype(np.float64), bins=B, range=(0.0, 1.0))
+        np.testing.assert_array_equal(h[e], want)
+    assert h.sum() == s.size
+
+
+def test_qb_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "qb_worked_example.json")))
+    s = np.array(g["scores"], F32)
+    hist = o.histogram(s, g["B"])
+    np.testing.assert_array_equal(hist, g["hist"])
+    q = o.qb_quantiles(hist, s.shape[0], g["k"])
+    np.testing.assert_array_equal(q, g["q"])
+    b = o.qb_update(hist, s.shape[0], g["k"], np.zeros(g["E"], F32))
+    np.testing.assert_array_equal(b, np.array(g["bias"], F32))
+    before = np.bincount(o.topk_select(s, np.zeros(2, F32), 1).ravel(), minlength=2)
+    after = np.bincount(o.topk_select(s, b, 1).ravel(), minlength=2)
+    np.testing.assert_array_equal(before, g["loads_before"])
+    np.testing.assert_array_equal(after, g["loads_after"])
+
+
+@pytest.mark.parametrize("T,E,k,B", [(256, 16, 2, 256), (2048, 256, 6, 256), (1024, 896, 16, 256), (999, 33, 5, 64)])
+def test_qb_quantile_within_one_bin_of_exact(T, E, k, B):
+    rng = np.random.default_rng(T + E)
+    s = o.sigmoid_r((rng.standard_normal((T, E)) + rng.standard_normal(E)[None, :]).astype(F32))
+    q = o.qb_quantiles(o.histogram(s, B), T, k)
+    exact = np.array([o.exact_quantile(s[:, e], T, k, E) for e in range(E)])
+    assert np.max(np.abs(q - exact)) <= 1.0 / B
+    # both lie in the same bin (the estimate may sit on the bin's lower edge)
+    assert np.all(np.floor(q * B) <= np.minimum(np.floor(exact * B), B - 1))
+
+
+def test_qb_bias_sums_to_zero_and_is_monotone():
+    rng = np.random.default_rng(11)
+    T, E, k = 4096, 64, 6
+    offset = np.linspace(0, 2, E).astype(F32)          # hotter experts have a larger offset
+    lg = (rng.standard_normal((T, E)) + offset[None, :]).astype(F32)
+    s = o.sigmoid_r(lg)
+    b = o.qb_update(o.histogram(s, 256), T, k, np.zeros(E, F32))
+    assert abs(b.astype(np.float64).sum()) <= E * 2.0 ** -24 * np.abs(b).max()
+    # hot -> lower bias: decreasing up to sampling noise of a few bins
+    assert np.all(np.diff(b.astype(np.float64)) <= 4.0 / 256)
+    assert np.corrcoef(offset, b)[0, 1] < -0.95
+    assert b[-1] < b[0]
+
+
+def test_qb_no_tokens_keeps_bias():
+    b0 = np.array([0.5, -0.5, 0.25], F32)
+    np.testing.assert_array_equal(o.qb_update(np.zeros((3, 8), np.int64), 0, 1, b0), b0)
+
+
+def test_qb_k_equals_E_takes_lowest_occupied_bin():
+    s = np.array([[0.3, 0.7], [0.6, 0.9]], F32)
+    q = o.qb_quantiles(o.histogram(s, 4), 2, 2)
+    np.testing.assert_array_equal(q, [0.25, 0.5])   # floor(min score * B) / B
+
+
+def test_qb_balances_skewed_load():
+    """One delayed update on the load-skew workload (Zipf logit offsets):
+    max/mean load drops from > 10 to < 1.6.  The demo shows the same trend
+    (3.7 -> 1.5 max/min, Tab 2 Fig. 2(a)) on shapes it does not state."""
+    figs = json.load(open(os.path.join(GOLDEN, "pages_figures.json")))
+    shape = wl.workload("skew", 4096)
+    W = wl.make_weights(shape)
+    c = wl.zipf_logit_offset(shape)
+
+    def scores(step):
+        h = o.bf16_round(o.rmsnorm(wl.make_x(shape, step), W["gamma"], shape.rms_eps))
+        return o.sigmoid_r(o.router_logits(h, W["W_r"], c))
+
+    b = np.zeros(shape.E, F32)
+    s0 = scores(0)
+    before = o.load_stats(np.bincount(o.topk_select(s0, b, shape.k).ravel(), minlength=shape.E))
+    b = o.qb_update(o.histogram(s0, shape.B), shape.T, shape.k, b)
+    s1 = scores(1)                                    # the bias acts on the next batch
+    after = o.load_stats(np.bincount(o.topk_select(s1, b, shape.k).ravel(), minlength=shape.E))
+    assert before["max_over_mean"] > 10
+    assert after["max_over_mean"] < 1.6
+    assert after["dead"] == 0
+    assert after["max_over_min"] < before["max_over_min"] / figs["qb_demo_max_over_min_before"]["value"]
+
+
+def test_qb_matches_exact_quantile_rule_in_balance():
+    """Setting b from the exact quantiles instead of the histogram ones gives
+    nearly the same loads: the estimator error (one bin) is what separates them."""
+    rng = np.random.default_rng(5)
+    T, E, k = 8192, 64, 4
+    s = o.sigmoid_r((rng.standard_normal((T, E)) + np.linspace(-1, 1, E)[None, :]).astype(F32))
+    q_exact = np.array([o.exact_quantile(s[:, e], T, k, E) for e in range(E)])
+    b_exact = o.qb_bias(q_exact)
+    b_hist = o.qb_update(o.histogram(s, 256), T, k, np.zeros(E, F32))
+    assert np.max(np.abs(b_exact - b_hist)) <= 2.0 / 256
+    ld = np.bincount(o.topk_select(s, b_hist, k).ravel(), minlength=E)
+    assert ld.max() / ld.mean() < 1.3
