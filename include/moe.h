@@ -1,0 +1,210 @@
+/*
+ * moe.h - C ABI of the Stable LatentMoE layer forward pass and its
+ * quantile-balancing (QB) router-bias update on one AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The layer (architecture paragraph and Tab 1 of the "Kimi K3 MoE lightweight
+ * replica demo" article; design survival table of the Attention->K3 course,
+ * Day 28):
+ *   h     = RMSNorm(x)                    per token, gamma-scaled, eps = rms_eps
+ *   l     = h W_r^T (+ c)                 router logits, fp32
+ *   s     = sigmoid(l)                    scores (fp32, fixed op by op)
+ *   idx   = top-k of s + b                the bias b only reroutes
+ *   g     = s[idx] / sum s[idx]           gates, renormalised, bias-free
+ *   G     = silu(h W_sg^T) * (h W_su^T)   shared expert at model width d
+ *   z     = h W_dn^T                      down-projection to latent width l
+ *   Y_e   = (silu(z W_g[e]^T) * (z W_u[e]^T)) W_d[e]^T   routed experts at l
+ *   y_lat = sum_j g_j Y_{idx_j}           gate-weighted combine
+ *   out   = G W_sd^T + y_lat W_up^T       no residual (the model adds its own)
+ * QB (Tab 2 Fig. 2(b) and Tab 8-10 of the demo article; idle-experts section
+ * of the "K3 tops open source" blog): every training forward adds each
+ * token's score to a per-expert histogram; qb_update() turns the histogram
+ * into the score q_e each expert must beat to get its share T*k/E of the
+ * tokens and sets b_e = mean(q) - q_e (mean-centred); the new bias is used by
+ * the next forward (one step late); in frozen mode nothing is accumulated or
+ * updated.
+ *
+ * Conventions
+ *   - Every pointer argument named as device memory is a HIP device pointer
+ *     the caller allocated; the library never allocates device memory and
+ *     keeps no pointer past moe_destroy() other than those in moe_weights and
+ *     the state buffer, which must outlive the context.
+ *   - Weights are row-major [out, in] (y = x W^T).  In MOE_BF16 mode x, out
+ *     and every weight except gamma and logit_offset are bf16; in MOE_F32 mode
+ *     all are fp32.  Logits, scores, gates and the bias are fp32; indices are
+ *     int32.  Accumulation is fp32.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call that
+ *     takes a stream only enqueues work on it and returns; results are valid
+ *     once the stream has reached them.  No call synchronises the device or
+ *     copies to the host, so forward/route/update can be captured in a graph.
+ *   - Errors: arguments are checked on the host before anything is enqueued;
+ *     a failed check returns an error code and enqueues nothing.  A launch
+ *     failure returns MOE_ERR_HIP.  moe_last_error() gives a message for the
+ *     last failure on the calling thread.  A context is not thread-safe.
+ *   - Calls that share a context, or a workspace, must be ordered (one
+ *     stream, or events) by the caller.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, unknown enum value            */
+  MOE_ERR_SHAPE = 2,       /* sizes out of the supported ranges          */
+  MOE_ERR_DTYPE = 3,       /* unsupported dtype                           */
+  MOE_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+  MOE_ERR_STATE = 5,       /* QB state would overflow; bad call order    */
+  MOE_ERR_HIP = 6          /* a HIP runtime call or a launch failed      */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Tab 10 of the demo article: QB updates during training, frozen at inference. */
+typedef enum moe_qb_mode { MOE_QB_TRAIN = 0, MOE_QB_FROZEN = 1 } moe_qb_mode;
+
+/*
+ * Layer sizes.  d, l, f must be multiples of 64 and f_s a multiple of 64 or 0
+ * (0 = no shared expert; several shared experts of hidden f are one of hidden
+ * n*f).  1 <= E <= 1024, 1 <= k <= min(E, 32), 2 <= qb_bins <= 512.
+ * max_tokens bounds T for every call (1 <= max_tokens, max_tokens*k < 2^31).
+ * rms_eps > 0.  routed_scale multiplies every gate (1 = plain renormalised).
+ */
+typedef struct moe_config {
+  int32_t d, l, E, k, f, f_s;
+  moe_dtype dtype;
+  float rms_eps;
+  int32_t qb_bins;
+  moe_qb_mode qb_mode;
+  int64_t max_tokens;
+  float routed_scale;
+} moe_config;
+
+/* Device pointers, caller-owned, read-only to the library. */
+typedef struct moe_weights {
+  const float* gamma;        /* [d]     fp32 RMSNorm scale                 */
+  const void* W_r;           /* [E,d]   router                             */
+  const float* logit_offset; /* [E]     fp32 added to the logits, or NULL  */
+  const void* W_sg;          /* [f_s,d] shared gate   (NULL when f_s == 0) */
+  const void* W_su;          /* [f_s,d] shared up     (NULL when f_s == 0) */
+  const void* W_sd;          /* [d,f_s] shared down   (NULL when f_s == 0) */
+  const void* W_dn;          /* [l,d]   down-projection d -> l             */
+  const void* W_g;           /* [E,f,l] expert gate                        */
+  const void* W_u;           /* [E,f,l] expert up                          */
+  const void* W_d;           /* [E,l,f] expert down                        */
+  const void* W_up;          /* [d,l]   up-projection l -> d               */
+} moe_weights;
+
+/*
+ * Routing results (device pointers).  Any field may be NULL; the library then
+ * keeps that array in the workspace.  Rows of the permutation are grouped by
+ * expert (offsets[e] .. offsets[e+1]) and keep token order inside a group.
+ */
+typedef struct moe_route_out {
+  float* logits;     /* [T,E]  fp32 router logits                      */
+  int32_t* topk_idx; /* [T,k]  experts by biased score desc, index asc */
+  float* gates;      /* [T,k]  renormalised unbiased scores            */
+  int32_t* counts;   /* [E]    tokens per expert                       */
+  int32_t* offsets;  /* [E+1]  exclusive prefix sum of counts          */
+  int32_t* perm_src; /* [T*k]  token of each grouped row               */
+  int32_t* inv;      /* [T,k]  grouped row of each (token, slot)       */
+} moe_route_out;
+
+/* Byte offsets of the pieces of the QB state buffer (see moe_state_bytes). */
+typedef struct moe_state_layout {
+  size_t bias;  /* [E] fp32 router bias                                   */
+  size_t count; /* uint64 tokens accumulated since the last qb_update     */
+  size_t q;     /* [E] fp64 quantiles of the last qb_update               */
+  size_t hist;  /* [E, qb_bins] uint32 score histogram                    */
+  size_t total;
+} moe_state_layout;
+
+/* Byte offsets, inside the workspace, of the intermediates of one call. */
+typedef struct moe_ws_layout {
+  size_t h, logits, idx, gates, chunk_counts, counts, offsets, tile_offsets, perm_src, inv;
+  size_t hist_partial, G, z, H, Y, y_lat;
+  size_t total;
+} moe_ws_layout;
+
+typedef struct moe_ctx moe_ctx;
+
+/* Bytes of the QB state buffer for `cfg` (0 when cfg is invalid). */
+size_t moe_state_bytes(const moe_config* cfg);
+moe_status moe_state_layout_of(const moe_config* cfg, moe_state_layout* out);
+
+/* Bytes of workspace moe_forward / moe_route need for T tokens (0 if invalid). */
+size_t moe_workspace_bytes(const moe_config* cfg, int64_t T);
+moe_status moe_workspace_layout(const moe_config* cfg, int64_t T, moe_ws_layout* out);
+
+/*
+ * Create a context for `cfg` over the caller's weights and QB state buffer
+ * (moe_state_bytes(cfg) bytes of device memory, 256-byte aligned).  Enqueues
+ * on `stream` the clearing of the state: bias 0, histogram 0, count 0.
+ * *out receives a host object freed by moe_destroy().
+ */
+moe_status moe_init(const moe_config* cfg, const moe_weights* w, void* state, void* stream, moe_ctx** out);
+
+/*
+ * Routing only (RMSNorm, router, scores, QB histogram in training mode,
+ * biased top-k, gates, counts, offsets, permutation) for T tokens of x[T,d].
+ * When `logits` (device fp32 [T,E]) is not NULL it replaces the router output
+ * and x is not read (x may be NULL): routing is then a pure function of the
+ * logits and the bias, bit for bit.
+ */
+moe_status moe_route(moe_ctx* ctx, const void* x, const float* logits, int64_t T, moe_route_out* r,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Whole layer for T tokens: out[T,d] from x[T,d] (0 <= T <= max_tokens; T=0
+ * enqueues nothing).  In training mode also adds the tokens' scores to the QB
+ * histogram.  `r` (may be NULL) receives the routing.  `ws` must hold
+ * moe_workspace_bytes(cfg, T) bytes of device memory (256-byte aligned).
+ */
+moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_route_out* r, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * QB update from the histogram accumulated since the last update: the new
+ * bias b_e = mean(q) - q_e, then histogram and count are cleared.  Keeps the
+ * bias when no token was accumulated.  A no-op returning MOE_OK in frozen mode.
+ */
+moe_status qb_update(moe_ctx* ctx, void* stream);
+
+/* Copy the current bias (E fp32) to / from device memory on `stream`. */
+moe_status moe_get_bias(moe_ctx* ctx, float* dst, void* stream);
+moe_status moe_set_bias(moe_ctx* ctx, const float* src, void* stream);
+
+/* Switch between training and frozen QB; the histogram is kept. */
+moe_status moe_set_qb_mode(moe_ctx* ctx, moe_qb_mode mode);
+
+void moe_destroy(moe_ctx* ctx);
+
+const char* moe_status_string(moe_status s);
+const char* moe_last_error(void);
+
+/*
+ * Per-kernel timing.  After moe_profile_begin(ctx, n), each kernel the context
+ * launches (up to n launches) is bracketed by HIP events on its stream.
+ * moe_profile_end() waits for those events and fills, for each kernel id
+ * 0..MOE_NUM_KERNELS-1, the summed milliseconds and the launch count; then
+ * profiling stops.  Host-side event objects only; no device memory.
+ */
+enum {
+  MOE_K_RMSNORM = 0, MOE_K_GEMM_H, MOE_K_TOPK, MOE_K_HIST, MOE_K_HIST_REDUCE, MOE_K_SCAN,
+  MOE_K_OFFSETS, MOE_K_SCATTER, MOE_K_EXPERT_UP, MOE_K_EXPERT_DOWN, MOE_K_COMBINE, MOE_K_GEMM_OUT,
+  MOE_K_QB_QUANTILE, MOE_K_QB_BIAS, MOE_NUM_KERNELS
+};
+const char* moe_kernel_name(int id);
+moe_status moe_profile_begin(moe_ctx* ctx, int max_launches);
+moe_status moe_profile_end(moe_ctx* ctx, double* ms, int64_t* launches, int n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,192 @@
+"""ctypes binding of libmoe.so (include/moe.h), with the same names.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI.  PyTorch provides device memory and the stream.  Loading
+fails loudly when the library has not been built; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
+from typing import Dict, Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_STATE, MOE_ERR_HIP = range(7)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_QB_TRAIN, MOE_QB_FROZEN = 0, 1
+KERNELS = ["rmsnorm", "gemm_h", "topk", "hist", "hist_reduce", "scan", "offsets", "scatter", "expert_up",
+           "expert_down", "combine", "gemm_out", "qb_quantile", "qb_bias"]
+MOE_NUM_KERNELS = len(KERNELS)
+
+
+class moe_config(ctypes.Structure):
+    _fields_ = [("d", c_int32), ("l", c_int32), ("E", c_int32), ("k", c_int32), ("f", c_int32), ("f_s", c_int32),
+                ("dtype", c_int), ("rms_eps", c_float), ("qb_bins", c_int32), ("qb_mode", c_int),
+                ("max_tokens", c_int64), ("routed_scale", c_float)]
+
+
+class moe_weights(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("gamma", "W_r", "logit_offset", "W_sg", "W_su", "W_sd", "W_dn", "W_g",
+                                        "W_u", "W_d", "W_up")]
+
+
+class moe_route_out(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("logits", "topk_idx", "gates", "counts", "offsets", "perm_src", "inv")]
+
+
+class moe_state_layout(ctypes.Structure):
+    _fields_ = [(n, c_size_t) for n in ("bias", "count", "q", "hist", "total")]
+
+
+class moe_ws_layout(ctypes.Structure):
+    _fields_ = [(n, c_size_t) for n in ("h", "logits", "idx", "gates", "chunk_counts", "counts", "offsets",
+                                        "tile_offsets", "perm_src", "inv", "hist_partial", "G", "z", "H", "Y",
+                                        "y_lat", "total")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoe.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sparse_moe_layer_rmsnorm_amd.build` "
+                               "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        cfgp = POINTER(moe_config)
+        sig = {
+            "moe_state_bytes": (c_size_t, [cfgp]),
+            "moe_state_layout_of": (c_int, [cfgp, POINTER(moe_state_layout)]),
+            "moe_workspace_bytes": (c_size_t, [cfgp, c_int64]),
+            "moe_workspace_layout": (c_int, [cfgp, c_int64, POINTER(moe_ws_layout)]),
+            "moe_init": (c_int, [cfgp, POINTER(moe_weights), c_void_p, c_void_p, POINTER(c_void_p)]),
+            "moe_route": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, POINTER(moe_route_out), c_void_p, c_size_t,
+                                  c_void_p]),
+            "moe_forward": (c_int, [c_void_p, c_void_p, c_int64, c_void_p, POINTER(moe_route_out), c_void_p,
+                                    c_size_t, c_void_p]),
+            "qb_update": (c_int, [c_void_p, c_void_p]),
+            "moe_get_bias": (c_int, [c_void_p, c_void_p, c_void_p]),
+            "moe_set_bias": (c_int, [c_void_p, c_void_p, c_void_p]),
+            "moe_set_qb_mode": (c_int, [c_void_p, c_int]),
+            "moe_destroy": (None, [c_void_p]),
+            "moe_status_string": (c_char_p, [c_int]),
+            "moe_last_error": (c_char_p, []),
+            "moe_kernel_name": (c_char_p, [c_int]),
+            "moe_profile_begin": (c_int, [c_void_p, c_int]),
+            "moe_profile_end": (c_int, [c_void_p, POINTER(c_double), POINTER(c_int64), c_int]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/moe.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:moe|qb)_\w+)\s*\(", text)))
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        L = lib()
+        msg = L.moe_last_error().decode()
+        super().__init__(f"{where}: {L.moe_status_string(status).decode()}: {msg}")
+        self.status = status
+
+
+def check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+# ---------------------------------------------------------------- wrappers --
+# Same names as the C functions; plain integers stand for device pointers and
+# the stream (a hipStream_t handle, e.g. torch.cuda.current_stream().cuda_stream).
+
+def moe_state_bytes(cfg: moe_config) -> int:
+    return lib().moe_state_bytes(ctypes.byref(cfg))
+
+
+def moe_workspace_bytes(cfg: moe_config, T: int) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(cfg), T)
+
+
+def moe_state_layout_of(cfg: moe_config) -> moe_state_layout:
+    out = moe_state_layout()
+    check(lib().moe_state_layout_of(ctypes.byref(cfg), ctypes.byref(out)), "moe_state_layout_of")
+    return out
+
+
+def moe_workspace_layout(cfg: moe_config, T: int) -> moe_ws_layout:
+    out = moe_ws_layout()
+    check(lib().moe_workspace_layout(ctypes.byref(cfg), T, ctypes.byref(out)), "moe_workspace_layout")
+    return out
+
+
+def moe_init(cfg: moe_config, w: moe_weights, state: int, stream: int) -> int:
+    ctx = c_void_p()
+    check(lib().moe_init(ctypes.byref(cfg), ctypes.byref(w), state, stream, ctypes.byref(ctx)), "moe_init")
+    return ctx.value
+
+
+def moe_route(ctx: int, x: Optional[int], logits: Optional[int], T: int, r: Optional[moe_route_out], ws: int,
+              ws_bytes: int, stream: int) -> None:
+    check(lib().moe_route(ctx, x, logits, T, ctypes.byref(r) if r is not None else None, ws, ws_bytes, stream),
+          "moe_route")
+
+
+def moe_forward(ctx: int, x: int, T: int, out: int, r: Optional[moe_route_out], ws: int, ws_bytes: int,
+                stream: int) -> None:
+    check(lib().moe_forward(ctx, x, T, out, ctypes.byref(r) if r is not None else None, ws, ws_bytes, stream),
+          "moe_forward")
+
+
+def qb_update(ctx: int, stream: int) -> None:
+    check(lib().qb_update(ctx, stream), "qb_update")
+
+
+def moe_get_bias(ctx: int, dst: int, stream: int) -> None:
+    check(lib().moe_get_bias(ctx, dst, stream), "moe_get_bias")
+
+
+def moe_set_bias(ctx: int, src: int, stream: int) -> None:
+    check(lib().moe_set_bias(ctx, src, stream), "moe_set_bias")
+
+
+def moe_set_qb_mode(ctx: int, mode: int) -> None:
+    check(lib().moe_set_qb_mode(ctx, mode), "moe_set_qb_mode")
+
+
+def moe_destroy(ctx: int) -> None:
+    lib().moe_destroy(ctx)
+
+
+def moe_profile_begin(ctx: int, max_launches: int) -> None:
+    check(lib().moe_profile_begin(ctx, max_launches), "moe_profile_begin")
+
+
+def moe_profile_end(ctx: int) -> Dict[str, tuple]:
+    """{kernel name: (total ms, launches)} for the launches since begin."""
+    ms = (c_double * MOE_NUM_KERNELS)()
+    n = (c_int64 * MOE_NUM_KERNELS)()
+    check(lib().moe_profile_end(ctx, ms, n, MOE_NUM_KERNELS), "moe_profile_end")
+    return {KERNELS[i]: (ms[i], n[i]) for i in range(MOE_NUM_KERNELS)}
+
+
+def make_config(d: int, l: int, E: int, k: int, f: int, f_s: int, *, dtype: str = "bf16", rms_eps: float = 1e-6,
+                qb_bins: int = 256, frozen: bool = False, max_tokens: int = 1, routed_scale: float = 1.0
+                ) -> moe_config:
+    return moe_config(d=d, l=l, E=E, k=k, f=f, f_s=f_s, dtype=MOE_BF16 if dtype == "bf16" else MOE_F32,
+                      rms_eps=rms_eps, qb_bins=qb_bins, qb_mode=MOE_QB_FROZEN if frozen else MOE_QB_TRAIN,
+                      max_tokens=max_tokens, routed_scale=routed_scale)

@@ -1,0 +1,95 @@
+// Device helpers shared by the HIP kernels of the LatentMoE layer (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_DEV __device__ __forceinline__
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// ---------------------------------------------------------------- bf16 ----
+MOE_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+MOE_DEV uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ------------------------------------------------------------- sigmoid ----
+// Router score s = 1 / (1 + exp(-l)), every step a separately rounded fp32
+// operation so that the result is reproducible bit for bit on any IEEE fp32
+// machine:  y = -clamp(l, -30, 30); n = rint(y log2 e);
+// r = (y - n ln2_hi) - n ln2_lo (Cody-Waite reduction with ln 2 split after
+// 16 significant bits, so n ln2_hi is exact); exp(r) by its degree-7 Taylor
+// polynomial in Horner form; e = exp(r) 2^n; s = 1 / (1 + e) (IEEE divide).
+MOE_DEV float router_sigmoid(float logit) {
+#pragma clang fp contract(off)
+  const float kLog2e = 0x1.715476p+0f;   // fp32(1 / ln 2)
+  const float kLn2Hi = 0x1.62e4p-1f;     // ln 2 truncated to 16 significant bits
+  const float kLn2Lo = 0x1.7f7d1cp-20f;  // fp32(ln 2 - kLn2Hi)
+  const float c7 = 0x1.a01a02p-13f;      // fp32(1/7!)
+  const float c6 = 0x1.6c16c2p-10f;      // fp32(1/6!)
+  const float c5 = 0x1.111112p-7f;       // fp32(1/5!)
+  const float c4 = 0x1.555556p-5f;       // fp32(1/4!)
+  const float c3 = 0x1.555556p-3f;       // fp32(1/3!)
+  float y = -fminf(fmaxf(logit, -30.0f), 30.0f);
+  float n = __builtin_rintf(y * kLog2e);
+  float r = (y - n * kLn2Hi) - n * kLn2Lo;
+  float p = c7;
+  p = p * r + c6;
+  p = p * r + c5;
+  p = p * r + c4;
+  p = p * r + c3;
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  float e = __builtin_ldexpf(p, (int)n);
+  return 1.0f / (1.0f + e);
+}
+
+// Histogram bin of a score in [0, 1]: min(B - 1, floor(s * B)), s*B in fp32.
+MOE_DEV int score_bin(float s, int B) {
+#pragma clang fp contract(off)
+  int b = (int)floorf(s * (float)B);
+  b = b > 0 ? b : 0;
+  return b < B - 1 ? b : B - 1;
+}
+
+// Orderable key of an fp32 value: a larger float gives a larger key; -0 and
+// +0 give the same key.
+MOE_DEV uint32_t float_order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u << 1) == 0) u = 0;  // canonical +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// --------------------------------------------------------- wave helpers ----
+MOE_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+MOE_DEV unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    unsigned long long w = __shfl_xor(v, o, 64);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Blocks are handed to the 8 XCDs of the chip round-robin.  Map the
+// hardware block id to a logical id so that each XCD works on one contiguous
+// range of logical ids [0, n) (a bijection on [0, n) for any n).
+MOE_DEV int xcd_remap(int b, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int xcd = b & 7, local = b >> 3;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}

@@ -1,0 +1,59 @@
+// Host-side launchers of the LatentMoE HIP kernels (internal to libmoe).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tokens per routing chunk: one wavefront's worth.  Top-k counts experts per
+// chunk and the scatter ranks tokens inside a chunk with 64-bit lane masks.
+constexpr int kChunk = 64;
+// Rows per tile of the grouped expert GEMMs (also the granularity of the
+// per-expert tile offsets computed by the offsets kernel).
+constexpr int kExpertBM = 128;
+// Experts per block of the histogram kernel.
+constexpr int kHistExperts = 64;
+
+struct Dims {
+  int d, l, E, k, f, f_s, B;
+  bool bf16;
+  float eps, routed_scale;
+};
+
+int hist_token_slices(int T, int E);
+
+hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s);
+hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, int T, int32_t* idx,
+                       float* gates, int32_t* chunk_counts, hipStream_t s);
+hipError_t launch_hist(const Dims& D, const float* logits, int T, uint32_t* partial, uint32_t* hist,
+                       unsigned long long* count, hipStream_t s);
+hipError_t launch_hist_reduce(const Dims& D, const uint32_t* partial, int nslices, int T, uint32_t* hist,
+                              unsigned long long* count, hipStream_t s);
+hipError_t launch_scan(const Dims& D, int32_t* chunk_counts, int nchunks, int32_t* counts, hipStream_t s);
+hipError_t launch_offsets(const Dims& D, const int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
+                          hipStream_t s);
+hipError_t launch_scatter(const Dims& D, const int32_t* idx, const int32_t* offsets, const int32_t* chunk_base,
+                          int T, int32_t* perm_src, int32_t* inv, hipStream_t s);
+hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, const int32_t* inv, int T,
+                          void* y_lat, hipStream_t s);
+hipError_t launch_qb_quantile(const Dims& D, uint32_t* hist, const unsigned long long* count, double* q,
+                              hipStream_t s);
+hipError_t launch_qb_bias(const Dims& D, const double* q, unsigned long long* count, float* bias,
+                          hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+// Dense GEMMs on h (router logits, shared GLU hidden, latent z) and for the
+// output ([G | y_lat] [W_sd | W_up]^T).
+hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
+                         const void* W_sg, const void* W_su, const void* W_dn, float* logits, void* G,
+                         void* z, hipStream_t s);
+hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int T, const void* W_sd,
+                           const void* W_up, void* out, hipStream_t s);
+// Grouped expert GEMMs over the permuted rows.
+hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_src, const int32_t* offsets,
+                            const int32_t* tile_offsets, int T, const void* W_g, const void* W_u, void* H,
+                            hipStream_t s);
+hipError_t launch_expert_down(const Dims& D, const void* H, const int32_t* offsets,
+                              const int32_t* tile_offsets, int T, const void* W_d, void* Y, hipStream_t s);
+
+}  // namespace moe

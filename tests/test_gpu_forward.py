@@ -1,0 +1,122 @@
+"""GPU parity of the whole layer forward through the C ABI.
+
+The GPU's router logits are checked against the oracle's own (tolerance),
+then injected into the oracle so that routing is compared bit for bit and the
+outputs (and intermediates) within max|d|/max|ref| <= 1e-4 (fp32) / 2e-2
+(bf16)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as o
+from sparse_moe_layer_rmsnorm_amd import workloads as wl
+
+from gpu_util import (LOGIT_TOL, OUT_TOL, assert_routing_equal, make_layer, rel_err, say, to_np, x_on_gpu)
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+
+
+def _run(shape, T, *, bias=None, c=None, step=0, compare_inner=True, layer=None, W=None):
+    W = wl.make_weights(shape) if W is None else W
+    if c is not None:
+        W = dict(W, c=c)
+    x = wl.make_x(shape.with_tokens(T), step)
+    own = layer is None
+    if own:
+        layer = make_layer(shape, W, max_tokens=T, c=c)
+        if bias is not None:
+            layer.set_bias(bias)
+    b = to_np(layer.get_bias())
+    r = layer.route_buffers(T)
+    out = layer.forward(x_on_gpu(x, layer), route=r)
+    torch.cuda.synchronize()
+    lg = to_np(r["logits"])
+    ref_own = o.forward(x, W, b, k=shape.k, dtype=shape.dtype, eps=shape.rms_eps, B=shape.B)
+    assert rel_err(lg, ref_own["logits"]) <= LOGIT_TOL[shape.dtype]
+    ref = o.forward(x, W, b, k=shape.k, dtype=shape.dtype, eps=shape.rms_eps, B=shape.B, logits=lg)
+    assert_routing_equal(r, ref, T)
+    err = rel_err(to_np(out), ref["out"])
+    say(f"  out rel err {err:.3e}")
+    assert err <= OUT_TOL[shape.dtype]
+    if compare_inner:
+        v = layer.ws_views(T)
+        for name in ("h", "z", "y_lat") + (("G",) if shape.f_s else ()):
+            e = rel_err(to_np(v[name]), ref[name])
+            say(f"  {name} rel err {e:.3e}")
+            assert e <= OUT_TOL[shape.dtype], name
+        for name in ("H", "Y"):
+            e = rel_err(to_np(v[name]), ref[name])
+            say(f"  {name} rel err {e:.3e}")
+            assert e <= OUT_TOL[shape.dtype], name
+    if own:
+        layer.close()
+    return ref, out
+
+
+def _small(dtype, **kw):
+    base = dict(T=1, d=128, l=64, E=16, k=2, f=64, f_s=128)
+    base.update(kw)
+    return wl.LayerShape("case", 9, dtype, **base)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 77, 300])
+def test_forward_small(dtype, T):
+    say(f"forward small {dtype} T={T}")
+    _run(_small(dtype), T, bias=(np.random.default_rng(T).standard_normal(16) * 0.05).astype(F32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_no_shared_expert(dtype):
+    say(f"forward no shared {dtype}")
+    _run(_small(dtype, f_s=0, E=40, k=5, l=128, f=192), 150)
+
+
+def test_tiny_workload_train_update_train():
+    """The tiny fp32 workload: forward (b = 0), QB update, second forward."""
+    shape = wl.workload("tiny")
+    say("tiny workload")
+    W = wl.make_weights(shape)
+    layer = make_layer(shape, W, max_tokens=shape.T)
+    ref0, _ = _run(shape, shape.T, layer=layer, W=W, step=0)
+    layer.qb_update()
+    torch.cuda.synchronize()
+    b1 = o.qb_update(ref0["hist"], shape.T, shape.k, np.zeros(shape.E, F32))
+    np.testing.assert_array_equal(to_np(layer.get_bias()).view(np.uint32), b1.view(np.uint32))
+    _run(shape, shape.T, layer=layer, W=W, step=1)
+    layer.close()
+
+
+def test_replica_shape_ragged():
+    shape = wl.workload("replica")
+    say("replica shape T=1000")
+    _run(shape, 1000, bias=(np.random.default_rng(5).standard_normal(shape.E) * 0.02).astype(F32))
+
+
+def test_replica_full_size_sampled():
+    """The replica workload at full size (T=8192), as the benchmark runs it:
+    logits by tolerance, routing bit-exact from the GPU logits, outputs on
+    sampled tokens through the oracle's per-token path."""
+    shape = wl.workload("replica")
+    T = shape.T
+    say(f"replica full T={T}")
+    W = wl.make_weights(shape)
+    x = wl.make_x(shape)
+    layer = make_layer(shape, W, max_tokens=T)
+    r = layer.route_buffers(T)
+    out = to_np(layer.forward(x_on_gpu(x, layer), route=r))
+    torch.cuda.synchronize()
+    lg = to_np(r["logits"])
+    pick = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(0).integers(0, T, 61)]))
+    h = o.bf16_round(o.rmsnorm(x[pick], W["gamma"], shape.rms_eps))
+    assert rel_err(lg[pick], o.router_logits(h, W["W_r"])) <= LOGIT_TOL["bf16"]
+    from gpu_util import oracle_routing
+    ref = oracle_routing(lg, np.zeros(shape.E, F32), shape.k, shape.E, shape.B)
+    assert_routing_equal(r, ref, T)
+    np.testing.assert_array_equal(to_np(layer.state_views()["hist"]), ref["hist"])
+    want = o.forward_tokens(x[pick], W, ref["idx"][pick], ref["gates"][pick], dtype="bf16", eps=shape.rms_eps)
+    err = rel_err(out[pick], want)
+    say(f"  sampled out rel err {err:.3e}")
+    assert err <= OUT_TOL["bf16"]
+    layer.close()
