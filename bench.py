@@ -1,0 +1,257 @@
+"""Benchmark: Stable LatentMoE layer forward + QB update on one MI355X.
+
+One step = one training forward of the whole layer (RMSNorm, router, scores,
+QB histogram, biased top-k, gates, permutation, shared GLU, experts, combine,
+up-projection) over a batch of synthetic tokens, followed by the QB bias
+update.  Inputs and weights are resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload replica]
+
+Prints one JSON line: tokens/s over the K timed steps, the per-kernel times
+(HIP events on the launch stream, inside the timed region), the roofline
+position of the dominant kernel and of the expert GEMMs / routing kernels, and
+the CPU oracle's tokens/s on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+METRIC = "MoE-layer fwd tokens/sec on 1 MI355X + % bf16 MFMA peak + routing GB/s"
+
+
+def kernel_work(s, T: int) -> dict:
+    """Algorithmic work per launch: FLOPs of the GEMMs, bytes of the
+    memory-bound kernels (each operand read once, each result written once)."""
+    es = 2 if s.dtype == "bf16" else 4
+    Tk = T * s.k
+    nchunks = (T + 31) // 32
+    flops = {
+        "gemm_h": 2.0 * T * s.d * (s.E + 2 * s.f_s + s.l),
+        "gemm_out": 2.0 * T * s.d * (s.f_s + s.l),
+        "expert_up": 2.0 * Tk * s.l * 2 * s.f,
+        "expert_down": 2.0 * Tk * s.f * s.l,
+    }
+    bytes_ = {
+        "rmsnorm": 2.0 * T * s.d * es + 4 * s.d,
+        "topk": 4.0 * T * s.E + 8.0 * Tk + 4.0 * nchunks * s.E + 4 * s.E,
+        "hist": 4.0 * T * s.E,
+        "scan": 12.0 * nchunks * s.E + 16.0 * s.E,
+        "scatter": 4.0 * Tk + 8.0 * Tk + 8.0 * nchunks * s.E,
+        "combine": 1.0 * Tk * s.l * es + 8.0 * Tk + 1.0 * T * s.l * es,
+        "qb_quantile": 8.0 * 16 * s.E * s.B,
+        "qb_bias": 20.0 * s.E,
+    }
+    return {"flops": flops, "bytes": bytes_}
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_moe_layer_rmsnorm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("kernels", {}).get(workload, {}).get(kernel)
+
+
+def cpu_baseline(shape, W, x, seconds: float = 12.0) -> dict:
+    """The CPU oracle (as it is) on a bounded sample of the same workload:
+    full training forward + QB update on the first T_s tokens, repeated until
+    about `seconds` of CPU time."""
+    from oracle import moe_oracle as o
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    Ts = min(shape.T, 1024)
+    xs = x[:Ts]
+    b = np.zeros(shape.E, np.float32)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        r = o.forward(xs, W, b, k=shape.k, dtype=shape.dtype, eps=shape.rms_eps, B=shape.B)
+        o.qb_update(r["hist"], Ts, shape.k, b)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    return {"value": reps * Ts / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} x full training forward + QB update of the first {Ts} tokens of the {shape.name} "
+                      f"workload (numpy fp64, {el:.1f} s)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="replica")
+    ap.add_argument("--tokens", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step as a captured HIP graph (per-kernel times then come from an extra "
+                         "eager pass after the timed region)")
+    ap.add_argument("--no-profile", action="store_true", help="no per-kernel events in the timed region")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the layer is built and measured per GPU); --gpus {args.gpus} "
+              "is not supported", file=sys.stderr)
+        return 2
+
+    import torch
+    from sparse_moe_layer_rmsnorm_amd import binding as B
+    from sparse_moe_layer_rmsnorm_amd import workloads as wl
+    from sparse_moe_layer_rmsnorm_amd.layer import layer_from_shape
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    B.lib()  # fail loudly if the HIP library is missing
+    shape = wl.workload(args.workload, args.tokens)
+    T = shape.T
+    W = wl.make_weights(shape)
+    x_np = wl.make_x(shape)
+    c = wl.zipf_logit_offset(shape) if shape.name == "skew" else None
+    frozen = shape.qb_frozen
+    layer = layer_from_shape(shape, W, max_tokens=T, logit_offset=c, frozen=frozen)
+    if frozen:
+        layer.set_bias(wl.frozen_bias(shape))
+    x = torch.from_numpy(x_np).cuda().to(layer.tdtype)
+    out = torch.empty(T, shape.d, dtype=layer.tdtype, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        layer.forward(x, out=out)
+        layer.qb_update()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        run = g.replay
+    in_region = not (args.graph or args.no_profile)
+    n_launch = 16 * args.steps + 16
+    if in_region:
+        B.moe_profile_begin(layer.ctx, n_launch)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    if not in_region:
+        B.moe_profile_begin(layer.ctx, n_launch)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+    prof = B.moe_profile_end(layer.ctx)
+    ms_step = total_ms / args.steps
+    tok_s = T / (ms_step / 1e3)
+
+    work = kernel_work(shape, T)
+    peak_mm = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
+    kernels = {}
+    for name, (ms, n) in prof.items():
+        if n == 0:
+            continue
+        avg_us = ms / n * 1e3
+        k = {"avg_us": round(avg_us, 3), "launches": int(n)}
+        if name in work["flops"]:
+            tf = work["flops"][name] / (avg_us * 1e-6) / 1e12
+            k.update(tflops=round(tf, 1), mfma_frac=round(tf / peak_mm, 4))
+        elif name in work["bytes"]:
+            gbs = work["bytes"][name] / (avg_us * 1e-6) / 1e9
+            k.update(gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
+        kernels[name] = k
+    dom = max(kernels, key=lambda kn: kernels[kn]["avg_us"] * kernels[kn]["launches"] / args.steps)
+    dk = kernels[dom]
+    if "tflops" in dk:
+        traffic = traffic_for(dom, shape.name)
+        roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": peak_mm, "unit": "TFLOP/s",
+                    "frac": round(dk["tflops"] / peak_mm, 4), "traffic": traffic, "kernel": dom,
+                    "algorithmic": f"{work['flops'][dom]:.4g} FLOP per launch"}
+    else:
+        traffic = traffic_for(dom, shape.name)
+        roofline = {"bound": "hbm", "achieved": dk["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(dk["gbs"] / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom,
+                    "algorithmic": f"{work['bytes'][dom]:.4g} bytes per launch"}
+    # expert GEMMs together, and routing + permutation + combine together
+    ex_us = sum(kernels[n]["avg_us"] for n in ("expert_up", "expert_down") if n in kernels)
+    ex_tf = (work["flops"]["expert_up"] + work["flops"]["expert_down"]) / (ex_us * 1e-6) / 1e12
+    rt_names = [n for n in ("topk", "hist", "scan", "scatter", "combine") if n in kernels]
+    rt_us = sum(kernels[n]["avg_us"] for n in rt_names)
+    rt_bytes = sum(work["bytes"].get(n, 0.0) for n in rt_names)
+    layer_flops = sum(work["flops"].values())
+
+    res = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic: seeded PCG64, x ~ N(0,1), weights ~ N(0,1/fan_in), rounded to bf16; random init",
+        "timing": "graph replay" if args.graph else ("eager, no events" if args.no_profile else
+                                                     "eager, per-kernel events in the timed region"),
+        "config": {"workload": f"{shape.name}: T={T} tokens, d={shape.d}, l={shape.l}, E={shape.E}, k={shape.k}, "
+                               f"f={shape.f}, f_s={shape.f_s}, B={shape.B}, QB {'frozen' if frozen else 'train'}",
+                   "global_batch": T, "step": "training forward + qb_update"},
+        "roofline": roofline,
+        "layer_mfma_frac": round(layer_flops / (ms_step * 1e-3) / 1e12 / peak_mm, 4),
+        "expert_gemm": {"tflops": round(ex_tf, 1), "mfma_frac": round(ex_tf / peak_mm, 4)},
+        "routing_permute_combine": {"gbs": round(rt_bytes / (rt_us * 1e-6) / 1e9, 1),
+                                    "hbm_frac": round(rt_bytes / (rt_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                                    "us": round(rt_us, 2)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(shape, dict(W, c=c) if c is not None else W, x_np, args.cpu_seconds)
+    layer.close()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -72,7 +72,7 @@ typedef enum moe_qb_mode { MOE_QB_TRAIN = 0, MOE_QB_FROZEN = 1 } moe_qb_mode;
 /*
  * Layer sizes.  d, l, f must be multiples of 64 and f_s a multiple of 64 or 0
  * (0 = no shared expert; several shared experts of hidden f are one of hidden
- * n*f).  1 <= E <= 1024, 1 <= k <= min(E, 32), 2 <= qb_bins <= 512.
+ * n*f).  1 <= E <= 1024, 1 <= k <= min(E, 32), 2 <= qb_bins <= 256.
  * max_tokens bounds T for every call (1 <= max_tokens, max_tokens*k < 2^31).
  * rms_eps > 0.  routed_scale multiplies every gate (1 = plain renormalised).
  */
@@ -121,14 +121,16 @@ typedef struct moe_state_layout {
   size_t bias;  /* [E] fp32 router bias                                   */
   size_t count; /* uint64 tokens accumulated since the last qb_update     */
   size_t q;     /* [E] fp64 quantiles of the last qb_update               */
-  size_t hist;  /* [E, qb_bins] uint32 score histogram                    */
+  size_t hist;  /* [hist_slices, E, qb_bins] uint32 score histogram; the
+                   histogram is the sum over the slices                   */
+  size_t hist_slices;
   size_t total;
 } moe_state_layout;
 
 /* Byte offsets, inside the workspace, of the intermediates of one call. */
 typedef struct moe_ws_layout {
-  size_t h, logits, idx, gates, chunk_counts, counts, offsets, tile_offsets, perm_src, inv;
-  size_t hist_partial, G, z, H, Y, y_lat;
+  size_t h, logits, idx, gates, bitmap, cbase, sbase, counts, offsets, tile_offsets, perm_src, inv;
+  size_t G, z, H, Y, y_lat;
   size_t total;
 } moe_ws_layout;
 
@@ -196,9 +198,9 @@ const char* moe_last_error(void);
  * profiling stops.  Host-side event objects only; no device memory.
  */
 enum {
-  MOE_K_RMSNORM = 0, MOE_K_GEMM_H, MOE_K_TOPK, MOE_K_HIST, MOE_K_HIST_REDUCE, MOE_K_SCAN,
-  MOE_K_OFFSETS, MOE_K_SCATTER, MOE_K_EXPERT_UP, MOE_K_EXPERT_DOWN, MOE_K_COMBINE, MOE_K_GEMM_OUT,
-  MOE_K_QB_QUANTILE, MOE_K_QB_BIAS, MOE_NUM_KERNELS
+  MOE_K_RMSNORM = 0, MOE_K_GEMM_H, MOE_K_TOPK, MOE_K_HIST, MOE_K_SCAN, MOE_K_SCATTER,
+  MOE_K_EXPERT_UP, MOE_K_EXPERT_DOWN, MOE_K_COMBINE, MOE_K_GEMM_OUT, MOE_K_QB_QUANTILE,
+  MOE_K_QB_BIAS, MOE_NUM_KERNELS
 };
 const char* moe_kernel_name(int id);
 moe_status moe_profile_begin(moe_ctx* ctx, int max_launches);

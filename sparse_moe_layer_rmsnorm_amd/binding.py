@@ -19,8 +19,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_STATE, MOE_ERR_HIP = range(7)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_QB_TRAIN, MOE_QB_FROZEN = 0, 1
-KERNELS = ["rmsnorm", "gemm_h", "topk", "hist", "hist_reduce", "scan", "offsets", "scatter", "expert_up",
-           "expert_down", "combine", "gemm_out", "qb_quantile", "qb_bias"]
+KERNELS = ["rmsnorm", "gemm_h", "topk", "hist", "scan", "scatter", "expert_up", "expert_down", "combine",
+           "gemm_out", "qb_quantile", "qb_bias"]
 MOE_NUM_KERNELS = len(KERNELS)
 
 
@@ -40,13 +40,13 @@ class moe_route_out(ctypes.Structure):
 
 
 class moe_state_layout(ctypes.Structure):
-    _fields_ = [(n, c_size_t) for n in ("bias", "count", "q", "hist", "total")]
+    _fields_ = [(n, c_size_t) for n in ("bias", "count", "q", "hist", "hist_slices", "total")]
 
 
 class moe_ws_layout(ctypes.Structure):
-    _fields_ = [(n, c_size_t) for n in ("h", "logits", "idx", "gates", "chunk_counts", "counts", "offsets",
-                                        "tile_offsets", "perm_src", "inv", "hist_partial", "G", "z", "H", "Y",
-                                        "y_lat", "total")]
+    _fields_ = [(n, c_size_t) for n in ("h", "logits", "idx", "gates", "bitmap", "cbase", "sbase", "counts",
+                                        "offsets", "tile_offsets", "perm_src", "inv", "G", "z", "H", "Y", "y_lat",
+                                        "total")]
 
 
 _lib = None

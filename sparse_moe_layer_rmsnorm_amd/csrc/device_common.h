@@ -76,13 +76,40 @@ MOE_DEV float wave_sum(float v) {
   return v;
 }
 
+// DPP row shift of a 64-bit value; lanes whose source falls outside their
+// row of 16 keep their own value.
+template <int CTRL>
+MOE_DEV unsigned long long dpp_u64(unsigned long long v) {
+  const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF,
+                                             false);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+MOE_DEV unsigned long long readlane_u64(unsigned long long v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Maximum over the 64 lanes, returned to every lane (wave-uniform).  Row
+// shifts 1, 2, 4, 8 leave each row's maximum in its lane 15; the four row
+// maxima are then read out as scalars.  All lanes must be active.
 MOE_DEV unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    unsigned long long w = __shfl_xor(v, o, 64);
-    v = w > v ? w : v;
-  }
-  return v;
+  unsigned long long w;
+  w = dpp_u64<0x111>(v);  // row_shr:1
+  v = w > v ? w : v;
+  w = dpp_u64<0x112>(v);  // row_shr:2
+  v = w > v ? w : v;
+  w = dpp_u64<0x114>(v);  // row_shr:4
+  v = w > v ? w : v;
+  w = dpp_u64<0x118>(v);  // row_shr:8
+  v = w > v ? w : v;
+  unsigned long long a = readlane_u64(v, 15), b = readlane_u64(v, 31);
+  unsigned long long c = readlane_u64(v, 47), d = readlane_u64(v, 63);
+  a = a > b ? a : b;
+  c = c > d ? c : d;
+  return a > c ? a : c;
 }
 
 // Blocks are handed to the 8 XCDs of the chip round-robin.  Map the

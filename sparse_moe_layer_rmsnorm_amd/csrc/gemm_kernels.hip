@@ -54,56 +54,80 @@ MOE_DEV void mfma_chunk(f32x4_t& acc, const uint4& w, const uint4& a) {
   }
 }
 
-MOE_DEV uint4 ld16(const char* p) { return p ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0); }
+// LDS address (32-bit) of a pointer into a __shared__ array.
+MOE_DEV uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
 
-// Row pointers of one K part: each thread loads rows tid/8 + 32 i of the A
-// and B tiles, 16-byte chunk tid%8 of each stage.  A null pointer is a row
-// outside the problem (loaded as zeros).
-template <int AR, int BR>
-struct Rows {
-  const char* a[AR];
-  const char* b[BR];
+// One 16-byte-per-lane global -> LDS DMA load (global_load_lds_dwordx4): lane
+// i of the wavefront writes LDS bytes [lds + 16 i, lds + 16 i + 16).  `lds`
+// must be wave-uniform.  Issued from inline asm so that the compiler does not
+// add a wait for all outstanding loads before every LDS read; the loop below
+// waits for its own loads explicitly.
+MOE_DEV void lds_dma16(const char* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+
+// Stage filling: a stage is BM + BN rows of 128 bytes (A rows, then B rows),
+// written by 1 KB DMA slots; thread (wave w, lane) fills slots i*4 + w, i < L.
+// The tile row and the logical 16-byte K chunk that a lane's piece of slot i
+// holds (the LDS chunk position is lane%8, XOR-swizzled by row):
+MOE_DEV int slot_row(int i, int wave, int lane) { return (i * 4 + wave) * 8 + (lane >> 3); }
+MOE_DEV int slot_chunk(int row, int lane) { return (lane & 7) ^ ((row & 7) ^ ((row >> 3) & 1)); }
+
+// Global source of each of this thread's slot pieces at k = 0, per K part;
+// the source advances 128 bytes per stage.  PARTS K parts are consumed one
+// after the other (kt[p] stages each).
+template <int L, int PARTS>
+struct Src {
+  const char* p[PARTS][L];
+  int kt[PARTS];
 };
 
 template <int BM, int BN, bool BF16>
 struct Core {
   static constexpr int WTM = BM / 2, WTN = BN / 2;
   static constexpr int MI = WTM / 16, NI = WTN / 16;
-  static constexpr int AR = BM / 32, BR = BN / 32;
   static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int LDS = 2 * STAGE;
+  static constexpr int L = STAGE / 1024 / 4;  // DMA slots per thread per stage
+  static_assert(STAGE % 4096 == 0, "stage must split into 1 KB slots over 4 wavefronts");
 
-  // Run `kt_n` stages of one K part, accumulating into acc.  Both row sets
-  // advance 128 bytes per stage.
-  MOE_DEV static void run(const Rows<AR, BR>& R, int kt_n, f32x4_t (&acc)[MI][NI], char* smem) {
+  // Accumulate all stages into acc.  Two LDS buffers: the loads of stage s+1
+  // are issued right after the barrier that ends stage s-1's reads, and run
+  // while stage s feeds the MFMAs.
+  template <int PARTS>
+  MOE_DEV static void run(const Src<L, PARTS>& S, f32x4_t (&acc)[MI][NI], char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int lrow = tid >> 3, lchunk = tid & 7;
-    uint4 ra[AR], rb[BR];
-    auto gload = [&](int kt) {
-      const int off = kt * kRowBytes + lchunk * 16;
+    int KT = S.kt[0];
+    if constexpr (PARTS > 1) KT += S.kt[1];
+    if (KT <= 0) return;
+    const uint32_t lds0 = lds_addr(smem) + wave * 1024;
+    auto issue = [&](int s, int buf) {
+      bool second = false;
+      int ks = s;
+      if constexpr (PARTS > 1) {
+        second = s >= S.kt[0];
+        ks = second ? s - S.kt[0] : s;
+      }
+      const uint32_t base = lds0 + buf * STAGE;
 #pragma unroll
-      for (int i = 0; i < AR; ++i) ra[i] = ld16(R.a[i] ? R.a[i] + off : nullptr);
-#pragma unroll
-      for (int i = 0; i < BR; ++i) rb[i] = ld16(R.b[i] ? R.b[i] + off : nullptr);
+      for (int i = 0; i < L; ++i) {
+        const char* g = S.p[0][i];
+        if constexpr (PARTS > 1) g = second ? S.p[1][i] : g;
+        lds_dma16(g + ks * kRowBytes, __builtin_amdgcn_readfirstlane(base + i * 4096));
+      }
     };
-    auto sstore = [&](char* st) {
+    issue(0, 0);
+    for (int s = 0; s < KT; ++s) {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (s + 1 < KT) issue(s + 1, (s + 1) & 1);
+      const char* cur = smem + (s & 1) * STAGE;
 #pragma unroll
-      for (int i = 0; i < AR; ++i) *reinterpret_cast<uint4*>(st + lds_off(lrow + 32 * i, lchunk)) = ra[i];
-#pragma unroll
-      for (int i = 0; i < BR; ++i) *reinterpret_cast<uint4*>(st + A_BYTES + lds_off(lrow + 32 * i, lchunk)) = rb[i];
-    };
-    if (kt_n <= 0) return;
-    gload(0);
-    sstore(smem);
-    __syncthreads();
-    for (int kt = 0; kt < kt_n; ++kt) {
-      char* cur = smem + (kt & 1) * STAGE;
-      if (kt + 1 < kt_n) gload(kt + 1);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int ch = ks * 4 + (lane >> 4);
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ch = kk * 4 + (lane >> 4);
         uint4 af[MI], wf[NI];
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
@@ -116,8 +140,6 @@ struct Core {
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni) mfma_chunk<BF16>(acc[mi][ni], wf[ni], af[mi]);
       }
-      if (kt + 1 < kt_n) sstore(smem + ((kt + 1) & 1) * STAGE);
-      __syncthreads();
     }
   }
 
@@ -210,7 +232,7 @@ constexpr int kGroupM = 8;
 template <int BM, int BN, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_gemm_dense(const DenseArgs args) {
   using C = Core<BM, BN, BF16>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   const int nblocks = args.m_tiles * args.total_ntiles;
   const int L = xcd_remap(blockIdx.x, nblocks);
   // groups of kGroupM m-tiles, m fastest inside a group
@@ -234,36 +256,39 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const DenseArgs args) {
   }
   const int m0 = mt * BM;
   const int rows_valid = min(BM, args.M - m0);
-  const int tid = threadIdx.x, lrow = tid >> 3;
-  f32x4_t acc[C::MI][C::NI];
-  C::zero(acc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  Src<C::L, 2> src;
 #pragma unroll
   for (int part = 0; part < 2; ++part) {
-    if (args.kt[part] == 0) continue;
-    Rows<C::AR, C::BR> R;
+    src.kt[part] = args.kt[part];
 #pragma unroll
-    for (int i = 0; i < C::AR; ++i) {
-      const int r = lrow + 32 * i;
-      R.a[i] = r < rows_valid ? args.A[part] + (size_t)(m0 + r) * args.lda_bytes[part] : nullptr;
-    }
-#pragma unroll
-    for (int i = 0; i < C::BR; ++i) {
-      const int c = lrow + 32 * i;
-      int wrow;
-      const char* base;
-      if (S.kind == EPI_GLU) {
-        const int half = (c & 31) >= 16;
-        wrow = nt * (BN / 2) + (c >> 5) * 16 + (c & 15);
-        base = half ? S.Bu[part] : S.B[part];
-        R.b[i] = wrow < S.N ? base + (size_t)wrow * args.ldb_bytes[part] : nullptr;
-      } else {
-        wrow = nt * BN + c;
-        base = S.B[part];
-        R.b[i] = wrow < S.N ? base + (size_t)wrow * args.ldb_bytes[part] : nullptr;
+    for (int i = 0; i < C::L; ++i) {
+      const int row = slot_row(i, wave, lane);
+      const int chunk = slot_chunk(row, lane);
+      const char* p;
+      if (row < BM) {  // A row (rows past the end read row m0: their results are not stored)
+        const int r = row < rows_valid ? row : 0;
+        p = args.A[part] + (size_t)(m0 + r) * args.lda_bytes[part];
+      } else {         // weight row of output column c (columns past N read row 0)
+        const int c = row - BM;
+        int wrow;
+        const char* base;
+        if (S.kind == EPI_GLU) {
+          wrow = nt * (BN / 2) + (c >> 5) * 16 + (c & 15);
+          base = ((c & 31) >= 16) ? S.Bu[part] : S.B[part];
+        } else {
+          wrow = nt * BN + c;
+          base = S.B[part];
+        }
+        if (wrow >= S.N) wrow = 0;
+        p = base + (size_t)wrow * args.ldb_bytes[part];
       }
+      src.p[part][i] = args.kt[part] > 0 ? p + chunk * 16 : nullptr;
     }
-    C::run(R, args.kt[part], acc, smem);
   }
+  f32x4_t acc[C::MI][C::NI];
+  C::zero(acc);
+  C::template run<2>(src, acc, smem);
   if (S.kind == EPI_F32)
     C::template epilogue<EPI_F32>(acc, rows_valid, nt * BN, S.N, S.out, S.ldo, (size_t)m0, S.col_off);
   else if (S.kind == EPI_GLU)
@@ -310,7 +335,7 @@ template <int BN, bool BF16, int KIND>
 __global__ __launch_bounds__(kThreads) void k_gemm_expert(const ExpertArgs args) {
   constexpr int BM = kExpertBM;
   using C = Core<BM, BN, BF16>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   const int total = args.tile_offsets[args.E] * args.NT;
   if ((int)blockIdx.x >= total) return;
   const int L = xcd_remap(blockIdx.x, total);
@@ -319,36 +344,40 @@ __global__ __launch_bounds__(kThreads) void k_gemm_expert(const ExpertArgs args)
   const int mt = gmt - args.tile_offsets[e];
   const int row0 = args.offsets[e] + mt * BM;
   const int rows_valid = min(BM, args.offsets[e + 1] - row0);
-  const int tid = threadIdx.x, lrow = tid >> 3;
-  Rows<C::AR, C::BR> R;
-#pragma unroll
-  for (int i = 0; i < C::AR; ++i) {
-    const int r = lrow + 32 * i;
-    if (r < rows_valid) {
-      int src = args.perm_src ? args.perm_src[row0 + r] : row0 + r;
-      src = (unsigned)src < (unsigned)args.src_rows ? src : 0;  // never taken for a consistent permutation
-      R.a[i] = args.A + (size_t)src * args.lda_bytes;
-    } else {
-      R.a[i] = nullptr;
-    }
-  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const char* Wg = args.W + (size_t)e * args.w_expert_bytes;
   const char* Wu = args.Wu ? args.Wu + (size_t)e * args.w_expert_bytes : nullptr;
+  Src<C::L, 1> src;
+  src.kt[0] = args.kt;
 #pragma unroll
-  for (int i = 0; i < C::BR; ++i) {
-    const int c = lrow + 32 * i;
-    if (KIND == EPI_GLU) {
-      const int wrow = nt * (BN / 2) + (c >> 5) * 16 + (c & 15);
-      const char* base = ((c & 31) >= 16) ? Wu : Wg;
-      R.b[i] = wrow < args.N ? base + (size_t)wrow * args.ldb_bytes : nullptr;
+  for (int i = 0; i < C::L; ++i) {
+    const int row = slot_row(i, wave, lane);
+    const int chunk = slot_chunk(row, lane);
+    const char* p;
+    if (row < BM) {  // rows past the expert's end read its first row (results not stored)
+      const int r = row0 + (row < rows_valid ? row : 0);
+      int srow = args.perm_src ? args.perm_src[r] : r;
+      srow = (unsigned)srow < (unsigned)args.src_rows ? srow : 0;  // never taken for a consistent permutation
+      p = args.A + (size_t)srow * args.lda_bytes;
     } else {
-      const int wrow = nt * BN + c;
-      R.b[i] = wrow < args.N ? Wg + (size_t)wrow * args.ldb_bytes : nullptr;
+      const int c = row - BM;
+      int wrow;
+      const char* base;
+      if (KIND == EPI_GLU) {
+        wrow = nt * (BN / 2) + (c >> 5) * 16 + (c & 15);
+        base = ((c & 31) >= 16) ? Wu : Wg;
+      } else {
+        wrow = nt * BN + c;
+        base = Wg;
+      }
+      if (wrow >= args.N) wrow = 0;
+      p = base + (size_t)wrow * args.ldb_bytes;
     }
+    src.p[0][i] = p + chunk * 16;
   }
   f32x4_t acc[C::MI][C::NI];
   C::zero(acc);
-  C::run(R, args.kt, acc, smem);
+  C::template run<1>(src, acc, smem);
   C::template epilogue<KIND>(acc, rows_valid, nt * BN, args.N, args.out, args.ldo, (size_t)row0, nullptr);
 }
 

@@ -5,11 +5,15 @@
 
 namespace moe {
 
-// Tokens per routing chunk: one wavefront's worth.  Top-k counts experts per
-// chunk and the scatter ranks tokens inside a chunk with 64-bit lane masks.
-constexpr int kChunk = 64;
+// Tokens per routing chunk: top-k records, per chunk and expert, a 32-bit
+// mask of the chunk's tokens that picked the expert.
+constexpr int kChunk = 32;
+// Chunks per super-chunk of the two-level prefix sum.
+constexpr int kSuper = 16;
+// Token slices of the QB histogram kept in the state ([slice][E][B]).
+constexpr int kHistSlices = 16;
 // Rows per tile of the grouped expert GEMMs (also the granularity of the
-// per-expert tile offsets computed by the offsets kernel).
+// per-expert tile offsets computed by the scan).
 constexpr int kExpertBM = 128;
 // Experts per block of the histogram kernel.
 constexpr int kHistExperts = 64;
@@ -20,20 +24,16 @@ struct Dims {
   float eps, routed_scale;
 };
 
-int hist_token_slices(int T, int E);
-
 hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s);
-hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, int T, int32_t* idx,
-                       float* gates, int32_t* chunk_counts, hipStream_t s);
-hipError_t launch_hist(const Dims& D, const float* logits, int T, uint32_t* partial, uint32_t* hist,
-                       unsigned long long* count, hipStream_t s);
-hipError_t launch_hist_reduce(const Dims& D, const uint32_t* partial, int nslices, int T, uint32_t* hist,
-                              unsigned long long* count, hipStream_t s);
-hipError_t launch_scan(const Dims& D, int32_t* chunk_counts, int nchunks, int32_t* counts, hipStream_t s);
-hipError_t launch_offsets(const Dims& D, const int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
-                          hipStream_t s);
-hipError_t launch_scatter(const Dims& D, const int32_t* idx, const int32_t* offsets, const int32_t* chunk_base,
-                          int T, int32_t* perm_src, int32_t* inv, hipStream_t s);
+hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, int T, int32_t* idx, float* gates,
+                       uint32_t* bitmap, hipStream_t s);
+hipError_t launch_hist(const Dims& D, const float* logits, int T, uint32_t* hist, unsigned long long* count,
+                       hipStream_t s);
+// Two launches: per-super-chunk prefix, then the global prefix + offsets.
+hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cbase, int32_t* sbase, int32_t* counts,
+                       int32_t* offsets, int32_t* tile_offsets, hipStream_t s);
+hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* cbase,
+                          const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s);
 hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, const int32_t* inv, int T,
                           void* y_lat, hipStream_t s);
 hipError_t launch_qb_quantile(const Dims& D, uint32_t* hist, const unsigned long long* count, double* q,

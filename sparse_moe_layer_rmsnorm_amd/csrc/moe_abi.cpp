@@ -76,7 +76,8 @@ void state_layout(const moe_config* c, moe_state_layout* L) {
   L->q = o;
   o = up(o + (size_t)c->E * 8);
   L->hist = o;
-  o = up(o + (size_t)c->E * c->qb_bins * 4);
+  L->hist_slices = kHistSlices;
+  o = up(o + (size_t)kHistSlices * c->E * c->qb_bins * 4);
   L->total = o;
 }
 
@@ -84,7 +85,7 @@ void ws_layout(const moe_config* c, int64_t T, moe_ws_layout* L) {
   const size_t es = c->dtype == MOE_BF16 ? 2 : 4;
   const size_t t = (size_t)T, E = (size_t)c->E, k = (size_t)c->k;
   const size_t nchunks = (t + kChunk - 1) / kChunk;
-  const size_t nslices = T > 0 ? (size_t)hist_token_slices((int)T, c->E) : 1;
+  const size_t nsuper = (nchunks + kSuper - 1) / kSuper;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -95,13 +96,14 @@ void ws_layout(const moe_config* c, int64_t T, moe_ws_layout* L) {
   L->logits = take(t * E * 4);
   L->idx = take(t * k * 4);
   L->gates = take(t * k * 4);
-  L->chunk_counts = take(nchunks * E * 4);
+  L->bitmap = take(nchunks * E * 4);
+  L->cbase = take(nchunks * E * 4);
+  L->sbase = take(nsuper * E * 4);
   L->counts = take(E * 4);
   L->offsets = take((E + 1) * 4);
   L->tile_offsets = take((E + 1) * 4);
   L->perm_src = take(t * k * 4);
   L->inv = take(t * k * 4);
-  L->hist_partial = take(nslices > 1 ? nslices * E * c->qb_bins * 4 : 0);
   L->G = take(t * c->f_s * es);
   L->z = take(t * c->l * es);
   L->H = take(t * k * c->f * es);
@@ -152,9 +154,9 @@ moe_status run(moe_ctx* c, int kid, hipStream_t s, F&& f) {
 
 struct RoutePtrs {
   float* logits;
-  int32_t *idx, *chunk_counts, *counts, *offsets, *tile_offsets, *perm_src, *inv;
+  int32_t *idx, *cbase, *sbase, *counts, *offsets, *tile_offsets, *perm_src, *inv;
+  uint32_t* bitmap;
   float* gates;
-  uint32_t* hist_partial;
 };
 
 RoutePtrs route_ptrs(const moe_ws_layout& L, char* ws, const moe_route_out* r) {
@@ -166,9 +168,10 @@ RoutePtrs route_ptrs(const moe_ws_layout& L, char* ws, const moe_route_out* r) {
   p.offsets = (r && r->offsets) ? r->offsets : reinterpret_cast<int32_t*>(ws + L.offsets);
   p.perm_src = (r && r->perm_src) ? r->perm_src : reinterpret_cast<int32_t*>(ws + L.perm_src);
   p.inv = (r && r->inv) ? r->inv : reinterpret_cast<int32_t*>(ws + L.inv);
-  p.chunk_counts = reinterpret_cast<int32_t*>(ws + L.chunk_counts);
+  p.bitmap = reinterpret_cast<uint32_t*>(ws + L.bitmap);
+  p.cbase = reinterpret_cast<int32_t*>(ws + L.cbase);
+  p.sbase = reinterpret_cast<int32_t*>(ws + L.sbase);
   p.tile_offsets = reinterpret_cast<int32_t*>(ws + L.tile_offsets);
-  p.hist_partial = reinterpret_cast<uint32_t*>(ws + L.hist_partial);
   return p;
 }
 
@@ -186,24 +189,20 @@ moe_status check_call(moe_ctx* ctx, int64_t T, void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
-// Steps after the logits: scores, QB histogram, top-k + gates + chunk counts,
-// per-expert scan, offsets, stable scatter.
+// Steps after the logits: scores, QB histogram, top-k + gates + selection
+// masks, two-level prefix sums with offsets, stable scatter.
 moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s) {
   const Dims& D = ctx->D;
   const float* bias = reinterpret_cast<const float*>(ctx->state + ctx->sl.bias);
-  MOE_RUN(MOE_K_TOPK, launch_topk(D, p.logits, bias, T, p.idx, p.gates, p.chunk_counts, s));
+  MOE_RUN(MOE_K_TOPK, launch_topk(D, p.logits, bias, T, p.idx, p.gates, p.bitmap, s));
   if (ctx->cfg.qb_mode == MOE_QB_TRAIN) {
     uint32_t* hist = reinterpret_cast<uint32_t*>(ctx->state + ctx->sl.hist);
     unsigned long long* cnt = reinterpret_cast<unsigned long long*>(ctx->state + ctx->sl.count);
-    const int ns = hist_token_slices(T, D.E);
-    MOE_RUN(MOE_K_HIST, launch_hist(D, p.logits, T, p.hist_partial, hist, cnt, s));
-    if (ns > 1) MOE_RUN(MOE_K_HIST_REDUCE, launch_hist_reduce(D, p.hist_partial, ns, T, hist, cnt, s));
+    MOE_RUN(MOE_K_HIST, launch_hist(D, p.logits, T, hist, cnt, s));
     ctx->pending_tokens += (uint64_t)T;
   }
-  const int nchunks = (T + kChunk - 1) / kChunk;
-  MOE_RUN(MOE_K_SCAN, launch_scan(D, p.chunk_counts, nchunks, p.counts, s));
-  MOE_RUN(MOE_K_OFFSETS, launch_offsets(D, p.counts, p.offsets, p.tile_offsets, s));
-  MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.offsets, p.chunk_counts, T, p.perm_src, p.inv, s));
+  MOE_RUN(MOE_K_SCAN, launch_scan(D, p.bitmap, T, p.cbase, p.sbase, p.counts, p.offsets, p.tile_offsets, s));
+  MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.bitmap, p.cbase, p.sbase, T, p.perm_src, p.inv, s));
   return MOE_OK;
 }
 
@@ -376,9 +375,9 @@ const char* moe_status_string(moe_status s) {
 const char* moe_last_error(void) { return g_err; }
 
 const char* moe_kernel_name(int id) {
-  static const char* names[MOE_NUM_KERNELS] = {
-      "rmsnorm",  "gemm_h",    "topk",        "hist",        "hist_reduce", "scan",        "offsets",
-      "scatter",  "expert_up", "expert_down", "combine",     "gemm_out",    "qb_quantile", "qb_bias"};
+  static const char* names[MOE_NUM_KERNELS] = {"rmsnorm",     "gemm_h",  "topk",     "hist",
+                                                "scan",        "scatter", "expert_up", "expert_down",
+                                                "combine",     "gemm_out", "qb_quantile", "qb_bias"};
   return (id >= 0 && id < MOE_NUM_KERNELS) ? names[id] : "unknown";
 }
 

@@ -76,19 +76,21 @@ hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void
 }
 
 // -------------------------------------------------- scores + top-k ----
-// One block per chunk of 64 tokens, one wavefront per token at a time.  Lane
-// i holds experts i, i+64, ... .  Each of the k rounds takes the wave-wide
-// maximum of the 64-bit key (order key of v = s + b, then the complement of
-// the expert index), so equal v go to the lower index.  Gates are the chosen
-// unbiased scores over their fp32 sum in slot order.  The chunk's per-expert
-// counts go to chunk_counts[chunk][E] (LDS integer atomics: order-free).
+// One block per chunk of kChunk = 32 tokens, 8 wavefronts, one token per
+// wavefront at a time (the next token's logits are loaded while the current
+// one is ranked).  Lane i holds experts i, i+64, ... .  Each of the k rounds
+// takes the wave-wide maximum (DPP, no LDS) of the 64-bit key (order key of
+// v = s + b, then the complement of the expert index), so equal v go to the
+// lower index.  Gates are the chosen unbiased scores over their fp32 sum in
+// slot order.  The chunk's selections leave as one 32-bit token mask per
+// expert: bitmap[chunk][e] bit t%32 is set iff token t picked e.
 template <int CPL>
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
+__global__ __launch_bounds__(512) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
                                               int T, int E, int k, float scale, int32_t* __restrict__ idx,
-                                              float* __restrict__ gates, int32_t* __restrict__ chunk_counts) {
+                                              float* __restrict__ gates, uint32_t* __restrict__ bitmap) {
 #pragma clang fp contract(off)
-  __shared__ int cnt[1024];
-  for (int i = threadIdx.x; i < E; i += 256) cnt[i] = 0;
+  __shared__ uint32_t mask[1024];
+  for (int i = threadIdx.x; i < E; i += 512) mask[i] = 0u;
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float b[CPL];
@@ -97,18 +99,29 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     const int e = lane + 64 * c;
     b[c] = e < E ? bias[e] : 0.f;
   }
-  const int t0 = blockIdx.x * kChunk;
-  for (int tt = wave; tt < kChunk; tt += 4) {
-    const int t = t0 + tt;
-    if (t >= T) break;
+  float nxt[CPL];
+  auto load = [&](int t) {
     const float* lr = logits + (size_t)t * E;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int e = lane + 64 * c;
+      nxt[c] = e < E ? lr[e] : 0.f;
+    }
+  };
+  int t = blockIdx.x * kChunk + wave;
+  if (t < T) load(t);
+  for (int it = 0; it < kChunk / 8; ++it, t += 8) {
+    if (t >= T) break;  // uniform across the wavefront
     float s[CPL];
     unsigned long long key[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) s[c] = nxt[c];
+    if (it + 1 < kChunk / 8 && t + 8 < T) load(t + 8);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int e = lane + 64 * c;
       if (e < E) {
-        s[c] = router_sigmoid(lr[e]);
+        s[c] = router_sigmoid(s[c]);
         const float v = s[c] + b[c];
         key[c] = ((unsigned long long)float_order_key(v) << 32) | (0xFFFFFFFFu - (uint32_t)e);
       } else {
@@ -119,21 +132,21 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     float S = 0.f, my_s = 0.f;
     int my_e = 0;
     for (int j = 0; j < k; ++j) {
-      unsigned long long best = 0ull;
+      unsigned long long best = key[0];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) best = key[c] > best ? key[c] : best;
+      for (int c = 1; c < CPL; ++c) best = key[c] > best ? key[c] : best;
       best = wave_max_u64(best);
       const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-      const int owner = e & 63;
-      float se = 0.f;
+      const int owner = e & 63, oc = e >> 6;
+      float sv = 0.f;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        if (lane == owner && c == (e >> 6)) {
-          se = s[c];
-          key[c] = 0ull;
+        if (c == oc) {
+          sv = s[c];
+          if (lane == owner) key[c] = 0ull;
         }
       }
-      se = __shfl(se, owner, 64);
+      const float se = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), owner));
       S = (j == 0) ? se : S + se;
       if (lane == j) {
         my_s = se;
@@ -144,20 +157,20 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
       const float g = (my_s / S) * scale;
       idx[(size_t)t * k + lane] = my_e;
       gates[(size_t)t * k + lane] = g;
-      atomicAdd(&cnt[my_e], 1);
+      atomicOr(&mask[my_e], 1u << (t & 31));
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < E; i += 256) chunk_counts[(size_t)blockIdx.x * E + i] = cnt[i];
+  for (int i = threadIdx.x; i < E; i += 512) bitmap[(size_t)blockIdx.x * E + i] = mask[i];
 }
 
 hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, int T, int32_t* idx, float* gates,
-                       int32_t* chunk_counts, hipStream_t s) {
+                       uint32_t* bitmap, hipStream_t s) {
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int cpl = (D.E + 63) / 64;
-  dim3 grid(nchunks), block(256);
+  dim3 grid(nchunks), block(512);
 #define MOE_TOPK(C) \
-  hipLaunchKernelGGL(k_topk<C>, grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, chunk_counts)
+  hipLaunchKernelGGL(k_topk<C>, grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, bitmap)
   if (cpl <= 1) MOE_TOPK(1);
   else if (cpl <= 2) MOE_TOPK(2);
   else if (cpl <= 4) MOE_TOPK(4);
@@ -168,23 +181,16 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
 }
 
 // ---------------------------------------------------------- QB histogram ----
-// Block (expert slice of 64, token slice): LDS histogram [64][B] with integer
-// atomics (order-free), then either written to its own partial slot or, when
-// there is only one token slice, added to the state histogram directly (each
-// block owns its experts' rows).
-int hist_token_slices(int T, int E) {
-  const int es = (E + kHistExperts - 1) / kHistExperts;
-  int want = (256 + es - 1) / es;               // about one block per CU
-  int by_tokens = (T + 255) / 256;              // at least 256 tokens per slice
-  int n = want < by_tokens ? want : by_tokens;
-  return n < 1 ? 1 : n;
-}
-
+// The state keeps the histogram as kHistSlices token slices [slice][E][B].
+// Block (64-expert group, slice) counts its tokens' score bins in LDS with
+// integer atomics (order-free) and adds them to its own rows of its own slice
+// (no other block of the launch writes them), so no reduction pass is needed
+// per forward; qb_update sums the slices.
 __global__ __launch_bounds__(1024) void k_hist(const float* __restrict__ logits, int T, int E, int B, int tps,
-                                               uint32_t* __restrict__ partial, uint32_t* __restrict__ hist,
-                                               unsigned long long* __restrict__ count) {
+                                               uint32_t* __restrict__ hist, unsigned long long* __restrict__ count) {
   __shared__ uint32_t lh[kHistExperts * 256];
   const int e0 = blockIdx.x * kHistExperts, ts = blockIdx.y;
+  const int ne = min(kHistExperts, E - e0);
   const int nb = kHistExperts * B;
   for (int i = threadIdx.x; i < nb; i += 1024) lh[i] = 0;
   __syncthreads();
@@ -192,99 +198,74 @@ __global__ __launch_bounds__(1024) void k_hist(const float* __restrict__ logits,
   const int e = e0 + lane;
   const int tb = ts * tps, te = min(T, tb + tps);
   if (e < E) {
-    for (int t = tb + wave; t < te; t += 16) {
-      const float sc = router_sigmoid(logits[(size_t)t * E + e]);
-      atomicAdd(&lh[lane * B + score_bin(sc, B)], 1u);
+    int t = tb + wave;
+    for (; t + 48 < te; t += 64) {
+      const float l0 = logits[(size_t)t * E + e], l1 = logits[(size_t)(t + 16) * E + e];
+      const float l2 = logits[(size_t)(t + 32) * E + e], l3 = logits[(size_t)(t + 48) * E + e];
+      atomicAdd(&lh[lane * B + score_bin(router_sigmoid(l0), B)], 1u);
+      atomicAdd(&lh[lane * B + score_bin(router_sigmoid(l1), B)], 1u);
+      atomicAdd(&lh[lane * B + score_bin(router_sigmoid(l2), B)], 1u);
+      atomicAdd(&lh[lane * B + score_bin(router_sigmoid(l3), B)], 1u);
     }
+    for (; t < te; t += 16) atomicAdd(&lh[lane * B + score_bin(router_sigmoid(logits[(size_t)t * E + e]), B)], 1u);
   }
   __syncthreads();
-  const int ne = min(kHistExperts, E - e0);
-  if (partial) {
-    uint32_t* dst = partial + ((size_t)ts * E + e0) * B;
-    for (int i = threadIdx.x; i < ne * B; i += 1024) dst[i] = lh[i];
-  } else {
-    uint32_t* dst = hist + (size_t)e0 * B;
-    for (int i = threadIdx.x; i < ne * B; i += 1024) dst[i] += lh[i];
-    if (blockIdx.x == 0 && threadIdx.x == 0) *count += (unsigned long long)T;
+  if (tb < T) {
+    uint32_t* dst = hist + ((size_t)ts * E + e0) * B;
+    for (int i = threadIdx.x; i < ne * B; i += 1024) {
+      const uint32_t v = lh[i];
+      if (v) dst[i] += v;
+    }
   }
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *count += (unsigned long long)T;
 }
 
-__global__ __launch_bounds__(256) void k_hist_reduce(const uint32_t* __restrict__ partial, int nslices, int EB,
-                                                     int T, uint32_t* __restrict__ hist,
-                                                     unsigned long long* __restrict__ count) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < EB) {
-    uint32_t acc = hist[i];
-    for (int sl = 0; sl < nslices; ++sl) acc += partial[(size_t)sl * EB + i];
-    hist[i] = acc;
-  }
-  if (i == 0) *count += (unsigned long long)T;
-}
-
-hipError_t launch_hist(const Dims& D, const float* logits, int T, uint32_t* partial, uint32_t* hist,
-                       unsigned long long* count, hipStream_t s) {
-  const int ns = hist_token_slices(T, D.E);
-  const int tps = (T + ns - 1) / ns;
-  dim3 grid((D.E + kHistExperts - 1) / kHistExperts, ns);
-  hipLaunchKernelGGL(k_hist, grid, dim3(1024), 0, s, logits, T, D.E, D.B, tps, ns > 1 ? partial : nullptr, hist,
-                     count);
-  return hipGetLastError();
-}
-
-hipError_t launch_hist_reduce(const Dims& D, const uint32_t* partial, int nslices, int T, uint32_t* hist,
-                              unsigned long long* count, hipStream_t s) {
-  const int EB = D.E * D.B;
-  hipLaunchKernelGGL(k_hist_reduce, dim3((EB + 255) / 256), dim3(256), 0, s, partial, nslices, EB, T, hist, count);
+hipError_t launch_hist(const Dims& D, const float* logits, int T, uint32_t* hist, unsigned long long* count,
+                       hipStream_t s) {
+  const int tps = (T + kHistSlices - 1) / kHistSlices;
+  dim3 grid((D.E + kHistExperts - 1) / kHistExperts, kHistSlices);
+  hipLaunchKernelGGL(k_hist, grid, dim3(1024), 0, s, logits, T, D.E, D.B, tps, hist, count);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------- counts / scan ----
-// Per expert, exclusive prefix over the chunks of chunk_counts[chunk][E] (in
-// place: it becomes each chunk's base row inside the expert's group) and the
-// expert's total.  64 experts per block (one per lane, coalesced rows), the
-// chunks split over 16 wavefronts.
-__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ cc, int nchunks, int E,
-                                               int32_t* __restrict__ counts) {
-  __shared__ int part[16][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// Two-level exclusive prefix sums of the per-(chunk, expert) selection counts
+// popcount(bitmap[c][e]).  Local: per super-chunk of kSuper chunks, one lane
+// per expert walks its chunks: cbase[c][e] = count of expert e in the earlier
+// chunks of the super-chunk; sbase[sc][e] = the super-chunk's total.
+__global__ __launch_bounds__(256) void k_scan_local(const uint32_t* __restrict__ bitmap, int nchunks, int E,
+                                                    int32_t* __restrict__ cbase, int32_t* __restrict__ sbase) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = blockIdx.x * 64 + lane;
-  const int per = (nchunks + 15) / 16;
-  const int c0 = min(nchunks, w * per), c1 = min(nchunks, c0 + per);
-  int sum = 0;
-  if (e < E)
-    for (int c = c0; c < c1; ++c) sum += cc[(size_t)c * E + e];
-  part[w][lane] = sum;
-  __syncthreads();
-  int base = 0, total = 0;
-  for (int i = 0; i < 16; ++i) {
-    const int v = part[i][lane];
-    base += i < w ? v : 0;
-    total += v;
+  const int sc = blockIdx.y * 4 + wave;
+  const int c0 = sc * kSuper;
+  if (e >= E || c0 >= nchunks) return;
+  const int c1 = min(nchunks, c0 + kSuper);
+  int run = 0;
+  for (int c = c0; c < c1; ++c) {
+    const size_t i = (size_t)c * E + e;
+    const int v = __popc(bitmap[i]);
+    cbase[i] = run;
+    run += v;
   }
-  if (e < E) {
-    int run = base;
-    for (int c = c0; c < c1; ++c) {
-      const int v = cc[(size_t)c * E + e];
-      cc[(size_t)c * E + e] = run;
-      run += v;
-    }
-    if (w == 0) counts[e] = total;
-  }
+  sbase[(size_t)sc * E + e] = run;
 }
 
-hipError_t launch_scan(const Dims& D, int32_t* chunk_counts, int nchunks, int32_t* counts, hipStream_t s) {
-  hipLaunchKernelGGL(k_scan, dim3((D.E + 63) / 64), dim3(1024), 0, s, chunk_counts, nchunks, D.E, counts);
-  return hipGetLastError();
-}
-
-// Exclusive prefix sums over experts: row offsets[E+1] and, for the grouped
-// GEMMs, the first m-tile of each expert tile_offsets[E+1] (tiles of
-// kExpertBM rows; an empty expert has none).  One block of 1024 threads.
-__global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ counts, int E,
-                                                  int32_t* __restrict__ offsets, int32_t* __restrict__ tile_offsets) {
+// Global (one block of 1024 threads): per expert, the total and the exclusive
+// prefix over super-chunks (sbase becomes the absolute first row of each
+// super-chunk's part of the expert's group); over experts, the row offsets
+// and the first m-tile of each expert for the grouped GEMMs (tiles of
+// kExpertBM rows; an empty expert has none).
+__global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbase, int nsuper, int E,
+                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ tile_offsets) {
   __shared__ int wsum_r[16], wsum_t[16];
   const int i = threadIdx.x, lane = i & 63, w = i >> 6;
-  const int c = i < E ? counts[i] : 0;
+  int c = 0;
+  if (i < E) {
+#pragma unroll 8
+    for (int sc = 0; sc < nsuper; ++sc) c += sbase[(size_t)sc * E + i];
+  }
   const int tl = (c + kExpertBM - 1) / kExpertBM;
   int r = c, t = tl;  // inclusive wave scans
 #pragma unroll
@@ -308,8 +289,16 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
   r += br;
   t += bt;
   if (i < E) {
+    counts[i] = c;
     offsets[i + 1] = r;
     tile_offsets[i + 1] = t;
+    int run = r - c;  // exclusive offset of expert i
+    for (int sc = 0; sc < nsuper; ++sc) {
+      const size_t j = (size_t)sc * E + i;
+      const int v = sbase[j];
+      sbase[j] = run;
+      run += v;
+    }
   }
   if (i == 0) {
     offsets[0] = 0;
@@ -317,50 +306,44 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
   }
 }
 
-hipError_t launch_offsets(const Dims& D, const int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
-                          hipStream_t s) {
-  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, s, counts, D.E, offsets, tile_offsets);
+hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cbase, int32_t* sbase, int32_t* counts,
+                       int32_t* offsets, int32_t* tile_offsets, hipStream_t s) {
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const int nsuper = (nchunks + kSuper - 1) / kSuper;
+  dim3 g1((D.E + 63) / 64, (nsuper + 3) / 4);
+  hipLaunchKernelGGL(k_scan_local, g1, dim3(256), 0, s, bitmap, nchunks, D.E, cbase, sbase);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_scan_global, dim3(1), dim3(1024), 0, s, sbase, nsuper, D.E, counts, offsets, tile_offsets);
   return hipGetLastError();
 }
 
 // -------------------------------------------------------------- scatter ----
-// Stable rows without order-dependent atomics: one wavefront per chunk of 64
-// tokens (lane = token).  Every lane ORs its bit into the LDS mask of each
-// expert it picked; the rank of (t, j) inside the chunk's part of expert e's
-// group is the number of lower lanes in mask[e].
-__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, const int32_t* __restrict__ offsets,
-                                                 const int32_t* __restrict__ cbase, int T, int E, int k,
-                                                 int nchunks, int32_t* __restrict__ perm_src,
+// Stable rows without order-dependent atomics, one thread per (t, j): the row
+// of token t in expert e's group is the super-chunk base + the chunk base +
+// the number of earlier tokens of the chunk in the chunk's mask for e.
+__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, const uint32_t* __restrict__ bitmap,
+                                                 const int32_t* __restrict__ cbase, const int32_t* __restrict__ sbase,
+                                                 int T, int E, int k, int32_t* __restrict__ perm_src,
                                                  int32_t* __restrict__ inv) {
-  extern __shared__ unsigned long long masks[];  // [4][E]
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  unsigned long long* m = masks + (size_t)w * E;
-  for (int e = lane; e < E; e += 64) m[e] = 0ull;
-  __syncthreads();
-  const int chunk = blockIdx.x * 4 + w;
-  const int t = chunk * kChunk + lane;
-  const bool valid = chunk < nchunks && t < T;
-  if (valid)
-    for (int j = 0; j < k; ++j) atomicOr(&m[idx[(size_t)t * k + j]], 1ull << lane);
-  __syncthreads();
-  if (valid) {
-    const unsigned long long below = (1ull << lane) - 1ull;
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(size_t)t * k + j];
-      const int rank = __popcll(m[e] & below);
-      const int row = offsets[e] + cbase[(size_t)chunk * E + e] + rank;
-      if (row < T * k) perm_src[row] = t;  // always true for consistent counts
-      inv[(size_t)t * k + j] = row;
-    }
-  }
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int Tk = T * k;
+  if (i >= Tk) return;
+  const int t = i / k;
+  const int e = idx[i];
+  const int c = t / kChunk;
+  const size_t ce = (size_t)c * E + e;
+  const uint32_t below = bitmap[ce] & ((1u << (t % kChunk)) - 1u);
+  const int row = sbase[(size_t)(c / kSuper) * E + e] + cbase[ce] + __popc(below);
+  if ((unsigned)row < (unsigned)Tk) perm_src[row] = t;  // always true for a consistent permutation
+  inv[i] = row;
 }
 
-hipError_t launch_scatter(const Dims& D, const int32_t* idx, const int32_t* offsets, const int32_t* chunk_base, int T,
-                          int32_t* perm_src, int32_t* inv, hipStream_t s) {
-  const int nchunks = (T + kChunk - 1) / kChunk;
-  const size_t lds = (size_t)4 * D.E * sizeof(unsigned long long);
-  hipLaunchKernelGGL(k_scatter, dim3((nchunks + 3) / 4), dim3(256), lds, s, idx, offsets, chunk_base, T, D.E, D.k,
-                     nchunks, perm_src, inv);
+hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* cbase,
+                          const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s) {
+  const long long n = (long long)T * D.k;
+  hipLaunchKernelGGL(k_scatter, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, bitmap, cbase, sbase, T,
+                     D.E, D.k, perm_src, inv);
   return hipGetLastError();
 }
 
@@ -422,40 +405,47 @@ hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, cons
 }
 
 // ------------------------------------------------------------ QB update ----
-// Per expert (one block each): the histogram row goes to LDS and is cleared;
-// scanning bins from the top, the bin j with A*E < N*k <= (A+c_j)*E (A =
-// tokens above bin j; exact integer tests) holds the score the expert must
-// beat to get N*k/E tokens; inside it the estimate is linear:
-// q = (j+1)/B - ((N*k - A*E) / (E*c_j)) / B, fp64.
+// Per expert (one block each, one thread per bin): sum the bin over the
+// histogram slices and clear it; with A_j = tokens above bin j (a parallel
+// suffix sum), the one bin with A_j*E < N*k <= (A_j + c_j)*E (exact integer
+// tests) holds the score the expert must beat to receive N*k/E tokens; inside
+// it the estimate is linear: q = (j+1)/B - ((N*k - A_j*E) / (E*c_j)) / B, fp64.
 __global__ __launch_bounds__(256) void k_qb_quantile(uint32_t* __restrict__ hist,
                                                      const unsigned long long* __restrict__ count, int E, int B,
                                                      int k, double* __restrict__ q) {
 #pragma clang fp contract(off)
-  __shared__ uint32_t row[256];
+  __shared__ unsigned long long suf[2][256];
   const unsigned long long N = *count;
   if (N == 0) return;
-  const int e = blockIdx.x;
-  uint32_t* hr = hist + (size_t)e * B;
-  for (int i = threadIdx.x; i < B; i += 256) {
-    row[i] = hr[i];
-    hr[i] = 0u;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned long long target = N * (unsigned long long)k;
-    const unsigned long long EE = (unsigned long long)E;
-    unsigned long long above = 0;
-    double qe = 0.0;
-    for (int j = B - 1; j >= 0; --j) {
-      const unsigned long long c = row[j];
-      if (above * EE < target && target <= (above + c) * EE) {
-        const double frac = (double)(target - above * EE) / (double)(EE * c);
-        qe = (double)(j + 1) / (double)B - frac / (double)B;
-        break;
-      }
-      above += c;
+  const int e = blockIdx.x, j = threadIdx.x;
+  unsigned long long c = 0;
+  if (j < B) {
+#pragma unroll 4
+    for (int sl = 0; sl < kHistSlices; ++sl) {
+      uint32_t* p = hist + ((size_t)sl * E + e) * B + j;
+      c += *p;
+      *p = 0u;
     }
-    q[e] = qe;
+  }
+  // inclusive suffix sums over bins (Hillis-Steele, double-buffered)
+  int cur = 0;
+  suf[0][j] = c;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const unsigned long long v = suf[cur][j] + (j + o < 256 ? suf[cur][j + o] : 0ull);
+    suf[cur ^ 1][j] = v;
+    cur ^= 1;
+    __syncthreads();
+  }
+  if (j == 0) q[e] = 0.0;
+  __syncthreads();
+  if (j < B) {
+    const unsigned long long incl = suf[cur][j], above = incl - c;
+    const unsigned long long target = N * (unsigned long long)k, EE = (unsigned long long)E;
+    if (above * EE < target && target <= incl * EE) {
+      const double frac = (double)(target - above * EE) / (double)(EE * c);
+      q[e] = (double)(j + 1) / (double)B - frac / (double)B;
+    }
   }
 }
 
@@ -464,16 +454,20 @@ __global__ __launch_bounds__(256) void k_qb_quantile(uint32_t* __restrict__ hist
 __global__ __launch_bounds__(1024) void k_qb_bias(const double* __restrict__ q, unsigned long long* __restrict__ count,
                                                   int E, float* __restrict__ bias) {
 #pragma clang fp contract(off)
+  __shared__ double qs[1024];
   __shared__ double mu_s;
   if (*count == 0) return;
+  for (int e = threadIdx.x; e < E; e += 1024) qs[e] = q[e];
+  __syncthreads();
   if (threadIdx.x == 0) {
     double mu = 0.0;
-    for (int e = 0; e < E; ++e) mu += q[e];
+#pragma unroll 8
+    for (int e = 0; e < E; ++e) mu += qs[e];
     mu_s = mu / (double)E;
   }
   __syncthreads();
   const double mu = mu_s;
-  for (int e = threadIdx.x; e < E; e += 1024) bias[e] = (float)(mu - q[e]);
+  for (int e = threadIdx.x; e < E; e += 1024) bias[e] = (float)(mu - qs[e]);
   __syncthreads();
   if (threadIdx.x == 0) *count = 0ull;
 }

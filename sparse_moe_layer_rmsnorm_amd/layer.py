@@ -89,13 +89,14 @@ class MoeLayer:
         }
 
     def state_views(self) -> Dict[str, torch.Tensor]:
-        E, nb = self.dims["E"], self.dims["B"]
+        E, nb, S = self.dims["E"], self.dims["B"], self.sl.hist_slices
         s = self.state
         return {
             "bias": s[self.sl.bias:self.sl.bias + 4 * E].view(torch.float32),
             "count": s[self.sl.count:self.sl.count + 8].view(torch.int64),
             "q": s[self.sl.q:self.sl.q + 8 * E].view(torch.float64),
-            "hist": s[self.sl.hist:self.sl.hist + 4 * E * nb].view(torch.int32).view(E, nb),
+            "hist_slices": s[self.sl.hist:self.sl.hist + 4 * S * E * nb].view(torch.int32).view(S, E, nb),
+            "hist": s[self.sl.hist:self.sl.hist + 4 * S * E * nb].view(torch.int32).view(S, E, nb).sum(0),
         }
 
     def route_buffers(self, T: int) -> Dict[str, torch.Tensor]:
