@@ -155,6 +155,15 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # Per-kernel times: one pass of K steps with every launch bracketed by HIP
+    # events on the launch stream (outside the timed region: 24 events a step
+    # would add their own cost to it).
+    B.moe_profile_begin(layer.ctx, 16 * args.steps + 16)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = B.moe_profile_end(layer.ctx)
+    dom = max((n for n in prof if prof[n][1]), key=lambda n: prof[n][0])
     run = step
     if args.graph:
         g = torch.cuda.CUDAGraph()
@@ -164,10 +173,11 @@ def main() -> int:
         for _ in range(3):
             g.replay()
         run = g.replay
-    in_region = not (args.graph or args.no_profile)
-    n_launch = 16 * args.steps + 16
-    if in_region:
-        B.moe_profile_begin(layer.ctx, n_launch)
+    # Timed region: K steps; the dominant kernel's launches alone are bracketed
+    # by events (its roofline position is measured live here).
+    live = not (args.graph or args.no_profile)
+    if live:
+        B.moe_profile_begin(layer.ctx, args.steps + 4, [dom])
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
@@ -176,12 +186,10 @@ def main() -> int:
     ev1.record(stream)
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
-    if not in_region:
-        B.moe_profile_begin(layer.ctx, n_launch)
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-    prof = B.moe_profile_end(layer.ctx)
+    if live:
+        prof_dom = B.moe_profile_end(layer.ctx)[dom]
+    else:
+        prof_dom = prof[dom]
     ms_step = total_ms / args.steps
     tok_s = T / (ms_step / 1e3)
 
@@ -200,18 +208,18 @@ def main() -> int:
             gbs = work["bytes"][name] / (avg_us * 1e-6) / 1e9
             k.update(gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
         kernels[name] = k
-    dom = max(kernels, key=lambda kn: kernels[kn]["avg_us"] * kernels[kn]["launches"] / args.steps)
-    dk = kernels[dom]
-    if "tflops" in dk:
-        traffic = traffic_for(dom, shape.name)
-        roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": peak_mm, "unit": "TFLOP/s",
-                    "frac": round(dk["tflops"] / peak_mm, 4), "traffic": traffic, "kernel": dom,
-                    "algorithmic": f"{work['flops'][dom]:.4g} FLOP per launch"}
+    dom_us = prof_dom[0] / prof_dom[1] * 1e3
+    traffic = traffic_for(dom, shape.name)
+    if dom in work["flops"]:
+        ach = work["flops"][dom] / (dom_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_mm, "unit": "TFLOP/s",
+                    "frac": round(ach / peak_mm, 4), "traffic": traffic, "kernel": dom,
+                    "avg_us": round(dom_us, 3), "algorithmic": f"{work['flops'][dom]:.6g} FLOP per launch"}
     else:
-        traffic = traffic_for(dom, shape.name)
-        roofline = {"bound": "hbm", "achieved": dk["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(dk["gbs"] / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom,
-                    "algorithmic": f"{work['bytes'][dom]:.4g} bytes per launch"}
+        ach = work["bytes"][dom] / (dom_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom,
+                    "avg_us": round(dom_us, 3), "algorithmic": f"{work['bytes'][dom]:.6g} bytes per launch"}
     # expert GEMMs together, and routing + permutation + combine together
     ex_us = sum(kernels[n]["avg_us"] for n in ("expert_up", "expert_down") if n in kernels)
     ex_tf = (work["flops"]["expert_up"] + work["flops"]["expert_down"]) / (ex_us * 1e-6) / 1e12
@@ -233,8 +241,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": shape.dtype,
         "data": "synthetic: seeded PCG64, x ~ N(0,1), weights ~ N(0,1/fan_in), rounded to bf16; random init",
-        "timing": "graph replay" if args.graph else ("eager, no events" if args.no_profile else
-                                                     "eager, per-kernel events in the timed region"),
+        "timing": ("graph replay" if args.graph else "eager") + (
+            "; dominant kernel bracketed by HIP events in the timed region" if live else "") +
+            "; per-kernel table from a separate profiled pass of the same K steps",
         "config": {"workload": f"{shape.name}: T={T} tokens, d={shape.d}, l={shape.l}, E={shape.E}, k={shape.k}, "
                                f"f={shape.f}, f_s={shape.f_s}, B={shape.B}, QB {'frozen' if frozen else 'train'}",
                    "global_batch": T, "step": "training forward + qb_update"},

@@ -191,11 +191,12 @@ const char* moe_status_string(moe_status s);
 const char* moe_last_error(void);
 
 /*
- * Per-kernel timing.  After moe_profile_begin(ctx, n), each kernel the context
- * launches (up to n launches) is bracketed by HIP events on its stream.
- * moe_profile_end() waits for those events and fills, for each kernel id
- * 0..MOE_NUM_KERNELS-1, the summed milliseconds and the launch count; then
- * profiling stops.  Host-side event objects only; no device memory.
+ * Per-kernel timing.  After moe_profile_begin(ctx, n, mask), each kernel the
+ * context launches whose id has its bit set in `mask` (0 = every kernel), up
+ * to n launches, is bracketed by HIP events on its stream.  moe_profile_end()
+ * waits for those events and fills, for each kernel id 0..n_ids-1, the summed
+ * milliseconds and the launch count; then profiling stops.  Host-side event
+ * objects only; no device memory.
  */
 enum {
   MOE_K_RMSNORM = 0, MOE_K_GEMM_H, MOE_K_TOPK, MOE_K_HIST, MOE_K_SCAN, MOE_K_SCATTER,
@@ -203,7 +204,7 @@ enum {
   MOE_K_QB_BIAS, MOE_NUM_KERNELS
 };
 const char* moe_kernel_name(int id);
-moe_status moe_profile_begin(moe_ctx* ctx, int max_launches);
+moe_status moe_profile_begin(moe_ctx* ctx, int max_launches, uint32_t mask);
 moe_status moe_profile_end(moe_ctx* ctx, double* ms, int64_t* launches, int n);
 
 #ifdef __cplusplus

@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
             "moe_status_string": (c_char_p, [c_int]),
             "moe_last_error": (c_char_p, []),
             "moe_kernel_name": (c_char_p, [c_int]),
-            "moe_profile_begin": (c_int, [c_void_p, c_int]),
+            "moe_profile_begin": (c_int, [c_void_p, c_int, ctypes.c_uint32]),
             "moe_profile_end": (c_int, [c_void_p, POINTER(c_double), POINTER(c_int64), c_int]),
         }
         for name, (res, args) in sig.items():
@@ -172,8 +172,10 @@ def moe_destroy(ctx: int) -> None:
     lib().moe_destroy(ctx)
 
 
-def moe_profile_begin(ctx: int, max_launches: int) -> None:
-    check(lib().moe_profile_begin(ctx, max_launches), "moe_profile_begin")
+def moe_profile_begin(ctx: int, max_launches: int, kernels=None) -> None:
+    """Time the launches of the named kernels (all when None)."""
+    mask = 0 if not kernels else sum(1 << KERNELS.index(k) for k in kernels)
+    check(lib().moe_profile_begin(ctx, max_launches, mask), "moe_profile_begin")
 
 
 def moe_profile_end(ctx: int) -> Dict[str, tuple]:

@@ -125,6 +125,7 @@ struct moe_ctx {
   uint64_t pending_tokens;  // accumulated into the histogram since the last update (host mirror)
   // per-kernel timing
   bool prof = false;
+  uint32_t prof_mask = 0;
   int prof_max = 0, prof_n = 0;
   std::vector<hipEvent_t> ev;
   std::vector<int> ev_kernel;
@@ -134,7 +135,7 @@ namespace {
 
 template <class F>
 moe_status run(moe_ctx* c, int kid, hipStream_t s, F&& f) {
-  const bool rec = c->prof && c->prof_n < c->prof_max;
+  const bool rec = c->prof && c->prof_n < c->prof_max && (c->prof_mask == 0 || ((c->prof_mask >> kid) & 1u));
   if (rec && hipEventRecord(c->ev[2 * c->prof_n], s) != hipSuccess)
     return fail(MOE_ERR_HIP, "hipEventRecord failed");
   hipError_t e = f();
@@ -381,7 +382,7 @@ const char* moe_kernel_name(int id) {
   return (id >= 0 && id < MOE_NUM_KERNELS) ? names[id] : "unknown";
 }
 
-moe_status moe_profile_begin(moe_ctx* ctx, int max_launches) {
+moe_status moe_profile_begin(moe_ctx* ctx, int max_launches, uint32_t mask) {
   if (!ctx || max_launches < 1) return fail(MOE_ERR_INVALID_ARG, "bad profiling arguments");
   if ((int)ctx->ev.size() < 2 * max_launches) {
     while ((int)ctx->ev.size() < 2 * max_launches) {
@@ -391,6 +392,7 @@ moe_status moe_profile_begin(moe_ctx* ctx, int max_launches) {
     }
   }
   ctx->ev_kernel.assign(max_launches, -1);
+  ctx->prof_mask = mask;
   ctx->prof_max = max_launches;
   ctx->prof_n = 0;
   ctx->prof = true;

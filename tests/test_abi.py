@@ -1,0 +1,103 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/moe.h declares, sizes its buffers consistently, and rejects
+bad arguments before touching the device.  Every call here returns before
+any HIP runtime call."""
+import ctypes
+import subprocess
+
+import pytest
+
+from sparse_moe_layer_rmsnorm_amd import binding as B
+
+REPLICA = dict(d=1024, l=256, E=256, k=6, f=512, f_s=2048)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = B.header_functions()
+    assert {"moe_init", "moe_route", "moe_forward", "qb_update"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(L, n)
+
+
+def test_status_strings(L):
+    for code, name in enumerate(["MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_SHAPE", "MOE_ERR_DTYPE",
+                                 "MOE_ERR_WORKSPACE", "MOE_ERR_STATE", "MOE_ERR_HIP"]):
+        assert L.moe_status_string(code).decode() == name
+    assert L.moe_kernel_name(0).decode() == "rmsnorm"
+    assert [L.moe_kernel_name(i).decode() for i in range(B.MOE_NUM_KERNELS)] == B.KERNELS
+
+
+def test_sizes_and_layouts():
+    cfg = B.make_config(**REPLICA, max_tokens=8192)
+    st = B.moe_state_layout_of(cfg)
+    assert B.moe_state_bytes(cfg) == st.total
+    assert st.bias == 0 and st.count >= 4 * 256 and st.q > st.count and st.hist > st.q
+    assert st.total >= st.hist + st.hist_slices * 256 * 256 * 4
+    for T in (0, 1, 1000, 8192):
+        ws = B.moe_workspace_layout(cfg, T)
+        assert B.moe_workspace_bytes(cfg, T) == ws.total
+        offs = [getattr(ws, n) for n, _ in B.moe_ws_layout._fields_]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    ws = B.moe_workspace_layout(cfg, 8192)
+    assert ws.H - ws.G >= 8192 * 2048 * 2 and ws.Y - ws.H >= 8192 * 6 * 512 * 2
+    assert B.moe_workspace_bytes(cfg, 8193) == 0          # above max_tokens
+    assert B.moe_workspace_bytes(cfg, -1) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d", 1000, B.MOE_ERR_SHAPE), ("l", 0, B.MOE_ERR_SHAPE), ("f", 96, B.MOE_ERR_SHAPE),
+    ("f_s", 100, B.MOE_ERR_SHAPE), ("E", 0, B.MOE_ERR_SHAPE), ("E", 1025, B.MOE_ERR_SHAPE),
+    ("k", 0, B.MOE_ERR_SHAPE), ("k", 33, B.MOE_ERR_SHAPE), ("k", 300, B.MOE_ERR_SHAPE),
+    ("qb_bins", 1, B.MOE_ERR_SHAPE), ("qb_bins", 257, B.MOE_ERR_SHAPE), ("dtype", 7, B.MOE_ERR_DTYPE),
+    ("qb_mode", 5, B.MOE_ERR_INVALID_ARG), ("rms_eps", 0.0, B.MOE_ERR_INVALID_ARG),
+    ("max_tokens", 0, B.MOE_ERR_SHAPE), ("max_tokens", 2 ** 30, B.MOE_ERR_SHAPE),
+])
+def test_bad_config_rejected_before_any_device_call(L, field, value, status):
+    cfg = B.make_config(**REPLICA, max_tokens=64)
+    setattr(cfg, field, value)
+    assert B.moe_state_bytes(cfg) == 0
+    ctx = ctypes.c_void_p()
+    w = B.moe_weights(*([1] * 11))                       # never dereferenced: the config fails first
+    assert L.moe_init(ctypes.byref(cfg), ctypes.byref(w), 256, None, ctypes.byref(ctx)) == status
+    assert ctx.value is None
+    assert L.moe_last_error()
+
+
+def test_null_arguments_rejected(L):
+    cfg = B.make_config(**REPLICA, max_tokens=64)
+    ctx = ctypes.c_void_p()
+    w = B.moe_weights(*([1] * 11))
+    assert L.moe_init(None, ctypes.byref(w), 256, None, ctypes.byref(ctx)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_init(ctypes.byref(cfg), None, 256, None, ctypes.byref(ctx)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_init(ctypes.byref(cfg), ctypes.byref(w), None, None, ctypes.byref(ctx)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_init(ctypes.byref(cfg), ctypes.byref(w), 128, None, ctypes.byref(ctx)) == B.MOE_ERR_INVALID_ARG
+    w2 = B.moe_weights(*([1] * 11))
+    w2.W_g = None
+    assert L.moe_init(ctypes.byref(cfg), ctypes.byref(w2), 256, None, ctypes.byref(ctx)) == B.MOE_ERR_INVALID_ARG
+    w3 = B.moe_weights(*([1] * 11))
+    w3.W_sd = None                                       # shared weights are needed when f_s > 0
+    assert L.moe_init(ctypes.byref(cfg), ctypes.byref(w3), 256, None, ctypes.byref(ctx)) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_forward(None, 1, 8, 1, None, 256, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_route(None, 1, None, 8, None, 256, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert L.qb_update(None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_get_bias(None, 1, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_set_bias(None, 1, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_set_qb_mode(None, 0) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_profile_begin(None, 4, 0) == B.MOE_ERR_INVALID_ARG
+    L.moe_destroy(None)
+
+
+def test_python_wrappers_raise_with_message():
+    cfg = B.make_config(**REPLICA, max_tokens=64)
+    cfg.k = 0
+    with pytest.raises(B.MoeError, match="MOE_ERR_SHAPE"):
+        B.moe_state_layout_of(cfg)

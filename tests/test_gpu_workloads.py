@@ -1,0 +1,209 @@
+"""GPU parity on the full-size workloads (load-skew 20-step QB loop, K3-routing
+shape, decode-like frozen pass), plus graph replay and argument errors on the
+device path.  Large batches are checked bit for bit on the routing and on
+sampled tokens for the outputs (the oracle's per-token path)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as o
+from sparse_moe_layer_rmsnorm_amd import binding as Bd
+from sparse_moe_layer_rmsnorm_amd import workloads as wl
+
+from gpu_util import (LOGIT_TOL, OUT_TOL, assert_routing_equal, make_layer, oracle_routing, rel_err, say, to_np,
+                      x_on_gpu)
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+
+
+def _sampled_outputs(shape, W, x, out, ref, n=24, seed=0):
+    T = x.shape[0]
+    pick = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(seed).integers(0, T, n)]))
+    want = o.forward_tokens(x[pick], W, ref["idx"][pick], ref["gates"][pick], dtype=shape.dtype, eps=shape.rms_eps)
+    return rel_err(out[pick], want)
+
+
+def _check_logits(shape, W, x, lg, n=16):
+    pick = np.linspace(0, x.shape[0] - 1, n).astype(int)
+    h = o.bf16_round(o.rmsnorm(x[pick], W["gamma"], shape.rms_eps))
+    return rel_err(lg[pick], o.router_logits(h, W["W_r"], W.get("c")))
+
+
+def test_skew_workload_20_step_qb_loop():
+    """Zipf-offset logits, 20 forward + QB steps (fresh x each step): routing
+    and bias bit-exact every step; load balance from > 10x mean to < 1.6x."""
+    shape = wl.workload("skew")
+    T = shape.T
+    W = wl.make_weights(shape)
+    c = wl.zipf_logit_offset(shape)
+    W = dict(W, c=c)
+    layer = make_layer(shape, W, max_tokens=T, c=c)
+    bias = np.zeros(shape.E, F32)
+    r = layer.route_buffers(T)
+    ratios = []
+    for step in range(20):
+        say(f"skew step {step}")
+        x = wl.make_x(shape, step)
+        out = layer.forward(x_on_gpu(x, layer), route=r)
+        layer.qb_update()
+        torch.cuda.synchronize()
+        lg = to_np(r["logits"])
+        ref = oracle_routing(lg, bias, shape.k, shape.E, shape.B)
+        assert_routing_equal(r, ref, T)
+        st = o.load_stats(ref["counts"])
+        ratios.append(st["max_over_mean"])
+        say(f"  max/min {st['max_over_min']:.2f} max/mean {st['max_over_mean']:.2f} dead {st['dead']}")
+        bias = o.qb_update(ref["hist"], T, shape.k, bias)
+        np.testing.assert_array_equal(to_np(layer.get_bias()).view(np.uint32), bias.view(np.uint32))
+        if step in (0, 19):
+            assert _check_logits(shape, W, x, lg) <= LOGIT_TOL["bf16"]
+            assert _sampled_outputs(shape, W, x, to_np(out), ref, seed=step) <= OUT_TOL["bf16"]
+    assert ratios[0] > 10
+    assert max(ratios[1:]) < 1.6
+    layer.close()
+
+
+def test_k3_routing_shape_full():
+    """E=896 experts, top-16, T=16384, d=4096, l=1024 (widths assumed)."""
+    shape = wl.workload("k3")
+    T = shape.T
+    say("k3 weights")
+    W = wl.make_weights(shape)
+    x = wl.make_x(shape)
+    layer = make_layer(shape, W, max_tokens=T)
+    r = layer.route_buffers(T)
+    say("k3 forward")
+    out = to_np(layer.forward(x_on_gpu(x, layer), route=r))
+    torch.cuda.synchronize()
+    lg = to_np(r["logits"])
+    assert _check_logits(shape, W, x, lg) <= LOGIT_TOL["bf16"]
+    ref = oracle_routing(lg, np.zeros(shape.E, F32), shape.k, shape.E, shape.B)
+    assert_routing_equal(r, ref, T)
+    np.testing.assert_array_equal(to_np(layer.state_views()["hist"]), ref["hist"])
+    err = _sampled_outputs(shape, W, x, out, ref, n=12)
+    say(f"  sampled out rel err {err:.3e}")
+    assert err <= OUT_TOL["bf16"]
+    layer.qb_update()
+    torch.cuda.synchronize()
+    b = o.qb_update(ref["hist"], T, shape.k, np.zeros(shape.E, F32))
+    np.testing.assert_array_equal(to_np(layer.get_bias()).view(np.uint32), b.view(np.uint32))
+    layer.close()
+
+
+@pytest.mark.parametrize("std,forced", [(0.1, 0), (0.04, 8)])
+def test_decode_frozen_full(std, forced):
+    """T=131072 with a frozen, mean-centred N(0, std) bias: forward only, no
+    histogram, empty experts handled."""
+    shape = wl.workload("decode")
+    T = shape.T
+    W = wl.make_weights(shape)
+    x = wl.make_x(shape)
+    b = wl.frozen_bias(shape, std=std, n_forced_empty=forced)
+    layer = make_layer(shape, W, max_tokens=T, frozen=True)
+    layer.set_bias(b)
+    r = layer.route_buffers(T)
+    say(f"decode std={std} forced={forced}")
+    out = to_np(layer.forward(x_on_gpu(x, layer), route=r))
+    layer.qb_update()                                  # frozen: no-op
+    torch.cuda.synchronize()
+    lg = to_np(r["logits"])
+    ref = oracle_routing(lg, b, shape.k, shape.E, shape.B)
+    assert_routing_equal(r, ref, T)
+    st = o.load_stats(ref["counts"])
+    say(f"  dead {st['dead']} max/mean {st['max_over_mean']:.2f}")
+    if forced:
+        assert st["dead"] >= forced
+    else:
+        assert st["dead"] > 0                          # the literal draw leaves experts empty
+    sv = layer.state_views()
+    assert int(sv["count"].item()) == 0 and int(sv["hist_slices"].abs().sum().item()) == 0
+    np.testing.assert_array_equal(to_np(layer.get_bias()), b)
+    err = _sampled_outputs(shape, W, x, out, ref)
+    say(f"  sampled out rel err {err:.3e}")
+    assert err <= OUT_TOL["bf16"]
+    layer.close()
+
+
+def test_graph_replay_matches_eager():
+    """forward + qb_update captured in a graph: every replay (with eager work
+    and synchronisation between replays) equals the eager result."""
+    shape = wl.workload("replica", 2048)
+    T = shape.T
+    W = wl.make_weights(shape)
+    layer = make_layer(shape, W, max_tokens=T)
+    xt = x_on_gpu(wl.make_x(shape), layer)
+    r = layer.route_buffers(T)
+    out = torch.empty(T, shape.d, dtype=layer.tdtype, device="cuda")
+    # eager reference: forward with bias 0, update, forward with the new bias
+    layer.forward(xt, out=out, route=r)
+    layer.qb_update()
+    eager1 = out.clone()
+    layer.forward(xt, out=out, route=r)
+    eager2 = out.clone()
+    b2 = layer.get_bias().clone()
+    layer.qb_update()
+    torch.cuda.synchronize()
+    b3 = layer.get_bias().clone()
+    assert torch.equal(b2, b3)                          # same batch: single-step convergence
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(xt, out=out, route=r)            # warm the capture stream
+        layer.qb_update()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        layer.forward(xt, out=out, route=r)
+        layer.qb_update()
+    for i in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager2), f"replay {i}"
+        assert torch.equal(layer.get_bias(), b3)
+        _ = (xt.float() * 2).sum().item()              # unrelated eager work between replays
+    assert not torch.equal(eager1, eager2)              # the bias changed the routing
+    layer.close()
+
+
+def test_zero_tokens_and_argument_errors():
+    shape = wl.workload("replica", 64)
+    layer = make_layer(shape, wl.make_weights(shape), max_tokens=64)
+    xt = x_on_gpu(wl.make_x(shape), layer)
+    ws = layer.workspace(64)
+    st0 = layer.state.clone()
+    Bd.moe_forward(layer.ctx, xt.data_ptr(), 0, xt.data_ptr(), None, 0, 0, 0)   # T = 0: nothing, no workspace needed
+    torch.cuda.synchronize()
+    assert torch.equal(layer.state, st0)
+    with pytest.raises(Bd.MoeError, match="MOE_ERR_SHAPE"):
+        Bd.moe_forward(layer.ctx, xt.data_ptr(), 65, xt.data_ptr(), None, ws.data_ptr(), ws.numel(), 0)
+    with pytest.raises(Bd.MoeError, match="MOE_ERR_WORKSPACE"):
+        Bd.moe_forward(layer.ctx, xt.data_ptr(), 64, xt.data_ptr(), None, ws.data_ptr(), 1024, 0)
+    with pytest.raises(Bd.MoeError, match="MOE_ERR_WORKSPACE"):
+        Bd.moe_forward(layer.ctx, xt.data_ptr(), 64, xt.data_ptr(), None, ws.data_ptr() + 16, ws.numel() - 16, 0)
+    with pytest.raises(Bd.MoeError, match="MOE_ERR_INVALID_ARG"):
+        Bd.moe_route(layer.ctx, None, None, 64, None, ws.data_ptr(), ws.numel(), 0)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.state, st0)               # nothing was enqueued
+    layer.close()
+
+
+def test_route_from_x_equals_forward_routing():
+    shape = wl.workload("replica", 777)
+    T = shape.T
+    W = wl.make_weights(shape)
+    layer = make_layer(shape, W, max_tokens=T)
+    xt = x_on_gpu(wl.make_x(shape), layer)
+    r1 = layer.route(T, x=xt)
+    r2 = layer.route_buffers(T)
+    layer.forward(xt, route=r2)
+    torch.cuda.synchronize()
+    for k in r1:
+        assert torch.equal(r1[k], r2[k]), k
+    h = layer.state_views()["hist"]
+    ref = oracle_routing(to_np(r1["logits"]), np.zeros(shape.E, F32), shape.k, shape.E, shape.B)
+    np.testing.assert_array_equal(to_np(h), 2 * ref["hist"])       # both calls accumulated
+    assert int(layer.state_views()["count"].item()) == 2 * T
+    layer.close()
