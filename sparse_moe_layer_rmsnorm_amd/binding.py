@@ -45,8 +45,8 @@ class moe_state_layout(ctypes.Structure):
 
 class moe_ws_layout(ctypes.Structure):
     _fields_ = [(n, c_size_t) for n in ("h", "logits", "idx", "gates", "bitmap", "cbase", "sbase", "counts",
-                                        "offsets", "tile_offsets", "perm_src", "inv", "G", "z", "H", "Y", "y_lat",
-                                        "total")]
+                                        "offsets", "tile_offsets", "perm_src", "inv", "tile_info", "G", "z", "X",
+                                        "H", "Y", "y_lat", "total")]
 
 
 _lib = None

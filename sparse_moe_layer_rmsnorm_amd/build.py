@@ -26,6 +26,8 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
     # packed fp32 arithmetic stays off (see the design notes)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: avoids AGPR<->VGPR copies in the GEMM loops
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE, "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]

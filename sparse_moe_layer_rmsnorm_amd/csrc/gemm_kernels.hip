@@ -5,8 +5,8 @@
 //   * gemm_h:      h [T,d] against [W_r | W_sg,W_su | W_dn] -> fp32 router
 //                  logits, the shared GLU hidden G = silu(h W_sg^T)*(h W_su^T)
 //                  and the latent z = h W_dn^T in one launch (one pass of h);
-//   * expert_up:   per expert, rows z[perm_src] (gathered in the A loader)
-//                  against W_g[e], W_u[e] with the GLU in the epilogue -> H;
+//   * expert_up:   per expert, its dispatched rows X against W_g[e], W_u[e]
+//                  with the GLU in the epilogue -> H;
 //   * expert_down: per expert, H rows against W_d[e] -> Y;
 //   * gemm_out:    [G | y_lat] against [W_sd | W_up] (one K loop over both
 //                  parts) -> out, so the shared and routed paths are summed in
@@ -16,15 +16,22 @@
 // GLUs as batched matmuls per expert group: capsule 20 of the "Pretraining a
 // Mini Kimi K3" review.)
 //
-// Tiling: 256 threads = 4 wavefronts in a 2x2 grid over a BM x BN block tile;
-// K advances 128 bytes per stage (64 bf16 or 32 fp32).  Stages are
-// double-buffered in LDS; the next stage's global loads are in flight while
-// the current one feeds the MFMAs.  bf16 uses v_mfma_f32_16x16x32_bf16, fp32
-// four v_mfma_f32_16x16x4_f32 per 16-byte fragment.  The weight fragment is
-// the MFMA's first operand, so each lane's accumulators hold 4 consecutive
-// output columns of one row (8- or 16-byte stores).  LDS rows are 128 bytes
-// with 16-byte chunks XOR-swizzled by row, so the 16 rows a fragment read
-// touches fall in distinct banks.
+// Execution: persistent blocks of 4 wavefronts.  Block b runs on XCD b%8 and
+// walks a contiguous range of the logical tile order that belongs to its XCD,
+// so the tiles in flight on one XCD share operands in that XCD's L2.  The K
+// loops of a block's consecutive tiles form one continuous stream of 128-byte
+// K stages through an NS-deep ring of LDS buffers: stages are filled with
+// global_load_lds_dwordx4 (global -> LDS DMA, no registers) NS-1 stages ahead,
+// also across tile boundaries, so a tile's first loads are in flight while the
+// previous tile still computes.  Tile metadata comes from kernel arguments or
+// scalar loads, so the stage DMA is the only vector-memory load in the loop
+// and the explicit vmcnt waits stay exact.
+//
+// MFMA: bf16 v_mfma_f32_16x16x32_bf16; fp32 four v_mfma_f32_16x16x4_f32 per
+// 16-byte fragment.  The weight fragment is the MFMA's first operand, so each
+// lane's accumulators hold 4 consecutive output columns of one row.  LDS rows
+// are 128 bytes with 16-byte chunks XOR-swizzled by row, so the 16 rows a
+// fragment read touches fall in distinct banks.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -62,10 +69,30 @@ MOE_DEV uint32_t lds_addr(const char* p) {
 // One 16-byte-per-lane global -> LDS DMA load (global_load_lds_dwordx4): lane
 // i of the wavefront writes LDS bytes [lds + 16 i, lds + 16 i + 16).  `lds`
 // must be wave-uniform.  Issued from inline asm so that the compiler does not
-// add a wait for all outstanding loads before every LDS read; the loop below
+// add a wait for all outstanding loads before every LDS read; the stream loop
 // waits for its own loads explicitly.
 MOE_DEV void lds_dma16(const char* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wavefront are
+// outstanding.  Loads complete in issue order, so with N = the number of DMA
+// loads issued after a stage, that stage has landed in LDS (stores still in
+// flight can only lengthen the wait).
+template <int N>
+MOE_DEV void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+MOE_DEV void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Scalar (SMEM) load of wave-uniform tile metadata written by an earlier kernel.
+MOE_DEV int2 scalar_load2(const int2* p, int i) {
+  const unsigned long long v = *((const __attribute__((address_space(4))) unsigned long long*)p + i);
+  return make_int2((int)(uint32_t)v, (int)(uint32_t)(v >> 32));
+}
+MOE_DEV int scalar_load(const int32_t* p, int i) {
+  return *((const __attribute__((address_space(4))) int32_t*)p + i);
 }
 
 // Stage filling: a stage is BM + BN rows of 128 bytes (A rows, then B rows),
@@ -75,79 +102,53 @@ MOE_DEV void lds_dma16(const char* g, uint32_t lds) {
 MOE_DEV int slot_row(int i, int wave, int lane) { return (i * 4 + wave) * 8 + (lane >> 3); }
 MOE_DEV int slot_chunk(int row, int lane) { return (lane & 7) ^ ((row & 7) ^ ((row >> 3) & 1)); }
 
-// Global source of each of this thread's slot pieces at k = 0, per K part;
-// the source advances 128 bytes per stage.  PARTS K parts are consumed one
-// after the other (kt[p] stages each).
-template <int L, int PARTS>
-struct Src {
-  const char* p[PARTS][L];
-  int kt[PARTS];
-};
-
-template <int BM, int BN, bool BF16>
-struct Core {
-  static constexpr int WTM = BM / 2, WTN = BN / 2;
+// Block tile BM x BN over 4 wavefronts laid out (4/WN) x WN; NS LDS stages.
+template <int BM_, int BN_, int WN, int NS_, bool BF16>
+struct Pipe {
+  static constexpr int BM = BM_, BN = BN_, NS = NS_;
+  static constexpr int WM = 4 / WN;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int MI = WTM / 16, NI = WTN / 16;
-  static constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int A_BYTES = BM * kRowBytes;
+  static constexpr int STAGE = (BM + BN) * kRowBytes;
+  static constexpr int LDS = NS * STAGE;
   static constexpr int L = STAGE / 1024 / 4;  // DMA slots per thread per stage
   static_assert(STAGE % 4096 == 0, "stage must split into 1 KB slots over 4 wavefronts");
+  static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+  using Acc = f32x4_t[MI][NI];
 
-  // Accumulate all stages into acc.  Two LDS buffers: the loads of stage s+1
-  // are issued right after the barrier that ends stage s-1's reads, and run
-  // while stage s feeds the MFMAs.
-  template <int PARTS>
-  MOE_DEV static void run(const Src<L, PARTS>& S, f32x4_t (&acc)[MI][NI], char* smem) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    int KT = S.kt[0];
-    if constexpr (PARTS > 1) KT += S.kt[1];
-    if (KT <= 0) return;
-    const uint32_t lds0 = lds_addr(smem) + wave * 1024;
-    auto issue = [&](int s, int buf) {
-      bool second = false;
-      int ks = s;
-      if constexpr (PARTS > 1) {
-        second = s >= S.kt[0];
-        ks = second ? s - S.kt[0] : s;
-      }
-      const uint32_t base = lds0 + buf * STAGE;
+  MOE_DEV static void compute(const char* cur, Acc& acc) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
 #pragma unroll
-      for (int i = 0; i < L; ++i) {
-        const char* g = S.p[0][i];
-        if constexpr (PARTS > 1) g = second ? S.p[1][i] : g;
-        lds_dma16(g + ks * kRowBytes, __builtin_amdgcn_readfirstlane(base + i * 4096));
-      }
-    };
-    issue(0, 0);
-    for (int s = 0; s < KT; ++s) {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      if (s + 1 < KT) issue(s + 1, (s + 1) & 1);
-      const char* cur = smem + (s & 1) * STAGE;
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ch = kk * 4 + (lane >> 4);
+      uint4 af[MI], wf[NI];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int ch = kk * 4 + (lane >> 4);
-        uint4 af[MI], wf[NI];
+      for (int mi = 0; mi < MI; ++mi)
+        af[mi] = *reinterpret_cast<const uint4*>(cur + lds_off(wm * WTM + mi * 16 + (lane & 15), ch));
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-          af[mi] = *reinterpret_cast<const uint4*>(cur + lds_off(wm * WTM + mi * 16 + (lane & 15), ch));
+      for (int ni = 0; ni < NI; ++ni)
+        wf[ni] = *reinterpret_cast<const uint4*>(cur + A_BYTES + lds_off(wn * WTN + ni * 16 + (lane & 15), ch));
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          wf[ni] = *reinterpret_cast<const uint4*>(cur + A_BYTES + lds_off(wn * WTN + ni * 16 + (lane & 15), ch));
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) mfma_chunk<BF16>(acc[mi][ni], wf[ni], af[mi]);
-      }
+        for (int ni = 0; ni < NI; ++ni) mfma_chunk<BF16>(acc[mi][ni], wf[ni], af[mi]);
     }
   }
 
-  MOE_DEV static void zero(f32x4_t (&acc)[MI][NI]) {
+  MOE_DEV static void zero(Acc& acc) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Wait for a stage after which `after` further stages were issued.
+  MOE_DEV static void wait_stage(int after) {
+    if (after <= 0) wait_vmcnt<0>();
+    else if (after == 1) wait_vmcnt<L>();
+    else wait_vmcnt<2 * L>();
   }
 
   // Row-major store of 4 consecutive columns.
@@ -166,10 +167,10 @@ struct Core {
   //   EPI_GLU:   tile columns alternate 16 gate / 16 up; output column
   //              n0/2 + 16*(c/32) + c%16 gets silu(gate) * up.
   template <int KIND>
-  MOE_DEV static void epilogue(const f32x4_t (&acc)[MI][NI], int rows_valid, int n0, int N, void* out, int ldo,
-                               size_t row_base, const float* col_off) {
+  MOE_DEV static void epilogue(const Acc& acc, int rows_valid, int n0, int N, void* out, int ldo, size_t row_base,
+                               const float* col_off) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       const int m = wm * WTM + mi * 16 + (lane & 15);
@@ -205,10 +206,67 @@ struct Core {
   }
 };
 
+// A tile of the logical order: first output row, rows in use, n-tile, and the
+// segment (dense) or expert (grouped) it belongs to.  Wave-uniform.
+struct Tile {
+  int row0, rows, nt, sel;
+};
+
+// The persistent stream over this block's tiles.  Prob supplies total(),
+// kt(), tile(logical), sources(tile, src), issue(src, ks, lds) and
+// epilogue(tile, acc).
+template <class Pp, class Prob>
+MOE_DEV void stream(const Prob& prob, char* smem) {
+  const int G = gridDim.x, b = blockIdx.x;
+  const int x = b & 7, q = b >> 3, Gx = G >> 3;  // the grid is a multiple of 8
+  const int total_tiles = prob.total();
+  const int per = (total_tiles + 7) >> 3;
+  const int lo = x * per, hi = min(total_tiles, lo + per);
+  const int span = hi - lo - q;
+  const int my_n = span > 0 ? (span + Gx - 1) / Gx : 0;
+  if (my_n <= 0) return;
+  const int KT = prob.kt();
+  const int total = my_n * KT;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t lds0 = lds_addr(smem) + wave * 1024;
+
+  typename Prob::template SrcT<Pp::L> src;
+  int iss_j = 0, iss_ks = 0, issued = 0;
+  prob.sources(prob.tile(lo + q), src);
+  auto issue = [&]() {
+    const uint32_t base = lds0 + (uint32_t)((issued % Pp::NS) * Pp::STAGE);
+    prob.issue(src, iss_ks, base);
+    ++issued;
+    if (++iss_ks == KT) {
+      iss_ks = 0;
+      if (++iss_j < my_n) prob.sources(prob.tile(lo + q + iss_j * Gx), src);
+    }
+  };
+  for (int s = 0; s < Pp::NS - 1; ++s)
+    if (issued < total) issue();
+
+  typename Pp::Acc acc;
+  Pp::zero(acc);
+  int cj = 0, cks = 0;
+  Tile ct = prob.tile(lo + q);
+  for (int g = 0; g < total; ++g) {
+    Pp::wait_stage(issued - g - 1);
+    block_barrier();
+    if (issued < total) issue();
+    Pp::compute(smem + (g % Pp::NS) * Pp::STAGE, acc);
+    if (++cks == KT) {
+      prob.epilogue(ct, acc);
+      Pp::zero(acc);
+      cks = 0;
+      if (++cj < my_n) ct = prob.tile(lo + q + cj * Gx);
+    }
+  }
+}
+
 // ------------------------------------------------------------ dense GEMMs --
 struct DenseSeg {
   const char* B[2];   // weight rows of K part 0 / 1 (gate rows for a GLU)
-  const char* Bu[2];  // up rows for a GLU
+  const char* Bu[2];  // up rows for a GLU (part 0 only)
   int N;              // output columns
   int ntiles;
   int kind;
@@ -229,93 +287,110 @@ struct DenseArgs {
 
 constexpr int kGroupM = 8;
 
-template <int BM, int BN, bool BF16>
-__global__ __launch_bounds__(kThreads) void k_gemm_dense(const DenseArgs args) {
-  using C = Core<BM, BN, BF16>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-  const int nblocks = args.m_tiles * args.total_ntiles;
-  const int L = xcd_remap(blockIdx.x, nblocks);
+template <class Pp>
+struct DenseProb {
+  static constexpr int PARTS = 2;
+  template <int L>
+  struct SrcT {
+    const char* p[2][L];
+  };
+  const DenseArgs& a;
+
+  MOE_DEV int total() const { return a.m_tiles * a.total_ntiles; }
+  MOE_DEV int kt() const { return a.kt[0] + a.kt[1]; }
+  MOE_DEV const DenseSeg& seg(int s) const { return s == 0 ? a.seg[0] : (s == 1 ? a.seg[1] : a.seg[2]); }
+
   // groups of kGroupM m-tiles, m fastest inside a group
-  const int per_group = kGroupM * args.total_ntiles;
-  const int group = L / per_group;
-  const int first_m = group * kGroupM;
-  const int gm = min(args.m_tiles - first_m, kGroupM);
-  const int in_group = L - group * per_group;
-  const int mt = first_m + in_group % gm;
-  int nt = in_group / gm;
-  // segment of this n-tile (selects, not a dynamic index into the kernel
-  // argument, so the descriptor stays in scalar registers)
-  DenseSeg S = args.seg[0];
-  if (args.nseg > 1 && nt >= args.seg[0].ntiles) {
-    nt -= args.seg[0].ntiles;
-    S = args.seg[1];
-    if (args.nseg > 2 && nt >= args.seg[1].ntiles) {
-      nt -= args.seg[1].ntiles;
-      S = args.seg[2];
-    }
-  }
-  const int m0 = mt * BM;
-  const int rows_valid = min(BM, args.M - m0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  Src<C::L, 2> src;
-#pragma unroll
-  for (int part = 0; part < 2; ++part) {
-    src.kt[part] = args.kt[part];
-#pragma unroll
-    for (int i = 0; i < C::L; ++i) {
-      const int row = slot_row(i, wave, lane);
-      const int chunk = slot_chunk(row, lane);
-      const char* p;
-      if (row < BM) {  // A row (rows past the end read row m0: their results are not stored)
-        const int r = row < rows_valid ? row : 0;
-        p = args.A[part] + (size_t)(m0 + r) * args.lda_bytes[part];
-      } else {         // weight row of output column c (columns past N read row 0)
-        const int c = row - BM;
-        int wrow;
-        const char* base;
-        if (S.kind == EPI_GLU) {
-          wrow = nt * (BN / 2) + (c >> 5) * 16 + (c & 15);
-          base = ((c & 31) >= 16) ? S.Bu[part] : S.B[part];
-        } else {
-          wrow = nt * BN + c;
-          base = S.B[part];
-        }
-        if (wrow >= S.N) wrow = 0;
-        p = base + (size_t)wrow * args.ldb_bytes[part];
+  MOE_DEV Tile tile(int L) const {
+    const int per_group = kGroupM * a.total_ntiles;
+    const int group = L / per_group;
+    const int first_m = group * kGroupM;
+    const int gm = min(a.m_tiles - first_m, kGroupM);
+    const int in_group = L - group * per_group;
+    Tile t;
+    t.row0 = (first_m + in_group % gm) * Pp::BM;
+    t.rows = min(Pp::BM, a.M - t.row0);
+    int nt = in_group / gm, s = 0;
+    if (a.nseg > 1 && nt >= a.seg[0].ntiles) {
+      nt -= a.seg[0].ntiles;
+      s = 1;
+      if (a.nseg > 2 && nt >= a.seg[1].ntiles) {
+        nt -= a.seg[1].ntiles;
+        s = 2;
       }
-      src.p[part][i] = args.kt[part] > 0 ? p + chunk * 16 : nullptr;
+    }
+    t.nt = nt;
+    t.sel = s;
+    return t;
+  }
+
+  template <int L>
+  MOE_DEV void sources(const Tile& t, SrcT<L>& src) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const DenseSeg& S = seg(t.sel);
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        const int row = slot_row(i, wave, lane);
+        const int chunk = slot_chunk(row, lane);
+        const char* p;
+        if (row < Pp::BM) {  // A row (rows past the end read row0: their results are not stored)
+          const int r = row < t.rows ? row : 0;
+          p = a.A[part] + (size_t)(t.row0 + r) * a.lda_bytes[part];
+        } else {  // weight row of tile column c (columns past N read row 0)
+          const int c = row - Pp::BM;
+          int wrow;
+          const char* base;
+          if (S.kind == EPI_GLU) {
+            wrow = t.nt * (Pp::BN / 2) + (c >> 5) * 16 + (c & 15);
+            base = ((c & 31) >= 16) ? S.Bu[part] : S.B[part];
+          } else {
+            wrow = t.nt * Pp::BN + c;
+            base = S.B[part];
+          }
+          if (wrow >= S.N) wrow = 0;
+          p = base + (size_t)wrow * a.ldb_bytes[part];
+        }
+        src.p[part][i] = a.kt[part] > 0 ? p + chunk * 16 : nullptr;
+      }
     }
   }
-  f32x4_t acc[C::MI][C::NI];
-  C::zero(acc);
-  C::template run<2>(src, acc, smem);
-  if (S.kind == EPI_F32)
-    C::template epilogue<EPI_F32>(acc, rows_valid, nt * BN, S.N, S.out, S.ldo, (size_t)m0, S.col_off);
-  else if (S.kind == EPI_GLU)
-    C::template epilogue<EPI_GLU>(acc, rows_valid, nt * BN, S.N, S.out, S.ldo, (size_t)m0, nullptr);
-  else
-    C::template epilogue<EPI_STORE>(acc, rows_valid, nt * BN, S.N, S.out, S.ldo, (size_t)m0, nullptr);
+
+  template <int L>
+  MOE_DEV void issue(const SrcT<L>& src, int ks, uint32_t lds) const {
+    const bool second = ks >= a.kt[0];
+    const int off = (second ? ks - a.kt[0] : ks) * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      lds_dma16((second ? src.p[1][i] : src.p[0][i]) + off, __builtin_amdgcn_readfirstlane(lds + i * 4096));
+  }
+
+  MOE_DEV void epilogue(const Tile& t, const typename Pp::Acc& acc) const {
+    const DenseSeg& S = seg(t.sel);
+    if (S.kind == EPI_F32)
+      Pp::template epilogue<EPI_F32>(acc, t.rows, t.nt * Pp::BN, S.N, S.out, S.ldo, (size_t)t.row0, S.col_off);
+    else if (S.kind == EPI_GLU)
+      Pp::template epilogue<EPI_GLU>(acc, t.rows, t.nt * Pp::BN, S.N, S.out, S.ldo, (size_t)t.row0, nullptr);
+    else
+      Pp::template epilogue<EPI_STORE>(acc, t.rows, t.nt * Pp::BN, S.N, S.out, S.ldo, (size_t)t.row0, nullptr);
+  }
+};
+
+template <class Pp>
+__global__ __launch_bounds__(kThreads) void k_gemm_dense(const DenseArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
+  DenseProb<Pp> prob{args};
+  stream<Pp>(prob, smem);
 }
 
 // ---------------------------------------------------------- expert GEMMs --
-// Tile decode: logical tile L -> global m-tile L / NT (owned by the expert e
-// with tile_offsets[e] <= L/NT < tile_offsets[e+1], found by binary search)
-// and n-tile L % NT.  The grid is an upper bound; blocks past the device-side
-// tile count exit at once.
-MOE_DEV int find_expert(const int32_t* __restrict__ tile_offsets, int E, int gmt) {
-  int lo = 0, hi = E - 1;  // largest e with tile_offsets[e] <= gmt
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_offsets[mid] <= gmt) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
+// Tiles: global m-tile g (of kExpertBM rows) x n-tile; tile_info[g] =
+// {first row, expert << 8 | rows in use}, written by the offsets scan; the
+// m-tile count is tile_offsets[E].  Logical tile L -> m-tile L / NT, n-tile
+// L % NT.
 struct ExpertArgs {
-  const char* A;            // z (up) or H (down)
-  const int32_t* perm_src;  // gather rows through it (up) or nullptr (down)
-  int src_rows;             // rows of A
+  const char* A;  // X (up) or H (down), rows grouped by expert
   int lda_bytes;
   const char* W;   // W_g (up) or W_d (down), [E, N, K]
   const char* Wu;  // W_u (up) or nullptr
@@ -324,81 +399,115 @@ struct ExpertArgs {
   int N;  // output columns
   int NT;
   int kt;
-  const int32_t* offsets;
-  const int32_t* tile_offsets;
-  int E;
+  const int2* tile_info;
+  const int32_t* n_mtiles;  // -> tile_offsets[E]
   void* out;
   int ldo;
 };
 
-template <int BN, bool BF16, int KIND>
-__global__ __launch_bounds__(kThreads) void k_gemm_expert(const ExpertArgs args) {
-  constexpr int BM = kExpertBM;
-  using C = Core<BM, BN, BF16>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-  const int total = args.tile_offsets[args.E] * args.NT;
-  if ((int)blockIdx.x >= total) return;
-  const int L = xcd_remap(blockIdx.x, total);
-  const int gmt = L / args.NT, nt = L - gmt * args.NT;
-  const int e = find_expert(args.tile_offsets, args.E, gmt);
-  const int mt = gmt - args.tile_offsets[e];
-  const int row0 = args.offsets[e] + mt * BM;
-  const int rows_valid = min(BM, args.offsets[e + 1] - row0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const char* Wg = args.W + (size_t)e * args.w_expert_bytes;
-  const char* Wu = args.Wu ? args.Wu + (size_t)e * args.w_expert_bytes : nullptr;
-  Src<C::L, 1> src;
-  src.kt[0] = args.kt;
-#pragma unroll
-  for (int i = 0; i < C::L; ++i) {
-    const int row = slot_row(i, wave, lane);
-    const int chunk = slot_chunk(row, lane);
-    const char* p;
-    if (row < BM) {  // rows past the expert's end read its first row (results not stored)
-      const int r = row0 + (row < rows_valid ? row : 0);
-      int srow = args.perm_src ? args.perm_src[r] : r;
-      srow = (unsigned)srow < (unsigned)args.src_rows ? srow : 0;  // never taken for a consistent permutation
-      p = args.A + (size_t)srow * args.lda_bytes;
-    } else {
-      const int c = row - BM;
-      int wrow;
-      const char* base;
-      if (KIND == EPI_GLU) {
-        wrow = nt * (BN / 2) + (c >> 5) * 16 + (c & 15);
-        base = ((c & 31) >= 16) ? Wu : Wg;
-      } else {
-        wrow = nt * BN + c;
-        base = Wg;
-      }
-      if (wrow >= args.N) wrow = 0;
-      p = base + (size_t)wrow * args.ldb_bytes;
-    }
-    src.p[0][i] = p + chunk * 16;
+template <class Pp, int KIND>
+struct ExpertProb {
+  static constexpr int PARTS = 1;
+  template <int L>
+  struct SrcT {
+    const char* p[L];
+  };
+  const ExpertArgs& a;
+
+  MOE_DEV int total() const { return scalar_load(a.n_mtiles, 0) * a.NT; }
+  MOE_DEV int kt() const { return a.kt; }
+
+  MOE_DEV Tile tile(int L) const {
+    const int g = L / a.NT;
+    const int2 info = scalar_load2(a.tile_info, g);
+    Tile t;
+    t.row0 = info.x;
+    t.rows = info.y & 0xFF;
+    t.sel = info.y >> 8;
+    t.nt = L - g * a.NT;
+    return t;
   }
-  f32x4_t acc[C::MI][C::NI];
-  C::zero(acc);
-  C::template run<1>(src, acc, smem);
-  C::template epilogue<KIND>(acc, rows_valid, nt * BN, args.N, args.out, args.ldo, (size_t)row0, nullptr);
+
+  template <int L>
+  MOE_DEV void sources(const Tile& t, SrcT<L>& src) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const char* Wg = a.W + (size_t)t.sel * a.w_expert_bytes;
+    const char* Wu = a.Wu ? a.Wu + (size_t)t.sel * a.w_expert_bytes : nullptr;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int row = slot_row(i, wave, lane);
+      const int chunk = slot_chunk(row, lane);
+      const char* p;
+      if (row < Pp::BM) {  // rows past the expert's end read its first row (results not stored)
+        p = a.A + (size_t)(t.row0 + (row < t.rows ? row : 0)) * a.lda_bytes;
+      } else {
+        const int c = row - Pp::BM;
+        int wrow;
+        const char* base;
+        if (KIND == EPI_GLU) {
+          wrow = t.nt * (Pp::BN / 2) + (c >> 5) * 16 + (c & 15);
+          base = ((c & 31) >= 16) ? Wu : Wg;
+        } else {
+          wrow = t.nt * Pp::BN + c;
+          base = Wg;
+        }
+        if (wrow >= a.N) wrow = 0;
+        p = base + (size_t)wrow * a.ldb_bytes;
+      }
+      src.p[i] = p + chunk * 16;
+    }
+  }
+
+  template <int L>
+  MOE_DEV void issue(const SrcT<L>& src, int ks, uint32_t lds) const {
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      lds_dma16(src.p[i] + ks * kRowBytes, __builtin_amdgcn_readfirstlane(lds + i * 4096));
+  }
+
+  MOE_DEV void epilogue(const Tile& t, const typename Pp::Acc& acc) const {
+    Pp::template epilogue<KIND>(acc, t.rows, t.nt * Pp::BN, a.N, a.out, a.ldo, (size_t)t.row0, nullptr);
+  }
+};
+
+template <class Pp, int KIND>
+__global__ __launch_bounds__(kThreads) void k_gemm_expert(const ExpertArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
+  ExpertProb<Pp, KIND> prob{args};
+  stream<Pp>(prob, smem);
 }
 
-constexpr int kDenseBM = 128, kDenseBN = 128;
-constexpr int kExpertBN = 128;
+// Tile shapes and pipeline depths.
+template <bool BF16>
+using DensePipe = Pipe<128, 128, 2, 2, BF16>;
+template <bool BF16>
+using ExpertPipe = Pipe<kExpertBM, 256, 4, 2, BF16>;
+constexpr int kBlocksPerCU = 2;  // 2 x (2 x 32..40 KB) of LDS per CU
+constexpr int kCUs = 256;
 
 }  // namespace
 
 static int esz(const Dims& D) { return D.bf16 ? 2 : 4; }
 
+// Persistent grid: at most kBlocksPerCU blocks per CU, a multiple of 8.
+static int persistent_grid(long long tiles) {
+  long long g = (long long)kCUs * kBlocksPerCU;
+  if (tiles < g) g = (tiles + 7) / 8 * 8;
+  return (int)(g < 8 ? 8 : g);
+}
+
 template <bool BF16>
 static hipError_t launch_dense(const DenseArgs& a, hipStream_t s) {
-  const int nblocks = a.m_tiles * a.total_ntiles;
-  if (nblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_dense<kDenseBM, kDenseBN, BF16>), dim3(nblocks), dim3(kThreads), 0, s, a);
+  const long long tiles = (long long)a.m_tiles * a.total_ntiles;
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm_dense<DensePipe<BF16>>), dim3(persistent_grid(tiles)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
                          const void* W_sg, const void* W_su, const void* W_dn, float* logits, void* G, void* z,
                          hipStream_t s) {
+  constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN;
   const int es = esz(D);
   DenseArgs a{};
   a.A[0] = static_cast<const char*>(h);
@@ -407,13 +516,13 @@ hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, c
   a.kt[0] = D.d * es / kRowBytes;
   a.kt[1] = 0;
   a.M = T;
-  a.m_tiles = (T + kDenseBM - 1) / kDenseBM;
+  a.m_tiles = (T + BM - 1) / BM;
   int ns = 0;
   if (logits) {  // router logits, fp32
     DenseSeg& g = a.seg[ns++];
     g.B[0] = static_cast<const char*>(W_r);
     g.N = D.E;
-    g.ntiles = (D.E + kDenseBN - 1) / kDenseBN;
+    g.ntiles = (D.E + BN - 1) / BN;
     g.kind = EPI_F32;
     g.out = logits;
     g.ldo = D.E;
@@ -424,7 +533,7 @@ hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, c
     g.B[0] = static_cast<const char*>(W_sg);
     g.Bu[0] = static_cast<const char*>(W_su);
     g.N = D.f_s;
-    g.ntiles = (2 * D.f_s + kDenseBN - 1) / kDenseBN;
+    g.ntiles = (2 * D.f_s + BN - 1) / BN;
     g.kind = EPI_GLU;
     g.out = G;
     g.ldo = D.f_s;
@@ -433,7 +542,7 @@ hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, c
     DenseSeg& g = a.seg[ns++];
     g.B[0] = static_cast<const char*>(W_dn);
     g.N = D.l;
-    g.ntiles = (D.l + kDenseBN - 1) / kDenseBN;
+    g.ntiles = (D.l + BN - 1) / BN;
     g.kind = EPI_STORE;
     g.out = z;
     g.ldo = D.l;
@@ -447,6 +556,7 @@ hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, c
 
 hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int T, const void* W_sd,
                            const void* W_up, void* out, hipStream_t s) {
+  constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN;
   const int es = esz(D);
   DenseArgs a{};
   int p = 0;
@@ -464,9 +574,9 @@ hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int 
   a.kt[p] = D.l * es / kRowBytes;
   a.seg[0].B[p] = static_cast<const char*>(W_up);
   a.M = T;
-  a.m_tiles = (T + kDenseBM - 1) / kDenseBM;
+  a.m_tiles = (T + BM - 1) / BM;
   a.seg[0].N = D.d;
-  a.seg[0].ntiles = (D.d + kDenseBN - 1) / kDenseBN;
+  a.seg[0].ntiles = (D.d + BN - 1) / BN;
   a.seg[0].kind = EPI_STORE;
   a.seg[0].out = out;
   a.seg[0].ldo = D.d;
@@ -475,69 +585,63 @@ hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int 
   return D.bf16 ? launch_dense<true>(a, s) : launch_dense<false>(a, s);
 }
 
-static int expert_grid(const Dims& D, int T, int NT) {
-  // sum_e ceil(n_e / BM) <= T*k/BM + E (at most one partial tile per expert)
-  const long long tiles = ((long long)T * D.k + kExpertBM - 1) / kExpertBM + D.E;
-  return (int)(tiles * NT);
+int expert_max_mtiles(int T, int k, int E) {
+  // sum_e ceil(n_e / BM) <= ceil(T*k / BM) + E (at most one partial tile per expert)
+  return (int)(((long long)T * k + kExpertBM - 1) / kExpertBM + E);
 }
 
-hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_src, const int32_t* offsets,
-                            const int32_t* tile_offsets, int T, const void* W_g, const void* W_u, void* H,
-                            hipStream_t s) {
+template <int KIND>
+static hipError_t launch_expert(const Dims& D, const ExpertArgs& a, int T, hipStream_t s) {
+  const long long tiles = (long long)expert_max_mtiles(T, D.k, D.E) * a.NT;
+  if (tiles == 0) return hipSuccess;
+  const int grid = persistent_grid(tiles);
+  if (D.bf16)
+    hipLaunchKernelGGL((k_gemm_expert<ExpertPipe<true>, KIND>), dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_gemm_expert<ExpertPipe<false>, KIND>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_up(const Dims& D, const void* X, const int2* tile_info, const int32_t* n_mtiles, int T,
+                            const void* W_g, const void* W_u, void* H, hipStream_t s) {
+  constexpr int BN = ExpertPipe<true>::BN;
   const int es = esz(D);
   ExpertArgs a{};
-  a.A = static_cast<const char*>(z);
-  a.perm_src = perm_src;
-  a.src_rows = T;
+  a.A = static_cast<const char*>(X);
   a.lda_bytes = D.l * es;
   a.W = static_cast<const char*>(W_g);
   a.Wu = static_cast<const char*>(W_u);
   a.ldb_bytes = D.l * es;
   a.w_expert_bytes = (size_t)D.f * D.l * es;
   a.N = D.f;
-  a.NT = (2 * D.f + kExpertBN - 1) / kExpertBN;
+  a.NT = (2 * D.f + BN - 1) / BN;
   a.kt = D.l * es / kRowBytes;
-  a.offsets = offsets;
-  a.tile_offsets = tile_offsets;
-  a.E = D.E;
+  a.tile_info = tile_info;
+  a.n_mtiles = n_mtiles;
   a.out = H;
   a.ldo = D.f;
-  const int grid = expert_grid(D, T, a.NT);
-  if (grid == 0) return hipSuccess;
-  if (D.bf16)
-    hipLaunchKernelGGL((k_gemm_expert<kExpertBN, true, EPI_GLU>), dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_gemm_expert<kExpertBN, false, EPI_GLU>), dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_expert<EPI_GLU>(D, a, T, s);
 }
 
-hipError_t launch_expert_down(const Dims& D, const void* H, const int32_t* offsets, const int32_t* tile_offsets,
-                              int T, const void* W_d, void* Y, hipStream_t s) {
+hipError_t launch_expert_down(const Dims& D, const void* H, const int2* tile_info, const int32_t* n_mtiles, int T,
+                              const void* W_d, void* Y, hipStream_t s) {
+  constexpr int BN = ExpertPipe<true>::BN;
   const int es = esz(D);
   ExpertArgs a{};
   a.A = static_cast<const char*>(H);
-  a.perm_src = nullptr;
-  a.src_rows = T * D.k;
   a.lda_bytes = D.f * es;
   a.W = static_cast<const char*>(W_d);
   a.Wu = nullptr;
   a.ldb_bytes = D.f * es;
   a.w_expert_bytes = (size_t)D.l * D.f * es;
   a.N = D.l;
-  a.NT = (D.l + kExpertBN - 1) / kExpertBN;
+  a.NT = (D.l + BN - 1) / BN;
   a.kt = D.f * es / kRowBytes;
-  a.offsets = offsets;
-  a.tile_offsets = tile_offsets;
-  a.E = D.E;
+  a.tile_info = tile_info;
+  a.n_mtiles = n_mtiles;
   a.out = Y;
   a.ldo = D.l;
-  const int grid = expert_grid(D, T, a.NT);
-  if (grid == 0) return hipSuccess;
-  if (D.bf16)
-    hipLaunchKernelGGL((k_gemm_expert<kExpertBN, true, EPI_STORE>), dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_gemm_expert<kExpertBN, false, EPI_STORE>), dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  return launch_expert<EPI_STORE>(D, a, T, s);
 }
 
 }  // namespace moe

@@ -14,7 +14,7 @@ constexpr int kSuper = 16;
 constexpr int kHistSlices = 16;
 // Rows per tile of the grouped expert GEMMs (also the granularity of the
 // per-expert tile offsets computed by the scan).
-constexpr int kExpertBM = 128;
+constexpr int kExpertBM = 64;
 // Experts per block of the histogram kernel.
 constexpr int kHistExperts = 64;
 
@@ -29,11 +29,15 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
                        uint32_t* bitmap, hipStream_t s);
 hipError_t launch_hist(const Dims& D, const float* logits, int T, uint32_t* hist, unsigned long long* count,
                        hipStream_t s);
-// Two launches: per-super-chunk prefix, then the global prefix + offsets.
+// Two launches: per-super-chunk prefix, then the global prefix, the row and
+// m-tile offsets and the m-tile table tile_info[g] = {first row, expert << 8 |
+// rows in use} of the grouped GEMMs.
 hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cbase, int32_t* sbase, int32_t* counts,
-                       int32_t* offsets, int32_t* tile_offsets, hipStream_t s);
+                       int32_t* offsets, int32_t* tile_offsets, int2* tile_info, hipStream_t s);
+// Rows of the permutation, and the dispatch buffer X[row] = z[token].
 hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* cbase,
-                          const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s);
+                          const int32_t* sbase, int T, const void* z, int32_t* perm_src, int32_t* inv, void* X,
+                          hipStream_t s);
 hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, const int32_t* inv, int T,
                           void* y_lat, hipStream_t s);
 hipError_t launch_qb_quantile(const Dims& D, uint32_t* hist, const unsigned long long* count, double* q,
@@ -49,11 +53,12 @@ hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, c
                          void* z, hipStream_t s);
 hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int T, const void* W_sd,
                            const void* W_up, void* out, hipStream_t s);
-// Grouped expert GEMMs over the permuted rows.
-hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_src, const int32_t* offsets,
-                            const int32_t* tile_offsets, int T, const void* W_g, const void* W_u, void* H,
-                            hipStream_t s);
-hipError_t launch_expert_down(const Dims& D, const void* H, const int32_t* offsets,
-                              const int32_t* tile_offsets, int T, const void* W_d, void* Y, hipStream_t s);
+// Grouped expert GEMMs over the rows grouped by expert (m-tiles of
+// kExpertBM rows from tile_info; n_mtiles points at their count).
+int expert_max_mtiles(int T, int k, int E);
+hipError_t launch_expert_up(const Dims& D, const void* X, const int2* tile_info, const int32_t* n_mtiles, int T,
+                            const void* W_g, const void* W_u, void* H, hipStream_t s);
+hipError_t launch_expert_down(const Dims& D, const void* H, const int2* tile_info, const int32_t* n_mtiles, int T,
+                              const void* W_d, void* Y, hipStream_t s);
 
 }  // namespace moe

@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void k_scan_local(const uint32_t* __restrict__
 // kExpertBM rows; an empty expert has none).
 __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbase, int nsuper, int E,
                                                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ tile_offsets) {
+                                                      int32_t* __restrict__ tile_offsets, int2* __restrict__ tile_info) {
   __shared__ int wsum_r[16], wsum_t[16];
   const int i = threadIdx.x, lane = i & 63, w = i >> 6;
   int c = 0;
@@ -299,6 +299,9 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
       sbase[j] = run;
       run += v;
     }
+    const int row0 = r - c, tile0 = t - tl;
+    for (int j = 0; j < tl; ++j)
+      tile_info[tile0 + j] = make_int2(row0 + j * kExpertBM, (i << 8) | min(kExpertBM, c - j * kExpertBM));
   }
   if (i == 0) {
     offsets[0] = 0;
@@ -307,43 +310,62 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
 }
 
 hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cbase, int32_t* sbase, int32_t* counts,
-                       int32_t* offsets, int32_t* tile_offsets, hipStream_t s) {
+                       int32_t* offsets, int32_t* tile_offsets, int2* tile_info, hipStream_t s) {
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int nsuper = (nchunks + kSuper - 1) / kSuper;
   dim3 g1((D.E + 63) / 64, (nsuper + 3) / 4);
   hipLaunchKernelGGL(k_scan_local, g1, dim3(256), 0, s, bitmap, nchunks, D.E, cbase, sbase);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scan_global, dim3(1), dim3(1024), 0, s, sbase, nsuper, D.E, counts, offsets, tile_offsets);
+  hipLaunchKernelGGL(k_scan_global, dim3(1), dim3(1024), 0, s, sbase, nsuper, D.E, counts, offsets, tile_offsets,
+                     tile_info);
   return hipGetLastError();
 }
 
 // -------------------------------------------------------------- scatter ----
-// Stable rows without order-dependent atomics, one thread per (t, j): the row
-// of token t in expert e's group is the super-chunk base + the chunk base +
-// the number of earlier tokens of the chunk in the chunk's mask for e.
+// Stable rows without order-dependent atomics.  One wavefront per token:
+// lane j < k finds the row of (t, j) in expert e's group as the super-chunk
+// base + the chunk base + the number of earlier tokens of the chunk in the
+// chunk's mask for e; then the wavefront copies the token's latent row z[t]
+// to the dispatch buffer X at each of its k rows (coalesced 16-byte pieces).
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, const uint32_t* __restrict__ bitmap,
                                                  const int32_t* __restrict__ cbase, const int32_t* __restrict__ sbase,
-                                                 int T, int E, int k, int32_t* __restrict__ perm_src,
-                                                 int32_t* __restrict__ inv) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
+                                                 const uint4* __restrict__ z, int T, int E, int k, int row16,
+                                                 int32_t* __restrict__ perm_src, int32_t* __restrict__ inv,
+                                                 uint4* __restrict__ X) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
   const int Tk = T * k;
-  if (i >= Tk) return;
-  const int t = i / k;
-  const int e = idx[i];
-  const int c = t / kChunk;
-  const size_t ce = (size_t)c * E + e;
-  const uint32_t below = bitmap[ce] & ((1u << (t % kChunk)) - 1u);
-  const int row = sbase[(size_t)(c / kSuper) * E + e] + cbase[ce] + __popc(below);
-  if ((unsigned)row < (unsigned)Tk) perm_src[row] = t;  // always true for a consistent permutation
-  inv[i] = row;
+  int my_row = -1;
+  if (lane < k) {
+    const int e = idx[(size_t)t * k + lane];
+    const int c = t / kChunk;
+    const size_t ce = (size_t)c * E + e;
+    const uint32_t below = bitmap[ce] & ((1u << (t % kChunk)) - 1u);
+    const int row = sbase[(size_t)(c / kSuper) * E + e] + cbase[ce] + __popc(below);
+    inv[(size_t)t * k + lane] = row;
+    if ((unsigned)row < (unsigned)Tk) {  // always true for a consistent permutation
+      perm_src[row] = t;
+      my_row = row;
+    }
+  }
+  const uint4* src = z + (size_t)t * row16;
+  for (int c = lane; c < row16; c += 64) {
+    const uint4 v = src[c];
+    for (int j = 0; j < k; ++j) {
+      const int row = __builtin_amdgcn_readlane(my_row, j);
+      if (row >= 0) X[(size_t)row * row16 + c] = v;
+    }
+  }
 }
 
 hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* cbase,
-                          const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s) {
-  const long long n = (long long)T * D.k;
-  hipLaunchKernelGGL(k_scatter, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, bitmap, cbase, sbase, T,
-                     D.E, D.k, perm_src, inv);
+                          const int32_t* sbase, int T, const void* z, int32_t* perm_src, int32_t* inv, void* X,
+                          hipStream_t s) {
+  const int row16 = (z && X) ? D.l * (D.bf16 ? 2 : 4) / 16 : 0;  // routing only: no dispatch copy
+  hipLaunchKernelGGL(k_scatter, dim3((T + 3) / 4), dim3(256), 0, s, idx, bitmap, cbase, sbase,
+                     static_cast<const uint4*>(z), T, D.E, D.k, row16, perm_src, inv, static_cast<uint4*>(X));
   return hipGetLastError();
 }
 
