@@ -120,6 +120,8 @@ def main() -> int:
                     help="replay the step as a captured HIP graph (per-kernel times then come from an extra "
                          "eager pass after the timed region)")
     ap.add_argument("--no-profile", action="store_true", help="no per-kernel events in the timed region")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain device copy of 256 MiB (the reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the layer is built and measured per GPU); --gpus {args.gpus} "
@@ -147,6 +149,13 @@ def main() -> int:
     x = torch.from_numpy(x_np).cuda().to(layer.tdtype)
     out = torch.empty(T, shape.d, dtype=layer.tdtype, device="cuda")
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         layer.forward(x, out=out)

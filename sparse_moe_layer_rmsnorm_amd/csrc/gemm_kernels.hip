@@ -38,7 +38,6 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kRowBytes = 128;  // K bytes per stage
 
 enum EpiKind { EPI_F32 = 0, EPI_STORE = 1, EPI_GLU = 2 };
@@ -96,24 +95,25 @@ MOE_DEV int scalar_load(const int32_t* p, int i) {
 }
 
 // Stage filling: a stage is BM + BN rows of 128 bytes (A rows, then B rows),
-// written by 1 KB DMA slots; thread (wave w, lane) fills slots i*4 + w, i < L.
-// The tile row and the logical 16-byte K chunk that a lane's piece of slot i
-// holds (the LDS chunk position is lane%8, XOR-swizzled by row):
-MOE_DEV int slot_row(int i, int wave, int lane) { return (i * 4 + wave) * 8 + (lane >> 3); }
+// written by 1 KB DMA slots; thread (wave w of NW, lane) fills slots i*NW + w,
+// i < L.  The tile row and the logical 16-byte K chunk that a lane's piece of
+// slot i holds (the LDS chunk position is lane%8, XOR-swizzled by row):
+template <int NW>
+MOE_DEV int slot_row(int i, int wave, int lane) { return (i * NW + wave) * 8 + (lane >> 3); }
 MOE_DEV int slot_chunk(int row, int lane) { return (lane & 7) ^ ((row & 7) ^ ((row >> 3) & 1)); }
 
-// Block tile BM x BN over 4 wavefronts laid out (4/WN) x WN; NS LDS stages.
-template <int BM_, int BN_, int WN, int NS_, bool BF16>
+// Block tile BM x BN over WM x WN wavefronts; NS LDS stages.
+template <int BM_, int BN_, int WM_, int WN_, int NS_, bool BF16>
 struct Pipe {
   static constexpr int BM = BM_, BN = BN_, NS = NS_;
-  static constexpr int WM = 4 / WN;
+  static constexpr int WM = WM_, WN = WN_, NW = WM * WN, THREADS = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int MI = WTM / 16, NI = WTN / 16;
   static constexpr int A_BYTES = BM * kRowBytes;
   static constexpr int STAGE = (BM + BN) * kRowBytes;
   static constexpr int LDS = NS * STAGE;
-  static constexpr int L = STAGE / 1024 / 4;  // DMA slots per thread per stage
-  static_assert(STAGE % 4096 == 0, "stage must split into 1 KB slots over 4 wavefronts");
+  static constexpr int L = STAGE / 1024 / NW;  // DMA slots per thread per stage
+  static_assert(STAGE % (1024 * NW) == 0, "stage must split into 1 KB slots over the wavefronts");
   static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
   using Acc = f32x4_t[MI][NI];
 
@@ -332,7 +332,7 @@ struct DenseProb {
     for (int part = 0; part < 2; ++part) {
 #pragma unroll
       for (int i = 0; i < L; ++i) {
-        const int row = slot_row(i, wave, lane);
+        const int row = slot_row<Pp::NW>(i, wave, lane);
         const int chunk = slot_chunk(row, lane);
         const char* p;
         if (row < Pp::BM) {  // A row (rows past the end read row0: their results are not stored)
@@ -363,7 +363,7 @@ struct DenseProb {
     const int off = (second ? ks - a.kt[0] : ks) * kRowBytes;
 #pragma unroll
     for (int i = 0; i < L; ++i)
-      lds_dma16((second ? src.p[1][i] : src.p[0][i]) + off, __builtin_amdgcn_readfirstlane(lds + i * 4096));
+      lds_dma16((second ? src.p[1][i] : src.p[0][i]) + off, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
   }
 
   MOE_DEV void epilogue(const Tile& t, const typename Pp::Acc& acc) const {
@@ -378,7 +378,7 @@ struct DenseProb {
 };
 
 template <class Pp>
-__global__ __launch_bounds__(kThreads) void k_gemm_dense(const DenseArgs args) {
+__global__ __launch_bounds__(Pp::THREADS) void k_gemm_dense(const DenseArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
   DenseProb<Pp> prob{args};
   stream<Pp>(prob, smem);
@@ -435,7 +435,7 @@ struct ExpertProb {
     const char* Wu = a.Wu ? a.Wu + (size_t)t.sel * a.w_expert_bytes : nullptr;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      const int row = slot_row(i, wave, lane);
+      const int row = slot_row<Pp::NW>(i, wave, lane);
       const int chunk = slot_chunk(row, lane);
       const char* p;
       if (row < Pp::BM) {  // rows past the expert's end read its first row (results not stored)
@@ -462,7 +462,7 @@ struct ExpertProb {
   MOE_DEV void issue(const SrcT<L>& src, int ks, uint32_t lds) const {
 #pragma unroll
     for (int i = 0; i < L; ++i)
-      lds_dma16(src.p[i] + ks * kRowBytes, __builtin_amdgcn_readfirstlane(lds + i * 4096));
+      lds_dma16(src.p[i] + ks * kRowBytes, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
   }
 
   MOE_DEV void epilogue(const Tile& t, const typename Pp::Acc& acc) const {
@@ -471,27 +471,44 @@ struct ExpertProb {
 };
 
 template <class Pp, int KIND>
-__global__ __launch_bounds__(kThreads) void k_gemm_expert(const ExpertArgs args) {
+__global__ __launch_bounds__(Pp::THREADS) void k_gemm_expert(const ExpertArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
   ExpertProb<Pp, KIND> prob{args};
   stream<Pp>(prob, smem);
 }
 
 // Tile shapes and pipeline depths.
+#ifndef MOE_DENSE_NS
+#define MOE_DENSE_NS 2
+#endif
+#ifndef MOE_EXPERT_NS
+#define MOE_EXPERT_NS 2
+#endif
+#ifndef MOE_DENSE_BPC
+#define MOE_DENSE_BPC 2
+#endif
+#ifndef MOE_EXPERT_BPC
+#define MOE_EXPERT_BPC 2
+#endif
+#ifndef MOE_DENSE_TILE
+#define MOE_DENSE_TILE 128, 128, 2, 2
+#endif
+#ifndef MOE_EXPERT_TILE
+#define MOE_EXPERT_TILE kExpertBM, 256, 1, 4
+#endif
 template <bool BF16>
-using DensePipe = Pipe<128, 128, 2, 2, BF16>;
+using DensePipe = Pipe<MOE_DENSE_TILE, MOE_DENSE_NS, BF16>;
 template <bool BF16>
-using ExpertPipe = Pipe<kExpertBM, 256, 4, 2, BF16>;
-constexpr int kBlocksPerCU = 2;  // 2 x (2 x 32..40 KB) of LDS per CU
+using ExpertPipe = Pipe<MOE_EXPERT_TILE, MOE_EXPERT_NS, BF16>;
 constexpr int kCUs = 256;
 
 }  // namespace
 
 static int esz(const Dims& D) { return D.bf16 ? 2 : 4; }
 
-// Persistent grid: at most kBlocksPerCU blocks per CU, a multiple of 8.
-static int persistent_grid(long long tiles) {
-  long long g = (long long)kCUs * kBlocksPerCU;
+// Persistent grid: at most bpc blocks per CU, a multiple of 8.
+static int persistent_grid(long long tiles, int bpc) {
+  long long g = (long long)kCUs * bpc;
   if (tiles < g) g = (tiles + 7) / 8 * 8;
   return (int)(g < 8 ? 8 : g);
 }
@@ -500,7 +517,8 @@ template <bool BF16>
 static hipError_t launch_dense(const DenseArgs& a, hipStream_t s) {
   const long long tiles = (long long)a.m_tiles * a.total_ntiles;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_dense<DensePipe<BF16>>), dim3(persistent_grid(tiles)), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k_gemm_dense<DensePipe<BF16>>), dim3(persistent_grid(tiles, MOE_DENSE_BPC)),
+                     dim3(DensePipe<BF16>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -594,11 +612,11 @@ template <int KIND>
 static hipError_t launch_expert(const Dims& D, const ExpertArgs& a, int T, hipStream_t s) {
   const long long tiles = (long long)expert_max_mtiles(T, D.k, D.E) * a.NT;
   if (tiles == 0) return hipSuccess;
-  const int grid = persistent_grid(tiles);
+  const int grid = persistent_grid(tiles, MOE_EXPERT_BPC);
   if (D.bf16)
-    hipLaunchKernelGGL((k_gemm_expert<ExpertPipe<true>, KIND>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_expert<ExpertPipe<true>, KIND>), dim3(grid), dim3(ExpertPipe<true>::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemm_expert<ExpertPipe<false>, KIND>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_expert<ExpertPipe<false>, KIND>), dim3(grid), dim3(ExpertPipe<false>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

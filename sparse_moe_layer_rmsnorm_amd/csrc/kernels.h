@@ -14,7 +14,10 @@ constexpr int kSuper = 16;
 constexpr int kHistSlices = 16;
 // Rows per tile of the grouped expert GEMMs (also the granularity of the
 // per-expert tile offsets computed by the scan).
-constexpr int kExpertBM = 64;
+#ifndef MOE_EXPERT_BM
+#define MOE_EXPERT_BM 64
+#endif
+constexpr int kExpertBM = MOE_EXPERT_BM;
 // Experts per block of the histogram kernel.
 constexpr int kHistExperts = 64;
 
