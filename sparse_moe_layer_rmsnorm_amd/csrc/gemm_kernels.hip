@@ -30,22 +30,19 @@
 // MFMA: bf16 v_mfma_f32_16x16x32_bf16; fp32 four v_mfma_f32_16x16x4_f32 per
 // 16-byte fragment.  The weight fragment is the MFMA's first operand, so each
 // lane's accumulators hold 4 consecutive output columns of one row.  LDS rows
-// are 128 bytes with 16-byte chunks XOR-swizzled by row, so the 16 rows a
-// fragment read touches fall in distinct banks.
+// are 128 bytes; 16-byte chunk c of row r sits at position c ^ (r % 8).  A
+// ds_read_b128 is served 16 lanes per LDS cycle (64 banks of 4 bytes) in lane
+// groups that are not 16 consecutive lanes (measured: the variant that also
+// flips chunk bit 0 for rows 8..15 costs twice the cycles); with this
+// placement each group of a fragment read hits 16 distinct 16-byte bank slots.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int kRowBytes = 128;  // K bytes per stage
-
 enum EpiKind { EPI_F32 = 0, EPI_STORE = 1, EPI_GLU = 2 };
 
-MOE_DEV int lds_off(int row, int chunk) {
-  const int sw = (row & 7) ^ ((row >> 3) & 1);
-  return row * kRowBytes + ((chunk ^ sw) << 4);
-}
 
 template <bool BF16>
 MOE_DEV void mfma_chunk(f32x4_t& acc, const uint4& w, const uint4& a) {
@@ -74,6 +71,7 @@ MOE_DEV void lds_dma16(const char* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
 }
 
+
 // Wait until at most N vector-memory operations of this wavefront are
 // outstanding.  Loads complete in issue order, so with N = the number of DMA
 // loads issued after a stage, that stage has landed in LDS (stores still in
@@ -94,47 +92,79 @@ MOE_DEV int scalar_load(const int32_t* p, int i) {
   return *((const __attribute__((address_space(4))) int32_t*)p + i);
 }
 
-// Stage filling: a stage is BM + BN rows of 128 bytes (A rows, then B rows),
-// written by 1 KB DMA slots; thread (wave w of NW, lane) fills slots i*NW + w,
-// i < L.  The tile row and the logical 16-byte K chunk that a lane's piece of
-// slot i holds (the LDS chunk position is lane%8, XOR-swizzled by row):
-template <int NW>
-MOE_DEV int slot_row(int i, int wave, int lane) { return (i * NW + wave) * 8 + (lane >> 3); }
-MOE_DEV int slot_chunk(int row, int lane) { return (lane & 7) ^ ((row & 7) ^ ((row >> 3) & 1)); }
+// A wave-uniform pointer read into scalar registers.  Per-lane choices
+// between two kernel-argument pointers are made on these values, so the
+// compiler cannot turn them into a vector load through a per-lane argument
+// address (such a load would need a wait on every DMA load in flight).
+MOE_DEV const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+MOE_DEV int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Block tile BM x BN over WM x WN wavefronts; NS LDS stages.
-template <int BM_, int BN_, int WM_, int WN_, int NS_, bool BF16>
+// Block tile BM x BN over WM x WN wavefronts, NS LDS stages of RB K-bytes
+// per row (64 or 128), BPC blocks per CU.
+//
+// LDS layout of a stage: BM + BN rows of RB bytes (A rows, then weight rows).
+// 16-byte chunk c of row r sits at chunk position c ^ sw(r): sw = r % 8 for
+// 128-byte rows, (r / 2) % 4 for 64-byte rows.  A ds_read_b128 is served 16
+// lanes per LDS cycle (64 banks of 4 bytes) in lane groups that are not 16
+// consecutive lanes (measured: placing rows 8..15 with chunk bit 0 flipped
+// costs twice the cycles); with these placements the 16 lanes of a group that
+// read one fragment (16 rows, one logical chunk) hit 16 distinct bank slots.
+//
+// Stage filling: 1 KB DMA slots (RB = 128: 8 rows of 8 chunks; RB = 64: 16
+// rows of 4 chunks); thread (wave w of NW, lane) fills slots i*NW + w, i < L,
+// lane l writing chunk position l % (RB/16) of its row, i.e. logical chunk
+// (l % (RB/16)) ^ sw(row).
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int RB_, int BPC_, bool BF16>
 struct Pipe {
-  static constexpr int BM = BM_, BN = BN_, NS = NS_;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, RB = RB_, BPC = BPC_;
   static constexpr int WM = WM_, WN = WN_, NW = WM * WN, THREADS = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int MI = WTM / 16, NI = WTN / 16;
-  static constexpr int A_BYTES = BM * kRowBytes;
-  static constexpr int STAGE = (BM + BN) * kRowBytes;
+  static constexpr int KK = RB / 64;                 // 64-byte K steps (one MFMA K each) per stage
+  static constexpr int CPR = RB / 16;                // 16-byte chunks per row
+  static constexpr int A_BYTES = BM * RB;
+  static constexpr int STAGE = (BM + BN) * RB;
   static constexpr int LDS = NS * STAGE;
   static constexpr int L = STAGE / 1024 / NW;  // DMA slots per thread per stage
+  static_assert(RB == 64 || RB == 128, "64- or 128-byte stage rows");
   static_assert(STAGE % (1024 * NW) == 0, "stage must split into 1 KB slots over the wavefronts");
   static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+  static_assert(LDS * BPC <= 160 * 1024, "LDS per CU");
   using Acc = f32x4_t[MI][NI];
 
+  MOE_DEV static int swz(int row) { return RB == 128 ? (row & 7) : ((row >> 1) & 3); }
+  MOE_DEV static int lds_off(int row, int chunk) { return row * RB + ((chunk ^ swz(row)) << 4); }
+  MOE_DEV static int slot_row(int i, int wave, int lane) { return (i * NW + wave) * (1024 / RB) + lane / CPR; }
+  MOE_DEV static int slot_chunk(int row, int lane) { return (lane % CPR) ^ swz(row); }
+
+  // All fragment reads of the stage are issued before the first MFMA, so
+  // the wavefront waits for LDS once per stage rather than once per group.
   MOE_DEV static void compute(const char* cur, Acc& acc) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
+    uint4 af[KK][MI], wf[KK][NI];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
-      uint4 af[MI], wf[NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        af[mi] = *reinterpret_cast<const uint4*>(cur + lds_off(wm * WTM + mi * 16 + (lane & 15), ch));
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        wf[ni] = *reinterpret_cast<const uint4*>(cur + A_BYTES + lds_off(wn * WTN + ni * 16 + (lane & 15), ch));
+        wf[kk][ni] = *reinterpret_cast<const uint4*>(cur + A_BYTES + lds_off(wn * WTN + ni * 16 + (lane & 15), ch));
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        af[kk][mi] = *reinterpret_cast<const uint4*>(cur + lds_off(wm * WTM + mi * 16 + (lane & 15), ch));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) mfma_chunk<BF16>(acc[mi][ni], wf[ni], af[mi]);
-    }
+        for (int ni = 0; ni < NI; ++ni) mfma_chunk<BF16>(acc[mi][ni], wf[kk][ni], af[kk][mi]);
   }
 
   MOE_DEV static void zero(Acc& acc) {
@@ -162,13 +192,13 @@ struct Pipe {
 
   // Epilogues.  Lane holds rows m = wm*WTM + mi*16 + lane%16 and columns
   // n = wn*WTN + ni*16 + 4*(lane/16) + r (r = 0..3) of the block tile.
-  //   EPI_F32:   fp32 store (+ per-column offset), columns < N only.
+  //   EPI_F32:   fp32 store (+ per-column offset, read from LDS), columns < N only.
   //   EPI_STORE: store in the activation dtype (N a multiple of 4).
   //   EPI_GLU:   tile columns alternate 16 gate / 16 up; output column
   //              n0/2 + 16*(c/32) + c%16 gets silu(gate) * up.
   template <int KIND>
   MOE_DEV static void epilogue(const Acc& acc, int rows_valid, int n0, int N, void* out, int ldo, size_t row_base,
-                               const float* col_off) {
+                               const __attribute__((address_space(3))) float* col_off) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
 #pragma unroll
@@ -184,7 +214,7 @@ struct Pipe {
           if (c >= N) continue;
           float o[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = g[r] / (1.0f + __expf(-g[r])) * u[r];
+          for (int r = 0; r < 4; ++r) o[r] = g[r] * u[r] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[r]));
           store4(out, orow + c, o[0], o[1], o[2], o[3]);
         }
       } else {
@@ -272,8 +302,10 @@ struct DenseSeg {
   int kind;
   void* out;
   int ldo;
-  const float* col_off;
+  const float* col_off;  // per-column offset (EPI_F32), at most kMaxColOff columns
 };
+
+constexpr int kMaxColOff = 1024;
 
 struct DenseArgs {
   const char* A[2];
@@ -295,6 +327,7 @@ struct DenseProb {
     const char* p[2][L];
   };
   const DenseArgs& a;
+  const __attribute__((address_space(3))) float* col_lds;  // copy of the EPI_F32 segment's col_off
 
   MOE_DEV int total() const { return a.m_tiles * a.total_ntiles; }
   MOE_DEV int kt() const { return a.kt[0] + a.kt[1]; }
@@ -324,6 +357,27 @@ struct DenseProb {
     return t;
   }
 
+  // Start of stage row `row` (A rows first, then weight rows) of K part `part`.
+  MOE_DEV const char* row_ptr(const Tile& t, const DenseSeg& S, int part, int row) const {
+    if (row < Pp::BM) {  // A row (rows past the end read row0: their results are not stored)
+      const int r = row < t.rows ? row : 0;
+      return uniform_ptr(a.A[part]) + (size_t)(t.row0 + r) * uniform_int(a.lda_bytes[part]);
+    }
+    const int c = row - Pp::BM;  // weight row of tile column c (columns past N read row 0)
+    const char* gate = uniform_ptr(S.B[part]);
+    int wrow;
+    const char* base;
+    if (S.kind == EPI_GLU) {
+      wrow = t.nt * (Pp::BN / 2) + (c >> 5) * 16 + (c & 15);
+      base = ((c & 31) >= 16) ? uniform_ptr(S.Bu[part]) : gate;
+    } else {
+      wrow = t.nt * Pp::BN + c;
+      base = gate;
+    }
+    if (wrow >= uniform_int(S.N)) wrow = 0;
+    return base + (size_t)wrow * uniform_int(a.ldb_bytes[part]);
+  }
+
   template <int L>
   MOE_DEV void sources(const Tile& t, SrcT<L>& src) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -332,27 +386,8 @@ struct DenseProb {
     for (int part = 0; part < 2; ++part) {
 #pragma unroll
       for (int i = 0; i < L; ++i) {
-        const int row = slot_row<Pp::NW>(i, wave, lane);
-        const int chunk = slot_chunk(row, lane);
-        const char* p;
-        if (row < Pp::BM) {  // A row (rows past the end read row0: their results are not stored)
-          const int r = row < t.rows ? row : 0;
-          p = a.A[part] + (size_t)(t.row0 + r) * a.lda_bytes[part];
-        } else {  // weight row of tile column c (columns past N read row 0)
-          const int c = row - Pp::BM;
-          int wrow;
-          const char* base;
-          if (S.kind == EPI_GLU) {
-            wrow = t.nt * (Pp::BN / 2) + (c >> 5) * 16 + (c & 15);
-            base = ((c & 31) >= 16) ? S.Bu[part] : S.B[part];
-          } else {
-            wrow = t.nt * Pp::BN + c;
-            base = S.B[part];
-          }
-          if (wrow >= S.N) wrow = 0;
-          p = base + (size_t)wrow * a.ldb_bytes[part];
-        }
-        src.p[part][i] = a.kt[part] > 0 ? p + chunk * 16 : nullptr;
+        const int row = Pp::slot_row(i, wave, lane);
+        src.p[part][i] = a.kt[part] > 0 ? row_ptr(t, S, part, row) + Pp::slot_chunk(row, lane) * 16 : nullptr;
       }
     }
   }
@@ -360,16 +395,18 @@ struct DenseProb {
   template <int L>
   MOE_DEV void issue(const SrcT<L>& src, int ks, uint32_t lds) const {
     const bool second = ks >= a.kt[0];
-    const int off = (second ? ks - a.kt[0] : ks) * kRowBytes;
+    const int off = (second ? ks - a.kt[0] : ks) * Pp::RB;
 #pragma unroll
     for (int i = 0; i < L; ++i)
       lds_dma16((second ? src.p[1][i] : src.p[0][i]) + off, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
   }
 
+
   MOE_DEV void epilogue(const Tile& t, const typename Pp::Acc& acc) const {
     const DenseSeg& S = seg(t.sel);
     if (S.kind == EPI_F32)
-      Pp::template epilogue<EPI_F32>(acc, t.rows, t.nt * Pp::BN, S.N, S.out, S.ldo, (size_t)t.row0, S.col_off);
+      Pp::template epilogue<EPI_F32>(acc, t.rows, t.nt * Pp::BN, S.N, S.out, S.ldo, (size_t)t.row0,
+                                     S.col_off ? col_lds : nullptr);
     else if (S.kind == EPI_GLU)
       Pp::template epilogue<EPI_GLU>(acc, t.rows, t.nt * Pp::BN, S.N, S.out, S.ldo, (size_t)t.row0, nullptr);
     else
@@ -378,9 +415,18 @@ struct DenseProb {
 };
 
 template <class Pp>
-__global__ __launch_bounds__(Pp::THREADS) void k_gemm_dense(const DenseArgs args) {
+__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_dense(const DenseArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
-  DenseProb<Pp> prob{args};
+  // Per-column offsets go through LDS: a vector load in the epilogue would
+  // have to wait for every stage DMA in flight.  Copied before the first DMA.
+  __shared__ float col_lds[kMaxColOff];
+  for (int s = 0; s < args.nseg; ++s) {
+    const DenseSeg& S = s == 0 ? args.seg[0] : (s == 1 ? args.seg[1] : args.seg[2]);
+    if (S.kind == EPI_F32 && S.col_off)
+      for (int i = threadIdx.x; i < S.N; i += Pp::THREADS) col_lds[i] = S.col_off[i];
+  }
+  __syncthreads();
+  DenseProb<Pp> prob{args, (const __attribute__((address_space(3))) float*)col_lds};
   stream<Pp>(prob, smem);
 }
 
@@ -428,41 +474,41 @@ struct ExpertProb {
     return t;
   }
 
+  // Start of stage row `row` (A rows first, then weight rows).
+  MOE_DEV const char* row_ptr(const Tile& t, int row) const {
+    if (row < Pp::BM)  // rows past the expert's end read its first row (results not stored)
+      return uniform_ptr(a.A) + (size_t)(t.row0 + (row < t.rows ? row : 0)) * uniform_int(a.lda_bytes);
+    const int c = row - Pp::BM;
+    const char* gate = uniform_ptr(a.W);
+    int wrow;
+    const char* base;
+    if (KIND == EPI_GLU) {
+      wrow = t.nt * (Pp::BN / 2) + (c >> 5) * 16 + (c & 15);
+      base = ((c & 31) >= 16) ? uniform_ptr(a.Wu) : gate;
+    } else {
+      wrow = t.nt * Pp::BN + c;
+      base = gate;
+    }
+    if (wrow >= uniform_int(a.N)) wrow = 0;
+    return base + (size_t)t.sel * a.w_expert_bytes + (size_t)wrow * uniform_int(a.ldb_bytes);
+  }
+
   template <int L>
   MOE_DEV void sources(const Tile& t, SrcT<L>& src) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const char* Wg = a.W + (size_t)t.sel * a.w_expert_bytes;
-    const char* Wu = a.Wu ? a.Wu + (size_t)t.sel * a.w_expert_bytes : nullptr;
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      const int row = slot_row<Pp::NW>(i, wave, lane);
-      const int chunk = slot_chunk(row, lane);
-      const char* p;
-      if (row < Pp::BM) {  // rows past the expert's end read its first row (results not stored)
-        p = a.A + (size_t)(t.row0 + (row < t.rows ? row : 0)) * a.lda_bytes;
-      } else {
-        const int c = row - Pp::BM;
-        int wrow;
-        const char* base;
-        if (KIND == EPI_GLU) {
-          wrow = t.nt * (Pp::BN / 2) + (c >> 5) * 16 + (c & 15);
-          base = ((c & 31) >= 16) ? Wu : Wg;
-        } else {
-          wrow = t.nt * Pp::BN + c;
-          base = Wg;
-        }
-        if (wrow >= a.N) wrow = 0;
-        p = base + (size_t)wrow * a.ldb_bytes;
-      }
-      src.p[i] = p + chunk * 16;
+      const int row = Pp::slot_row(i, wave, lane);
+      src.p[i] = row_ptr(t, row) + Pp::slot_chunk(row, lane) * 16;
     }
   }
+
 
   template <int L>
   MOE_DEV void issue(const SrcT<L>& src, int ks, uint32_t lds) const {
 #pragma unroll
     for (int i = 0; i < L; ++i)
-      lds_dma16(src.p[i] + ks * kRowBytes, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
+      lds_dma16(src.p[i] + ks * Pp::RB, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
   }
 
   MOE_DEV void epilogue(const Tile& t, const typename Pp::Acc& acc) const {
@@ -471,35 +517,23 @@ struct ExpertProb {
 };
 
 template <class Pp, int KIND>
-__global__ __launch_bounds__(Pp::THREADS) void k_gemm_expert(const ExpertArgs args) {
+__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expert(const ExpertArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
   ExpertProb<Pp, KIND> prob{args};
   stream<Pp>(prob, smem);
 }
 
-// Tile shapes and pipeline depths.
-#ifndef MOE_DENSE_NS
-#define MOE_DENSE_NS 2
+// Tile shapes and pipeline depths: BM, BN, WM, WN, NS, RB, BPC.
+#ifndef MOE_DENSE_CFG
+#define MOE_DENSE_CFG 128, 128, 2, 2, 2, 128, 2
 #endif
-#ifndef MOE_EXPERT_NS
-#define MOE_EXPERT_NS 2
-#endif
-#ifndef MOE_DENSE_BPC
-#define MOE_DENSE_BPC 2
-#endif
-#ifndef MOE_EXPERT_BPC
-#define MOE_EXPERT_BPC 2
-#endif
-#ifndef MOE_DENSE_TILE
-#define MOE_DENSE_TILE 128, 128, 2, 2
-#endif
-#ifndef MOE_EXPERT_TILE
-#define MOE_EXPERT_TILE kExpertBM, 256, 1, 4
+#ifndef MOE_EXPERT_CFG
+#define MOE_EXPERT_CFG kExpertBM, 256, 1, 4, 2, 128, 2
 #endif
 template <bool BF16>
-using DensePipe = Pipe<MOE_DENSE_TILE, MOE_DENSE_NS, BF16>;
+using DensePipe = Pipe<MOE_DENSE_CFG, BF16>;
 template <bool BF16>
-using ExpertPipe = Pipe<MOE_EXPERT_TILE, MOE_EXPERT_NS, BF16>;
+using ExpertPipe = Pipe<MOE_EXPERT_CFG, BF16>;
 constexpr int kCUs = 256;
 
 }  // namespace
@@ -517,7 +551,7 @@ template <bool BF16>
 static hipError_t launch_dense(const DenseArgs& a, hipStream_t s) {
   const long long tiles = (long long)a.m_tiles * a.total_ntiles;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_dense<DensePipe<BF16>>), dim3(persistent_grid(tiles, MOE_DENSE_BPC)),
+  hipLaunchKernelGGL((k_gemm_dense<DensePipe<BF16>>), dim3(persistent_grid(tiles, DensePipe<BF16>::BPC)),
                      dim3(DensePipe<BF16>::THREADS), 0, s, a);
   return hipGetLastError();
 }
@@ -525,18 +559,19 @@ static hipError_t launch_dense(const DenseArgs& a, hipStream_t s) {
 hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
                          const void* W_sg, const void* W_su, const void* W_dn, float* logits, void* G, void* z,
                          hipStream_t s) {
-  constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN;
+  constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN, RB = DensePipe<true>::RB;
   const int es = esz(D);
   DenseArgs a{};
   a.A[0] = static_cast<const char*>(h);
   a.lda_bytes[0] = D.d * es;
   a.ldb_bytes[0] = D.d * es;
-  a.kt[0] = D.d * es / kRowBytes;
+  a.kt[0] = D.d * es / RB;
   a.kt[1] = 0;
   a.M = T;
   a.m_tiles = (T + BM - 1) / BM;
   int ns = 0;
   if (logits) {  // router logits, fp32
+    if (logit_offset && D.E > kMaxColOff) return hipErrorInvalidValue;
     DenseSeg& g = a.seg[ns++];
     g.B[0] = static_cast<const char*>(W_r);
     g.N = D.E;
@@ -574,7 +609,7 @@ hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, c
 
 hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int T, const void* W_sd,
                            const void* W_up, void* out, hipStream_t s) {
-  constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN;
+  constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN, RB = DensePipe<true>::RB;
   const int es = esz(D);
   DenseArgs a{};
   int p = 0;
@@ -582,14 +617,14 @@ hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int 
     a.A[p] = static_cast<const char*>(G);
     a.lda_bytes[p] = D.f_s * es;
     a.ldb_bytes[p] = D.f_s * es;
-    a.kt[p] = D.f_s * es / kRowBytes;
+    a.kt[p] = D.f_s * es / RB;
     a.seg[0].B[p] = static_cast<const char*>(W_sd);
     ++p;
   }
   a.A[p] = static_cast<const char*>(y_lat);
   a.lda_bytes[p] = D.l * es;
   a.ldb_bytes[p] = D.l * es;
-  a.kt[p] = D.l * es / kRowBytes;
+  a.kt[p] = D.l * es / RB;
   a.seg[0].B[p] = static_cast<const char*>(W_up);
   a.M = T;
   a.m_tiles = (T + BM - 1) / BM;
@@ -612,7 +647,7 @@ template <int KIND>
 static hipError_t launch_expert(const Dims& D, const ExpertArgs& a, int T, hipStream_t s) {
   const long long tiles = (long long)expert_max_mtiles(T, D.k, D.E) * a.NT;
   if (tiles == 0) return hipSuccess;
-  const int grid = persistent_grid(tiles, MOE_EXPERT_BPC);
+  const int grid = persistent_grid(tiles, ExpertPipe<true>::BPC);
   if (D.bf16)
     hipLaunchKernelGGL((k_gemm_expert<ExpertPipe<true>, KIND>), dim3(grid), dim3(ExpertPipe<true>::THREADS), 0, s, a);
   else
@@ -622,7 +657,7 @@ static hipError_t launch_expert(const Dims& D, const ExpertArgs& a, int T, hipSt
 
 hipError_t launch_expert_up(const Dims& D, const void* X, const int2* tile_info, const int32_t* n_mtiles, int T,
                             const void* W_g, const void* W_u, void* H, hipStream_t s) {
-  constexpr int BN = ExpertPipe<true>::BN;
+  constexpr int BN = ExpertPipe<true>::BN, RB = ExpertPipe<true>::RB;
   const int es = esz(D);
   ExpertArgs a{};
   a.A = static_cast<const char*>(X);
@@ -633,7 +668,7 @@ hipError_t launch_expert_up(const Dims& D, const void* X, const int2* tile_info,
   a.w_expert_bytes = (size_t)D.f * D.l * es;
   a.N = D.f;
   a.NT = (2 * D.f + BN - 1) / BN;
-  a.kt = D.l * es / kRowBytes;
+  a.kt = D.l * es / RB;
   a.tile_info = tile_info;
   a.n_mtiles = n_mtiles;
   a.out = H;
@@ -643,7 +678,7 @@ hipError_t launch_expert_up(const Dims& D, const void* X, const int2* tile_info,
 
 hipError_t launch_expert_down(const Dims& D, const void* H, const int2* tile_info, const int32_t* n_mtiles, int T,
                               const void* W_d, void* Y, hipStream_t s) {
-  constexpr int BN = ExpertPipe<true>::BN;
+  constexpr int BN = ExpertPipe<true>::BN, RB = ExpertPipe<true>::RB;
   const int es = esz(D);
   ExpertArgs a{};
   a.A = static_cast<const char*>(H);
@@ -654,7 +689,7 @@ hipError_t launch_expert_down(const Dims& D, const void* H, const int2* tile_inf
   a.w_expert_bytes = (size_t)D.l * D.f * es;
   a.N = D.l;
   a.NT = (D.l + BN - 1) / BN;
-  a.kt = D.f * es / kRowBytes;
+  a.kt = D.f * es / RB;
   a.tile_info = tile_info;
   a.n_mtiles = n_mtiles;
   a.out = Y;

@@ -1,0 +1,140 @@
+"""Summaries of rocprofv3 output for the layer's kernels (text for profiles/).
+
+    python -m sparse_moe_layer_rmsnorm_amd.profsum trace <kernel_trace.csv> <workload> "<command>"
+    python -m sparse_moe_layer_rmsnorm_amd.profsum traffic <fetch.csv> <write.csv> <workload> "<command>"
+
+`trace` prints a markdown table of per-kernel launch counts and durations
+from a `--kernel-trace` CSV.  `traffic` reads two `--pmc FETCH_SIZE` and
+`--pmc WRITE_SIZE` counter CSVs of the same command, scales each counter by
+what it reads for the plain 256 MiB device copy that `bench.py
+--copy-calibration` runs first, and prints a markdown table plus the JSON
+record (HBM bytes per launch per kernel) that bench.py reports as
+`roofline.traffic`.
+
+The two dense GEMM launches of a step share one kernel symbol: the first of
+each step is gemm_h, the second gemm_out.  The grouped expert GEMM with the
+GLU epilogue is expert_up, the other expert_down.
+"""
+from __future__ import annotations
+
+import csv
+import json
+import sys
+from collections import OrderedDict, defaultdict
+
+COPY_BYTES = 256 << 20
+
+
+def logical_name(symbol: str, dense_seen: int) -> str | None:
+    if "k_gemm_dense" in symbol:
+        return "gemm_h" if dense_seen % 2 == 0 else "gemm_out"
+    if "k_gemm_expert" in symbol:
+        return "expert_up" if symbol.rstrip().endswith("2>(moe::(anonymous namespace)::ExpertArgs)") else "expert_down"
+    for k in ("rmsnorm", "topk", "hist", "scan_local", "scan_global", "scatter", "combine", "qb_quantile",
+              "qb_bias", "zero"):
+        if f"k_{k}" in symbol:
+            return k
+    if "rocclr_copyBuffer" in symbol:
+        return "copy"
+    return None
+
+
+def _label(rows):
+    """rows: (dispatch id, symbol, ...) in dispatch order -> list of logical names."""
+    out, dense = [], 0
+    for r in rows:
+        name = logical_name(r[1], dense)
+        if name in ("gemm_h", "gemm_out"):
+            dense += 1
+        out.append(name)
+    return out
+
+
+def trace_table(path: str) -> OrderedDict:
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    stats: OrderedDict = OrderedDict()
+    for (did, sym, t0, t1), name in zip(rows, _label(rows)):
+        if name is None:
+            continue
+        s = stats.setdefault(name, {"calls": 0, "total_ns": 0, "min_ns": None, "max_ns": 0})
+        d = t1 - t0
+        s["calls"] += 1
+        s["total_ns"] += d
+        s["min_ns"] = d if s["min_ns"] is None else min(s["min_ns"], d)
+        s["max_ns"] = max(s["max_ns"], d)
+    return stats
+
+
+def counter_per_dispatch(path: str) -> list:
+    acc: OrderedDict = OrderedDict()
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            did = int(r["Dispatch_Id"])
+            e = acc.setdefault(did, [did, r["Kernel_Name"], 0.0])
+            e[2] += float(r["Counter_Value"])  # summed over XCD / channel instances
+    return sorted(acc.values())
+
+
+def traffic_table(fetch_csv: str, write_csv: str):
+    per = {}
+    factors = {}
+    for which, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = counter_per_dispatch(path)
+        names = _label(rows)
+        copy = [r[2] * 1024 for r, n in zip(rows, names) if n == "copy" and r[2] > 0]
+        if not copy:
+            raise SystemExit(f"{path}: no calibration copy found (run bench.py with --copy-calibration)")
+        factor = COPY_BYTES / copy[-1]
+        factors[which] = factor
+        sums = defaultdict(list)
+        for r, n in zip(rows, names):
+            if n and n != "copy":
+                sums[n].append(r[2] * 1024 * factor)
+        for n, v in sums.items():
+            # skip the first (warm-up) launch of each kernel when there are more
+            vals = v[1:] if len(v) > 1 else v
+            per.setdefault(n, {})[which] = sum(vals) / len(vals)
+    return per, factors
+
+
+def main(argv) -> int:
+    if len(argv) >= 4 and argv[0] == "trace":
+        path, workload, cmd = argv[1], argv[2], argv[3]
+        st = trace_table(path)
+        total = sum(s["total_ns"] for s in st.values())
+        print(f"# Kernel durations, {workload} workload\n")
+        print(f"Command: `{cmd}`\n")
+        print("| kernel | launches | avg us | min us | max us | share |")
+        print("|---|---:|---:|---:|---:|---:|")
+        for n, s in sorted(st.items(), key=lambda kv: -kv[1]["total_ns"]):
+            print(f"| {n} | {s['calls']} | {s['total_ns'] / s['calls'] / 1e3:.2f} | {s['min_ns'] / 1e3:.2f} | "
+                  f"{s['max_ns'] / 1e3:.2f} | {100.0 * s['total_ns'] / total:.1f}% |")
+        return 0
+    if len(argv) >= 5 and argv[0] == "traffic":
+        fetch, write, workload, cmd = argv[1], argv[2], argv[3], argv[4]
+        per, factors = traffic_table(fetch, write)
+        print(f"# HBM traffic per launch, {workload} workload\n")
+        print(f"Command (one run per counter): `{cmd}`\n")
+        print(f"Calibration: a 256 MiB device copy reads FETCH_SIZE x {factors['fetch']:.3f} and "
+              f"WRITE_SIZE x {factors['write']:.3f} of its true bytes; the figures below are scaled by those "
+              "factors.\n")
+        print("| kernel | read MiB | written MiB | total MiB |")
+        print("|---|---:|---:|---:|")
+        for n, v in per.items():
+            r, w = v.get("fetch", 0.0), v.get("write", 0.0)
+            print(f"| {n} | {r / 2**20:.1f} | {w / 2**20:.1f} | {(r + w) / 2**20:.1f} |")
+        rec = {n: int(v.get("fetch", 0.0) + v.get("write", 0.0)) for n, v in per.items()}
+        print("\n```json")
+        print(json.dumps({workload: rec}, indent=1))
+        print("```")
+        return 0
+    print(__doc__)
+    return 2
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
