@@ -116,6 +116,17 @@ MOE_DEV unsigned long long wave_max_u64(unsigned long long v) {
   return a > c ? a : c;
 }
 
+// Maximum of a 32-bit value over the 64 lanes, wave-uniform (same scheme).
+MOE_DEV uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 15), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 47), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  return max(max(a, b), max(c, d));
+}
+
 // Blocks are handed to the 8 XCDs of the chip round-robin.  Map the
 // hardware block id to a logical id so that each XCD works on one contiguous
 // range of logical ids [0, n) (a bijection on [0, n) for any n).

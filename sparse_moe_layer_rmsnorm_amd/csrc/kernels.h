@@ -18,8 +18,8 @@ constexpr int kHistSlices = 16;
 #define MOE_EXPERT_BM 64
 #endif
 constexpr int kExpertBM = MOE_EXPERT_BM;
-// Experts per block of the histogram kernel.
-constexpr int kHistExperts = 64;
+// Experts per block of the histogram kernel (16 x 256 bins = 16 KB of LDS).
+constexpr int kHistExperts = 16;
 
 struct Dims {
   int d, l, E, k, f, f_s, B;
@@ -45,8 +45,7 @@ hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, cons
                           void* y_lat, hipStream_t s);
 hipError_t launch_qb_quantile(const Dims& D, uint32_t* hist, const unsigned long long* count, double* q,
                               hipStream_t s);
-hipError_t launch_qb_bias(const Dims& D, const double* q, unsigned long long* count, float* bias,
-                          hipStream_t s);
+hipError_t launch_qb_bias(const Dims& D, const double* q, unsigned long long* count, float* bias, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 // Dense GEMMs on h (router logits, shared GLU hidden, latent z) and for the

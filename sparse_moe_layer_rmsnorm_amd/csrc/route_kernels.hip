@@ -18,8 +18,47 @@ namespace moe {
 
 // ------------------------------------------------------------- RMSNorm ----
 // One wavefront per token row; h = (x * rstd) * gamma, rstd = 1/sqrt(mean(x^2)
-// + eps), fp32 arithmetic, stored in the activation dtype.
+// + eps), fp32 arithmetic, stored in the activation dtype.  Rows of up to
+// 64*CPL 16-byte chunks are read once into registers (all loads in flight
+// together); longer rows take the two-pass loop (CPL = 0).
 template <bool BF16>
+MOE_DEV float chunk_sumsq(const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (BF16) {
+      const float a = bf16_bits_to_f32(w[i] & 0xFFFFu), b = bf16_bits_to_f32(w[i] >> 16);
+      ss += a * a + b * b;
+    } else {
+      const float a = __uint_as_float(w[i]);
+      ss += a * a;
+    }
+  }
+  return ss;
+}
+
+template <bool BF16>
+MOE_DEV uint4 chunk_scale(const uint4& v, float rstd, const float* g) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+  if (BF16) {
+    const float4 g0 = *reinterpret_cast<const float4*>(g), g1 = *reinterpret_cast<const float4*>(g + 4);
+    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = pack_bf16x2(bf16_bits_to_f32(w[i] & 0xFFFFu) * rstd * gg[2 * i],
+                         bf16_bits_to_f32(w[i] >> 16) * rstd * gg[2 * i + 1]);
+  } else {
+    const float4 g0 = *reinterpret_cast<const float4*>(g);
+    const float gg[4] = {g0.x, g0.y, g0.z, g0.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(__uint_as_float(w[i]) * rstd * gg[i]);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+template <bool BF16, int CPL>
 __global__ __launch_bounds__(256) void k_rmsnorm(const void* __restrict__ x, const float* __restrict__ gamma,
                                                  void* __restrict__ h, int T, int d, float eps) {
   const int lane = threadIdx.x & 63;
@@ -31,66 +70,140 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const void* __restrict__ x, con
   const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const char*>(x) + (size_t)row * rbytes);
   uint4* hr = reinterpret_cast<uint4*>(static_cast<char*>(h) + (size_t)row * rbytes);
   float ss = 0.f;
-  for (int c = lane; c < nch; c += 64) {
-    uint4 v = xr[c];
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (CPL > 0) {
+    uint4 v[CPL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (BF16) {
-        float a = bf16_bits_to_f32(w[i] & 0xFFFFu), b = bf16_bits_to_f32(w[i] >> 16);
-        ss += a * a + b * b;
-      } else {
-        float a = __uint_as_float(w[i]);
-        ss += a * a;
-      }
-    }
-  }
-  ss = wave_sum(ss);
-  const float rstd = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int c = lane; c < nch; c += 64) {
-    uint4 v = xr[c];
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    const float* g = gamma + c * EPC;
-    uint32_t o[4];
+    for (int i = 0; i < CPL; ++i) v[i] = lane + 64 * i < nch ? xr[lane + 64 * i] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (BF16) {
-        float a = bf16_bits_to_f32(w[i] & 0xFFFFu) * rstd * g[2 * i];
-        float b = bf16_bits_to_f32(w[i] >> 16) * rstd * g[2 * i + 1];
-        o[i] = pack_bf16x2(a, b);
-      } else {
-        o[i] = __float_as_uint(__uint_as_float(w[i]) * rstd * g[i]);
-      }
+    for (int i = 0; i < CPL; ++i) ss += chunk_sumsq<BF16>(v[i]);
+    ss = wave_sum(ss);
+    const float rstd = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nch) hr[c] = chunk_scale<BF16>(v[i], rstd, gamma + c * EPC);
     }
-    hr[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  } else {
+    for (int c = lane; c < nch; c += 64) ss += chunk_sumsq<BF16>(xr[c]);
+    ss = wave_sum(ss);
+    const float rstd = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int c = lane; c < nch; c += 64) hr[c] = chunk_scale<BF16>(xr[c], rstd, gamma + c * EPC);
   }
 }
 
+template <bool BF16>
+static void rmsnorm_dispatch(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s) {
+  const int per_lane = (D.d / (BF16 ? 8 : 4) + 63) / 64;
+  dim3 grid((T + 3) / 4), block(256);
+  if (per_lane <= 1) hipLaunchKernelGGL((k_rmsnorm<BF16, 1>), grid, block, 0, s, x, gamma, h, T, D.d, D.eps);
+  else if (per_lane <= 2) hipLaunchKernelGGL((k_rmsnorm<BF16, 2>), grid, block, 0, s, x, gamma, h, T, D.d, D.eps);
+  else if (per_lane <= 4) hipLaunchKernelGGL((k_rmsnorm<BF16, 4>), grid, block, 0, s, x, gamma, h, T, D.d, D.eps);
+  else if (per_lane <= 8) hipLaunchKernelGGL((k_rmsnorm<BF16, 8>), grid, block, 0, s, x, gamma, h, T, D.d, D.eps);
+  else hipLaunchKernelGGL((k_rmsnorm<BF16, 0>), grid, block, 0, s, x, gamma, h, T, D.d, D.eps);
+}
+
 hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s) {
-  dim3 grid((T + 3) / 4);
   if (D.bf16)
-    hipLaunchKernelGGL(k_rmsnorm<true>, grid, dim3(256), 0, s, x, gamma, h, T, D.d, D.eps);
+    rmsnorm_dispatch<true>(D, x, gamma, h, T, s);
   else
-    hipLaunchKernelGGL(k_rmsnorm<false>, grid, dim3(256), 0, s, x, gamma, h, T, D.d, D.eps);
+    rmsnorm_dispatch<false>(D, x, gamma, h, T, s);
   return hipGetLastError();
 }
 
 // -------------------------------------------------- scores + top-k ----
-// One block per chunk of kChunk = 32 tokens, 8 wavefronts, one token per
-// wavefront at a time (the next token's logits are loaded while the current
-// one is ranked).  Lane i holds experts i, i+64, ... .  Each of the k rounds
-// takes the wave-wide maximum (DPP, no LDS) of the 64-bit key (order key of
-// v = s + b, then the complement of the expert index), so equal v go to the
-// lower index.  Gates are the chosen unbiased scores over their fp32 sum in
-// slot order.  The chunk's selections leave as one 32-bit token mask per
-// expert: bitmap[chunk][e] bit t%32 is set iff token t picked e.
-template <int CPL>
-__global__ __launch_bounds__(512) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
-                                              int T, int E, int k, float scale, int32_t* __restrict__ idx,
-                                              float* __restrict__ gates, uint32_t* __restrict__ bitmap) {
+// One block per chunk of kChunk = 32 tokens, 16 wavefronts, two tokens per
+// wavefront ranked side by side (independent chains hide each other's
+// latency).  Lane i holds experts i, i+64, ... .  Each of the k rounds takes
+// the wave-wide maximum (DPP, no LDS) of the order key of v = s + b; among
+// equal keys the lowest expert index wins (first the lowest column c of any
+// lane holding the key, then the lowest such lane, by ballots).  Gates are
+// the chosen unbiased scores over their fp32 sum in slot order.  The chunk's
+// selections leave as one 32-bit token mask per expert: bitmap[chunk][e] bit
+// t%32 is set iff token t picked e.
+template <int CPL, int NT>
+MOE_DEV void topk_tokens(const float* __restrict__ logits, const float (&b)[CPL], const int (&t)[NT], int E, int k,
+                         float scale, int32_t* __restrict__ idx, float* __restrict__ gates, uint32_t* mask) {
 #pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  float s[NT][CPL];
+  uint32_t key[NT][CPL];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const float* lr = logits + (size_t)t[n] * E;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int e = lane + 64 * c;
+      s[n][c] = e < E ? lr[e] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int e = lane + 64 * c;
+      if (e < E) {
+        s[n][c] = router_sigmoid(s[n][c]);
+        key[n][c] = float_order_key(s[n][c] + b[c]);  // > 0 for any finite v
+      } else {
+        s[n][c] = 0.f;
+        key[n][c] = 0u;
+      }
+    }
+  float S[NT], my_s[NT];
+  int my_e[NT];
+  for (int j = 0; j < k; ++j) {
+    uint32_t best[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      best[n] = key[n][0];
+#pragma unroll
+      for (int c = 1; c < CPL; ++c) best[n] = max(best[n], key[n][c]);
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) best[n] = wave_max_u32(best[n]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      int sel_c = 0;
+      unsigned long long sel = 0;
+#pragma unroll
+      for (int c = CPL - 1; c >= 0; --c) {
+        const unsigned long long m = __ballot(key[n][c] == best[n]);
+        if (m) {
+          sel = m;
+          sel_c = c;
+        }
+      }
+      const int owner = (int)__builtin_ctzll(sel);
+      float sv = s[n][0];
+#pragma unroll
+      for (int c = 1; c < CPL; ++c) sv = (c == sel_c) ? s[n][c] : sv;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        if (c == sel_c && lane == owner) key[n][c] = 0u;
+      const float se = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), owner));
+      S[n] = (j == 0) ? se : S[n] + se;
+      if (lane == j) {
+        my_s[n] = se;
+        my_e[n] = sel_c * 64 + owner;
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+    if (lane < k) {
+      const float g = (my_s[n] / S[n]) * scale;
+      idx[(size_t)t[n] * k + lane] = my_e[n];
+      gates[(size_t)t[n] * k + lane] = g;
+      atomicOr(&mask[my_e[n]], 1u << (t[n] & 31));
+    }
+}
+
+template <int CPL>
+__global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
+                                               int T, int E, int k, float scale, int32_t* __restrict__ idx,
+                                               float* __restrict__ gates, uint32_t* __restrict__ bitmap) {
   __shared__ uint32_t mask[1024];
-  for (int i = threadIdx.x; i < E; i += 512) mask[i] = 0u;
+  for (int i = threadIdx.x; i < E; i += 1024) mask[i] = 0u;
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float b[CPL];
@@ -99,76 +212,23 @@ __global__ __launch_bounds__(512) void k_topk(const float* __restrict__ logits, 
     const int e = lane + 64 * c;
     b[c] = e < E ? bias[e] : 0.f;
   }
-  float nxt[CPL];
-  auto load = [&](int t) {
-    const float* lr = logits + (size_t)t * E;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int e = lane + 64 * c;
-      nxt[c] = e < E ? lr[e] : 0.f;
-    }
-  };
-  int t = blockIdx.x * kChunk + wave;
-  if (t < T) load(t);
-  for (int it = 0; it < kChunk / 8; ++it, t += 8) {
-    if (t >= T) break;  // uniform across the wavefront
-    float s[CPL];
-    unsigned long long key[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) s[c] = nxt[c];
-    if (it + 1 < kChunk / 8 && t + 8 < T) load(t + 8);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int e = lane + 64 * c;
-      if (e < E) {
-        s[c] = router_sigmoid(s[c]);
-        const float v = s[c] + b[c];
-        key[c] = ((unsigned long long)float_order_key(v) << 32) | (0xFFFFFFFFu - (uint32_t)e);
-      } else {
-        s[c] = 0.f;
-        key[c] = 0ull;
-      }
-    }
-    float S = 0.f, my_s = 0.f;
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-      unsigned long long best = key[0];
-#pragma unroll
-      for (int c = 1; c < CPL; ++c) best = key[c] > best ? key[c] : best;
-      best = wave_max_u64(best);
-      const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-      const int owner = e & 63, oc = e >> 6;
-      float sv = 0.f;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        if (c == oc) {
-          sv = s[c];
-          if (lane == owner) key[c] = 0ull;
-        }
-      }
-      const float se = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), owner));
-      S = (j == 0) ? se : S + se;
-      if (lane == j) {
-        my_s = se;
-        my_e = e;
-      }
-    }
-    if (lane < k) {
-      const float g = (my_s / S) * scale;
-      idx[(size_t)t * k + lane] = my_e;
-      gates[(size_t)t * k + lane] = g;
-      atomicOr(&mask[my_e], 1u << (t & 31));
-    }
+  const int t0 = blockIdx.x * kChunk + wave, t1 = t0 + 16;
+  if (t1 < T) {
+    const int t[2] = {t0, t1};
+    topk_tokens<CPL, 2>(logits, b, t, E, k, scale, idx, gates, mask);
+  } else if (t0 < T) {
+    const int t[1] = {t0};
+    topk_tokens<CPL, 1>(logits, b, t, E, k, scale, idx, gates, mask);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < E; i += 512) bitmap[(size_t)blockIdx.x * E + i] = mask[i];
+  for (int i = threadIdx.x; i < E; i += 1024) bitmap[(size_t)blockIdx.x * E + i] = mask[i];
 }
 
 hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, int T, int32_t* idx, float* gates,
                        uint32_t* bitmap, hipStream_t s) {
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int cpl = (D.E + 63) / 64;
-  dim3 grid(nchunks), block(512);
+  dim3 grid(nchunks), block(1024);
 #define MOE_TOPK(C) \
   hipLaunchKernelGGL(k_topk<C>, grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, bitmap)
   if (cpl <= 1) MOE_TOPK(1);
@@ -182,37 +242,40 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
 
 // ---------------------------------------------------------- QB histogram ----
 // The state keeps the histogram as kHistSlices token slices [slice][E][B].
-// Block (64-expert group, slice) counts its tokens' score bins in LDS with
+// Block (16-expert group, slice) counts its tokens' score bins in LDS with
 // integer atomics (order-free) and adds them to its own rows of its own slice
 // (no other block of the launch writes them), so no reduction pass is needed
 // per forward; qb_update sums the slices.
-__global__ __launch_bounds__(1024) void k_hist(const float* __restrict__ logits, int T, int E, int B, int tps,
-                                               uint32_t* __restrict__ hist, unsigned long long* __restrict__ count) {
+__global__ __launch_bounds__(512) void k_hist(const float* __restrict__ logits, int T, int E, int B, int tps,
+                                              uint32_t* __restrict__ hist, unsigned long long* __restrict__ count) {
   __shared__ uint32_t lh[kHistExperts * 256];
   const int e0 = blockIdx.x * kHistExperts, ts = blockIdx.y;
   const int ne = min(kHistExperts, E - e0);
   const int nb = kHistExperts * B;
-  for (int i = threadIdx.x; i < nb; i += 1024) lh[i] = 0;
+  for (int i = threadIdx.x; i < nb; i += 512) lh[i] = 0;
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = e0 + lane;
+  // thread -> expert e0 + (i % 16), tokens (i / 16) + 32 m: each wavefront
+  // reads four 64-byte row pieces per step
+  const int el = threadIdx.x % kHistExperts, tl = threadIdx.x / kHistExperts;
+  const int e = e0 + el;
   const int tb = ts * tps, te = min(T, tb + tps);
   if (e < E) {
-    int t = tb + wave;
-    for (; t + 48 < te; t += 64) {
-      const float l0 = logits[(size_t)t * E + e], l1 = logits[(size_t)(t + 16) * E + e];
-      const float l2 = logits[(size_t)(t + 32) * E + e], l3 = logits[(size_t)(t + 48) * E + e];
-      atomicAdd(&lh[lane * B + score_bin(router_sigmoid(l0), B)], 1u);
-      atomicAdd(&lh[lane * B + score_bin(router_sigmoid(l1), B)], 1u);
-      atomicAdd(&lh[lane * B + score_bin(router_sigmoid(l2), B)], 1u);
-      atomicAdd(&lh[lane * B + score_bin(router_sigmoid(l3), B)], 1u);
+    uint32_t* row = lh + el * B;
+    int t = tb + tl;
+    for (; t + 96 < te; t += 128) {
+      const float l0 = logits[(size_t)t * E + e], l1 = logits[(size_t)(t + 32) * E + e];
+      const float l2 = logits[(size_t)(t + 64) * E + e], l3 = logits[(size_t)(t + 96) * E + e];
+      atomicAdd(&row[score_bin(router_sigmoid(l0), B)], 1u);
+      atomicAdd(&row[score_bin(router_sigmoid(l1), B)], 1u);
+      atomicAdd(&row[score_bin(router_sigmoid(l2), B)], 1u);
+      atomicAdd(&row[score_bin(router_sigmoid(l3), B)], 1u);
     }
-    for (; t < te; t += 16) atomicAdd(&lh[lane * B + score_bin(router_sigmoid(logits[(size_t)t * E + e]), B)], 1u);
+    for (; t < te; t += 32) atomicAdd(&row[score_bin(router_sigmoid(logits[(size_t)t * E + e]), B)], 1u);
   }
   __syncthreads();
   if (tb < T) {
     uint32_t* dst = hist + ((size_t)ts * E + e0) * B;
-    for (int i = threadIdx.x; i < ne * B; i += 1024) {
+    for (int i = threadIdx.x; i < ne * B; i += 512) {
       const uint32_t v = lh[i];
       if (v) dst[i] += v;
     }
@@ -224,7 +287,7 @@ hipError_t launch_hist(const Dims& D, const float* logits, int T, uint32_t* hist
                        hipStream_t s) {
   const int tps = (T + kHistSlices - 1) / kHistSlices;
   dim3 grid((D.E + kHistExperts - 1) / kHistExperts, kHistSlices);
-  hipLaunchKernelGGL(k_hist, grid, dim3(1024), 0, s, logits, T, D.E, D.B, tps, hist, count);
+  hipLaunchKernelGGL(k_hist, grid, dim3(512), 0, s, logits, T, D.E, D.B, tps, hist, count);
   return hipGetLastError();
 }
 
@@ -428,41 +491,41 @@ hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, cons
 
 // ------------------------------------------------------------ QB update ----
 // Per expert (one block each, one thread per bin): sum the bin over the
-// histogram slices and clear it; with A_j = tokens above bin j (a parallel
-// suffix sum), the one bin with A_j*E < N*k <= (A_j + c_j)*E (exact integer
-// tests) holds the score the expert must beat to receive N*k/E tokens; inside
-// it the estimate is linear: q = (j+1)/B - ((N*k - A_j*E) / (E*c_j)) / B, fp64.
+// histogram slices and clear it; with A_j = tokens above bin j (a suffix sum:
+// wave shuffles, then the wave totals), the one bin with
+// A_j*E < N*k <= (A_j + c_j)*E (exact integer tests) holds the score the
+// expert must beat to receive N*k/E tokens; inside it the estimate is linear:
+// q = (j+1)/B - ((N*k - A_j*E) / (E*c_j)) / B, fp64.
 __global__ __launch_bounds__(256) void k_qb_quantile(uint32_t* __restrict__ hist,
                                                      const unsigned long long* __restrict__ count, int E, int B,
                                                      int k, double* __restrict__ q) {
 #pragma clang fp contract(off)
-  __shared__ unsigned long long suf[2][256];
+  __shared__ unsigned long long wtot[4];
   const unsigned long long N = *count;
   if (N == 0) return;
-  const int e = blockIdx.x, j = threadIdx.x;
+  const int e = blockIdx.x, j = threadIdx.x, lane = j & 63, w = j >> 6;
   unsigned long long c = 0;
   if (j < B) {
-#pragma unroll 4
+    uint32_t v[kHistSlices];
+#pragma unroll
+    for (int sl = 0; sl < kHistSlices; ++sl) v[sl] = hist[((size_t)sl * E + e) * B + j];
+#pragma unroll
     for (int sl = 0; sl < kHistSlices; ++sl) {
-      uint32_t* p = hist + ((size_t)sl * E + e) * B + j;
-      c += *p;
-      *p = 0u;
+      c += v[sl];
+      hist[((size_t)sl * E + e) * B + j] = 0u;
     }
   }
-  // inclusive suffix sums over bins (Hillis-Steele, double-buffered)
-  int cur = 0;
-  suf[0][j] = c;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const unsigned long long v = suf[cur][j] + (j + o < 256 ? suf[cur][j + o] : 0ull);
-    suf[cur ^ 1][j] = v;
-    cur ^= 1;
-    __syncthreads();
+  unsigned long long incl = c;  // inclusive suffix sum inside the wavefront
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long u = __shfl_down(incl, o, 64);
+    if (lane + o < 64) incl += u;
   }
-  if (j == 0) q[e] = 0.0;
+  if (lane == 0) wtot[w] = incl;
   __syncthreads();
+  for (int w2 = w + 1; w2 < 4; ++w2) incl += wtot[w2];
   if (j < B) {
-    const unsigned long long incl = suf[cur][j], above = incl - c;
+    const unsigned long long above = incl - c;
     const unsigned long long target = N * (unsigned long long)k, EE = (unsigned long long)E;
     if (above * EE < target && target <= incl * EE) {
       const double frac = (double)(target - above * EE) / (double)(EE * c);
@@ -471,8 +534,9 @@ __global__ __launch_bounds__(256) void k_qb_quantile(uint32_t* __restrict__ hist
   }
 }
 
-// b_e = fp32(mu - q_e), mu the fp64 mean of q summed in expert order; then the
-// token count is cleared.  Keeps the bias when no token was accumulated.
+// b_e = fp32(mu - q_e), mu the fp64 mean of q summed in expert order (the q
+// are staged in LDS by all threads, the sum is one thread's); then the token
+// count is cleared.  Keeps the bias when no token was accumulated.
 __global__ __launch_bounds__(1024) void k_qb_bias(const double* __restrict__ q, unsigned long long* __restrict__ count,
                                                   int E, float* __restrict__ bias) {
 #pragma clang fp contract(off)
@@ -483,7 +547,6 @@ __global__ __launch_bounds__(1024) void k_qb_bias(const double* __restrict__ q, 
   __syncthreads();
   if (threadIdx.x == 0) {
     double mu = 0.0;
-#pragma unroll 8
     for (int e = 0; e < E; ++e) mu += qs[e];
     mu_s = mu / (double)E;
   }

@@ -30,8 +30,8 @@ def logical_name(symbol: str, dense_seen: int) -> str | None:
         return "gemm_h" if dense_seen % 2 == 0 else "gemm_out"
     if "k_gemm_expert" in symbol:
         return "expert_up" if symbol.rstrip().endswith("2>(moe::(anonymous namespace)::ExpertArgs)") else "expert_down"
-    for k in ("rmsnorm", "topk", "hist", "scan_local", "scan_global", "scatter", "combine", "qb_quantile",
-              "qb_bias", "zero"):
+    for k in ("rmsnorm", "topk", "hist", "scan_local", "scan_global", "scatter", "combine", "qb_update",
+              "qb_quantile", "qb_bias", "zero"):
         if f"k_{k}" in symbol:
             return k
     if "rocclr_copyBuffer" in symbol:
