@@ -42,6 +42,7 @@ def kernel_work(s, T: int) -> dict:
     nchunks = (T + 31) // 32
     flops = {
         "gemm_h": 2.0 * T * s.d * (s.E + 2 * s.f_s + s.l),
+        "gemm_rz": 2.0 * T * s.d * s.E,
         "gemm_out": 2.0 * T * s.d * (s.f_s + s.l),
         "expert_up": 2.0 * Tk * s.l * 2 * s.f,
         "expert_down": 2.0 * Tk * s.f * s.l,

@@ -201,7 +201,7 @@ const char* moe_last_error(void);
 enum {
   MOE_K_RMSNORM = 0, MOE_K_GEMM_H, MOE_K_TOPK, MOE_K_HIST, MOE_K_SCAN, MOE_K_SCATTER,
   MOE_K_EXPERT_UP, MOE_K_EXPERT_DOWN, MOE_K_COMBINE, MOE_K_GEMM_OUT, MOE_K_QB_QUANTILE,
-  MOE_K_QB_BIAS, MOE_NUM_KERNELS
+  MOE_K_QB_BIAS, MOE_K_GEMM_RZ, MOE_NUM_KERNELS
 };
 const char* moe_kernel_name(int id);
 moe_status moe_profile_begin(moe_ctx* ctx, int max_launches, uint32_t mask);

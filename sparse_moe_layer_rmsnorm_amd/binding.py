@@ -20,7 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MO
 MOE_F32, MOE_BF16 = 0, 1
 MOE_QB_TRAIN, MOE_QB_FROZEN = 0, 1
 KERNELS = ["rmsnorm", "gemm_h", "topk", "hist", "scan", "scatter", "expert_up", "expert_down", "combine",
-           "gemm_out", "qb_quantile", "qb_bias"]
+           "gemm_out", "qb_quantile", "qb_bias", "gemm_rz"]
 MOE_NUM_KERNELS = len(KERNELS)
 
 

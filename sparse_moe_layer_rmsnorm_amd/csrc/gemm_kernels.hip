@@ -543,7 +543,9 @@ struct DenseProb {
   }
 };
 
-template <class Pp>
+// TAG only names the launch (0: the h GEMM of a forward, 1: router logits
+// alone, 2: the output GEMM) so that profiles tell the dense GEMMs apart.
+template <class Pp, int TAG>
 __global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::GROUPS * Pp::NW / 4) void k_gemm_dense(const DenseArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
   // Per-column offsets go through LDS: a vector load in the epilogue would
@@ -684,18 +686,27 @@ static int persistent_grid(long long tiles, int bpc, int groups) {
   return (int)(g < 8 ? 8 : g);
 }
 
-template <bool BF16>
+template <bool BF16, int TAG>
 static hipError_t launch_dense(const DenseArgs& a, hipStream_t s) {
+  using P = DensePipe<BF16>;
   const long long tiles = (long long)a.m_tiles * a.total_ntiles;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_dense<DensePipe<BF16>>), dim3(persistent_grid(tiles, DensePipe<BF16>::BPC, DensePipe<BF16>::GROUPS)),
-                     dim3(DensePipe<BF16>::THREADS), 0, s, a);
+  hipLaunchKernelGGL((k_gemm_dense<P, TAG>), dim3(persistent_grid(tiles, P::BPC, P::GROUPS)), dim3(P::THREADS), 0, s,
+                     a);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
-                         const void* W_sg, const void* W_su, const void* W_dn, float* logits, void* G, void* z,
-                         hipStream_t s) {
+template <int TAG>
+static hipError_t launch_dense_any(const Dims& D, const DenseArgs& a, hipStream_t s) {
+  return D.bf16 ? launch_dense<true, TAG>(a, s) : launch_dense<false, TAG>(a, s);
+}
+
+// One K pass over h for the given segments (in this order: router logits,
+// shared GLU, latent z); a NULL output drops its segment.
+template <int TAG>
+static hipError_t launch_gemm_hsegs(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
+                                    const void* W_sg, const void* W_su, const void* W_dn, float* logits, void* G,
+                                    void* z, hipStream_t s) {
   constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN, RB = DensePipe<true>::RB;
   const int es = esz(D);
   DenseArgs a{};
@@ -741,7 +752,18 @@ hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, c
   a.nseg = ns;
   a.total_ntiles = 0;
   for (int i = 0; i < ns; ++i) a.total_ntiles += a.seg[i].ntiles;
-  return D.bf16 ? launch_dense<true>(a, s) : launch_dense<false>(a, s);
+  return launch_dense_any<TAG>(D, a, s);
+}
+
+hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
+                         const void* W_sg, const void* W_su, const void* W_dn, float* logits, void* G, void* z,
+                         hipStream_t s) {
+  return launch_gemm_hsegs<0>(D, h, T, W_r, logit_offset, W_sg, W_su, W_dn, logits, G, z, s);
+}
+
+hipError_t launch_gemm_rz(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
+                          float* logits, hipStream_t s) {
+  return launch_gemm_hsegs<1>(D, h, T, W_r, logit_offset, nullptr, nullptr, nullptr, logits, nullptr, nullptr, s);
 }
 
 hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int T, const void* W_sd,
@@ -772,7 +794,7 @@ hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int 
   a.seg[0].ldo = D.d;
   a.nseg = 1;
   a.total_ntiles = a.seg[0].ntiles;
-  return D.bf16 ? launch_dense<true>(a, s) : launch_dense<false>(a, s);
+  return launch_dense_any<2>(D, a, s);
 }
 
 int expert_max_mtiles(int T, int k, int E) {

@@ -50,9 +50,15 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 // Dense GEMMs on h (router logits, shared GLU hidden, latent z) and for the
 // output ([G | y_lat] [W_sd | W_up]^T).
+// h [T,d] against [W_r | W_sg,W_su | W_dn] -> fp32 router logits (+ offset),
+// shared GLU hidden G and latent z in one launch; a NULL output drops its
+// part.
 hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
-                         const void* W_sg, const void* W_su, const void* W_dn, float* logits, void* G,
-                         void* z, hipStream_t s);
+                         const void* W_sg, const void* W_su, const void* W_dn, float* logits, void* G, void* z,
+                         hipStream_t s);
+// h against W_r alone -> fp32 logits (+ offset) (the routing-only pass).
+hipError_t launch_gemm_rz(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
+                          float* logits, hipStream_t s);
 hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int T, const void* W_sd,
                            const void* W_up, void* out, hipStream_t s);
 // Grouped expert GEMMs over the rows grouped by expert (m-tiles of

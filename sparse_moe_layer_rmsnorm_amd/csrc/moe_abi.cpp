@@ -291,8 +291,7 @@ moe_status moe_route(moe_ctx* ctx, const void* x, const float* logits, int64_t T
     const Dims& D = ctx->D;
     void* h = w + L.h;
     MOE_RUN(MOE_K_RMSNORM, launch_rmsnorm(D, x, ctx->w.gamma, h, t, s));
-    MOE_RUN(MOE_K_GEMM_H, launch_gemm_h(D, h, t, ctx->w.W_r, ctx->w.logit_offset, nullptr, nullptr, nullptr,
-                                        p.logits, nullptr, nullptr, s));
+    MOE_RUN(MOE_K_GEMM_RZ, launch_gemm_rz(D, h, t, ctx->w.W_r, ctx->w.logit_offset, p.logits, s));
   }
   return route_tail(ctx, p, t, nullptr, nullptr, s);
 }
@@ -383,7 +382,7 @@ const char* moe_last_error(void) { return g_err; }
 const char* moe_kernel_name(int id) {
   static const char* names[MOE_NUM_KERNELS] = {"rmsnorm",     "gemm_h",  "topk",     "hist",
                                                 "scan",        "scatter", "expert_up", "expert_down",
-                                                "combine",     "gemm_out", "qb_quantile", "qb_bias"};
+                                                "combine",     "gemm_out", "qb_quantile", "qb_bias", "gemm_rz"};
   return (id >= 0 && id < MOE_NUM_KERNELS) ? names[id] : "unknown";
 }
 

@@ -111,9 +111,8 @@ hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void
 }
 
 // -------------------------------------------------- scores + top-k ----
-// One block per chunk of kChunk = 32 tokens, 16 wavefronts, two tokens per
-// wavefront ranked side by side (independent chains hide each other's
-// latency).  Lane i holds experts i, i+64, ... .  Each of the k rounds takes
+// One block per chunk of kChunk = 32 tokens, kTopkNT tokens per wavefront
+// ranked side by side (independent chains hide each other's latency).  Lane i holds experts i, i+64, ... .  Each of the k rounds takes
 // the wave-wide maximum (DPP, no LDS) of the order key of v = s + b; among
 // equal keys the lowest expert index wins (first the lowest column c of any
 // lane holding the key, then the lowest such lane, by ballots).  Gates are
@@ -198,12 +197,20 @@ MOE_DEV void topk_tokens(const float* __restrict__ logits, const float (&b)[CPL]
     }
 }
 
+#ifndef MOE_TOPK_NT
+#define MOE_TOPK_NT 2
+#endif
+constexpr int kTopkNT = MOE_TOPK_NT;                    // tokens ranked side by side per wavefront
+constexpr int kTopkThreads = kChunk / kTopkNT * 64;      // one token group per wavefront
+
 template <int CPL>
-__global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
-                                               int T, int E, int k, float scale, int32_t* __restrict__ idx,
-                                               float* __restrict__ gates, uint32_t* __restrict__ bitmap) {
+__global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ logits,
+                                                       const float* __restrict__ bias, int T, int E, int k,
+                                                       float scale, int32_t* __restrict__ idx,
+                                                       float* __restrict__ gates, uint32_t* __restrict__ bitmap) {
+  constexpr int NW = kChunk / kTopkNT;
   __shared__ uint32_t mask[1024];
-  for (int i = threadIdx.x; i < E; i += 1024) mask[i] = 0u;
+  for (int i = threadIdx.x; i < E; i += kTopkThreads) mask[i] = 0u;
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float b[CPL];
@@ -212,23 +219,30 @@ __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ logits,
     const int e = lane + 64 * c;
     b[c] = e < E ? bias[e] : 0.f;
   }
-  const int t0 = blockIdx.x * kChunk + wave, t1 = t0 + 16;
-  if (t1 < T) {
-    const int t[2] = {t0, t1};
-    topk_tokens<CPL, 2>(logits, b, t, E, k, scale, idx, gates, mask);
-  } else if (t0 < T) {
-    const int t[1] = {t0};
-    topk_tokens<CPL, 1>(logits, b, t, E, k, scale, idx, gates, mask);
+  int t[kTopkNT];
+  int n = 0;
+#pragma unroll
+  for (int u = 0; u < kTopkNT; ++u) {
+    t[u] = blockIdx.x * kChunk + wave + NW * u;
+    n += t[u] < T;
+  }
+  if (n == kTopkNT) {
+    topk_tokens<CPL, kTopkNT>(logits, b, t, E, k, scale, idx, gates, mask);
+  } else {
+    for (int u = 0; u < n; ++u) {  // ragged last chunk: one at a time
+      const int t1[1] = {t[u]};
+      topk_tokens<CPL, 1>(logits, b, t1, E, k, scale, idx, gates, mask);
+    }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < E; i += 1024) bitmap[(size_t)blockIdx.x * E + i] = mask[i];
+  for (int i = threadIdx.x; i < E; i += kTopkThreads) bitmap[(size_t)blockIdx.x * E + i] = mask[i];
 }
 
 hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, int T, int32_t* idx, float* gates,
                        uint32_t* bitmap, hipStream_t s) {
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int cpl = (D.E + 63) / 64;
-  dim3 grid(nchunks), block(1024);
+  dim3 grid(nchunks), block(kTopkThreads);
 #define MOE_TOPK(C) \
   hipLaunchKernelGGL(k_topk<C>, grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, bitmap)
   if (cpl <= 1) MOE_TOPK(1);
@@ -314,11 +328,11 @@ __global__ __launch_bounds__(256) void k_scan_local(const uint32_t* __restrict__
   sbase[(size_t)sc * E + e] = run;
 }
 
-// Global (one block of 1024 threads): per expert, the total and the exclusive
-// prefix over super-chunks (sbase becomes the absolute first row of each
-// super-chunk's part of the expert's group); over experts, the row offsets
-// and the first m-tile of each expert for the grouped GEMMs (tiles of
-// kExpertBM rows; an empty expert has none).
+// Global (one block of 1024 threads, one expert per thread): per expert, the
+// total and the exclusive prefix over super-chunks (sbase becomes the
+// absolute first row of each super-chunk's part of the expert's group); over
+// experts, the row offsets and the first m-tile of each expert for the grouped
+// GEMMs (tiles of kExpertBM rows; an empty expert has none).
 __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbase, int nsuper, int E,
                                                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ tile_offsets, int2* __restrict__ tile_info) {
@@ -326,7 +340,7 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
   const int i = threadIdx.x, lane = i & 63, w = i >> 6;
   int c = 0;
   if (i < E) {
-#pragma unroll 8
+#pragma unroll 16
     for (int sc = 0; sc < nsuper; ++sc) c += sbase[(size_t)sc * E + i];
   }
   const int tl = (c + kExpertBM - 1) / kExpertBM;
@@ -344,18 +358,16 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
     wsum_t[w] = t;
   }
   __syncthreads();
-  int br = 0, bt = 0;
   for (int j = 0; j < w; ++j) {
-    br += wsum_r[j];
-    bt += wsum_t[j];
+    r += wsum_r[j];
+    t += wsum_t[j];
   }
-  r += br;
-  t += bt;
   if (i < E) {
     counts[i] = c;
     offsets[i + 1] = r;
     tile_offsets[i + 1] = t;
     int run = r - c;  // exclusive offset of expert i
+#pragma unroll 16
     for (int sc = 0; sc < nsuper; ++sc) {
       const size_t j = (size_t)sc * E + i;
       const int v = sbase[j];

@@ -11,9 +11,11 @@ what it reads for the plain 256 MiB device copy that `bench.py
 record (HBM bytes per launch per kernel) that bench.py reports as
 `roofline.traffic`.
 
-The two dense GEMM launches of a step share one kernel symbol: the first of
-each step is gemm_h, the second gemm_out.  The grouped expert GEMM with the
-GLU epilogue is expert_up, the other expert_down.
+The dense GEMM launches carry a tag template argument: 0 the h GEMM of a
+forward (gemm_h), 1 router logits alone (gemm_rz, routing-only pass), 2 the
+output GEMM (gemm_out).
+The grouped expert GEMM with the GLU epilogue is expert_up, the other
+expert_down.
 """
 from __future__ import annotations
 
@@ -27,7 +29,8 @@ COPY_BYTES = 256 << 20
 
 def logical_name(symbol: str, dense_seen: int) -> str | None:
     if "k_gemm_dense" in symbol:
-        return "gemm_h" if dense_seen % 2 == 0 else "gemm_out"
+        tag = symbol.split(">, ")[-1].split(">")[0].strip()
+        return {"0": "gemm_h", "1": "gemm_rz", "2": "gemm_out"}.get(tag, "gemm_dense")
     if "k_gemm_expert" in symbol:
         return "expert_up" if symbol.rstrip().endswith("2>(moe::(anonymous namespace)::ExpertArgs)") else "expert_down"
     for k in ("rmsnorm", "topk", "hist", "scan_local", "scan_global", "scatter", "combine", "qb_update",
