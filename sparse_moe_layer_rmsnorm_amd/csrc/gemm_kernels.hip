@@ -119,33 +119,26 @@ MOE_DEV int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 // rows of 4 chunks); thread (wave w of NW, lane) fills slots i*NW + w, i < L,
 // lane l writing chunk position l % (RB/16) of its row, i.e. logical chunk
 // (l % (RB/16)) ^ sw(row).
-template <int BM_, int BN_, int WM_, int WN_, int NS_, int RB_, int BPC_, int PP_, bool BF16>
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int RB_, int BPC_, bool BF16>
 struct Pipe {
-  static constexpr int BM = BM_, BN = BN_, NS = NS_, RB = RB_, BPC = BPC_, PP = PP_;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, RB = RB_, BPC = BPC_;
   static constexpr int WM = WM_, WN = WN_, NW = WM * WN;
-  static constexpr int GROUPS = PP ? 2 : 1;     // wavefront groups per block (ping-pong: 2)
-  static constexpr int THREADS = GROUPS * NW * 64;
+  static constexpr int THREADS = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int MI = WTM / 16, NI = WTN / 16;
   static constexpr int KK = RB / 64;                 // 64-byte K steps (one MFMA K each) per stage
   static constexpr int CPR = RB / 16;                // 16-byte chunks per row
   static constexpr int A_BYTES = BM * RB;
   static constexpr int STAGE = (BM + BN) * RB;
-  static constexpr int RING = NS * STAGE;   // LDS ring of one group
-  static constexpr int LDS = GROUPS * RING;
+  static constexpr int LDS = NS * STAGE;
   static constexpr int L = STAGE / 1024 / NW;  // DMA slots per thread per stage
   static_assert(RB == 64 || RB == 128, "64- or 128-byte stage rows");
   static_assert(STAGE % (1024 * NW) == 0, "stage must split into 1 KB slots over the wavefronts");
   static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
   static_assert(LDS * BPC <= 160 * 1024, "LDS per CU");
-  static_assert(!PP || BPC == 1, "one ping-pong block per CU");
   using Acc = f32x4_t[MI][NI];
-  struct Frags {
-    uint4 a[KK][MI], w[KK][NI];
-  };
 
-  MOE_DEV static int wave_id() { return (threadIdx.x >> 6) % NW; }  // wavefront within its group
-  MOE_DEV static int group_id() { return (threadIdx.x >> 6) / NW; }
+  MOE_DEV static int wave_id() { return threadIdx.x >> 6; }
 
   MOE_DEV static int swz(int row) { return RB == 128 ? (row & 7) : ((row >> 1) & 3); }
   MOE_DEV static int lds_off(int row, int chunk) { return row * RB + ((chunk ^ swz(row)) << 4); }
@@ -194,31 +187,6 @@ struct Pipe {
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) mfma_chunk<BF16>(acc[mi][ni], wf[kk][ni], af[kk][mi]);
-  }
-
-  // The two halves of compute() for the ping-pong schedule: all fragment
-  // reads of a stage (waited for), then the MFMAs on registers only.
-  MOE_DEV static void load_frags(const char* cur, Frags& F) {
-    const int lane = threadIdx.x & 63, wave = wave_id();
-    const int wm = wave / WN, wn = wave % WN;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int ch = kk * 4 + (lane >> 4);
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        F.w[kk][ni] = *reinterpret_cast<const uint4*>(cur + A_BYTES + lds_off(wn * WTN + ni * 16 + (lane & 15), ch));
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        F.a[kk][mi] = *reinterpret_cast<const uint4*>(cur + lds_off(wm * WTM + mi * 16 + (lane & 15), ch));
-    }
-  }
-  MOE_DEV static void mfma_all(const Frags& F, Acc& acc) {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) mfma_chunk<BF16>(acc[mi][ni], F.w[kk][ni], F.a[kk][mi]);
   }
 
   MOE_DEV static void zero(Acc& acc) {
@@ -346,82 +314,6 @@ MOE_DEV void stream(const Prob& prob, char* smem) {
   }
 }
 
-// Ping-pong variant: a block holds two groups of NW wavefronts, one per SIMD
-// each, that run two independent tile streams (virtual blocks 2b and 2b+1)
-// through their own LDS rings.  Every block barrier separates two intervals;
-// group 1 starts one barrier late, so while one group issues MFMAs from
-// registers the other waits for its stage, issues the next DMA, reads its
-// fragments from LDS and runs the previous tile's epilogue.  The two
-// wavefronts sharing a SIMD thus take turns on the matrix core instead of
-// stalling together.
-template <class Pp, class Prob>
-MOE_DEV void stream_pp(const Prob& prob, char* smem) {
-  const int grp = Pp::group_id();
-  const int G = gridDim.x, b = blockIdx.x;
-  const int x = b & 7, Gx = (G >> 3) * 2;  // the grid is a multiple of 8
-  const int total_tiles = prob.total();
-  const int per = (total_tiles + 7) >> 3;
-  const int lo = x * per, hi = min(total_tiles, lo + per);
-  const int q0 = (b >> 3) * 2;
-  const int s0 = hi - lo - q0, s1 = s0 - 1;
-  const int n0 = s0 > 0 ? (s0 + Gx - 1) / Gx : 0, n1 = s1 > 0 ? (s1 + Gx - 1) / Gx : 0;
-  const int q = q0 + grp, my_n = grp ? n1 : n0;
-  const int KT = prob.kt();
-  const int total = my_n * KT;
-  const int steps = max(n0, n1) * KT;  // the same for every wavefront of the block
-  if (steps == 0) return;
-  char* gsm = smem + grp * Pp::RING;
-  const uint32_t lds0 = lds_addr(gsm) + Pp::wave_id() * 1024;
-
-  typename Prob::template SrcT<Pp::L> src;
-  int iss_j = 0, iss_ks = 0, issued = 0;
-  if (total > 0) prob.sources(prob.tile(lo + q), src);
-  auto issue = [&]() {
-    const uint32_t base = lds0 + (uint32_t)((issued % Pp::NS) * Pp::STAGE);
-    prob.issue(src, iss_ks, base);
-    ++issued;
-    if (++iss_ks == KT) {
-      iss_ks = 0;
-      if (++iss_j < my_n) prob.sources(prob.tile(lo + q + iss_j * Gx), src);
-    }
-  };
-  if (grp == 1) block_barrier();
-  for (int s = 0; s < Pp::NS - 1; ++s)
-    if (issued < total) issue();
-
-  typename Pp::Acc acc;
-  typename Pp::Frags F;
-  Pp::zero(acc);
-  int cj = 0, cks = 0;
-  bool pending = false;  // tile cj - 1 awaits its epilogue
-  for (int g = 0; g < steps; ++g) {
-    const bool active = g < total;
-    if (active) Pp::wait_stage(issued - g - 1);
-    block_barrier();
-    if (active) {
-      if (pending) {
-        prob.epilogue(prob.tile(lo + q + (cj - 1) * Gx), acc);
-        Pp::zero(acc);
-        pending = false;
-      }
-      if (issued < total) issue();
-      Pp::load_frags(gsm + (g % Pp::NS) * Pp::STAGE, F);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
-    block_barrier();
-    if (active) {
-      Pp::mfma_all(F, acc);
-      if (++cks == KT) {
-        cks = 0;
-        ++cj;
-        pending = true;
-      }
-    }
-  }
-  if (grp == 0) block_barrier();
-  if (pending) prob.epilogue(prob.tile(lo + q + (cj - 1) * Gx), acc);
-}
-
 // ------------------------------------------------------------ dense GEMMs --
 struct DenseSeg {
   const char* B[2];   // weight rows of K part 0 / 1 (gate rows for a GLU)
@@ -546,7 +438,7 @@ struct DenseProb {
 // TAG only names the launch (0: the h GEMM of a forward, 1: router logits
 // alone, 2: the output GEMM) so that profiles tell the dense GEMMs apart.
 template <class Pp, int TAG>
-__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::GROUPS * Pp::NW / 4) void k_gemm_dense(const DenseArgs args) {
+__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_dense(const DenseArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
   // Per-column offsets go through LDS: a vector load in the epilogue would
   // have to wait for every stage DMA in flight.  Copied before the first DMA.
@@ -558,10 +450,7 @@ __global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::GROUPS * Pp::NW / 4) voi
   }
   __syncthreads();
   DenseProb<Pp> prob{args, (const __attribute__((address_space(3))) float*)col_lds};
-  if constexpr (Pp::PP)
-    stream_pp<Pp>(prob, smem);
-  else
-    stream<Pp>(prob, smem);
+  stream<Pp>(prob, smem);
 }
 
 // ---------------------------------------------------------- expert GEMMs --
@@ -651,21 +540,18 @@ struct ExpertProb {
 };
 
 template <class Pp, int KIND>
-__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::GROUPS * Pp::NW / 4) void k_gemm_expert(const ExpertArgs args) {
+__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expert(const ExpertArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
   ExpertProb<Pp, KIND> prob{args};
-  if constexpr (Pp::PP)
-    stream_pp<Pp>(prob, smem);
-  else
-    stream<Pp>(prob, smem);
+  stream<Pp>(prob, smem);
 }
 
-// Tile shapes and pipeline depths: BM, BN, WM, WN, NS, RB, BPC, PP.
+// Tile shapes and pipeline depths: BM, BN, WM, WN, NS, RB, BPC.
 #ifndef MOE_DENSE_CFG
-#define MOE_DENSE_CFG 128, 128, 2, 2, 2, 128, 2, 0
+#define MOE_DENSE_CFG 128, 128, 2, 2, 2, 128, 2
 #endif
 #ifndef MOE_EXPERT_CFG
-#define MOE_EXPERT_CFG kExpertBM, 256, 1, 4, 2, 128, 2, 0
+#define MOE_EXPERT_CFG kExpertBM, 256, 1, 4, 2, 128, 2
 #endif
 template <bool BF16>
 using DensePipe = Pipe<MOE_DENSE_CFG, BF16>;
@@ -677,12 +563,10 @@ constexpr int kCUs = 256;
 
 static int esz(const Dims& D) { return D.bf16 ? 2 : 4; }
 
-// Persistent grid: at most bpc blocks per CU, a multiple of 8; a block runs
-// `groups` tile streams.
-static int persistent_grid(long long tiles, int bpc, int groups) {
+// Persistent grid: at most bpc blocks per CU, a multiple of 8.
+static int persistent_grid(long long tiles, int bpc) {
   long long g = (long long)kCUs * bpc;
-  const long long streams = (tiles + groups - 1) / groups;
-  if (streams < g) g = (streams + 7) / 8 * 8;
+  if (tiles < g) g = (tiles + 7) / 8 * 8;
   return (int)(g < 8 ? 8 : g);
 }
 
@@ -691,7 +575,7 @@ static hipError_t launch_dense(const DenseArgs& a, hipStream_t s) {
   using P = DensePipe<BF16>;
   const long long tiles = (long long)a.m_tiles * a.total_ntiles;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_dense<P, TAG>), dim3(persistent_grid(tiles, P::BPC, P::GROUPS)), dim3(P::THREADS), 0, s,
+  hipLaunchKernelGGL((k_gemm_dense<P, TAG>), dim3(persistent_grid(tiles, P::BPC)), dim3(P::THREADS), 0, s,
                      a);
   return hipGetLastError();
 }
@@ -806,7 +690,7 @@ template <int KIND>
 static hipError_t launch_expert(const Dims& D, const ExpertArgs& a, int T, hipStream_t s) {
   const long long tiles = (long long)expert_max_mtiles(T, D.k, D.E) * a.NT;
   if (tiles == 0) return hipSuccess;
-  const int grid = persistent_grid(tiles, ExpertPipe<true>::BPC, ExpertPipe<true>::GROUPS);
+  const int grid = persistent_grid(tiles, ExpertPipe<true>::BPC);
   if (D.bf16)
     hipLaunchKernelGGL((k_gemm_expert<ExpertPipe<true>, KIND>), dim3(grid), dim3(ExpertPipe<true>::THREADS), 0, s, a);
   else
