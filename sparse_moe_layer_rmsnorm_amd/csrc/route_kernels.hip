@@ -260,15 +260,18 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
 // integer atomics (order-free) and adds them to its own rows of its own slice
 // (no other block of the launch writes them), so no reduction pass is needed
 // per forward; qb_update sums the slices.
-__global__ __launch_bounds__(512) void k_hist(const float* __restrict__ logits, int T, int E, int B, int tps,
-                                              uint32_t* __restrict__ hist, unsigned long long* __restrict__ count) {
+constexpr int kHistThreads = 1024;
+__global__ __launch_bounds__(kHistThreads) void k_hist(const float* __restrict__ logits, int T, int E, int B,
+                                                       int tps, uint32_t* __restrict__ hist,
+                                                       unsigned long long* __restrict__ count) {
+  constexpr int TR = kHistThreads / kHistExperts;  // token rows in flight per step
   __shared__ uint32_t lh[kHistExperts * 256];
   const int e0 = blockIdx.x * kHistExperts, ts = blockIdx.y;
   const int ne = min(kHistExperts, E - e0);
   const int nb = kHistExperts * B;
-  for (int i = threadIdx.x; i < nb; i += 512) lh[i] = 0;
+  for (int i = threadIdx.x; i < nb; i += kHistThreads) lh[i] = 0;
   __syncthreads();
-  // thread -> expert e0 + (i % 16), tokens (i / 16) + 32 m: each wavefront
+  // thread -> expert e0 + (i % 16), tokens (i / 16) + TR m: each wavefront
   // reads four 64-byte row pieces per step
   const int el = threadIdx.x % kHistExperts, tl = threadIdx.x / kHistExperts;
   const int e = e0 + el;
@@ -276,20 +279,17 @@ __global__ __launch_bounds__(512) void k_hist(const float* __restrict__ logits, 
   if (e < E) {
     uint32_t* row = lh + el * B;
     int t = tb + tl;
-    for (; t + 96 < te; t += 128) {
-      const float l0 = logits[(size_t)t * E + e], l1 = logits[(size_t)(t + 32) * E + e];
-      const float l2 = logits[(size_t)(t + 64) * E + e], l3 = logits[(size_t)(t + 96) * E + e];
+    for (; t + TR < te; t += 2 * TR) {
+      const float l0 = logits[(size_t)t * E + e], l1 = logits[(size_t)(t + TR) * E + e];
       atomicAdd(&row[score_bin(router_sigmoid(l0), B)], 1u);
       atomicAdd(&row[score_bin(router_sigmoid(l1), B)], 1u);
-      atomicAdd(&row[score_bin(router_sigmoid(l2), B)], 1u);
-      atomicAdd(&row[score_bin(router_sigmoid(l3), B)], 1u);
     }
-    for (; t < te; t += 32) atomicAdd(&row[score_bin(router_sigmoid(logits[(size_t)t * E + e]), B)], 1u);
+    for (; t < te; t += TR) atomicAdd(&row[score_bin(router_sigmoid(logits[(size_t)t * E + e]), B)], 1u);
   }
   __syncthreads();
   if (tb < T) {
     uint32_t* dst = hist + ((size_t)ts * E + e0) * B;
-    for (int i = threadIdx.x; i < ne * B; i += 512) {
+    for (int i = threadIdx.x; i < ne * B; i += kHistThreads) {
       const uint32_t v = lh[i];
       if (v) dst[i] += v;
     }
@@ -301,7 +301,7 @@ hipError_t launch_hist(const Dims& D, const float* logits, int T, uint32_t* hist
                        hipStream_t s) {
   const int tps = (T + kHistSlices - 1) / kHistSlices;
   dim3 grid((D.E + kHistExperts - 1) / kHistExperts, kHistSlices);
-  hipLaunchKernelGGL(k_hist, grid, dim3(512), 0, s, logits, T, D.E, D.B, tps, hist, count);
+  hipLaunchKernelGGL(k_hist, grid, dim3(kHistThreads), 0, s, logits, T, D.E, D.B, tps, hist, count);
   return hipGetLastError();
 }
 
@@ -398,38 +398,39 @@ hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cb
 }
 
 // -------------------------------------------------------------- scatter ----
-// Stable rows without order-dependent atomics.  One wavefront per token:
-// lane j < k finds the row of (t, j) in expert e's group as the super-chunk
-// base + the chunk base + the number of earlier tokens of the chunk in the
-// chunk's mask for e; then the wavefront copies the token's latent row z[t]
-// to the dispatch buffer X at each of its k rows (coalesced 16-byte pieces).
+// Stable rows without order-dependent atomics.  Two tokens per wavefront, one
+// per half: lane j < k of a half finds the row of (t, j) in expert e's group
+// as the super-chunk base + the chunk base + the number of earlier tokens of
+// the chunk in the chunk's mask for e; then the half copies the token's latent
+// row z[t] to the dispatch buffer X at each of its k rows (16-byte pieces).
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, const uint32_t* __restrict__ bitmap,
                                                  const int32_t* __restrict__ cbase, const int32_t* __restrict__ sbase,
                                                  const uint4* __restrict__ z, int T, int E, int k, int row16,
                                                  int32_t* __restrict__ perm_src, int32_t* __restrict__ inv,
                                                  uint4* __restrict__ X) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const int lane = threadIdx.x & 63, half = lane >> 5, hl = lane & 31;
+  const int t = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + half;
+  const bool live = t < T;
   const int Tk = T * k;
   int my_row = -1;
-  if (lane < k) {
-    const int e = idx[(size_t)t * k + lane];
+  if (live && hl < k) {
+    const int e = idx[(size_t)t * k + hl];
     const int c = t / kChunk;
     const size_t ce = (size_t)c * E + e;
     const uint32_t below = bitmap[ce] & ((1u << (t % kChunk)) - 1u);
     const int row = sbase[(size_t)(c / kSuper) * E + e] + cbase[ce] + __popc(below);
-    inv[(size_t)t * k + lane] = row;
+    inv[(size_t)t * k + hl] = row;
     if ((unsigned)row < (unsigned)Tk) {  // always true for a consistent permutation
       perm_src[row] = t;
       my_row = row;
     }
   }
+  if (!live) return;
   const uint4* src = z + (size_t)t * row16;
-  for (int c = lane; c < row16; c += 64) {
+  for (int c = hl; c < row16; c += 32) {
     const uint4 v = src[c];
     for (int j = 0; j < k; ++j) {
-      const int row = __builtin_amdgcn_readlane(my_row, j);
+      const int row = __shfl(my_row, (lane & 32) + j, 64);
       if (row >= 0) X[(size_t)row * row16 + c] = v;
     }
   }
@@ -439,7 +440,7 @@ hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bit
                           const int32_t* sbase, int T, const void* z, int32_t* perm_src, int32_t* inv, void* X,
                           hipStream_t s) {
   const int row16 = (z && X) ? D.l * (D.bf16 ? 2 : 4) / 16 : 0;  // routing only: no dispatch copy
-  hipLaunchKernelGGL(k_scatter, dim3((T + 3) / 4), dim3(256), 0, s, idx, bitmap, cbase, sbase,
+  hipLaunchKernelGGL(k_scatter, dim3((T + 7) / 8), dim3(256), 0, s, idx, bitmap, cbase, sbase,
                      static_cast<const uint4*>(z), T, D.E, D.k, row16, perm_src, inv, static_cast<uint4*>(X));
   return hipGetLastError();
 }
