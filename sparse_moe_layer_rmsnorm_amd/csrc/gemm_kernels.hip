@@ -338,7 +338,10 @@ struct DenseArgs {
   DenseSeg seg[3];
 };
 
-constexpr int kGroupM = 8;
+// Logical tile order: groups of kGroupM m-tiles, m fastest inside a group.
+// Measured on the replica h GEMM (8192 x 4608 x 1024): groups of 1-3 m-tiles
+// run 7-9% faster than 8 and 30% faster than 64.
+constexpr int kGroupM = 2;
 
 template <class Pp>
 struct DenseProb {
@@ -354,7 +357,6 @@ struct DenseProb {
   MOE_DEV int kt() const { return a.kt[0] + a.kt[1]; }
   MOE_DEV const DenseSeg& seg(int s) const { return s == 0 ? a.seg[0] : (s == 1 ? a.seg[1] : a.seg[2]); }
 
-  // groups of kGroupM m-tiles, m fastest inside a group
   MOE_DEV Tile tile(int L) const {
     const int per_group = kGroupM * a.total_ntiles;
     const int group = L / per_group;
