@@ -430,7 +430,10 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
   for (int c = hl; c < row16; c += 32) {
     const uint4 v = src[c];
     for (int j = 0; j < k; ++j) {
-      const int row = __shfl(my_row, (lane & 32) + j, 64);
+      // readlane, not a shuffle: lanes past row16 are inactive in this loop,
+      // and a shuffle returns nothing from an inactive source lane
+      const int r0 = __builtin_amdgcn_readlane(my_row, j), r1 = __builtin_amdgcn_readlane(my_row, 32 + j);
+      const int row = half ? r1 : r0;
       if (row >= 0) X[(size_t)row * row16 + c] = v;
     }
   }
@@ -467,8 +470,9 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ Y, con
   for (int q = lane; q < nq; q += 64) {
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
     for (int j = 0; j < k; ++j) {
-      const int row = __shfl(my_row, j, 64);
-      const float g = __shfl(my_g, j, 64);
+      // readlane, not a shuffle: lanes past l/4 are inactive in this loop
+      const int row = __builtin_amdgcn_readlane(my_row, j);
+      const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), j));
       if (BF16) {
         const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(Y) + (size_t)row * l + 4 * q);
         a0 += g * bf16_bits_to_f32(v.x & 0xFFFFu);

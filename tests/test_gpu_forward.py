@@ -36,19 +36,15 @@ def _run(shape, T, *, bias=None, c=None, step=0, compare_inner=True, layer=None,
     assert rel_err(lg, ref_own["logits"]) <= LOGIT_TOL[shape.dtype]
     ref = o.forward(x, W, b, k=shape.k, dtype=shape.dtype, eps=shape.rms_eps, B=shape.B, logits=lg)
     assert_routing_equal(r, ref, T)
+    if compare_inner:  # intermediates first: a failure then names the first wrong step
+        v = layer.ws_views(T)
+        for name in ("h", "z") + (("G",) if shape.f_s else ()) + ("H", "Y", "y_lat"):
+            e = rel_err(to_np(v[name]), ref[name])
+            say(f"  {name} rel err {e:.3e}")
+            assert e <= OUT_TOL[shape.dtype], name
     err = rel_err(to_np(out), ref["out"])
     say(f"  out rel err {err:.3e}")
     assert err <= OUT_TOL[shape.dtype]
-    if compare_inner:
-        v = layer.ws_views(T)
-        for name in ("h", "z", "y_lat") + (("G",) if shape.f_s else ()):
-            e = rel_err(to_np(v[name]), ref[name])
-            say(f"  {name} rel err {e:.3e}")
-            assert e <= OUT_TOL[shape.dtype], name
-        for name in ("H", "Y"):
-            e = rel_err(to_np(v[name]), ref[name])
-            say(f"  {name} rel err {e:.3e}")
-            assert e <= OUT_TOL[shape.dtype], name
     if own:
         layer.close()
     return ref, out
@@ -119,4 +115,39 @@ def test_replica_full_size_sampled():
     err = rel_err(out[pick], want)
     say(f"  sampled out rel err {err:.3e}")
     assert err <= OUT_TOL["bf16"]
+    layer.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_odd_widths(dtype):
+    """Widths that are multiples of 64 but not of the tiles: d=192, l=64,
+    f=192, f_s=320, E=96 (partial router and latent tiles, 96 experts over
+    64-lane columns), k=7, and a ragged T."""
+    say(f"forward odd widths {dtype}")
+    shape = wl.LayerShape("odd", 10, dtype, T=1, d=192, l=64, E=96, k=7, f=192, f_s=320)
+    _run(shape, 203, bias=(np.random.default_rng(3).standard_normal(96) * 0.03).astype(F32))
+
+
+def test_forward_k_max_and_single_expert():
+    """k = 32 of E = 64 (the largest k), then E = k = 1 (one expert takes every token)."""
+    say("forward k=32 of 64")
+    _run(wl.LayerShape("kmax", 11, "bf16", T=1, d=128, l=64, E=64, k=32, f=64, f_s=64), 96)
+    say("forward E=k=1")
+    _run(wl.LayerShape("one", 12, "bf16", T=1, d=128, l=64, E=1, k=1, f=128, f_s=0), 130)
+
+
+def test_forward_is_deterministic():
+    """Two forwards of the same batch give bit-identical outputs and routing
+    (no order-dependent atomics anywhere on the path)."""
+    shape = wl.workload("replica", 2048)
+    W = wl.make_weights(shape)
+    layer = make_layer(shape, W, max_tokens=shape.T, frozen=True)
+    xt = x_on_gpu(wl.make_x(shape), layer)
+    r1, r2 = layer.route_buffers(shape.T), layer.route_buffers(shape.T)
+    o1 = layer.forward(xt, route=r1).clone()
+    o2 = layer.forward(xt, route=r2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    for key in r1:
+        assert torch.equal(r1[key], r2[key]), key
     layer.close()
