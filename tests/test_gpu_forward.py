@@ -151,3 +151,29 @@ def test_forward_is_deterministic():
     for key in r1:
         assert torch.equal(r1[key], r2[key]), key
     layer.close()
+
+
+def test_forward_many_experts():
+    """E = 1024 experts, k = 32 (the ABI's limits), small widths."""
+    say("forward E=1024 k=32")
+    _run(wl.LayerShape("wide", 13, "bf16", T=1, d=128, l=64, E=1024, k=32, f=64, f_s=64), 300,
+         bias=(np.random.default_rng(13).standard_normal(1024) * 0.02).astype(F32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_route_from_x_odd_shape(dtype):
+    """The routing-only pass from x (RMSNorm + the router-only GEMM) on odd
+    widths: routing bit-exact from its own logits, logits by tolerance."""
+    shape = wl.LayerShape("odd", 14, dtype, T=1, d=320, l=64, E=96, k=5, f=64, f_s=0)
+    T = 257
+    W = wl.make_weights(shape)
+    x = wl.make_x(shape.with_tokens(T))
+    layer = make_layer(shape, W, max_tokens=T)
+    r = layer.route(T, x=x_on_gpu(x, layer))
+    torch.cuda.synchronize()
+    lg = to_np(r["logits"])
+    ref_own = o.forward(x, W, np.zeros(96, F32), k=shape.k, dtype=dtype, eps=shape.rms_eps, B=shape.B)
+    assert rel_err(lg, ref_own["logits"]) <= LOGIT_TOL[dtype]
+    ref = o.forward(x, W, np.zeros(96, F32), k=shape.k, dtype=dtype, eps=shape.rms_eps, B=shape.B, logits=lg)
+    assert_routing_equal(r, ref, T)
+    layer.close()

@@ -72,7 +72,8 @@ def test_sigmoid_bitexact_sweep():
     layer.close()
 
 
-@pytest.mark.parametrize("E,k,T,B", [(16, 2, 256, 256), (256, 6, 8192, 256), (896, 16, 4096, 256), (33, 3, 999, 64)])
+@pytest.mark.parametrize("E,k,T,B", [(16, 2, 256, 256), (256, 6, 8192, 256), (896, 16, 4096, 256), (33, 3, 999, 64),
+                                     (8, 2, 100, 2), (1024, 32, 700, 3)])
 def test_qb_update_bitexact(E, k, T, B):
     say(f"qb_update E={E} k={k} T={T} B={B}")
     rng = np.random.default_rng(E + T)
