@@ -218,11 +218,58 @@ struct Pipe {
   //   EPI_STORE: store in the activation dtype (N a multiple of 4).
   //   EPI_GLU:   tile columns alternate 16 gate / 16 up; output column
   //              n0/2 + 16*(c/32) + c%16 gets silu(gate) * up.
+  // bf16 outputs of two adjacent 16-column blocks as one 16-byte store per
+  // lane: lanes l and l^16 (column quads q, q^1) swap one block's quad, so
+  // an even-q lane holds columns 4q..4q+7 of the first block and an odd-q
+  // lane columns 4(q-1)..4q+3 of the second.  Every lane takes part in the
+  // swap; the stores are then masked.  c0 is the first block's first column.
+  MOE_DEV static void store_pair(void* out, size_t orow, int c0, int N, bool row_ok, const float (&x)[4],
+                                 const float (&y)[4]) {
+    const int lane = threadIdx.x & 63, q = (lane >> 4) & 3;
+    const bool odd = q & 1;
+    const uint32_t a0 = pack_bf16x2(x[0], x[1]), a1 = pack_bf16x2(x[2], x[3]);
+    const uint32_t b0 = pack_bf16x2(y[0], y[1]), b1 = pack_bf16x2(y[2], y[3]);
+    const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? a0 : b0), 16, 64);
+    const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? a1 : b1), 16, 64);
+    const uint4 v = odd ? make_uint4(r0, r1, b0, b1) : make_uint4(a0, a1, r0, r1);
+    const int c = c0 + (odd ? 16 + 4 * (q - 1) : 4 * q);
+    if (row_ok && c < N) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + orow + c) = v;
+  }
+
   template <int KIND>
   MOE_DEV static void epilogue(const Acc& acc, int rows_valid, int n0, int N, void* out, int ldo, size_t row_base,
                                const __attribute__((address_space(3))) float* col_off) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / WN, wn = wave % WN;
+    if constexpr (BF16 && KIND != EPI_F32 && NI % 4 == 0) {  // paired 16-byte stores (N is a multiple of 64)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int m = wm * WTM + mi * 16 + (lane & 15);
+        const bool row_ok = m < rows_valid;
+        const size_t orow = (row_base + (size_t)(row_ok ? m : 0)) * (size_t)ldo;
+        if constexpr (KIND == EPI_GLU) {
+#pragma unroll
+          for (int p = 0; p < NI / 2; p += 2) {
+            float o[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const f32x4_t g = acc[mi][2 * (p + h)], u = acc[mi][2 * (p + h) + 1];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) o[h][r] = g[r] * u[r] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[r]));
+            }
+            store_pair(out, orow, n0 / 2 + ((wn * WTN) / 32 + p) * 16, N, row_ok, o[0], o[1]);
+          }
+        } else {
+#pragma unroll
+          for (int ni = 0; ni < NI; ni += 2) {
+            const float x[4] = {acc[mi][ni][0], acc[mi][ni][1], acc[mi][ni][2], acc[mi][ni][3]};
+            const float y[4] = {acc[mi][ni + 1][0], acc[mi][ni + 1][1], acc[mi][ni + 1][2], acc[mi][ni + 1][3]};
+            store_pair(out, orow, n0 + wn * WTN + ni * 16, N, row_ok, x, y);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       const int m = wm * WTM + mi * 16 + (lane & 15);
