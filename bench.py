@@ -49,8 +49,9 @@ def kernel_work(s, T: int) -> dict:
     }
     bytes_ = {
         "rmsnorm": 2.0 * T * s.d * es + 4 * s.d,
-        "topk": 4.0 * T * s.E + 8.0 * Tk + 4.0 * nchunks * s.E + 4 * s.E,
-        "hist": 4.0 * T * s.E,
+        # scores, top-k, gates, masks; in training the same launch also adds
+        # the score histogram into its 16 token slices (read + write)
+        "topk": 4.0 * T * s.E + 8.0 * Tk + 4.0 * nchunks * s.E + 4 * s.E + 8.0 * 16 * s.E * s.B,
         "scan": 12.0 * nchunks * s.E + 16.0 * s.E,
         "scatter": 4.0 * Tk + 8.0 * Tk + 8.0 * nchunks * s.E,
         "combine": 1.0 * Tk * s.l * es + 8.0 * Tk + 1.0 * T * s.l * es,
@@ -233,7 +234,7 @@ def main() -> int:
     # expert GEMMs together, and routing + permutation + combine together
     ex_us = sum(kernels[n]["avg_us"] for n in ("expert_up", "expert_down") if n in kernels)
     ex_tf = (work["flops"]["expert_up"] + work["flops"]["expert_down"]) / (ex_us * 1e-6) / 1e12
-    rt_names = [n for n in ("topk", "hist", "scan", "scatter", "combine") if n in kernels]
+    rt_names = [n for n in ("topk", "scan", "scatter", "combine") if n in kernels]
     rt_us = sum(kernels[n]["avg_us"] for n in rt_names)
     rt_bytes = sum(work["bytes"].get(n, 0.0) for n in rt_names)
     layer_flops = sum(work["flops"].values())

@@ -196,7 +196,9 @@ const char* moe_last_error(void);
  * to n launches, is bracketed by HIP events on its stream.  moe_profile_end()
  * waits for those events and fills, for each kernel id 0..n_ids-1, the summed
  * milliseconds and the launch count; then profiling stops.  Host-side event
- * objects only; no device memory.
+ * objects only; no device memory.  MOE_K_HIST is kept for numbering only:
+ * in training mode the QB histogram is built inside the MOE_K_TOPK launch,
+ * so that id records no launches.
  */
 enum {
   MOE_K_RMSNORM = 0, MOE_K_GEMM_H, MOE_K_TOPK, MOE_K_HIST, MOE_K_SCAN, MOE_K_SCATTER,

@@ -28,10 +28,10 @@ struct Dims {
 };
 
 hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s);
+// Scores, biased top-k, gates and selection masks; with `hist` non-NULL
+// (training) the same launch adds the score histogram and the token count.
 hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, int T, int32_t* idx, float* gates,
-                       uint32_t* bitmap, hipStream_t s);
-hipError_t launch_hist(const Dims& D, const float* logits, int T, uint32_t* hist, unsigned long long* count,
-                       hipStream_t s);
+                       uint32_t* bitmap, uint32_t* hist, unsigned long long* count, hipStream_t s);
 // Two launches: per-super-chunk prefix, then the global prefix, the row and
 // m-tile offsets and the m-tile table tile_info[g] = {first row, expert << 8 |
 // rows in use} of the grouped GEMMs.

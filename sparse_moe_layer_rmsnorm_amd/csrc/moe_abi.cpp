@@ -199,13 +199,11 @@ moe_status check_call(moe_ctx* ctx, int64_t T, void* ws, size_t ws_bytes) {
 moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, const void* z, void* X, hipStream_t s) {
   const Dims& D = ctx->D;
   const float* bias = reinterpret_cast<const float*>(ctx->state + ctx->sl.bias);
-  MOE_RUN(MOE_K_TOPK, launch_topk(D, p.logits, bias, T, p.idx, p.gates, p.bitmap, s));
-  if (ctx->cfg.qb_mode == MOE_QB_TRAIN) {
-    uint32_t* hist = reinterpret_cast<uint32_t*>(ctx->state + ctx->sl.hist);
-    unsigned long long* cnt = reinterpret_cast<unsigned long long*>(ctx->state + ctx->sl.count);
-    MOE_RUN(MOE_K_HIST, launch_hist(D, p.logits, T, hist, cnt, s));
-    ctx->pending_tokens += (uint64_t)T;
-  }
+  const bool train = ctx->cfg.qb_mode == MOE_QB_TRAIN;
+  uint32_t* hist = train ? reinterpret_cast<uint32_t*>(ctx->state + ctx->sl.hist) : nullptr;
+  unsigned long long* cnt = reinterpret_cast<unsigned long long*>(ctx->state + ctx->sl.count);
+  MOE_RUN(MOE_K_TOPK, launch_topk(D, p.logits, bias, T, p.idx, p.gates, p.bitmap, hist, cnt, s));
+  if (train) ctx->pending_tokens += (uint64_t)T;
   MOE_RUN(MOE_K_SCAN,
           launch_scan(D, p.bitmap, T, p.cbase, p.sbase, p.counts, p.offsets, p.tile_offsets, p.tile_info, s));
   MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.bitmap, p.cbase, p.sbase, T, z, p.perm_src, p.inv, X, s));

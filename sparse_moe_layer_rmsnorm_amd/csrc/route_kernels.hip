@@ -204,12 +204,10 @@ constexpr int kTopkNT = MOE_TOPK_NT;                    // tokens ranked side by
 constexpr int kTopkThreads = kChunk / kTopkNT * 64;      // one token group per wavefront
 
 template <int CPL>
-__global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ logits,
-                                                       const float* __restrict__ bias, int T, int E, int k,
-                                                       float scale, int32_t* __restrict__ idx,
-                                                       float* __restrict__ gates, uint32_t* __restrict__ bitmap) {
+MOE_DEV void topk_block(int chunk, uint32_t* mask, const float* __restrict__ logits, const float* __restrict__ bias,
+                        int T, int E, int k, float scale, int32_t* __restrict__ idx, float* __restrict__ gates,
+                        uint32_t* __restrict__ bitmap) {
   constexpr int NW = kChunk / kTopkNT;
-  __shared__ uint32_t mask[1024];
   for (int i = threadIdx.x; i < E; i += kTopkThreads) mask[i] = 0u;
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -223,7 +221,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
   int n = 0;
 #pragma unroll
   for (int u = 0; u < kTopkNT; ++u) {
-    t[u] = blockIdx.x * kChunk + wave + NW * u;
+    t[u] = chunk * kChunk + wave + NW * u;
     n += t[u] < T;
   }
   if (n == kTopkNT) {
@@ -235,23 +233,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < E; i += kTopkThreads) bitmap[(size_t)blockIdx.x * E + i] = mask[i];
-}
-
-hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, int T, int32_t* idx, float* gates,
-                       uint32_t* bitmap, hipStream_t s) {
-  const int nchunks = (T + kChunk - 1) / kChunk;
-  const int cpl = (D.E + 63) / 64;
-  dim3 grid(nchunks), block(kTopkThreads);
-#define MOE_TOPK(C) \
-  hipLaunchKernelGGL(k_topk<C>, grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, bitmap)
-  if (cpl <= 1) MOE_TOPK(1);
-  else if (cpl <= 2) MOE_TOPK(2);
-  else if (cpl <= 4) MOE_TOPK(4);
-  else if (cpl <= 8) MOE_TOPK(8);
-  else MOE_TOPK(16);
-#undef MOE_TOPK
-  return hipGetLastError();
+  for (int i = threadIdx.x; i < E; i += kTopkThreads) bitmap[(size_t)chunk * E + i] = mask[i];
 }
 
 // ---------------------------------------------------------- QB histogram ----
@@ -260,16 +242,13 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
 // integer atomics (order-free) and adds them to its own rows of its own slice
 // (no other block of the launch writes them), so no reduction pass is needed
 // per forward; qb_update sums the slices.
-constexpr int kHistThreads = 1024;
-__global__ __launch_bounds__(kHistThreads) void k_hist(const float* __restrict__ logits, int T, int E, int B,
-                                                       int tps, uint32_t* __restrict__ hist,
-                                                       unsigned long long* __restrict__ count) {
-  constexpr int TR = kHistThreads / kHistExperts;  // token rows in flight per step
-  __shared__ uint32_t lh[kHistExperts * 256];
-  const int e0 = blockIdx.x * kHistExperts, ts = blockIdx.y;
+MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict__ logits, int T, int E, int B,
+                        int tps, uint32_t* __restrict__ hist, unsigned long long* __restrict__ count) {
+  constexpr int TR = kTopkThreads / kHistExperts;  // token rows in flight per step
+  const int e0 = group * kHistExperts;
   const int ne = min(kHistExperts, E - e0);
   const int nb = kHistExperts * B;
-  for (int i = threadIdx.x; i < nb; i += kHistThreads) lh[i] = 0;
+  for (int i = threadIdx.x; i < nb; i += kTopkThreads) lh[i] = 0;
   __syncthreads();
   // thread -> expert e0 + (i % 16), tokens (i / 16) + TR m: each wavefront
   // reads four 64-byte row pieces per step
@@ -289,19 +268,50 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(const float* __restrict__
   __syncthreads();
   if (tb < T) {
     uint32_t* dst = hist + ((size_t)ts * E + e0) * B;
-    for (int i = threadIdx.x; i < ne * B; i += kHistThreads) {
+    for (int i = threadIdx.x; i < ne * B; i += kTopkThreads) {
       const uint32_t v = lh[i];
       if (v) dst[i] += v;
     }
   }
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *count += (unsigned long long)T;
+  if (group == 0 && ts == 0 && threadIdx.x == 0) *count += (unsigned long long)T;
 }
 
-hipError_t launch_hist(const Dims& D, const float* logits, int T, uint32_t* hist, unsigned long long* count,
-                       hipStream_t s) {
+// One launch for the scores: blocks [0, nchunks) rank the chunks; in
+// training mode blocks past them build the QB histogram from the same
+// logits (independent work side by side instead of two launches).
+template <int CPL>
+__global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ logits,
+                                                       const float* __restrict__ bias, int T, int E, int k,
+                                                       float scale, int32_t* __restrict__ idx,
+                                                       float* __restrict__ gates, uint32_t* __restrict__ bitmap,
+                                                       int nchunks, int B, int tps, uint32_t* __restrict__ hist,
+                                                       unsigned long long* __restrict__ count) {
+  __shared__ uint32_t smem[kHistExperts * 256];
+  static_assert(kHistExperts * 256 >= 1024, "the top-k masks fit");
+  if ((int)blockIdx.x < nchunks) {
+    topk_block<CPL>(blockIdx.x, smem, logits, bias, T, E, k, scale, idx, gates, bitmap);
+  } else {
+    const int hb = blockIdx.x - nchunks, groups = (E + kHistExperts - 1) / kHistExperts;
+    hist_block(hb % groups, hb / groups, smem, logits, T, E, B, tps, hist, count);
+  }
+}
+
+hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, int T, int32_t* idx, float* gates,
+                       uint32_t* bitmap, uint32_t* hist, unsigned long long* count, hipStream_t s) {
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const int cpl = (D.E + 63) / 64;
   const int tps = (T + kHistSlices - 1) / kHistSlices;
-  dim3 grid((D.E + kHistExperts - 1) / kHistExperts, kHistSlices);
-  hipLaunchKernelGGL(k_hist, grid, dim3(kHistThreads), 0, s, logits, T, D.E, D.B, tps, hist, count);
+  const int hblocks = hist ? (D.E + kHistExperts - 1) / kHistExperts * kHistSlices : 0;
+  dim3 grid(nchunks + hblocks), block(kTopkThreads);
+#define MOE_TOPK(C)                                                                                                 \
+  hipLaunchKernelGGL(k_topk<C>, grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, bitmap, \
+                     nchunks, D.B, tps, hist, count)
+  if (cpl <= 1) MOE_TOPK(1);
+  else if (cpl <= 2) MOE_TOPK(2);
+  else if (cpl <= 4) MOE_TOPK(4);
+  else if (cpl <= 8) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
   return hipGetLastError();
 }
 
