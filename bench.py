@@ -15,7 +15,6 @@ the CPU oracle's tokens/s on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,6 +29,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+from sparse_moe_layer_rmsnorm_amd.profsum import source_hash  # noqa: E402
 
 METRIC = "MoE-layer fwd tokens/sec on 1 MI355X + % bf16 MFMA peak + routing GB/s"
 
@@ -53,21 +53,13 @@ def kernel_work(s, T: int) -> dict:
         # the score histogram into its 16 token slices (read + write)
         "topk": 4.0 * T * s.E + 8.0 * Tk + 4.0 * nchunks * s.E + 4 * s.E + 8.0 * 16 * s.E * s.B,
         "scan": 12.0 * nchunks * s.E + 16.0 * s.E,
-        "scatter": 4.0 * Tk + 8.0 * Tk + 8.0 * nchunks * s.E,
+        # rows and inverse rows, plus the dispatch copy X[r] = z[perm_src[r]]
+        "scatter": 4.0 * Tk + 8.0 * Tk + 8.0 * nchunks * s.E + 1.0 * T * s.l * es + 1.0 * Tk * s.l * es,
         "combine": 1.0 * Tk * s.l * es + 8.0 * Tk + 1.0 * T * s.l * es,
         "qb_quantile": 8.0 * 16 * s.E * s.B,
         "qb_bias": 20.0 * s.E,
     }
     return {"flops": flops, "bytes": bytes_}
-
-
-def source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_moe_layer_rmsnorm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel: str, workload: str):

@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 output for the layer's kernels (text for profiles/).
 
     python -m sparse_moe_layer_rmsnorm_amd.profsum trace <kernel_trace.csv> <workload> "<command>"
-    python -m sparse_moe_layer_rmsnorm_amd.profsum traffic <fetch.csv> <write.csv> <workload> "<command>"
+    python -m sparse_moe_layer_rmsnorm_amd.profsum traffic <fetch.csv> <write.csv> <workload> "<command>" [json]
 
 `trace` prints a markdown table of per-kernel launch counts and durations
 from a `--kernel-trace` CSV.  `traffic` reads two `--pmc FETCH_SIZE` and
@@ -9,7 +9,9 @@ from a `--kernel-trace` CSV.  `traffic` reads two `--pmc FETCH_SIZE` and
 what it reads for the plain 256 MiB device copy that `bench.py
 --copy-calibration` runs first, and prints a markdown table plus the JSON
 record (HBM bytes per launch per kernel) that bench.py reports as
-`roofline.traffic`.
+`roofline.traffic`; with a fifth argument it also writes that record, keyed
+by a hash of the kernel sources, to the given JSON file (bench.py reports the
+figure only while the sources still hash the same).
 
 The dense GEMM launches carry a tag template argument: 0 the h GEMM of a
 forward (gemm_h), 1 router logits alone (gemm_rz, routing-only pass), 2 the
@@ -20,11 +22,23 @@ expert_down.
 from __future__ import annotations
 
 import csv
+import hashlib
 import json
+import os
 import sys
 from collections import OrderedDict, defaultdict
 
 COPY_BYTES = 256 << 20
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def source_hash() -> str:
+    """Hash of the HIP/C++ sources: counter figures are valid for one hash."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
 
 
 def logical_name(symbol: str, dense_seen: int) -> str | None:
@@ -134,6 +148,14 @@ def main(argv) -> int:
         print("\n```json")
         print(json.dumps({workload: rec}, indent=1))
         print("```")
+        if len(argv) >= 6:
+            doc = {"source_hash": source_hash(),
+                   "note": "HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, each scaled by its 256 MiB device-copy "
+                           "factor); source_hash covers the kernel sources the counters were taken on",
+                   "kernels": {workload: rec}}
+            with open(argv[5], "w") as f:
+                json.dump(doc, f, indent=1)
+                f.write("\n")
         return 0
     print(__doc__)
     return 2
