@@ -53,8 +53,8 @@ def kernel_work(s, T: int) -> dict:
         # the score histogram into its 16 token slices (read + write)
         "topk": 4.0 * T * s.E + 8.0 * Tk + 4.0 * nchunks * s.E + 4 * s.E + 8.0 * 16 * s.E * s.B,
         "scan": 12.0 * nchunks * s.E + 16.0 * s.E,
-        # rows and inverse rows, plus the dispatch copy X[r] = z[perm_src[r]]
-        "scatter": 4.0 * Tk + 8.0 * Tk + 8.0 * nchunks * s.E + 1.0 * T * s.l * es + 1.0 * Tk * s.l * es,
+        # stable rows and inverse rows (the dispatch copy is in expert_up's operand load)
+        "scatter": 4.0 * Tk + 8.0 * Tk + 8.0 * nchunks * s.E,
         "combine": 1.0 * Tk * s.l * es + 8.0 * Tk + 1.0 * T * s.l * es,
         "qb_quantile": 8.0 * 16 * s.E * s.B,
         "qb_bias": 20.0 * s.E,

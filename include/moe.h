@@ -130,7 +130,8 @@ typedef struct moe_state_layout {
 /* Byte offsets, inside the workspace, of the intermediates of one call. */
 typedef struct moe_ws_layout {
   size_t h, logits, idx, gates, bitmap, cbase, sbase, counts, offsets, tile_offsets, perm_src, inv, tile_info;
-  size_t G, z, X, H, Y, y_lat;
+  size_t G, z, X, H, Y, y_lat; /* X: zero bytes (the expert GEMM reads z[perm_src[r]]
+                                  directly, so no dispatch buffer is written) */
   size_t total;
 } moe_ws_layout;
 

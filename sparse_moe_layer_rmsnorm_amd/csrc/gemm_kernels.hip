@@ -527,8 +527,9 @@ __global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_dens
 // m-tile count is tile_offsets[E].  Logical tile L -> m-tile L / NT, n-tile
 // L % NT.
 struct ExpertArgs {
-  const char* A;  // X (up) or H (down), rows grouped by expert
+  const char* A;  // z (up, gathered) or H (down, rows grouped by expert)
   int lda_bytes;
+  const int32_t* gather;  // A row of grouped row r is gather[r] (NULL: r itself)
   const char* W;   // W_g (up) or W_d (down), [E, N, K]
   const char* Wu;  // W_u (up) or nullptr
   int ldb_bytes;
@@ -584,13 +585,33 @@ struct ExpertProb {
     return base + (size_t)t.sel * a.w_expert_bytes + (size_t)wrow * uniform_int(a.ldb_bytes);
   }
 
+  // Dispatch fused into the operand load: the A rows of slot group `grp`
+  // (1024 / RB consecutive tile rows) are token rows gather[row0 + r] of z.
+  // The indices come through scalar loads (uniform addresses), so no vector
+  // load joins the DMA ring; each lane then picks the row it copies.
+  MOE_DEV const char* gathered_row_ptr(const Tile& t, int grp) const {
+    constexpr int R = 1024 / Pp::RB;
+    const int j = (threadIdx.x & 63) / Pp::CPR;
+    int src_row = 0;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int r = grp * R + q;
+      const int v = scalar_load(a.gather, t.row0 + (r < t.rows ? r : 0));
+      src_row = j == q ? v : src_row;
+    }
+    return uniform_ptr(a.A) + (size_t)src_row * uniform_int(a.lda_bytes);
+  }
+
   template <int L>
   MOE_DEV void sources(const Tile& t, SrcT<L>& src) const {
     const int lane = threadIdx.x & 63, wave = Pp::wave_id();
+    const int uwave = uniform_int(wave);
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const int row = Pp::slot_row(i, wave, lane);
-      src.p[i] = row_ptr(t, row) + Pp::slot_chunk(row, lane) * 16;
+      const int grp = i * Pp::NW + uwave;  // the slot's group of 1024 / RB rows
+      const char* p = (a.gather && grp * (1024 / Pp::RB) < Pp::BM) ? gathered_row_ptr(t, grp) : row_ptr(t, row);
+      src.p[i] = p + Pp::slot_chunk(row, lane) * 16;
     }
   }
 
@@ -766,13 +787,14 @@ static hipError_t launch_expert(const Dims& D, const ExpertArgs& a, int T, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_expert_up(const Dims& D, const void* X, const int2* tile_info, const int32_t* n_mtiles, int T,
-                            const void* W_g, const void* W_u, void* H, hipStream_t s) {
+hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_src, const int2* tile_info,
+                            const int32_t* n_mtiles, int T, const void* W_g, const void* W_u, void* H, hipStream_t s) {
   constexpr int BN = ExpertPipe<true>::BN, RB = ExpertPipe<true>::RB;
   const int es = esz(D);
   ExpertArgs a{};
-  a.A = static_cast<const char*>(X);
+  a.A = static_cast<const char*>(z);
   a.lda_bytes = D.l * es;
+  a.gather = perm_src;
   a.W = static_cast<const char*>(W_g);
   a.Wu = static_cast<const char*>(W_u);
   a.ldb_bytes = D.l * es;

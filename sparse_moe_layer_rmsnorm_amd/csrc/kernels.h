@@ -39,8 +39,7 @@ hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cb
                        int32_t* offsets, int32_t* tile_offsets, int2* tile_info, hipStream_t s);
 // Rows of the permutation, and the dispatch buffer X[row] = z[token].
 hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* cbase,
-                          const int32_t* sbase, int T, const void* z, int32_t* perm_src, int32_t* inv, void* X,
-                          hipStream_t s);
+                          const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s);
 hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, const int32_t* inv, int T,
                           void* y_lat, hipStream_t s);
 hipError_t launch_qb_quantile(const Dims& D, uint32_t* hist, const unsigned long long* count, double* q,
@@ -64,8 +63,10 @@ hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int 
 // Grouped expert GEMMs over the rows grouped by expert (m-tiles of
 // kExpertBM rows from tile_info; n_mtiles points at their count).
 int expert_max_mtiles(int T, int k, int E);
-hipError_t launch_expert_up(const Dims& D, const void* X, const int2* tile_info, const int32_t* n_mtiles, int T,
-                            const void* W_g, const void* W_u, void* H, hipStream_t s);
+// Expert GEMM 1 + GLU; its A rows are z[perm_src[r]] (the dispatch is part
+// of the operand load, no dispatch buffer is written).
+hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_src, const int2* tile_info,
+                            const int32_t* n_mtiles, int T, const void* W_g, const void* W_u, void* H, hipStream_t s);
 hipError_t launch_expert_down(const Dims& D, const void* H, const int2* tile_info, const int32_t* n_mtiles, int T,
                               const void* W_d, void* Y, hipStream_t s);
 

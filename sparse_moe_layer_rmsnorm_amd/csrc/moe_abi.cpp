@@ -107,7 +107,7 @@ void ws_layout(const moe_config* c, int64_t T, moe_ws_layout* L) {
   L->tile_info = take(T > 0 ? (size_t)expert_max_mtiles((int)T, c->k, c->E) * 8 : 0);
   L->G = take(t * c->f_s * es);
   L->z = take(t * c->l * es);
-  L->X = take(t * k * c->l * es);
+  L->X = take(0);  // no dispatch buffer: expert_up gathers z rows itself
   L->H = take(t * k * c->f * es);
   L->Y = take(t * k * c->l * es);
   L->y_lat = take(t * c->l * es);
@@ -195,8 +195,8 @@ moe_status check_call(moe_ctx* ctx, int64_t T, void* ws, size_t ws_bytes) {
 }
 
 // Steps after the logits: scores, QB histogram, top-k + gates + selection
-// masks, two-level prefix sums with offsets, stable scatter.
-moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, const void* z, void* X, hipStream_t s) {
+// masks, two-level prefix sums with offsets, stable rows (perm_src, inv).
+moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s) {
   const Dims& D = ctx->D;
   const float* bias = reinterpret_cast<const float*>(ctx->state + ctx->sl.bias);
   const bool train = ctx->cfg.qb_mode == MOE_QB_TRAIN;
@@ -206,7 +206,7 @@ moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, const void* z, vo
   if (train) ctx->pending_tokens += (uint64_t)T;
   MOE_RUN(MOE_K_SCAN,
           launch_scan(D, p.bitmap, T, p.cbase, p.sbase, p.counts, p.offsets, p.tile_offsets, p.tile_info, s));
-  MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.bitmap, p.cbase, p.sbase, T, z, p.perm_src, p.inv, X, s));
+  MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.bitmap, p.cbase, p.sbase, T, p.perm_src, p.inv, s));
   return MOE_OK;
 }
 
@@ -291,7 +291,7 @@ moe_status moe_route(moe_ctx* ctx, const void* x, const float* logits, int64_t T
     MOE_RUN(MOE_K_RMSNORM, launch_rmsnorm(D, x, ctx->w.gamma, h, t, s));
     MOE_RUN(MOE_K_GEMM_RZ, launch_gemm_rz(D, h, t, ctx->w.W_r, ctx->w.logit_offset, p.logits, s));
   }
-  return route_tail(ctx, p, t, nullptr, nullptr, s);
+  return route_tail(ctx, p, t, s);
 }
 
 moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_route_out* r, void* ws,
@@ -306,14 +306,16 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
   char* w = static_cast<char*>(ws);
   RoutePtrs p = route_ptrs(L, w, r);
   const int t = (int)T;
-  void *h = w + L.h, *G = w + L.G, *z = w + L.z, *X = w + L.X, *H = w + L.H, *Y = w + L.Y, *y_lat = w + L.y_lat;
+  void *h = w + L.h, *G = w + L.G, *z = w + L.z, *H = w + L.H, *Y = w + L.Y, *y_lat = w + L.y_lat;
   MOE_RUN(MOE_K_RMSNORM, launch_rmsnorm(D, x, ctx->w.gamma, h, t, s));
   MOE_RUN(MOE_K_GEMM_H, launch_gemm_h(D, h, t, ctx->w.W_r, ctx->w.logit_offset, ctx->w.W_sg, ctx->w.W_su,
                                       ctx->w.W_dn, p.logits, D.f_s > 0 ? G : nullptr, z, s));
-  st = route_tail(ctx, p, t, z, X, s);
+  st = route_tail(ctx, p, t, s);
   if (st != MOE_OK) return st;
   const int32_t* n_mtiles = p.tile_offsets + D.E;
-  MOE_RUN(MOE_K_EXPERT_UP, launch_expert_up(D, X, p.tile_info, n_mtiles, t, ctx->w.W_g, ctx->w.W_u, H, s));
+  // dispatch X[r] = z[perm_src[r]] happens inside expert_up's operand load
+  MOE_RUN(MOE_K_EXPERT_UP,
+          launch_expert_up(D, z, p.perm_src, p.tile_info, n_mtiles, t, ctx->w.W_g, ctx->w.W_u, H, s));
   MOE_RUN(MOE_K_EXPERT_DOWN, launch_expert_down(D, H, p.tile_info, n_mtiles, t, ctx->w.W_d, Y, s));
   MOE_RUN(MOE_K_COMBINE, launch_combine(D, Y, p.gates, p.inv, t, y_lat, s));
   MOE_RUN(MOE_K_GEMM_OUT, launch_gemm_out(D, G, y_lat, t, ctx->w.W_sd, ctx->w.W_up, out, s));

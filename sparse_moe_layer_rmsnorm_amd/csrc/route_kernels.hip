@@ -327,13 +327,14 @@ __global__ __launch_bounds__(256) void k_scan_local(const uint32_t* __restrict__
   const int sc = blockIdx.y * 4 + wave;
   const int c0 = sc * kSuper;
   if (e >= E || c0 >= nchunks) return;
-  const int c1 = min(nchunks, c0 + kSuper);
+  uint32_t m[kSuper];  // all loads of the super-chunk in flight together
+#pragma unroll
+  for (int j = 0; j < kSuper; ++j) m[j] = c0 + j < nchunks ? bitmap[(size_t)(c0 + j) * E + e] : 0u;
   int run = 0;
-  for (int c = c0; c < c1; ++c) {
-    const size_t i = (size_t)c * E + e;
-    const int v = __popc(bitmap[i]);
-    cbase[i] = run;
-    run += v;
+#pragma unroll
+  for (int j = 0; j < kSuper; ++j) {
+    if (c0 + j < nchunks) cbase[(size_t)(c0 + j) * E + e] = run;
+    run += __popc(m[j]);
   }
   sbase[(size_t)sc * E + e] = run;
 }
@@ -347,11 +348,21 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
                                                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ tile_offsets, int2* __restrict__ tile_info) {
   __shared__ int wsum_r[16], wsum_t[16];
+  constexpr int kReg = 16;  // up to this many super-chunk totals stay in registers
   const int i = threadIdx.x, lane = i & 63, w = i >> 6;
   int c = 0;
+  int v[kReg];
   if (i < E) {
+    if (nsuper <= kReg) {
+#pragma unroll
+      for (int sc = 0; sc < kReg; ++sc) {
+        v[sc] = sc < nsuper ? sbase[(size_t)sc * E + i] : 0;
+        c += v[sc];
+      }
+    } else {
 #pragma unroll 16
-    for (int sc = 0; sc < nsuper; ++sc) c += sbase[(size_t)sc * E + i];
+      for (int sc = 0; sc < nsuper; ++sc) c += sbase[(size_t)sc * E + i];
+    }
   }
   const int tl = (c + kExpertBM - 1) / kExpertBM;
   int r = c, t = tl;  // inclusive wave scans
@@ -377,12 +388,20 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
     offsets[i + 1] = r;
     tile_offsets[i + 1] = t;
     int run = r - c;  // exclusive offset of expert i
+    if (nsuper <= kReg) {
+#pragma unroll
+      for (int sc = 0; sc < kReg; ++sc) {
+        if (sc < nsuper) sbase[(size_t)sc * E + i] = run;
+        run += v[sc];
+      }
+    } else {
 #pragma unroll 16
-    for (int sc = 0; sc < nsuper; ++sc) {
-      const size_t j = (size_t)sc * E + i;
-      const int v = sbase[j];
-      sbase[j] = run;
-      run += v;
+      for (int sc = 0; sc < nsuper; ++sc) {
+        const size_t j = (size_t)sc * E + i;
+        const int x = sbase[j];
+        sbase[j] = run;
+        run += x;
+      }
     }
     const int row0 = r - c, tile0 = t - tl;
     for (int j = 0; j < tl; ++j)
@@ -408,53 +427,31 @@ hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cb
 }
 
 // -------------------------------------------------------------- scatter ----
-// Stable rows without order-dependent atomics.  Two tokens per wavefront, one
-// per half: lane j < k of a half finds the row of (t, j) in expert e's group
-// as the super-chunk base + the chunk base + the number of earlier tokens of
-// the chunk in the chunk's mask for e; then the half copies the token's latent
-// row z[t] to the dispatch buffer X at each of its k rows (16-byte pieces).
+// Stable rows without order-dependent atomics, one thread per (t, j): the row
+// of (t, j) in expert e's group is the super-chunk base + the chunk base +
+// the number of earlier tokens of the chunk in the chunk's mask for e.
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, const uint32_t* __restrict__ bitmap,
                                                  const int32_t* __restrict__ cbase, const int32_t* __restrict__ sbase,
-                                                 const uint4* __restrict__ z, int T, int E, int k, int row16,
-                                                 int32_t* __restrict__ perm_src, int32_t* __restrict__ inv,
-                                                 uint4* __restrict__ X) {
-  const int lane = threadIdx.x & 63, half = lane >> 5, hl = lane & 31;
-  const int t = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 2 + half;
-  const bool live = t < T;
+                                                 int T, int E, int k, int32_t* __restrict__ perm_src,
+                                                 int32_t* __restrict__ inv) {
   const int Tk = T * k;
-  int my_row = -1;
-  if (live && hl < k) {
-    const int e = idx[(size_t)t * k + hl];
-    const int c = t / kChunk;
-    const size_t ce = (size_t)c * E + e;
-    const uint32_t below = bitmap[ce] & ((1u << (t % kChunk)) - 1u);
-    const int row = sbase[(size_t)(c / kSuper) * E + e] + cbase[ce] + __popc(below);
-    inv[(size_t)t * k + hl] = row;
-    if ((unsigned)row < (unsigned)Tk) {  // always true for a consistent permutation
-      perm_src[row] = t;
-      my_row = row;
-    }
-  }
-  if (!live) return;
-  const uint4* src = z + (size_t)t * row16;
-  for (int c = hl; c < row16; c += 32) {
-    const uint4 v = src[c];
-    for (int j = 0; j < k; ++j) {
-      // readlane, not a shuffle: lanes past row16 are inactive in this loop,
-      // and a shuffle returns nothing from an inactive source lane
-      const int r0 = __builtin_amdgcn_readlane(my_row, j), r1 = __builtin_amdgcn_readlane(my_row, 32 + j);
-      const int row = half ? r1 : r0;
-      if (row >= 0) X[(size_t)row * row16 + c] = v;
-    }
-  }
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= Tk) return;
+  const int t = p / k;
+  const int e = idx[p];
+  const int c = t / kChunk;
+  const size_t ce = (size_t)c * E + e;
+  const uint32_t below = bitmap[ce] & ((1u << (t % kChunk)) - 1u);
+  const int row = sbase[(size_t)(c / kSuper) * E + e] + cbase[ce] + __popc(below);
+  inv[p] = row;
+  if ((unsigned)row < (unsigned)Tk) perm_src[row] = t;  // always true for a consistent permutation
 }
 
 hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* cbase,
-                          const int32_t* sbase, int T, const void* z, int32_t* perm_src, int32_t* inv, void* X,
-                          hipStream_t s) {
-  const int row16 = (z && X) ? D.l * (D.bf16 ? 2 : 4) / 16 : 0;  // routing only: no dispatch copy
-  hipLaunchKernelGGL(k_scatter, dim3((T + 7) / 8), dim3(256), 0, s, idx, bitmap, cbase, sbase,
-                     static_cast<const uint4*>(z), T, D.E, D.k, row16, perm_src, inv, static_cast<uint4*>(X));
+                          const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s) {
+  const long long Tk = (long long)T * D.k;
+  hipLaunchKernelGGL(k_scatter, dim3((unsigned)((Tk + 255) / 256)), dim3(256), 0, s, idx, bitmap, cbase, sbase, T,
+                     D.E, D.k, perm_src, inv);
   return hipGetLastError();
 }
 
