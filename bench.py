@@ -58,6 +58,7 @@ def kernel_work(s, T: int) -> dict:
         "combine": 1.0 * Tk * s.l * es + 8.0 * Tk + 1.0 * T * s.l * es,
         "qb_quantile": 8.0 * 16 * s.E * s.B,
         "qb_bias": 20.0 * s.E,
+        "sign_bias": 16.0 * s.E,
     }
     return {"flops": flops, "bytes": bytes_}
 
@@ -114,6 +115,8 @@ def main() -> int:
                     help="replay the step as a captured HIP graph (per-kernel times then come from an extra "
                          "eager pass after the timed region)")
     ap.add_argument("--no-profile", action="store_true", help="no per-kernel events in the timed region")
+    ap.add_argument("--balancer", choices=("qb", "sign"), default="qb",
+                    help="bias update rule of the step: quantile balancing (default) or the sign rule")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device copy of 256 MiB (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -137,7 +140,7 @@ def main() -> int:
     x_np = wl.make_x(shape)
     c = wl.zipf_logit_offset(shape) if shape.name == "skew" else None
     frozen = shape.qb_frozen
-    layer = layer_from_shape(shape, W, max_tokens=T, logit_offset=c, frozen=frozen)
+    layer = layer_from_shape(shape, W, max_tokens=T, logit_offset=c, frozen=frozen, balancer=args.balancer)
     if frozen:
         layer.set_bias(wl.frozen_bias(shape))
     x = torch.from_numpy(x_np).cuda().to(layer.tdtype)
@@ -248,7 +251,8 @@ def main() -> int:
             "; dominant kernel bracketed by HIP events in the timed region" if live else "") +
             "; per-kernel table from a separate profiled pass of the same K steps",
         "config": {"workload": f"{shape.name}: T={T} tokens, d={shape.d}, l={shape.l}, E={shape.E}, k={shape.k}, "
-                               f"f={shape.f}, f_s={shape.f_s}, B={shape.B}, QB {'frozen' if frozen else 'train'}",
+                               f"f={shape.f}, f_s={shape.f_s}, B={shape.B}, QB {'frozen' if frozen else 'train'}"
+                               + (", sign-rule balancer" if args.balancer == "sign" else ""),
                    "global_batch": T, "step": "training forward + qb_update"},
         "roofline": roofline,
         "layer_mfma_frac": round(layer_flops / (ms_step * 1e-3) / 1e12 / peak_mm, 4),

@@ -23,6 +23,11 @@
  * tokens and sets b_e = mean(q) - q_e (mean-centred); the new bias is used by
  * the next forward (one step late); in frozen mode nothing is accumulated or
  * updated.
+ * Sign-rule balancer (capsule 16 of the "Pretraining a Mini Kimi K3" e-book
+ * review, the noaux_tc bias rule), selected with moe_config.balancer: every
+ * training forward adds each expert's token count to a per-expert load, and
+ * the update moves each bias by sign_gamma towards balance:
+ * b_e += sign_gamma * sign(mean load - load_e).
  *
  * Conventions
  *   - Every pointer argument named as device memory is a HIP device pointer
@@ -70,11 +75,22 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum moe_qb_mode { MOE_QB_TRAIN = 0, MOE_QB_FROZEN = 1 } moe_qb_mode;
 
 /*
+ * Which rule qb_update() applies.  MOE_BALANCE_QB: quantile balancing from
+ * the score histogram (the demo article, Tab 8-10).  MOE_BALANCE_SIGN: the
+ * sign rule of capsule 16 of the e-book review, b_e += sign_gamma *
+ * sign(mean load - load_e) from the per-expert token counts (sign_gamma = 1e-2
+ * there); the histogram is then neither built nor read.
+ */
+typedef enum moe_balancer { MOE_BALANCE_QB = 0, MOE_BALANCE_SIGN = 1 } moe_balancer;
+
+/*
  * Layer sizes.  d, l, f must be multiples of 64 and f_s a multiple of 64 or 0
  * (0 = no shared expert; several shared experts of hidden f are one of hidden
  * n*f).  1 <= E <= 1024, 1 <= k <= min(E, 32), 2 <= qb_bins <= 256.
  * max_tokens bounds T for every call (1 <= max_tokens, max_tokens*k < 2^31).
  * rms_eps > 0.  routed_scale multiplies every gate (1 = plain renormalised).
+ * balancer picks the update rule; sign_gamma (finite, > 0) is read only for
+ * MOE_BALANCE_SIGN.  A zero-filled tail (balancer 0) selects QB.
  */
 typedef struct moe_config {
   int32_t d, l, E, k, f, f_s;
@@ -84,6 +100,8 @@ typedef struct moe_config {
   moe_qb_mode qb_mode;
   int64_t max_tokens;
   float routed_scale;
+  moe_balancer balancer;
+  float sign_gamma;
 } moe_config;
 
 /* Device pointers, caller-owned, read-only to the library. */
@@ -124,6 +142,8 @@ typedef struct moe_state_layout {
   size_t hist;  /* [hist_slices, E, qb_bins] uint32 score histogram; the
                    histogram is the sum over the slices                   */
   size_t hist_slices;
+  size_t load;  /* [E] uint32 tokens routed to each expert since the last
+                   update (sign-rule balancer only)                       */
   size_t total;
 } moe_state_layout;
 
@@ -173,9 +193,13 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
                        size_t ws_bytes, void* stream);
 
 /*
- * QB update from the histogram accumulated since the last update: the new
- * bias b_e = mean(q) - q_e, then histogram and count are cleared.  Keeps the
- * bias when no token was accumulated.  A no-op returning MOE_OK in frozen mode.
+ * Bias update from the statistics accumulated since the last update, then
+ * those statistics and the token count are cleared; the new bias is used by
+ * the next forward.  MOE_BALANCE_QB: from the histogram, b_e = mean(q) - q_e;
+ * keeps the bias when no token was accumulated.  MOE_BALANCE_SIGN: from the
+ * loads n_e, b_e <- fp32(b_e + sign_gamma * sign(sum(n) - E * n_e)) (the sign
+ * of mean load - n_e, taken exactly in integers; 0 leaves b_e unchanged, so no
+ * accumulated token changes nothing).  A no-op returning MOE_OK in frozen mode.
  */
 moe_status qb_update(moe_ctx* ctx, void* stream);
 
@@ -183,7 +207,7 @@ moe_status qb_update(moe_ctx* ctx, void* stream);
 moe_status moe_get_bias(moe_ctx* ctx, float* dst, void* stream);
 moe_status moe_set_bias(moe_ctx* ctx, const float* src, void* stream);
 
-/* Switch between training and frozen QB; the histogram is kept. */
+/* Switch between training and frozen QB; the accumulated statistics are kept. */
 moe_status moe_set_qb_mode(moe_ctx* ctx, moe_qb_mode mode);
 
 void moe_destroy(moe_ctx* ctx);
@@ -204,7 +228,7 @@ const char* moe_last_error(void);
 enum {
   MOE_K_RMSNORM = 0, MOE_K_GEMM_H, MOE_K_TOPK, MOE_K_HIST, MOE_K_SCAN, MOE_K_SCATTER,
   MOE_K_EXPERT_UP, MOE_K_EXPERT_DOWN, MOE_K_COMBINE, MOE_K_GEMM_OUT, MOE_K_QB_QUANTILE,
-  MOE_K_QB_BIAS, MOE_K_GEMM_RZ, MOE_NUM_KERNELS
+  MOE_K_QB_BIAS, MOE_K_GEMM_RZ, MOE_K_SIGN_BIAS, MOE_NUM_KERNELS
 };
 const char* moe_kernel_name(int id);
 moe_status moe_profile_begin(moe_ctx* ctx, int max_launches, uint32_t mask);

@@ -249,6 +249,29 @@ def qb_update(hist: np.ndarray, N: int, k: int, bias: np.ndarray) -> np.ndarray:
     return qb_bias(qb_quantiles(hist, N, k))
 
 
+def sign_update(load: np.ndarray, bias: np.ndarray, gamma: float) -> np.ndarray:
+    """Sign-rule balancer ([P1] capsule 16, the noaux_tc bias rule with
+    gamma = 1e-2 there): every expert's bias moves by gamma towards balance,
+    b_e <- b_e + gamma * sign(mean load - load_e), in fp32.
+
+    load_e is the number of (token, slot) pairs routed to e since the last
+    update and the mean load is sum(load) / E, so the sign is that of
+    sum(load) - E * load_e, decided here in exact integers.  A zero sign leaves
+    b_e unchanged.  No mean-centring (the page states none for this rule)."""
+    n = [int(v) for v in np.asarray(load).reshape(-1)]
+    E = len(n)
+    total = sum(n)
+    g = F32(gamma)
+    out = np.asarray(bias, dtype=F32).copy()
+    for e in range(E):
+        diff = total - E * n[e]
+        if diff > 0:
+            out[e] = F32(out[e] + g)
+        elif diff < 0:
+            out[e] = F32(out[e] - g)
+    return out
+
+
 def exact_quantile(s_col: np.ndarray, N: int, k: int, E: int) -> float:
     """Sort-based counterpart of ``qb_quantiles``: the ceil(N*k/E)-th largest
     score of one expert."""

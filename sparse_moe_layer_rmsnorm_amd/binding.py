@@ -19,15 +19,16 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_STATE, MOE_ERR_HIP = range(7)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_QB_TRAIN, MOE_QB_FROZEN = 0, 1
+MOE_BALANCE_QB, MOE_BALANCE_SIGN = 0, 1
 KERNELS = ["rmsnorm", "gemm_h", "topk", "hist", "scan", "scatter", "expert_up", "expert_down", "combine",
-           "gemm_out", "qb_quantile", "qb_bias", "gemm_rz"]
+           "gemm_out", "qb_quantile", "qb_bias", "gemm_rz", "sign_bias"]
 MOE_NUM_KERNELS = len(KERNELS)
 
 
 class moe_config(ctypes.Structure):
     _fields_ = [("d", c_int32), ("l", c_int32), ("E", c_int32), ("k", c_int32), ("f", c_int32), ("f_s", c_int32),
                 ("dtype", c_int), ("rms_eps", c_float), ("qb_bins", c_int32), ("qb_mode", c_int),
-                ("max_tokens", c_int64), ("routed_scale", c_float)]
+                ("max_tokens", c_int64), ("routed_scale", c_float), ("balancer", c_int), ("sign_gamma", c_float)]
 
 
 class moe_weights(ctypes.Structure):
@@ -40,7 +41,7 @@ class moe_route_out(ctypes.Structure):
 
 
 class moe_state_layout(ctypes.Structure):
-    _fields_ = [(n, c_size_t) for n in ("bias", "count", "q", "hist", "hist_slices", "total")]
+    _fields_ = [(n, c_size_t) for n in ("bias", "count", "q", "hist", "hist_slices", "load", "total")]
 
 
 class moe_ws_layout(ctypes.Structure):
@@ -187,8 +188,9 @@ def moe_profile_end(ctx: int) -> Dict[str, tuple]:
 
 
 def make_config(d: int, l: int, E: int, k: int, f: int, f_s: int, *, dtype: str = "bf16", rms_eps: float = 1e-6,
-                qb_bins: int = 256, frozen: bool = False, max_tokens: int = 1, routed_scale: float = 1.0
-                ) -> moe_config:
+                qb_bins: int = 256, frozen: bool = False, max_tokens: int = 1, routed_scale: float = 1.0,
+                balancer: str = "qb", sign_gamma: float = 1e-2) -> moe_config:
     return moe_config(d=d, l=l, E=E, k=k, f=f, f_s=f_s, dtype=MOE_BF16 if dtype == "bf16" else MOE_F32,
                       rms_eps=rms_eps, qb_bins=qb_bins, qb_mode=MOE_QB_FROZEN if frozen else MOE_QB_TRAIN,
-                      max_tokens=max_tokens, routed_scale=routed_scale)
+                      max_tokens=max_tokens, routed_scale=routed_scale,
+                      balancer=MOE_BALANCE_SIGN if balancer == "sign" else MOE_BALANCE_QB, sign_gamma=sign_gamma)

@@ -34,9 +34,11 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
                        uint32_t* bitmap, uint32_t* hist, unsigned long long* count, hipStream_t s);
 // Two launches: per-super-chunk prefix, then the global prefix, the row and
 // m-tile offsets and the m-tile table tile_info[g] = {first row, expert << 8 |
-// rows in use} of the grouped GEMMs.
+// rows in use} of the grouped GEMMs.  With `load` non-NULL (sign-rule training) the
+// counts are also added to load[E] and T to *count.
 hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cbase, int32_t* sbase, int32_t* counts,
-                       int32_t* offsets, int32_t* tile_offsets, int2* tile_info, hipStream_t s);
+                       int32_t* offsets, int32_t* tile_offsets, int2* tile_info, uint32_t* load,
+                       unsigned long long* count, hipStream_t s);
 // Rows of the permutation, and the dispatch buffer X[row] = z[token].
 hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* cbase,
                           const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s);
@@ -45,6 +47,9 @@ hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, cons
 hipError_t launch_qb_quantile(const Dims& D, uint32_t* hist, const unsigned long long* count, double* q,
                               hipStream_t s);
 hipError_t launch_qb_bias(const Dims& D, const double* q, unsigned long long* count, float* bias, hipStream_t s);
+// Sign-rule bias update from the accumulated loads; clears loads and count.
+hipError_t launch_sign_bias(const Dims& D, uint32_t* load, unsigned long long* count, float gamma, float* bias,
+                            hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 // Dense GEMMs on h (router logits, shared GLU hidden, latent z) and for the

@@ -36,6 +36,10 @@ moe_status check_config(const moe_config* c) {
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "unknown dtype %d", (int)c->dtype);
   if (c->qb_mode != MOE_QB_TRAIN && c->qb_mode != MOE_QB_FROZEN)
     return fail(MOE_ERR_INVALID_ARG, "unknown qb_mode %d", (int)c->qb_mode);
+  if (c->balancer != MOE_BALANCE_QB && c->balancer != MOE_BALANCE_SIGN)
+    return fail(MOE_ERR_INVALID_ARG, "unknown balancer %d", (int)c->balancer);
+  if (c->balancer == MOE_BALANCE_SIGN && !(c->sign_gamma > 0.f && std::isfinite(c->sign_gamma)))
+    return fail(MOE_ERR_INVALID_ARG, "sign_gamma must be finite and > 0");
   auto m64 = [](int32_t v) { return v > 0 && v % 64 == 0; };
   if (!m64(c->d) || !m64(c->l) || !m64(c->f))
     return fail(MOE_ERR_SHAPE, "d, l, f must be positive multiples of 64 (d=%d l=%d f=%d)", c->d, c->l, c->f);
@@ -78,6 +82,8 @@ void state_layout(const moe_config* c, moe_state_layout* L) {
   L->hist = o;
   L->hist_slices = kHistSlices;
   o = up(o + (size_t)kHistSlices * c->E * c->qb_bins * 4);
+  L->load = o;
+  o = up(o + (size_t)c->E * 4);
   L->total = o;
 }
 
@@ -200,12 +206,15 @@ moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s) {
   const Dims& D = ctx->D;
   const float* bias = reinterpret_cast<const float*>(ctx->state + ctx->sl.bias);
   const bool train = ctx->cfg.qb_mode == MOE_QB_TRAIN;
-  uint32_t* hist = train ? reinterpret_cast<uint32_t*>(ctx->state + ctx->sl.hist) : nullptr;
+  const bool sign = ctx->cfg.balancer == MOE_BALANCE_SIGN;
+  // training statistics: the score histogram (QB) or the per-expert loads (sign rule)
+  uint32_t* hist = train && !sign ? reinterpret_cast<uint32_t*>(ctx->state + ctx->sl.hist) : nullptr;
+  uint32_t* load = train && sign ? reinterpret_cast<uint32_t*>(ctx->state + ctx->sl.load) : nullptr;
   unsigned long long* cnt = reinterpret_cast<unsigned long long*>(ctx->state + ctx->sl.count);
   MOE_RUN(MOE_K_TOPK, launch_topk(D, p.logits, bias, T, p.idx, p.gates, p.bitmap, hist, cnt, s));
   if (train) ctx->pending_tokens += (uint64_t)T;
-  MOE_RUN(MOE_K_SCAN,
-          launch_scan(D, p.bitmap, T, p.cbase, p.sbase, p.counts, p.offsets, p.tile_offsets, p.tile_info, s));
+  MOE_RUN(MOE_K_SCAN, launch_scan(D, p.bitmap, T, p.cbase, p.sbase, p.counts, p.offsets, p.tile_offsets,
+                                  p.tile_info, load, train && sign ? cnt : nullptr, s));
   MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.bitmap, p.cbase, p.sbase, T, p.perm_src, p.inv, s));
   return MOE_OK;
 }
@@ -331,6 +340,12 @@ moe_status qb_update(moe_ctx* ctx, void* stream) {
   unsigned long long* cnt = reinterpret_cast<unsigned long long*>(ctx->state + ctx->sl.count);
   double* q = reinterpret_cast<double*>(ctx->state + ctx->sl.q);
   float* bias = reinterpret_cast<float*>(ctx->state + ctx->sl.bias);
+  if (ctx->cfg.balancer == MOE_BALANCE_SIGN) {
+    uint32_t* load = reinterpret_cast<uint32_t*>(ctx->state + ctx->sl.load);
+    MOE_RUN(MOE_K_SIGN_BIAS, launch_sign_bias(D, load, cnt, ctx->cfg.sign_gamma, bias, s));
+    ctx->pending_tokens = 0;
+    return MOE_OK;
+  }
   MOE_RUN(MOE_K_QB_QUANTILE, launch_qb_quantile(D, hist, cnt, q, s));
   MOE_RUN(MOE_K_QB_BIAS, launch_qb_bias(D, q, cnt, bias, s));
   ctx->pending_tokens = 0;
@@ -382,7 +397,8 @@ const char* moe_last_error(void) { return g_err; }
 const char* moe_kernel_name(int id) {
   static const char* names[MOE_NUM_KERNELS] = {"rmsnorm",     "gemm_h",  "topk",     "hist",
                                                 "scan",        "scatter", "expert_up", "expert_down",
-                                                "combine",     "gemm_out", "qb_quantile", "qb_bias", "gemm_rz"};
+                                                "combine",     "gemm_out", "qb_quantile", "qb_bias", "gemm_rz",
+                                                "sign_bias"};
   return (id >= 0 && id < MOE_NUM_KERNELS) ? names[id] : "unknown";
 }
 

@@ -343,10 +343,14 @@ __global__ __launch_bounds__(256) void k_scan_local(const uint32_t* __restrict__
 // total and the exclusive prefix over super-chunks (sbase becomes the
 // absolute first row of each super-chunk's part of the expert's group); over
 // experts, the row offsets and the first m-tile of each expert for the grouped
-// GEMMs (tiles of kExpertBM rows; an empty expert has none).
+// GEMMs (tiles of kExpertBM rows; an empty expert has none).  With `load`
+// (sign-rule training) each expert's count is added to its accumulated load
+// and T to the token count.
 __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbase, int nsuper, int E,
                                                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ tile_offsets, int2* __restrict__ tile_info) {
+                                                      int32_t* __restrict__ tile_offsets, int2* __restrict__ tile_info,
+                                                      uint32_t* __restrict__ load, unsigned long long* __restrict__ count,
+                                                      int T) {
   __shared__ int wsum_r[16], wsum_t[16];
   constexpr int kReg = 16;  // up to this many super-chunk totals stay in registers
   const int i = threadIdx.x, lane = i & 63, w = i >> 6;
@@ -385,6 +389,7 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
   }
   if (i < E) {
     counts[i] = c;
+    if (load) load[i] += (uint32_t)c;
     offsets[i + 1] = r;
     tile_offsets[i + 1] = t;
     int run = r - c;  // exclusive offset of expert i
@@ -410,11 +415,13 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
   if (i == 0) {
     offsets[0] = 0;
     tile_offsets[0] = 0;
+    if (load) *count += (unsigned long long)T;
   }
 }
 
 hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cbase, int32_t* sbase, int32_t* counts,
-                       int32_t* offsets, int32_t* tile_offsets, int2* tile_info, hipStream_t s) {
+                       int32_t* offsets, int32_t* tile_offsets, int2* tile_info, uint32_t* load,
+                       unsigned long long* count, hipStream_t s) {
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int nsuper = (nchunks + kSuper - 1) / kSuper;
   dim3 g1((D.E + 63) / 64, (nsuper + 3) / 4);
@@ -422,7 +429,7 @@ hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cb
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan_global, dim3(1), dim3(1024), 0, s, sbase, nsuper, D.E, counts, offsets, tile_offsets,
-                     tile_info);
+                     tile_info, load, load ? count : nullptr, T);
   return hipGetLastError();
 }
 
@@ -589,6 +596,40 @@ hipError_t launch_qb_quantile(const Dims& D, uint32_t* hist, const unsigned long
 
 hipError_t launch_qb_bias(const Dims& D, const double* q, unsigned long long* count, float* bias, hipStream_t s) {
   hipLaunchKernelGGL(k_qb_bias, dim3(1), dim3(1024), 0, s, q, count, D.E, bias);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- sign-rule bias ----
+// Sign-rule balancer (capsule 16 of the "Pretraining a Mini Kimi K3" review):
+// b_e += gamma * sign(mean load - n_e).  With S = sum of the loads, the sign
+// of S / E - n_e is that of S - E * n_e, compared exactly in 64-bit integers;
+// the bias moves by one fp32 add or subtract of gamma (or not at all).  One
+// block; the loads and the token count are cleared for the next window.
+__global__ __launch_bounds__(1024) void k_sign_bias(uint32_t* __restrict__ load, unsigned long long* __restrict__ count,
+                                                    int E, float gamma, float* __restrict__ bias) {
+  __shared__ unsigned long long part[16];
+  const int i = threadIdx.x, lane = i & 63, w = i >> 6;
+  const uint32_t n = i < E ? load[i] : 0u;
+  unsigned long long v = n;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) part[w] = v;
+  __syncthreads();
+  unsigned long long S = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) S += part[j];
+  if (i < E) {
+    const long long diff = (long long)S - (long long)E * (long long)n;
+    const float b = bias[i];
+    bias[i] = diff > 0 ? b + gamma : (diff < 0 ? b - gamma : b);
+    load[i] = 0u;
+  }
+  if (i == 0) *count = 0ull;
+}
+
+hipError_t launch_sign_bias(const Dims& D, uint32_t* load, unsigned long long* count, float gamma, float* bias,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(k_sign_bias, dim3(1), dim3(1024), 0, s, load, count, D.E, gamma, bias);
   return hipGetLastError();
 }
 

@@ -33,12 +33,14 @@ class MoeLayer:
 
     def __init__(self, *, d: int, l: int, E: int, k: int, f: int, f_s: int, dtype: str, weights: Dict,
                  max_tokens: int, qb_bins: int = 256, rms_eps: float = 1e-6, frozen: bool = False,
-                 routed_scale: float = 1.0, logit_offset=None, device: str = "cuda", stream=None):
+                 routed_scale: float = 1.0, logit_offset=None, device: str = "cuda", stream=None,
+                 balancer: str = "qb", sign_gamma: float = 1e-2):
         self.dtype = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.device = torch.device(device)
         self.cfg = B.make_config(d, l, E, k, f, f_s, dtype=dtype, rms_eps=rms_eps, qb_bins=qb_bins, frozen=frozen,
-                                 max_tokens=max_tokens, routed_scale=routed_scale)
+                                 max_tokens=max_tokens, routed_scale=routed_scale, balancer=balancer,
+                                 sign_gamma=sign_gamma)
         self.dims = dict(d=d, l=l, E=E, k=k, f=f, f_s=f_s, B=qb_bins)
         self.w: Dict[str, torch.Tensor] = {}
         for name in _WEIGHT_NAMES:
@@ -97,6 +99,7 @@ class MoeLayer:
             "q": s[self.sl.q:self.sl.q + 8 * E].view(torch.float64),
             "hist_slices": s[self.sl.hist:self.sl.hist + 4 * S * E * nb].view(torch.int32).view(S, E, nb),
             "hist": s[self.sl.hist:self.sl.hist + 4 * S * E * nb].view(torch.int32).view(S, E, nb).sum(0),
+            "load": s[self.sl.load:self.sl.load + 4 * E].view(torch.int32),
         }
 
     def route_buffers(self, T: int) -> Dict[str, torch.Tensor]:
@@ -162,9 +165,10 @@ class MoeLayer:
 
 
 def layer_from_shape(shape, weights: Dict, *, max_tokens: Optional[int] = None, frozen: Optional[bool] = None,
-                     logit_offset=None, device: str = "cuda") -> MoeLayer:
+                     logit_offset=None, device: str = "cuda", balancer: str = "qb",
+                     sign_gamma: float = 1e-2) -> MoeLayer:
     """MoeLayer for a workloads.LayerShape."""
     return MoeLayer(d=shape.d, l=shape.l, E=shape.E, k=shape.k, f=shape.f, f_s=shape.f_s, dtype=shape.dtype,
                     weights=weights, max_tokens=max_tokens or shape.T, qb_bins=shape.B, rms_eps=shape.rms_eps,
                     frozen=shape.qb_frozen if frozen is None else frozen, logit_offset=logit_offset,
-                    device=device)
+                    device=device, balancer=balancer, sign_gamma=sign_gamma)

@@ -48,7 +48,7 @@ def logical_name(symbol: str, dense_seen: int) -> str | None:
     if "k_gemm_expert" in symbol:
         return "expert_up" if symbol.rstrip().endswith("2>(moe::(anonymous namespace)::ExpertArgs)") else "expert_down"
     for k in ("rmsnorm", "topk", "hist", "scan_local", "scan_global", "scatter", "combine", "qb_update",
-              "qb_quantile", "qb_bias", "zero"):
+              "qb_quantile", "qb_bias", "sign_bias", "zero"):
         if f"k_{k}" in symbol:
             return k
     if "rocclr_copyBuffer" in symbol:

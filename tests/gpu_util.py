@@ -37,8 +37,8 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def make_layer(shape, W, *, max_tokens, c=None, frozen=None):
-    return layer_from_shape(shape, W, max_tokens=max_tokens, logit_offset=c, frozen=frozen)
+def make_layer(shape, W, *, max_tokens, c=None, frozen=None, **kw):
+    return layer_from_shape(shape, W, max_tokens=max_tokens, logit_offset=c, frozen=frozen, **kw)
 
 
 def x_on_gpu(x: np.ndarray, layer) -> torch.Tensor:

@@ -42,6 +42,7 @@ def test_sizes_and_layouts():
     assert B.moe_state_bytes(cfg) == st.total
     assert st.bias == 0 and st.count >= 4 * 256 and st.q > st.count and st.hist > st.q
     assert st.total >= st.hist + st.hist_slices * 256 * 256 * 4
+    assert st.load >= st.hist + st.hist_slices * 256 * 256 * 4 and st.total >= st.load + 256 * 4
     for T in (0, 1, 1000, 8192):
         ws = B.moe_workspace_layout(cfg, T)
         assert B.moe_workspace_bytes(cfg, T) == ws.total
@@ -60,6 +61,7 @@ def test_sizes_and_layouts():
     ("qb_bins", 1, B.MOE_ERR_SHAPE), ("qb_bins", 257, B.MOE_ERR_SHAPE), ("dtype", 7, B.MOE_ERR_DTYPE),
     ("qb_mode", 5, B.MOE_ERR_INVALID_ARG), ("rms_eps", 0.0, B.MOE_ERR_INVALID_ARG),
     ("max_tokens", 0, B.MOE_ERR_SHAPE), ("max_tokens", 2 ** 30, B.MOE_ERR_SHAPE),
+    ("balancer", 2, B.MOE_ERR_INVALID_ARG), ("balancer", -1, B.MOE_ERR_INVALID_ARG),
 ])
 def test_bad_config_rejected_before_any_device_call(L, field, value, status):
     cfg = B.make_config(**REPLICA, max_tokens=64)
@@ -70,6 +72,15 @@ def test_bad_config_rejected_before_any_device_call(L, field, value, status):
     assert L.moe_init(ctypes.byref(cfg), ctypes.byref(w), 256, None, ctypes.byref(ctx)) == status
     assert ctx.value is None
     assert L.moe_last_error()
+
+
+@pytest.mark.parametrize("gamma,ok", [(1e-2, True), (1e-3, True), (0.0, False), (-1e-2, False),
+                                      (float("inf"), False), (float("nan"), False)])
+def test_sign_gamma_checked_only_for_the_sign_balancer(gamma, ok):
+    sign = B.make_config(**REPLICA, max_tokens=64, balancer="sign", sign_gamma=gamma)
+    assert (B.moe_state_bytes(sign) > 0) == ok
+    qb = B.make_config(**REPLICA, max_tokens=64, balancer="qb", sign_gamma=gamma)
+    assert B.moe_state_bytes(qb) > 0                      # ignored by the QB rule
 
 
 def test_null_arguments_rejected(L):

@@ -116,3 +116,72 @@ def test_qb_matches_exact_quantile_rule_in_balance():
     assert np.max(np.abs(b_exact - b_hist)) <= 2.0 / 256
     ld = np.bincount(o.topk_select(s, b_hist, k).ravel(), minlength=E)
     assert ld.max() / ld.mean() < 1.3
+
+
+# ---------------------------------------------------------------------------
+# Sign-rule balancer ([P1] capsule 16): b_e += gamma * sign(mean load - load_e)
+# ---------------------------------------------------------------------------
+GAMMA = 1e-2  # the value [P1] capsule 16 settles on (DeepSeek-V3's 1e-3 did not transfer)
+
+
+def test_sign_rule_worked_example():
+    """Loads (10, 2, 4, 0) have mean 4: the first expert is over, the second
+    and fourth under, the third exactly at the mean (worked by hand)."""
+    b0 = np.array([0.5, -0.25, 0.125, 1.0], F32)
+    got = o.sign_update(np.array([10, 2, 4, 0]), b0, GAMMA)
+    g = F32(GAMMA)
+    want = np.array([F32(0.5) - g, F32(-0.25) + g, F32(0.125), F32(1.0) + g], F32)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_sign_rule_fractional_mean_and_ties():
+    """Mean 4/3 (not an integer): loads 1, 1 sit below it, 2 above.  Equal
+    loads, and no tokens at all, leave the bias bit for bit."""
+    got = o.sign_update(np.array([1, 1, 2]), np.zeros(3, F32), GAMMA)
+    np.testing.assert_array_equal(got, np.array([GAMMA, GAMMA, -GAMMA], F32))
+    b = np.random.default_rng(3).standard_normal(17).astype(F32)
+    for load in (np.full(17, 9), np.zeros(17, np.int64)):
+        np.testing.assert_array_equal(o.sign_update(load, b, GAMMA).view(np.uint32), b.view(np.uint32))
+
+
+def test_sign_rule_moves_each_bias_one_step_towards_the_mean():
+    """Every bias moves by exactly one fp32 add of +-gamma or not at all, up
+    for experts below the mean load and down for those above it."""
+    rng = np.random.default_rng(11)
+    for E in (1, 2, 16, 256, 1000):
+        load = rng.integers(0, 50, E)
+        b = (rng.standard_normal(E) * 0.3).astype(F32)
+        nb = o.sign_update(load, b, GAMMA)
+        mean = load.sum() / E
+        for e in range(E):
+            if load[e] < mean:
+                assert nb[e] == F32(b[e] + F32(GAMMA)) and nb[e] > b[e]
+            elif load[e] > mean:
+                assert nb[e] == F32(b[e] - F32(GAMMA)) and nb[e] < b[e]
+            else:
+                assert nb[e] == b[e]
+
+
+def test_sign_rule_balances_skewed_load_over_steps():
+    """Load-skew workload (Zipf logit offsets), fresh batch each step, the
+    bias of step t applied at step t+1: max/mean falls from > 10 to < 3
+    within 7 steps and stays below 2, while one QB step already reaches < 1.6
+    (the QB rule sets the bias outright, the sign rule walks gamma a step)."""
+    shape = wl.workload("skew", 4096)
+    W = wl.make_weights(shape)
+    c = wl.zipf_logit_offset(shape)
+
+    def scores(step):
+        h = o.bf16_round(o.rmsnorm(wl.make_x(shape, step), W["gamma"], shape.rms_eps))
+        return o.sigmoid_r(o.router_logits(h, W["W_r"], c))
+
+    b = np.zeros(shape.E, F32)
+    ratios = []
+    for step in range(14):
+        load = np.bincount(o.topk_select(scores(step), b, shape.k).ravel(), minlength=shape.E)
+        ratios.append(o.load_stats(load)["max_over_mean"])
+        b = o.sign_update(load, b, GAMMA)
+        assert np.abs(b).max() <= (step + 1) * GAMMA * (1 + 1e-5)
+    assert ratios[0] > 10
+    assert ratios[6] < 3
+    assert max(ratios[8:]) < 2
