@@ -393,6 +393,139 @@ def forward_tokens(x_rows: np.ndarray, W: Dict[str, np.ndarray], idx_rows: np.nd
     return out
 
 
+# --------------------------------------------------------------------------
+# Backward pass (the "next" step after the forward: the gradients that train
+# the layer).  The routing decisions (idx) are piecewise constant in the
+# inputs, so gradients flow through the gates, never into the bias b, which
+# only reroutes ([P4] Tab 8-10).
+# --------------------------------------------------------------------------
+
+
+def dsilu(a: np.ndarray) -> np.ndarray:
+    """d silu(a) / da = sigma(a) (1 + a (1 - sigma(a))) in fp64."""
+    sg = 1.0 / (1.0 + np.exp(-a))
+    return sg * (1.0 + a * (1.0 - sg))
+
+
+def glu_backward(P: np.ndarray, Q: np.ndarray, dG: np.ndarray):
+    """G = silu(P) * Q:  dP = dG * Q * silu'(P),  dQ = dG * silu(P)."""
+    return dG * Q * dsilu(P), dG * silu(P)
+
+
+def gates_backward(s: np.ndarray, idx: np.ndarray, dg: np.ndarray, routed_scale: float = 1.0) -> np.ndarray:
+    """Router-logit gradient dl[T,E] from the gate gradient dg[T,k].
+
+    g_j = c s_j / S with S = sum_i s_i over the selected experts, so
+    ds_m = (c / S) dg_m - (1 / S) sum_j dg_j g_j for a selected m, and
+    dl_m = ds_m s_m (1 - s_m) (sigmoid).  Unselected experts get 0."""
+    s_sel = np.take_along_axis(np.asarray(s, np.float64), idx.astype(np.int64), axis=1)
+    S = s_sel.sum(axis=1, keepdims=True)
+    g = routed_scale * s_sel / S
+    ds = routed_scale * dg / S - (dg * g).sum(axis=1, keepdims=True) / S
+    dl = np.zeros(np.asarray(s).shape, dtype=np.float64)
+    np.put_along_axis(dl, idx.astype(np.int64), ds * s_sel * (1.0 - s_sel), axis=1)
+    return dl
+
+
+def rmsnorm_backward(x: np.ndarray, gamma: np.ndarray, eps: float, dh: np.ndarray):
+    """h = gamma * x * r, r = (mean(x^2) + eps)^-1/2, per row of width d:
+    dx = r (gamma dh) - x r^3 sum(gamma dh x) / d;  dgamma = sum_t dh x r."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[1]
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+    u = np.asarray(gamma, np.float64)[None, :] * dh
+    dx = r * u - x * r ** 3 * (u * x).sum(axis=1, keepdims=True) / d
+    return dx, (dh * x * r).sum(axis=0)
+
+
+def backward(x: np.ndarray, W: Dict[str, np.ndarray], dout: np.ndarray, fwd: Dict[str, np.ndarray], *,
+             dtype: str, eps: float = 1e-6, routed_scale: float = 1.0) -> Dict[str, np.ndarray]:
+    """Gradients of sum(out * dout) for the forward ``fwd`` (from ``forward``)
+    with respect to x and every weight.
+
+    Chain, in the order the values are formed (bf16 mode rounds to bf16 at the
+    points the device stores bf16 operands of its products: the recomputed GLU
+    pre-activations P, Q, A, U; dG, dy_lat, dP, dQ, dY, dH, dA, dU, dX, dz
+    and the router-logit gradient; dh, the weight gradients and dgamma stay
+    unrounded):
+      out = G W_sd^T + y_lat W_up^T       -> dG, dy_lat, dW_sd, dW_up
+      y_lat = sum_j g_j Y[inv_j]          -> dY rows, dg (combine transpose)
+      Y_e = H_e W_d[e]^T                  -> dH, dW_d
+      H_e = silu(A) U, A = X W_g^T, U = X W_u^T -> dA, dU, dW_g, dW_u, dX
+      X = z[perm_src]                     -> dz[t] = sum_j dX[inv_j]
+      g = gates(s), s = sigmoid(l)        -> dl (selected experts only)
+      G = silu(P) Q, P = h W_sg^T, Q = h W_su^T -> dP, dQ, dW_sg, dW_su
+      z = h W_dn^T, l = h W_r^T (+c)      -> dW_dn, dW_r
+      dh = dP W_sg + dQ W_su + dz W_dn + dl W_r;  h = RMSNorm(x) -> dx, dgamma
+    """
+    f64 = lambda a: np.asarray(a, np.float64)  # noqa: E731
+    st = lambda a: _store(a, dtype)            # noqa: E731
+    x = f64(x)
+    dout = st(dout)
+    T = x.shape[0]
+    k = fwd["idx"].shape[1]
+    E = W["W_r"].shape[0]
+    h, z, G, H, Y, y_lat = fwd["h"], fwd["z"], fwd["G"], fwd["H"], fwd["Y"], fwd["y_lat"]
+    idx, gates, inv, offsets, perm_src = fwd["idx"], fwd["gates"], fwd["inv"], fwd["offsets"], fwd["perm_src"]
+    g: Dict[str, np.ndarray] = {}
+    shared = W.get("W_sg") is not None and W["W_sg"].shape[0] > 0
+    # output projections
+    g["W_up"] = dout.T @ y_lat
+    dy = st(dout @ f64(W["W_up"]))
+    dh = np.zeros_like(h)
+    if shared:
+        g["W_sd"] = dout.T @ G
+        dG = st(dout @ f64(W["W_sd"]))
+        P = st(h @ f64(W["W_sg"]).T)
+        Q = st(h @ f64(W["W_su"]).T)
+        dP, dQ = glu_backward(P, Q, dG)
+        dP, dQ = st(dP), st(dQ)
+        g["W_sg"] = dP.T @ h
+        g["W_su"] = dQ.T @ h
+        dh += dP @ f64(W["W_sg"]) + dQ @ f64(W["W_su"])
+    # combine transpose
+    dY = np.zeros_like(Y)
+    dg = np.zeros((T, k))
+    for j in range(k):
+        rows = inv[:, j]
+        dY[rows] = st(f64(gates[:, j])[:, None] * dy)
+        dg[:, j] = (dy * Y[rows]).sum(axis=1)
+    # experts
+    X = z[perm_src]
+    dX = np.zeros_like(X)
+    g["W_d"] = np.zeros(np.shape(W["W_d"]))
+    g["W_g"] = np.zeros(np.shape(W["W_g"]))
+    g["W_u"] = np.zeros(np.shape(W["W_u"]))
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        g["W_d"][e] = dY[a:b].T @ H[a:b]
+        dH = st(dY[a:b] @ f64(W["W_d"][e]))
+        A = st(X[a:b] @ f64(W["W_g"][e]).T)
+        U = st(X[a:b] @ f64(W["W_u"][e]).T)
+        dA, dU = glu_backward(A, U, dH)
+        dA, dU = st(dA), st(dU)
+        g["W_g"][e] = dA.T @ X[a:b]
+        g["W_u"][e] = dU.T @ X[a:b]
+        dX[a:b] = st(dA @ f64(W["W_g"][e]) + dU @ f64(W["W_u"][e]))
+    # dispatch transpose
+    dz = np.zeros_like(z)
+    for j in range(k):
+        dz += dX[inv[:, j]]
+    dz = st(dz)
+    g["W_dn"] = dz.T @ h
+    dh += dz @ f64(W["W_dn"])
+    # router
+    dl = st(gates_backward(fwd["s"], idx, dg, routed_scale))
+    g["W_r"] = dl.T @ h
+    dh += dl @ f64(W["W_r"])
+    dx, dgamma = rmsnorm_backward(x, W["gamma"], eps, dh)
+    g["x"] = st(dx)
+    g["gamma"] = dgamma
+    return g
+
+
 def load_stats(counts: np.ndarray) -> Dict[str, float]:
     """Balance statistics that do not hide dead experts ([P1] capsule 16: the
     router entropy read 0.9999 while 94.5% of experts were dead)."""
