@@ -203,6 +203,47 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
  */
 moe_status qb_update(moe_ctx* ctx, void* stream);
 
+/*
+ * Gradients of the layer (fp32, the shapes of moe_weights; every pointer is
+ * device memory, overwritten, not accumulated).  W_sg, W_su, W_sd may be NULL
+ * when f_s == 0.  The router bias gets no gradient: it only reroutes (Tab 8-10
+ * of the demo article), so a routing decision is a constant of the backward.
+ */
+typedef struct moe_grads {
+  float* gamma; /* [d]     */
+  float* W_r;   /* [E,d]   */
+  float* W_sg;  /* [f_s,d] */
+  float* W_su;  /* [f_s,d] */
+  float* W_sd;  /* [d,f_s] */
+  float* W_dn;  /* [l,d]   */
+  float* W_g;   /* [E,f,l] */
+  float* W_u;   /* [E,f,l] */
+  float* W_d;   /* [E,l,f] */
+  float* W_up;  /* [d,l]   */
+} moe_grads;
+
+/* Bytes of backward workspace for T tokens (0 if invalid). */
+size_t moe_backward_workspace_bytes(const moe_config* cfg, int64_t T);
+
+/*
+ * Backward pass of the forward that moe_forward(ctx, x, T, ..., r, fwd_ws,
+ * ...) last wrote into fwd_ws (same x, T and route outputs r, which may be
+ * NULL as in the forward; fwd_ws must not have been reused since): from
+ * dout[T,d] (activation dtype) writes dx[T,d] (activation dtype) and every
+ * weight gradient in *g, for the scalar sum(out * dout).  The chain: output
+ * projections, combine transpose (dY rows, gate gradients), grouped expert
+ * GEMM transposes with the GLU derivative (pre-activations recomputed),
+ * dispatch transpose (sum of each token's k rows), gate renormalisation and
+ * sigmoid derivative to the router logits, shared GLU, the summed gradient of
+ * h, RMSNorm.  Weight gradients of the experts take each expert's own tokens
+ * as the K range of one grouped product.  `ws` holds
+ * moe_backward_workspace_bytes(cfg, T) bytes (256-byte aligned).  QB state
+ * is neither read nor changed.  T = 0 enqueues nothing.
+ */
+moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T, const moe_route_out* r,
+                        const void* fwd_ws, size_t fwd_ws_bytes, void* dx, const moe_grads* g, void* ws,
+                        size_t ws_bytes, void* stream);
+
 /* Copy the current bias (E fp32) to / from device memory on `stream`. */
 moe_status moe_get_bias(moe_ctx* ctx, float* dst, void* stream);
 moe_status moe_set_bias(moe_ctx* ctx, const float* src, void* stream);
@@ -228,7 +269,10 @@ const char* moe_last_error(void);
 enum {
   MOE_K_RMSNORM = 0, MOE_K_GEMM_H, MOE_K_TOPK, MOE_K_HIST, MOE_K_SCAN, MOE_K_SCATTER,
   MOE_K_EXPERT_UP, MOE_K_EXPERT_DOWN, MOE_K_COMBINE, MOE_K_GEMM_OUT, MOE_K_QB_QUANTILE,
-  MOE_K_QB_BIAS, MOE_K_GEMM_RZ, MOE_K_SIGN_BIAS, MOE_NUM_KERNELS
+  MOE_K_QB_BIAS, MOE_K_GEMM_RZ, MOE_K_SIGN_BIAS,
+  /* backward: dense products, grouped expert products, per-expert weight
+     gradients, elementwise transposes and derivatives, operand transposes */
+  MOE_K_BWD_GEMM, MOE_K_BWD_EXPERT, MOE_K_BWD_WGRAD, MOE_K_BWD_ELTWISE, MOE_K_BWD_TRANSPOSE, MOE_NUM_KERNELS
 };
 const char* moe_kernel_name(int id);
 moe_status moe_profile_begin(moe_ctx* ctx, int max_launches, uint32_t mask);

@@ -21,7 +21,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_QB_TRAIN, MOE_QB_FROZEN = 0, 1
 MOE_BALANCE_QB, MOE_BALANCE_SIGN = 0, 1
 KERNELS = ["rmsnorm", "gemm_h", "topk", "hist", "scan", "scatter", "expert_up", "expert_down", "combine",
-           "gemm_out", "qb_quantile", "qb_bias", "gemm_rz", "sign_bias"]
+           "gemm_out", "qb_quantile", "qb_bias", "gemm_rz", "sign_bias", "bwd_gemm", "bwd_expert", "bwd_wgrad",
+           "bwd_eltwise", "bwd_transpose"]
 MOE_NUM_KERNELS = len(KERNELS)
 
 
@@ -38,6 +39,10 @@ class moe_weights(ctypes.Structure):
 
 class moe_route_out(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("logits", "topk_idx", "gates", "counts", "offsets", "perm_src", "inv")]
+
+
+class moe_grads(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("gamma", "W_r", "W_sg", "W_su", "W_sd", "W_dn", "W_g", "W_u", "W_d", "W_up")]
 
 
 class moe_state_layout(ctypes.Structure):
@@ -72,6 +77,9 @@ def lib() -> ctypes.CDLL:
                                   c_void_p]),
             "moe_forward": (c_int, [c_void_p, c_void_p, c_int64, c_void_p, POINTER(moe_route_out), c_void_p,
                                     c_size_t, c_void_p]),
+            "moe_backward_workspace_bytes": (c_size_t, [cfgp, c_int64]),
+            "moe_backward": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, POINTER(moe_route_out), c_void_p,
+                                     c_size_t, c_void_p, POINTER(moe_grads), c_void_p, c_size_t, c_void_p]),
             "qb_update": (c_int, [c_void_p, c_void_p]),
             "moe_get_bias": (c_int, [c_void_p, c_void_p, c_void_p]),
             "moe_set_bias": (c_int, [c_void_p, c_void_p, c_void_p]),
@@ -151,6 +159,16 @@ def moe_forward(ctx: int, x: int, T: int, out: int, r: Optional[moe_route_out], 
                 stream: int) -> None:
     check(lib().moe_forward(ctx, x, T, out, ctypes.byref(r) if r is not None else None, ws, ws_bytes, stream),
           "moe_forward")
+
+
+def moe_backward_workspace_bytes(cfg: moe_config, T: int) -> int:
+    return lib().moe_backward_workspace_bytes(ctypes.byref(cfg), T)
+
+
+def moe_backward(ctx: int, x: int, dout: int, T: int, r: Optional[moe_route_out], fwd_ws: int, fwd_ws_bytes: int,
+                 dx: int, g: moe_grads, ws: int, ws_bytes: int, stream: int) -> None:
+    check(lib().moe_backward(ctx, x, dout, T, ctypes.byref(r) if r is not None else None, fwd_ws, fwd_ws_bytes, dx,
+                             ctypes.byref(g), ws, ws_bytes, stream), "moe_backward")
 
 
 def qb_update(ctx: int, stream: int) -> None:

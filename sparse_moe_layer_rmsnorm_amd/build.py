@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["route_kernels.hip", "gemm_kernels.hip", "moe_abi.cpp"]
+SOURCES = ["route_kernels.hip", "gemm_kernels.hip", "bwd_kernels.hip", "moe_abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

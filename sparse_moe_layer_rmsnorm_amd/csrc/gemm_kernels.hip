@@ -635,6 +635,143 @@ __global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expe
   stream<Pp>(prob, smem);
 }
 
+// ------------------------------------------- per-expert weight gradients --
+// C_e = A_e B_e^T for every expert e, with the K range of each expert its
+// own: A [M, Ktot] and B [N, Ktot] hold the experts' rows side by side along
+// K in segments koff[e] .. koff[e+1] (elements, padded to whole stages and at
+// least one stage, pad columns zero).  C_e [M, N] fp32 at out + e*M*N.  Used
+// for dW = dY_e^T H_e style products, whose K is the expert's token count.
+struct WgradArgs {
+  const char* A;
+  int lda_bytes;
+  const char* B;
+  int ldb_bytes;
+  const int32_t* koff;
+  int es;  // element bytes
+  int M, N, MT, NT, E;
+  float* out;
+};
+
+template <class Pp>
+struct WgradProb {
+  static constexpr int PARTS = 1;
+  template <int L>
+  struct SrcT {
+    const char* p[L];
+  };
+  const WgradArgs& a;
+
+  MOE_DEV int total() const { return a.E * a.MT * a.NT; }
+  MOE_DEV Tile tile(int L) const {
+    const int per = a.MT * a.NT;
+    const int e = L / per, r = L - e * per;
+    const int mt = r / a.NT;
+    Tile t;
+    t.row0 = mt * Pp::BM;
+    t.rows = min(Pp::BM, a.M - t.row0);
+    t.nt = r - mt * a.NT;
+    t.sel = e;
+    return t;
+  }
+  MOE_DEV int kt_of(const Tile& t) const {
+    return (scalar_load(a.koff, t.sel + 1) - scalar_load(a.koff, t.sel)) * uniform_int(a.es) / Pp::RB;
+  }
+  MOE_DEV const char* row_ptr(const Tile& t, int row) const {
+    const size_t k0 = (size_t)scalar_load(a.koff, t.sel) * uniform_int(a.es);
+    if (row < Pp::BM) {  // rows past M read the tile's first row (not stored)
+      const int r = row < t.rows ? row : 0;
+      return uniform_ptr(a.A) + (size_t)(t.row0 + r) * uniform_int(a.lda_bytes) + k0;
+    }
+    int n = t.nt * Pp::BN + (row - Pp::BM);
+    if (n >= uniform_int(a.N)) n = 0;
+    return uniform_ptr(a.B) + (size_t)n * uniform_int(a.ldb_bytes) + k0;
+  }
+  template <int L>
+  MOE_DEV void sources(const Tile& t, SrcT<L>& src) const {
+    const int lane = threadIdx.x & 63, wave = Pp::wave_id();
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int row = Pp::slot_row(i, wave, lane);
+      src.p[i] = row_ptr(t, row) + Pp::slot_chunk(row, lane) * 16;
+    }
+  }
+  template <int L>
+  MOE_DEV void issue(const SrcT<L>& src, int ks, uint32_t lds) const {
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      lds_dma16(src.p[i] + ks * Pp::RB, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
+  }
+  MOE_DEV void epilogue(const Tile& t, const typename Pp::Acc& acc) const {
+    Pp::template epilogue<EPI_F32>(acc, t.rows, t.nt * Pp::BN, a.N, a.out + (size_t)t.sel * a.M * a.N, a.N,
+                                   (size_t)t.row0, nullptr);
+  }
+};
+
+// The persistent stream for tiles whose K length varies (kt_of(tile) >= 1
+// stages): the issue and the compute cursors each track their own tile's
+// length; otherwise as stream().
+template <class Pp, class Prob>
+MOE_DEV void stream_var(const Prob& prob, char* smem) {
+  const int G = gridDim.x, b = blockIdx.x;
+  const int x = b & 7, q = b >> 3, Gx = G >> 3;
+  const int total_tiles = prob.total();
+  const int per = (total_tiles + 7) >> 3;
+  const int lo = x * per, hi = min(total_tiles, lo + per);
+  const int span = hi - lo - q;
+  const int my_n = span > 0 ? (span + Gx - 1) / Gx : 0;
+  if (my_n <= 0) return;
+  const uint32_t lds0 = lds_addr(smem) + Pp::wave_id() * 1024;
+
+  typename Prob::template SrcT<Pp::L> src;
+  int iss_j = 0, iss_ks = 0, issued = 0;
+  Tile it = prob.tile(lo + q);
+  int iss_kt = prob.kt_of(it);
+  prob.sources(it, src);
+  auto issue = [&]() {
+    const uint32_t base = lds0 + (uint32_t)((issued % Pp::NS) * Pp::STAGE);
+    prob.issue(src, iss_ks, base);
+    ++issued;
+    if (++iss_ks == iss_kt) {
+      iss_ks = 0;
+      if (++iss_j < my_n) {
+        it = prob.tile(lo + q + iss_j * Gx);
+        iss_kt = prob.kt_of(it);
+        prob.sources(it, src);
+      }
+    }
+  };
+  for (int s = 0; s < Pp::NS - 1; ++s)
+    if (iss_j < my_n) issue();
+
+  typename Pp::Acc acc;
+  Pp::zero(acc);
+  int cj = 0, cks = 0;
+  Tile ct = prob.tile(lo + q);
+  int ckt = prob.kt_of(ct);
+  for (int g = 0; cj < my_n; ++g) {
+    Pp::wait_stage(issued - g - 1);
+    block_barrier();
+    if (iss_j < my_n) issue();
+    Pp::compute(smem + (g % Pp::NS) * Pp::STAGE, acc);
+    if (++cks == ckt) {
+      prob.epilogue(ct, acc);
+      Pp::zero(acc);
+      cks = 0;
+      if (++cj < my_n) {
+        ct = prob.tile(lo + q + cj * Gx);
+        ckt = prob.kt_of(ct);
+      }
+    }
+  }
+}
+
+template <class Pp>
+__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_wgrad(const WgradArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
+  WgradProb<Pp> prob{args};
+  stream_var<Pp>(prob, smem);
+}
+
 // Tile shapes and pipeline depths: BM, BN, WM, WN, NS, RB, BPC.
 #ifndef MOE_DENSE_CFG
 #define MOE_DENSE_CFG 128, 128, 2, 2, 2, 128, 2
@@ -828,6 +965,95 @@ hipError_t launch_expert_down(const Dims& D, const void* H, const int2* tile_inf
   a.out = Y;
   a.ldo = D.l;
   return launch_expert<EPI_STORE>(D, a, T, s);
+}
+
+// ------------------------------------------------------ backward launchers --
+hipError_t launch_dense_nt(const Dims& D, int tag, const void* A, int lda_bytes, int M, int K_bytes,
+                           const DenseSegSpec* segs, int nseg, int ldb_bytes, hipStream_t s) {
+  constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN, RB = DensePipe<true>::RB;
+  if (nseg < 1 || nseg > 3 || K_bytes <= 0 || K_bytes % RB || lda_bytes % 16 || ldb_bytes % 16)
+    return hipErrorInvalidValue;
+  if (M == 0) return hipSuccess;
+  DenseArgs a{};
+  a.A[0] = static_cast<const char*>(A);
+  a.lda_bytes[0] = lda_bytes;
+  a.ldb_bytes[0] = ldb_bytes;
+  a.kt[0] = K_bytes / RB;
+  a.kt[1] = 0;
+  a.M = M;
+  a.m_tiles = (M + BM - 1) / BM;
+  a.nseg = nseg;
+  a.total_ntiles = 0;
+  for (int i = 0; i < nseg; ++i) {
+    if (segs[i].kind != EPI_F32 && segs[i].kind != EPI_STORE) return hipErrorInvalidValue;
+    DenseSeg& g = a.seg[i];
+    g.B[0] = static_cast<const char*>(segs[i].B);
+    g.N = segs[i].N;
+    g.ntiles = (segs[i].N + BN - 1) / BN;
+    g.kind = segs[i].kind;
+    g.out = segs[i].out;
+    g.ldo = segs[i].ldo;
+    g.col_off = nullptr;
+    a.total_ntiles += g.ntiles;
+  }
+  switch (tag) {
+    case 3: return launch_dense_any<3>(D, a, s);
+    case 4: return launch_dense_any<4>(D, a, s);
+    case 5: return launch_dense_any<5>(D, a, s);
+    case 6: return launch_dense_any<6>(D, a, s);
+    default: return launch_dense_any<7>(D, a, s);
+  }
+}
+
+hipError_t launch_expert_nt(const Dims& D, const void* A, int lda_bytes, const int32_t* gather, const void* W,
+                            size_t w_expert_bytes, int ldb_bytes, int N, int K_bytes, const int2* tile_info,
+                            const int32_t* n_mtiles, int T, void* out, int ldo, hipStream_t s) {
+  constexpr int BN = ExpertPipe<true>::BN, RB = ExpertPipe<true>::RB;
+  if (K_bytes <= 0 || K_bytes % RB || lda_bytes % 16 || ldb_bytes % 16) return hipErrorInvalidValue;
+  ExpertArgs a{};
+  a.A = static_cast<const char*>(A);
+  a.lda_bytes = lda_bytes;
+  a.gather = gather;
+  a.W = static_cast<const char*>(W);
+  a.Wu = nullptr;
+  a.ldb_bytes = ldb_bytes;
+  a.w_expert_bytes = w_expert_bytes;
+  a.N = N;
+  a.NT = (N + BN - 1) / BN;
+  a.kt = K_bytes / RB;
+  a.tile_info = tile_info;
+  a.n_mtiles = n_mtiles;
+  a.out = out;
+  a.ldo = ldo;
+  return launch_expert<EPI_STORE>(D, a, T, s);
+}
+
+hipError_t launch_wgrad(const Dims& D, const void* A, int lda_bytes, const void* B, int ldb_bytes,
+                        const int32_t* koff, int M, int N, float* out, hipStream_t s) {
+  constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN;
+  if (lda_bytes % 16 || ldb_bytes % 16) return hipErrorInvalidValue;
+  WgradArgs a{};
+  a.A = static_cast<const char*>(A);
+  a.lda_bytes = lda_bytes;
+  a.B = static_cast<const char*>(B);
+  a.ldb_bytes = ldb_bytes;
+  a.koff = koff;
+  a.es = esz(D);
+  a.M = M;
+  a.N = N;
+  a.MT = (M + BM - 1) / BM;
+  a.NT = (N + BN - 1) / BN;
+  a.E = D.E;
+  a.out = out;
+  const long long tiles = (long long)a.E * a.MT * a.NT;
+  if (tiles == 0) return hipSuccess;
+  if (D.bf16)
+    hipLaunchKernelGGL(k_gemm_wgrad<DensePipe<true>>, dim3(persistent_grid(tiles, DensePipe<true>::BPC)),
+                       dim3(DensePipe<true>::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_gemm_wgrad<DensePipe<false>>, dim3(persistent_grid(tiles, DensePipe<false>::BPC)),
+                       dim3(DensePipe<false>::THREADS), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -75,4 +75,50 @@ hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_sr
 hipError_t launch_expert_down(const Dims& D, const void* H, const int2* tile_info, const int32_t* n_mtiles, int T,
                               const void* W_d, void* Y, hipStream_t s);
 
+// ---------------------------------------------------------------- backward --
+// One column segment of a dense NT product C = A B^T: B [N, K] rows of ldb
+// bytes; kind 0 = fp32 output, 1 = output in the activation dtype.
+struct DenseSegSpec {
+  const void* B;
+  int N;
+  int kind;
+  void* out;
+  int ldo;
+};
+// Dense C = A B^T, A [M, K] (lda bytes), up to 3 column segments sharing
+// ldb; K_bytes a multiple of the stage row (128 B).  `tag` (3..7) only names
+// the launch for profiles.
+hipError_t launch_dense_nt(const Dims& D, int tag, const void* A, int lda_bytes, int M, int K_bytes,
+                           const DenseSegSpec* segs, int nseg, int ldb_bytes, hipStream_t s);
+// Grouped C_e = A_e W_e^T over the forward's expert m-tiles (rows grouped by
+// expert, optionally gathered: A row of grouped row r = gather[r]); W_e at
+// W + e * w_expert_bytes, [N, K]; output in the activation dtype.
+hipError_t launch_expert_nt(const Dims& D, const void* A, int lda_bytes, const int32_t* gather, const void* W,
+                            size_t w_expert_bytes, int ldb_bytes, int N, int K_bytes, const int2* tile_info,
+                            const int32_t* n_mtiles, int T, void* out, int ldo, hipStream_t s);
+// Per-expert fp32 C_e [M, N] = A_e B_e^T with expert e's K range
+// koff[e] .. koff[e+1] (elements, padded segments of A [M, *] and B [N, *]).
+hipError_t launch_wgrad(const Dims& D, const void* A, int lda_bytes, const void* B, int ldb_bytes,
+                        const int32_t* koff, int M, int N, float* out, hipStream_t s);
+
+// dst[c][col_off + p] = src[gather[colmap[p]]][c] (maps optional), 0 for
+// rows < 0 or >= R; `batch` matrices at the given strides (elements).
+hipError_t launch_transpose(const Dims& D, const void* src, int R, int C, long long ld_src, long long src_bstride,
+                            const int32_t* gather, const int32_t* colmap, int P, void* dst, long long ld_dst,
+                            long long col_off, long long dst_bstride, int batch, hipStream_t s);
+// Padded per-expert K segments (whole 64-element stages, at least one) and
+// the map from padded column to grouped row (-1 = pad) up to Kt columns.
+hipError_t launch_pad_map(const Dims& D, const int32_t* offsets, int Kt, int32_t* koff, int32_t* colmap,
+                          hipStream_t s);
+hipError_t launch_glu_bwd(const Dims& D, const void* P, const void* Q, const void* dG, long long R, int n, void* dP,
+                          void* dQ, int ldo, hipStream_t s);
+hipError_t launch_combine_bwd(const Dims& D, const void* dy, const void* Y, const float* gates, const int32_t* inv,
+                              int T, void* dY, float* dg, hipStream_t s);
+hipError_t launch_dispatch_bwd(const Dims& D, const void* dX, const int32_t* inv, int T, void* dz, int ldo,
+                               hipStream_t s);
+hipError_t launch_gates_bwd(const Dims& D, const float* logits, const int32_t* idx, const float* dg, int T, int Epad,
+                            void* dl, int ldo, hipStream_t s);
+hipError_t launch_rmsnorm_bwd(const Dims& D, const void* x, const float* gamma, const float* dh, int T, void* dx,
+                              float* rstd, float* part, int slices, float* dgamma, hipStream_t s);
+
 }  // namespace moe

@@ -219,6 +219,67 @@ moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s) {
   return MOE_OK;
 }
 
+// ----------------------------------------------------------------- backward --
+struct BwdLayout {
+  size_t Bop1, Bop2, WdT, WguT, P, Q, dG, dy, dAcat, dg, dY, dH, Apre, U, dAU, dX, dh, rstd, gpart;
+  size_t doutT, GyT, dAcatT, hT, dYT, HT, dAUT, XT, dWcat, dWgu, koff, colmap, total;
+  int Tp, Kt, Epad, Kc;
+};
+constexpr int kGammaSlices = 64;
+
+void bwd_layout(const moe_config* c, int64_t T, BwdLayout* L) {
+  const size_t es = c->dtype == MOE_BF16 ? 2 : 4;
+  const size_t t = (size_t)T, E = (size_t)c->E, k = (size_t)c->k, d = c->d, l = c->l, f = c->f, fs = c->f_s;
+  const size_t Tk = t * k;
+  L->Tp = (int)((t + 63) / 64 * 64);
+  L->Kt = (int)((Tk + 64 * E + 63) / 64 * 64);
+  L->Epad = (int)((E + 63) / 64 * 64);
+  L->Kc = (int)(2 * fs + l + (size_t)L->Epad);
+  const size_t Tp = L->Tp, Kt = L->Kt, Kc = L->Kc;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = up(o + bytes);
+    return at;
+  };
+  L->Bop1 = take((fs + l) * d * es);
+  L->Bop2 = take(d * Kc * es);
+  L->WdT = take(E * f * l * es);
+  L->WguT = take(E * l * 2 * f * es);
+  L->P = take(t * fs * es);
+  L->Q = take(t * fs * es);
+  L->dG = take(t * fs * es);
+  L->dy = take(t * l * es);
+  L->dAcat = take(t * Kc * es);
+  L->dg = take(t * k * 4);
+  L->dY = take(Tk * l * es);
+  L->dH = take(Tk * f * es);
+  L->Apre = take(Tk * f * es);
+  L->U = take(Tk * f * es);
+  L->dAU = take(Tk * 2 * f * es);
+  L->dX = take(Tk * l * es);
+  L->dh = take(t * d * 4);
+  L->rstd = take(t * 4);
+  L->gpart = take((size_t)kGammaSlices * d * 4);
+  L->doutT = take(d * Tp * es);
+  L->GyT = take((fs + l) * Tp * es);
+  L->dAcatT = take(Kc * Tp * es);
+  L->hT = take(d * Tp * es);
+  L->dYT = take(l * Kt * es);
+  L->HT = take(f * Kt * es);
+  L->dAUT = take(2 * f * Kt * es);
+  L->XT = take(l * Kt * es);
+  L->dWcat = take(Kc * d * 4);
+  L->dWgu = take(E * 2 * f * l * 4);
+  L->koff = take((E + 1) * 4);
+  L->colmap = take(Kt * 4);
+  L->total = o;
+}
+
+moe_status hip_ok(hipError_t e, const char* what) {
+  return e == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
 }  // namespace
 
 extern "C" {
@@ -352,6 +413,166 @@ moe_status qb_update(moe_ctx* ctx, void* stream) {
   return MOE_OK;
 }
 
+size_t moe_backward_workspace_bytes(const moe_config* cfg, int64_t T) {
+  if (check_config(cfg) != MOE_OK || T < 0 || T > cfg->max_tokens) return 0;
+  BwdLayout L;
+  bwd_layout(cfg, T, &L);
+  return L.total;
+}
+
+moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T, const moe_route_out* r,
+                        const void* fwd_ws, size_t fwd_ws_bytes, void* dx, const moe_grads* g, void* ws,
+                        size_t ws_bytes, void* stream) {
+  moe_status st = check_call(ctx, T, const_cast<void*>(fwd_ws), fwd_ws_bytes);
+  if (st != MOE_OK || T == 0) return st;
+  if (!x || !dout || !dx || !g) return fail(MOE_ERR_INVALID_ARG, "x, dout, dx or grads is NULL");
+  const moe_config& c = ctx->cfg;
+  if (!g->gamma || !g->W_r || !g->W_dn || !g->W_g || !g->W_u || !g->W_d || !g->W_up ||
+      (c.f_s > 0 && (!g->W_sg || !g->W_su || !g->W_sd)))
+    return fail(MOE_ERR_INVALID_ARG, "a required gradient pointer is NULL");
+  BwdLayout B;
+  bwd_layout(&c, T, &B);
+  if (!ws || ws_bytes < B.total)
+    return fail(MOE_ERR_WORKSPACE, "backward workspace of %zu bytes given, %zu needed", ws ? ws_bytes : (size_t)0,
+                B.total);
+  if (!aligned(ws, kAlign)) return fail(MOE_ERR_WORKSPACE, "backward workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Dims& D = ctx->D;
+  const int t = (int)T, E = c.E, k = c.k, d = c.d, l = c.l, f = c.f, fs = c.f_s;
+  const int es = c.dtype == MOE_BF16 ? 2 : 4;
+  const int Tk = t * k, Tp = B.Tp, Kt = B.Kt, Kc = B.Kc, Epad = B.Epad;
+  moe_ws_layout L;
+  ws_layout(&c, T, &L);
+  char* fw = static_cast<char*>(const_cast<void*>(fwd_ws));
+  const RoutePtrs p = route_ptrs(L, fw, r);
+  const void *h = fw + L.h, *G = fw + L.G, *z = fw + L.z, *H = fw + L.H, *Y = fw + L.Y, *y_lat = fw + L.y_lat;
+  const int32_t* n_mtiles = p.tile_offsets + E;
+  char* w = static_cast<char*>(ws);
+  auto at = [&](size_t off) { return static_cast<void*>(w + off); };
+  void *Bop1 = at(B.Bop1), *Bop2 = at(B.Bop2), *WdT = at(B.WdT), *WguT = at(B.WguT), *P = at(B.P), *Q = at(B.Q);
+  void *dG = at(B.dG), *dy = at(B.dy), *dAcat = at(B.dAcat), *dY = at(B.dY), *dH = at(B.dH), *Apre = at(B.Apre);
+  void *U = at(B.U), *dAU = at(B.dAU), *dX = at(B.dX), *doutT = at(B.doutT), *GyT = at(B.GyT);
+  void *dAcatT = at(B.dAcatT), *hT = at(B.hT), *dYT = at(B.dYT), *HT = at(B.HT), *dAUT = at(B.dAUT), *XT = at(B.XT);
+  float* dg = static_cast<float*>(at(B.dg));
+  float* dh = static_cast<float*>(at(B.dh));
+  float* dWcat = static_cast<float*>(at(B.dWcat));
+  float* dWgu = static_cast<float*>(at(B.dWgu));
+  int32_t* koff = static_cast<int32_t*>(at(B.koff));
+  int32_t* colmap = static_cast<int32_t*>(at(B.colmap));
+  auto el = [&](const void* base, size_t elems) { return static_cast<const char*>(base) + elems * es; };
+  auto elw = [&](void* base, size_t elems) { return static_cast<char*>(base) + elems * es; };
+  const moe_weights& W = ctx->w;
+
+  // weight operands of the data-gradient products, K-contiguous
+  MOE_RUN(MOE_K_BWD_TRANSPOSE, [&]() -> hipError_t {
+    hipError_t e = hipSuccess;
+    if (fs > 0) e = launch_transpose(D, W.W_sd, d, fs, fs, 0, nullptr, nullptr, d, Bop1, d, 0, 0, 1, s);  // W_sd^T
+    if (e == hipSuccess)
+      e = launch_transpose(D, W.W_up, d, l, l, 0, nullptr, nullptr, d, elw(Bop1, (size_t)fs * d), d, 0, 0, 1, s);
+    if (e == hipSuccess && fs > 0) e = launch_transpose(D, W.W_sg, fs, d, d, 0, nullptr, nullptr, fs, Bop2, Kc, 0, 0, 1, s);
+    if (e == hipSuccess && fs > 0)
+      e = launch_transpose(D, W.W_su, fs, d, d, 0, nullptr, nullptr, fs, Bop2, Kc, fs, 0, 1, s);
+    if (e == hipSuccess) e = launch_transpose(D, W.W_dn, l, d, d, 0, nullptr, nullptr, l, Bop2, Kc, 2 * fs, 0, 1, s);
+    if (e == hipSuccess)
+      e = launch_transpose(D, W.W_r, E, d, d, 0, nullptr, nullptr, Epad, Bop2, Kc, 2 * fs + l, 0, 1, s);
+    if (e == hipSuccess)  // W_d[e] [l,f] -> [f,l]
+      e = launch_transpose(D, W.W_d, l, f, f, (long long)l * f, nullptr, nullptr, l, WdT, l, 0, (long long)f * l, E, s);
+    if (e == hipSuccess)  // W_g[e], W_u[e] [f,l] -> [l, 2f] = [W_g^T | W_u^T]
+      e = launch_transpose(D, W.W_g, f, l, l, (long long)f * l, nullptr, nullptr, f, WguT, 2 * f, 0,
+                           (long long)l * 2 * f, E, s);
+    if (e == hipSuccess)
+      e = launch_transpose(D, W.W_u, f, l, l, (long long)f * l, nullptr, nullptr, f, WguT, 2 * f, f,
+                           (long long)l * 2 * f, E, s);
+    return e;
+  }());
+  // output projections: [dG | dy_lat] = dout [W_sd | W_up]
+  {
+    DenseSegSpec sg[2];
+    int n = 0;
+    if (fs > 0) sg[n++] = {Bop1, fs, 1, dG, fs};
+    sg[n++] = {el(Bop1, (size_t)fs * d), l, 1, dy, l};
+    MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 4, dout, d * es, t, d * es, sg, n, d * es, s));
+  }
+  if (fs > 0) {  // shared GLU: recompute P, Q; dP, dQ into the first 2 f_s columns of dAcat
+    DenseSegSpec sg[2] = {{W.W_sg, fs, 1, P, fs}, {W.W_su, fs, 1, Q, fs}};
+    MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 3, h, d * es, t, d * es, sg, 2, d * es, s));
+    MOE_RUN(MOE_K_BWD_ELTWISE, launch_glu_bwd(D, P, Q, dG, t, fs, dAcat, elw(dAcat, fs), Kc, s));
+  }
+  // combine transpose: dY rows and gate gradients
+  MOE_RUN(MOE_K_BWD_ELTWISE, launch_combine_bwd(D, dy, Y, p.gates, p.inv, t, dY, dg, s));
+  // experts: dH = dY W_d; recompute A = X W_g^T, U = X W_u^T; GLU derivative; dX = [dA|dU] [W_g; W_u]
+  const size_t wfl = (size_t)f * l * es;
+  MOE_RUN(MOE_K_BWD_EXPERT,
+          launch_expert_nt(D, dY, l * es, nullptr, WdT, wfl, l * es, f, l * es, p.tile_info, n_mtiles, t, dH, f, s));
+  MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, z, l * es, p.perm_src, W.W_g, wfl, l * es, f, l * es, p.tile_info,
+                                             n_mtiles, t, Apre, f, s));
+  MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, z, l * es, p.perm_src, W.W_u, wfl, l * es, f, l * es, p.tile_info,
+                                             n_mtiles, t, U, f, s));
+  MOE_RUN(MOE_K_BWD_ELTWISE, launch_glu_bwd(D, Apre, U, dH, Tk, f, dAU, elw(dAU, f), 2 * f, s));
+  MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, dAU, 2 * f * es, nullptr, WguT, wfl * 2, 2 * f * es, l, 2 * f * es,
+                                             p.tile_info, n_mtiles, t, dX, l, s));
+  // dispatch transpose and router: dz and dl into their columns of dAcat
+  MOE_RUN(MOE_K_BWD_ELTWISE, launch_dispatch_bwd(D, dX, p.inv, t, elw(dAcat, 2 * fs), Kc, s));
+  MOE_RUN(MOE_K_BWD_ELTWISE, launch_gates_bwd(D, p.logits, p.idx, dg, t, Epad, elw(dAcat, 2 * fs + l), Kc, s));
+  // dh = [dP | dQ | dz | dl] [W_sg; W_su; W_dn; W_r], then RMSNorm
+  {
+    DenseSegSpec sg[1] = {{Bop2, d, 0, dh, d}};
+    MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 5, dAcat, Kc * es, t, Kc * es, sg, 1, Kc * es, s));
+  }
+  MOE_RUN(MOE_K_BWD_ELTWISE, launch_rmsnorm_bwd(D, x, W.gamma, dh, t, dx, static_cast<float*>(at(B.rstd)),
+                                                static_cast<float*>(at(B.gpart)), kGammaSlices, g->gamma, s));
+  // weight gradients of the dense products: K = tokens (padded to Tp with zeros)
+  MOE_RUN(MOE_K_BWD_TRANSPOSE, [&]() -> hipError_t {
+    hipError_t e = launch_transpose(D, dout, t, d, d, 0, nullptr, nullptr, Tp, doutT, Tp, 0, 0, 1, s);
+    if (e == hipSuccess && fs > 0) e = launch_transpose(D, G, t, fs, fs, 0, nullptr, nullptr, Tp, GyT, Tp, 0, 0, 1, s);
+    if (e == hipSuccess)
+      e = launch_transpose(D, y_lat, t, l, l, 0, nullptr, nullptr, Tp, elw(GyT, (size_t)fs * Tp), Tp, 0, 0, 1, s);
+    if (e == hipSuccess) e = launch_transpose(D, dAcat, t, Kc, Kc, 0, nullptr, nullptr, Tp, dAcatT, Tp, 0, 0, 1, s);
+    if (e == hipSuccess) e = launch_transpose(D, h, t, d, d, 0, nullptr, nullptr, Tp, hT, Tp, 0, 0, 1, s);
+    return e;
+  }());
+  {
+    DenseSegSpec sg[2];
+    int n = 0;
+    if (fs > 0) sg[n++] = {GyT, fs, 0, g->W_sd, fs};
+    sg[n++] = {el(GyT, (size_t)fs * Tp), l, 0, g->W_up, l};
+    MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 7, doutT, Tp * es, d, Tp * es, sg, n, Tp * es, s));
+    DenseSegSpec sw[1] = {{hT, d, 0, dWcat, d}};
+    MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 6, dAcatT, Tp * es, Kc, Tp * es, sw, 1, Tp * es, s));
+  }
+  st = hip_ok([&]() -> hipError_t {
+    const size_t row = (size_t)d * 4;
+    hipError_t e = hipSuccess;
+    if (fs > 0) e = hipMemcpyAsync(g->W_sg, dWcat, fs * row, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && fs > 0) e = hipMemcpyAsync(g->W_su, dWcat + (size_t)fs * d, fs * row, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(g->W_dn, dWcat + (size_t)2 * fs * d, (size_t)l * row, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(g->W_r, dWcat + (size_t)(2 * fs + l) * d, (size_t)E * row, hipMemcpyDeviceToDevice, s);
+    return e;
+  }(), "gradient copy");
+  if (st != MOE_OK) return st;
+  // per-expert weight gradients: K = the expert's rows, padded segments
+  MOE_RUN(MOE_K_BWD_TRANSPOSE, [&]() -> hipError_t {
+    hipError_t e = launch_pad_map(D, p.offsets, Kt, koff, colmap, s);
+    if (e == hipSuccess) e = launch_transpose(D, dY, Tk, l, l, 0, nullptr, colmap, Kt, dYT, Kt, 0, 0, 1, s);
+    if (e == hipSuccess) e = launch_transpose(D, H, Tk, f, f, 0, nullptr, colmap, Kt, HT, Kt, 0, 0, 1, s);
+    if (e == hipSuccess) e = launch_transpose(D, dAU, Tk, 2 * f, 2 * f, 0, nullptr, colmap, Kt, dAUT, Kt, 0, 0, 1, s);
+    if (e == hipSuccess) e = launch_transpose(D, z, Tk, l, l, 0, p.perm_src, colmap, Kt, XT, Kt, 0, 0, 1, s);
+    return e;
+  }());
+  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, dYT, Kt * es, HT, Kt * es, koff, l, f, g->W_d, s));
+  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, dAUT, Kt * es, XT, Kt * es, koff, 2 * f, l, dWgu, s));
+  return hip_ok([&]() -> hipError_t {
+    const size_t blk = (size_t)f * l * 4;
+    hipError_t e = hipMemcpy2DAsync(g->W_g, blk, dWgu, 2 * blk, blk, E, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(g->W_u, blk, reinterpret_cast<char*>(dWgu) + blk, 2 * blk, blk, E,
+                           hipMemcpyDeviceToDevice, s);
+    return e;
+  }(), "gradient copy");
+}
+
 moe_status moe_get_bias(moe_ctx* ctx, float* dst, void* stream) {
   if (!ctx || !dst) return fail(MOE_ERR_INVALID_ARG, "context or destination is NULL");
   hipError_t e = hipMemcpyAsync(dst, ctx->state + ctx->sl.bias, (size_t)ctx->cfg.E * 4, hipMemcpyDefault,
@@ -398,7 +619,8 @@ const char* moe_kernel_name(int id) {
   static const char* names[MOE_NUM_KERNELS] = {"rmsnorm",     "gemm_h",  "topk",     "hist",
                                                 "scan",        "scatter", "expert_up", "expert_down",
                                                 "combine",     "gemm_out", "qb_quantile", "qb_bias", "gemm_rz",
-                                                "sign_bias"};
+                                                "sign_bias",   "bwd_gemm", "bwd_expert", "bwd_wgrad",
+                                                "bwd_eltwise", "bwd_transpose"};
   return (id >= 0 && id < MOE_NUM_KERNELS) ? names[id] : "unknown";
 }
 

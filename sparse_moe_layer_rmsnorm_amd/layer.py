@@ -136,6 +136,30 @@ class MoeLayer:
                     _stream(stream))
         return route
 
+    def backward(self, x: torch.Tensor, dout: torch.Tensor, route: Optional[Dict[str, torch.Tensor]] = None,
+                 grads: Optional[Dict[str, torch.Tensor]] = None, stream=None):
+        """Gradients for the last forward(x, route=route): returns (dx, grads),
+        grads fp32 tensors keyed like the weights (plus "gamma")."""
+        T = x.shape[0]
+        dm = self.dims
+        if grads is None:
+            shapes = {"gamma": (dm["d"],), "W_r": (dm["E"], dm["d"]), "W_sg": (dm["f_s"], dm["d"]),
+                      "W_su": (dm["f_s"], dm["d"]), "W_sd": (dm["d"], dm["f_s"]), "W_dn": (dm["l"], dm["d"]),
+                      "W_g": (dm["E"], dm["f"], dm["l"]), "W_u": (dm["E"], dm["f"], dm["l"]),
+                      "W_d": (dm["E"], dm["l"], dm["f"]), "W_up": (dm["d"], dm["l"])}
+            grads = {n: torch.empty(*sh, dtype=torch.float32, device=self.device) for n, sh in shapes.items()
+                     if not (n in ("W_sg", "W_su", "W_sd") and dm["f_s"] == 0)}
+        dx = torch.empty_like(x)
+        fws = self.workspace(T)
+        need = B.moe_backward_workspace_bytes(self.cfg, T)
+        if getattr(self, "_bws", None) is None or self._bws.numel() < need:
+            self._bws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        g = B.moe_grads(**{n: _ptr(grads.get(n)) for n in ("gamma", "W_r", "W_sg", "W_su", "W_sd", "W_dn", "W_g",
+                                                            "W_u", "W_d", "W_up")})
+        B.moe_backward(self.ctx, x.data_ptr(), dout.data_ptr(), T, self._route_struct(route), fws.data_ptr(),
+                       fws.numel(), dx.data_ptr(), g, self._bws.data_ptr(), self._bws.numel(), _stream(stream))
+        return dx, grads
+
     def qb_update(self, stream=None) -> None:
         B.qb_update(self.ctx, _stream(stream))
 
