@@ -32,6 +32,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 from sparse_moe_layer_rmsnorm_amd.profsum import source_hash  # noqa: E402
 
 METRIC = "MoE-layer fwd tokens/sec on 1 MI355X + % bf16 MFMA peak + routing GB/s"
+METRIC_BWD = "MoE-layer fwd+bwd tokens/sec on 1 MI355X (training step: forward, backward, bias update)"
 
 
 def kernel_work(s, T: int) -> dict:
@@ -61,6 +62,21 @@ def kernel_work(s, T: int) -> dict:
         "sign_bias": 16.0 * s.E,
     }
     return {"flops": flops, "bytes": bytes_}
+
+
+def backward_flops(s, T: int) -> dict:
+    """GEMM FLOPs of one backward pass per launch group (0: memory-bound
+    groups): the dense products (shared pre-activations recomputed, the two
+    output-projection transposes, dh, and the dense weight gradients), the
+    grouped expert products (dH, A and U recomputed, dX) and the per-expert
+    weight gradients."""
+    Tk = T * s.k
+    Kc = 2 * s.f_s + s.l + (s.E + 63) // 64 * 64
+    dense = 2.0 * T * s.d * (2 * s.f_s) + 2.0 * T * s.d * (s.f_s + s.l) + 2.0 * T * Kc * s.d \
+        + 2.0 * s.d * T * (s.f_s + s.l) + 2.0 * Kc * T * s.d
+    expert = 2.0 * Tk * s.l * s.f * 3 + 2.0 * Tk * 2 * s.f * s.l
+    wgrad = 2.0 * Tk * s.l * s.f + 2.0 * Tk * 2 * s.f * s.l
+    return {"bwd_gemm": dense, "bwd_expert": expert, "bwd_wgrad": wgrad, "bwd_eltwise": 0.0, "bwd_transpose": 0.0}
 
 
 def traffic_for(kernel: str, workload: str):
@@ -117,6 +133,9 @@ def main() -> int:
     ap.add_argument("--no-profile", action="store_true", help="no per-kernel events in the timed region")
     ap.add_argument("--balancer", choices=("qb", "sign"), default="qb",
                     help="bias update rule of the step: quantile balancing (default) or the sign rule")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the training step with the backward pass: forward, moe_backward (dx and all weight "
+                         "gradients) and the bias update")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device copy of 256 MiB (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -154,8 +173,16 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    grads = None
+    if args.backward:
+        dout = torch.randn(T, shape.d, generator=torch.Generator().manual_seed(7)).cuda().to(layer.tdtype)
+        layer.forward(x, out=out)
+        _, grads = layer.backward(x, dout)
+
     def step():
         layer.forward(x, out=out)
+        if args.backward:
+            layer.backward(x, dout, grads=grads)
         layer.qb_update()
 
     for _ in range(args.warmup):
@@ -164,12 +191,13 @@ def main() -> int:
     # Per-kernel times: one pass of K steps with every launch bracketed by HIP
     # events on the launch stream (outside the timed region: 24 events a step
     # would add their own cost to it).
-    B.moe_profile_begin(layer.ctx, 16 * args.steps + 16)
+    B.moe_profile_begin(layer.ctx, 64 * args.steps + 64)
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     prof = B.moe_profile_end(layer.ctx)
-    dom = max((n for n in prof if prof[n][1]), key=lambda n: prof[n][0])
+    # the roofline object describes the forward's dominant kernel
+    dom = max((n for n in prof if prof[n][1] and not n.startswith("bwd_")), key=lambda n: prof[n][0])
     run = step
     if args.graph:
         g = torch.cuda.CUDAGraph()
@@ -232,10 +260,25 @@ def main() -> int:
     rt_names = [n for n in ("topk", "scan", "scatter", "combine") if n in kernels]
     rt_us = sum(kernels[n]["avg_us"] for n in rt_names)
     rt_bytes = sum(work["bytes"].get(n, 0.0) for n in rt_names)
-    layer_flops = sum(work["flops"].values())
+    # GEMM FLOPs of one step: the launched forward GEMMs (plus the backward's)
+    layer_flops = sum(work["flops"][n] * kernels[n]["launches"] / args.steps for n in kernels if n in work["flops"])
+    if args.backward:
+        layer_flops += sum(backward_flops(shape, T).values())
 
+    bwd = None
+    if args.backward:
+        bf = backward_flops(shape, T)
+        bwd = {}
+        for n, fl in bf.items():
+            ms, cnt = prof.get(n, (0.0, 0))
+            if cnt:
+                us = ms / args.steps * 1e3
+                bwd[n] = {"us_per_step": round(us, 2), "launches_per_step": cnt // args.steps}
+                if fl:
+                    bwd[n].update(tflops=round(fl / (us * 1e-6) / 1e12, 1),
+                                  mfma_frac=round(fl / (us * 1e-6) / 1e12 / peak_mm, 4))
     res = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if args.backward else METRIC,
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -253,7 +296,9 @@ def main() -> int:
         "config": {"workload": f"{shape.name}: T={T} tokens, d={shape.d}, l={shape.l}, E={shape.E}, k={shape.k}, "
                                f"f={shape.f}, f_s={shape.f_s}, B={shape.B}, QB {'frozen' if frozen else 'train'}"
                                + (", sign-rule balancer" if args.balancer == "sign" else ""),
-                   "global_batch": T, "step": "training forward + qb_update"},
+                   "global_batch": T,
+                   "step": "training forward + backward + qb_update" if args.backward else
+                           "training forward + qb_update"},
         "roofline": roofline,
         "layer_mfma_frac": round(layer_flops / (ms_step * 1e-3) / 1e12 / peak_mm, 4),
         "expert_gemm": {"tflops": round(ex_tf, 1), "mfma_frac": round(ex_tf / peak_mm, 4)},
@@ -262,6 +307,8 @@ def main() -> int:
                                     "us": round(rt_us, 2)},
         "kernels": kernels,
     }
+    if bwd is not None:
+        res["backward"] = bwd
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(shape, dict(W, c=c) if c is not None else W, x_np, args.cpu_seconds)
     layer.close()
