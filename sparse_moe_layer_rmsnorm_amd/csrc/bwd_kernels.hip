@@ -11,6 +11,32 @@
 namespace moe {
 namespace {
 
+// 16 bytes <-> 8 bf16 or 4 fp32 values
+template <bool BF16>
+MOE_DEV void unpack(const uint4& v, float* f) {
+  if constexpr (BF16) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[2 * q] = bf16_bits_to_f32(w[q] & 0xFFFFu);
+      f[2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
+    }
+  } else {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+}
+template <bool BF16>
+MOE_DEV uint4 pack(const float* f) {
+  if constexpr (BF16)
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                      pack_bf16x2(f[6], f[7]));
+  else
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+}
+
 template <bool BF16>
 MOE_DEV float ld_act(const void* p, size_t i) {
   if constexpr (BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
@@ -61,6 +87,76 @@ __global__ __launch_bounds__(256) void k_transpose(const E* __restrict__ src, in
   }
 }
 
+// Vectorised transposes for the common case (C and P multiples of 64, rows
+// and column offsets on 16-byte boundaries): each wavefront reads 8 (bf16) or
+// 4 (fp32) source rows as whole 128/256-byte runs and writes whole 128-byte
+// runs of destination rows; the tile sits in LDS as dwords with one pad
+// dword per row, so that neither phase has bank conflicts beyond two-way.
+MOE_DEV int src_row_of(int p, int R, const int32_t* __restrict__ gather, const int32_t* __restrict__ colmap) {
+  const int r = colmap ? colmap[p] : p;
+  return (r >= 0 && r < R) ? (gather ? gather[r] : r) : -1;
+}
+
+__global__ __launch_bounds__(256) void k_transpose_b16(const uint16_t* __restrict__ src, int R, long long ld_src,
+                                                       long long src_bstride, const int32_t* __restrict__ gather,
+                                                       const int32_t* __restrict__ colmap, uint16_t* __restrict__ dst,
+                                                       long long ld_dst, long long col_off, long long dst_bstride) {
+  __shared__ uint32_t tile[64][33];  // row p: 64 bf16 of c as 32 dwords
+  const int p0 = blockIdx.x * 64, c0 = blockIdx.y * 64, t = threadIdx.x;
+  src += (size_t)blockIdx.z * src_bstride;
+  dst += (size_t)blockIdx.z * dst_bstride;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = t + 256 * i, pr = idx >> 3, ch = idx & 7;
+    const int sr = src_row_of(p0 + pr, R, gather, colmap);
+    const uint4 v = sr >= 0 ? *reinterpret_cast<const uint4*>(src + (size_t)sr * ld_src + c0 + 8 * ch)
+                            : make_uint4(0, 0, 0, 0);
+    tile[pr][4 * ch + 0] = v.x;
+    tile[pr][4 * ch + 1] = v.y;
+    tile[pr][4 * ch + 2] = v.z;
+    tile[pr][4 * ch + 3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = t + 256 * i, pc = idx & 7, cr = idx >> 3;
+    const int sh = (cr & 1) * 16;
+    uint32_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = (tile[8 * pc + j][cr >> 1] >> sh) & 0xFFFFu;
+    *reinterpret_cast<uint4*>(dst + (size_t)(c0 + cr) * ld_dst + col_off + p0 + 8 * pc) =
+        make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+  }
+}
+
+__global__ __launch_bounds__(256) void k_transpose_b32(const uint32_t* __restrict__ src, int R, long long ld_src,
+                                                       long long src_bstride, const int32_t* __restrict__ gather,
+                                                       const int32_t* __restrict__ colmap, uint32_t* __restrict__ dst,
+                                                       long long ld_dst, long long col_off, long long dst_bstride) {
+  __shared__ uint32_t tile[64][65];
+  const int p0 = blockIdx.x * 64, c0 = blockIdx.y * 64, t = threadIdx.x;
+  src += (size_t)blockIdx.z * src_bstride;
+  dst += (size_t)blockIdx.z * dst_bstride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = t + 256 * i, pr = idx >> 4, ch = idx & 15;
+    const int sr = src_row_of(p0 + pr, R, gather, colmap);
+    const uint4 v = sr >= 0 ? *reinterpret_cast<const uint4*>(src + (size_t)sr * ld_src + c0 + 4 * ch)
+                            : make_uint4(0, 0, 0, 0);
+    tile[pr][4 * ch + 0] = v.x;
+    tile[pr][4 * ch + 1] = v.y;
+    tile[pr][4 * ch + 2] = v.z;
+    tile[pr][4 * ch + 3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = t + 256 * i, pc = idx & 15, cr = idx >> 4;
+    *reinterpret_cast<uint4*>(dst + (size_t)(c0 + cr) * ld_dst + col_off + p0 + 4 * pc) =
+        make_uint4(tile[4 * pc][cr], tile[4 * pc + 1][cr], tile[4 * pc + 2][cr], tile[4 * pc + 3][cr]);
+  }
+}
+
 // ---------------------------------------------------- padded expert K map ----
 // koff[e] = sum over e' < e of pad(n_e'), pad(n) = max(1, ceil(n / 64)) * 64,
 // koff[E] the total; colmap[koff[e] + j] = offsets[e] + j for j < n_e, else
@@ -86,10 +182,10 @@ __global__ __launch_bounds__(1024) void k_pad_map(const int32_t* __restrict__ of
   if (i < E) koff[i] = r - pad;
   if (i == E - 1) koff[E] = r;
   __syncthreads();
-  for (int e = 0; e < E; ++e) {
+  for (int e = w; e < E; e += 16) {  // one wavefront per expert
     const int b = base[e], off = offsets[e], ne = offsets[e + 1] - off;
     const int pe = max(1, (ne + 63) / 64) * 64;
-    for (int j = i; j < pe; j += 1024) colmap[b + j] = j < ne ? off + j : -1;
+    for (int j = lane; j < pe; j += 64) colmap[b + j] = j < ne ? off + j : -1;
   }
   const int tot = base[E - 1] + max(1, (offsets[E] - offsets[E - 1] + 63) / 64) * 64;
   for (int j = tot + i; j < Kt; j += 1024) colmap[j] = -1;
@@ -99,30 +195,44 @@ __global__ __launch_bounds__(1024) void k_pad_map(const int32_t* __restrict__ of
 // G = silu(P) * Q  ->  dP = dG * Q * silu'(P), dQ = dG * silu(P), with
 // silu'(a) = sig(a) (1 + a (1 - sig(a))).  P, Q, dG [R, n] (ld n); dP, dQ at
 // rows of ldo elements.  fp32 arithmetic, stored in the activation dtype.
+// 16 bytes per thread and operand (n is a multiple of 64).
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_glu_bwd(const void* __restrict__ P, const void* __restrict__ Q,
                                                  const void* __restrict__ dG, long long R, int n, void* __restrict__ dP,
                                                  void* __restrict__ dQ, int ldo) {
-  const long long total = R * n;
+  constexpr int V = BF16 ? 8 : 4;
+  const long long total = R * n / V;
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
-    const long long r = i / n;
-    const int c = (int)(i - r * n);
-    const float a = ld_act<BF16>(P, i), u = ld_act<BF16>(Q, i), g = ld_act<BF16>(dG, i);
-    const float sg = 1.0f / (1.0f + __expf(-a));
-    const size_t o = (size_t)r * ldo + c;
-    st_act<BF16>(dP, o, g * u * (sg * (1.0f + a * (1.0f - sg))));
-    st_act<BF16>(dQ, o, g * a * sg);
+    const long long e0 = i * V;
+    const long long r = e0 / n;
+    const int c = (int)(e0 - r * n);
+    const uint4 pa = reinterpret_cast<const uint4*>(P)[i], qa = reinterpret_cast<const uint4*>(Q)[i];
+    const uint4 ga = reinterpret_cast<const uint4*>(dG)[i];
+    float a[V], u[V], g[V], op[V], oq[V];
+    unpack<BF16>(pa, a);
+    unpack<BF16>(qa, u);
+    unpack<BF16>(ga, g);
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const float sg = 1.0f / (1.0f + __expf(-a[j]));
+      op[j] = g[j] * u[j] * (sg * (1.0f + a[j] * (1.0f - sg)));
+      oq[j] = g[j] * a[j] * sg;
+    }
+    const size_t o = ((size_t)r * ldo + c) / V;
+    reinterpret_cast<uint4*>(dP)[o] = pack<BF16>(op);
+    reinterpret_cast<uint4*>(dQ)[o] = pack<BF16>(oq);
   }
 }
 
 // -------------------------------------------------------------- combine ----
 // y_lat[t] = sum_j g_tj Y[inv_tj]  ->  dY[inv_tj] = g_tj dy[t],
-// dg_tj = <dy[t], Y[inv_tj]>.  One wavefront per token.
+// dg_tj = <dy[t], Y[inv_tj]>.  One wavefront per token, 16-byte chunks.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_combine_bwd(const void* __restrict__ dy, const void* __restrict__ Y,
                                                      const float* __restrict__ gates, const int32_t* __restrict__ inv,
                                                      int T, int l, int k, void* __restrict__ dY,
                                                      float* __restrict__ dg) {
+  constexpr int V = BF16 ? 8 : 4;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -132,14 +242,24 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const void* __restrict__ dy
     my_row = inv[(size_t)t * k + lane];
     my_g = gates[(size_t)t * k + lane];
   }
+  const int nc = l / V;
+  const uint4* dyr = reinterpret_cast<const uint4*>(dy) + (size_t)t * nc;
   for (int j = 0; j < k; ++j) {
     const int row = __builtin_amdgcn_readlane(my_row, j);
     const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), j));
+    const uint4* yr = reinterpret_cast<const uint4*>(Y) + (size_t)row * nc;
+    uint4* out = reinterpret_cast<uint4*>(dY) + (size_t)row * nc;
     float dot = 0.f;
-    for (int c = lane; c < l; c += 64) {
-      const float v = ld_act<BF16>(dy, (size_t)t * l + c);
-      dot += v * ld_act<BF16>(Y, (size_t)row * l + c);
-      st_act<BF16>(dY, (size_t)row * l + c, g * v);
+    for (int c = lane; c < nc; c += 64) {
+      float a[V], b[V], o[V];
+      unpack<BF16>(dyr[c], a);
+      unpack<BF16>(yr[c], b);
+#pragma unroll
+      for (int q = 0; q < V; ++q) {
+        dot += a[q] * b[q];
+        o[q] = g * a[q];
+      }
+      out[c] = pack<BF16>(o);
     }
     dot = wave_sum(dot);
     if (lane == 0) dg[(size_t)t * k + j] = dot;
@@ -151,14 +271,23 @@ __global__ __launch_bounds__(256) void k_combine_bwd(const void* __restrict__ dy
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_dispatch_bwd(const void* __restrict__ dX, const int32_t* __restrict__ inv,
                                                       int T, int l, int k, void* __restrict__ dz, int ldo) {
+  constexpr int V = BF16 ? 8 : 4;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int my_row = lane < k ? inv[(size_t)t * k + lane] : 0;
-  for (int c = lane; c < l; c += 64) {
-    float a = 0.f;
-    for (int j = 0; j < k; ++j) a += ld_act<BF16>(dX, (size_t)__builtin_amdgcn_readlane(my_row, j) * l + c);
-    st_act<BF16>(dz, (size_t)t * ldo + c, a);
+  const int nc = l / V;
+  for (int c = lane; c < nc; c += 64) {
+    float a[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) a[q] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float b[V];
+      unpack<BF16>(reinterpret_cast<const uint4*>(dX)[(size_t)__builtin_amdgcn_readlane(my_row, j) * nc + c], b);
+#pragma unroll
+      for (int q = 0; q < V; ++q) a[q] += b[q];
+    }
+    reinterpret_cast<uint4*>(dz)[((size_t)t * ldo) / V + c] = pack<BF16>(a);
   }
 }
 
@@ -208,23 +337,42 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const void* __restrict__ x, const float* __restrict__ gamma,
                                                      const float* __restrict__ dh, int T, int d, float eps,
                                                      void* __restrict__ dx, float* __restrict__ rstd) {
+  constexpr int V = BF16 ? 8 : 4;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const size_t o = (size_t)t * d;
+  const int nc = d / V;
+  const uint4* xr = reinterpret_cast<const uint4*>(x) + (size_t)t * nc;
+  const float4* dhr = reinterpret_cast<const float4*>(dh + (size_t)t * d);
+  const float4* gr = reinterpret_cast<const float4*>(gamma);
   float ss = 0.f, dot = 0.f;
-  for (int c = lane; c < d; c += 64) {
-    const float v = ld_act<BF16>(x, o + c);
-    ss += v * v;
-    dot += gamma[c] * dh[o + c] * v;
+  for (int c = lane; c < nc; c += 64) {
+    float a[V];
+    unpack<BF16>(xr[c], a);
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      const float4 u = dhr[c * (V / 4) + q], gm = gr[c * (V / 4) + q];
+      ss += a[4 * q] * a[4 * q] + a[4 * q + 1] * a[4 * q + 1] + a[4 * q + 2] * a[4 * q + 2] + a[4 * q + 3] * a[4 * q + 3];
+      dot += gm.x * u.x * a[4 * q] + gm.y * u.y * a[4 * q + 1] + gm.z * u.z * a[4 * q + 2] + gm.w * u.w * a[4 * q + 3];
+    }
   }
   ss = wave_sum(ss);
   dot = wave_sum(dot);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
   const float corr = r * r * r * dot / (float)d;
-  for (int c = lane; c < d; c += 64) {
-    const float v = ld_act<BF16>(x, o + c);
-    st_act<BF16>(dx, o + c, r * gamma[c] * dh[o + c] - v * corr);
+  uint4* dxr = reinterpret_cast<uint4*>(dx) + (size_t)t * nc;
+  for (int c = lane; c < nc; c += 64) {
+    float a[V], o[V];
+    unpack<BF16>(xr[c], a);
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      const float4 u = dhr[c * (V / 4) + q], gm = gr[c * (V / 4) + q];
+      o[4 * q] = r * gm.x * u.x - a[4 * q] * corr;
+      o[4 * q + 1] = r * gm.y * u.y - a[4 * q + 1] * corr;
+      o[4 * q + 2] = r * gm.z * u.z - a[4 * q + 2] * corr;
+      o[4 * q + 3] = r * gm.w * u.w - a[4 * q + 3] * corr;
+    }
+    dxr[c] = pack<BF16>(o);
   }
   if (lane == 0) rstd[t] = r;
 }
@@ -239,6 +387,7 @@ __global__ __launch_bounds__(256) void k_dgamma_part(const void* __restrict__ x,
   if (c >= d) return;
   const int t0 = blockIdx.y * rows_per, t1 = min(T, t0 + rows_per);
   float a = 0.f;
+#pragma unroll 8
   for (int t = t0; t < t1; ++t) a += dh[(size_t)t * d + c] * ld_act<BF16>(x, (size_t)t * d + c) * rstd[t];
   part[(size_t)blockIdx.y * d + c] = a;
 }
@@ -248,6 +397,7 @@ __global__ __launch_bounds__(256) void k_sum_slices(const float* __restrict__ pa
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= n) return;
   float a = 0.f;
+#pragma unroll 16
   for (int s = 0; s < S; ++s) a += part[(size_t)s * n + c];
   out[c] = a;
 }
@@ -264,6 +414,19 @@ hipError_t launch_transpose(const Dims& D, const void* src, int R, int C, long l
                             long long col_off, long long dst_bstride, int batch, hipStream_t s) {
   if (P <= 0 || C <= 0 || batch <= 0) return hipSuccess;
   dim3 grid((P + 63) / 64, (C + 63) / 64, batch);
+  const int V = D.bf16 ? 8 : 4;
+  const bool vec = C % 64 == 0 && P % 64 == 0 && ld_src % V == 0 && ld_dst % V == 0 && col_off % V == 0 &&
+                   src_bstride % V == 0 && dst_bstride % V == 0 && ((uintptr_t)src & 15) == 0 &&
+                   ((uintptr_t)dst & 15) == 0;
+  if (vec) {
+    if (D.bf16)
+      hipLaunchKernelGGL(k_transpose_b16, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), R, ld_src,
+                         src_bstride, gather, colmap, static_cast<uint16_t*>(dst), ld_dst, col_off, dst_bstride);
+    else
+      hipLaunchKernelGGL(k_transpose_b32, grid, dim3(256), 0, s, static_cast<const uint32_t*>(src), R, ld_src,
+                         src_bstride, gather, colmap, static_cast<uint32_t*>(dst), ld_dst, col_off, dst_bstride);
+    return hipGetLastError();
+  }
   if (D.bf16)
     hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), R, C, ld_src,
                        src_bstride, gather, colmap, P, static_cast<uint16_t*>(dst), ld_dst, col_off, dst_bstride);
@@ -282,7 +445,8 @@ hipError_t launch_pad_map(const Dims& D, const int32_t* offsets, int Kt, int32_t
 hipError_t launch_glu_bwd(const Dims& D, const void* P, const void* Q, const void* dG, long long R, int n, void* dP,
                           void* dQ, int ldo, hipStream_t s) {
   if (R == 0 || n == 0) return hipSuccess;
-  const unsigned g = blocks_for(R * n, 256 * 4);
+  if (n % 64 || ldo % 64) return hipErrorInvalidValue;
+  const unsigned g = blocks_for(R * n / (D.bf16 ? 8 : 4), 256 * 2);
   if (D.bf16) hipLaunchKernelGGL(k_glu_bwd<true>, dim3(g), dim3(256), 0, s, P, Q, dG, R, n, dP, dQ, ldo);
   else hipLaunchKernelGGL(k_glu_bwd<false>, dim3(g), dim3(256), 0, s, P, Q, dG, R, n, dP, dQ, ldo);
   return hipGetLastError();

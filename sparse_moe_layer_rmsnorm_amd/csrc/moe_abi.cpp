@@ -222,7 +222,7 @@ moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s) {
 // ----------------------------------------------------------------- backward --
 struct BwdLayout {
   size_t Bop1, Bop2, WdT, WguT, P, Q, dG, dy, dAcat, dg, dY, dH, Apre, U, dAU, dX, dh, rstd, gpart;
-  size_t doutT, GyT, dAcatT, hT, dYT, HT, dAUT, XT, dWcat, dWgu, koff, colmap, total;
+  size_t doutT, GyT, dAcatT, hT, dYT, HT, dAUT, XT, dWcat, koff, colmap, total;
   int Tp, Kt, Epad, Kc;
 };
 constexpr int kGammaSlices = 64;
@@ -270,7 +270,6 @@ void bwd_layout(const moe_config* c, int64_t T, BwdLayout* L) {
   L->dAUT = take(2 * f * Kt * es);
   L->XT = take(l * Kt * es);
   L->dWcat = take(Kc * d * 4);
-  L->dWgu = take(E * 2 * f * l * 4);
   L->koff = take((E + 1) * 4);
   L->colmap = take(Kt * 4);
   L->total = o;
@@ -456,7 +455,6 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   float* dg = static_cast<float*>(at(B.dg));
   float* dh = static_cast<float*>(at(B.dh));
   float* dWcat = static_cast<float*>(at(B.dWcat));
-  float* dWgu = static_cast<float*>(at(B.dWgu));
   int32_t* koff = static_cast<int32_t*>(at(B.koff));
   int32_t* colmap = static_cast<int32_t*>(at(B.colmap));
   auto el = [&](const void* base, size_t elems) { return static_cast<const char*>(base) + elems * es; };
@@ -562,15 +560,10 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
     return e;
   }());
   MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, dYT, Kt * es, HT, Kt * es, koff, l, f, g->W_d, s));
-  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, dAUT, Kt * es, XT, Kt * es, koff, 2 * f, l, dWgu, s));
-  return hip_ok([&]() -> hipError_t {
-    const size_t blk = (size_t)f * l * 4;
-    hipError_t e = hipMemcpy2DAsync(g->W_g, blk, dWgu, 2 * blk, blk, E, hipMemcpyDeviceToDevice, s);
-    if (e == hipSuccess)
-      e = hipMemcpy2DAsync(g->W_u, blk, reinterpret_cast<char*>(dWgu) + blk, 2 * blk, blk, E,
-                           hipMemcpyDeviceToDevice, s);
-    return e;
-  }(), "gradient copy");
+  // dW_g[e] = dA_e^T X_e and dW_u[e] = dU_e^T X_e: the two halves of dAU^T
+  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, dAUT, Kt * es, XT, Kt * es, koff, f, l, g->W_g, s));
+  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, el(dAUT, (size_t)f * Kt), Kt * es, XT, Kt * es, koff, f, l, g->W_u, s));
+  return MOE_OK;
 }
 
 moe_status moe_get_bias(moe_ctx* ctx, float* dst, void* stream) {
