@@ -97,12 +97,29 @@ MOE_DEV int src_row_of(int p, int R, const int32_t* __restrict__ gather, const i
   return (r >= 0 && r < R) ? (gather ? gather[r] : r) : -1;
 }
 
+// Segment mode (seg_tile non-NULL): the columns p form per-expert segments
+// seg_koff[e] .. seg_koff[e+1] (whole 64-column tiles, seg_tile[p / 64] = e,
+// -1 past the last); each expert's transposed block [C, pad_e] is stored
+// contiguously at seg_koff[e] * C, so that its rows are pad_e long.
+MOE_DEV bool seg_dst(const int32_t* __restrict__ seg_koff, const int32_t* __restrict__ seg_tile, int C, int p0,
+                     long long& base, long long& ld) {
+  const int e = seg_tile[p0 / 64];
+  if (e < 0) return false;
+  const int s0 = seg_koff[e];
+  ld = seg_koff[e + 1] - s0;
+  base = (long long)s0 * C - s0;  // + c * ld + p
+  return true;
+}
+
 __global__ __launch_bounds__(256) void k_transpose_b16(const uint16_t* __restrict__ src, int R, long long ld_src,
                                                        long long src_bstride, const int32_t* __restrict__ gather,
                                                        const int32_t* __restrict__ colmap, uint16_t* __restrict__ dst,
-                                                       long long ld_dst, long long col_off, long long dst_bstride) {
+                                                       long long ld_dst, long long col_off, long long dst_bstride,
+                                                       const int32_t* __restrict__ seg_koff,
+                                                       const int32_t* __restrict__ seg_tile) {
   __shared__ uint32_t tile[64][33];  // row p: 64 bf16 of c as 32 dwords
   const int p0 = blockIdx.x * 64, c0 = blockIdx.y * 64, t = threadIdx.x;
+  if (seg_tile && !seg_dst(seg_koff, seg_tile, gridDim.y * 64, p0, col_off, ld_dst)) return;
   src += (size_t)blockIdx.z * src_bstride;
   dst += (size_t)blockIdx.z * dst_bstride;
 #pragma unroll
@@ -132,9 +149,12 @@ __global__ __launch_bounds__(256) void k_transpose_b16(const uint16_t* __restric
 __global__ __launch_bounds__(256) void k_transpose_b32(const uint32_t* __restrict__ src, int R, long long ld_src,
                                                        long long src_bstride, const int32_t* __restrict__ gather,
                                                        const int32_t* __restrict__ colmap, uint32_t* __restrict__ dst,
-                                                       long long ld_dst, long long col_off, long long dst_bstride) {
+                                                       long long ld_dst, long long col_off, long long dst_bstride,
+                                                       const int32_t* __restrict__ seg_koff,
+                                                       const int32_t* __restrict__ seg_tile) {
   __shared__ uint32_t tile[64][65];
   const int p0 = blockIdx.x * 64, c0 = blockIdx.y * 64, t = threadIdx.x;
+  if (seg_tile && !seg_dst(seg_koff, seg_tile, gridDim.y * 64, p0, col_off, ld_dst)) return;
   src += (size_t)blockIdx.z * src_bstride;
   dst += (size_t)blockIdx.z * dst_bstride;
 #pragma unroll
@@ -163,7 +183,8 @@ __global__ __launch_bounds__(256) void k_transpose_b32(const uint32_t* __restric
 // -1, and -1 from koff[E] up to Kt (the host's bound on the total).  One
 // block of 1024 threads (E <= 1024).
 __global__ __launch_bounds__(1024) void k_pad_map(const int32_t* __restrict__ offsets, int E, int Kt,
-                                                  int32_t* __restrict__ koff, int32_t* __restrict__ colmap) {
+                                                  int32_t* __restrict__ koff, int32_t* __restrict__ colmap,
+                                                  int32_t* __restrict__ seg_tile) {
   __shared__ int wsum[16];
   __shared__ int base[1024];
   const int i = threadIdx.x, lane = i & 63, w = i >> 6;
@@ -186,9 +207,11 @@ __global__ __launch_bounds__(1024) void k_pad_map(const int32_t* __restrict__ of
     const int b = base[e], off = offsets[e], ne = offsets[e + 1] - off;
     const int pe = max(1, (ne + 63) / 64) * 64;
     for (int j = lane; j < pe; j += 64) colmap[b + j] = j < ne ? off + j : -1;
+    for (int j = lane; j < pe / 64; j += 64) seg_tile[b / 64 + j] = e;
   }
   const int tot = base[E - 1] + max(1, (offsets[E] - offsets[E - 1] + 63) / 64) * 64;
   for (int j = tot + i; j < Kt; j += 1024) colmap[j] = -1;
+  for (int j = tot / 64 + i; j < Kt / 64; j += 1024) seg_tile[j] = -1;
 }
 
 // ------------------------------------------------------------------ GLU ----
@@ -411,20 +434,24 @@ unsigned blocks_for(long long n, int per_block) {
 
 hipError_t launch_transpose(const Dims& D, const void* src, int R, int C, long long ld_src, long long src_bstride,
                             const int32_t* gather, const int32_t* colmap, int P, void* dst, long long ld_dst,
-                            long long col_off, long long dst_bstride, int batch, hipStream_t s) {
+                            long long col_off, long long dst_bstride, int batch, hipStream_t s,
+                            const int32_t* seg_koff, const int32_t* seg_tile) {
   if (P <= 0 || C <= 0 || batch <= 0) return hipSuccess;
   dim3 grid((P + 63) / 64, (C + 63) / 64, batch);
   const int V = D.bf16 ? 8 : 4;
   const bool vec = C % 64 == 0 && P % 64 == 0 && ld_src % V == 0 && ld_dst % V == 0 && col_off % V == 0 &&
                    src_bstride % V == 0 && dst_bstride % V == 0 && ((uintptr_t)src & 15) == 0 &&
                    ((uintptr_t)dst & 15) == 0;
+  if (seg_tile && !vec) return hipErrorInvalidValue;
   if (vec) {
     if (D.bf16)
       hipLaunchKernelGGL(k_transpose_b16, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), R, ld_src,
-                         src_bstride, gather, colmap, static_cast<uint16_t*>(dst), ld_dst, col_off, dst_bstride);
+                         src_bstride, gather, colmap, static_cast<uint16_t*>(dst), ld_dst, col_off, dst_bstride,
+                         seg_koff, seg_tile);
     else
       hipLaunchKernelGGL(k_transpose_b32, grid, dim3(256), 0, s, static_cast<const uint32_t*>(src), R, ld_src,
-                         src_bstride, gather, colmap, static_cast<uint32_t*>(dst), ld_dst, col_off, dst_bstride);
+                         src_bstride, gather, colmap, static_cast<uint32_t*>(dst), ld_dst, col_off, dst_bstride,
+                         seg_koff, seg_tile);
     return hipGetLastError();
   }
   if (D.bf16)
@@ -437,8 +464,8 @@ hipError_t launch_transpose(const Dims& D, const void* src, int R, int C, long l
 }
 
 hipError_t launch_pad_map(const Dims& D, const int32_t* offsets, int Kt, int32_t* koff, int32_t* colmap,
-                          hipStream_t s) {
-  hipLaunchKernelGGL(k_pad_map, dim3(1), dim3(1024), 0, s, offsets, D.E, Kt, koff, colmap);
+                          int32_t* seg_tile, hipStream_t s) {
+  hipLaunchKernelGGL(k_pad_map, dim3(1), dim3(1024), 0, s, offsets, D.E, Kt, koff, colmap, seg_tile);
   return hipGetLastError();
 }
 

@@ -293,9 +293,16 @@ struct Pipe {
           const f32x4_t v = acc[mi][ni];
           if constexpr (KIND == EPI_F32) {
             float* o = static_cast<float*>(out) + orow;
+            float w[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (c + r < N) o[c + r] = v[r] + (col_off ? col_off[c + r] : 0.f);
+            for (int r = 0; r < 4; ++r) w[r] = v[r] + (col_off && c + r < N ? col_off[c + r] : 0.f);
+            if (c + 3 < N && ((ldo | n0) & 3) == 0 && ((uintptr_t)out & 15) == 0) {  // one 16-byte store
+              *reinterpret_cast<float4*>(o + c) = make_float4(w[0], w[1], w[2], w[3]);
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (c + r < N) o[c + r] = w[r];
+            }
           } else {
             if (c < N) store4(out, orow + c, v[0], v[1], v[2], v[3]);
           }
@@ -636,16 +643,14 @@ __global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expe
 }
 
 // ------------------------------------------- per-expert weight gradients --
-// C_e = A_e B_e^T for every expert e, with the K range of each expert its
-// own: A [M, Ktot] and B [N, Ktot] hold the experts' rows side by side along
-// K in segments koff[e] .. koff[e+1] (elements, padded to whole stages and at
-// least one stage, pad columns zero).  C_e [M, N] fp32 at out + e*M*N.  Used
-// for dW = dY_e^T H_e style products, whose K is the expert's token count.
+// C_e = A_e B_e^T for every expert e, K = the expert's own (padded) token
+// count pad_e = koff[e+1] - koff[e] (whole stages, at least one, pad columns
+// zero): A_e [M, pad_e] is a contiguous block at element koff[e] * M of A,
+// B_e [N, pad_e] at koff[e] * N of B, so a tile's rows are short and close.
+// C_e [M, N] fp32 at out + e*M*N.  Used for dW = dY_e^T H_e style products.
 struct WgradArgs {
   const char* A;
-  int lda_bytes;
   const char* B;
-  int ldb_bytes;
   const int32_t* koff;
   int es;  // element bytes
   int M, N, MT, NT, E;
@@ -677,14 +682,15 @@ struct WgradProb {
     return (scalar_load(a.koff, t.sel + 1) - scalar_load(a.koff, t.sel)) * uniform_int(a.es) / Pp::RB;
   }
   MOE_DEV const char* row_ptr(const Tile& t, int row) const {
-    const size_t k0 = (size_t)scalar_load(a.koff, t.sel) * uniform_int(a.es);
+    const int s0 = scalar_load(a.koff, t.sel), pad = scalar_load(a.koff, t.sel + 1) - s0;
+    const size_t es = uniform_int(a.es);
     if (row < Pp::BM) {  // rows past M read the tile's first row (not stored)
       const int r = row < t.rows ? row : 0;
-      return uniform_ptr(a.A) + (size_t)(t.row0 + r) * uniform_int(a.lda_bytes) + k0;
+      return uniform_ptr(a.A) + ((size_t)s0 * uniform_int(a.M) + (size_t)(t.row0 + r) * pad) * es;
     }
     int n = t.nt * Pp::BN + (row - Pp::BM);
     if (n >= uniform_int(a.N)) n = 0;
-    return uniform_ptr(a.B) + (size_t)n * uniform_int(a.ldb_bytes) + k0;
+    return uniform_ptr(a.B) + ((size_t)s0 * uniform_int(a.N) + (size_t)n * pad) * es;
   }
   template <int L>
   MOE_DEV void sources(const Tile& t, SrcT<L>& src) const {
@@ -1028,15 +1034,12 @@ hipError_t launch_expert_nt(const Dims& D, const void* A, int lda_bytes, const i
   return launch_expert<EPI_STORE>(D, a, T, s);
 }
 
-hipError_t launch_wgrad(const Dims& D, const void* A, int lda_bytes, const void* B, int ldb_bytes,
-                        const int32_t* koff, int M, int N, float* out, hipStream_t s) {
+hipError_t launch_wgrad(const Dims& D, const void* A, const void* B, const int32_t* koff, int M, int N, float* out,
+                        hipStream_t s) {
   constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN;
-  if (lda_bytes % 16 || ldb_bytes % 16) return hipErrorInvalidValue;
   WgradArgs a{};
   a.A = static_cast<const char*>(A);
-  a.lda_bytes = lda_bytes;
   a.B = static_cast<const char*>(B);
-  a.ldb_bytes = ldb_bytes;
   a.koff = koff;
   a.es = esz(D);
   a.M = M;

@@ -96,20 +96,25 @@ hipError_t launch_dense_nt(const Dims& D, int tag, const void* A, int lda_bytes,
 hipError_t launch_expert_nt(const Dims& D, const void* A, int lda_bytes, const int32_t* gather, const void* W,
                             size_t w_expert_bytes, int ldb_bytes, int N, int K_bytes, const int2* tile_info,
                             const int32_t* n_mtiles, int T, void* out, int ldo, hipStream_t s);
-// Per-expert fp32 C_e [M, N] = A_e B_e^T with expert e's K range
-// koff[e] .. koff[e+1] (elements, padded segments of A [M, *] and B [N, *]).
-hipError_t launch_wgrad(const Dims& D, const void* A, int lda_bytes, const void* B, int ldb_bytes,
-                        const int32_t* koff, int M, int N, float* out, hipStream_t s);
+// Per-expert fp32 C_e [M, N] = A_e B_e^T, K = pad_e = koff[e+1] - koff[e]:
+// A_e is the block [M, pad_e] at element koff[e] * M of A, B_e [N, pad_e] at
+// koff[e] * N of B (the segment layout of launch_transpose).
+hipError_t launch_wgrad(const Dims& D, const void* A, const void* B, const int32_t* koff, int M, int N, float* out,
+                        hipStream_t s);
 
 // dst[c][col_off + p] = src[gather[colmap[p]]][c] (maps optional), 0 for
-// rows < 0 or >= R; `batch` matrices at the given strides (elements).
+// rows < 0 or >= R; `batch` matrices at the given strides (elements).  With
+// seg_tile, expert e's columns seg_koff[e] .. seg_koff[e+1] go to their own
+// contiguous block [C, pad_e] at element seg_koff[e] * C (ld_dst, col_off
+// unused; C and P multiples of 64).
 hipError_t launch_transpose(const Dims& D, const void* src, int R, int C, long long ld_src, long long src_bstride,
                             const int32_t* gather, const int32_t* colmap, int P, void* dst, long long ld_dst,
-                            long long col_off, long long dst_bstride, int batch, hipStream_t s);
+                            long long col_off, long long dst_bstride, int batch, hipStream_t s,
+                            const int32_t* seg_koff = nullptr, const int32_t* seg_tile = nullptr);
 // Padded per-expert K segments (whole 64-element stages, at least one) and
 // the map from padded column to grouped row (-1 = pad) up to Kt columns.
 hipError_t launch_pad_map(const Dims& D, const int32_t* offsets, int Kt, int32_t* koff, int32_t* colmap,
-                          hipStream_t s);
+                          int32_t* seg_tile, hipStream_t s);
 hipError_t launch_glu_bwd(const Dims& D, const void* P, const void* Q, const void* dG, long long R, int n, void* dP,
                           void* dQ, int ldo, hipStream_t s);
 hipError_t launch_combine_bwd(const Dims& D, const void* dy, const void* Y, const float* gates, const int32_t* inv,

@@ -222,7 +222,7 @@ moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s) {
 // ----------------------------------------------------------------- backward --
 struct BwdLayout {
   size_t Bop1, Bop2, WdT, WguT, P, Q, dG, dy, dAcat, dg, dY, dH, Apre, U, dAU, dX, dh, rstd, gpart;
-  size_t doutT, GyT, dAcatT, hT, dYT, HT, dAUT, XT, dWcat, koff, colmap, total;
+  size_t doutT, GyT, dAcatT, hT, dYT, HT, dAUT, XT, dWcat, koff, colmap, seg_tile, total;
   int Tp, Kt, Epad, Kc;
 };
 constexpr int kGammaSlices = 64;
@@ -272,6 +272,7 @@ void bwd_layout(const moe_config* c, int64_t T, BwdLayout* L) {
   L->dWcat = take(Kc * d * 4);
   L->koff = take((E + 1) * 4);
   L->colmap = take(Kt * 4);
+  L->seg_tile = take(Kt / 64 * 4);
   L->total = o;
 }
 
@@ -457,6 +458,7 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   float* dWcat = static_cast<float*>(at(B.dWcat));
   int32_t* koff = static_cast<int32_t*>(at(B.koff));
   int32_t* colmap = static_cast<int32_t*>(at(B.colmap));
+  int32_t* seg_tile = static_cast<int32_t*>(at(B.seg_tile));
   auto el = [&](const void* base, size_t elems) { return static_cast<const char*>(base) + elems * es; };
   auto elw = [&](void* base, size_t elems) { return static_cast<char*>(base) + elems * es; };
   const moe_weights& W = ctx->w;
@@ -552,17 +554,23 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   if (st != MOE_OK) return st;
   // per-expert weight gradients: K = the expert's rows, padded segments
   MOE_RUN(MOE_K_BWD_TRANSPOSE, [&]() -> hipError_t {
-    hipError_t e = launch_pad_map(D, p.offsets, Kt, koff, colmap, s);
-    if (e == hipSuccess) e = launch_transpose(D, dY, Tk, l, l, 0, nullptr, colmap, Kt, dYT, Kt, 0, 0, 1, s);
-    if (e == hipSuccess) e = launch_transpose(D, H, Tk, f, f, 0, nullptr, colmap, Kt, HT, Kt, 0, 0, 1, s);
-    if (e == hipSuccess) e = launch_transpose(D, dAU, Tk, 2 * f, 2 * f, 0, nullptr, colmap, Kt, dAUT, Kt, 0, 0, 1, s);
-    if (e == hipSuccess) e = launch_transpose(D, z, Tk, l, l, 0, p.perm_src, colmap, Kt, XT, Kt, 0, 0, 1, s);
+    // per-expert blocks: dY_e^T [l, pad_e], H_e^T [f, pad_e], dA_e^T, dU_e^T [f, pad_e], X_e^T [l, pad_e]
+    hipError_t e = launch_pad_map(D, p.offsets, Kt, koff, colmap, seg_tile, s);
+    if (e == hipSuccess) e = launch_transpose(D, dY, Tk, l, l, 0, nullptr, colmap, Kt, dYT, 0, 0, 0, 1, s, koff, seg_tile);
+    if (e == hipSuccess) e = launch_transpose(D, H, Tk, f, f, 0, nullptr, colmap, Kt, HT, 0, 0, 0, 1, s, koff, seg_tile);
+    if (e == hipSuccess)
+      e = launch_transpose(D, dAU, Tk, f, 2 * f, 0, nullptr, colmap, Kt, dAUT, 0, 0, 0, 1, s, koff, seg_tile);
+    if (e == hipSuccess)
+      e = launch_transpose(D, el(dAU, f), Tk, f, 2 * f, 0, nullptr, colmap, Kt, elw(dAUT, (size_t)f * Kt), 0, 0, 0,
+                           1, s, koff, seg_tile);
+    if (e == hipSuccess)
+      e = launch_transpose(D, z, Tk, l, l, 0, p.perm_src, colmap, Kt, XT, 0, 0, 0, 1, s, koff, seg_tile);
     return e;
   }());
-  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, dYT, Kt * es, HT, Kt * es, koff, l, f, g->W_d, s));
-  // dW_g[e] = dA_e^T X_e and dW_u[e] = dU_e^T X_e: the two halves of dAU^T
-  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, dAUT, Kt * es, XT, Kt * es, koff, f, l, g->W_g, s));
-  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, el(dAUT, (size_t)f * Kt), Kt * es, XT, Kt * es, koff, f, l, g->W_u, s));
+  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, dYT, HT, koff, l, f, g->W_d, s));
+  // dW_g[e] = dA_e^T X_e and dW_u[e] = dU_e^T X_e
+  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, dAUT, XT, koff, f, l, g->W_g, s));
+  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, el(dAUT, (size_t)f * Kt), XT, koff, f, l, g->W_u, s));
   return MOE_OK;
 }
 
