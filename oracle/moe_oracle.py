@@ -284,6 +284,56 @@ def exact_quantile(s_col: np.ndarray, N: int, k: int, E: int) -> float:
 # --------------------------------------------------------------------------
 
 
+# --------------------------------------------------------------------------
+# Low-precision experts (the "next" step of FP8 activations and weights):
+# OCP microscaling MXFP8 -- blocks of 32 consecutive elements along the
+# contraction axis share one power-of-two scale (E8M0 byte), each element is
+# an FP8 E4M3 value (bias 7, 3 mantissa bits, largest 448, no infinities).
+# --------------------------------------------------------------------------
+MX_BLOCK = 32
+E4M3_MAX = 448.0
+E4M3_EMAX = 8            # exponent of the largest E4M3 binade (448 = 1.75 * 2^8)
+
+
+def e4m3_round(v: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 value (ties to even), saturating at +-448 (fp64 out).
+
+    Normal binade 2^e (e >= -6) has step 2^(e-3); below 2^-6 the
+    subnormal step is 2^-9."""
+    v = np.asarray(v, dtype=np.float64)
+    _, E = np.frexp(v)                       # |v| = m 2^E, 0.5 <= m < 1, so e = E - 1
+    step = np.ldexp(1.0, np.maximum(E - 1, -6) - 3)
+    q = np.rint(v / step) * step
+    return np.clip(q, -E4M3_MAX, E4M3_MAX)
+
+
+def mx_scale_bytes(a: np.ndarray) -> np.ndarray:
+    """E8M0 scale byte of each block of 32 along the last axis:
+    2^(floor(log2 amax) - 8) stored as its biased exponent (bias 127),
+    clamped to [0, 254]; an all-zero block gets byte 0."""
+    a = np.asarray(a, dtype=np.float64)
+    blocks = a.reshape(a.shape[:-1] + (a.shape[-1] // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(blocks).max(axis=-1)
+    _, E = np.frexp(amax)
+    b = np.clip(E - 1 - E4M3_EMAX + 127, 0, 254)
+    return np.where(amax > 0, b, 0).astype(np.int64)
+
+
+def mx_quantize(a: np.ndarray):
+    """(elements as E4M3 values, scale bytes) of `a` in MXFP8 along the last
+    axis (its length a multiple of 32): element = e4m3_round(a / 2^(byte - 127))."""
+    a = np.asarray(a, dtype=np.float64)
+    sb = mx_scale_bytes(a)
+    scale = np.repeat(np.ldexp(1.0, sb - 127), MX_BLOCK, axis=-1)
+    return e4m3_round(a / scale), sb
+
+
+def mx_round(a: np.ndarray) -> np.ndarray:
+    """The value an MXFP8 round trip gives: element * scale (fp64)."""
+    q, sb = mx_quantize(a)
+    return q * np.repeat(np.ldexp(1.0, sb - 127), MX_BLOCK, axis=-1)
+
+
 def router_logits(h: np.ndarray, W_r: np.ndarray, c: Optional[np.ndarray] = None) -> np.ndarray:
     """l = h W_r^T (+ c) in fp64, stored as fp32 ([P4] Tab 1 routing branch)."""
     l = h @ np.asarray(W_r, np.float64).T
@@ -292,9 +342,17 @@ def router_logits(h: np.ndarray, W_r: np.ndarray, c: Optional[np.ndarray] = None
     return l.astype(F32)
 
 
-def expert_outputs(X: np.ndarray, offsets: np.ndarray, W: Dict[str, np.ndarray], dtype: str):
+def expert_outputs(X: np.ndarray, offsets: np.ndarray, W: Dict[str, np.ndarray], dtype: str,
+                   experts: str = "bf16"):
     """Per expert e on its rows X[off_e:off_e+1]: H = silu(X Wg^T) * (X Wu^T),
-    Y = H Wd^T  ([P1] capsule 20: three batched matmuls per expert group)."""
+    Y = H Wd^T  ([P1] capsule 20: three batched matmuls per expert group).
+
+    experts="mxfp8": both operands of each product are MXFP8 along their
+    contraction axis (X and W_g, W_u along l; H, stored first, and W_d along
+    f); the products and sums are exact (fp64) on the rounded values."""
+    mx = experts == "mxfp8"
+    if mx:
+        X = mx_round(X)
     E = len(offsets) - 1
     f = W["W_g"].shape[1]
     lat = W["W_d"].shape[1]
@@ -304,15 +362,19 @@ def expert_outputs(X: np.ndarray, offsets: np.ndarray, W: Dict[str, np.ndarray],
         a, b = int(offsets[e]), int(offsets[e + 1])
         if a == b:
             continue
-        He = _store(glu(X[a:b], W["W_g"][e], W["W_u"][e]), dtype)
+        Wg, Wu, Wd = W["W_g"][e], W["W_u"][e], W["W_d"][e]
+        if mx:
+            Wg, Wu, Wd = mx_round(Wg), mx_round(Wu), mx_round(Wd)
+        He = _store(glu(X[a:b], Wg, Wu), dtype)
         H[a:b] = He
-        Y[a:b] = _store(He @ np.asarray(W["W_d"][e], np.float64).T, dtype)
+        Y[a:b] = _store((mx_round(He) if mx else He) @ np.asarray(Wd, np.float64).T, dtype)
     return H, Y
 
 
 def forward(x: np.ndarray, W: Dict[str, np.ndarray], bias: np.ndarray, *, k: int, dtype: str,
             eps: float = 1e-6, B: int = 256, routed_scale: float = 1.0,
-            logits: Optional[np.ndarray] = None, with_hist: bool = True) -> Dict[str, np.ndarray]:
+            logits: Optional[np.ndarray] = None, with_hist: bool = True,
+            experts: str = "bf16") -> Dict[str, np.ndarray]:
     """One training (or frozen) forward of the layer on x[T,d].
 
     ``logits`` (fp32 [T,E]) replaces the router output when given, so that the
@@ -349,7 +411,7 @@ def forward(x: np.ndarray, W: Dict[str, np.ndarray], bias: np.ndarray, *, k: int
     z = _store(h @ np.asarray(W["W_dn"], np.float64).T, dtype)        # S11
     r["z"] = z
     X = z[perm_src]                                                    # S12
-    H, Y = expert_outputs(X, offsets, W, dtype)                        # S13-S14
+    H, Y = expert_outputs(X, offsets, W, dtype, experts)               # S13-S14
     r["H"], r["Y"] = H, Y
     y_lat = np.zeros((T, z.shape[1]), dtype=np.float64)                # S15
     for j in range(k):
@@ -363,7 +425,7 @@ def forward(x: np.ndarray, W: Dict[str, np.ndarray], bias: np.ndarray, *, k: int
 
 
 def forward_tokens(x_rows: np.ndarray, W: Dict[str, np.ndarray], idx_rows: np.ndarray,
-                   gates_rows: np.ndarray, *, dtype: str, eps: float = 1e-6) -> np.ndarray:
+                   gates_rows: np.ndarray, *, dtype: str, eps: float = 1e-6, experts: str = "bf16") -> np.ndarray:
     """Layer output for a few tokens given their routing (idx, gates).
 
     Every token is independent of the others once its routing is fixed, so
@@ -375,12 +437,17 @@ def forward_tokens(x_rows: np.ndarray, W: Dict[str, np.ndarray], idx_rows: np.nd
     h = _store(rmsnorm(x_rows, W["gamma"], eps), dtype)
     z = _store(h @ np.asarray(W["W_dn"], np.float64).T, dtype)
     out = np.zeros_like(x_rows)
+    mx = experts == "mxfp8"
     for t in range(x_rows.shape[0]):
         y_lat = np.zeros(z.shape[1])
+        zt = mx_round(z[t:t + 1]) if mx else z[t:t + 1]
         for j in range(idx_rows.shape[1]):
             e = int(idx_rows[t, j])
-            He = _store(glu(z[t:t + 1], W["W_g"][e], W["W_u"][e]), dtype)
-            Ye = _store(He @ np.asarray(W["W_d"][e], np.float64).T, dtype)
+            Wg, Wu, Wd = W["W_g"][e], W["W_u"][e], W["W_d"][e]
+            if mx:
+                Wg, Wu, Wd = mx_round(Wg), mx_round(Wu), mx_round(Wd)
+            He = _store(glu(zt, Wg, Wu), dtype)
+            Ye = _store((mx_round(He) if mx else He) @ np.asarray(Wd, np.float64).T, dtype)
             y_lat += float(gates_rows[t, j]) * Ye[0]
         y_lat = _store(y_lat, dtype)
         y_r = y_lat @ np.asarray(W["W_up"], np.float64).T
