@@ -59,6 +59,8 @@ def kernel_work(s, T: int) -> dict:
         "combine": 1.0 * Tk * s.l * es + 8.0 * Tk + 1.0 * T * s.l * es,
         "qb_quantile": 8.0 * 16 * s.E * s.B,
         "qb_bias": 20.0 * s.E,
+        # MXFP8 quantisation of z and H (one launch each): read bf16, write bytes + scales
+        "mx_quant": 0.5 * (2.0 + 1.0 + 1.0 / 32) * (T * s.l + Tk * s.f),
         "sign_bias": 16.0 * s.E,
     }
     return {"flops": flops, "bytes": bytes_}
@@ -133,6 +135,8 @@ def main() -> int:
     ap.add_argument("--no-profile", action="store_true", help="no per-kernel events in the timed region")
     ap.add_argument("--balancer", choices=("qb", "sign"), default="qb",
                     help="bias update rule of the step: quantile balancing (default) or the sign rule")
+    ap.add_argument("--experts", choices=("bf16", "mxfp8"), default="bf16",
+                    help="storage of the routed experts' operands (MXFP8: E4M3 + E8M0 block scales)")
     ap.add_argument("--backward", action="store_true",
                     help="time the training step with the backward pass: forward, moe_backward (dx and all weight "
                          "gradients) and the bias update")
@@ -159,7 +163,8 @@ def main() -> int:
     x_np = wl.make_x(shape)
     c = wl.zipf_logit_offset(shape) if shape.name == "skew" else None
     frozen = shape.qb_frozen
-    layer = layer_from_shape(shape, W, max_tokens=T, logit_offset=c, frozen=frozen, balancer=args.balancer)
+    layer = layer_from_shape(shape, W, max_tokens=T, logit_offset=c, frozen=frozen, balancer=args.balancer,
+                             experts=args.experts)
     if frozen:
         layer.set_bias(wl.frozen_bias(shape))
     x = torch.from_numpy(x_np).cuda().to(layer.tdtype)
@@ -295,7 +300,8 @@ def main() -> int:
             "; per-kernel table from a separate profiled pass of the same K steps",
         "config": {"workload": f"{shape.name}: T={T} tokens, d={shape.d}, l={shape.l}, E={shape.E}, k={shape.k}, "
                                f"f={shape.f}, f_s={shape.f_s}, B={shape.B}, QB {'frozen' if frozen else 'train'}"
-                               + (", sign-rule balancer" if args.balancer == "sign" else ""),
+                               + (", sign-rule balancer" if args.balancer == "sign" else "")
+                               + (", MXFP8 experts" if args.experts == "mxfp8" else ""),
                    "global_batch": T,
                    "step": "training forward + backward + qb_update" if args.backward else
                            "training forward + qb_update"},

@@ -84,6 +84,19 @@ typedef enum moe_qb_mode { MOE_QB_TRAIN = 0, MOE_QB_FROZEN = 1 } moe_qb_mode;
 typedef enum moe_balancer { MOE_BALANCE_QB = 0, MOE_BALANCE_SIGN = 1 } moe_balancer;
 
 /*
+ * Storage of the routed experts' operands.  MOE_EXPERTS_BF16: as the rest of
+ * the layer.  MOE_EXPERTS_MXFP8 (low-precision experts, bf16 mode only; l
+ * and f multiples of 128, at most 512): W_g, W_u, W_d are held in the state
+ * buffer as OCP MXFP8 -- FP8 E4M3 elements with one power-of-two E8M0 scale
+ * per 32 consecutive elements along the contraction axis -- quantised at
+ * moe_init (again by moe_requantize_experts after the caller changes them);
+ * each forward quantises z and the expert hidden H the same way, and the
+ * expert GEMMs multiply on the MFMA's block-scaled FP8 path with fp32 sums.
+ * The backward pass needs MOE_EXPERTS_BF16.
+ */
+typedef enum moe_expert_format { MOE_EXPERTS_BF16 = 0, MOE_EXPERTS_MXFP8 = 1 } moe_expert_format;
+
+/*
  * Layer sizes.  d, l, f must be multiples of 64 and f_s a multiple of 64 or 0
  * (0 = no shared expert; several shared experts of hidden f are one of hidden
  * n*f).  1 <= E <= 1024, 1 <= k <= min(E, 32), 2 <= qb_bins <= 256.
@@ -102,6 +115,7 @@ typedef struct moe_config {
   float routed_scale;
   moe_balancer balancer;
   float sign_gamma;
+  moe_expert_format experts;
 } moe_config;
 
 /* Device pointers, caller-owned, read-only to the library. */
@@ -144,6 +158,8 @@ typedef struct moe_state_layout {
   size_t hist_slices;
   size_t load;  /* [E] uint32 tokens routed to each expert since the last
                    update (sign-rule balancer only)                       */
+  size_t mx;    /* MXFP8 experts only: W_g, W_u [E,f,l] and W_d [E,l,f] as
+                   E4M3 bytes, then their E8M0 scales [.., K/32]          */
   size_t total;
 } moe_state_layout;
 
@@ -152,6 +168,9 @@ typedef struct moe_ws_layout {
   size_t h, logits, idx, gates, bitmap, cbase, sbase, counts, offsets, tile_offsets, perm_src, inv, tile_info;
   size_t G, z, X, H, Y, y_lat; /* X: zero bytes (the expert GEMM reads z[perm_src[r]]
                                   directly, so no dispatch buffer is written) */
+  size_t z8, zs, Xs, H8, Hs;    /* MXFP8 experts only (else zero bytes): z and H as
+                                  E4M3 bytes and E8M0 scales; Xs the scale rows of
+                                  the grouped rows */
   size_t total;
 } moe_ws_layout;
 
@@ -244,6 +263,9 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
                         const void* fwd_ws, size_t fwd_ws_bytes, void* dx, const moe_grads* g, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* MXFP8 experts: quantise the caller's W_g, W_u, W_d again (after an update). */
+moe_status moe_requantize_experts(moe_ctx* ctx, void* stream);
+
 /* Copy the current bias (E fp32) to / from device memory on `stream`. */
 moe_status moe_get_bias(moe_ctx* ctx, float* dst, void* stream);
 moe_status moe_set_bias(moe_ctx* ctx, const float* src, void* stream);
@@ -272,7 +294,9 @@ enum {
   MOE_K_QB_BIAS, MOE_K_GEMM_RZ, MOE_K_SIGN_BIAS,
   /* backward: dense products, grouped expert products, per-expert weight
      gradients, elementwise transposes and derivatives, operand transposes */
-  MOE_K_BWD_GEMM, MOE_K_BWD_EXPERT, MOE_K_BWD_WGRAD, MOE_K_BWD_ELTWISE, MOE_K_BWD_TRANSPOSE, MOE_NUM_KERNELS
+  MOE_K_BWD_GEMM, MOE_K_BWD_EXPERT, MOE_K_BWD_WGRAD, MOE_K_BWD_ELTWISE, MOE_K_BWD_TRANSPOSE,
+  MOE_K_MX_QUANT, /* MXFP8 quantisation of z and H */
+  MOE_NUM_KERNELS
 };
 const char* moe_kernel_name(int id);
 moe_status moe_profile_begin(moe_ctx* ctx, int max_launches, uint32_t mask);

@@ -20,16 +20,18 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MO
 MOE_F32, MOE_BF16 = 0, 1
 MOE_QB_TRAIN, MOE_QB_FROZEN = 0, 1
 MOE_BALANCE_QB, MOE_BALANCE_SIGN = 0, 1
+MOE_EXPERTS_BF16, MOE_EXPERTS_MXFP8 = 0, 1
 KERNELS = ["rmsnorm", "gemm_h", "topk", "hist", "scan", "scatter", "expert_up", "expert_down", "combine",
            "gemm_out", "qb_quantile", "qb_bias", "gemm_rz", "sign_bias", "bwd_gemm", "bwd_expert", "bwd_wgrad",
-           "bwd_eltwise", "bwd_transpose"]
+           "bwd_eltwise", "bwd_transpose", "mx_quant"]
 MOE_NUM_KERNELS = len(KERNELS)
 
 
 class moe_config(ctypes.Structure):
     _fields_ = [("d", c_int32), ("l", c_int32), ("E", c_int32), ("k", c_int32), ("f", c_int32), ("f_s", c_int32),
                 ("dtype", c_int), ("rms_eps", c_float), ("qb_bins", c_int32), ("qb_mode", c_int),
-                ("max_tokens", c_int64), ("routed_scale", c_float), ("balancer", c_int), ("sign_gamma", c_float)]
+                ("max_tokens", c_int64), ("routed_scale", c_float), ("balancer", c_int), ("sign_gamma", c_float),
+                ("experts", c_int)]
 
 
 class moe_weights(ctypes.Structure):
@@ -46,13 +48,13 @@ class moe_grads(ctypes.Structure):
 
 
 class moe_state_layout(ctypes.Structure):
-    _fields_ = [(n, c_size_t) for n in ("bias", "count", "q", "hist", "hist_slices", "load", "total")]
+    _fields_ = [(n, c_size_t) for n in ("bias", "count", "q", "hist", "hist_slices", "load", "mx", "total")]
 
 
 class moe_ws_layout(ctypes.Structure):
     _fields_ = [(n, c_size_t) for n in ("h", "logits", "idx", "gates", "bitmap", "cbase", "sbase", "counts",
                                         "offsets", "tile_offsets", "perm_src", "inv", "tile_info", "G", "z", "X",
-                                        "H", "Y", "y_lat", "total")]
+                                        "H", "Y", "y_lat", "z8", "zs", "Xs", "H8", "Hs", "total")]
 
 
 _lib = None
@@ -81,6 +83,7 @@ def lib() -> ctypes.CDLL:
             "moe_backward": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, POINTER(moe_route_out), c_void_p,
                                      c_size_t, c_void_p, POINTER(moe_grads), c_void_p, c_size_t, c_void_p]),
             "qb_update": (c_int, [c_void_p, c_void_p]),
+            "moe_requantize_experts": (c_int, [c_void_p, c_void_p]),
             "moe_get_bias": (c_int, [c_void_p, c_void_p, c_void_p]),
             "moe_set_bias": (c_int, [c_void_p, c_void_p, c_void_p]),
             "moe_set_qb_mode": (c_int, [c_void_p, c_int]),
@@ -171,6 +174,10 @@ def moe_backward(ctx: int, x: int, dout: int, T: int, r: Optional[moe_route_out]
                              ctypes.byref(g), ws, ws_bytes, stream), "moe_backward")
 
 
+def moe_requantize_experts(ctx: int, stream: int) -> None:
+    check(lib().moe_requantize_experts(ctx, stream), "moe_requantize_experts")
+
+
 def qb_update(ctx: int, stream: int) -> None:
     check(lib().qb_update(ctx, stream), "qb_update")
 
@@ -207,8 +214,9 @@ def moe_profile_end(ctx: int) -> Dict[str, tuple]:
 
 def make_config(d: int, l: int, E: int, k: int, f: int, f_s: int, *, dtype: str = "bf16", rms_eps: float = 1e-6,
                 qb_bins: int = 256, frozen: bool = False, max_tokens: int = 1, routed_scale: float = 1.0,
-                balancer: str = "qb", sign_gamma: float = 1e-2) -> moe_config:
+                balancer: str = "qb", sign_gamma: float = 1e-2, experts: str = "bf16") -> moe_config:
     return moe_config(d=d, l=l, E=E, k=k, f=f, f_s=f_s, dtype=MOE_BF16 if dtype == "bf16" else MOE_F32,
                       rms_eps=rms_eps, qb_bins=qb_bins, qb_mode=MOE_QB_FROZEN if frozen else MOE_QB_TRAIN,
                       max_tokens=max_tokens, routed_scale=routed_scale,
-                      balancer=MOE_BALANCE_SIGN if balancer == "sign" else MOE_BALANCE_QB, sign_gamma=sign_gamma)
+                      balancer=MOE_BALANCE_SIGN if balancer == "sign" else MOE_BALANCE_QB, sign_gamma=sign_gamma,
+                      experts=MOE_EXPERTS_MXFP8 if experts == "mxfp8" else MOE_EXPERTS_BF16)

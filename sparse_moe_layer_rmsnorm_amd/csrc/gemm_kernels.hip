@@ -537,6 +537,12 @@ struct ExpertArgs {
   const char* A;  // z (up, gathered) or H (down, rows grouped by expert)
   int lda_bytes;
   const int32_t* gather;  // A row of grouped row r is gather[r] (NULL: r itself)
+  // MXFP8 operands only: E8M0 scale rows (one byte per 32 elements of K)
+  const uint8_t* sA;   // of A rows, by grouped row (already gathered)
+  const uint8_t* sW;   // of W rows (gate rows for a GLU)
+  const uint8_t* sWu;  // of up rows for a GLU
+  int s_ld;            // scale bytes per row = K / 32
+  int w_rows;          // weight rows per expert
   const char* W;   // W_g (up) or W_d (down), [E, N, K]
   const char* Wu;  // W_u (up) or nullptr
   int ldb_bytes;
@@ -776,6 +782,213 @@ __global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_wgra
   __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
   WgradProb<Pp> prob{args};
   stream_var<Pp>(prob, smem);
+}
+
+// ------------------------------------------------ MXFP8 expert GEMMs --
+// Operands are FP8 E4M3 bytes with one E8M0 scale per 32 elements along K
+// (OCP microscaling); one v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 block
+// and 128-byte stage.  Its operand layout (measured on gfx950): lane (i, g =
+// lane / 16) holds K bytes [16g, 16g+16) and [64+16g, 64+16g+16) of row i of
+// the window, i.e. logical 16-byte chunks g and 4+g of the LDS row; the scale
+// it supplies (byte 0 of the operand) is that of row i's block g of 32.  The
+// DMA ring, LDS layout and epilogues are those of the bf16 expert GEMM.
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+template <class Pp>
+MOE_DEV void mx_compute(const char* cur, typename Pp::Acc& acc, const uint32_t (&sa)[Pp::MI][4],
+                        const uint32_t (&sb)[Pp::NI][4], int s) {
+  const int lane = threadIdx.x & 63, wave = Pp::wave_id();
+  const int wm = wave / Pp::WN, wn = wave % Pp::WN, g = lane >> 4;
+  v8i_t af[Pp::MI], wf[Pp::NI];
+#pragma unroll
+  for (int ni = 0; ni < Pp::NI; ++ni) {
+    const int row = Pp::BM + wn * Pp::WTN + ni * 16 + (lane & 15);
+    const uint4 lo = *reinterpret_cast<const uint4*>(cur + Pp::lds_off(row, g));
+    const uint4 hi = *reinterpret_cast<const uint4*>(cur + Pp::lds_off(row, 4 + g));
+    wf[ni] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+#pragma unroll
+  for (int mi = 0; mi < Pp::MI; ++mi) {
+    const int row = wm * Pp::WTM + mi * 16 + (lane & 15);
+    const uint4 lo = *reinterpret_cast<const uint4*>(cur + Pp::lds_off(row, g));
+    const uint4 hi = *reinterpret_cast<const uint4*>(cur + Pp::lds_off(row, 4 + g));
+    af[mi] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  const int sh = 8 * g;
+  auto pick = [&](const uint32_t (&w)[4]) -> int {
+    const uint32_t v = s == 0 ? w[0] : (s == 1 ? w[1] : (s == 2 ? w[2] : w[3]));
+    return (int)((v >> sh) & 0xFFu);
+  };
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int mi = 0; mi < Pp::MI; ++mi) {
+    const int sA = pick(sa[mi]);
+#pragma unroll
+    for (int ni = 0; ni < Pp::NI; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[ni], af[mi], acc[mi][ni], 0, 0, 0, pick(sb[ni]),
+                                                                     0, sA);
+  }
+}
+
+template <class Pp, int KIND>
+struct ExpertMxProb : ExpertProb<Pp, KIND> {
+  using ExpertProb<Pp, KIND>::a;
+  // The scale words (4 bytes = the 4 blocks of one 128-byte stage; K <= 512)
+  // of the lane's A rows and weight rows for tile t.  Vector loads: the
+  // caller consumes them before its next DMA issue.
+  MOE_DEV void load_scales(const Tile& t, uint32_t (&sa)[Pp::MI][4], uint32_t (&sb)[Pp::NI][4]) const {
+    const int lane = threadIdx.x & 63, wave = Pp::wave_id();
+    const int wm = wave / Pp::WN, wn = wave % Pp::WN;
+    const int sld = uniform_int(a.s_ld), nd = sld / 4;
+#pragma unroll
+    for (int mi = 0; mi < Pp::MI; ++mi) {
+      const int lr = wm * Pp::WTM + mi * 16 + (lane & 15);
+      const int gr = t.row0 + (lr < t.rows ? lr : 0);
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(a.sA + (size_t)gr * sld);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sa[mi][q] = q < nd ? p[q] : 0u;
+    }
+#pragma unroll
+    for (int ni = 0; ni < Pp::NI; ++ni) {
+      const int c = wn * Pp::WTN + ni * 16 + (lane & 15);
+      int wrow;
+      const uint8_t* base;
+      if (KIND == EPI_GLU) {
+        wrow = t.nt * (Pp::BN / 2) + (c >> 5) * 16 + (c & 15);
+        base = (c & 31) >= 16 ? a.sWu : a.sW;
+      } else {
+        wrow = t.nt * Pp::BN + c;
+        base = a.sW;
+      }
+      if (wrow >= a.N) wrow = 0;
+      const uint32_t* p =
+          reinterpret_cast<const uint32_t*>(base + ((size_t)t.sel * a.w_rows + wrow) * (size_t)sld);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sb[ni][q] = q < nd ? p[q] : 0u;
+    }
+  }
+};
+
+template <class Pp, int KIND>
+__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expert_mx(const ExpertArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
+  ExpertMxProb<Pp, KIND> prob{args};
+  const int G = gridDim.x, b = blockIdx.x;
+  const int x = b & 7, q = b >> 3, Gx = G >> 3;
+  const int total_tiles = prob.total();
+  const int per = (total_tiles + 7) >> 3;
+  const int lo = x * per, hi = min(total_tiles, lo + per);
+  const int span = hi - lo - q;
+  const int my_n = span > 0 ? (span + Gx - 1) / Gx : 0;
+  if (my_n <= 0) return;
+  const int KT = prob.kt();
+  const int total = my_n * KT;
+  const uint32_t lds0 = lds_addr(smem) + Pp::wave_id() * 1024;
+  typename ExpertMxProb<Pp, KIND>::template SrcT<Pp::L> src;
+  int iss_j = 0, iss_ks = 0, issued = 0;
+  prob.sources(prob.tile(lo + q), src);
+  auto issue = [&]() {
+    const uint32_t base = lds0 + (uint32_t)((issued % Pp::NS) * Pp::STAGE);
+    prob.issue(src, iss_ks, base);
+    ++issued;
+    if (++iss_ks == KT) {
+      iss_ks = 0;
+      if (++iss_j < my_n) prob.sources(prob.tile(lo + q + iss_j * Gx), src);
+    }
+  };
+  uint32_t sa[Pp::MI][4], sb[Pp::NI][4];
+  Tile ct = prob.tile(lo + q);
+  prob.load_scales(ct, sa, sb);
+  for (int s0 = 0; s0 < Pp::NS - 1; ++s0)
+    if (issued < total) issue();
+  typename Pp::Acc acc;
+  Pp::zero(acc);
+  int cj = 0, cks = 0;
+  for (int g = 0; g < total; ++g) {
+    Pp::wait_stage(issued - g - 1);
+    block_barrier();
+    // use the scale words here: the compiler's wait for their loads then
+    // comes before the next DMA issue instead of draining it
+#pragma unroll
+    for (int i = 0; i < Pp::MI; ++i) asm volatile("" ::"v"(sa[i][0]), "v"(sa[i][1]), "v"(sa[i][2]), "v"(sa[i][3]));
+#pragma unroll
+    for (int i = 0; i < Pp::NI; ++i) asm volatile("" ::"v"(sb[i][0]), "v"(sb[i][1]), "v"(sb[i][2]), "v"(sb[i][3]));
+    if (issued < total) issue();
+    mx_compute<Pp>(smem + (g % Pp::NS) * Pp::STAGE, acc, sa, sb, cks);
+    if (++cks == KT) {
+      prob.epilogue(ct, acc);
+      Pp::zero(acc);
+      cks = 0;
+      if (++cj < my_n) {
+        ct = prob.tile(lo + q + cj * Gx);
+        prob.load_scales(ct, sa, sb);
+      }
+    }
+  }
+}
+
+// MXFP8 quantisation of rows: each block of 32 consecutive elements gets the
+// scale 2^(floor(log2 amax) - 8) (E8M0 byte, clamped to [0, 254], 0 for an
+// all-zero block) and E4M3 elements, round to nearest even, saturating at 448.
+MOE_DEV uint32_t f32_to_e4m3(float v) {
+  const uint32_t sgn = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (!(a < 464.0f)) return sgn | 0x7Eu;
+  if (a < 0x1p-6f) return sgn | (uint32_t)__builtin_rintf(a * 512.0f);  // subnormal step 2^-9 (8 -> 2^-6)
+  int e;
+  (void)frexpf(a, &e);
+  const int E = e - 1;
+  const float m = ldexpf(a, -E);
+  uint32_t mq = (uint32_t)__builtin_rintf((m - 1.0f) * 8.0f);
+  int eb = E + 7;
+  if (mq == 8u) {
+    mq = 0u;
+    ++eb;
+  }
+  return sgn | ((uint32_t)eb << 3) | mq;
+}
+
+__global__ __launch_bounds__(256) void k_mx_quant(const uint16_t* __restrict__ src, long long rows, int K,
+                                                  long long ld_src, uint8_t* __restrict__ dst,
+                                                  uint8_t* __restrict__ scales) {
+  const int nb = K / 32;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * nb) return;
+  const long long r = i / nb;
+  const int bk = (int)(i - r * nb);
+  const uint4* p = reinterpret_cast<const uint4*>(src + r * ld_src + (long long)bk * 32);
+  float v[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 w = p[q];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      v[8 * q + 2 * h] = bf16_bits_to_f32(ww[h] & 0xFFFFu);
+      v[8 * q + 2 * h + 1] = bf16_bits_to_f32(ww[h] >> 16);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  int byte = 0;
+  if (amax > 0.f) {
+    int e;
+    (void)frexpf(amax, &e);
+    byte = min(254, max(0, e - 1 - 8 + 127));
+  }
+  uint32_t o[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x |= f32_to_e4m3(ldexpf(v[4 * w + j], 127 - byte)) << (8 * j);
+    o[w] = x;
+  }
+  uint4* d = reinterpret_cast<uint4*>(dst + r * K + (long long)bk * 32);
+  d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  scales[r * nb + bk] = (uint8_t)byte;
 }
 
 // Tile shapes and pipeline depths: BM, BN, WM, WN, NS, RB, BPC.
@@ -1057,6 +1270,82 @@ hipError_t launch_wgrad(const Dims& D, const void* A, const void* B, const int32
     hipLaunchKernelGGL(k_gemm_wgrad<DensePipe<false>>, dim3(persistent_grid(tiles, DensePipe<false>::BPC)),
                        dim3(DensePipe<false>::THREADS), 0, s, a);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------- MXFP8 --
+hipError_t launch_mx_quant(const void* src, long long rows, int K, long long ld_src, uint8_t* dst, uint8_t* scales,
+                           hipStream_t s) {
+  if (K % 32 || ld_src % 8) return hipErrorInvalidValue;
+  const long long n = rows * (K / 32);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_mx_quant, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(src), rows, K, ld_src, dst, scales);
+  return hipGetLastError();
+}
+
+template <int KIND>
+static hipError_t launch_expert_mx(const Dims& D, const ExpertArgs& a, int T, hipStream_t s) {
+  using P = ExpertPipe<true>;
+  const long long tiles = (long long)expert_max_mtiles(T, D.k, D.E) * a.NT;
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm_expert_mx<P, KIND>), dim3(persistent_grid(tiles, P::BPC)), dim3(P::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_up_mx(const Dims& D, const uint8_t* z8, const uint8_t* Xs, const int32_t* perm_src,
+                               const int2* tile_info, const int32_t* n_mtiles, int T, const uint8_t* Wg8,
+                               const uint8_t* Wgs, const uint8_t* Wu8, const uint8_t* Wus, void* H, hipStream_t s) {
+  constexpr int BN = ExpertPipe<true>::BN, RB = ExpertPipe<true>::RB;
+  if (D.l % RB || D.l > 4 * RB) return hipErrorInvalidValue;
+  ExpertArgs a{};
+  a.A = reinterpret_cast<const char*>(z8);
+  a.lda_bytes = D.l;
+  a.gather = perm_src;
+  a.W = reinterpret_cast<const char*>(Wg8);
+  a.Wu = reinterpret_cast<const char*>(Wu8);
+  a.ldb_bytes = D.l;
+  a.w_expert_bytes = (size_t)D.f * D.l;
+  a.N = D.f;
+  a.NT = (2 * D.f + BN - 1) / BN;
+  a.kt = D.l / RB;
+  a.tile_info = tile_info;
+  a.n_mtiles = n_mtiles;
+  a.out = H;
+  a.ldo = D.f;
+  a.sA = Xs;
+  a.sW = Wgs;
+  a.sWu = Wus;
+  a.s_ld = D.l / 32;
+  a.w_rows = D.f;
+  return launch_expert_mx<EPI_GLU>(D, a, T, s);
+}
+
+hipError_t launch_expert_down_mx(const Dims& D, const uint8_t* H8, const uint8_t* Hs, const int2* tile_info,
+                                 const int32_t* n_mtiles, int T, const uint8_t* Wd8, const uint8_t* Wds, void* Y,
+                                 hipStream_t s) {
+  constexpr int BN = ExpertPipe<true>::BN, RB = ExpertPipe<true>::RB;
+  if (D.f % RB || D.f > 4 * RB) return hipErrorInvalidValue;
+  ExpertArgs a{};
+  a.A = reinterpret_cast<const char*>(H8);
+  a.lda_bytes = D.f;
+  a.gather = nullptr;
+  a.W = reinterpret_cast<const char*>(Wd8);
+  a.Wu = nullptr;
+  a.ldb_bytes = D.f;
+  a.w_expert_bytes = (size_t)D.l * D.f;
+  a.N = D.l;
+  a.NT = (D.l + BN - 1) / BN;
+  a.kt = D.f / RB;
+  a.tile_info = tile_info;
+  a.n_mtiles = n_mtiles;
+  a.out = Y;
+  a.ldo = D.l;
+  a.sA = Hs;
+  a.sW = Wds;
+  a.sWu = nullptr;
+  a.s_ld = D.f / 32;
+  a.w_rows = D.l;
+  return launch_expert_mx<EPI_STORE>(D, a, T, s);
 }
 
 }  // namespace moe

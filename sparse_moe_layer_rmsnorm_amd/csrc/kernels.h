@@ -40,8 +40,11 @@ hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cb
                        int32_t* offsets, int32_t* tile_offsets, int2* tile_info, uint32_t* load,
                        unsigned long long* count, hipStream_t s);
 // Rows of the permutation, and the dispatch buffer X[row] = z[token].
+// With zs non-NULL (MXFP8 experts) also copies each token's z scale row
+// (s_ld bytes, a multiple of 4) to Xs at each of its grouped rows.
 hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* cbase,
-                          const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s);
+                          const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s,
+                          const uint8_t* zs = nullptr, uint8_t* Xs = nullptr, int s_ld = 0);
 hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, const int32_t* inv, int T,
                           void* y_lat, hipStream_t s);
 hipError_t launch_qb_quantile(const Dims& D, uint32_t* hist, const unsigned long long* count, double* q,
@@ -125,5 +128,21 @@ hipError_t launch_gates_bwd(const Dims& D, const float* logits, const int32_t* i
                             void* dl, int ldo, hipStream_t s);
 hipError_t launch_rmsnorm_bwd(const Dims& D, const void* x, const float* gamma, const float* dh, int T, void* dx,
                               float* rstd, float* part, int slices, float* dgamma, hipStream_t s);
+
+// ------------------------------------------------------------------ MXFP8 --
+// rows x K bf16 (ld_src elements) -> E4M3 bytes [rows, K] + E8M0 scales
+// [rows, K/32] (one per 32 consecutive elements).
+hipError_t launch_mx_quant(const void* src, long long rows, int K, long long ld_src, uint8_t* dst, uint8_t* scales,
+                           hipStream_t s);
+// Expert GEMM 1 + GLU with MXFP8 operands (A rows z8[perm_src[r]] with the
+// scale rows Xs[r] the scatter copied; K = l <= 512, a multiple of 128); H
+// in bf16.
+hipError_t launch_expert_up_mx(const Dims& D, const uint8_t* z8, const uint8_t* Xs, const int32_t* perm_src,
+                               const int2* tile_info, const int32_t* n_mtiles, int T, const uint8_t* Wg8,
+                               const uint8_t* Wgs, const uint8_t* Wu8, const uint8_t* Wus, void* H, hipStream_t s);
+// Expert GEMM 2 with MXFP8 operands (K = f <= 512, a multiple of 128); Y in bf16.
+hipError_t launch_expert_down_mx(const Dims& D, const uint8_t* H8, const uint8_t* Hs, const int2* tile_info,
+                                 const int32_t* n_mtiles, int T, const uint8_t* Wd8, const uint8_t* Wds, void* Y,
+                                 hipStream_t s);
 
 }  // namespace moe

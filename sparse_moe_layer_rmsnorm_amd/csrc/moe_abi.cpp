@@ -40,6 +40,13 @@ moe_status check_config(const moe_config* c) {
     return fail(MOE_ERR_INVALID_ARG, "unknown balancer %d", (int)c->balancer);
   if (c->balancer == MOE_BALANCE_SIGN && !(c->sign_gamma > 0.f && std::isfinite(c->sign_gamma)))
     return fail(MOE_ERR_INVALID_ARG, "sign_gamma must be finite and > 0");
+  if (c->experts != MOE_EXPERTS_BF16 && c->experts != MOE_EXPERTS_MXFP8)
+    return fail(MOE_ERR_INVALID_ARG, "unknown expert format %d", (int)c->experts);
+  if (c->experts == MOE_EXPERTS_MXFP8) {
+    if (c->dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "MXFP8 experts need the bf16 mode");
+    if (c->l % 128 || c->f % 128 || c->l > 512 || c->f > 512)
+      return fail(MOE_ERR_SHAPE, "MXFP8 experts need l and f multiples of 128, at most 512 (l=%d f=%d)", c->l, c->f);
+  }
   auto m64 = [](int32_t v) { return v > 0 && v % 64 == 0; };
   if (!m64(c->d) || !m64(c->l) || !m64(c->f))
     return fail(MOE_ERR_SHAPE, "d, l, f must be positive multiples of 64 (d=%d l=%d f=%d)", c->d, c->l, c->f);
@@ -84,6 +91,11 @@ void state_layout(const moe_config* c, moe_state_layout* L) {
   o = up(o + (size_t)kHistSlices * c->E * c->qb_bins * 4);
   L->load = o;
   o = up(o + (size_t)c->E * 4);
+  L->mx = o;
+  if (c->experts == MOE_EXPERTS_MXFP8) {
+    const size_t w = (size_t)c->E * c->f * c->l;  // elements of each expert weight tensor
+    o = up(o + 3 * w + 3 * (w / 32));
+  }
   L->total = o;
 }
 
@@ -117,6 +129,12 @@ void ws_layout(const moe_config* c, int64_t T, moe_ws_layout* L) {
   L->H = take(t * k * c->f * es);
   L->Y = take(t * k * c->l * es);
   L->y_lat = take(t * c->l * es);
+  const bool mx = c->experts == MOE_EXPERTS_MXFP8;
+  L->z8 = take(mx ? t * c->l : 0);
+  L->zs = take(mx ? t * c->l / 32 : 0);
+  L->Xs = take(mx ? t * k * c->l / 32 : 0);
+  L->H8 = take(mx ? t * k * c->f : 0);
+  L->Hs = take(mx ? t * k * c->f / 32 : 0);
   L->total = o;
 }
 
@@ -202,7 +220,8 @@ moe_status check_call(moe_ctx* ctx, int64_t T, void* ws, size_t ws_bytes) {
 
 // Steps after the logits: scores, QB histogram, top-k + gates + selection
 // masks, two-level prefix sums with offsets, stable rows (perm_src, inv).
-moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s) {
+moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s, const uint8_t* zs = nullptr,
+                      uint8_t* Xs = nullptr) {
   const Dims& D = ctx->D;
   const float* bias = reinterpret_cast<const float*>(ctx->state + ctx->sl.bias);
   const bool train = ctx->cfg.qb_mode == MOE_QB_TRAIN;
@@ -215,7 +234,7 @@ moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s) {
   if (train) ctx->pending_tokens += (uint64_t)T;
   MOE_RUN(MOE_K_SCAN, launch_scan(D, p.bitmap, T, p.cbase, p.sbase, p.counts, p.offsets, p.tile_offsets,
                                   p.tile_info, load, train && sign ? cnt : nullptr, s));
-  MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.bitmap, p.cbase, p.sbase, T, p.perm_src, p.inv, s));
+  MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.bitmap, p.cbase, p.sbase, T, p.perm_src, p.inv, s, zs, Xs, D.l / 32));
   return MOE_OK;
 }
 
@@ -276,6 +295,25 @@ void bwd_layout(const moe_config* c, int64_t T, BwdLayout* L) {
   L->total = o;
 }
 
+struct MxWeights {
+  uint8_t *g8, *u8, *d8, *gs, *us, *ds;
+};
+MxWeights mx_weights(moe_ctx* ctx) {
+  const size_t w = (size_t)ctx->cfg.E * ctx->cfg.f * ctx->cfg.l;
+  uint8_t* b = reinterpret_cast<uint8_t*>(ctx->state + ctx->sl.mx);
+  return {b, b + w, b + 2 * w, b + 3 * w, b + 3 * w + w / 32, b + 3 * w + 2 * (w / 32)};
+}
+
+hipError_t quantize_experts(moe_ctx* ctx, hipStream_t s) {
+  const moe_config& c = ctx->cfg;
+  const MxWeights m = mx_weights(ctx);
+  const long long rows_gu = (long long)c.E * c.f, rows_d = (long long)c.E * c.l;
+  hipError_t e = launch_mx_quant(ctx->w.W_g, rows_gu, c.l, c.l, m.g8, m.gs, s);
+  if (e == hipSuccess) e = launch_mx_quant(ctx->w.W_u, rows_gu, c.l, c.l, m.u8, m.us, s);
+  if (e == hipSuccess) e = launch_mx_quant(ctx->w.W_d, rows_d, c.f, c.f, m.d8, m.ds, s);
+  return e;
+}
+
 moe_status hip_ok(hipError_t e, const char* what) {
   return e == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
 }
@@ -334,6 +372,7 @@ moe_status moe_init(const moe_config* cfg, const moe_weights* w, void* state, vo
   c->D = dims_of(cfg);
   c->pending_tokens = 0;
   hipError_t e = launch_zero(state, c->sl.total, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && cfg->experts == MOE_EXPERTS_MXFP8) e = quantize_experts(c, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     delete c;
     return fail(MOE_ERR_HIP, "clearing the state failed: %s", hipGetErrorString(e));
@@ -380,13 +419,28 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
   MOE_RUN(MOE_K_RMSNORM, launch_rmsnorm(D, x, ctx->w.gamma, h, t, s));
   MOE_RUN(MOE_K_GEMM_H, launch_gemm_h(D, h, t, ctx->w.W_r, ctx->w.logit_offset, ctx->w.W_sg, ctx->w.W_su,
                                       ctx->w.W_dn, p.logits, D.f_s > 0 ? G : nullptr, z, s));
-  st = route_tail(ctx, p, t, s);
-  if (st != MOE_OK) return st;
   const int32_t* n_mtiles = p.tile_offsets + D.E;
-  // dispatch X[r] = z[perm_src[r]] happens inside expert_up's operand load
-  MOE_RUN(MOE_K_EXPERT_UP,
-          launch_expert_up(D, z, p.perm_src, p.tile_info, n_mtiles, t, ctx->w.W_g, ctx->w.W_u, H, s));
-  MOE_RUN(MOE_K_EXPERT_DOWN, launch_expert_down(D, H, p.tile_info, n_mtiles, t, ctx->w.W_d, Y, s));
+  if (ctx->cfg.experts == MOE_EXPERTS_MXFP8) {
+    // z -> MXFP8; the scatter copies each token's scale row to its grouped rows
+    uint8_t *z8 = reinterpret_cast<uint8_t*>(w + L.z8), *zs = reinterpret_cast<uint8_t*>(w + L.zs);
+    uint8_t *Xs = reinterpret_cast<uint8_t*>(w + L.Xs), *H8 = reinterpret_cast<uint8_t*>(w + L.H8);
+    uint8_t* Hs = reinterpret_cast<uint8_t*>(w + L.Hs);
+    const MxWeights m = mx_weights(ctx);
+    MOE_RUN(MOE_K_MX_QUANT, launch_mx_quant(z, t, D.l, D.l, z8, zs, s));
+    st = route_tail(ctx, p, t, s, zs, Xs);
+    if (st != MOE_OK) return st;
+    MOE_RUN(MOE_K_EXPERT_UP, launch_expert_up_mx(D, z8, Xs, p.perm_src, p.tile_info, n_mtiles, t, m.g8, m.gs, m.u8,
+                                                 m.us, H, s));
+    MOE_RUN(MOE_K_MX_QUANT, launch_mx_quant(H, (long long)t * D.k, D.f, D.f, H8, Hs, s));
+    MOE_RUN(MOE_K_EXPERT_DOWN, launch_expert_down_mx(D, H8, Hs, p.tile_info, n_mtiles, t, m.d8, m.ds, Y, s));
+  } else {
+    st = route_tail(ctx, p, t, s);
+    if (st != MOE_OK) return st;
+    // dispatch X[r] = z[perm_src[r]] happens inside expert_up's operand load
+    MOE_RUN(MOE_K_EXPERT_UP,
+            launch_expert_up(D, z, p.perm_src, p.tile_info, n_mtiles, t, ctx->w.W_g, ctx->w.W_u, H, s));
+    MOE_RUN(MOE_K_EXPERT_DOWN, launch_expert_down(D, H, p.tile_info, n_mtiles, t, ctx->w.W_d, Y, s));
+  }
   MOE_RUN(MOE_K_COMBINE, launch_combine(D, Y, p.gates, p.inv, t, y_lat, s));
   MOE_RUN(MOE_K_GEMM_OUT, launch_gemm_out(D, G, y_lat, t, ctx->w.W_sd, ctx->w.W_up, out, s));
   return MOE_OK;
@@ -426,6 +480,7 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   moe_status st = check_call(ctx, T, const_cast<void*>(fwd_ws), fwd_ws_bytes);
   if (st != MOE_OK || T == 0) return st;
   if (!x || !dout || !dx || !g) return fail(MOE_ERR_INVALID_ARG, "x, dout, dx or grads is NULL");
+  if (ctx->cfg.experts != MOE_EXPERTS_BF16) return fail(MOE_ERR_STATE, "the backward pass needs bf16 experts");
   const moe_config& c = ctx->cfg;
   if (!g->gamma || !g->W_r || !g->W_dn || !g->W_g || !g->W_u || !g->W_d || !g->W_up ||
       (c.f_s > 0 && (!g->W_sg || !g->W_su || !g->W_sd)))
@@ -574,6 +629,12 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   return MOE_OK;
 }
 
+moe_status moe_requantize_experts(moe_ctx* ctx, void* stream) {
+  if (!ctx) return fail(MOE_ERR_INVALID_ARG, "context is NULL");
+  if (ctx->cfg.experts != MOE_EXPERTS_MXFP8) return MOE_OK;
+  return hip_ok(quantize_experts(ctx, static_cast<hipStream_t>(stream)), "expert quantisation");
+}
+
 moe_status moe_get_bias(moe_ctx* ctx, float* dst, void* stream) {
   if (!ctx || !dst) return fail(MOE_ERR_INVALID_ARG, "context or destination is NULL");
   hipError_t e = hipMemcpyAsync(dst, ctx->state + ctx->sl.bias, (size_t)ctx->cfg.E * 4, hipMemcpyDefault,
@@ -621,7 +682,7 @@ const char* moe_kernel_name(int id) {
                                                 "scan",        "scatter", "expert_up", "expert_down",
                                                 "combine",     "gemm_out", "qb_quantile", "qb_bias", "gemm_rz",
                                                 "sign_bias",   "bwd_gemm", "bwd_expert", "bwd_wgrad",
-                                                "bwd_eltwise", "bwd_transpose"};
+                                                "bwd_eltwise", "bwd_transpose", "mx_quant"};
   return (id >= 0 && id < MOE_NUM_KERNELS) ? names[id] : "unknown";
 }
 

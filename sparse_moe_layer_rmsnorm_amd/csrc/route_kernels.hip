@@ -440,7 +440,8 @@ hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cb
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, const uint32_t* __restrict__ bitmap,
                                                  const int32_t* __restrict__ cbase, const int32_t* __restrict__ sbase,
                                                  int T, int E, int k, int32_t* __restrict__ perm_src,
-                                                 int32_t* __restrict__ inv) {
+                                                 int32_t* __restrict__ inv, const uint32_t* __restrict__ zs,
+                                                 uint32_t* __restrict__ Xs, int s4) {
   const int Tk = T * k;
   const int p = blockIdx.x * 256 + threadIdx.x;
   if (p >= Tk) return;
@@ -451,14 +452,20 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
   const uint32_t below = bitmap[ce] & ((1u << (t % kChunk)) - 1u);
   const int row = sbase[(size_t)(c / kSuper) * E + e] + cbase[ce] + __popc(below);
   inv[p] = row;
-  if ((unsigned)row < (unsigned)Tk) perm_src[row] = t;  // always true for a consistent permutation
+  if ((unsigned)row < (unsigned)Tk) {  // always true for a consistent permutation
+    perm_src[row] = t;
+    for (int q = 0; q < s4; ++q) Xs[(size_t)row * s4 + q] = zs[(size_t)t * s4 + q];
+  }
 }
 
 hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* cbase,
-                          const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s) {
+                          const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s,
+                          const uint8_t* zs, uint8_t* Xs, int s_ld) {
   const long long Tk = (long long)T * D.k;
+  if (zs && s_ld % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_scatter, dim3((unsigned)((Tk + 255) / 256)), dim3(256), 0, s, idx, bitmap, cbase, sbase, T,
-                     D.E, D.k, perm_src, inv);
+                     D.E, D.k, perm_src, inv, reinterpret_cast<const uint32_t*>(zs), reinterpret_cast<uint32_t*>(Xs),
+                     zs ? s_ld / 4 : 0);
   return hipGetLastError();
 }
 

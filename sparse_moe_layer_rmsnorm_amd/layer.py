@@ -34,13 +34,13 @@ class MoeLayer:
     def __init__(self, *, d: int, l: int, E: int, k: int, f: int, f_s: int, dtype: str, weights: Dict,
                  max_tokens: int, qb_bins: int = 256, rms_eps: float = 1e-6, frozen: bool = False,
                  routed_scale: float = 1.0, logit_offset=None, device: str = "cuda", stream=None,
-                 balancer: str = "qb", sign_gamma: float = 1e-2):
+                 balancer: str = "qb", sign_gamma: float = 1e-2, experts: str = "bf16"):
         self.dtype = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.device = torch.device(device)
         self.cfg = B.make_config(d, l, E, k, f, f_s, dtype=dtype, rms_eps=rms_eps, qb_bins=qb_bins, frozen=frozen,
                                  max_tokens=max_tokens, routed_scale=routed_scale, balancer=balancer,
-                                 sign_gamma=sign_gamma)
+                                 sign_gamma=sign_gamma, experts=experts)
         self.dims = dict(d=d, l=l, E=E, k=k, f=f, f_s=f_s, B=qb_bins)
         self.w: Dict[str, torch.Tensor] = {}
         for name in _WEIGHT_NAMES:
@@ -88,6 +88,11 @@ class MoeLayer:
             "Y": view(L.Y, T * dm["k"] * dm["l"], es, (T * dm["k"], dm["l"])),
             "y_lat": view(L.y_lat, T * dm["l"], es, (T, dm["l"])),
             "tile_offsets": view(L.tile_offsets, dm["E"] + 1, torch.int32, (dm["E"] + 1,)),
+            # MXFP8 experts only (empty otherwise): E4M3 bytes and E8M0 scales of z and H
+            "z8": view(L.z8, L.zs - L.z8, torch.uint8, (-1,)),
+            "zs": view(L.zs, L.Xs - L.zs, torch.uint8, (-1,)),
+            "H8": view(L.H8, L.Hs - L.H8, torch.uint8, (-1,)),
+            "Hs": view(L.Hs, L.total - L.Hs, torch.uint8, (-1,)),
         }
 
     def state_views(self) -> Dict[str, torch.Tensor]:
@@ -190,9 +195,9 @@ class MoeLayer:
 
 def layer_from_shape(shape, weights: Dict, *, max_tokens: Optional[int] = None, frozen: Optional[bool] = None,
                      logit_offset=None, device: str = "cuda", balancer: str = "qb",
-                     sign_gamma: float = 1e-2) -> MoeLayer:
+                     sign_gamma: float = 1e-2, experts: str = "bf16") -> MoeLayer:
     """MoeLayer for a workloads.LayerShape."""
     return MoeLayer(d=shape.d, l=shape.l, E=shape.E, k=shape.k, f=shape.f, f_s=shape.f_s, dtype=shape.dtype,
                     weights=weights, max_tokens=max_tokens or shape.T, qb_bins=shape.B, rms_eps=shape.rms_eps,
                     frozen=shape.qb_frozen if frozen is None else frozen, logit_offset=logit_offset,
-                    device=device, balancer=balancer, sign_gamma=sign_gamma)
+                    device=device, balancer=balancer, sign_gamma=sign_gamma, experts=experts)

@@ -83,6 +83,30 @@ def test_sign_gamma_checked_only_for_the_sign_balancer(gamma, ok):
     assert B.moe_state_bytes(qb) > 0                      # ignored by the QB rule
 
 
+@pytest.mark.parametrize("over,status", [
+    (dict(), None), (dict(dtype="f32"), B.MOE_ERR_DTYPE), (dict(l=64), B.MOE_ERR_SHAPE),
+    (dict(f=192), B.MOE_ERR_SHAPE), (dict(f=640), B.MOE_ERR_SHAPE), (dict(l=1024), B.MOE_ERR_SHAPE),
+])
+def test_mxfp8_experts_config(L, over, status):
+    """MXFP8 experts: bf16 mode only, l and f multiples of 128 up to 512; the
+    state then holds the quantised expert weights and their scales."""
+    args = dict(REPLICA)
+    dtype = over.pop("dtype", "bf16")
+    args.update(over)
+    cfg = B.make_config(**args, dtype=dtype, max_tokens=64, experts="mxfp8")
+    if status is None:
+        st = B.moe_state_layout_of(cfg)
+        w = args["E"] * args["f"] * args["l"]
+        assert st.total >= st.mx + 3 * w + 3 * w // 32
+        ref = B.make_config(**args, dtype=dtype, max_tokens=64)
+        assert B.moe_state_bytes(cfg) >= B.moe_state_bytes(ref) + 3 * w
+    else:
+        assert B.moe_state_bytes(cfg) == 0
+        ctx = ctypes.c_void_p()
+        w_ = B.moe_weights(*([1] * 11))
+        assert L.moe_init(ctypes.byref(cfg), ctypes.byref(w_), 256, None, ctypes.byref(ctx)) == status
+
+
 def test_null_arguments_rejected(L):
     cfg = B.make_config(**REPLICA, max_tokens=64)
     ctx = ctypes.c_void_p()
