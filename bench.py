@@ -115,9 +115,47 @@ def cpu_baseline(shape, W, x, seconds: float = 12.0) -> dict:
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 50:
             break
-    return {"value": reps * Ts / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{reps} x full training forward + QB update of the first {Ts} tokens of the {shape.name} "
-                      f"workload (numpy fp64, {el:.1f} s)"}
+    res = {"value": reps * Ts / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{reps} x full training forward + QB update of the first {Ts} tokens of the {shape.name} "
+                     f"workload (numpy fp64, {el:.1f} s)"}
+    # the same sample on one host thread, about a third of the time budget
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            r1, t1 = 0, time.perf_counter()
+            while True:
+                r = o.forward(xs, W, b, k=shape.k, dtype=shape.dtype, eps=shape.rms_eps, B=shape.B)
+                o.qb_update(r["hist"], Ts, shape.k, b)
+                r1 += 1
+                e1 = time.perf_counter() - t1
+                if e1 >= seconds / 3 or r1 >= 20:
+                    break
+        res["value_1_thread"] = r1 * Ts / e1
+    except Exception:
+        pass
+    return res
+
+
+def cold_forward(layer, x, out, stream, n: int) -> dict:
+    """Forward time with the 256 MB MALL flushed first: before each of n
+    forwards a 512 MB buffer is written; events bracket the forward alone."""
+    import torch
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ms = []
+    for _ in range(n):
+        scratch.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        layer.forward(x, out=out)
+        e1.record(stream)
+        layer.qb_update()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del scratch
+    ms.sort()
+    med = ms[len(ms) // 2]
+    return {"ms_per_forward_median": round(med, 5), "tokens_per_s": round(x.shape[0] / (med / 1e3), 1),
+            "forwards": n, "flush": "512 MB device write before each forward"}
 
 
 def main() -> int:
@@ -231,6 +269,7 @@ def main() -> int:
         prof_dom = prof[dom]
     ms_step = total_ms / args.steps
     tok_s = T / (ms_step / 1e3)
+    cold = cold_forward(layer, x, out, stream, min(args.steps, 20)) if not args.backward else None
 
     work = kernel_work(shape, T)
     peak_mm = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -313,6 +352,8 @@ def main() -> int:
                                     "us": round(rt_us, 2)},
         "kernels": kernels,
     }
+    if cold is not None:
+        res["cold_mall"] = cold
     if bwd is not None:
         res["backward"] = bwd
     if not args.no_cpu_baseline:

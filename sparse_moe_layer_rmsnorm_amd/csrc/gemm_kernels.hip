@@ -200,7 +200,8 @@ struct Pipe {
   MOE_DEV static void wait_stage(int after) {
     if (after <= 0) wait_vmcnt<0>();
     else if (after == 1) wait_vmcnt<L>();
-    else wait_vmcnt<2 * L>();
+    else if (after == 2 || 3 * L > 63) wait_vmcnt<2 * L>();
+    else wait_vmcnt<(3 * L > 63 ? 2 * L : 3 * L)>();
   }
 
   // Row-major store of 4 consecutive columns.
@@ -1002,6 +1003,8 @@ template <bool BF16>
 using DensePipe = Pipe<MOE_DENSE_CFG, BF16>;
 template <bool BF16>
 using ExpertPipe = Pipe<MOE_EXPERT_CFG, BF16>;
+// MXFP8 experts: one 128-element K step (128 bytes) per stage
+using ExpertMxPipe = Pipe<kExpertBM, 256, 1, 4, 2, 128, 2, true>;
 constexpr int kCUs = 256;
 
 }  // namespace
@@ -1285,7 +1288,7 @@ hipError_t launch_mx_quant(const void* src, long long rows, int K, long long ld_
 
 template <int KIND>
 static hipError_t launch_expert_mx(const Dims& D, const ExpertArgs& a, int T, hipStream_t s) {
-  using P = ExpertPipe<true>;
+  using P = ExpertMxPipe;
   const long long tiles = (long long)expert_max_mtiles(T, D.k, D.E) * a.NT;
   if (tiles == 0) return hipSuccess;
   hipLaunchKernelGGL((k_gemm_expert_mx<P, KIND>), dim3(persistent_grid(tiles, P::BPC)), dim3(P::THREADS), 0, s, a);
@@ -1295,7 +1298,7 @@ static hipError_t launch_expert_mx(const Dims& D, const ExpertArgs& a, int T, hi
 hipError_t launch_expert_up_mx(const Dims& D, const uint8_t* z8, const uint8_t* Xs, const int32_t* perm_src,
                                const int2* tile_info, const int32_t* n_mtiles, int T, const uint8_t* Wg8,
                                const uint8_t* Wgs, const uint8_t* Wu8, const uint8_t* Wus, void* H, hipStream_t s) {
-  constexpr int BN = ExpertPipe<true>::BN, RB = ExpertPipe<true>::RB;
+  constexpr int BN = ExpertMxPipe::BN, RB = ExpertMxPipe::RB;
   if (D.l % RB || D.l > 4 * RB) return hipErrorInvalidValue;
   ExpertArgs a{};
   a.A = reinterpret_cast<const char*>(z8);
@@ -1323,7 +1326,7 @@ hipError_t launch_expert_up_mx(const Dims& D, const uint8_t* z8, const uint8_t* 
 hipError_t launch_expert_down_mx(const Dims& D, const uint8_t* H8, const uint8_t* Hs, const int2* tile_info,
                                  const int32_t* n_mtiles, int T, const uint8_t* Wd8, const uint8_t* Wds, void* Y,
                                  hipStream_t s) {
-  constexpr int BN = ExpertPipe<true>::BN, RB = ExpertPipe<true>::RB;
+  constexpr int BN = ExpertMxPipe::BN, RB = ExpertMxPipe::RB;
   if (D.f % RB || D.f > 4 * RB) return hipErrorInvalidValue;
   ExpertArgs a{};
   a.A = reinterpret_cast<const char*>(H8);

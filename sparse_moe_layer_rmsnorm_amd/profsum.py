@@ -54,8 +54,10 @@ def logical_name(symbol: str, dense_seen: int) -> str | None:
         return "bwd_wgrad"
     if "k_gemm_expert" in symbol:
         return "expert_up" if symbol.rstrip().endswith("2>(moe::(anonymous namespace)::ExpertArgs)") else "expert_down"
+    if "k_gemm_expert_mx" in symbol:
+        return "expert_up" if "Li2EEEv" in symbol else "expert_down"
     for k in ("rmsnorm_bwd", "dgamma_part", "sum_slices", "transpose", "pad_map", "glu_bwd", "combine_bwd",
-              "dispatch_bwd", "gates_bwd"):
+              "dispatch_bwd", "gates_bwd", "mx_quant"):
         if f"k_{k}" in symbol:
             return k
     for k in ("rmsnorm", "topk", "hist", "scan_local", "scan_global", "scatter", "combine", "qb_update",
