@@ -68,16 +68,16 @@ def kernel_work(s, T: int) -> dict:
 
 def backward_flops(s, T: int) -> dict:
     """GEMM FLOPs of one backward pass per launch group (0: memory-bound
-    groups): the dense products (shared pre-activations recomputed, the two
-    output-projection transposes, dh, and the dense weight gradients), the
-    grouped expert products (dH, A and U recomputed, dX) and the per-expert
-    weight gradients."""
+    groups): the dense products (shared pre-activations recomputed, the
+    output-projection transposes, dh), the grouped expert products (dH, A and
+    U recomputed, dX) and the weight gradients (per expert, and the two dense
+    ones split along the tokens)."""
     Tk = T * s.k
     Kc = 2 * s.f_s + s.l + (s.E + 63) // 64 * 64
-    dense = 2.0 * T * s.d * (2 * s.f_s) + 2.0 * T * s.d * (s.f_s + s.l) + 2.0 * T * Kc * s.d \
-        + 2.0 * s.d * T * (s.f_s + s.l) + 2.0 * Kc * T * s.d
+    dense = 2.0 * T * s.d * (2 * s.f_s) + 2.0 * T * s.d * (s.f_s + s.l) + 2.0 * T * Kc * s.d
     expert = 2.0 * Tk * s.l * s.f * 3 + 2.0 * Tk * 2 * s.f * s.l
-    wgrad = 2.0 * Tk * s.l * s.f + 2.0 * Tk * 2 * s.f * s.l
+    # weight gradients: the per-expert ones and the two split-K dense ones
+    wgrad = 2.0 * Tk * s.l * s.f + 2.0 * Tk * 2 * s.f * s.l + 2.0 * s.d * T * (s.f_s + s.l) + 2.0 * Kc * T * s.d
     return {"bwd_gemm": dense, "bwd_expert": expert, "bwd_wgrad": wgrad, "bwd_eltwise": 0.0, "bwd_transpose": 0.0}
 
 

@@ -425,12 +425,60 @@ __global__ __launch_bounds__(256) void k_sum_slices(const float* __restrict__ pa
   out[c] = a;
 }
 
+__global__ void k_fill_koff(int32_t* __restrict__ koff, int n, int step, int total) {
+  const int j = threadIdx.x;
+  if (j <= n) koff[j] = min(j * step, total);
+}
+
+// C = sum over the S partials, then stored into the segment that holds the
+// row (by_rows) or column; four consecutive columns per thread.
+__global__ __launch_bounds__(256) void k_reduce_split(const float4* __restrict__ part, int S, int M, int N,
+                                                      const SplitOut o) {
+  const long long q = (long long)blockIdx.x * 256 + threadIdx.x;  // float4 index
+  const long long n4 = (long long)M * N / 4;
+  if (q >= n4) return;
+  float4 a = part[q];
+  for (int j = 1; j < S; ++j) {
+    const float4 v = part[(size_t)j * n4 + q];
+    a.x += v.x;
+    a.y += v.y;
+    a.z += v.z;
+    a.w += v.w;
+  }
+  const int m = (int)(q * 4 / N), n = (int)(q * 4 - (long long)m * N);
+  const int key = o.by_rows ? m : n;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < o.nseg && key >= o.start[i] && key < o.start[i] + o.len[i]) {
+      const int r = o.by_rows ? m - o.start[i] : m, c = o.by_rows ? n : n - o.start[i];
+      *reinterpret_cast<float4*>(o.out[i] + (size_t)r * o.ld[i] + c) = a;
+    }
+  }
+}
+
 unsigned blocks_for(long long n, int per_block) {
   long long b = (n + per_block - 1) / per_block;
   return (unsigned)(b < 1 ? 1 : (b > 65535 ? 65535 : b));
 }
 
 }  // namespace
+
+hipError_t launch_fill_koff(int32_t* koff, int n, int step, int total, hipStream_t s) {
+  if (n < 1 || n > 255) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_fill_koff, dim3(1), dim3(256), 0, s, koff, n, step, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_split(const float* part, int S, int M, int N, const SplitOut& o, hipStream_t s) {
+  if (N % 4) return hipErrorInvalidValue;
+  for (int i = 0; i < o.nseg; ++i)
+    if ((!o.by_rows && o.start[i] % 4) || o.ld[i] % 4 || ((uintptr_t)o.out[i] & 15)) return hipErrorInvalidValue;
+  const long long n4 = (long long)M * N / 4;
+  if (n4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_reduce_split, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(part), S, M, N, o);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose(const Dims& D, const void* src, int R, int C, long long ld_src, long long src_bstride,
                             const int32_t* gather, const int32_t* colmap, int P, void* dst, long long ld_dst,

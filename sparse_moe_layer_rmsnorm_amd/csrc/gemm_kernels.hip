@@ -659,6 +659,7 @@ struct WgradArgs {
   const char* A;
   const char* B;
   const int32_t* koff;
+  long long lda, ldb;  // > 0: plain row-major A [M, *], B [N, *] (K slices of one product)
   int es;  // element bytes
   int M, N, MT, NT, E;
   float* out;
@@ -691,13 +692,17 @@ struct WgradProb {
   MOE_DEV const char* row_ptr(const Tile& t, int row) const {
     const int s0 = scalar_load(a.koff, t.sel), pad = scalar_load(a.koff, t.sel + 1) - s0;
     const size_t es = uniform_int(a.es);
+    const bool plain = a.lda > 0;
     if (row < Pp::BM) {  // rows past M read the tile's first row (not stored)
       const int r = row < t.rows ? row : 0;
-      return uniform_ptr(a.A) + ((size_t)s0 * uniform_int(a.M) + (size_t)(t.row0 + r) * pad) * es;
+      const size_t m = (size_t)(t.row0 + r);
+      return uniform_ptr(a.A) +
+             (plain ? m * (size_t)a.lda + s0 : (size_t)s0 * uniform_int(a.M) + m * pad) * es;
     }
     int n = t.nt * Pp::BN + (row - Pp::BM);
     if (n >= uniform_int(a.N)) n = 0;
-    return uniform_ptr(a.B) + ((size_t)s0 * uniform_int(a.N) + (size_t)n * pad) * es;
+    return uniform_ptr(a.B) +
+           (plain ? (size_t)n * (size_t)a.ldb + s0 : (size_t)s0 * uniform_int(a.N) + (size_t)n * pad) * es;
   }
   template <int L>
   MOE_DEV void sources(const Tile& t, SrcT<L>& src) const {
@@ -1251,18 +1256,20 @@ hipError_t launch_expert_nt(const Dims& D, const void* A, int lda_bytes, const i
 }
 
 hipError_t launch_wgrad(const Dims& D, const void* A, const void* B, const int32_t* koff, int M, int N, float* out,
-                        hipStream_t s) {
+                        hipStream_t s, int nseg, long long lda, long long ldb) {
   constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN;
   WgradArgs a{};
   a.A = static_cast<const char*>(A);
   a.B = static_cast<const char*>(B);
   a.koff = koff;
+  a.lda = lda;
+  a.ldb = ldb;
   a.es = esz(D);
   a.M = M;
   a.N = N;
   a.MT = (M + BM - 1) / BM;
   a.NT = (N + BN - 1) / BN;
-  a.E = D.E;
+  a.E = nseg > 0 ? nseg : D.E;
   a.out = out;
   const long long tiles = (long long)a.E * a.MT * a.NT;
   if (tiles == 0) return hipSuccess;

@@ -102,8 +102,22 @@ hipError_t launch_expert_nt(const Dims& D, const void* A, int lda_bytes, const i
 // Per-expert fp32 C_e [M, N] = A_e B_e^T, K = pad_e = koff[e+1] - koff[e]:
 // A_e is the block [M, pad_e] at element koff[e] * M of A, B_e [N, pad_e] at
 // koff[e] * N of B (the segment layout of launch_transpose).
+// With nseg > 0 and lda, ldb > 0 (elements) instead: nseg K slices
+// koff[j] .. koff[j+1] of one product of row-major A [M, *] and B [N, *],
+// partial C_j at out + j*M*N (split K).
 hipError_t launch_wgrad(const Dims& D, const void* A, const void* B, const int32_t* koff, int M, int N, float* out,
-                        hipStream_t s);
+                        hipStream_t s, int nseg = 0, long long lda = 0, long long ldb = 0);
+// koff[j] = min(j * step, total) for j <= n (split-K boundaries).
+hipError_t launch_fill_koff(int32_t* koff, int n, int step, int total, hipStream_t s);
+// Sum of S fp32 partials [S, M, N] into up to 4 outputs, each a block of
+// rows (by_rows) or of columns of C: segment i covers [start_i, start_i +
+// len_i) and is stored row-major with ld_i at out_i.
+struct SplitOut {
+  int nseg, by_rows;
+  int start[4], len[4], ld[4];
+  float* out[4];
+};
+hipError_t launch_reduce_split(const float* part, int S, int M, int N, const SplitOut& o, hipStream_t s);
 
 // dst[c][col_off + p] = src[gather[colmap[p]]][c] (maps optional), 0 for
 // rows < 0 or >= R; `batch` matrices at the given strides (elements).  With

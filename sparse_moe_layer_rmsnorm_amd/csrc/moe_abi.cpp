@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -241,10 +242,11 @@ moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s, co
 // ----------------------------------------------------------------- backward --
 struct BwdLayout {
   size_t Bop1, Bop2, WdT, WguT, P, Q, dG, dy, dAcat, dg, dY, dH, Apre, U, dAU, dX, dh, rstd, gpart;
-  size_t doutT, GyT, dAcatT, hT, dYT, HT, dAUT, XT, dWcat, koff, colmap, seg_tile, total;
+  size_t doutT, GyT, dAcatT, hT, dYT, HT, dAUT, XT, dWcat, ksplit, koff, colmap, seg_tile, total;
   int Tp, Kt, Epad, Kc;
 };
 constexpr int kGammaSlices = 64;
+constexpr int kSplitOut = 3, kSplitCat = 3;  // K slices of the two dense weight-gradient products (144 and 304 output tiles at the replica shape: 3 slices fill 512 block slots best)
 
 void bwd_layout(const moe_config* c, int64_t T, BwdLayout* L) {
   const size_t es = c->dtype == MOE_BF16 ? 2 : 4;
@@ -288,7 +290,8 @@ void bwd_layout(const moe_config* c, int64_t T, BwdLayout* L) {
   L->HT = take(f * Kt * es);
   L->dAUT = take(2 * f * Kt * es);
   L->XT = take(l * Kt * es);
-  L->dWcat = take(Kc * d * 4);
+  L->dWcat = take(std::max((size_t)kSplitOut * d * (fs + l), (size_t)kSplitCat * Kc * d) * 4);  // split-K partials
+  L->ksplit = take(16 * 4);
   L->koff = take((E + 1) * 4);
   L->colmap = take(Kt * 4);
   L->seg_tile = take(Kt / 64 * 4);
@@ -586,27 +589,58 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
     if (e == hipSuccess) e = launch_transpose(D, h, t, d, d, 0, nullptr, nullptr, Tp, hT, Tp, 0, 0, 1, s);
     return e;
   }());
+  // Dense weight gradients, K = tokens split in slices (few output tiles:
+  // d x (f_s + l) and (2 f_s + l + Epad) x d), partials summed into the outputs.
   {
-    DenseSegSpec sg[2];
-    int n = 0;
-    if (fs > 0) sg[n++] = {GyT, fs, 0, g->W_sd, fs};
-    sg[n++] = {el(GyT, (size_t)fs * Tp), l, 0, g->W_up, l};
-    MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 7, doutT, Tp * es, d, Tp * es, sg, n, Tp * es, s));
-    DenseSegSpec sw[1] = {{hT, d, 0, dWcat, d}};
-    MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 6, dAcatT, Tp * es, Kc, Tp * es, sw, 1, Tp * es, s));
+    const int u = Tp / 64;
+    auto slices = [&](int want, int* step) {
+      const int c = (u + want - 1) / want;  // 64-token stages per slice
+      *step = 64 * c;
+      return (u + c - 1) / c;               // every slice non-empty
+    };
+    int step_o, step_c;
+    const int S_o = slices(kSplitOut, &step_o), S_c = slices(kSplitCat, &step_c);
+    int32_t* ko = static_cast<int32_t*>(at(B.ksplit));
+    int32_t* kc = ko + 8;
+    auto dense_wgrad = [&]() -> hipError_t {
+      hipError_t e = launch_fill_koff(ko, S_o, step_o, Tp, s);
+      if (e == hipSuccess) e = launch_fill_koff(kc, S_c, step_c, Tp, s);
+      if (e == hipSuccess)  // [dW_sd | dW_up] = dout^T [G | y_lat]
+        e = launch_wgrad(D, doutT, GyT, ko, d, fs + l, dWcat, s, S_o, Tp, Tp);
+      SplitOut o{};
+      o.by_rows = 0;
+      auto addc = [&](int start, int len, float* out) {
+        o.start[o.nseg] = start;
+        o.len[o.nseg] = len;
+        o.ld[o.nseg] = len;
+        o.out[o.nseg] = out;
+        ++o.nseg;
+      };
+      if (fs > 0) addc(0, fs, g->W_sd);
+      addc(fs, l, g->W_up);
+      if (e == hipSuccess) e = launch_reduce_split(dWcat, S_o, d, fs + l, o, s);
+      if (e == hipSuccess)  // [dW_sg; dW_su; dW_dn; dW_r] = dA_cat^T h
+        e = launch_wgrad(D, dAcatT, hT, kc, Kc, d, dWcat, s, S_c, Tp, Tp);
+      SplitOut c{};
+      c.by_rows = 1;
+      auto add = [&](int start, int len, float* out) {
+        c.start[c.nseg] = start;
+        c.len[c.nseg] = len;
+        c.ld[c.nseg] = d;
+        c.out[c.nseg] = out;
+        ++c.nseg;
+      };
+      if (fs > 0) {
+        add(0, fs, g->W_sg);
+        add(fs, fs, g->W_su);
+      }
+      add(2 * fs, l, g->W_dn);
+      add(2 * fs + l, E, g->W_r);
+      if (e == hipSuccess) e = launch_reduce_split(dWcat, S_c, Kc, d, c, s);
+      return e;
+    };
+    MOE_RUN(MOE_K_BWD_WGRAD, dense_wgrad());
   }
-  st = hip_ok([&]() -> hipError_t {
-    const size_t row = (size_t)d * 4;
-    hipError_t e = hipSuccess;
-    if (fs > 0) e = hipMemcpyAsync(g->W_sg, dWcat, fs * row, hipMemcpyDeviceToDevice, s);
-    if (e == hipSuccess && fs > 0) e = hipMemcpyAsync(g->W_su, dWcat + (size_t)fs * d, fs * row, hipMemcpyDeviceToDevice, s);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(g->W_dn, dWcat + (size_t)2 * fs * d, (size_t)l * row, hipMemcpyDeviceToDevice, s);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(g->W_r, dWcat + (size_t)(2 * fs + l) * d, (size_t)E * row, hipMemcpyDeviceToDevice, s);
-    return e;
-  }(), "gradient copy");
-  if (st != MOE_OK) return st;
   // per-expert weight gradients: K = the expert's rows, padded segments
   MOE_RUN(MOE_K_BWD_TRANSPOSE, [&]() -> hipError_t {
     // per-expert blocks: dY_e^T [l, pad_e], H_e^T [f, pad_e], dA_e^T, dU_e^T [f, pad_e], X_e^T [l, pad_e]

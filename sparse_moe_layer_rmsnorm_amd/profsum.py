@@ -57,7 +57,7 @@ def logical_name(symbol: str, dense_seen: int) -> str | None:
     if "k_gemm_expert_mx" in symbol:
         return "expert_up" if "Li2EEEv" in symbol else "expert_down"
     for k in ("rmsnorm_bwd", "dgamma_part", "sum_slices", "transpose", "pad_map", "glu_bwd", "combine_bwd",
-              "dispatch_bwd", "gates_bwd", "mx_quant"):
+              "dispatch_bwd", "gates_bwd", "mx_quant", "reduce_split", "fill_koff"):
         if f"k_{k}" in symbol:
             return k
     for k in ("rmsnorm", "topk", "hist", "scan_local", "scan_global", "scatter", "combine", "qb_update",
