@@ -78,7 +78,7 @@ def backward_flops(s, T: int) -> dict:
     expert = 2.0 * Tk * s.l * s.f * 3 + 2.0 * Tk * 2 * s.f * s.l
     # weight gradients: the per-expert ones and the two split-K dense ones
     wgrad = 2.0 * Tk * s.l * s.f + 2.0 * Tk * 2 * s.f * s.l + 2.0 * s.d * T * (s.f_s + s.l) + 2.0 * Kc * T * s.d
-    return {"bwd_gemm": dense, "bwd_expert": expert, "bwd_wgrad": wgrad, "bwd_eltwise": 0.0, "bwd_transpose": 0.0}
+    return {"bwd_gemm": dense, "bwd_expert": expert, "bwd_wgrad": wgrad, "bwd_eltwise": 0.0}
 
 
 def traffic_for(kernel: str, workload: str):

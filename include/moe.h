@@ -284,16 +284,17 @@ const char* moe_last_error(void);
  * to n launches, is bracketed by HIP events on its stream.  moe_profile_end()
  * waits for those events and fills, for each kernel id 0..n_ids-1, the summed
  * milliseconds and the launch count; then profiling stops.  Host-side event
- * objects only; no device memory.  MOE_K_HIST is kept for numbering only:
- * in training mode the QB histogram is built inside the MOE_K_TOPK launch,
- * so that id records no launches.
+ * objects only; no device memory.  MOE_K_HIST and MOE_K_BWD_TRANSPOSE are
+ * kept for numbering only and record no launches: in training mode the QB
+ * histogram is built inside the MOE_K_TOPK launch, and the backward's GEMMs
+ * read their operands as stored (K-major tiles), with no transposed copies.
  */
 enum {
   MOE_K_RMSNORM = 0, MOE_K_GEMM_H, MOE_K_TOPK, MOE_K_HIST, MOE_K_SCAN, MOE_K_SCATTER,
   MOE_K_EXPERT_UP, MOE_K_EXPERT_DOWN, MOE_K_COMBINE, MOE_K_GEMM_OUT, MOE_K_QB_QUANTILE,
   MOE_K_QB_BIAS, MOE_K_GEMM_RZ, MOE_K_SIGN_BIAS,
-  /* backward: dense products, grouped expert products, per-expert weight
-     gradients, elementwise transposes and derivatives, operand transposes */
+  /* backward: dense products, grouped expert products, weight gradients,
+     elementwise transposes and derivatives, (unused) */
   MOE_K_BWD_GEMM, MOE_K_BWD_EXPERT, MOE_K_BWD_WGRAD, MOE_K_BWD_ELTWISE, MOE_K_BWD_TRANSPOSE,
   MOE_K_MX_QUANT, /* MXFP8 quantisation of z and H */
   MOE_NUM_KERNELS

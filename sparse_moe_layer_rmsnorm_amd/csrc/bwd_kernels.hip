@@ -1,6 +1,6 @@
-// Memory-bound kernels of the layer's backward pass (gfx950): operand
-// transposes for the weight-gradient products, the padded per-expert K map,
-// the GLU, combine, dispatch and gate transposes, and the RMSNorm gradient.
+// Memory-bound kernels of the layer's backward pass (gfx950): the GLU,
+// combine, dispatch and gate transposes (the adjoints of those forward
+// steps), the RMSNorm gradient and the split-K partial sums.
 // The products themselves run on the GEMM kernels of gemm_kernels.hip.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -46,172 +46,6 @@ template <bool BF16>
 MOE_DEV void st_act(void* p, size_t i, float v) {
   if constexpr (BF16) static_cast<uint16_t*>(p)[i] = (uint16_t)f32_to_bf16_bits(v);
   else static_cast<float*>(p)[i] = v;
-}
-
-// ------------------------------------------------------------ transpose ----
-// dst[c][col_off + p] = src[row(p)][c] for p < P, c < C, where row(p) =
-// gather[colmap[p]] (each map optional: identity when NULL); p whose row is
-// negative or >= R gives 0 (pad columns).  64 x 64 tiles through LDS, reads
-// coalesced along c, writes along p; blockIdx.z walks a batch of matrices.
-template <typename E>
-__global__ __launch_bounds__(256) void k_transpose(const E* __restrict__ src, int R, int C, long long ld_src,
-                                                   long long src_bstride, const int32_t* __restrict__ gather,
-                                                   const int32_t* __restrict__ colmap, int P, E* __restrict__ dst,
-                                                   long long ld_dst, long long col_off, long long dst_bstride) {
-  __shared__ E tile[64][65];
-  const int p0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  src += (size_t)blockIdx.z * src_bstride;
-  dst += (size_t)blockIdx.z * dst_bstride;
-  const int tid = threadIdx.x;
-  {
-    const int cl = tid & 63, pg = tid >> 6;
-    const int c = c0 + cl;
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      const int pl = pg + 4 * i, p = p0 + pl;
-      E v = 0;
-      if (p < P && c < C) {
-        const int r = colmap ? colmap[p] : p;
-        if (r >= 0 && r < R) v = src[(size_t)(gather ? gather[r] : r) * ld_src + c];
-      }
-      tile[pl][cl] = v;
-    }
-  }
-  __syncthreads();
-  const int pl = tid & 63, cg = tid >> 6;
-  const int p = p0 + pl;
-#pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const int cl = cg + 4 * i, c = c0 + cl;
-    if (c < C && p < P) dst[(size_t)c * ld_dst + col_off + p] = tile[pl][cl];
-  }
-}
-
-// Vectorised transposes for the common case (C and P multiples of 64, rows
-// and column offsets on 16-byte boundaries): each wavefront reads 8 (bf16) or
-// 4 (fp32) source rows as whole 128/256-byte runs and writes whole 128-byte
-// runs of destination rows; the tile sits in LDS as dwords with one pad
-// dword per row, so that neither phase has bank conflicts beyond two-way.
-MOE_DEV int src_row_of(int p, int R, const int32_t* __restrict__ gather, const int32_t* __restrict__ colmap) {
-  const int r = colmap ? colmap[p] : p;
-  return (r >= 0 && r < R) ? (gather ? gather[r] : r) : -1;
-}
-
-// Segment mode (seg_tile non-NULL): the columns p form per-expert segments
-// seg_koff[e] .. seg_koff[e+1] (whole 64-column tiles, seg_tile[p / 64] = e,
-// -1 past the last); each expert's transposed block [C, pad_e] is stored
-// contiguously at seg_koff[e] * C, so that its rows are pad_e long.
-MOE_DEV bool seg_dst(const int32_t* __restrict__ seg_koff, const int32_t* __restrict__ seg_tile, int C, int p0,
-                     long long& base, long long& ld) {
-  const int e = seg_tile[p0 / 64];
-  if (e < 0) return false;
-  const int s0 = seg_koff[e];
-  ld = seg_koff[e + 1] - s0;
-  base = (long long)s0 * C - s0;  // + c * ld + p
-  return true;
-}
-
-__global__ __launch_bounds__(256) void k_transpose_b16(const uint16_t* __restrict__ src, int R, long long ld_src,
-                                                       long long src_bstride, const int32_t* __restrict__ gather,
-                                                       const int32_t* __restrict__ colmap, uint16_t* __restrict__ dst,
-                                                       long long ld_dst, long long col_off, long long dst_bstride,
-                                                       const int32_t* __restrict__ seg_koff,
-                                                       const int32_t* __restrict__ seg_tile) {
-  __shared__ uint32_t tile[64][33];  // row p: 64 bf16 of c as 32 dwords
-  const int p0 = blockIdx.x * 64, c0 = blockIdx.y * 64, t = threadIdx.x;
-  if (seg_tile && !seg_dst(seg_koff, seg_tile, gridDim.y * 64, p0, col_off, ld_dst)) return;
-  src += (size_t)blockIdx.z * src_bstride;
-  dst += (size_t)blockIdx.z * dst_bstride;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = t + 256 * i, pr = idx >> 3, ch = idx & 7;
-    const int sr = src_row_of(p0 + pr, R, gather, colmap);
-    const uint4 v = sr >= 0 ? *reinterpret_cast<const uint4*>(src + (size_t)sr * ld_src + c0 + 8 * ch)
-                            : make_uint4(0, 0, 0, 0);
-    tile[pr][4 * ch + 0] = v.x;
-    tile[pr][4 * ch + 1] = v.y;
-    tile[pr][4 * ch + 2] = v.z;
-    tile[pr][4 * ch + 3] = v.w;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = t + 256 * i, pc = idx & 7, cr = idx >> 3;
-    const int sh = (cr & 1) * 16;
-    uint32_t e[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = (tile[8 * pc + j][cr >> 1] >> sh) & 0xFFFFu;
-    *reinterpret_cast<uint4*>(dst + (size_t)(c0 + cr) * ld_dst + col_off + p0 + 8 * pc) =
-        make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
-  }
-}
-
-__global__ __launch_bounds__(256) void k_transpose_b32(const uint32_t* __restrict__ src, int R, long long ld_src,
-                                                       long long src_bstride, const int32_t* __restrict__ gather,
-                                                       const int32_t* __restrict__ colmap, uint32_t* __restrict__ dst,
-                                                       long long ld_dst, long long col_off, long long dst_bstride,
-                                                       const int32_t* __restrict__ seg_koff,
-                                                       const int32_t* __restrict__ seg_tile) {
-  __shared__ uint32_t tile[64][65];
-  const int p0 = blockIdx.x * 64, c0 = blockIdx.y * 64, t = threadIdx.x;
-  if (seg_tile && !seg_dst(seg_koff, seg_tile, gridDim.y * 64, p0, col_off, ld_dst)) return;
-  src += (size_t)blockIdx.z * src_bstride;
-  dst += (size_t)blockIdx.z * dst_bstride;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = t + 256 * i, pr = idx >> 4, ch = idx & 15;
-    const int sr = src_row_of(p0 + pr, R, gather, colmap);
-    const uint4 v = sr >= 0 ? *reinterpret_cast<const uint4*>(src + (size_t)sr * ld_src + c0 + 4 * ch)
-                            : make_uint4(0, 0, 0, 0);
-    tile[pr][4 * ch + 0] = v.x;
-    tile[pr][4 * ch + 1] = v.y;
-    tile[pr][4 * ch + 2] = v.z;
-    tile[pr][4 * ch + 3] = v.w;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = t + 256 * i, pc = idx & 15, cr = idx >> 4;
-    *reinterpret_cast<uint4*>(dst + (size_t)(c0 + cr) * ld_dst + col_off + p0 + 4 * pc) =
-        make_uint4(tile[4 * pc][cr], tile[4 * pc + 1][cr], tile[4 * pc + 2][cr], tile[4 * pc + 3][cr]);
-  }
-}
-
-// ---------------------------------------------------- padded expert K map ----
-// koff[e] = sum over e' < e of pad(n_e'), pad(n) = max(1, ceil(n / 64)) * 64,
-// koff[E] the total; colmap[koff[e] + j] = offsets[e] + j for j < n_e, else
-// -1, and -1 from koff[E] up to Kt (the host's bound on the total).  One
-// block of 1024 threads (E <= 1024).
-__global__ __launch_bounds__(1024) void k_pad_map(const int32_t* __restrict__ offsets, int E, int Kt,
-                                                  int32_t* __restrict__ koff, int32_t* __restrict__ colmap,
-                                                  int32_t* __restrict__ seg_tile) {
-  __shared__ int wsum[16];
-  __shared__ int base[1024];
-  const int i = threadIdx.x, lane = i & 63, w = i >> 6;
-  const int n = i < E ? offsets[i + 1] - offsets[i] : 0;
-  const int pad = i < E ? max(1, (n + 63) / 64) * 64 : 0;
-  int r = pad;  // inclusive wave scan
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(r, o, 64);
-    if (lane >= o) r += v;
-  }
-  if (lane == 63) wsum[w] = r;
-  __syncthreads();
-  for (int j = 0; j < w; ++j) r += wsum[j];
-  base[i] = r - pad;
-  if (i < E) koff[i] = r - pad;
-  if (i == E - 1) koff[E] = r;
-  __syncthreads();
-  for (int e = w; e < E; e += 16) {  // one wavefront per expert
-    const int b = base[e], off = offsets[e], ne = offsets[e + 1] - off;
-    const int pe = max(1, (ne + 63) / 64) * 64;
-    for (int j = lane; j < pe; j += 64) colmap[b + j] = j < ne ? off + j : -1;
-    for (int j = lane; j < pe / 64; j += 64) seg_tile[b / 64 + j] = e;
-  }
-  const int tot = base[E - 1] + max(1, (offsets[E] - offsets[E - 1] + 63) / 64) * 64;
-  for (int j = tot + i; j < Kt; j += 1024) colmap[j] = -1;
-  for (int j = tot / 64 + i; j < Kt / 64; j += 1024) seg_tile[j] = -1;
 }
 
 // ------------------------------------------------------------------ GLU ----
@@ -425,11 +259,6 @@ __global__ __launch_bounds__(256) void k_sum_slices(const float* __restrict__ pa
   out[c] = a;
 }
 
-__global__ void k_fill_koff(int32_t* __restrict__ koff, int n, int step, int total) {
-  const int j = threadIdx.x;
-  if (j <= n) koff[j] = min(j * step, total);
-}
-
 // C = sum over the S partials, then stored into the segment that holds the
 // row (by_rows) or column; four consecutive columns per thread.
 __global__ __launch_bounds__(256) void k_reduce_split(const float4* __restrict__ part, int S, int M, int N,
@@ -463,12 +292,6 @@ unsigned blocks_for(long long n, int per_block) {
 
 }  // namespace
 
-hipError_t launch_fill_koff(int32_t* koff, int n, int step, int total, hipStream_t s) {
-  if (n < 1 || n > 255) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_fill_koff, dim3(1), dim3(256), 0, s, koff, n, step, total);
-  return hipGetLastError();
-}
-
 hipError_t launch_reduce_split(const float* part, int S, int M, int N, const SplitOut& o, hipStream_t s) {
   if (N % 4) return hipErrorInvalidValue;
   for (int i = 0; i < o.nseg; ++i)
@@ -477,43 +300,6 @@ hipError_t launch_reduce_split(const float* part, int S, int M, int N, const Spl
   if (n4 == 0) return hipSuccess;
   hipLaunchKernelGGL(k_reduce_split, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<const float4*>(part), S, M, N, o);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose(const Dims& D, const void* src, int R, int C, long long ld_src, long long src_bstride,
-                            const int32_t* gather, const int32_t* colmap, int P, void* dst, long long ld_dst,
-                            long long col_off, long long dst_bstride, int batch, hipStream_t s,
-                            const int32_t* seg_koff, const int32_t* seg_tile) {
-  if (P <= 0 || C <= 0 || batch <= 0) return hipSuccess;
-  dim3 grid((P + 63) / 64, (C + 63) / 64, batch);
-  const int V = D.bf16 ? 8 : 4;
-  const bool vec = C % 64 == 0 && P % 64 == 0 && ld_src % V == 0 && ld_dst % V == 0 && col_off % V == 0 &&
-                   src_bstride % V == 0 && dst_bstride % V == 0 && ((uintptr_t)src & 15) == 0 &&
-                   ((uintptr_t)dst & 15) == 0;
-  if (seg_tile && !vec) return hipErrorInvalidValue;
-  if (vec) {
-    if (D.bf16)
-      hipLaunchKernelGGL(k_transpose_b16, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), R, ld_src,
-                         src_bstride, gather, colmap, static_cast<uint16_t*>(dst), ld_dst, col_off, dst_bstride,
-                         seg_koff, seg_tile);
-    else
-      hipLaunchKernelGGL(k_transpose_b32, grid, dim3(256), 0, s, static_cast<const uint32_t*>(src), R, ld_src,
-                         src_bstride, gather, colmap, static_cast<uint32_t*>(dst), ld_dst, col_off, dst_bstride,
-                         seg_koff, seg_tile);
-    return hipGetLastError();
-  }
-  if (D.bf16)
-    hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), R, C, ld_src,
-                       src_bstride, gather, colmap, P, static_cast<uint16_t*>(dst), ld_dst, col_off, dst_bstride);
-  else
-    hipLaunchKernelGGL(k_transpose<uint32_t>, grid, dim3(256), 0, s, static_cast<const uint32_t*>(src), R, C, ld_src,
-                       src_bstride, gather, colmap, P, static_cast<uint32_t*>(dst), ld_dst, col_off, dst_bstride);
-  return hipGetLastError();
-}
-
-hipError_t launch_pad_map(const Dims& D, const int32_t* offsets, int Kt, int32_t* koff, int32_t* colmap,
-                          int32_t* seg_tile, hipStream_t s) {
-  hipLaunchKernelGGL(k_pad_map, dim3(1), dim3(1024), 0, s, offsets, D.E, Kt, koff, colmap, seg_tile);
   return hipGetLastError();
 }
 

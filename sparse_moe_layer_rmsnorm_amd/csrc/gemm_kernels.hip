@@ -35,6 +35,8 @@
 // groups that are not 16 consecutive lanes (measured: the variant that also
 // flips chunk bit 0 for rows 8..15 costs twice the cycles); with this
 // placement each group of a fragment read hits 16 distinct 16-byte bank slots.
+#include <cstring>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -103,6 +105,15 @@ MOE_DEV const char* uniform_ptr(const char* p) {
   return (const char*)(((uint64_t)hi << 32) | lo);
 }
 MOE_DEV int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+MOE_DEV long long uniform_ll(long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (long long)(((uint64_t)hi << 32) | lo);
+}
+
+// Source of K rows that lie past an operand's end (read by the stage DMA in
+// place of a row): 1 KB, never written, zero from load.
+__device__ __attribute__((aligned(16))) uint4 g_zero_row[64] = {};
 
 // Block tile BM x BN over WM x WN wavefronts, NS LDS stages of RB K-bytes
 // per row (64 or 128), BPC blocks per CU.
@@ -119,9 +130,22 @@ MOE_DEV int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 // rows of 4 chunks); thread (wave w of NW, lane) fills slots i*NW + w, i < L,
 // lane l writing chunk position l % (RB/16) of its row, i.e. logical chunk
 // (l % (RB/16)) ^ sw(row).
-template <int BM_, int BN_, int WM_, int WN_, int NS_, int RB_, int BPC_, bool BF16>
+//
+// K-major operands (KM bit 0: A, bit 1: B).  Such an operand is stored with
+// K as its rows and the tile's M (or N) columns contiguous, e.g. a token-major
+// activation in a product that contracts over tokens.  Its region of a stage
+// holds KR = RB / element-bytes K rows of P = BM (BN) * element-bytes bytes,
+// 16-byte chunk c of row r at position c ^ swzk(r), and fragments are read
+// with ds_read_b64_tr_b16 (bf16): lane s of each 16-lane group addresses row
+// s / 4 and columns 4 (s % 4) .. + 3 of a 4 x 16 block, and lane i receives
+// column i of the block's 4 rows (measured on gfx950), i.e. the MFMA operand
+// layout of 16 rows (columns here) by 4 consecutive K values.  fp32 K-major
+// fragments are four ds_read_b32 per lane.  The swizzle spreads the rows one
+// fragment read touches at once (bf16: rows r % 4 and r / 8 odd or even; fp32:
+// the 4 lane groups' rows) over distinct bank slots.
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int RB_, int BPC_, bool BF16, int KM_ = 0>
 struct Pipe {
-  static constexpr int BM = BM_, BN = BN_, NS = NS_, RB = RB_, BPC = BPC_;
+  static constexpr int BM = BM_, BN = BN_, NS = NS_, RB = RB_, BPC = BPC_, KM = KM_;
   static constexpr int WM = WM_, WN = WN_, NW = WM * WN;
   static constexpr int THREADS = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -137,6 +161,12 @@ struct Pipe {
   static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
   static_assert(LDS * BPC <= 160 * 1024, "LDS per CU");
   using Acc = f32x4_t[MI][NI];
+  static constexpr int ES = BF16 ? 2 : 4;
+  static constexpr int KR = RB / ES;                 // K rows of a K-major region per stage
+  static constexpr int PA = BM * ES, PB = BN * ES;   // row bytes of K-major A / B regions
+  static constexpr int LA = A_BYTES / (1024 * NW);   // DMA slots of the A region per thread
+  static_assert(KM == 0 || (A_BYTES % (1024 * NW) == 0 && PA >= 128 && PB >= 128 && PA <= 1024 && PB <= 1024),
+                "K-major regions: whole slots per wavefront, 128- to 1024-byte rows");
 
   MOE_DEV static int wave_id() { return threadIdx.x >> 6; }
 
@@ -144,6 +174,51 @@ struct Pipe {
   MOE_DEV static int lds_off(int row, int chunk) { return row * RB + ((chunk ^ swz(row)) << 4); }
   MOE_DEV static int slot_row(int i, int wave, int lane) { return (i * NW + wave) * (1024 / RB) + lane / CPR; }
   MOE_DEV static int slot_chunk(int row, int lane) { return (lane % CPR) ^ swz(row); }
+
+  template <int P>
+  MOE_DEV static int swzk(int row) {
+    if constexpr (BF16) return (2 * ((row & 3) | (((row >> 3) & 1) << 2))) & (P / 16 - 1);
+    else return (((row >> 2) & 3) << 2) & (P / 16 - 1);
+  }
+  template <int P>
+  MOE_DEV static int km_off(int row, int colbyte) {
+    return row * P + (((colbyte >> 4) ^ swzk<P>(row)) << 4) + (colbyte & 15);
+  }
+  // DMA slot mapping of a K-major region: lane -> K row of the stage and the
+  // logical byte offset (within the tile's columns) of its 16-byte chunk.
+  template <int P>
+  MOE_DEV static int km_slot_row(int ls, int lane) { return ls * (1024 / P) + lane / (P / 16); }
+  template <int P>
+  MOE_DEV static int km_slot_colbyte(int row, int lane) { return ((lane % (P / 16)) ^ swzk<P>(row)) << 4; }
+
+  // Fragment of a K-major region: columns col0 .. col0 + 15, 64-byte K step kk.
+  template <int P>
+  MOE_DEV static uint4 frag_km(const char* region, int col0, int kk) {
+    const int lane = threadIdx.x & 63, s = lane & 15, g = lane >> 4;
+    if constexpr (BF16) {
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s* lds_v4s;
+      const int r0 = kk * 32 + 8 * g + (s >> 2), cb = 2 * col0 + 8 * (s & 3);
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(region + km_off<P>(r0, cb)));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(region + km_off<P>(r0 + 4, cb)));
+      const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+      return make_uint4(a.x, a.y, b.x, b.y);
+    } else {
+      uint32_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = *reinterpret_cast<const uint32_t*>(region + km_off<P>(kk * 16 + 4 * g + j, 4 * (col0 + s)));
+      return make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  }
+  MOE_DEV static uint4 frag_a(const char* cur, int row0, int ch, int kk) {
+    if constexpr (KM & 1) return frag_km<PA>(cur, row0, kk);
+    else return *reinterpret_cast<const uint4*>(cur + lds_off(row0 + (threadIdx.x & 15), ch));
+  }
+  MOE_DEV static uint4 frag_b(const char* cur, int row0, int ch, int kk) {
+    if constexpr (KM & 2) return frag_km<PB>(cur + A_BYTES, row0, kk);
+    else return *reinterpret_cast<const uint4*>(cur + A_BYTES + lds_off(row0 + (threadIdx.x & 15), ch));
+  }
 
   // All fragment reads of the stage are issued before the first MFMA, so
   // the wavefront waits for LDS once per stage rather than once per group.
@@ -156,11 +231,9 @@ struct Pipe {
         const int ch = kk * 4 + (lane >> 4);
         uint4 af[MI], wf[NI];
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          wf[ni] = *reinterpret_cast<const uint4*>(cur + A_BYTES + lds_off(wn * WTN + ni * 16 + (lane & 15), ch));
+        for (int ni = 0; ni < NI; ++ni) wf[ni] = frag_b(cur, wn * WTN + ni * 16, ch, kk);
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-          af[mi] = *reinterpret_cast<const uint4*>(cur + lds_off(wm * WTM + mi * 16 + (lane & 15), ch));
+        for (int mi = 0; mi < MI; ++mi) af[mi] = frag_a(cur, wm * WTM + mi * 16, ch, kk);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
@@ -174,11 +247,9 @@ struct Pipe {
     for (int kk = 0; kk < KK; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        wf[kk][ni] = *reinterpret_cast<const uint4*>(cur + A_BYTES + lds_off(wn * WTN + ni * 16 + (lane & 15), ch));
+      for (int ni = 0; ni < NI; ++ni) wf[kk][ni] = frag_b(cur, wn * WTN + ni * 16, ch, kk);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        af[kk][mi] = *reinterpret_cast<const uint4*>(cur + lds_off(wm * WTM + mi * 16 + (lane & 15), ch));
+      for (int mi = 0; mi < MI; ++mi) af[kk][mi] = frag_a(cur, wm * WTM + mi * 16, ch, kk);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -404,6 +475,45 @@ struct DenseArgs {
 constexpr int kGroupM = 2;
 constexpr int kNSplit = 2;
 
+// Logical tile L -> (first row, rows, n-tile within its segment, segment) in
+// the order above; segment s has ntiles[s] n-tiles (at most 3 segments).
+template <int BM>
+MOE_DEV Tile dense_tile(int L, int m_tiles, int total_ntiles, int M, int nseg, int nt0, int nt1) {
+  // kNSplit column ranges, each over all m-tiles, one after the other
+  int n_base = 0, n_cnt = total_ntiles;
+#pragma unroll
+  for (int h = 0; h < kNSplit - 1; ++h) {
+    const int cnt = (total_ntiles - n_base + (kNSplit - h) - 1) / (kNSplit - h);
+    if (L < m_tiles * cnt) {
+      n_cnt = cnt;
+      break;
+    }
+    L -= m_tiles * cnt;
+    n_base += cnt;
+    n_cnt = total_ntiles - n_base;
+  }
+  const int per_group = kGroupM * n_cnt;
+  const int group = L / per_group;
+  const int first_m = group * kGroupM;
+  const int gm = min(m_tiles - first_m, kGroupM);
+  const int in_group = L - group * per_group;
+  Tile t;
+  t.row0 = (first_m + in_group % gm) * BM;
+  t.rows = min(BM, M - t.row0);
+  int nt = n_base + in_group / gm, sg = 0;
+  if (nseg > 1 && nt >= nt0) {
+    nt -= nt0;
+    sg = 1;
+    if (nseg > 2 && nt >= nt1) {
+      nt -= nt1;
+      sg = 2;
+    }
+  }
+  t.nt = nt;
+  t.sel = sg;
+  return t;
+}
+
 template <class Pp>
 struct DenseProb {
   static constexpr int PARTS = 2;
@@ -419,39 +529,7 @@ struct DenseProb {
   MOE_DEV const DenseSeg& seg(int s) const { return s == 0 ? a.seg[0] : (s == 1 ? a.seg[1] : a.seg[2]); }
 
   MOE_DEV Tile tile(int L) const {
-    // kNSplit column ranges, each over all m-tiles, one after the other
-    int n_base = 0, n_cnt = a.total_ntiles;
-#pragma unroll
-    for (int h = 0; h < kNSplit - 1; ++h) {
-      const int cnt = (a.total_ntiles - n_base + (kNSplit - h) - 1) / (kNSplit - h);
-      if (L < a.m_tiles * cnt) {
-        n_cnt = cnt;
-        break;
-      }
-      L -= a.m_tiles * cnt;
-      n_base += cnt;
-      n_cnt = a.total_ntiles - n_base;
-    }
-    const int per_group = kGroupM * n_cnt;
-    const int group = L / per_group;
-    const int first_m = group * kGroupM;
-    const int gm = min(a.m_tiles - first_m, kGroupM);
-    const int in_group = L - group * per_group;
-    Tile t;
-    t.row0 = (first_m + in_group % gm) * Pp::BM;
-    t.rows = min(Pp::BM, a.M - t.row0);
-    int nt = n_base + in_group / gm, s = 0;
-    if (a.nseg > 1 && nt >= a.seg[0].ntiles) {
-      nt -= a.seg[0].ntiles;
-      s = 1;
-      if (a.nseg > 2 && nt >= a.seg[1].ntiles) {
-        nt -= a.seg[1].ntiles;
-        s = 2;
-      }
-    }
-    t.nt = nt;
-    t.sel = s;
-    return t;
+    return dense_tile<Pp::BM>(L, a.m_tiles, a.total_ntiles, a.M, a.nseg, a.seg[0].ntiles, a.seg[1].ntiles);
   }
 
   // Start of stage row `row` (A rows first, then weight rows) of K part `part`.
@@ -649,81 +727,133 @@ __global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expe
   stream<Pp>(prob, smem);
 }
 
-// ------------------------------------------- per-expert weight gradients --
-// C_e = A_e B_e^T for every expert e, K = the expert's own (padded) token
-// count pad_e = koff[e+1] - koff[e] (whole stages, at least one, pad columns
-// zero): A_e [M, pad_e] is a contiguous block at element koff[e] * M of A,
-// B_e [N, pad_e] at koff[e] * N of B, so a tile's rows are short and close.
-// C_e [M, N] fp32 at out + e*M*N.  Used for dW = dY_e^T H_e style products.
-struct WgradArgs {
-  const char* A;
-  const char* B;
-  const int32_t* koff;
-  long long lda, ldb;  // > 0: plain row-major A [M, *], B [N, *] (K slices of one product)
-  int es;  // element bytes
-  int M, N, MT, NT, E;
-  float* out;
+// ------------------------------------ data gradients with K-major weights --
+// C = A B with A row-major (K contiguous: dout, dA_cat, dY, [dA | dU]) and B
+// the weights as stored, i.e. K-major ([in, out] rows of a y = x W^T layer
+// read along their first index), so no transposed weight copies are made.
+// K is a concatenation of up to 4 pieces: piece j covers stages [st[j],
+// st[j+1]) and reads its K rows from B[j] (row stride ldb[j]); rows past
+// rows[j] are read from the zero row.  Dense mode: the dense tile order over
+// up to 2 output segments (each with its own pieces' sources, N and output);
+// expert mode: the grouped tiles of the expert GEMMs, B advancing by
+// b_expert_bytes per expert.
+struct DgradSeg {
+  const char* B[4];
+  long long ldb[4];  // elements
+  int N, ntiles, kind;
+  void* out;
+  int ldo;
 };
 
-template <class Pp>
-struct WgradProb {
+struct DgradArgs {
+  const char* A;
+  int lda_bytes;
+  int M, m_tiles, nseg, total_ntiles;  // dense mode
+  DgradSeg seg[2];
+  int st[5], rows[4], npiece;
+  int es;
+  const int2* tile_info;  // expert mode
+  const int32_t* n_mtiles;
+  size_t b_expert_bytes;
+};
+
+template <class Pp, bool EXPERT>
+struct DgradProb {
   static constexpr int PARTS = 1;
+  static constexpr int LA = Pp::LA, KR = Pp::KR;
   template <int L>
   struct SrcT {
-    const char* p[L];
+    const char* pa[LA];       // A chunk addresses at the first stage
+    uint32_t cb[L - LA];      // B chunk byte offsets within a K row
+    int sel;                  // the tile's segment (dense) or expert (wave-uniform)
   };
-  const WgradArgs& a;
+  const DgradArgs& a;
 
-  MOE_DEV int total() const { return a.E * a.MT * a.NT; }
+  MOE_DEV int total() const {
+    if constexpr (EXPERT) return scalar_load(a.n_mtiles, 0) * a.seg[0].ntiles;
+    else return a.m_tiles * a.total_ntiles;
+  }
+  MOE_DEV int kt() const { return a.st[a.npiece]; }
   MOE_DEV Tile tile(int L) const {
-    const int per = a.MT * a.NT;
-    const int e = L / per, r = L - e * per;
-    const int mt = r / a.NT;
-    Tile t;
-    t.row0 = mt * Pp::BM;
-    t.rows = min(Pp::BM, a.M - t.row0);
-    t.nt = r - mt * a.NT;
-    t.sel = e;
-    return t;
-  }
-  MOE_DEV int kt_of(const Tile& t) const {
-    return (scalar_load(a.koff, t.sel + 1) - scalar_load(a.koff, t.sel)) * uniform_int(a.es) / Pp::RB;
-  }
-  MOE_DEV const char* row_ptr(const Tile& t, int row) const {
-    const int s0 = scalar_load(a.koff, t.sel), pad = scalar_load(a.koff, t.sel + 1) - s0;
-    const size_t es = uniform_int(a.es);
-    const bool plain = a.lda > 0;
-    if (row < Pp::BM) {  // rows past M read the tile's first row (not stored)
-      const int r = row < t.rows ? row : 0;
-      const size_t m = (size_t)(t.row0 + r);
-      return uniform_ptr(a.A) +
-             (plain ? m * (size_t)a.lda + s0 : (size_t)s0 * uniform_int(a.M) + m * pad) * es;
+    if constexpr (EXPERT) {
+      const int NT = a.seg[0].ntiles, g = L / NT;
+      const int2 info = scalar_load2(a.tile_info, g);
+      Tile t;
+      t.row0 = info.x;
+      t.rows = info.y & 0xFF;
+      t.sel = info.y >> 8;
+      t.nt = L - g * NT;
+      return t;
+    } else {
+      return dense_tile<Pp::BM>(L, a.m_tiles, a.total_ntiles, a.M, a.nseg, a.seg[0].ntiles, 0);
     }
-    int n = t.nt * Pp::BN + (row - Pp::BM);
-    if (n >= uniform_int(a.N)) n = 0;
-    return uniform_ptr(a.B) +
-           (plain ? (size_t)n * (size_t)a.ldb + s0 : (size_t)s0 * uniform_int(a.N) + (size_t)n * pad) * es;
+  }
+  MOE_DEV const DgradSeg& seg(const Tile& t) const {
+    if constexpr (EXPERT) return a.seg[0];
+    else return t.sel == 0 ? a.seg[0] : a.seg[1];
   }
   template <int L>
   MOE_DEV void sources(const Tile& t, SrcT<L>& src) const {
-    const int lane = threadIdx.x & 63, wave = Pp::wave_id();
+    const int lane = threadIdx.x & 63, wave = Pp::wave_id(), uwave = uniform_int(wave);
+    const DgradSeg& S = seg(t);
+    const size_t es = uniform_int(a.es);
+    const int lda = uniform_int(a.lda_bytes), N = uniform_int(S.N);
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
+    for (int i = 0; i < LA; ++i) {  // A rows past the tile's end read its first row (not stored)
       const int row = Pp::slot_row(i, wave, lane);
-      src.p[i] = row_ptr(t, row) + Pp::slot_chunk(row, lane) * 16;
+      src.pa[i] = uniform_ptr(a.A) + (size_t)(t.row0 + (row < t.rows ? row : 0)) * lda + Pp::slot_chunk(row, lane) * 16;
     }
+#pragma unroll
+    for (int i = LA; i < L; ++i) {
+      const int row = Pp::template km_slot_row<Pp::PB>((i - LA) * Pp::NW + uwave, lane);
+      int col = t.nt * Pp::BN + Pp::template km_slot_colbyte<Pp::PB>(row, lane) / (int)es;
+      if (col >= N) col = 0;
+      src.cb[i - LA] = (uint32_t)(col * es);
+    }
+    src.sel = t.sel;
   }
   template <int L>
   MOE_DEV void issue(const SrcT<L>& src, int ks, uint32_t lds) const {
+    const int lane = threadIdx.x & 63, uwave = uniform_int(Pp::wave_id());
 #pragma unroll
-    for (int i = 0; i < L; ++i)
-      lds_dma16(src.p[i] + ks * Pp::RB, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
+    for (int i = 0; i < LA; ++i)
+      lds_dma16(src.pa[i] + ks * Pp::RB, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
+    // the stage's piece and its source, from the kernel arguments (wave-uniform)
+    int j = 0;
+#pragma unroll
+    for (int q = 1; q < 4; ++q) j = (q < a.npiece && ks >= a.st[q]) ? q : j;
+    j = uniform_int(j);
+    const int sel = uniform_int(src.sel);
+    const DgradSeg& S = EXPERT || sel == 0 ? a.seg[0] : a.seg[1];
+    const char* B = uniform_ptr(S.B[j] + (EXPERT ? (size_t)sel * a.b_expert_bytes : 0));
+    const size_t ldb = (size_t)uniform_ll(S.ldb[j]) * uniform_int(a.es);
+    const int rows = uniform_int(a.rows[j]);
+    const int kr0 = uniform_int((ks - a.st[j]) * KR);
+    const char* zero = reinterpret_cast<const char*>(g_zero_row) + (lane << 4);
+#pragma unroll
+    for (int i = LA; i < L; ++i) {
+      const int kr = kr0 + Pp::template km_slot_row<Pp::PB>((i - LA) * Pp::NW + uwave, lane);
+      const char* q = kr < rows ? B + (size_t)kr * ldb + src.cb[i - LA] : zero;
+      lds_dma16(q, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
+    }
   }
   MOE_DEV void epilogue(const Tile& t, const typename Pp::Acc& acc) const {
-    Pp::template epilogue<EPI_F32>(acc, t.rows, t.nt * Pp::BN, a.N, a.out + (size_t)t.sel * a.M * a.N, a.N,
-                                   (size_t)t.row0, nullptr);
+    const DgradSeg& S = seg(t);
+    if (!EXPERT && S.kind == EPI_F32)
+      Pp::template epilogue<EPI_F32>(acc, t.rows, t.nt * Pp::BN, S.N, S.out, S.ldo, (size_t)t.row0, nullptr);
+    else
+      Pp::template epilogue<EPI_STORE>(acc, t.rows, t.nt * Pp::BN, S.N, S.out, S.ldo, (size_t)t.row0, nullptr);
   }
 };
+
+// TAG names the launch for profiles (4: dout products, 5: dh, 8: expert dH,
+// 9: expert dX).
+template <class Pp, bool EXPERT, int TAG>
+__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_dgrad(const DgradArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
+  DgradProb<Pp, EXPERT> prob{args};
+  stream<Pp>(prob, smem);
+}
 
 // The persistent stream for tiles whose K length varies (kt_of(tile) >= 1
 // stages): the issue and the compute cursors each track their own tile's
@@ -783,10 +913,148 @@ MOE_DEV void stream_var(const Prob& prob, char* smem) {
   }
 }
 
+// ------------------------------- weight gradients from token-major operands --
+// C_e = A_e^T B_e for every segment e of the token (K) axis, with A and B
+// stored token-major (row k holds that token's M or N values), so neither is
+// transposed in memory: both enter the MFMA through K-major LDS regions.
+// Segment e covers rows [koff[e], koff[e+1]) (koff == nullptr: [e kstep,
+// (e+1) kstep)), cut at kend; rows past the segment's end, up to its last
+// whole stage, are read from a zero row.  B's columns n < nsplit come from
+// B[0], the rest from B[1] (two operands side by side, e.g. [G | y_lat]);
+// with `gather`, B's row k is row gather[k] (the dispatch permutation).
+// C_e [M, N] fp32 at out + e M N.
+struct WgradKmArgs {
+  const char* A;
+  const char* B[2];
+  long long lda, ldb[2];  // row strides, elements
+  const int32_t* koff;
+  const int32_t* gather;
+  int kstep, kend, ngather, nsplit;
+  int es, M, N, MT, NT, E;
+  float* out;
+};
+
 template <class Pp>
-__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_wgrad(const WgradArgs args) {
+struct WgradKmProb {
+  static constexpr int PARTS = 1;
+  static constexpr int LA = Pp::LA, KR = Pp::KR;
+  template <int L>
+  struct SrcT {
+    const char* p[L];   // chunk address at the first stage (gathered B: at row 0)
+    uint32_t stride[L]; // bytes per stage (gathered B: per row)
+    int k0, n;          // the segment's first row and row count (wave-uniform)
+  };
+  const WgradKmArgs& a;
+
+  MOE_DEV int total() const { return a.E * a.MT * a.NT; }
+  MOE_DEV Tile tile(int L) const {
+    const int per = a.MT * a.NT;
+    const int e = L / per, r = L - e * per;
+    const int mt = r / a.NT;
+    Tile t;
+    t.row0 = mt * Pp::BM;
+    t.rows = min(Pp::BM, a.M - t.row0);
+    t.nt = r - mt * a.NT;
+    t.sel = e;
+    return t;
+  }
+  MOE_DEV int2 seg(const Tile& t) const {  // first row, row count
+    const int kend = uniform_int(a.kend);
+    int k0, k1;
+    if (a.koff) {
+      k0 = scalar_load(a.koff, t.sel);
+      k1 = scalar_load(a.koff, t.sel + 1);
+    } else {
+      k0 = t.sel * uniform_int(a.kstep);
+      k1 = k0 + uniform_int(a.kstep);
+    }
+    k1 = min(k1, kend);
+    return make_int2(k0, max(0, k1 - k0));
+  }
+  MOE_DEV int kt_of(const Tile& t) const { return max(1, (seg(t).y + KR - 1) / KR); }
+  template <int L>
+  MOE_DEV void sources(const Tile& t, SrcT<L>& src) const {
+    const int lane = threadIdx.x & 63, wave = uniform_int(Pp::wave_id());
+    const int2 sg = seg(t);
+    src.k0 = sg.x;
+    src.n = sg.y;
+    const size_t es = uniform_int(a.es);
+    const int M = uniform_int(a.M), N = uniform_int(a.N), nsplit = uniform_int(a.nsplit);
+    const bool gather = a.gather != nullptr;
+    const size_t lda = (size_t)uniform_ll(a.lda), ldb0 = (size_t)uniform_ll(a.ldb[0]),
+                 ldb1 = (size_t)uniform_ll(a.ldb[1]);
+    const char *A = uniform_ptr(a.A), *B0 = uniform_ptr(a.B[0]), *B1 = uniform_ptr(a.B[1]);
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int si = i * Pp::NW + wave;
+      if (i < LA) {
+        const int row = Pp::template km_slot_row<Pp::PA>(si, lane);
+        int col = t.row0 + Pp::template km_slot_colbyte<Pp::PA>(row, lane) / (int)es;
+        if (col >= M) col = 0;
+        src.p[i] = A + ((size_t)(sg.x + row) * lda + col) * es;
+        src.stride[i] = (uint32_t)(KR * lda * es);
+      } else {
+        const int row = Pp::template km_slot_row<Pp::PB>(si - LA * Pp::NW, lane);
+        int col = t.nt * Pp::BN + Pp::template km_slot_colbyte<Pp::PB>(row, lane) / (int)es;
+        if (col >= N) col = 0;
+        const bool second = col >= nsplit;
+        const char* base = second ? B1 : B0;
+        const size_t ld = second ? ldb1 : ldb0;
+        const size_t c = (size_t)(second ? col - nsplit : col);
+        if (gather) {
+          src.p[i] = base + c * es;
+          src.stride[i] = (uint32_t)(ld * es);
+        } else {
+          src.p[i] = base + ((size_t)(sg.x + row) * ld + c) * es;
+          src.stride[i] = (uint32_t)(KR * ld * es);
+        }
+      }
+    }
+  }
+  template <int L>
+  MOE_DEV void issue(const SrcT<L>& src, int ks, uint32_t lds) const {
+    const int lane = threadIdx.x & 63, wave = uniform_int(Pp::wave_id());
+    const char* zero = reinterpret_cast<const char*>(g_zero_row) + (lane << 4);
+    const bool gather = a.gather != nullptr;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int si = i * Pp::NW + wave;
+      const char* q;
+      int row;
+      if (i < LA) {
+        row = Pp::template km_slot_row<Pp::PA>(si, lane);
+        q = src.p[i] + (size_t)ks * src.stride[i];
+      } else {
+        constexpr int RPS = 1024 / Pp::PB, LPR = Pp::PB / 16;  // rows per slot, lanes per row
+        const int ls = si - LA * Pp::NW;
+        row = Pp::template km_slot_row<Pp::PB>(ls, lane);
+        if (gather) {  // the slot's RPS rows: scalar loads of their source rows
+          const int first = uniform_int(src.k0 + ks * KR + ls * RPS), last = uniform_int(a.ngather) - 1;
+          int gi = 0;
+#pragma unroll
+          for (int j = 0; j < RPS; ++j) {
+            const int v = scalar_load(a.gather, min(first + j, last));
+            gi = lane / LPR == j ? v : gi;
+          }
+          q = src.p[i] + (size_t)gi * src.stride[i];
+        } else {
+          q = src.p[i] + (size_t)ks * src.stride[i];
+        }
+      }
+      if (ks * KR + row >= src.n) q = zero;
+      lds_dma16(q, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
+    }
+  }
+  MOE_DEV void epilogue(const Tile& t, const typename Pp::Acc& acc) const {
+    Pp::template epilogue<EPI_F32>(acc, t.rows, t.nt * Pp::BN, a.N, a.out + (size_t)t.sel * a.M * a.N, a.N,
+                                   (size_t)t.row0, nullptr);
+  }
+};
+
+template <class Pp>
+__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_wgrad_km(const WgradKmArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
-  WgradProb<Pp> prob{args};
+  WgradKmProb<Pp> prob{args};
   stream_var<Pp>(prob, smem);
 }
 
@@ -1008,6 +1276,12 @@ template <bool BF16>
 using DensePipe = Pipe<MOE_DENSE_CFG, BF16>;
 template <bool BF16>
 using ExpertPipe = Pipe<MOE_EXPERT_CFG, BF16>;
+template <bool BF16>
+using WgradKmPipe = Pipe<MOE_DENSE_CFG, BF16, 3>;
+template <bool BF16>
+using DgradPipe = Pipe<MOE_DENSE_CFG, BF16, 2>;
+template <bool BF16>
+using DgradExpertPipe = Pipe<MOE_EXPERT_CFG, BF16, 2>;
 // MXFP8 experts: one 128-element K step (128 bytes) per stage
 using ExpertMxPipe = Pipe<kExpertBM, 256, 1, 4, 2, 128, 2, true>;
 constexpr int kCUs = 256;
@@ -1223,13 +1497,8 @@ hipError_t launch_dense_nt(const Dims& D, int tag, const void* A, int lda_bytes,
     g.col_off = nullptr;
     a.total_ntiles += g.ntiles;
   }
-  switch (tag) {
-    case 3: return launch_dense_any<3>(D, a, s);
-    case 4: return launch_dense_any<4>(D, a, s);
-    case 5: return launch_dense_any<5>(D, a, s);
-    case 6: return launch_dense_any<6>(D, a, s);
-    default: return launch_dense_any<7>(D, a, s);
-  }
+  if (tag != 3) return hipErrorInvalidValue;
+  return launch_dense_any<3>(D, a, s);
 }
 
 hipError_t launch_expert_nt(const Dims& D, const void* A, int lda_bytes, const int32_t* gather, const void* W,
@@ -1255,30 +1524,161 @@ hipError_t launch_expert_nt(const Dims& D, const void* A, int lda_bytes, const i
   return launch_expert<EPI_STORE>(D, a, T, s);
 }
 
-hipError_t launch_wgrad(const Dims& D, const void* A, const void* B, const int32_t* koff, int M, int N, float* out,
-                        hipStream_t s, int nseg, long long lda, long long ldb) {
-  constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN;
-  WgradArgs a{};
+// K pieces -> stage boundaries; false if a piece is not whole stages or is
+// malformed.  K is counted in 64-value units so that bf16 and fp32 agree.
+static bool dgrad_pieces(const Dims& D, const KPiece* pc, int npiece, DgradArgs& a, DgradSeg& g) {
+  const int kr = DgradPipe<true>::RB / esz(D), ce = 16 / esz(D);
+  if (npiece < 1 || npiece > 4) return false;
+  int st = 0;
+  for (int j = 0; j < 4; ++j) {
+    if (j < npiece) {
+      if (pc[j].span <= 0 || pc[j].span % 64 || pc[j].rows < 0 || pc[j].rows > pc[j].span || !pc[j].B ||
+          pc[j].ldb % ce || ((uintptr_t)pc[j].B & 15))
+        return false;
+      a.st[j] = st;
+      a.rows[j] = pc[j].rows;
+      g.B[j] = static_cast<const char*>(pc[j].B);
+      g.ldb[j] = pc[j].ldb;
+      st += pc[j].span / kr;
+    } else {
+      a.st[j] = st;
+      a.rows[j] = 0;
+      g.B[j] = static_cast<const char*>(pc[0].B);
+      g.ldb[j] = pc[0].ldb;
+    }
+  }
+  a.st[4] = st;
+  a.npiece = npiece;
+  return true;
+}
+
+template <bool EXPERT, int TAG>
+static hipError_t launch_dgrad_any(const Dims& D, const DgradArgs& a, long long tiles, hipStream_t s) {
+  if (tiles == 0) return hipSuccess;
+  if (EXPERT) {
+    if (D.bf16)
+      hipLaunchKernelGGL((k_gemm_dgrad<DgradExpertPipe<true>, true, TAG>),
+                         dim3(persistent_grid(tiles, DgradExpertPipe<true>::BPC)), dim3(DgradExpertPipe<true>::THREADS),
+                         0, s, a);
+    else
+      hipLaunchKernelGGL((k_gemm_dgrad<DgradExpertPipe<false>, true, TAG>),
+                         dim3(persistent_grid(tiles, DgradExpertPipe<false>::BPC)),
+                         dim3(DgradExpertPipe<false>::THREADS), 0, s, a);
+  } else {
+    if (D.bf16)
+      hipLaunchKernelGGL((k_gemm_dgrad<DgradPipe<true>, false, TAG>), dim3(persistent_grid(tiles, DgradPipe<true>::BPC)),
+                         dim3(DgradPipe<true>::THREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_gemm_dgrad<DgradPipe<false>, false, TAG>),
+                         dim3(persistent_grid(tiles, DgradPipe<false>::BPC)), dim3(DgradPipe<false>::THREADS), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dgrad_dense(const Dims& D, int tag, const void* A, int lda_bytes, int M, const DgradSegSpec* segs,
+                              int nseg, int npiece, hipStream_t s) {
+  constexpr int BM = DgradPipe<true>::BM, BN = DgradPipe<true>::BN;
+  if (nseg < 1 || nseg > 2 || !A || lda_bytes % 16 || ((uintptr_t)A & 15)) return hipErrorInvalidValue;
+  if (M == 0) return hipSuccess;
+  DgradArgs a{};
   a.A = static_cast<const char*>(A);
-  a.B = static_cast<const char*>(B);
-  a.koff = koff;
-  a.lda = lda;
-  a.ldb = ldb;
-  a.es = esz(D);
+  a.lda_bytes = lda_bytes;
   a.M = M;
-  a.N = N;
-  a.MT = (M + BM - 1) / BM;
-  a.NT = (N + BN - 1) / BN;
-  a.E = nseg > 0 ? nseg : D.E;
-  a.out = out;
+  a.m_tiles = (M + BM - 1) / BM;
+  a.nseg = nseg;
+  a.es = esz(D);
+  for (int i = 0; i < nseg; ++i) {
+    DgradArgs b{};
+    DgradSeg& g = a.seg[i];
+    if (!dgrad_pieces(D, segs[i].piece, npiece, b, g)) return hipErrorInvalidValue;
+    if (i == 0) {
+      std::memcpy(a.st, b.st, sizeof a.st);
+      std::memcpy(a.rows, b.rows, sizeof a.rows);
+      a.npiece = b.npiece;
+    } else if (std::memcmp(a.st, b.st, sizeof a.st) || std::memcmp(a.rows, b.rows, sizeof a.rows)) {
+      return hipErrorInvalidValue;  // segments share the K structure
+    }
+    if (segs[i].N <= 0 || (segs[i].kind != EPI_F32 && segs[i].kind != EPI_STORE) || !segs[i].out)
+      return hipErrorInvalidValue;
+    g.N = segs[i].N;
+    g.ntiles = (segs[i].N + BN - 1) / BN;
+    g.kind = segs[i].kind;
+    g.out = segs[i].out;
+    g.ldo = segs[i].ldo;
+    a.total_ntiles += g.ntiles;
+  }
+  if ((long long)a.st[4] * DgradPipe<true>::RB > lda_bytes) return hipErrorInvalidValue;  // A rows hold all of K
+  const long long tiles = (long long)a.m_tiles * a.total_ntiles;
+  switch (tag) {
+    case 4: return launch_dgrad_any<false, 4>(D, a, tiles, s);
+    default: return launch_dgrad_any<false, 5>(D, a, tiles, s);
+  }
+}
+
+hipError_t launch_dgrad_expert(const Dims& D, int tag, const void* A, int lda_bytes, const KPiece* pieces, int npiece,
+                               size_t b_expert_bytes, int N, const int2* tile_info, const int32_t* n_mtiles, int T,
+                               void* out, int ldo, hipStream_t s) {
+  constexpr int BN = DgradExpertPipe<true>::BN;
+  if (!A || lda_bytes % 16 || ((uintptr_t)A & 15) || N <= 0 || !out || b_expert_bytes % 16) return hipErrorInvalidValue;
+  DgradArgs a{};
+  a.A = static_cast<const char*>(A);
+  a.lda_bytes = lda_bytes;
+  a.es = esz(D);
+  DgradSeg& g = a.seg[0];
+  if (!dgrad_pieces(D, pieces, npiece, a, g)) return hipErrorInvalidValue;
+  if ((long long)a.st[4] * DgradExpertPipe<true>::RB > lda_bytes) return hipErrorInvalidValue;
+  g.N = N;
+  g.ntiles = (N + BN - 1) / BN;
+  g.kind = EPI_STORE;
+  g.out = out;
+  g.ldo = ldo;
+  a.nseg = 1;
+  a.tile_info = tile_info;
+  a.n_mtiles = n_mtiles;
+  a.b_expert_bytes = b_expert_bytes;
+  const long long tiles = (long long)expert_max_mtiles(T, D.k, D.E) * g.ntiles;
+  switch (tag) {
+    case 8: return launch_dgrad_any<true, 8>(D, a, tiles, s);
+    default: return launch_dgrad_any<true, 9>(D, a, tiles, s);
+  }
+}
+
+hipError_t launch_wgrad_km(const Dims& D, const WgradKmSpec& w, hipStream_t s) {
+  constexpr int BM = WgradKmPipe<true>::BM, BN = WgradKmPipe<true>::BN;
+  const int es = esz(D), ce = 16 / es;  // elements per 16-byte chunk
+  auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (w.M <= 0 || w.N <= 0 || w.nseg < 0 || !w.A || !w.B1 || !w.out || (w.nsplit > 0 && !w.B0) ||
+      w.nsplit < 0 || w.nsplit % ce || w.lda % ce || w.ldb0 % ce || w.ldb1 % ce || !al(w.A) || !al(w.B0) ||
+      !al(w.B1) || (!w.koff && w.kstep <= 0) || (w.gather && w.ngather <= 0))
+    return hipErrorInvalidValue;
+  WgradKmArgs a{};
+  a.A = static_cast<const char*>(w.A);
+  a.B[0] = static_cast<const char*>(w.nsplit > 0 ? w.B0 : w.B1);
+  a.B[1] = static_cast<const char*>(w.B1);
+  a.lda = w.lda;
+  a.ldb[0] = w.nsplit > 0 ? w.ldb0 : w.ldb1;
+  a.ldb[1] = w.ldb1;
+  a.koff = w.koff;
+  a.gather = w.gather;
+  a.kstep = w.kstep;
+  a.kend = w.kend;
+  a.ngather = w.ngather;
+  a.nsplit = w.nsplit;
+  a.es = es;
+  a.M = w.M;
+  a.N = w.N;
+  a.MT = (w.M + BM - 1) / BM;
+  a.NT = (w.N + BN - 1) / BN;
+  a.E = w.nseg;
+  a.out = w.out;
   const long long tiles = (long long)a.E * a.MT * a.NT;
   if (tiles == 0) return hipSuccess;
   if (D.bf16)
-    hipLaunchKernelGGL(k_gemm_wgrad<DensePipe<true>>, dim3(persistent_grid(tiles, DensePipe<true>::BPC)),
-                       dim3(DensePipe<true>::THREADS), 0, s, a);
+    hipLaunchKernelGGL(k_gemm_wgrad_km<WgradKmPipe<true>>, dim3(persistent_grid(tiles, WgradKmPipe<true>::BPC)),
+                       dim3(WgradKmPipe<true>::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL(k_gemm_wgrad<DensePipe<false>>, dim3(persistent_grid(tiles, DensePipe<false>::BPC)),
-                       dim3(DensePipe<false>::THREADS), 0, s, a);
+    hipLaunchKernelGGL(k_gemm_wgrad_km<WgradKmPipe<false>>, dim3(persistent_grid(tiles, WgradKmPipe<false>::BPC)),
+                       dim3(WgradKmPipe<false>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

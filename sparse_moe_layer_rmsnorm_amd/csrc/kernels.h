@@ -89,7 +89,7 @@ struct DenseSegSpec {
   int ldo;
 };
 // Dense C = A B^T, A [M, K] (lda bytes), up to 3 column segments sharing
-// ldb; K_bytes a multiple of the stage row (128 B).  `tag` (3..7) only names
+// ldb; K_bytes a multiple of the stage row (128 B).  `tag` (3) only names
 // the launch for profiles.
 hipError_t launch_dense_nt(const Dims& D, int tag, const void* A, int lda_bytes, int M, int K_bytes,
                            const DenseSegSpec* segs, int nseg, int ldb_bytes, hipStream_t s);
@@ -99,16 +99,53 @@ hipError_t launch_dense_nt(const Dims& D, int tag, const void* A, int lda_bytes,
 hipError_t launch_expert_nt(const Dims& D, const void* A, int lda_bytes, const int32_t* gather, const void* W,
                             size_t w_expert_bytes, int ldb_bytes, int N, int K_bytes, const int2* tile_info,
                             const int32_t* n_mtiles, int T, void* out, int ldo, hipStream_t s);
-// Per-expert fp32 C_e [M, N] = A_e B_e^T, K = pad_e = koff[e+1] - koff[e]:
-// A_e is the block [M, pad_e] at element koff[e] * M of A, B_e [N, pad_e] at
-// koff[e] * N of B (the segment layout of launch_transpose).
-// With nseg > 0 and lda, ldb > 0 (elements) instead: nseg K slices
-// koff[j] .. koff[j+1] of one product of row-major A [M, *] and B [N, *],
-// partial C_j at out + j*M*N (split K).
-hipError_t launch_wgrad(const Dims& D, const void* A, const void* B, const int32_t* koff, int M, int N, float* out,
-                        hipStream_t s, int nseg = 0, long long lda = 0, long long ldb = 0);
-// koff[j] = min(j * step, total) for j <= n (split-K boundaries).
-hipError_t launch_fill_koff(int32_t* koff, int n, int step, int total, hipStream_t s);
+// Weight gradients C_e = A_e^T B_e over segments e of the token axis, A and
+// B token-major (no transposed copies): segment e is rows [koff[e],
+// koff[e+1]) (koff null: [e kstep, (e+1) kstep)) cut at kend; B's columns
+// n < nsplit come from B0 (row stride ldb0), the rest from B1; with gather,
+// B's row k is row gather[k] of B0/B1 (gather has ngather entries).  Strides
+// and nsplit in elements, multiples of 16 bytes; C_e [M, N] fp32 at out + e M N.
+struct WgradKmSpec {
+  const void* A;
+  long long lda;
+  const void* B0;
+  long long ldb0;
+  const void* B1;
+  long long ldb1;
+  int nsplit;
+  const int32_t* koff;
+  int kstep, kend;
+  const int32_t* gather;
+  int ngather;
+  int M, N, nseg;
+  float* out;
+};
+hipError_t launch_wgrad_km(const Dims& D, const WgradKmSpec& w, hipStream_t s);
+// Data gradients C = A B with B K-major (weights as stored, read along their
+// input index).  K is a concatenation of up to 4 pieces: piece j spans `span`
+// K values (a multiple of 64) read from rows 0 .. rows-1 of B (row stride ldb
+// elements, a multiple of 16 bytes); rows rows .. span-1 count as zero.  A is
+// row-major with K contiguous (lda_bytes per row, the pieces' spans summed).
+struct KPiece {
+  const void* B;
+  long long ldb;
+  int span, rows;
+};
+struct DgradSegSpec {
+  KPiece piece[4];
+  int N, kind;  // kind 0: fp32 output, 1: output in the activation dtype
+  void* out;
+  int ldo;
+};
+// Dense: rows 0..M-1 of A, up to 2 output segments (same K pieces' spans and
+// rows, each its own sources); tag 4 or 5 names the launch in profiles.
+hipError_t launch_dgrad_dense(const Dims& D, int tag, const void* A, int lda_bytes, int M, const DgradSegSpec* segs,
+                              int nseg, int npiece, hipStream_t s);
+// Grouped expert rows (tiles of the dispatch order), B advancing by
+// b_expert_bytes per expert; output in the activation dtype; tag 8 or 9.
+hipError_t launch_dgrad_expert(const Dims& D, int tag, const void* A, int lda_bytes, const KPiece* pieces, int npiece,
+                               size_t b_expert_bytes, int N, const int2* tile_info, const int32_t* n_mtiles, int T,
+                               void* out, int ldo, hipStream_t s);
 // Sum of S fp32 partials [S, M, N] into up to 4 outputs, each a block of
 // rows (by_rows) or of columns of C: segment i covers [start_i, start_i +
 // len_i) and is stored row-major with ld_i at out_i.
@@ -119,19 +156,6 @@ struct SplitOut {
 };
 hipError_t launch_reduce_split(const float* part, int S, int M, int N, const SplitOut& o, hipStream_t s);
 
-// dst[c][col_off + p] = src[gather[colmap[p]]][c] (maps optional), 0 for
-// rows < 0 or >= R; `batch` matrices at the given strides (elements).  With
-// seg_tile, expert e's columns seg_koff[e] .. seg_koff[e+1] go to their own
-// contiguous block [C, pad_e] at element seg_koff[e] * C (ld_dst, col_off
-// unused; C and P multiples of 64).
-hipError_t launch_transpose(const Dims& D, const void* src, int R, int C, long long ld_src, long long src_bstride,
-                            const int32_t* gather, const int32_t* colmap, int P, void* dst, long long ld_dst,
-                            long long col_off, long long dst_bstride, int batch, hipStream_t s,
-                            const int32_t* seg_koff = nullptr, const int32_t* seg_tile = nullptr);
-// Padded per-expert K segments (whole 64-element stages, at least one) and
-// the map from padded column to grouped row (-1 = pad) up to Kt columns.
-hipError_t launch_pad_map(const Dims& D, const int32_t* offsets, int Kt, int32_t* koff, int32_t* colmap,
-                          int32_t* seg_tile, hipStream_t s);
 hipError_t launch_glu_bwd(const Dims& D, const void* P, const void* Q, const void* dG, long long R, int n, void* dP,
                           void* dQ, int ldo, hipStream_t s);
 hipError_t launch_combine_bwd(const Dims& D, const void* dy, const void* Y, const float* gates, const int32_t* inv,

@@ -241,9 +241,9 @@ moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s, co
 
 // ----------------------------------------------------------------- backward --
 struct BwdLayout {
-  size_t Bop1, Bop2, WdT, WguT, P, Q, dG, dy, dAcat, dg, dY, dH, Apre, U, dAU, dX, dh, rstd, gpart;
-  size_t doutT, GyT, dAcatT, hT, dYT, HT, dAUT, XT, dWcat, ksplit, koff, colmap, seg_tile, total;
-  int Tp, Kt, Epad, Kc;
+  size_t P, Q, dG, dy, dAcat, dg, dY, dH, Apre, U, dAU, dX, dh, rstd, gpart;
+  size_t dWcat, total;
+  int Tp, Epad, Kc;
 };
 constexpr int kGammaSlices = 64;
 constexpr int kSplitOut = 3, kSplitCat = 3;  // K slices of the two dense weight-gradient products (144 and 304 output tiles at the replica shape: 3 slices fill 512 block slots best)
@@ -253,20 +253,15 @@ void bwd_layout(const moe_config* c, int64_t T, BwdLayout* L) {
   const size_t t = (size_t)T, E = (size_t)c->E, k = (size_t)c->k, d = c->d, l = c->l, f = c->f, fs = c->f_s;
   const size_t Tk = t * k;
   L->Tp = (int)((t + 63) / 64 * 64);
-  L->Kt = (int)((Tk + 64 * E + 63) / 64 * 64);
   L->Epad = (int)((E + 63) / 64 * 64);
   L->Kc = (int)(2 * fs + l + (size_t)L->Epad);
-  const size_t Tp = L->Tp, Kt = L->Kt, Kc = L->Kc;
+  const size_t Kc = L->Kc;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
     o = up(o + bytes);
     return at;
   };
-  L->Bop1 = take((fs + l) * d * es);
-  L->Bop2 = take(d * Kc * es);
-  L->WdT = take(E * f * l * es);
-  L->WguT = take(E * l * 2 * f * es);
   L->P = take(t * fs * es);
   L->Q = take(t * fs * es);
   L->dG = take(t * fs * es);
@@ -282,19 +277,7 @@ void bwd_layout(const moe_config* c, int64_t T, BwdLayout* L) {
   L->dh = take(t * d * 4);
   L->rstd = take(t * 4);
   L->gpart = take((size_t)kGammaSlices * d * 4);
-  L->doutT = take(d * Tp * es);
-  L->GyT = take((fs + l) * Tp * es);
-  L->dAcatT = take(Kc * Tp * es);
-  L->hT = take(d * Tp * es);
-  L->dYT = take(l * Kt * es);
-  L->HT = take(f * Kt * es);
-  L->dAUT = take(2 * f * Kt * es);
-  L->XT = take(l * Kt * es);
   L->dWcat = take(std::max((size_t)kSplitOut * d * (fs + l), (size_t)kSplitCat * Kc * d) * 4);  // split-K partials
-  L->ksplit = take(16 * 4);
-  L->koff = take((E + 1) * 4);
-  L->colmap = take(Kt * 4);
-  L->seg_tile = take(Kt / 64 * 4);
   L->total = o;
 }
 
@@ -498,7 +481,7 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   const Dims& D = ctx->D;
   const int t = (int)T, E = c.E, k = c.k, d = c.d, l = c.l, f = c.f, fs = c.f_s;
   const int es = c.dtype == MOE_BF16 ? 2 : 4;
-  const int Tk = t * k, Tp = B.Tp, Kt = B.Kt, Kc = B.Kc, Epad = B.Epad;
+  const int Tk = t * k, Tp = B.Tp, Kc = B.Kc, Epad = B.Epad;
   moe_ws_layout L;
   ws_layout(&c, T, &L);
   char* fw = static_cast<char*>(const_cast<void*>(fwd_ws));
@@ -507,49 +490,24 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   const int32_t* n_mtiles = p.tile_offsets + E;
   char* w = static_cast<char*>(ws);
   auto at = [&](size_t off) { return static_cast<void*>(w + off); };
-  void *Bop1 = at(B.Bop1), *Bop2 = at(B.Bop2), *WdT = at(B.WdT), *WguT = at(B.WguT), *P = at(B.P), *Q = at(B.Q);
+  void *P = at(B.P), *Q = at(B.Q);
   void *dG = at(B.dG), *dy = at(B.dy), *dAcat = at(B.dAcat), *dY = at(B.dY), *dH = at(B.dH), *Apre = at(B.Apre);
-  void *U = at(B.U), *dAU = at(B.dAU), *dX = at(B.dX), *doutT = at(B.doutT), *GyT = at(B.GyT);
-  void *dAcatT = at(B.dAcatT), *hT = at(B.hT), *dYT = at(B.dYT), *HT = at(B.HT), *dAUT = at(B.dAUT), *XT = at(B.XT);
+  void *U = at(B.U), *dAU = at(B.dAU), *dX = at(B.dX);
   float* dg = static_cast<float*>(at(B.dg));
   float* dh = static_cast<float*>(at(B.dh));
   float* dWcat = static_cast<float*>(at(B.dWcat));
-  int32_t* koff = static_cast<int32_t*>(at(B.koff));
-  int32_t* colmap = static_cast<int32_t*>(at(B.colmap));
-  int32_t* seg_tile = static_cast<int32_t*>(at(B.seg_tile));
   auto el = [&](const void* base, size_t elems) { return static_cast<const char*>(base) + elems * es; };
   auto elw = [&](void* base, size_t elems) { return static_cast<char*>(base) + elems * es; };
   const moe_weights& W = ctx->w;
 
-  // weight operands of the data-gradient products, K-contiguous
-  MOE_RUN(MOE_K_BWD_TRANSPOSE, [&]() -> hipError_t {
-    hipError_t e = hipSuccess;
-    if (fs > 0) e = launch_transpose(D, W.W_sd, d, fs, fs, 0, nullptr, nullptr, d, Bop1, d, 0, 0, 1, s);  // W_sd^T
-    if (e == hipSuccess)
-      e = launch_transpose(D, W.W_up, d, l, l, 0, nullptr, nullptr, d, elw(Bop1, (size_t)fs * d), d, 0, 0, 1, s);
-    if (e == hipSuccess && fs > 0) e = launch_transpose(D, W.W_sg, fs, d, d, 0, nullptr, nullptr, fs, Bop2, Kc, 0, 0, 1, s);
-    if (e == hipSuccess && fs > 0)
-      e = launch_transpose(D, W.W_su, fs, d, d, 0, nullptr, nullptr, fs, Bop2, Kc, fs, 0, 1, s);
-    if (e == hipSuccess) e = launch_transpose(D, W.W_dn, l, d, d, 0, nullptr, nullptr, l, Bop2, Kc, 2 * fs, 0, 1, s);
-    if (e == hipSuccess)
-      e = launch_transpose(D, W.W_r, E, d, d, 0, nullptr, nullptr, Epad, Bop2, Kc, 2 * fs + l, 0, 1, s);
-    if (e == hipSuccess)  // W_d[e] [l,f] -> [f,l]
-      e = launch_transpose(D, W.W_d, l, f, f, (long long)l * f, nullptr, nullptr, l, WdT, l, 0, (long long)f * l, E, s);
-    if (e == hipSuccess)  // W_g[e], W_u[e] [f,l] -> [l, 2f] = [W_g^T | W_u^T]
-      e = launch_transpose(D, W.W_g, f, l, l, (long long)f * l, nullptr, nullptr, f, WguT, 2 * f, 0,
-                           (long long)l * 2 * f, E, s);
-    if (e == hipSuccess)
-      e = launch_transpose(D, W.W_u, f, l, l, (long long)f * l, nullptr, nullptr, f, WguT, 2 * f, f,
-                           (long long)l * 2 * f, E, s);
-    return e;
-  }());
+  // Data-gradient products read the weights as stored (K-major B operands).
   // output projections: [dG | dy_lat] = dout [W_sd | W_up]
   {
-    DenseSegSpec sg[2];
+    DgradSegSpec sg[2] = {};
     int n = 0;
-    if (fs > 0) sg[n++] = {Bop1, fs, 1, dG, fs};
-    sg[n++] = {el(Bop1, (size_t)fs * d), l, 1, dy, l};
-    MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 4, dout, d * es, t, d * es, sg, n, d * es, s));
+    if (fs > 0) sg[n++] = {{{W.W_sd, fs, d, d}}, fs, 1, dG, fs};
+    sg[n++] = {{{W.W_up, l, d, d}}, l, 1, dy, l};
+    MOE_RUN(MOE_K_BWD_GEMM, launch_dgrad_dense(D, 4, dout, d * es, t, sg, n, 1, s));
   }
   if (fs > 0) {  // shared GLU: recompute P, Q; dP, dQ into the first 2 f_s columns of dAcat
     DenseSegSpec sg[2] = {{W.W_sg, fs, 1, P, fs}, {W.W_su, fs, 1, Q, fs}};
@@ -560,37 +518,46 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   MOE_RUN(MOE_K_BWD_ELTWISE, launch_combine_bwd(D, dy, Y, p.gates, p.inv, t, dY, dg, s));
   // experts: dH = dY W_d; recompute A = X W_g^T, U = X W_u^T; GLU derivative; dX = [dA|dU] [W_g; W_u]
   const size_t wfl = (size_t)f * l * es;
-  MOE_RUN(MOE_K_BWD_EXPERT,
-          launch_expert_nt(D, dY, l * es, nullptr, WdT, wfl, l * es, f, l * es, p.tile_info, n_mtiles, t, dH, f, s));
+  {
+    const KPiece wd[1] = {{W.W_d, f, l, l}};  // W_d[e] [l, f]: K = l
+    MOE_RUN(MOE_K_BWD_EXPERT,
+            launch_dgrad_expert(D, 8, dY, l * es, wd, 1, wfl, f, p.tile_info, n_mtiles, t, dH, f, s));
+  }
   MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, z, l * es, p.perm_src, W.W_g, wfl, l * es, f, l * es, p.tile_info,
                                              n_mtiles, t, Apre, f, s));
   MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, z, l * es, p.perm_src, W.W_u, wfl, l * es, f, l * es, p.tile_info,
                                              n_mtiles, t, U, f, s));
   MOE_RUN(MOE_K_BWD_ELTWISE, launch_glu_bwd(D, Apre, U, dH, Tk, f, dAU, elw(dAU, f), 2 * f, s));
-  MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, dAU, 2 * f * es, nullptr, WguT, wfl * 2, 2 * f * es, l, 2 * f * es,
-                                             p.tile_info, n_mtiles, t, dX, l, s));
+  {
+    const KPiece wgu[2] = {{W.W_g, l, f, f}, {W.W_u, l, f, f}};  // [W_g[e]; W_u[e]] [2f, l]: K = 2f
+    MOE_RUN(MOE_K_BWD_EXPERT,
+            launch_dgrad_expert(D, 9, dAU, 2 * f * es, wgu, 2, wfl, l, p.tile_info, n_mtiles, t, dX, l, s));
+  }
   // dispatch transpose and router: dz and dl into their columns of dAcat
   MOE_RUN(MOE_K_BWD_ELTWISE, launch_dispatch_bwd(D, dX, p.inv, t, elw(dAcat, 2 * fs), Kc, s));
   MOE_RUN(MOE_K_BWD_ELTWISE, launch_gates_bwd(D, p.logits, p.idx, dg, t, Epad, elw(dAcat, 2 * fs + l), Kc, s));
   // dh = [dP | dQ | dz | dl] [W_sg; W_su; W_dn; W_r], then RMSNorm
   {
-    DenseSegSpec sg[1] = {{Bop2, d, 0, dh, d}};
-    MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 5, dAcat, Kc * es, t, Kc * es, sg, 1, Kc * es, s));
+    DgradSegSpec sg = {};
+    int np = 0;
+    if (fs > 0) {
+      sg.piece[np++] = {W.W_sg, d, fs, fs};
+      sg.piece[np++] = {W.W_su, d, fs, fs};
+    }
+    sg.piece[np++] = {W.W_dn, d, l, l};
+    sg.piece[np++] = {W.W_r, d, Epad, E};  // pad rows of W_r count as zero
+    sg.N = d;
+    sg.kind = 0;
+    sg.out = dh;
+    sg.ldo = d;
+    MOE_RUN(MOE_K_BWD_GEMM, launch_dgrad_dense(D, 5, dAcat, Kc * es, t, &sg, 1, np, s));
   }
   MOE_RUN(MOE_K_BWD_ELTWISE, launch_rmsnorm_bwd(D, x, W.gamma, dh, t, dx, static_cast<float*>(at(B.rstd)),
                                                 static_cast<float*>(at(B.gpart)), kGammaSlices, g->gamma, s));
-  // weight gradients of the dense products: K = tokens (padded to Tp with zeros)
-  MOE_RUN(MOE_K_BWD_TRANSPOSE, [&]() -> hipError_t {
-    hipError_t e = launch_transpose(D, dout, t, d, d, 0, nullptr, nullptr, Tp, doutT, Tp, 0, 0, 1, s);
-    if (e == hipSuccess && fs > 0) e = launch_transpose(D, G, t, fs, fs, 0, nullptr, nullptr, Tp, GyT, Tp, 0, 0, 1, s);
-    if (e == hipSuccess)
-      e = launch_transpose(D, y_lat, t, l, l, 0, nullptr, nullptr, Tp, elw(GyT, (size_t)fs * Tp), Tp, 0, 0, 1, s);
-    if (e == hipSuccess) e = launch_transpose(D, dAcat, t, Kc, Kc, 0, nullptr, nullptr, Tp, dAcatT, Tp, 0, 0, 1, s);
-    if (e == hipSuccess) e = launch_transpose(D, h, t, d, d, 0, nullptr, nullptr, Tp, hT, Tp, 0, 0, 1, s);
-    return e;
-  }());
   // Dense weight gradients, K = tokens split in slices (few output tiles:
-  // d x (f_s + l) and (2 f_s + l + Epad) x d), partials summed into the outputs.
+  // d x (f_s + l) and (2 f_s + l + Epad) x d), partials summed into the
+  // outputs.  All weight-gradient products read their token-major operands
+  // as stored (K-major tiles), so nothing is transposed.
   {
     const int u = Tp / 64;
     auto slices = [&](int want, int* step) {
@@ -600,13 +567,10 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
     };
     int step_o, step_c;
     const int S_o = slices(kSplitOut, &step_o), S_c = slices(kSplitCat, &step_c);
-    int32_t* ko = static_cast<int32_t*>(at(B.ksplit));
-    int32_t* kc = ko + 8;
     auto dense_wgrad = [&]() -> hipError_t {
-      hipError_t e = launch_fill_koff(ko, S_o, step_o, Tp, s);
-      if (e == hipSuccess) e = launch_fill_koff(kc, S_c, step_c, Tp, s);
-      if (e == hipSuccess)  // [dW_sd | dW_up] = dout^T [G | y_lat]
-        e = launch_wgrad(D, doutT, GyT, ko, d, fs + l, dWcat, s, S_o, Tp, Tp);
+      // [dW_sd | dW_up] = dout^T [G | y_lat]
+      WgradKmSpec wo{dout, d, G, fs, y_lat, l, fs, nullptr, step_o, t, nullptr, 0, d, fs + l, S_o, dWcat};
+      hipError_t e = launch_wgrad_km(D, wo, s);
       SplitOut o{};
       o.by_rows = 0;
       auto addc = [&](int start, int len, float* out) {
@@ -619,8 +583,9 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
       if (fs > 0) addc(0, fs, g->W_sd);
       addc(fs, l, g->W_up);
       if (e == hipSuccess) e = launch_reduce_split(dWcat, S_o, d, fs + l, o, s);
-      if (e == hipSuccess)  // [dW_sg; dW_su; dW_dn; dW_r] = dA_cat^T h
-        e = launch_wgrad(D, dAcatT, hT, kc, Kc, d, dWcat, s, S_c, Tp, Tp);
+      // [dW_sg; dW_su; dW_dn; dW_r] = dA_cat^T h
+      WgradKmSpec wc{dAcat, Kc, nullptr, 0, h, d, 0, nullptr, step_c, t, nullptr, 0, Kc, d, S_c, dWcat};
+      if (e == hipSuccess) e = launch_wgrad_km(D, wc, s);
       SplitOut c{};
       c.by_rows = 1;
       auto add = [&](int start, int len, float* out) {
@@ -641,25 +606,17 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
     };
     MOE_RUN(MOE_K_BWD_WGRAD, dense_wgrad());
   }
-  // per-expert weight gradients: K = the expert's rows, padded segments
-  MOE_RUN(MOE_K_BWD_TRANSPOSE, [&]() -> hipError_t {
-    // per-expert blocks: dY_e^T [l, pad_e], H_e^T [f, pad_e], dA_e^T, dU_e^T [f, pad_e], X_e^T [l, pad_e]
-    hipError_t e = launch_pad_map(D, p.offsets, Kt, koff, colmap, seg_tile, s);
-    if (e == hipSuccess) e = launch_transpose(D, dY, Tk, l, l, 0, nullptr, colmap, Kt, dYT, 0, 0, 0, 1, s, koff, seg_tile);
-    if (e == hipSuccess) e = launch_transpose(D, H, Tk, f, f, 0, nullptr, colmap, Kt, HT, 0, 0, 0, 1, s, koff, seg_tile);
-    if (e == hipSuccess)
-      e = launch_transpose(D, dAU, Tk, f, 2 * f, 0, nullptr, colmap, Kt, dAUT, 0, 0, 0, 1, s, koff, seg_tile);
-    if (e == hipSuccess)
-      e = launch_transpose(D, el(dAU, f), Tk, f, 2 * f, 0, nullptr, colmap, Kt, elw(dAUT, (size_t)f * Kt), 0, 0, 0,
-                           1, s, koff, seg_tile);
-    if (e == hipSuccess)
-      e = launch_transpose(D, z, Tk, l, l, 0, p.perm_src, colmap, Kt, XT, 0, 0, 0, 1, s, koff, seg_tile);
-    return e;
-  }());
-  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, dYT, HT, koff, l, f, g->W_d, s));
-  // dW_g[e] = dA_e^T X_e and dW_u[e] = dU_e^T X_e
-  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, dAUT, XT, koff, f, l, g->W_g, s));
-  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad(D, el(dAUT, (size_t)f * Kt), XT, koff, f, l, g->W_u, s));
+  // per-expert weight gradients, K = the expert's rows of the dispatch order
+  // dW_d[e] = dY_e^T H_e
+  const WgradKmSpec wd{dY, l, nullptr, 0, H, f, 0, p.offsets, 0, Tk, nullptr, 0, l, f, E, g->W_d};
+  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad_km(D, wd, s));
+  // dW_g[e] = dA_e^T X_e and dW_u[e] = dU_e^T X_e, X_e's rows gathered from z
+  const WgradKmSpec wg{dAU, 2 * f, nullptr, 0, z, l, 0, p.offsets, 0, Tk, p.perm_src, Tk, f, l, E, g->W_g};
+  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad_km(D, wg, s));
+  WgradKmSpec wu = wg;
+  wu.A = el(dAU, f);
+  wu.out = g->W_u;
+  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad_km(D, wu, s));
   return MOE_OK;
 }
 

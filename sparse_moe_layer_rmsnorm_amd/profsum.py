@@ -16,12 +16,13 @@ figure only while the sources still hash the same).
 The dense GEMM launches carry a tag template argument: 0 the h GEMM of a
 forward (gemm_h), 1 router logits alone (gemm_rz, routing-only pass), 2 the
 output GEMM (gemm_out).
-Tags 3-7 are the backward's dense products (recomputed shared GLU
-pre-activations, output-projection transposes, dh, the fused dW of the
-h-side weights, dW_sd | dW_up).  The grouped expert GEMM with the GLU
-epilogue is expert_up, the other expert_down (the backward's grouped products
-use that same kernel and are counted there); k_gemm_wgrad is the per-expert
-weight-gradient GEMM.
+Tag 3 is the backward's recomputation of the shared GLU pre-activations
+(bwd_pq).  The grouped expert GEMM with the GLU epilogue is expert_up, the
+other expert_down (the backward's recomputation of the expert pre-activations
+uses that same kernel and is counted there).  The backward's data-gradient
+products with K-major weights carry tags too: 4 dout against [W_sd | W_up]
+(bwd_dout), 5 dh (bwd_dh), 8 the experts' dH (bwd_dH), 9 their dX (bwd_dX);
+k_gemm_wgrad_km is the weight-gradient GEMM (bwd_wgrad, dense and per expert).
 """
 from __future__ import annotations
 
@@ -50,14 +51,17 @@ def logical_name(symbol: str, dense_seen: int) -> str | None:
         tag = symbol.split(">, ")[-1].split(">")[0].strip()
         return {"0": "gemm_h", "1": "gemm_rz", "2": "gemm_out", "3": "bwd_pq", "4": "bwd_dout", "5": "bwd_dh",
                 "6": "bwd_wcat", "7": "bwd_wout"}.get(tag, "gemm_dense")
+    if "k_gemm_dgrad" in symbol:
+        tag = symbol.split(">(")[0].rsplit(",", 1)[-1].strip()
+        return {"4": "bwd_dout", "5": "bwd_dh", "8": "bwd_dH", "9": "bwd_dX"}.get(tag, "bwd_dgrad")
     if "k_gemm_wgrad" in symbol:
         return "bwd_wgrad"
     if "k_gemm_expert" in symbol:
         return "expert_up" if symbol.rstrip().endswith("2>(moe::(anonymous namespace)::ExpertArgs)") else "expert_down"
     if "k_gemm_expert_mx" in symbol:
         return "expert_up" if "Li2EEEv" in symbol else "expert_down"
-    for k in ("rmsnorm_bwd", "dgamma_part", "sum_slices", "transpose", "pad_map", "glu_bwd", "combine_bwd",
-              "dispatch_bwd", "gates_bwd", "mx_quant", "reduce_split", "fill_koff"):
+    for k in ("rmsnorm_bwd", "dgamma_part", "sum_slices", "glu_bwd", "combine_bwd", "dispatch_bwd", "gates_bwd",
+              "mx_quant", "reduce_split"):
         if f"k_{k}" in symbol:
             return k
     for k in ("rmsnorm", "topk", "hist", "scan_local", "scan_global", "scatter", "combine", "qb_update",
