@@ -66,16 +66,17 @@ def kernel_work(s, T: int) -> dict:
     return {"flops": flops, "bytes": bytes_}
 
 
-def backward_flops(s, T: int) -> dict:
+def backward_flops(s, T: int, keep: bool = False) -> dict:
     """GEMM FLOPs of one backward pass per launch group (0: memory-bound
-    groups): the dense products (shared pre-activations recomputed, the
-    output-projection transposes, dh), the grouped expert products (dH, A and
-    U recomputed, dX) and the weight gradients (per expert, and the two dense
-    ones split along the tokens)."""
+    groups): the dense products (shared pre-activations recomputed unless the
+    forward kept them, the output-projection transposes, dh), the grouped
+    expert products (dH, A and U recomputed unless kept, dX) and the weight
+    gradients (per expert, and the two dense ones split along the tokens)."""
     Tk = T * s.k
     Kc = 2 * s.f_s + s.l + (s.E + 63) // 64 * 64
-    dense = 2.0 * T * s.d * (2 * s.f_s) + 2.0 * T * s.d * (s.f_s + s.l) + 2.0 * T * Kc * s.d
-    expert = 2.0 * Tk * s.l * s.f * 3 + 2.0 * Tk * 2 * s.f * s.l
+    rec = 0 if keep else 1
+    dense = rec * 2.0 * T * s.d * (2 * s.f_s) + 2.0 * T * s.d * (s.f_s + s.l) + 2.0 * T * Kc * s.d
+    expert = 2.0 * Tk * s.l * s.f * (1 + 2 * rec) + 2.0 * Tk * 2 * s.f * s.l
     # weight gradients: the per-expert ones and the two split-K dense ones
     wgrad = 2.0 * Tk * s.l * s.f + 2.0 * Tk * 2 * s.f * s.l + 2.0 * s.d * T * (s.f_s + s.l) + 2.0 * Kc * T * s.d
     return {"bwd_gemm": dense, "bwd_expert": expert, "bwd_wgrad": wgrad, "bwd_eltwise": 0.0}
@@ -178,6 +179,9 @@ def main() -> int:
     ap.add_argument("--backward", action="store_true",
                     help="time the training step with the backward pass: forward, moe_backward (dx and all weight "
                          "gradients) and the bias update")
+    ap.add_argument("--keep-preact", action="store_true",
+                    help="the forward also stores the GLU pre-activations (keep_preact) and the backward reads them "
+                         "instead of recomputing them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device copy of 256 MiB (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -202,7 +206,7 @@ def main() -> int:
     c = wl.zipf_logit_offset(shape) if shape.name == "skew" else None
     frozen = shape.qb_frozen
     layer = layer_from_shape(shape, W, max_tokens=T, logit_offset=c, frozen=frozen, balancer=args.balancer,
-                             experts=args.experts)
+                             experts=args.experts, keep_preact=args.keep_preact)
     if frozen:
         layer.set_bias(wl.frozen_bias(shape))
     x = torch.from_numpy(x_np).cuda().to(layer.tdtype)
@@ -307,11 +311,11 @@ def main() -> int:
     # GEMM FLOPs of one step: the launched forward GEMMs (plus the backward's)
     layer_flops = sum(work["flops"][n] * kernels[n]["launches"] / args.steps for n in kernels if n in work["flops"])
     if args.backward:
-        layer_flops += sum(backward_flops(shape, T).values())
+        layer_flops += sum(backward_flops(shape, T, args.keep_preact).values())
 
     bwd = None
     if args.backward:
-        bf = backward_flops(shape, T)
+        bf = backward_flops(shape, T, args.keep_preact)
         bwd = {}
         for n, fl in bf.items():
             ms, cnt = prof.get(n, (0.0, 0))
@@ -340,7 +344,8 @@ def main() -> int:
         "config": {"workload": f"{shape.name}: T={T} tokens, d={shape.d}, l={shape.l}, E={shape.E}, k={shape.k}, "
                                f"f={shape.f}, f_s={shape.f_s}, B={shape.B}, QB {'frozen' if frozen else 'train'}"
                                + (", sign-rule balancer" if args.balancer == "sign" else "")
-                               + (", MXFP8 experts" if args.experts == "mxfp8" else ""),
+                               + (", MXFP8 experts" if args.experts == "mxfp8" else "")
+                               + (", GLU pre-activations kept by the forward" if args.keep_preact else ""),
                    "global_batch": T,
                    "step": "training forward + backward + qb_update" if args.backward else
                            "training forward + qb_update"},

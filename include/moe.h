@@ -104,6 +104,12 @@ typedef enum moe_expert_format { MOE_EXPERTS_BF16 = 0, MOE_EXPERTS_MXFP8 = 1 } m
  * rms_eps > 0.  routed_scale multiplies every gate (1 = plain renormalised).
  * balancer picks the update rule; sign_gamma (finite, > 0) is read only for
  * MOE_BALANCE_SIGN.  A zero-filled tail (balancer 0) selects QB.
+ * keep_preact (0 or 1; bf16 experts only): every forward also stores the
+ * GLU pre-activations -- P = h W_sg^T, Q = h W_su^T of the shared expert and
+ * A = X W_g^T, U = X W_u^T of the routed experts, in the activation dtype --
+ * in the workspace (moe_ws_layout P, Q, A, U), and moe_backward reads them
+ * instead of recomputing them (two GEMM passes fewer per training step, for
+ * 2 (T f_s + T k f) more stored elements per forward).
  */
 typedef struct moe_config {
   int32_t d, l, E, k, f, f_s;
@@ -116,6 +122,7 @@ typedef struct moe_config {
   moe_balancer balancer;
   float sign_gamma;
   moe_expert_format experts;
+  int32_t keep_preact;
 } moe_config;
 
 /* Device pointers, caller-owned, read-only to the library. */
@@ -171,6 +178,9 @@ typedef struct moe_ws_layout {
   size_t z8, zs, Xs, H8, Hs;    /* MXFP8 experts only (else zero bytes): z and H as
                                   E4M3 bytes and E8M0 scales; Xs the scale rows of
                                   the grouped rows */
+  size_t P, Q, A, U;            /* keep_preact only (else zero bytes): the GLU
+                                  pre-activations, P, Q [T, f_s], A, U [T k, f]
+                                  (grouped rows, as H) */
   size_t total;
 } moe_ws_layout;
 

@@ -31,7 +31,7 @@ class moe_config(ctypes.Structure):
     _fields_ = [("d", c_int32), ("l", c_int32), ("E", c_int32), ("k", c_int32), ("f", c_int32), ("f_s", c_int32),
                 ("dtype", c_int), ("rms_eps", c_float), ("qb_bins", c_int32), ("qb_mode", c_int),
                 ("max_tokens", c_int64), ("routed_scale", c_float), ("balancer", c_int), ("sign_gamma", c_float),
-                ("experts", c_int)]
+                ("experts", c_int), ("keep_preact", c_int32)]
 
 
 class moe_weights(ctypes.Structure):
@@ -54,7 +54,8 @@ class moe_state_layout(ctypes.Structure):
 class moe_ws_layout(ctypes.Structure):
     _fields_ = [(n, c_size_t) for n in ("h", "logits", "idx", "gates", "bitmap", "cbase", "sbase", "counts",
                                         "offsets", "tile_offsets", "perm_src", "inv", "tile_info", "G", "z", "X",
-                                        "H", "Y", "y_lat", "z8", "zs", "Xs", "H8", "Hs", "total")]
+                                        "H", "Y", "y_lat", "z8", "zs", "Xs", "H8", "Hs", "P", "Q", "A", "U",
+                                        "total")]
 
 
 _lib = None
@@ -214,9 +215,11 @@ def moe_profile_end(ctx: int) -> Dict[str, tuple]:
 
 def make_config(d: int, l: int, E: int, k: int, f: int, f_s: int, *, dtype: str = "bf16", rms_eps: float = 1e-6,
                 qb_bins: int = 256, frozen: bool = False, max_tokens: int = 1, routed_scale: float = 1.0,
-                balancer: str = "qb", sign_gamma: float = 1e-2, experts: str = "bf16") -> moe_config:
+                balancer: str = "qb", sign_gamma: float = 1e-2, experts: str = "bf16",
+                keep_preact: bool = False) -> moe_config:
     return moe_config(d=d, l=l, E=E, k=k, f=f, f_s=f_s, dtype=MOE_BF16 if dtype == "bf16" else MOE_F32,
                       rms_eps=rms_eps, qb_bins=qb_bins, qb_mode=MOE_QB_FROZEN if frozen else MOE_QB_TRAIN,
                       max_tokens=max_tokens, routed_scale=routed_scale,
                       balancer=MOE_BALANCE_SIGN if balancer == "sign" else MOE_BALANCE_QB, sign_gamma=sign_gamma,
-                      experts=MOE_EXPERTS_MXFP8 if experts == "mxfp8" else MOE_EXPERTS_BF16)
+                      experts=MOE_EXPERTS_MXFP8 if experts == "mxfp8" else MOE_EXPERTS_BF16,
+                      keep_preact=1 if keep_preact else 0)

@@ -308,9 +308,12 @@ struct Pipe {
     if (row_ok && c < N) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + orow + c) = v;
   }
 
+  // EPI_GLU with keep_g / keep_u (wave-uniform, nullable): the gate and up
+  // pre-activations are stored too, at the same place as the output.
   template <int KIND>
   MOE_DEV static void epilogue(const Acc& acc, int rows_valid, int n0, int N, void* out, int ldo, size_t row_base,
-                               const __attribute__((address_space(3))) float* col_off) {
+                               const __attribute__((address_space(3))) float* col_off, void* keep_g = nullptr,
+                               void* keep_u = nullptr) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / WN, wn = wave % WN;
     if constexpr (BF16 && KIND != EPI_F32 && NI % 4 == 0) {  // paired 16-byte stores (N is a multiple of 64)
@@ -322,14 +325,23 @@ struct Pipe {
         if constexpr (KIND == EPI_GLU) {
 #pragma unroll
           for (int p = 0; p < NI / 2; p += 2) {
-            float o[2][4];
+            float o[2][4], gk[2][4], uk[2][4];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const f32x4_t g = acc[mi][2 * (p + h)], u = acc[mi][2 * (p + h) + 1];
 #pragma unroll
-              for (int r = 0; r < 4; ++r) o[h][r] = g[r] * u[r] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[r]));
+              for (int r = 0; r < 4; ++r) {
+                o[h][r] = g[r] * u[r] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[r]));
+                gk[h][r] = g[r];
+                uk[h][r] = u[r];
+              }
             }
-            store_pair(out, orow, n0 / 2 + ((wn * WTN) / 32 + p) * 16, N, row_ok, o[0], o[1]);
+            const int c0 = n0 / 2 + ((wn * WTN) / 32 + p) * 16;
+            store_pair(out, orow, c0, N, row_ok, o[0], o[1]);
+            if (keep_g) {
+              store_pair(keep_g, orow, c0, N, row_ok, gk[0], gk[1]);
+              store_pair(keep_u, orow, c0, N, row_ok, uk[0], uk[1]);
+            }
           }
         } else {
 #pragma unroll
@@ -357,6 +369,10 @@ struct Pipe {
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[r] = g[r] * u[r] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[r]));
           store4(out, orow + c, o[0], o[1], o[2], o[3]);
+          if (keep_g) {
+            store4(keep_g, orow + c, g[0], g[1], g[2], g[3]);
+            store4(keep_u, orow + c, u[0], u[1], u[2], u[3]);
+          }
         }
       } else {
 #pragma unroll
@@ -450,6 +466,7 @@ struct DenseSeg {
   void* out;
   int ldo;
   const float* col_off;  // per-column offset (EPI_F32), at most kMaxColOff columns
+  void* keep[2];         // EPI_GLU: gate / up pre-activations also stored (nullable)
 };
 
 constexpr int kMaxColOff = 1024;
@@ -583,7 +600,8 @@ struct DenseProb {
       Pp::template epilogue<EPI_F32>(acc, t.rows, t.nt * Pp::BN, S.N, S.out, S.ldo, (size_t)t.row0,
                                      S.col_off ? col_lds : nullptr);
     else if (S.kind == EPI_GLU)
-      Pp::template epilogue<EPI_GLU>(acc, t.rows, t.nt * Pp::BN, S.N, S.out, S.ldo, (size_t)t.row0, nullptr);
+      Pp::template epilogue<EPI_GLU>(acc, t.rows, t.nt * Pp::BN, S.N, S.out, S.ldo, (size_t)t.row0, nullptr,
+                                     S.keep[0], S.keep[1]);
     else
       Pp::template epilogue<EPI_STORE>(acc, t.rows, t.nt * Pp::BN, S.N, S.out, S.ldo, (size_t)t.row0, nullptr);
   }
@@ -633,6 +651,7 @@ struct ExpertArgs {
   const int32_t* n_mtiles;  // -> tile_offsets[E]
   void* out;
   int ldo;
+  void* keep[2];  // EPI_GLU: gate / up pre-activations also stored (nullable)
 };
 
 template <class Pp, int KIND>
@@ -716,7 +735,8 @@ struct ExpertProb {
   }
 
   MOE_DEV void epilogue(const Tile& t, const typename Pp::Acc& acc) const {
-    Pp::template epilogue<KIND>(acc, t.rows, t.nt * Pp::BN, a.N, a.out, a.ldo, (size_t)t.row0, nullptr);
+    Pp::template epilogue<KIND>(acc, t.rows, t.nt * Pp::BN, a.N, a.out, a.ldo, (size_t)t.row0, nullptr, a.keep[0],
+                                a.keep[1]);
   }
 };
 
@@ -1317,7 +1337,7 @@ static hipError_t launch_dense_any(const Dims& D, const DenseArgs& a, hipStream_
 template <int TAG>
 static hipError_t launch_gemm_hsegs(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
                                     const void* W_sg, const void* W_su, const void* W_dn, float* logits, void* G,
-                                    void* z, hipStream_t s) {
+                                    void* z, hipStream_t s, void* P = nullptr, void* Q = nullptr) {
   constexpr int BM = DensePipe<true>::BM, BN = DensePipe<true>::BN, RB = DensePipe<true>::RB;
   const int es = esz(D);
   DenseArgs a{};
@@ -1349,6 +1369,8 @@ static hipError_t launch_gemm_hsegs(const Dims& D, const void* h, int T, const v
     g.kind = EPI_GLU;
     g.out = G;
     g.ldo = D.f_s;
+    g.keep[0] = P;
+    g.keep[1] = Q;
   }
   if (z) {  // latent z
     DenseSeg& g = a.seg[ns++];
@@ -1368,8 +1390,9 @@ static hipError_t launch_gemm_hsegs(const Dims& D, const void* h, int T, const v
 
 hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
                          const void* W_sg, const void* W_su, const void* W_dn, float* logits, void* G, void* z,
-                         hipStream_t s) {
-  return launch_gemm_hsegs<0>(D, h, T, W_r, logit_offset, W_sg, W_su, W_dn, logits, G, z, s);
+                         hipStream_t s, void* P, void* Q) {
+  if ((P == nullptr) != (Q == nullptr)) return hipErrorInvalidValue;
+  return launch_gemm_hsegs<0>(D, h, T, W_r, logit_offset, W_sg, W_su, W_dn, logits, G, z, s, P, Q);
 }
 
 hipError_t launch_gemm_rz(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
@@ -1426,7 +1449,9 @@ static hipError_t launch_expert(const Dims& D, const ExpertArgs& a, int T, hipSt
 }
 
 hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_src, const int2* tile_info,
-                            const int32_t* n_mtiles, int T, const void* W_g, const void* W_u, void* H, hipStream_t s) {
+                            const int32_t* n_mtiles, int T, const void* W_g, const void* W_u, void* H, hipStream_t s,
+                            void* A, void* U) {
+  if ((A == nullptr) != (U == nullptr)) return hipErrorInvalidValue;
   constexpr int BN = ExpertPipe<true>::BN, RB = ExpertPipe<true>::RB;
   const int es = esz(D);
   ExpertArgs a{};
@@ -1442,6 +1467,8 @@ hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_sr
   a.kt = D.l * es / RB;
   a.tile_info = tile_info;
   a.n_mtiles = n_mtiles;
+  a.keep[0] = A;
+  a.keep[1] = U;
   a.out = H;
   a.ldo = D.f;
   return launch_expert<EPI_GLU>(D, a, T, s);

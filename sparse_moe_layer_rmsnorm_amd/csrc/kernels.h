@@ -59,10 +59,11 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 // output ([G | y_lat] [W_sd | W_up]^T).
 // h [T,d] against [W_r | W_sg,W_su | W_dn] -> fp32 router logits (+ offset),
 // shared GLU hidden G and latent z in one launch; a NULL output drops its
-// part.
+// part.  P, Q (both or neither): the GLU's pre-activations h W_sg^T, h W_su^T
+// are stored there as well.
 hipError_t launch_gemm_h(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
                          const void* W_sg, const void* W_su, const void* W_dn, float* logits, void* G, void* z,
-                         hipStream_t s);
+                         hipStream_t s, void* P = nullptr, void* Q = nullptr);
 // h against W_r alone -> fp32 logits (+ offset) (the routing-only pass).
 hipError_t launch_gemm_rz(const Dims& D, const void* h, int T, const void* W_r, const float* logit_offset,
                           float* logits, hipStream_t s);
@@ -72,9 +73,11 @@ hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int 
 // kExpertBM rows from tile_info; n_mtiles points at their count).
 int expert_max_mtiles(int T, int k, int E);
 // Expert GEMM 1 + GLU; its A rows are z[perm_src[r]] (the dispatch is part
-// of the operand load, no dispatch buffer is written).
+// of the operand load, no dispatch buffer is written).  A, U (both or
+// neither): the pre-activations X W_g^T, X W_u^T are stored there as well.
 hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_src, const int2* tile_info,
-                            const int32_t* n_mtiles, int T, const void* W_g, const void* W_u, void* H, hipStream_t s);
+                            const int32_t* n_mtiles, int T, const void* W_g, const void* W_u, void* H, hipStream_t s,
+                            void* A = nullptr, void* U = nullptr);
 hipError_t launch_expert_down(const Dims& D, const void* H, const int2* tile_info, const int32_t* n_mtiles, int T,
                               const void* W_d, void* Y, hipStream_t s);
 

@@ -48,6 +48,9 @@ moe_status check_config(const moe_config* c) {
     if (c->l % 128 || c->f % 128 || c->l > 512 || c->f > 512)
       return fail(MOE_ERR_SHAPE, "MXFP8 experts need l and f multiples of 128, at most 512 (l=%d f=%d)", c->l, c->f);
   }
+  if (c->keep_preact != 0 && c->keep_preact != 1) return fail(MOE_ERR_INVALID_ARG, "keep_preact must be 0 or 1");
+  if (c->keep_preact && c->experts != MOE_EXPERTS_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "keep_preact needs bf16 experts");
   auto m64 = [](int32_t v) { return v > 0 && v % 64 == 0; };
   if (!m64(c->d) || !m64(c->l) || !m64(c->f))
     return fail(MOE_ERR_SHAPE, "d, l, f must be positive multiples of 64 (d=%d l=%d f=%d)", c->d, c->l, c->f);
@@ -136,6 +139,11 @@ void ws_layout(const moe_config* c, int64_t T, moe_ws_layout* L) {
   L->Xs = take(mx ? t * k * c->l / 32 : 0);
   L->H8 = take(mx ? t * k * c->f : 0);
   L->Hs = take(mx ? t * k * c->f / 32 : 0);
+  const bool keep = c->keep_preact != 0;
+  L->P = take(keep ? t * c->f_s * es : 0);
+  L->Q = take(keep ? t * c->f_s * es : 0);
+  L->A = take(keep ? t * k * c->f * es : 0);
+  L->U = take(keep ? t * k * c->f * es : 0);
   L->total = o;
 }
 
@@ -262,16 +270,17 @@ void bwd_layout(const moe_config* c, int64_t T, BwdLayout* L) {
     o = up(o + bytes);
     return at;
   };
-  L->P = take(t * fs * es);
-  L->Q = take(t * fs * es);
+  const size_t rec = c->keep_preact ? 0 : 1;  // pre-activations recomputed here unless the forward kept them
+  L->P = take(rec * t * fs * es);
+  L->Q = take(rec * t * fs * es);
   L->dG = take(t * fs * es);
   L->dy = take(t * l * es);
   L->dAcat = take(t * Kc * es);
   L->dg = take(t * k * 4);
   L->dY = take(Tk * l * es);
   L->dH = take(Tk * f * es);
-  L->Apre = take(Tk * f * es);
-  L->U = take(Tk * f * es);
+  L->Apre = take(rec * Tk * f * es);
+  L->U = take(rec * Tk * f * es);
   L->dAU = take(Tk * 2 * f * es);
   L->dX = take(Tk * l * es);
   L->dh = take(t * d * 4);
@@ -402,9 +411,11 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
   RoutePtrs p = route_ptrs(L, w, r);
   const int t = (int)T;
   void *h = w + L.h, *G = w + L.G, *z = w + L.z, *H = w + L.H, *Y = w + L.Y, *y_lat = w + L.y_lat;
+  const bool keep = ctx->cfg.keep_preact != 0;
   MOE_RUN(MOE_K_RMSNORM, launch_rmsnorm(D, x, ctx->w.gamma, h, t, s));
   MOE_RUN(MOE_K_GEMM_H, launch_gemm_h(D, h, t, ctx->w.W_r, ctx->w.logit_offset, ctx->w.W_sg, ctx->w.W_su,
-                                      ctx->w.W_dn, p.logits, D.f_s > 0 ? G : nullptr, z, s));
+                                      ctx->w.W_dn, p.logits, D.f_s > 0 ? G : nullptr, z, s,
+                                      keep && D.f_s > 0 ? w + L.P : nullptr, keep && D.f_s > 0 ? w + L.Q : nullptr));
   const int32_t* n_mtiles = p.tile_offsets + D.E;
   if (ctx->cfg.experts == MOE_EXPERTS_MXFP8) {
     // z -> MXFP8; the scatter copies each token's scale row to its grouped rows
@@ -423,8 +434,8 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
     st = route_tail(ctx, p, t, s);
     if (st != MOE_OK) return st;
     // dispatch X[r] = z[perm_src[r]] happens inside expert_up's operand load
-    MOE_RUN(MOE_K_EXPERT_UP,
-            launch_expert_up(D, z, p.perm_src, p.tile_info, n_mtiles, t, ctx->w.W_g, ctx->w.W_u, H, s));
+    MOE_RUN(MOE_K_EXPERT_UP, launch_expert_up(D, z, p.perm_src, p.tile_info, n_mtiles, t, ctx->w.W_g, ctx->w.W_u, H,
+                                              s, keep ? w + L.A : nullptr, keep ? w + L.U : nullptr));
     MOE_RUN(MOE_K_EXPERT_DOWN, launch_expert_down(D, H, p.tile_info, n_mtiles, t, ctx->w.W_d, Y, s));
   }
   MOE_RUN(MOE_K_COMBINE, launch_combine(D, Y, p.gates, p.inv, t, y_lat, s));
@@ -509,9 +520,18 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
     sg[n++] = {{{W.W_up, l, d, d}}, l, 1, dy, l};
     MOE_RUN(MOE_K_BWD_GEMM, launch_dgrad_dense(D, 4, dout, d * es, t, sg, n, 1, s));
   }
-  if (fs > 0) {  // shared GLU: recompute P, Q; dP, dQ into the first 2 f_s columns of dAcat
-    DenseSegSpec sg[2] = {{W.W_sg, fs, 1, P, fs}, {W.W_su, fs, 1, Q, fs}};
-    MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 3, h, d * es, t, d * es, sg, 2, d * es, s));
+  const bool kept = c.keep_preact != 0;  // pre-activations stored by the forward
+  if (kept) {
+    P = fw + L.P;
+    Q = fw + L.Q;
+    Apre = fw + L.A;
+    U = fw + L.U;
+  }
+  if (fs > 0) {  // shared GLU: P, Q (recomputed unless kept); dP, dQ into the first 2 f_s columns of dAcat
+    if (!kept) {
+      DenseSegSpec sg[2] = {{W.W_sg, fs, 1, P, fs}, {W.W_su, fs, 1, Q, fs}};
+      MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 3, h, d * es, t, d * es, sg, 2, d * es, s));
+    }
     MOE_RUN(MOE_K_BWD_ELTWISE, launch_glu_bwd(D, P, Q, dG, t, fs, dAcat, elw(dAcat, fs), Kc, s));
   }
   // combine transpose: dY rows and gate gradients
@@ -523,10 +543,12 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
     MOE_RUN(MOE_K_BWD_EXPERT,
             launch_dgrad_expert(D, 8, dY, l * es, wd, 1, wfl, f, p.tile_info, n_mtiles, t, dH, f, s));
   }
-  MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, z, l * es, p.perm_src, W.W_g, wfl, l * es, f, l * es, p.tile_info,
-                                             n_mtiles, t, Apre, f, s));
-  MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, z, l * es, p.perm_src, W.W_u, wfl, l * es, f, l * es, p.tile_info,
-                                             n_mtiles, t, U, f, s));
+  if (!kept) {
+    MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, z, l * es, p.perm_src, W.W_g, wfl, l * es, f, l * es, p.tile_info,
+                                               n_mtiles, t, Apre, f, s));
+    MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, z, l * es, p.perm_src, W.W_u, wfl, l * es, f, l * es, p.tile_info,
+                                               n_mtiles, t, U, f, s));
+  }
   MOE_RUN(MOE_K_BWD_ELTWISE, launch_glu_bwd(D, Apre, U, dH, Tk, f, dAU, elw(dAU, f), 2 * f, s));
   {
     const KPiece wgu[2] = {{W.W_g, l, f, f}, {W.W_u, l, f, f}};  // [W_g[e]; W_u[e]] [2f, l]: K = 2f

@@ -34,13 +34,13 @@ class MoeLayer:
     def __init__(self, *, d: int, l: int, E: int, k: int, f: int, f_s: int, dtype: str, weights: Dict,
                  max_tokens: int, qb_bins: int = 256, rms_eps: float = 1e-6, frozen: bool = False,
                  routed_scale: float = 1.0, logit_offset=None, device: str = "cuda", stream=None,
-                 balancer: str = "qb", sign_gamma: float = 1e-2, experts: str = "bf16"):
+                 balancer: str = "qb", sign_gamma: float = 1e-2, experts: str = "bf16", keep_preact: bool = False):
         self.dtype = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.device = torch.device(device)
         self.cfg = B.make_config(d, l, E, k, f, f_s, dtype=dtype, rms_eps=rms_eps, qb_bins=qb_bins, frozen=frozen,
                                  max_tokens=max_tokens, routed_scale=routed_scale, balancer=balancer,
-                                 sign_gamma=sign_gamma, experts=experts)
+                                 sign_gamma=sign_gamma, experts=experts, keep_preact=keep_preact)
         self.dims = dict(d=d, l=l, E=E, k=k, f=f, f_s=f_s, B=qb_bins)
         self.w: Dict[str, torch.Tensor] = {}
         for name in _WEIGHT_NAMES:
@@ -74,6 +74,7 @@ class MoeLayer:
         ws = self.workspace(T)
         dm = self.dims
         es = self.tdtype
+        keep = int(self.cfg.keep_preact)
 
         def view(off, n, dt, shape):
             nbytes = n * torch.tensor([], dtype=dt).element_size()
@@ -92,7 +93,12 @@ class MoeLayer:
             "z8": view(L.z8, L.zs - L.z8, torch.uint8, (-1,)),
             "zs": view(L.zs, L.Xs - L.zs, torch.uint8, (-1,)),
             "H8": view(L.H8, L.Hs - L.H8, torch.uint8, (-1,)),
-            "Hs": view(L.Hs, L.total - L.Hs, torch.uint8, (-1,)),
+            "Hs": view(L.Hs, L.P - L.Hs, torch.uint8, (-1,)),
+            # keep_preact only (empty otherwise): the GLU pre-activations
+            "P": view(L.P, keep * T * dm["f_s"], es, (-1, dm["f_s"]) if keep else (0,)),
+            "Q": view(L.Q, keep * T * dm["f_s"], es, (-1, dm["f_s"]) if keep else (0,)),
+            "A": view(L.A, keep * T * dm["k"] * dm["f"], es, (-1, dm["f"]) if keep else (0,)),
+            "U": view(L.U, keep * T * dm["k"] * dm["f"], es, (-1, dm["f"]) if keep else (0,)),
         }
 
     def state_views(self) -> Dict[str, torch.Tensor]:
@@ -195,9 +201,10 @@ class MoeLayer:
 
 def layer_from_shape(shape, weights: Dict, *, max_tokens: Optional[int] = None, frozen: Optional[bool] = None,
                      logit_offset=None, device: str = "cuda", balancer: str = "qb",
-                     sign_gamma: float = 1e-2, experts: str = "bf16") -> MoeLayer:
+                     sign_gamma: float = 1e-2, experts: str = "bf16", keep_preact: bool = False) -> MoeLayer:
     """MoeLayer for a workloads.LayerShape."""
     return MoeLayer(d=shape.d, l=shape.l, E=shape.E, k=shape.k, f=shape.f, f_s=shape.f_s, dtype=shape.dtype,
                     weights=weights, max_tokens=max_tokens or shape.T, qb_bins=shape.B, rms_eps=shape.rms_eps,
                     frozen=shape.qb_frozen if frozen is None else frozen, logit_offset=logit_offset,
-                    device=device, balancer=balancer, sign_gamma=sign_gamma, experts=experts)
+                    device=device, balancer=balancer, sign_gamma=sign_gamma, experts=experts,
+                    keep_preact=keep_preact)

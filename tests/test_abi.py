@@ -107,6 +107,30 @@ def test_mxfp8_experts_config(L, over, status):
         assert L.moe_init(ctypes.byref(cfg), ctypes.byref(w_), 256, None, ctypes.byref(ctx)) == status
 
 
+def test_keep_preact_config_and_workspaces(L):
+    """keep_preact is 0 or 1 and needs bf16 experts; it adds exactly the four
+    pre-activation buffers to the forward workspace and takes the backward's
+    own copies of them away."""
+    T = 1000
+    es = 2
+    base = B.make_config(**REPLICA, max_tokens=T)
+    keep = B.make_config(**REPLICA, max_tokens=T, keep_preact=True)
+    Lb, Lk = B.moe_workspace_layout(base, T), B.moe_workspace_layout(keep, T)
+    fs, f, k = REPLICA["f_s"], REPLICA["f"], REPLICA["k"]
+    assert Lb.P == Lb.Q == Lb.A == Lb.U == Lb.total
+    assert Lk.Q - Lk.P >= T * fs * es and Lk.U - Lk.A >= T * k * f * es and Lk.total - Lk.U >= T * k * f * es
+    grow = B.moe_workspace_bytes(keep, T) - B.moe_workspace_bytes(base, T)
+    need = 2 * (T * fs + T * k * f) * es
+    assert need <= grow <= need + 4 * 256
+    shrink = B.moe_backward_workspace_bytes(base, T) - B.moe_backward_workspace_bytes(keep, T)
+    assert need <= shrink <= need + 4 * 256
+    for bad in (dict(keep_preact=2), dict(keep_preact=-1)):
+        cfg = B.make_config(**REPLICA, max_tokens=T)
+        cfg.keep_preact = bad["keep_preact"]
+        assert B.moe_state_bytes(cfg) == 0
+    assert B.moe_state_bytes(B.make_config(**REPLICA, max_tokens=T, keep_preact=True, experts="mxfp8")) == 0
+
+
 def test_null_arguments_rejected(L):
     cfg = B.make_config(**REPLICA, max_tokens=64)
     ctx = ctypes.c_void_p()

@@ -28,10 +28,13 @@ CASES = [  # name, dtype, T, d, l, E, k, f, f_s
 ]
 
 
+@pytest.mark.parametrize("keep", [False, True], ids=["recompute", "kept"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_backward_matches_oracle(case):
+def test_backward_matches_oracle(case, keep):
+    """keep: the forward stores the GLU pre-activations (keep_preact) and the
+    backward reads them instead of recomputing them."""
     name, dtype, T, d, l, E, k, f, f_s = case
-    say(f"backward {name}: T={T} d={d} l={l} E={E} k={k} f={f} f_s={f_s} {dtype}")
+    say(f"backward {name}: T={T} d={d} l={l} E={E} k={k} f={f} f_s={f_s} {dtype} keep={keep}")
     shape = wl.LayerShape(name, 21, dtype, T=T, d=d, l=l, E=E, k=k, f=f, f_s=f_s, B=256)
     W = wl.make_weights(shape)
     rng = np.random.default_rng(T + E)
@@ -41,7 +44,7 @@ def test_backward_matches_oracle(case):
     if dtype == "bf16":
         dout = o.bf16_round(dout).astype(F32)
     bias = (rng.standard_normal(E) * 0.05).astype(F32)
-    layer = make_layer(shape, W, max_tokens=T)
+    layer = make_layer(shape, W, max_tokens=T, keep_preact=keep)
     layer.set_bias(bias)
     r = layer.route_buffers(T)
     xg = x_on_gpu(x, layer)
@@ -82,3 +85,43 @@ def test_backward_is_deterministic_and_leaves_qb_state():
     for n, v in layer.state_views().items():
         assert torch.equal(v, st0[n]), n
     layer.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kept_preactivations(dtype):
+    """keep_preact changes no output bit of the forward, and the stored P, Q,
+    A, U are the products of the GPU's own h and dispatched z rows with the
+    weights (oracle in fp64, rounded to the storage dtype) at the layer
+    tolerance."""
+    shape = wl.LayerShape("keep", 23, dtype, T=1000, d=1024, l=256, E=256, k=6, f=512, f_s=2048, B=256)
+    if dtype == "f32":
+        shape = wl.LayerShape("keep", 23, dtype, T=300, d=256, l=128, E=32, k=4, f=192, f_s=128, B=256)
+    W = wl.make_weights(shape)
+    x = wl.make_x(shape)
+    T = shape.T
+    say(f"kept pre-activations {dtype}: T={T}")
+    plain = make_layer(shape, W, max_tokens=T, frozen=True)
+    kept = make_layer(shape, W, max_tokens=T, frozen=True, keep_preact=True)
+    out0 = plain.forward(x_on_gpu(x, plain)).clone()
+    r = kept.route_buffers(T)
+    out1 = kept.forward(x_on_gpu(x, kept), route=r)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1)
+    v = kept.ws_views(T)
+    h = to_np(v["h"]).astype(np.float64)
+    st = o.bf16_round if dtype == "bf16" else (lambda a: a.astype(F32).astype(np.float64))
+    tol = OUT_TOL[dtype]
+    for n, w in (("P", "W_sg"), ("Q", "W_su")):
+        want = st(h @ W[w].astype(np.float64).T)
+        assert rel_err(to_np(v[n]), want) <= tol, n
+    X = to_np(v["z"]).astype(np.float64)[to_np(r["perm_src"])]
+    offs = to_np(r["offsets"])
+    for n, w in (("A", "W_g"), ("U", "W_u")):
+        got = to_np(v[n]).astype(np.float64)
+        want = np.zeros_like(got)
+        for e in range(shape.E):
+            a, b = int(offs[e]), int(offs[e + 1])
+            want[a:b] = st(X[a:b] @ W[w][e].astype(np.float64).T)
+        assert rel_err(got, want) <= tol, n
+    plain.close()
+    kept.close()
