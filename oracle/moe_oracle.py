@@ -23,7 +23,8 @@ Sources (page title + place on the page):
        Tab 8-10 (QB reroutes only, weight normalisation, delayed update,
        mean centring, frozen at inference).
   [P5] "K3 tops open source" blog, idle-experts section (hot windows raise
-       the threshold, cold ones lower it).
+       the threshold, cold ones lower it); fourth-waste section (4-bit
+       expert weights, 8-bit run-time data).
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): sigmoid scores; router on the d-wide normalised h; SiLU GLU for
@@ -334,6 +335,66 @@ def mx_round(a: np.ndarray) -> np.ndarray:
     return q * np.repeat(np.ldexp(1.0, sb - 127), MX_BLOCK, axis=-1)
 
 
+# 4-bit expert weights with 8-bit activations ([P5] "K3 tops open source"
+# blog, fourth-waste section: expert weights held in 4 bits and the data
+# flowing at run time in 8 bits during quantisation-aware training; the
+# format is not named -- reading: OCP MXFP4 weights, E2M1 elements (1 sign,
+# 2 exponent bits of bias 1, 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6)
+# under the same E8M0 block scale per 32 along K, against MXFP8 activations).
+E2M1_MAX = 6.0
+E2M1_EMAX = 2            # exponent of the largest E2M1 binade (6 = 1.5 * 2^2)
+
+
+def e2m1_round(v: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 value (ties to even), saturating at +-6 (fp64 out).
+
+    Binade 2^e (e >= 0) has step 2^(e-1); below 1 the subnormal step is 1/2."""
+    v = np.asarray(v, dtype=np.float64)
+    _, E = np.frexp(v)
+    step = np.ldexp(1.0, np.maximum(E - 1, 0) - 1)
+    q = np.rint(v / step) * step
+    return np.clip(q, -E2M1_MAX, E2M1_MAX)
+
+
+def mx4_scale_bytes(a: np.ndarray) -> np.ndarray:
+    """E8M0 scale byte of each block of 32 along the last axis for MXFP4:
+    2^(floor(log2 amax) - 2), biased by 127, clamped to [0, 254]; an
+    all-zero block gets byte 0."""
+    a = np.asarray(a, dtype=np.float64)
+    blocks = a.reshape(a.shape[:-1] + (a.shape[-1] // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(blocks).max(axis=-1)
+    _, E = np.frexp(amax)
+    b = np.clip(E - 1 - E2M1_EMAX + 127, 0, 254)
+    return np.where(amax > 0, b, 0).astype(np.int64)
+
+
+def mx4_quantize(a: np.ndarray):
+    """(elements as E2M1 values, scale bytes) of `a` in MXFP4 along the last
+    axis: element = e2m1_round(a / 2^(byte - 127))."""
+    a = np.asarray(a, dtype=np.float64)
+    sb = mx4_scale_bytes(a)
+    scale = np.repeat(np.ldexp(1.0, sb - 127), MX_BLOCK, axis=-1)
+    return e2m1_round(a / scale), sb
+
+
+def mx4_round(a: np.ndarray) -> np.ndarray:
+    """The value an MXFP4 round trip gives: element * scale (fp64)."""
+    q, sb = mx4_quantize(a)
+    return q * np.repeat(np.ldexp(1.0, sb - 127), MX_BLOCK, axis=-1)
+
+
+def _expert_rounding(experts: str):
+    """(activation rounding, weight rounding) of an expert format; None for
+    bf16 experts."""
+    if experts == "mxfp8":
+        return mx_round, mx_round
+    if experts == "mxfp4":
+        return mx_round, mx4_round
+    if experts != "bf16":
+        raise ValueError(f"unknown expert format {experts}")
+    return None, None
+
+
 def router_logits(h: np.ndarray, W_r: np.ndarray, c: Optional[np.ndarray] = None) -> np.ndarray:
     """l = h W_r^T (+ c) in fp64, stored as fp32 ([P4] Tab 1 routing branch)."""
     l = h @ np.asarray(W_r, np.float64).T
@@ -349,10 +410,12 @@ def expert_outputs(X: np.ndarray, offsets: np.ndarray, W: Dict[str, np.ndarray],
 
     experts="mxfp8": both operands of each product are MXFP8 along their
     contraction axis (X and W_g, W_u along l; H, stored first, and W_d along
-    f); the products and sums are exact (fp64) on the rounded values."""
-    mx = experts == "mxfp8"
+    f); experts="mxfp4": the weights are MXFP4 instead (activations still
+    MXFP8).  The products and sums are exact (fp64) on the rounded values."""
+    ra, rw = _expert_rounding(experts)
+    mx = ra is not None
     if mx:
-        X = mx_round(X)
+        X = ra(X)
     E = len(offsets) - 1
     f = W["W_g"].shape[1]
     lat = W["W_d"].shape[1]
@@ -364,10 +427,10 @@ def expert_outputs(X: np.ndarray, offsets: np.ndarray, W: Dict[str, np.ndarray],
             continue
         Wg, Wu, Wd = W["W_g"][e], W["W_u"][e], W["W_d"][e]
         if mx:
-            Wg, Wu, Wd = mx_round(Wg), mx_round(Wu), mx_round(Wd)
+            Wg, Wu, Wd = rw(Wg), rw(Wu), rw(Wd)
         He = _store(glu(X[a:b], Wg, Wu), dtype)
         H[a:b] = He
-        Y[a:b] = _store((mx_round(He) if mx else He) @ np.asarray(Wd, np.float64).T, dtype)
+        Y[a:b] = _store((ra(He) if mx else He) @ np.asarray(Wd, np.float64).T, dtype)
     return H, Y
 
 
@@ -437,17 +500,18 @@ def forward_tokens(x_rows: np.ndarray, W: Dict[str, np.ndarray], idx_rows: np.nd
     h = _store(rmsnorm(x_rows, W["gamma"], eps), dtype)
     z = _store(h @ np.asarray(W["W_dn"], np.float64).T, dtype)
     out = np.zeros_like(x_rows)
-    mx = experts == "mxfp8"
+    ra, rw = _expert_rounding(experts)
+    mx = ra is not None
     for t in range(x_rows.shape[0]):
         y_lat = np.zeros(z.shape[1])
-        zt = mx_round(z[t:t + 1]) if mx else z[t:t + 1]
+        zt = ra(z[t:t + 1]) if mx else z[t:t + 1]
         for j in range(idx_rows.shape[1]):
             e = int(idx_rows[t, j])
             Wg, Wu, Wd = W["W_g"][e], W["W_u"][e], W["W_d"][e]
             if mx:
-                Wg, Wu, Wd = mx_round(Wg), mx_round(Wu), mx_round(Wd)
+                Wg, Wu, Wd = rw(Wg), rw(Wu), rw(Wd)
             He = _store(glu(zt, Wg, Wu), dtype)
-            Ye = _store((mx_round(He) if mx else He) @ np.asarray(Wd, np.float64).T, dtype)
+            Ye = _store((ra(He) if mx else He) @ np.asarray(Wd, np.float64).T, dtype)
             y_lat += float(gates_rows[t, j]) * Ye[0]
         y_lat = _store(y_lat, dtype)
         y_r = y_lat @ np.asarray(W["W_up"], np.float64).T

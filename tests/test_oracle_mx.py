@@ -85,3 +85,101 @@ def test_mx_experts_equal_bf16_where_exact():
     den = np.abs(fb["out"]).max()
     assert 0 < np.abs(fm["out"] - fb["out"]).max() / den < 0.1
     np.testing.assert_array_equal(fm["H"] != 0, fb["H"] != 0)
+
+
+# ---------------------------------------------------------------- MXFP4 --
+def _e2m1_codes():
+    """(value, mantissa bit) of the 16 E2M1 codes, decoded from the bit
+    fields: sign, 2 exponent bits (bias 1, 0 = subnormal), 1 mantissa bit."""
+    out = []
+    for code in range(16):
+        s = -1.0 if code & 8 else 1.0
+        e, m = (code >> 1) & 3, code & 1
+        v = m * 0.5 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1)
+        out.append((s * v, m))
+    return out
+
+
+def _e2m1_brute(x):
+    """Nearest code value by search; ties to the code whose mantissa bit is
+    0; beyond the largest value, saturate."""
+    codes = _e2m1_codes()
+    res = np.empty(len(x))
+    for i, v in enumerate(x):
+        v = float(np.clip(v, -6.0, 6.0))
+        d = [abs(v - c) for c, _ in codes]
+        best = min(d)
+        cands = [(c, m) for (c, m), dd in zip(codes, d) if dd == best]
+        even = [c for c, m in cands if m == 0]
+        res[i] = (even or [cands[0][0]])[0]
+    return res
+
+
+def test_e2m1_round_matches_brute_force():
+    vals = np.unique([c for c, _ in _e2m1_codes()])
+    assert len(vals) == 15 and vals.max() == 6.0            # +-0 coincide
+    mids = (vals[1:] + vals[:-1]) / 2
+    rng = np.random.default_rng(4)
+    rand = rng.uniform(-9, 9, 4000)
+    x = np.concatenate([vals, mids, np.nextafter(mids, -1e9), np.nextafter(mids, 1e9), rand, [7.0, -7.5, 1e9]])
+    np.testing.assert_array_equal(o.e2m1_round(x), _e2m1_brute(x))
+
+
+def test_e2m1_ties_table():
+    x = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 5.0001, 6.9, 7.0, 100.0])
+    want = np.array([0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0, 6.0, 6.0, 6.0])
+    np.testing.assert_array_equal(o.e2m1_round(x), want)
+    np.testing.assert_array_equal(o.e2m1_round(-x), -want)
+
+
+def test_mx4_scale_closed_form():
+    """Block scale 2^(floor(log2 amax) - 2): amax 6 and 4 -> byte 127, amax
+    just under 4 -> 126, amax 1 -> 125, zero block -> 0."""
+    for amax, byte in [(6.0, 127), (4.0, 127), (3.999, 126), (1.0, 125), (0.0, 0), (2.0 ** -130, 0)]:
+        blk = np.zeros(32)
+        blk[3] = amax
+        assert o.mx4_scale_bytes(blk[None, :])[0, 0] == byte, amax
+    q, sb = o.mx4_quantize(np.full((1, 32), 3.0))            # 3 = 1.5 * 2^1: scale 2^-1, element 6
+    assert sb[0, 0] == 126 and np.all(q == 6.0)
+
+
+def test_mx4_round_trip_error_bound():
+    """Elements of a block lie in [4, 8) * scale at most for the block
+    maximum: relative error <= 1/4 inside the normal range (|a| / scale >=
+    1, below the 6 -> 7 saturation edge), and the clipped maximum loses
+    < 25%."""
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((64, 256)) * np.exp2(rng.integers(-20, 20, (64, 1)))
+    r = o.mx4_round(a)
+    q, sb = o.mx4_quantize(a)
+    assert np.all(np.abs(q) <= 6)
+    scale = np.repeat(np.ldexp(1.0, sb - 127), 32, axis=1)
+    u = np.abs(a) / scale
+    rel = np.abs(r - a) / np.abs(a)
+    assert np.all(rel[(u >= 1) & (u < 7)] <= 0.25 + 1e-12)
+    assert np.all(rel[u >= 7] < 0.25)
+    np.testing.assert_array_equal(o.mx4_round(r), r)
+
+
+def test_mxfp4_layer_equals_mxfp8_where_both_exact():
+    """Weights from {0, +-1/2, +-1, +-3/2, +-2, +-3, +-4, +-6} * 2^-4 with a 6
+    in every block are exact in MXFP4 and in MXFP8; the two expert formats
+    then give the same layer bit for bit (the activations are MXFP8 in both).
+    Random weights: the MXFP4 layer differs from the MXFP8 one."""
+    shape = wl.LayerShape("mx4", 29, "bf16", T=48, d=128, l=128, E=4, k=2, f=128, f_s=0, B=256)
+    W = wl.make_weights(shape)
+    x = wl.make_x(shape)
+    f8 = o.forward(x, W, np.zeros(4, F32), k=2, dtype="bf16", experts="mxfp8")
+    f4 = o.forward(x, W, np.zeros(4, F32), k=2, dtype="bf16", logits=f8["logits"], experts="mxfp4")
+    assert not np.array_equal(f4["out"], f8["out"])
+    rng = np.random.default_rng(2)
+    for n in ("W_g", "W_u", "W_d"):
+        v = rng.choice([0.0, 0.5, -0.5, 1.0, -1.0, 1.5, -1.5, 2.0, 3.0, -3.0, 4.0, -4.0, 6.0, -6.0], size=W[n].shape)
+        v[..., ::32] = 6.0
+        W[n] = (v * 2.0 ** -4).astype(F32)
+        np.testing.assert_array_equal(o.mx4_round(W[n]), W[n])
+        np.testing.assert_array_equal(o.mx_round(W[n]), W[n])
+    f8 = o.forward(x, W, np.zeros(4, F32), k=2, dtype="bf16", experts="mxfp8")
+    f4 = o.forward(x, W, np.zeros(4, F32), k=2, dtype="bf16", logits=f8["logits"], experts="mxfp4")
+    for n in ("H", "Y", "out"):
+        np.testing.assert_array_equal(f4[n], f8[n])
