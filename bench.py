@@ -174,8 +174,9 @@ def main() -> int:
     ap.add_argument("--no-profile", action="store_true", help="no per-kernel events in the timed region")
     ap.add_argument("--balancer", choices=("qb", "sign"), default="qb",
                     help="bias update rule of the step: quantile balancing (default) or the sign rule")
-    ap.add_argument("--experts", choices=("bf16", "mxfp8"), default="bf16",
-                    help="storage of the routed experts' operands (MXFP8: E4M3 + E8M0 block scales)")
+    ap.add_argument("--experts", choices=("bf16", "mxfp8", "mxfp4"), default="bf16",
+                    help="storage of the routed experts' operands (MXFP8: E4M3 + E8M0 block scales; MXFP4: E2M1 "
+                         "weights + E8M0 block scales against MXFP8 activations)")
     ap.add_argument("--backward", action="store_true",
                     help="time the training step with the backward pass: forward, moe_backward (dx and all weight "
                          "gradients) and the bias update")
@@ -344,7 +345,8 @@ def main() -> int:
         "config": {"workload": f"{shape.name}: T={T} tokens, d={shape.d}, l={shape.l}, E={shape.E}, k={shape.k}, "
                                f"f={shape.f}, f_s={shape.f_s}, B={shape.B}, QB {'frozen' if frozen else 'train'}"
                                + (", sign-rule balancer" if args.balancer == "sign" else "")
-                               + (", MXFP8 experts" if args.experts == "mxfp8" else "")
+                               + {"bf16": "", "mxfp8": ", MXFP8 experts",
+                                  "mxfp4": ", MXFP4 expert weights with MXFP8 activations"}[args.experts]
                                + (", GLU pre-activations kept by the forward" if args.keep_preact else ""),
                    "global_batch": T,
                    "step": "training forward + backward + qb_update" if args.backward else

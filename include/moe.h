@@ -92,9 +92,19 @@ typedef enum moe_balancer { MOE_BALANCE_QB = 0, MOE_BALANCE_SIGN = 1 } moe_balan
  * moe_init (again by moe_requantize_experts after the caller changes them);
  * each forward quantises z and the expert hidden H the same way, and the
  * expert GEMMs multiply on the MFMA's block-scaled FP8 path with fp32 sums.
+ * MOE_EXPERTS_MXFP4 (same conditions): 4-bit expert weights with 8-bit
+ * activations ("K3 tops open source" blog, fourth-waste section; the format
+ * is not named there, this is the OCP one): W_g, W_u, W_d as MXFP4 -- E2M1
+ * elements (0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives), two per byte,
+ * low nibble first, with the same E8M0 scale per 32 along K, 2^(floor(log2
+ * amax) - 2) -- against z and H in MXFP8 as above.
  * The backward pass needs MOE_EXPERTS_BF16.
  */
-typedef enum moe_expert_format { MOE_EXPERTS_BF16 = 0, MOE_EXPERTS_MXFP8 = 1 } moe_expert_format;
+typedef enum moe_expert_format {
+  MOE_EXPERTS_BF16 = 0,
+  MOE_EXPERTS_MXFP8 = 1,
+  MOE_EXPERTS_MXFP4 = 2
+} moe_expert_format;
 
 /*
  * Layer sizes.  d, l, f must be multiples of 64 and f_s a multiple of 64 or 0
@@ -165,8 +175,9 @@ typedef struct moe_state_layout {
   size_t hist_slices;
   size_t load;  /* [E] uint32 tokens routed to each expert since the last
                    update (sign-rule balancer only)                       */
-  size_t mx;    /* MXFP8 experts only: W_g, W_u [E,f,l] and W_d [E,l,f] as
-                   E4M3 bytes, then their E8M0 scales [.., K/32]          */
+  size_t mx;    /* block-scaled experts only: W_g, W_u [E,f,l] and W_d
+                   [E,l,f] as E4M3 bytes (MXFP8) or E2M1 pairs [.., K/2]
+                   (MXFP4), then their E8M0 scales [.., K/32]             */
   size_t total;
 } moe_state_layout;
 
@@ -175,7 +186,7 @@ typedef struct moe_ws_layout {
   size_t h, logits, idx, gates, bitmap, cbase, sbase, counts, offsets, tile_offsets, perm_src, inv, tile_info;
   size_t G, z, X, H, Y, y_lat; /* X: zero bytes (the expert GEMM reads z[perm_src[r]]
                                   directly, so no dispatch buffer is written) */
-  size_t z8, zs, Xs, H8, Hs;    /* MXFP8 experts only (else zero bytes): z and H as
+  size_t z8, zs, Xs, H8, Hs;    /* block-scaled experts only (else zero bytes): z and H as
                                   E4M3 bytes and E8M0 scales; Xs the scale rows of
                                   the grouped rows */
   size_t P, Q, A, U;            /* keep_preact only (else zero bytes): the GLU

@@ -20,7 +20,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MO
 MOE_F32, MOE_BF16 = 0, 1
 MOE_QB_TRAIN, MOE_QB_FROZEN = 0, 1
 MOE_BALANCE_QB, MOE_BALANCE_SIGN = 0, 1
-MOE_EXPERTS_BF16, MOE_EXPERTS_MXFP8 = 0, 1
+MOE_EXPERTS_BF16, MOE_EXPERTS_MXFP8, MOE_EXPERTS_MXFP4 = 0, 1, 2
+_EXPERT_FORMATS = {"bf16": MOE_EXPERTS_BF16, "mxfp8": MOE_EXPERTS_MXFP8, "mxfp4": MOE_EXPERTS_MXFP4}
 KERNELS = ["rmsnorm", "gemm_h", "topk", "hist", "scan", "scatter", "expert_up", "expert_down", "combine",
            "gemm_out", "qb_quantile", "qb_bias", "gemm_rz", "sign_bias", "bwd_gemm", "bwd_expert", "bwd_wgrad",
            "bwd_eltwise", "bwd_transpose", "mx_quant"]
@@ -221,5 +222,5 @@ def make_config(d: int, l: int, E: int, k: int, f: int, f_s: int, *, dtype: str 
                       rms_eps=rms_eps, qb_bins=qb_bins, qb_mode=MOE_QB_FROZEN if frozen else MOE_QB_TRAIN,
                       max_tokens=max_tokens, routed_scale=routed_scale,
                       balancer=MOE_BALANCE_SIGN if balancer == "sign" else MOE_BALANCE_QB, sign_gamma=sign_gamma,
-                      experts=MOE_EXPERTS_MXFP8 if experts == "mxfp8" else MOE_EXPERTS_BF16,
+                      experts=_EXPERT_FORMATS[experts],
                       keep_preact=1 if keep_preact else 0)

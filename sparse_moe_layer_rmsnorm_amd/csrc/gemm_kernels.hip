@@ -1163,10 +1163,100 @@ struct ExpertMxProb : ExpertProb<Pp, KIND> {
   }
 };
 
+// MXFP4 weights (4-bit E2M1 elements, two per byte, low nibble first, one
+// E8M0 scale per 32 along K) against MXFP8 activations.  The FP4 operand of
+// v_mfma_scale_f32_16x16x128_f8f6f4 (cbsz = 4, measured on gfx950): lane (i,
+// g = lane / 16) holds K elements [32g, 32g+32) of row i as 16 contiguous
+// bytes, and its scale byte scales exactly those; the upper half of the
+// 8-register operand is not read.  A stage covers 128 K values: activation
+// rows of 128 bytes as in the MXFP8 GEMM, weight rows of 64 bytes (16-byte
+// chunk j of weight row c at position j ^ (c / 2) % 4).
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int BPC_>
+struct Mx4Pipe : Pipe<BM_, BN_, WM_, WN_, NS_, 128, BPC_, true> {
+  using Base = Pipe<BM_, BN_, WM_, WN_, NS_, 128, BPC_, true>;
+  static constexpr int RBW = 64;
+  static constexpr int STAGE = Base::A_BYTES + Base::BN * RBW;
+  static constexpr int LDS = Base::NS * STAGE;
+  static constexpr int L = STAGE / 1024 / Base::NW;
+  static constexpr int LA = Base::A_BYTES / (1024 * Base::NW);
+  static_assert(STAGE % (1024 * Base::NW) == 0 && Base::A_BYTES % (1024 * Base::NW) == 0, "whole DMA slots");
+  static_assert(LDS * Base::BPC <= 160 * 1024, "LDS per CU");
+  MOE_DEV static int w_off(int c, int j) { return Base::A_BYTES + c * RBW + ((j ^ ((c >> 1) & 3)) << 4); }
+  MOE_DEV static void wait_stage(int after) {
+    if (after <= 0) wait_vmcnt<0>();
+    else if (after == 1) wait_vmcnt<L>();
+    else wait_vmcnt<2 * L>();
+  }
+};
+
+template <class Pp>
+MOE_DEV void mx4_compute(const char* cur, typename Pp::Acc& acc, const uint32_t (&sa)[Pp::MI][4],
+                         const uint32_t (&sb)[Pp::NI][4], int s) {
+  const int lane = threadIdx.x & 63, wave = Pp::wave_id();
+  const int wm = wave / Pp::WN, wn = wave % Pp::WN, g = lane >> 4;
+  v8i_t af[Pp::MI], wf[Pp::NI];
+#pragma unroll
+  for (int ni = 0; ni < Pp::NI; ++ni) {
+    const uint4 w = *reinterpret_cast<const uint4*>(cur + Pp::w_off(wn * Pp::WTN + ni * 16 + (lane & 15), g));
+    wf[ni] = v8i_t{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int mi = 0; mi < Pp::MI; ++mi) {
+    const int row = wm * Pp::WTM + mi * 16 + (lane & 15);
+    const uint4 lo = *reinterpret_cast<const uint4*>(cur + Pp::lds_off(row, g));
+    const uint4 hi = *reinterpret_cast<const uint4*>(cur + Pp::lds_off(row, 4 + g));
+    af[mi] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  const int sh = 8 * g;
+  auto pick = [&](const uint32_t (&w)[4]) -> int {
+    const uint32_t v = s == 0 ? w[0] : (s == 1 ? w[1] : (s == 2 ? w[2] : w[3]));
+    return (int)((v >> sh) & 0xFFu);
+  };
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int mi = 0; mi < Pp::MI; ++mi) {
+    const int sA = pick(sa[mi]);
+#pragma unroll
+    for (int ni = 0; ni < Pp::NI; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[ni], af[mi], acc[mi][ni], 4, 0, 0,
+                                                                     pick(sb[ni]), 0, sA);
+  }
+}
+
 template <class Pp, int KIND>
-__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expert_mx(const ExpertArgs args) {
-  __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
-  ExpertMxProb<Pp, KIND> prob{args};
+struct ExpertMx4Prob : ExpertMxProb<Pp, KIND> {
+  using ExpertMxProb<Pp, KIND>::a;
+  template <int L>
+  using SrcT = typename ExpertProb<Pp, KIND>::template SrcT<L>;
+  template <int L>
+  MOE_DEV void sources(const Tile& t, SrcT<L>& src) const {
+    const int lane = threadIdx.x & 63, wave = Pp::wave_id(), uwave = uniform_int(wave);
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      if (i < Pp::LA) {  // activation rows: as the MXFP8 GEMM
+        const int row = Pp::slot_row(i, wave, lane);
+        const int grp = i * Pp::NW + uwave;
+        const char* p = a.gather ? this->gathered_row_ptr(t, grp) : this->row_ptr(t, row);
+        src.p[i] = p + Pp::slot_chunk(row, lane) * 16;
+      } else {  // weight rows of 64 bytes: 16 per slot, 4 lanes each
+        const int c = ((i - Pp::LA) * Pp::NW + wave) * 16 + lane / 4;
+        src.p[i] = this->row_ptr(t, Pp::BM + c) + (((lane & 3) ^ ((c >> 1) & 3)) << 4);
+      }
+    }
+  }
+  template <int L>
+  MOE_DEV void issue(const SrcT<L>& src, int ks, uint32_t lds) const {
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      lds_dma16(src.p[i] + ks * (i < Pp::LA ? Pp::RB : Pp::RBW),
+                __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
+  }
+};
+
+// The persistent stream of the block-scaled expert GEMMs (W4: MXFP4 weights).
+template <class Pp, class Prob, bool W4>
+MOE_DEV void expert_mx_stream(const ExpertArgs& args, char* smem) {
+  Prob prob{args};
   const int G = gridDim.x, b = blockIdx.x;
   const int x = b & 7, q = b >> 3, Gx = G >> 3;
   const int total_tiles = prob.total();
@@ -1178,7 +1268,7 @@ __global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expe
   const int KT = prob.kt();
   const int total = my_n * KT;
   const uint32_t lds0 = lds_addr(smem) + Pp::wave_id() * 1024;
-  typename ExpertMxProb<Pp, KIND>::template SrcT<Pp::L> src;
+  typename Prob::template SrcT<Pp::L> src;
   int iss_j = 0, iss_ks = 0, issued = 0;
   prob.sources(prob.tile(lo + q), src);
   auto issue = [&]() {
@@ -1208,7 +1298,8 @@ __global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expe
 #pragma unroll
     for (int i = 0; i < Pp::NI; ++i) asm volatile("" ::"v"(sb[i][0]), "v"(sb[i][1]), "v"(sb[i][2]), "v"(sb[i][3]));
     if (issued < total) issue();
-    mx_compute<Pp>(smem + (g % Pp::NS) * Pp::STAGE, acc, sa, sb, cks);
+    if constexpr (W4) mx4_compute<Pp>(smem + (g % Pp::NS) * Pp::STAGE, acc, sa, sb, cks);
+    else mx_compute<Pp>(smem + (g % Pp::NS) * Pp::STAGE, acc, sa, sb, cks);
     if (++cks == KT) {
       prob.epilogue(ct, acc);
       Pp::zero(acc);
@@ -1219,6 +1310,18 @@ __global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expe
       }
     }
   }
+}
+
+template <class Pp, int KIND>
+__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expert_mx(const ExpertArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
+  expert_mx_stream<Pp, ExpertMxProb<Pp, KIND>, false>(args, smem);
+}
+
+template <class Pp, int KIND>
+__global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expert_mx4(const ExpertArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem[Pp::LDS];
+  expert_mx_stream<Pp, ExpertMx4Prob<Pp, KIND>, true>(args, smem);
 }
 
 // MXFP8 quantisation of rows: each block of 32 consecutive elements gets the
@@ -1242,6 +1345,28 @@ MOE_DEV uint32_t f32_to_e4m3(float v) {
   return sgn | ((uint32_t)eb << 3) | mq;
 }
 
+// MXFP4 element: nearest E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6; ties to
+// even), saturating at 6; 4-bit code sign | exponent (2 bits, bias 1) | mantissa.
+MOE_DEV uint32_t f32_to_e2m1(float v) {
+  const uint32_t sgn = (__float_as_uint(v) >> 28) & 0x8u;
+  const float a = fabsf(v);
+  if (!(a < 6.0f)) return sgn | 0x7u;
+  if (a < 1.0f) return sgn | (uint32_t)__builtin_rintf(a * 2.0f);  // 0, 0.5 or 1.0 (codes 0, 1, 2)
+  int e;
+  (void)frexpf(a, &e);
+  int E = e - 1;  // 0, 1 or 2
+  uint32_t mq = (uint32_t)__builtin_rintf((ldexpf(a, -E) - 1.0f) * 2.0f);
+  if (mq == 2u) {
+    mq = 0u;
+    ++E;
+  }
+  if (E > 2) return sgn | 0x7u;
+  return sgn | ((uint32_t)(E + 1) << 1) | mq;
+}
+
+// W4: MXFP4 instead (scale 2^(floor(log2 amax) - 2), E2M1 elements, two per
+// byte, low nibble first; dst rows of K / 2 bytes).
+template <bool W4>
 __global__ __launch_bounds__(256) void k_mx_quant(const uint16_t* __restrict__ src, long long rows, int K,
                                                   long long ld_src, uint8_t* __restrict__ dst,
                                                   uint8_t* __restrict__ scales) {
@@ -1269,7 +1394,20 @@ __global__ __launch_bounds__(256) void k_mx_quant(const uint16_t* __restrict__ s
   if (amax > 0.f) {
     int e;
     (void)frexpf(amax, &e);
-    byte = min(254, max(0, e - 1 - 8 + 127));
+    byte = min(254, max(0, e - 1 - (W4 ? 2 : 8) + 127));
+  }
+  if constexpr (W4) {
+    uint32_t o[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x |= f32_to_e2m1(ldexpf(v[8 * w + j], 127 - byte)) << (4 * j);
+      o[w] = x;
+    }
+    *reinterpret_cast<uint4*>(dst + r * (K / 2) + (long long)bk * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+    scales[r * nb + bk] = (uint8_t)byte;
+    return;
   }
   uint32_t o[8];
 #pragma unroll
@@ -1711,37 +1849,52 @@ hipError_t launch_wgrad_km(const Dims& D, const WgradKmSpec& w, hipStream_t s) {
 
 // ------------------------------------------------------------- MXFP8 --
 hipError_t launch_mx_quant(const void* src, long long rows, int K, long long ld_src, uint8_t* dst, uint8_t* scales,
-                           hipStream_t s) {
+                           hipStream_t s, bool w4) {
   if (K % 32 || ld_src % 8) return hipErrorInvalidValue;
   const long long n = rows * (K / 32);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_mx_quant, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(src), rows, K, ld_src, dst, scales);
+  if (w4)
+    hipLaunchKernelGGL(k_mx_quant<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src), rows, K, ld_src, dst, scales);
+  else
+    hipLaunchKernelGGL(k_mx_quant<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src), rows, K, ld_src, dst, scales);
   return hipGetLastError();
 }
 
+using ExpertMx4Pipe = Mx4Pipe<kExpertBM, 256, 1, 4, 2, 2>;
+static_assert(ExpertMx4Pipe::BN == ExpertMxPipe::BN, "one weight-row tiling for both block-scaled formats");
+
 template <int KIND>
-static hipError_t launch_expert_mx(const Dims& D, const ExpertArgs& a, int T, hipStream_t s) {
-  using P = ExpertMxPipe;
+static hipError_t launch_expert_mx(const Dims& D, const ExpertArgs& a, int T, hipStream_t s, bool w4) {
   const long long tiles = (long long)expert_max_mtiles(T, D.k, D.E) * a.NT;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_expert_mx<P, KIND>), dim3(persistent_grid(tiles, P::BPC)), dim3(P::THREADS), 0, s, a);
+  if (w4) {
+    using P = ExpertMx4Pipe;
+    hipLaunchKernelGGL((k_gemm_expert_mx4<P, KIND>), dim3(persistent_grid(tiles, P::BPC)), dim3(P::THREADS), 0, s,
+                       a);
+  } else {
+    using P = ExpertMxPipe;
+    hipLaunchKernelGGL((k_gemm_expert_mx<P, KIND>), dim3(persistent_grid(tiles, P::BPC)), dim3(P::THREADS), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_expert_up_mx(const Dims& D, const uint8_t* z8, const uint8_t* Xs, const int32_t* perm_src,
                                const int2* tile_info, const int32_t* n_mtiles, int T, const uint8_t* Wg8,
-                               const uint8_t* Wgs, const uint8_t* Wu8, const uint8_t* Wus, void* H, hipStream_t s) {
+                               const uint8_t* Wgs, const uint8_t* Wu8, const uint8_t* Wus, void* H, hipStream_t s,
+                               bool w4) {
   constexpr int BN = ExpertMxPipe::BN, RB = ExpertMxPipe::RB;
   if (D.l % RB || D.l > 4 * RB) return hipErrorInvalidValue;
+  const int wb = w4 ? D.l / 2 : D.l;  // weight row bytes
   ExpertArgs a{};
   a.A = reinterpret_cast<const char*>(z8);
   a.lda_bytes = D.l;
   a.gather = perm_src;
   a.W = reinterpret_cast<const char*>(Wg8);
   a.Wu = reinterpret_cast<const char*>(Wu8);
-  a.ldb_bytes = D.l;
-  a.w_expert_bytes = (size_t)D.f * D.l;
+  a.ldb_bytes = wb;
+  a.w_expert_bytes = (size_t)D.f * wb;
   a.N = D.f;
   a.NT = (2 * D.f + BN - 1) / BN;
   a.kt = D.l / RB;
@@ -1754,22 +1907,23 @@ hipError_t launch_expert_up_mx(const Dims& D, const uint8_t* z8, const uint8_t* 
   a.sWu = Wus;
   a.s_ld = D.l / 32;
   a.w_rows = D.f;
-  return launch_expert_mx<EPI_GLU>(D, a, T, s);
+  return launch_expert_mx<EPI_GLU>(D, a, T, s, w4);
 }
 
 hipError_t launch_expert_down_mx(const Dims& D, const uint8_t* H8, const uint8_t* Hs, const int2* tile_info,
                                  const int32_t* n_mtiles, int T, const uint8_t* Wd8, const uint8_t* Wds, void* Y,
-                                 hipStream_t s) {
+                                 hipStream_t s, bool w4) {
   constexpr int BN = ExpertMxPipe::BN, RB = ExpertMxPipe::RB;
   if (D.f % RB || D.f > 4 * RB) return hipErrorInvalidValue;
+  const int wb = w4 ? D.f / 2 : D.f;  // weight row bytes
   ExpertArgs a{};
   a.A = reinterpret_cast<const char*>(H8);
   a.lda_bytes = D.f;
   a.gather = nullptr;
   a.W = reinterpret_cast<const char*>(Wd8);
   a.Wu = nullptr;
-  a.ldb_bytes = D.f;
-  a.w_expert_bytes = (size_t)D.l * D.f;
+  a.ldb_bytes = wb;
+  a.w_expert_bytes = (size_t)D.l * wb;
   a.N = D.l;
   a.NT = (D.l + BN - 1) / BN;
   a.kt = D.f / RB;
@@ -1782,7 +1936,7 @@ hipError_t launch_expert_down_mx(const Dims& D, const uint8_t* H8, const uint8_t
   a.sWu = nullptr;
   a.s_ld = D.f / 32;
   a.w_rows = D.l;
-  return launch_expert_mx<EPI_STORE>(D, a, T, s);
+  return launch_expert_mx<EPI_STORE>(D, a, T, s, w4);
 }
 
 }  // namespace moe

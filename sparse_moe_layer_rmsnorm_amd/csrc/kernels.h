@@ -170,20 +170,23 @@ hipError_t launch_gates_bwd(const Dims& D, const float* logits, const int32_t* i
 hipError_t launch_rmsnorm_bwd(const Dims& D, const void* x, const float* gamma, const float* dh, int T, void* dx,
                               float* rstd, float* part, int slices, float* dgamma, hipStream_t s);
 
-// ------------------------------------------------------------------ MXFP8 --
+// ------------------------------------------------------- block-scaled experts --
 // rows x K bf16 (ld_src elements) -> E4M3 bytes [rows, K] + E8M0 scales
-// [rows, K/32] (one per 32 consecutive elements).
+// [rows, K/32] (one per 32 consecutive elements); w4: E2M1 elements two per
+// byte (low nibble first) [rows, K/2] with the MXFP4 scale instead.
 hipError_t launch_mx_quant(const void* src, long long rows, int K, long long ld_src, uint8_t* dst, uint8_t* scales,
-                           hipStream_t s);
-// Expert GEMM 1 + GLU with MXFP8 operands (A rows z8[perm_src[r]] with the
-// scale rows Xs[r] the scatter copied; K = l <= 512, a multiple of 128); H
-// in bf16.
+                           hipStream_t s, bool w4 = false);
+// Expert GEMM 1 + GLU with MXFP8 activations (A rows z8[perm_src[r]] with the
+// scale rows Xs[r] the scatter copied; K = l <= 512, a multiple of 128) and
+// MXFP8 weights, or MXFP4 weights with w4; H in bf16.
 hipError_t launch_expert_up_mx(const Dims& D, const uint8_t* z8, const uint8_t* Xs, const int32_t* perm_src,
                                const int2* tile_info, const int32_t* n_mtiles, int T, const uint8_t* Wg8,
-                               const uint8_t* Wgs, const uint8_t* Wu8, const uint8_t* Wus, void* H, hipStream_t s);
-// Expert GEMM 2 with MXFP8 operands (K = f <= 512, a multiple of 128); Y in bf16.
+                               const uint8_t* Wgs, const uint8_t* Wu8, const uint8_t* Wus, void* H, hipStream_t s,
+                               bool w4 = false);
+// Expert GEMM 2 with MXFP8 activations (K = f <= 512, a multiple of 128) and
+// MXFP8 or (w4) MXFP4 weights; Y in bf16.
 hipError_t launch_expert_down_mx(const Dims& D, const uint8_t* H8, const uint8_t* Hs, const int2* tile_info,
                                  const int32_t* n_mtiles, int T, const uint8_t* Wd8, const uint8_t* Wds, void* Y,
-                                 hipStream_t s);
+                                 hipStream_t s, bool w4 = false);
 
 }  // namespace moe

@@ -41,12 +41,14 @@ moe_status check_config(const moe_config* c) {
     return fail(MOE_ERR_INVALID_ARG, "unknown balancer %d", (int)c->balancer);
   if (c->balancer == MOE_BALANCE_SIGN && !(c->sign_gamma > 0.f && std::isfinite(c->sign_gamma)))
     return fail(MOE_ERR_INVALID_ARG, "sign_gamma must be finite and > 0");
-  if (c->experts != MOE_EXPERTS_BF16 && c->experts != MOE_EXPERTS_MXFP8)
+  if (c->experts != MOE_EXPERTS_BF16 && c->experts != MOE_EXPERTS_MXFP8 && c->experts != MOE_EXPERTS_MXFP4)
     return fail(MOE_ERR_INVALID_ARG, "unknown expert format %d", (int)c->experts);
-  if (c->experts == MOE_EXPERTS_MXFP8) {
-    if (c->dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "MXFP8 experts need the bf16 mode");
+  if (c->experts != MOE_EXPERTS_BF16) {
+    const char* fmt = c->experts == MOE_EXPERTS_MXFP8 ? "MXFP8" : "MXFP4";
+    if (c->dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "%s experts need the bf16 mode", fmt);
     if (c->l % 128 || c->f % 128 || c->l > 512 || c->f > 512)
-      return fail(MOE_ERR_SHAPE, "MXFP8 experts need l and f multiples of 128, at most 512 (l=%d f=%d)", c->l, c->f);
+      return fail(MOE_ERR_SHAPE, "%s experts need l and f multiples of 128, at most 512 (l=%d f=%d)", fmt, c->l,
+                  c->f);
   }
   if (c->keep_preact != 0 && c->keep_preact != 1) return fail(MOE_ERR_INVALID_ARG, "keep_preact must be 0 or 1");
   if (c->keep_preact && c->experts != MOE_EXPERTS_BF16)
@@ -96,9 +98,10 @@ void state_layout(const moe_config* c, moe_state_layout* L) {
   L->load = o;
   o = up(o + (size_t)c->E * 4);
   L->mx = o;
-  if (c->experts == MOE_EXPERTS_MXFP8) {
+  if (c->experts != MOE_EXPERTS_BF16) {
     const size_t w = (size_t)c->E * c->f * c->l;  // elements of each expert weight tensor
-    o = up(o + 3 * w + 3 * (w / 32));
+    const size_t wb = c->experts == MOE_EXPERTS_MXFP4 ? w / 2 : w;  // their bytes: E2M1 pairs or E4M3
+    o = up(o + 3 * wb + 3 * (w / 32));
   }
   L->total = o;
 }
@@ -133,7 +136,7 @@ void ws_layout(const moe_config* c, int64_t T, moe_ws_layout* L) {
   L->H = take(t * k * c->f * es);
   L->Y = take(t * k * c->l * es);
   L->y_lat = take(t * c->l * es);
-  const bool mx = c->experts == MOE_EXPERTS_MXFP8;
+  const bool mx = c->experts != MOE_EXPERTS_BF16;  // MXFP8 activations in both block-scaled formats
   L->z8 = take(mx ? t * c->l : 0);
   L->zs = take(mx ? t * c->l / 32 : 0);
   L->Xs = take(mx ? t * k * c->l / 32 : 0);
@@ -293,19 +296,23 @@ void bwd_layout(const moe_config* c, int64_t T, BwdLayout* L) {
 struct MxWeights {
   uint8_t *g8, *u8, *d8, *gs, *us, *ds;
 };
+// The block-scaled expert weights in the state: W_g, W_u, W_d elements (E4M3
+// bytes, or E2M1 pairs for MXFP4), then their scale bytes.
 MxWeights mx_weights(moe_ctx* ctx) {
   const size_t w = (size_t)ctx->cfg.E * ctx->cfg.f * ctx->cfg.l;
+  const size_t wb = ctx->cfg.experts == MOE_EXPERTS_MXFP4 ? w / 2 : w;
   uint8_t* b = reinterpret_cast<uint8_t*>(ctx->state + ctx->sl.mx);
-  return {b, b + w, b + 2 * w, b + 3 * w, b + 3 * w + w / 32, b + 3 * w + 2 * (w / 32)};
+  return {b, b + wb, b + 2 * wb, b + 3 * wb, b + 3 * wb + w / 32, b + 3 * wb + 2 * (w / 32)};
 }
 
 hipError_t quantize_experts(moe_ctx* ctx, hipStream_t s) {
   const moe_config& c = ctx->cfg;
   const MxWeights m = mx_weights(ctx);
+  const bool w4 = c.experts == MOE_EXPERTS_MXFP4;
   const long long rows_gu = (long long)c.E * c.f, rows_d = (long long)c.E * c.l;
-  hipError_t e = launch_mx_quant(ctx->w.W_g, rows_gu, c.l, c.l, m.g8, m.gs, s);
-  if (e == hipSuccess) e = launch_mx_quant(ctx->w.W_u, rows_gu, c.l, c.l, m.u8, m.us, s);
-  if (e == hipSuccess) e = launch_mx_quant(ctx->w.W_d, rows_d, c.f, c.f, m.d8, m.ds, s);
+  hipError_t e = launch_mx_quant(ctx->w.W_g, rows_gu, c.l, c.l, m.g8, m.gs, s, w4);
+  if (e == hipSuccess) e = launch_mx_quant(ctx->w.W_u, rows_gu, c.l, c.l, m.u8, m.us, s, w4);
+  if (e == hipSuccess) e = launch_mx_quant(ctx->w.W_d, rows_d, c.f, c.f, m.d8, m.ds, s, w4);
   return e;
 }
 
@@ -367,7 +374,7 @@ moe_status moe_init(const moe_config* cfg, const moe_weights* w, void* state, vo
   c->D = dims_of(cfg);
   c->pending_tokens = 0;
   hipError_t e = launch_zero(state, c->sl.total, static_cast<hipStream_t>(stream));
-  if (e == hipSuccess && cfg->experts == MOE_EXPERTS_MXFP8) e = quantize_experts(c, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && cfg->experts != MOE_EXPERTS_BF16) e = quantize_experts(c, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     delete c;
     return fail(MOE_ERR_HIP, "clearing the state failed: %s", hipGetErrorString(e));
@@ -417,7 +424,8 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
                                       ctx->w.W_dn, p.logits, D.f_s > 0 ? G : nullptr, z, s,
                                       keep && D.f_s > 0 ? w + L.P : nullptr, keep && D.f_s > 0 ? w + L.Q : nullptr));
   const int32_t* n_mtiles = p.tile_offsets + D.E;
-  if (ctx->cfg.experts == MOE_EXPERTS_MXFP8) {
+  if (ctx->cfg.experts != MOE_EXPERTS_BF16) {
+    const bool w4 = ctx->cfg.experts == MOE_EXPERTS_MXFP4;
     // z -> MXFP8; the scatter copies each token's scale row to its grouped rows
     uint8_t *z8 = reinterpret_cast<uint8_t*>(w + L.z8), *zs = reinterpret_cast<uint8_t*>(w + L.zs);
     uint8_t *Xs = reinterpret_cast<uint8_t*>(w + L.Xs), *H8 = reinterpret_cast<uint8_t*>(w + L.H8);
@@ -427,9 +435,9 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
     st = route_tail(ctx, p, t, s, zs, Xs);
     if (st != MOE_OK) return st;
     MOE_RUN(MOE_K_EXPERT_UP, launch_expert_up_mx(D, z8, Xs, p.perm_src, p.tile_info, n_mtiles, t, m.g8, m.gs, m.u8,
-                                                 m.us, H, s));
+                                                 m.us, H, s, w4));
     MOE_RUN(MOE_K_MX_QUANT, launch_mx_quant(H, (long long)t * D.k, D.f, D.f, H8, Hs, s));
-    MOE_RUN(MOE_K_EXPERT_DOWN, launch_expert_down_mx(D, H8, Hs, p.tile_info, n_mtiles, t, m.d8, m.ds, Y, s));
+    MOE_RUN(MOE_K_EXPERT_DOWN, launch_expert_down_mx(D, H8, Hs, p.tile_info, n_mtiles, t, m.d8, m.ds, Y, s, w4));
   } else {
     st = route_tail(ctx, p, t, s);
     if (st != MOE_OK) return st;
@@ -644,7 +652,7 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
 
 moe_status moe_requantize_experts(moe_ctx* ctx, void* stream) {
   if (!ctx) return fail(MOE_ERR_INVALID_ARG, "context is NULL");
-  if (ctx->cfg.experts != MOE_EXPERTS_MXFP8) return MOE_OK;
+  if (ctx->cfg.experts == MOE_EXPERTS_BF16) return MOE_OK;
   return hip_ok(quantize_experts(ctx, static_cast<hipStream_t>(stream)), "expert quantisation");
 }
 

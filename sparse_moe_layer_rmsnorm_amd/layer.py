@@ -89,7 +89,7 @@ class MoeLayer:
             "Y": view(L.Y, T * dm["k"] * dm["l"], es, (T * dm["k"], dm["l"])),
             "y_lat": view(L.y_lat, T * dm["l"], es, (T, dm["l"])),
             "tile_offsets": view(L.tile_offsets, dm["E"] + 1, torch.int32, (dm["E"] + 1,)),
-            # MXFP8 experts only (empty otherwise): E4M3 bytes and E8M0 scales of z and H
+            # block-scaled experts only (empty otherwise): E4M3 bytes and E8M0 scales of z and H
             "z8": view(L.z8, L.zs - L.z8, torch.uint8, (-1,)),
             "zs": view(L.zs, L.Xs - L.zs, torch.uint8, (-1,)),
             "H8": view(L.H8, L.Hs - L.H8, torch.uint8, (-1,)),

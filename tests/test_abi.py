@@ -87,19 +87,23 @@ def test_sign_gamma_checked_only_for_the_sign_balancer(gamma, ok):
     (dict(), None), (dict(dtype="f32"), B.MOE_ERR_DTYPE), (dict(l=64), B.MOE_ERR_SHAPE),
     (dict(f=192), B.MOE_ERR_SHAPE), (dict(f=640), B.MOE_ERR_SHAPE), (dict(l=1024), B.MOE_ERR_SHAPE),
 ])
-def test_mxfp8_experts_config(L, over, status):
-    """MXFP8 experts: bf16 mode only, l and f multiples of 128 up to 512; the
-    state then holds the quantised expert weights and their scales."""
+@pytest.mark.parametrize("fmt,bpe", [("mxfp8", 1.0), ("mxfp4", 0.5)])
+def test_mxfp8_experts_config(L, over, status, fmt, bpe):
+    """Block-scaled experts (MXFP8; MXFP4 weights): bf16 mode only, l and f
+    multiples of 128 up to 512; the state then holds the quantised expert
+    weights (1 or 1/2 byte per element) and their scales."""
     args = dict(REPLICA)
+    over = dict(over)
     dtype = over.pop("dtype", "bf16")
     args.update(over)
-    cfg = B.make_config(**args, dtype=dtype, max_tokens=64, experts="mxfp8")
+    cfg = B.make_config(**args, dtype=dtype, max_tokens=64, experts=fmt)
     if status is None:
         st = B.moe_state_layout_of(cfg)
         w = args["E"] * args["f"] * args["l"]
-        assert st.total >= st.mx + 3 * w + 3 * w // 32
+        need = int(3 * w * bpe) + 3 * w // 32
+        assert need <= st.total - st.mx <= need + 256
         ref = B.make_config(**args, dtype=dtype, max_tokens=64)
-        assert B.moe_state_bytes(cfg) >= B.moe_state_bytes(ref) + 3 * w
+        assert B.moe_state_bytes(cfg) >= B.moe_state_bytes(ref) + int(3 * w * bpe)
     else:
         assert B.moe_state_bytes(cfg) == 0
         ctx = ctypes.c_void_p()

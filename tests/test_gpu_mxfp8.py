@@ -1,14 +1,15 @@
-"""GPU parity of the MXFP8 expert path (low-precision experts) through the C
-ABI, against the oracle's MXFP8 rounding (itself pinned to torch's E4M3
-conversion).
+"""GPU parity of the block-scaled expert paths (low-precision experts) through
+the C ABI: MXFP8 weights and activations, and MXFP4 weights against MXFP8
+activations, each against the oracle's rounding (MXFP8 pinned to torch's E4M3
+conversion, MXFP4 to a brute-force E2M1 search).
 
 The quantised weights in the state buffer must equal the oracle's element
-for element (bytes decoded to values, scales bit for bit); a forward routes
-bit-exactly given its logits, and z, H, Y, y_lat and out agree with the
-oracle: the quantisation of z and H bit for bit given the same bf16 input,
-each expert GEMM on the GPU's own input within the layer tolerance (2e-2 of
-the largest magnitude), and the whole chain end to end within 5e-2 (a
-one-ulp bf16 difference upstream can move an element by one E4M3 step)."""
+for element (bytes or nibbles decoded to values, scales bit for bit); a
+forward routes bit-exactly given its logits, and z, H, Y, y_lat and out agree
+with the oracle: the quantisation of z and H bit for bit given the same bf16
+input, each expert GEMM on the GPU's own input within the layer tolerance
+(2e-2 of the largest magnitude), and the whole chain end to end within 5e-2
+(a one-ulp bf16 difference upstream can move an element by one E4M3 step)."""
 import numpy as np
 import pytest
 import torch
@@ -35,13 +36,34 @@ def _e4m3_values(b: np.ndarray) -> np.ndarray:
     return s * v
 
 
-def _state_mx(layer, shape):
+def _e2m1_values(b: np.ndarray) -> np.ndarray:
+    """Bytes holding two E2M1 codes (low nibble first) -> 2 values each."""
+    b = b.astype(np.int64)
+    codes = np.stack([b & 15, b >> 4], axis=-1).reshape(-1)
+    s = np.where(codes & 8, -1.0, 1.0)
+    e, m = (codes >> 1) & 3, codes & 1
+    return s * np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e - 1.0))
+
+
+FORMATS = {  # name: (decode of the weight bytes, weight rounding, bytes per element)
+    "mxfp8": (_e4m3_values, o.mx_quantize, 1.0),
+    "mxfp4": (_e2m1_values, o.mx4_quantize, 0.5),
+}
+
+
+def _state_mx(layer, shape, fmt):
     E, f, l = shape.E, shape.f, shape.l
     w = E * f * l
-    raw = to_np(layer.state[layer.sl.mx:layer.sl.mx + 3 * w + 3 * (w // 32)])
-    q = [_e4m3_values(raw[i * w:(i + 1) * w]) for i in range(3)]
-    sc = [raw[3 * w + i * (w // 32): 3 * w + (i + 1) * (w // 32)].astype(np.int64) for i in range(3)]
+    dec, _, bpe = FORMATS[fmt]
+    wb = int(w * bpe)
+    raw = to_np(layer.state[layer.sl.mx:layer.sl.mx + 3 * wb + 3 * (w // 32)])
+    q = [dec(raw[i * wb:(i + 1) * wb]) for i in range(3)]
+    sc = [raw[3 * wb + i * (w // 32): 3 * wb + (i + 1) * (w // 32)].astype(np.int64) for i in range(3)]
     return q, sc
+
+
+def _wround(fmt):
+    return o.mx4_round if fmt == "mxfp4" else o.mx_round
 
 
 SHAPES = [  # name, T, d, l, E, k, f, f_s
@@ -51,17 +73,20 @@ SHAPES = [  # name, T, d, l, E, k, f, f_s
 ]
 
 
+@pytest.mark.parametrize("fmt", list(FORMATS))
 @pytest.mark.parametrize("case", SHAPES, ids=[c[0] for c in SHAPES])
-def test_mxfp8_weights_and_forward_match_oracle(case):
+def test_mxfp8_weights_and_forward_match_oracle(case, fmt):
     name, T, d, l, E, k, f, f_s = case
-    say(f"mxfp8 {name}: T={T} d={d} l={l} E={E} k={k} f={f} f_s={f_s}")
+    say(f"{fmt} {name}: T={T} d={d} l={l} E={E} k={k} f={f} f_s={f_s}")
     shape = wl.LayerShape(name, 31, "bf16", T=T, d=d, l=l, E=E, k=k, f=f, f_s=f_s, B=256)
     W = wl.make_weights(shape)
-    layer = make_layer(shape, W, max_tokens=T, experts="mxfp8")
+    layer = make_layer(shape, W, max_tokens=T, experts=fmt)
     torch.cuda.synchronize()
-    q, sc = _state_mx(layer, shape)
+    q, sc = _state_mx(layer, shape, fmt)
+    wq = FORMATS[fmt][1]
+    rw = _wround(fmt)
     for i, n in enumerate(("W_g", "W_u", "W_d")):
-        rq, rs = o.mx_quantize(W[n].reshape(-1, W[n].shape[-1]))
+        rq, rs = wq(W[n].reshape(-1, W[n].shape[-1]))
         np.testing.assert_array_equal(sc[i], rs.reshape(-1), err_msg=n)
         np.testing.assert_array_equal(q[i], rq.reshape(-1), err_msg=n)
     x = wl.make_x(shape)
@@ -69,7 +94,7 @@ def test_mxfp8_weights_and_forward_match_oracle(case):
     out = layer.forward(x_on_gpu(x, layer), route=r)
     torch.cuda.synchronize()
     lg = to_np(r["logits"])
-    ref = o.forward(x, W, np.zeros(E, F32), k=k, dtype="bf16", eps=shape.rms_eps, logits=lg, experts="mxfp8")
+    ref = o.forward(x, W, np.zeros(E, F32), k=k, dtype="bf16", eps=shape.rms_eps, logits=lg, experts=fmt)
     assert_routing_equal(r, ref, T)
     v = layer.ws_views(T)
     z, H, Y = to_np(v["z"]).astype(np.float64), to_np(v["H"]).astype(np.float64), to_np(v["Y"]).astype(np.float64)
@@ -85,8 +110,8 @@ def test_mxfp8_weights_and_forward_match_oracle(case):
     for e in range(E):
         a, b = int(offs[e]), int(offs[e + 1])
         if a < b:
-            H_ref[a:b] = o.bf16_round(o.glu(Xq[a:b], o.mx_round(W["W_g"][e]), o.mx_round(W["W_u"][e])))
-            Y_ref[a:b] = o.bf16_round(o.mx_round(H[a:b]) @ o.mx_round(W["W_d"][e]).T)
+            H_ref[a:b] = o.bf16_round(o.glu(Xq[a:b], rw(W["W_g"][e]), rw(W["W_u"][e])))
+            Y_ref[a:b] = o.bf16_round(o.mx_round(H[a:b]) @ rw(W["W_d"][e]).T)
     for n, got, want in (("H", H, H_ref), ("Y", Y, Y_ref)):
         err = rel_err(got, want)
         say(f"  {n} (on the GPU's input) rel err {err:.3e}")
@@ -110,33 +135,35 @@ def _check_quant(q8, qs, a):
     np.testing.assert_array_equal(_e4m3_values(q8), rq.reshape(-1))
 
 
-def test_mxfp8_replica_sampled_and_requantize():
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_mxfp8_replica_sampled_and_requantize(fmt):
     """Full replica size (T=8192): routing bit-exact, sampled tokens within
     tolerance; moe_requantize_experts after changing W_d picks up the change."""
     shape = wl.workload("replica")
     T = shape.T
+    say(f"{fmt} replica T={T}")
     W = wl.make_weights(shape)
-    layer = make_layer(shape, W, max_tokens=T, experts="mxfp8")
+    layer = make_layer(shape, W, max_tokens=T, experts=fmt)
     x = wl.make_x(shape)
     r = layer.route_buffers(T)
     out = layer.forward(x_on_gpu(x, layer), route=r)
     torch.cuda.synchronize()
     lg = to_np(r["logits"])
     ref = o.forward(x, W, np.zeros(shape.E, F32), k=shape.k, dtype="bf16", eps=shape.rms_eps, logits=lg,
-                    experts="mxfp8")
+                    experts=fmt)
     assert_routing_equal(r, ref, T)
     pick = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(5).integers(0, T, 24)]))
     want = o.forward_tokens(x[pick], W, ref["idx"][pick], ref["gates"][pick], dtype="bf16", eps=shape.rms_eps,
-                            experts="mxfp8")
+                            experts=fmt)
     e = rel_err(to_np(out)[pick], want)
     say(f"  replica sampled out rel err {e:.3e}")
     assert e <= MX_E2E_TOL
-    layer.w["W_d"].mul_(2)                                   # exact in bf16 and in MXFP8 (scale + 1)
+    layer.w["W_d"].mul_(2)                                   # exact in bf16 and in MX formats (scale + 1)
     Bd.moe_requantize_experts(layer.ctx, torch.cuda.current_stream().cuda_stream)
     out2 = layer.forward(x_on_gpu(x, layer), route=r)
     torch.cuda.synchronize()
     W2 = dict(W, W_d=W["W_d"] * 2)
     want2 = o.forward_tokens(x[pick], W2, ref["idx"][pick], ref["gates"][pick], dtype="bf16", eps=shape.rms_eps,
-                             experts="mxfp8")
+                             experts=fmt)
     assert rel_err(to_np(out2)[pick], want2) <= MX_E2E_TOL
     layer.close()
