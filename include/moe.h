@@ -317,7 +317,7 @@ enum {
   /* backward: dense products, grouped expert products, weight gradients,
      elementwise transposes and derivatives, (unused) */
   MOE_K_BWD_GEMM, MOE_K_BWD_EXPERT, MOE_K_BWD_WGRAD, MOE_K_BWD_ELTWISE, MOE_K_BWD_TRANSPOSE,
-  MOE_K_MX_QUANT, /* MXFP8 quantisation of z and H */
+  MOE_K_MX_QUANT, /* MXFP8 quantisation of z (H is quantised in expert_up's epilogue) */
   MOE_NUM_KERNELS
 };
 const char* moe_kernel_name(int id);

@@ -43,7 +43,10 @@
 namespace moe {
 namespace {
 
-enum EpiKind { EPI_F32 = 0, EPI_STORE = 1, EPI_GLU = 2 };
+// EPI_GLU_MX: EPI_GLU whose output is also quantised to MXFP8 (E4M3 + E8M0
+// per 32 columns) in the epilogue.
+enum EpiKind { EPI_F32 = 0, EPI_STORE = 1, EPI_GLU = 2, EPI_GLU_MX = 3 };
+constexpr bool is_glu(int kind) { return kind == EPI_GLU || kind == EPI_GLU_MX; }
 
 
 template <bool BF16>
@@ -109,6 +112,27 @@ MOE_DEV long long uniform_ll(long long v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
   return (long long)(((uint64_t)hi << 32) | lo);
+}
+
+// Block-scaled element conversion (MXFP8 / MXFP4) is the hardware's: the
+// value is scaled by the block's power of two in fp32 (exact), clamped to
+// +-448 (v_cvt_pk_fp8_f32 does not saturate: 464 and above become NaN) and
+// converted by v_cvt_pk_fp8_f32, which rounds to nearest even; E2M1 through
+// v_cvt_scalef32_pk_fp4_f32 with scale 1, which rounds to nearest even and
+// saturates at 6 by itself (both measured on gfx950 over every finite bf16
+// value at 11 scales: identical to the reference rounding).
+MOE_DEV uint32_t e4m3x4(float a, float b, float c, float d) {
+  auto cl = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), lo, true);
+}
+MOE_DEV uint32_t e2m1x8(const float* v) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[0], v[1], 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], 1.0f, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], 1.0f, 3);
+  return r;
 }
 
 // Source of K rows that lie past an operand's end (read by the stage DMA in
@@ -310,19 +334,58 @@ struct Pipe {
 
   // EPI_GLU with keep_g / keep_u (wave-uniform, nullable): the gate and up
   // pre-activations are stored too, at the same place as the output.
+  // MXFP8 quantisation of one 32-column block of a GLU output row (the two
+  // 16-column halves x, y of store_pair, c0 a multiple of 32): the values
+  // are rounded to bf16 as stored, the block maximum is taken over the 4
+  // lanes of the row, then each lane converts its 8 values.  q8 rows of N
+  // bytes, qs rows of N / 32 scale bytes.
+  MOE_DEV static void mx8_block(void* q8, void* qs, size_t row, int c0, int N, bool row_ok, const float (&x)[4],
+                                const float (&y)[4]) {
+    const int lane = threadIdx.x & 63, q = (lane >> 4) & 3;
+    const uint32_t p[4] = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]),
+                           pack_bf16x2(y[2], y[3])};
+    float v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_bits_to_f32(p[j] & 0xFFFFu);
+      v[2 * j + 1] = bf16_bits_to_f32(p[j] >> 16);
+      amax = fmaxf(amax, fmaxf(fabsf(v[2 * j]), fabsf(v[2 * j + 1])));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    int byte = 0;
+    if (amax > 0.f) {
+      int e;
+      (void)frexpf(amax, &e);
+      byte = min(254, max(0, e - 1 - 8 + 127));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = ldexpf(v[j], 127 - byte);
+    const uint32_t w0 = e4m3x4(v[0], v[1], v[2], v[3]), w1 = e4m3x4(v[4], v[5], v[6], v[7]);
+    if (row_ok && c0 < N) {
+      uint8_t* d = static_cast<uint8_t*>(q8) + row * (size_t)N + c0;
+      *reinterpret_cast<uint32_t*>(d + 4 * q) = w0;
+      *reinterpret_cast<uint32_t*>(d + 16 + 4 * q) = w1;
+      if (q == 0) static_cast<uint8_t*>(qs)[row * (size_t)(N / 32) + c0 / 32] = (uint8_t)byte;
+    }
+  }
+
+  // EPI_GLU_MX: keep_g / keep_u are the MXFP8 bytes and scale bytes of the output.
   template <int KIND>
   MOE_DEV static void epilogue(const Acc& acc, int rows_valid, int n0, int N, void* out, int ldo, size_t row_base,
                                const __attribute__((address_space(3))) float* col_off, void* keep_g = nullptr,
                                void* keep_u = nullptr) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int wm = wave / WN, wn = wave % WN;
+    static_assert(KIND != EPI_GLU_MX || (BF16 && NI % 4 == 0), "MXFP8 epilogue: paired bf16 stores only");
     if constexpr (BF16 && KIND != EPI_F32 && NI % 4 == 0) {  // paired 16-byte stores (N is a multiple of 64)
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int m = wm * WTM + mi * 16 + (lane & 15);
         const bool row_ok = m < rows_valid;
         const size_t orow = (row_base + (size_t)(row_ok ? m : 0)) * (size_t)ldo;
-        if constexpr (KIND == EPI_GLU) {
+        if constexpr (is_glu(KIND)) {
 #pragma unroll
           for (int p = 0; p < NI / 2; p += 2) {
             float o[2][4], gk[2][4], uk[2][4];
@@ -338,7 +401,9 @@ struct Pipe {
             }
             const int c0 = n0 / 2 + ((wn * WTN) / 32 + p) * 16;
             store_pair(out, orow, c0, N, row_ok, o[0], o[1]);
-            if (keep_g) {
+            if constexpr (KIND == EPI_GLU_MX) {
+              mx8_block(keep_g, keep_u, row_base + (size_t)(row_ok ? m : 0), c0, N, row_ok, o[0], o[1]);
+            } else if (keep_g) {
               store_pair(keep_g, orow, c0, N, row_ok, gk[0], gk[1]);
               store_pair(keep_u, orow, c0, N, row_ok, uk[0], uk[1]);
             }
@@ -685,7 +750,7 @@ struct ExpertProb {
     const char* gate = uniform_ptr(a.W);
     int wrow;
     const char* base;
-    if (KIND == EPI_GLU) {
+    if (is_glu(KIND)) {
       wrow = t.nt * (Pp::BN / 2) + (c >> 5) * 16 + (c & 15);
       base = ((c & 31) >= 16) ? uniform_ptr(a.Wu) : gate;
     } else {
@@ -1147,7 +1212,7 @@ struct ExpertMxProb : ExpertProb<Pp, KIND> {
       const int c = wn * Pp::WTN + ni * 16 + (lane & 15);
       int wrow;
       const uint8_t* base;
-      if (KIND == EPI_GLU) {
+      if (is_glu(KIND)) {
         wrow = t.nt * (Pp::BN / 2) + (c >> 5) * 16 + (c & 15);
         base = (c & 31) >= 16 ? a.sWu : a.sW;
       } else {
@@ -1327,43 +1392,6 @@ __global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_expe
 // MXFP8 quantisation of rows: each block of 32 consecutive elements gets the
 // scale 2^(floor(log2 amax) - 8) (E8M0 byte, clamped to [0, 254], 0 for an
 // all-zero block) and E4M3 elements, round to nearest even, saturating at 448.
-MOE_DEV uint32_t f32_to_e4m3(float v) {
-  const uint32_t sgn = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (!(a < 464.0f)) return sgn | 0x7Eu;
-  if (a < 0x1p-6f) return sgn | (uint32_t)__builtin_rintf(a * 512.0f);  // subnormal step 2^-9 (8 -> 2^-6)
-  int e;
-  (void)frexpf(a, &e);
-  const int E = e - 1;
-  const float m = ldexpf(a, -E);
-  uint32_t mq = (uint32_t)__builtin_rintf((m - 1.0f) * 8.0f);
-  int eb = E + 7;
-  if (mq == 8u) {
-    mq = 0u;
-    ++eb;
-  }
-  return sgn | ((uint32_t)eb << 3) | mq;
-}
-
-// MXFP4 element: nearest E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6; ties to
-// even), saturating at 6; 4-bit code sign | exponent (2 bits, bias 1) | mantissa.
-MOE_DEV uint32_t f32_to_e2m1(float v) {
-  const uint32_t sgn = (__float_as_uint(v) >> 28) & 0x8u;
-  const float a = fabsf(v);
-  if (!(a < 6.0f)) return sgn | 0x7u;
-  if (a < 1.0f) return sgn | (uint32_t)__builtin_rintf(a * 2.0f);  // 0, 0.5 or 1.0 (codes 0, 1, 2)
-  int e;
-  (void)frexpf(a, &e);
-  int E = e - 1;  // 0, 1 or 2
-  uint32_t mq = (uint32_t)__builtin_rintf((ldexpf(a, -E) - 1.0f) * 2.0f);
-  if (mq == 2u) {
-    mq = 0u;
-    ++E;
-  }
-  if (E > 2) return sgn | 0x7u;
-  return sgn | ((uint32_t)(E + 1) << 1) | mq;
-}
-
 // W4: MXFP4 instead (scale 2^(floor(log2 amax) - 2), E2M1 elements, two per
 // byte, low nibble first; dst rows of K / 2 bytes).
 template <bool W4>
@@ -1396,27 +1424,19 @@ __global__ __launch_bounds__(256) void k_mx_quant(const uint16_t* __restrict__ s
     (void)frexpf(amax, &e);
     byte = min(254, max(0, e - 1 - (W4 ? 2 : 8) + 127));
   }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) v[j] = ldexpf(v[j], 127 - byte);
   if constexpr (W4) {
     uint32_t o[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t x = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x |= f32_to_e2m1(ldexpf(v[8 * w + j], 127 - byte)) << (4 * j);
-      o[w] = x;
-    }
+    for (int w = 0; w < 4; ++w) o[w] = e2m1x8(v + 8 * w);
     *reinterpret_cast<uint4*>(dst + r * (K / 2) + (long long)bk * 16) = make_uint4(o[0], o[1], o[2], o[3]);
     scales[r * nb + bk] = (uint8_t)byte;
     return;
   }
   uint32_t o[8];
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t x = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x |= f32_to_e4m3(ldexpf(v[4 * w + j], 127 - byte)) << (8 * j);
-    o[w] = x;
-  }
+  for (int w = 0; w < 8; ++w) o[w] = e4m3x4(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3]);
   uint4* d = reinterpret_cast<uint4*>(dst + r * K + (long long)bk * 32);
   d[0] = make_uint4(o[0], o[1], o[2], o[3]);
   d[1] = make_uint4(o[4], o[5], o[6], o[7]);
@@ -1882,8 +1902,8 @@ static hipError_t launch_expert_mx(const Dims& D, const ExpertArgs& a, int T, hi
 
 hipError_t launch_expert_up_mx(const Dims& D, const uint8_t* z8, const uint8_t* Xs, const int32_t* perm_src,
                                const int2* tile_info, const int32_t* n_mtiles, int T, const uint8_t* Wg8,
-                               const uint8_t* Wgs, const uint8_t* Wu8, const uint8_t* Wus, void* H, hipStream_t s,
-                               bool w4) {
+                               const uint8_t* Wgs, const uint8_t* Wu8, const uint8_t* Wus, void* H, uint8_t* H8,
+                               uint8_t* Hs, hipStream_t s, bool w4) {
   constexpr int BN = ExpertMxPipe::BN, RB = ExpertMxPipe::RB;
   if (D.l % RB || D.l > 4 * RB) return hipErrorInvalidValue;
   const int wb = w4 ? D.l / 2 : D.l;  // weight row bytes
@@ -1907,7 +1927,10 @@ hipError_t launch_expert_up_mx(const Dims& D, const uint8_t* z8, const uint8_t* 
   a.sWu = Wus;
   a.s_ld = D.l / 32;
   a.w_rows = D.f;
-  return launch_expert_mx<EPI_GLU>(D, a, T, s, w4);
+  a.keep[0] = H8;  // H quantised to MXFP8 in the epilogue
+  a.keep[1] = Hs;
+  if (!H8 || !Hs) return hipErrorInvalidValue;
+  return launch_expert_mx<EPI_GLU_MX>(D, a, T, s, w4);
 }
 
 hipError_t launch_expert_down_mx(const Dims& D, const uint8_t* H8, const uint8_t* Hs, const int2* tile_info,

@@ -178,11 +178,12 @@ hipError_t launch_mx_quant(const void* src, long long rows, int K, long long ld_
                            hipStream_t s, bool w4 = false);
 // Expert GEMM 1 + GLU with MXFP8 activations (A rows z8[perm_src[r]] with the
 // scale rows Xs[r] the scatter copied; K = l <= 512, a multiple of 128) and
-// MXFP8 weights, or MXFP4 weights with w4; H in bf16.
+// MXFP8 weights, or MXFP4 weights with w4; H in bf16, and H quantised to
+// MXFP8 in the epilogue (H8 [rows, f] bytes, Hs [rows, f/32] scales).
 hipError_t launch_expert_up_mx(const Dims& D, const uint8_t* z8, const uint8_t* Xs, const int32_t* perm_src,
                                const int2* tile_info, const int32_t* n_mtiles, int T, const uint8_t* Wg8,
-                               const uint8_t* Wgs, const uint8_t* Wu8, const uint8_t* Wus, void* H, hipStream_t s,
-                               bool w4 = false);
+                               const uint8_t* Wgs, const uint8_t* Wu8, const uint8_t* Wus, void* H, uint8_t* H8,
+                               uint8_t* Hs, hipStream_t s, bool w4 = false);
 // Expert GEMM 2 with MXFP8 activations (K = f <= 512, a multiple of 128) and
 // MXFP8 or (w4) MXFP4 weights; Y in bf16.
 hipError_t launch_expert_down_mx(const Dims& D, const uint8_t* H8, const uint8_t* Hs, const int2* tile_info,

@@ -435,8 +435,7 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
     st = route_tail(ctx, p, t, s, zs, Xs);
     if (st != MOE_OK) return st;
     MOE_RUN(MOE_K_EXPERT_UP, launch_expert_up_mx(D, z8, Xs, p.perm_src, p.tile_info, n_mtiles, t, m.g8, m.gs, m.u8,
-                                                 m.us, H, s, w4));
-    MOE_RUN(MOE_K_MX_QUANT, launch_mx_quant(H, (long long)t * D.k, D.f, D.f, H8, Hs, s));
+                                                 m.us, H, H8, Hs, s, w4));
     MOE_RUN(MOE_K_EXPERT_DOWN, launch_expert_down_mx(D, H8, Hs, p.tile_info, n_mtiles, t, m.d8, m.ds, Y, s, w4));
   } else {
     st = route_tail(ctx, p, t, s);

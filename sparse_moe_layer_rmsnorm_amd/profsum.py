@@ -56,10 +56,10 @@ def logical_name(symbol: str, dense_seen: int) -> str | None:
         return {"4": "bwd_dout", "5": "bwd_dh", "8": "bwd_dH", "9": "bwd_dX"}.get(tag, "bwd_dgrad")
     if "k_gemm_wgrad" in symbol:
         return "bwd_wgrad"
-    if "k_gemm_expert" in symbol:
-        return "expert_up" if symbol.rstrip().endswith("2>(moe::(anonymous namespace)::ExpertArgs)") else "expert_down"
-    if "k_gemm_expert_mx" in symbol:
-        return "expert_up" if "Li2EEEv" in symbol else "expert_down"
+    if "k_gemm_expert" in symbol:  # the KIND argument: 2 GLU, 3 GLU + MXFP8 quantisation -> expert_up
+        tail = symbol.rstrip()
+        glu = any(tail.endswith(f"{k}>(moe::(anonymous namespace)::ExpertArgs)") for k in (2, 3))
+        return "expert_up" if glu or "Li2EEEv" in symbol or "Li3EEEv" in symbol else "expert_down"
     for k in ("rmsnorm_bwd", "dgamma_part", "sum_slices", "glu_bwd", "combine_bwd", "dispatch_bwd", "gates_bwd",
               "mx_quant", "reduce_split"):
         if f"k_{k}" in symbol:
