@@ -125,3 +125,52 @@ def test_kept_preactivations(dtype):
         assert rel_err(got, want) <= tol, n
     plain.close()
     kept.close()
+
+
+def test_training_step_graph_replay():
+    """forward (pre-activations kept) + backward + qb_update captured in one
+    graph: every replay, with eager work and synchronisation between
+    replays, equals the eager step bit for bit (out, dx, every gradient, bias)."""
+    shape = wl.LayerShape("graph", 24, "bf16", T=1024, d=1024, l=256, E=256, k=6, f=512, f_s=2048, B=256)
+    T = shape.T
+    say(f"training-step graph replay: T={T}")
+    W = wl.make_weights(shape)
+    layer = make_layer(shape, W, max_tokens=T, keep_preact=True)
+    xt = x_on_gpu(wl.make_x(shape), layer)
+    dout = x_on_gpu(o.bf16_round(np.random.default_rng(3).standard_normal((T, shape.d))).astype(F32), layer)
+    r = layer.route_buffers(T)
+    out = torch.empty(T, shape.d, dtype=layer.tdtype, device="cuda")
+
+    def step(grads=None):
+        layer.forward(xt, out=out, route=r)
+        dx, g = layer.backward(xt, dout, route=r, grads=grads)
+        layer.qb_update()
+        return dx, g
+
+    dx1, grads = step()                                  # bias 0, then the QB bias
+    dx2, _ = step(grads)                                 # the converged bias: a fixed point
+    torch.cuda.synchronize()
+    ref = {"out": out.clone(), "dx": dx2.clone(), "bias": layer.get_bias().clone()}
+    ref.update({n: v.clone() for n, v in grads.items()})
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(grads)                                      # warm the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dxc, _ = step(grads)
+    for i in range(4):
+        out.zero_()
+        dxc.zero_()
+        for v in grads.values():
+            v.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = {"out": out, "dx": dxc, "bias": layer.get_bias()}
+        got.update(grads)
+        for n, v in ref.items():
+            assert torch.equal(got[n], v), (i, n)
+        _ = (xt.float() * 2).sum().item()               # unrelated eager work between replays
+    layer.close()

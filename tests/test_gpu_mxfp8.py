@@ -167,3 +167,42 @@ def test_mxfp8_replica_sampled_and_requantize(fmt):
                              experts=fmt)
     assert rel_err(to_np(out2)[pick], want2) <= MX_E2E_TOL
     layer.close()
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_block_scaled_forward_graph_replay(fmt):
+    """The block-scaled forward (activation quantisation, fused H
+    quantisation) + qb_update captured in a graph: every replay equals the
+    eager result bit for bit."""
+    shape = wl.workload("replica", 2048)
+    T = shape.T
+    say(f"{fmt} graph replay T={T}")
+    W = wl.make_weights(shape)
+    layer = make_layer(shape, W, max_tokens=T, experts=fmt)
+    xt = x_on_gpu(wl.make_x(shape), layer)
+    r = layer.route_buffers(T)
+    out = torch.empty(T, shape.d, dtype=layer.tdtype, device="cuda")
+    for _ in range(2):                                   # bias 0, then the converged QB bias
+        layer.forward(xt, out=out, route=r)
+        layer.qb_update()
+    torch.cuda.synchronize()
+    want, bias = out.clone(), layer.get_bias().clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(xt, out=out, route=r)
+        layer.qb_update()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(xt, out=out, route=r)
+        layer.qb_update()
+    for i in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), i
+        assert torch.equal(layer.get_bias(), bias), i
+        _ = (xt.float() * 2).sum().item()
+    layer.close()
