@@ -1461,7 +1461,10 @@ using DgradPipe = Pipe<MOE_DENSE_CFG, BF16, 2>;
 template <bool BF16>
 using DgradExpertPipe = Pipe<MOE_EXPERT_CFG, BF16, 2>;
 // MXFP8 experts: one 128-element K step (128 bytes) per stage
-using ExpertMxPipe = Pipe<kExpertBM, 256, 1, 4, 2, 128, 2, true>;
+#ifndef MOE_EXPERT_MX_CFG
+#define MOE_EXPERT_MX_CFG kExpertBM, 256, 1, 4, 2, 128, 2
+#endif
+using ExpertMxPipe = Pipe<MOE_EXPERT_MX_CFG, true>;
 constexpr int kCUs = 256;
 
 }  // namespace
@@ -1709,11 +1712,12 @@ hipError_t launch_expert_nt(const Dims& D, const void* A, int lda_bytes, const i
   return launch_expert<EPI_STORE>(D, a, T, s);
 }
 
-// K pieces -> stage boundaries; false if a piece is not whole stages or is
-// malformed.  K is counted in 64-value units so that bf16 and fp32 agree.
-static bool dgrad_pieces(const Dims& D, const KPiece* pc, int npiece, DgradArgs& a, DgradSeg& g) {
-  const int kr = DgradPipe<true>::RB / esz(D), ce = 16 / esz(D);
-  if (npiece < 1 || npiece > 4) return false;
+// K pieces -> stage boundaries of a pipeline with rb-byte stage rows; false
+// if a piece is not whole stages (spans are multiples of 64 values, which
+// every stage depth here divides) or is malformed.
+static bool dgrad_pieces(const Dims& D, int rb, const KPiece* pc, int npiece, DgradArgs& a, DgradSeg& g) {
+  const int kr = rb / esz(D), ce = 16 / esz(D);
+  if (npiece < 1 || npiece > 4 || 64 % kr) return false;
   int st = 0;
   for (int j = 0; j < 4; ++j) {
     if (j < npiece) {
@@ -1775,7 +1779,7 @@ hipError_t launch_dgrad_dense(const Dims& D, int tag, const void* A, int lda_byt
   for (int i = 0; i < nseg; ++i) {
     DgradArgs b{};
     DgradSeg& g = a.seg[i];
-    if (!dgrad_pieces(D, segs[i].piece, npiece, b, g)) return hipErrorInvalidValue;
+    if (!dgrad_pieces(D, DgradPipe<true>::RB, segs[i].piece, npiece, b, g)) return hipErrorInvalidValue;
     if (i == 0) {
       std::memcpy(a.st, b.st, sizeof a.st);
       std::memcpy(a.rows, b.rows, sizeof a.rows);
@@ -1810,7 +1814,7 @@ hipError_t launch_dgrad_expert(const Dims& D, int tag, const void* A, int lda_by
   a.lda_bytes = lda_bytes;
   a.es = esz(D);
   DgradSeg& g = a.seg[0];
-  if (!dgrad_pieces(D, pieces, npiece, a, g)) return hipErrorInvalidValue;
+  if (!dgrad_pieces(D, DgradExpertPipe<true>::RB, pieces, npiece, a, g)) return hipErrorInvalidValue;
   if ((long long)a.st[4] * DgradExpertPipe<true>::RB > lda_bytes) return hipErrorInvalidValue;
   g.N = N;
   g.ntiles = (N + BN - 1) / BN;
@@ -1882,7 +1886,10 @@ hipError_t launch_mx_quant(const void* src, long long rows, int K, long long ld_
   return hipGetLastError();
 }
 
-using ExpertMx4Pipe = Mx4Pipe<kExpertBM, 256, 1, 4, 2, 2>;
+#ifndef MOE_EXPERT_MX4_CFG
+#define MOE_EXPERT_MX4_CFG kExpertBM, 256, 1, 4, 2, 2
+#endif
+using ExpertMx4Pipe = Mx4Pipe<MOE_EXPERT_MX4_CFG>;
 static_assert(ExpertMx4Pipe::BN == ExpertMxPipe::BN, "one weight-row tiling for both block-scaled formats");
 
 template <int KIND>
