@@ -1454,6 +1454,13 @@ template <bool BF16>
 using DensePipe = Pipe<MOE_DENSE_CFG, BF16>;
 template <bool BF16>
 using ExpertPipe = Pipe<MOE_EXPERT_CFG, BF16>;
+// bf16/fp32 expert down-projection over the kExpertBM2-row tile table: 4
+// wavefronts of 64x128, 3 stages of 64-byte rows, 2 blocks per CU.
+#ifndef MOE_EXPERT_DOWN_CFG
+#define MOE_EXPERT_DOWN_CFG kExpertBM2, 256, 2, 2, 3, 64, 2
+#endif
+template <bool BF16>
+using ExpertDownPipe = Pipe<MOE_EXPERT_DOWN_CFG, BF16>;
 template <bool BF16>
 using WgradKmPipe = Pipe<MOE_DENSE_CFG, BF16, 3>;
 template <bool BF16>
@@ -1592,20 +1599,21 @@ hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int 
   return launch_dense_any<2>(D, a, s);
 }
 
-int expert_max_mtiles(int T, int k, int E) {
+int expert_max_mtiles(int T, int k, int E, int bm) {
   // sum_e ceil(n_e / BM) <= ceil(T*k / BM) + E (at most one partial tile per expert)
-  return (int)(((long long)T * k + kExpertBM - 1) / kExpertBM + E);
+  return (int)(((long long)T * k + bm - 1) / bm + E);
 }
 
-template <int KIND>
+template <int KIND, template <bool> class PipeT = ExpertPipe>
 static hipError_t launch_expert(const Dims& D, const ExpertArgs& a, int T, hipStream_t s) {
-  const long long tiles = (long long)expert_max_mtiles(T, D.k, D.E) * a.NT;
+  static_assert(PipeT<true>::BM == PipeT<false>::BM, "one tile table per pipe");
+  const long long tiles = (long long)expert_max_mtiles(T, D.k, D.E, PipeT<true>::BM) * a.NT;
   if (tiles == 0) return hipSuccess;
-  const int grid = persistent_grid(tiles, ExpertPipe<true>::BPC);
+  const int grid = persistent_grid(tiles, PipeT<true>::BPC);
   if (D.bf16)
-    hipLaunchKernelGGL((k_gemm_expert<ExpertPipe<true>, KIND>), dim3(grid), dim3(ExpertPipe<true>::THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_expert<PipeT<true>, KIND>), dim3(grid), dim3(PipeT<true>::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemm_expert<ExpertPipe<false>, KIND>), dim3(grid), dim3(ExpertPipe<false>::THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_expert<PipeT<false>, KIND>), dim3(grid), dim3(PipeT<false>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1637,7 +1645,7 @@ hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_sr
 
 hipError_t launch_expert_down(const Dims& D, const void* H, const int2* tile_info, const int32_t* n_mtiles, int T,
                               const void* W_d, void* Y, hipStream_t s) {
-  constexpr int BN = ExpertPipe<true>::BN, RB = ExpertPipe<true>::RB;
+  constexpr int BN = ExpertDownPipe<true>::BN, RB = ExpertDownPipe<true>::RB;
   const int es = esz(D);
   ExpertArgs a{};
   a.A = static_cast<const char*>(H);
@@ -1653,7 +1661,7 @@ hipError_t launch_expert_down(const Dims& D, const void* H, const int2* tile_inf
   a.n_mtiles = n_mtiles;
   a.out = Y;
   a.ldo = D.l;
-  return launch_expert<EPI_STORE>(D, a, T, s);
+  return launch_expert<EPI_STORE, ExpertDownPipe>(D, a, T, s);
 }
 
 // ------------------------------------------------------ backward launchers --

@@ -18,6 +18,10 @@ constexpr int kHistSlices = 16;
 #define MOE_EXPERT_BM 64
 #endif
 constexpr int kExpertBM = MOE_EXPERT_BM;
+// Rows per tile of the second (coarser) tile table, used by the bf16 expert
+// down-projection: its output is only l wide, so 64-row tiles leave 1.7
+// waves of tiles on the chip at the replica shape and twice the weight passes.
+constexpr int kExpertBM2 = 2 * kExpertBM;
 // Experts per block of the histogram kernel (16 x 256 bins = 16 KB of LDS).
 constexpr int kHistExperts = 16;
 
@@ -36,9 +40,12 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
 // m-tile offsets and the m-tile table tile_info[g] = {first row, expert << 8 |
 // rows in use} of the grouped GEMMs.  With `load` non-NULL (sign-rule training) the
 // counts are also added to load[E] and T to *count.
+// tile_offsets / tile_info: the kExpertBM table; tile_offsets2 / tile_info2
+// (nullable): the kExpertBM2 table.
 hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cbase, int32_t* sbase, int32_t* counts,
                        int32_t* offsets, int32_t* tile_offsets, int2* tile_info, uint32_t* load,
-                       unsigned long long* count, hipStream_t s);
+                       unsigned long long* count, hipStream_t s, int32_t* tile_offsets2 = nullptr,
+                       int2* tile_info2 = nullptr);
 // Rows of the permutation, and the dispatch buffer X[row] = z[token].
 // With zs non-NULL (MXFP8 experts) also copies each token's z scale row
 // (s_ld bytes, a multiple of 4) to Xs at each of its grouped rows.
@@ -71,13 +78,14 @@ hipError_t launch_gemm_out(const Dims& D, const void* G, const void* y_lat, int 
                            const void* W_up, void* out, hipStream_t s);
 // Grouped expert GEMMs over the rows grouped by expert (m-tiles of
 // kExpertBM rows from tile_info; n_mtiles points at their count).
-int expert_max_mtiles(int T, int k, int E);
+int expert_max_mtiles(int T, int k, int E, int bm = kExpertBM);
 // Expert GEMM 1 + GLU; its A rows are z[perm_src[r]] (the dispatch is part
 // of the operand load, no dispatch buffer is written).  A, U (both or
 // neither): the pre-activations X W_g^T, X W_u^T are stored there as well.
 hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_src, const int2* tile_info,
                             const int32_t* n_mtiles, int T, const void* W_g, const void* W_u, void* H, hipStream_t s,
                             void* A = nullptr, void* U = nullptr);
+// Expert GEMM 2 over the kExpertBM2-row tile table (tile_info2, n_mtiles2).
 hipError_t launch_expert_down(const Dims& D, const void* H, const int2* tile_info, const int32_t* n_mtiles, int T,
                               const void* W_d, void* Y, hipStream_t s);
 

@@ -126,10 +126,12 @@ void ws_layout(const moe_config* c, int64_t T, moe_ws_layout* L) {
   L->sbase = take(nsuper * E * 4);
   L->counts = take(E * 4);
   L->offsets = take((E + 1) * 4);
-  L->tile_offsets = take((E + 1) * 4);
+  L->tile_offsets = take(2 * (E + 1) * 4);  // the kExpertBM table's, then the kExpertBM2 table's
   L->perm_src = take(t * k * 4);
   L->inv = take(t * k * 4);
-  L->tile_info = take(T > 0 ? (size_t)expert_max_mtiles((int)T, c->k, c->E) * 8 : 0);
+  L->tile_info = take(T > 0 ? ((size_t)expert_max_mtiles((int)T, c->k, c->E) +
+                                (size_t)expert_max_mtiles((int)T, c->k, c->E, kExpertBM2)) * 8
+                             : 0);  // both tile tables
   L->G = take(t * c->f_s * es);
   L->z = take(t * c->l * es);
   L->X = take(0);  // no dispatch buffer: expert_up gathers z rows itself
@@ -196,10 +198,12 @@ struct RoutePtrs {
   int32_t *idx, *cbase, *sbase, *counts, *offsets, *tile_offsets, *perm_src, *inv;
   uint32_t* bitmap;
   int2* tile_info;
+  int32_t* tile_offsets2;  // the kExpertBM2 tile table (expert down-projection)
+  int2* tile_info2;
   float* gates;
 };
 
-RoutePtrs route_ptrs(const moe_ws_layout& L, char* ws, const moe_route_out* r) {
+RoutePtrs route_ptrs(const moe_config& c, int64_t T, const moe_ws_layout& L, char* ws, const moe_route_out* r) {
   RoutePtrs p;
   p.logits = (r && r->logits) ? r->logits : reinterpret_cast<float*>(ws + L.logits);
   p.idx = (r && r->topk_idx) ? r->topk_idx : reinterpret_cast<int32_t*>(ws + L.idx);
@@ -213,6 +217,8 @@ RoutePtrs route_ptrs(const moe_ws_layout& L, char* ws, const moe_route_out* r) {
   p.sbase = reinterpret_cast<int32_t*>(ws + L.sbase);
   p.tile_offsets = reinterpret_cast<int32_t*>(ws + L.tile_offsets);
   p.tile_info = reinterpret_cast<int2*>(ws + L.tile_info);
+  p.tile_offsets2 = p.tile_offsets + (c.E + 1);
+  p.tile_info2 = p.tile_info + (T > 0 ? expert_max_mtiles((int)T, c.k, c.E) : 0);
   return p;
 }
 
@@ -245,7 +251,8 @@ moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s, co
   MOE_RUN(MOE_K_TOPK, launch_topk(D, p.logits, bias, T, p.idx, p.gates, p.bitmap, hist, cnt, s));
   if (train) ctx->pending_tokens += (uint64_t)T;
   MOE_RUN(MOE_K_SCAN, launch_scan(D, p.bitmap, T, p.cbase, p.sbase, p.counts, p.offsets, p.tile_offsets,
-                                  p.tile_info, load, train && sign ? cnt : nullptr, s));
+                                  p.tile_info, load, train && sign ? cnt : nullptr, s, p.tile_offsets2,
+                                  p.tile_info2));
   MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.bitmap, p.cbase, p.sbase, T, p.perm_src, p.inv, s, zs, Xs, D.l / 32));
   return MOE_OK;
 }
@@ -392,7 +399,7 @@ moe_status moe_route(moe_ctx* ctx, const void* x, const float* logits, int64_t T
   moe_ws_layout L;
   ws_layout(&ctx->cfg, T, &L);
   char* w = static_cast<char*>(ws);
-  RoutePtrs p = route_ptrs(L, w, r);
+  RoutePtrs p = route_ptrs(ctx->cfg, T, L, w, r);
   const int t = (int)T;
   if (logits) {
     p.logits = const_cast<float*>(logits);
@@ -415,7 +422,7 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
   moe_ws_layout L;
   ws_layout(&ctx->cfg, T, &L);
   char* w = static_cast<char*>(ws);
-  RoutePtrs p = route_ptrs(L, w, r);
+  RoutePtrs p = route_ptrs(ctx->cfg, T, L, w, r);
   const int t = (int)T;
   void *h = w + L.h, *G = w + L.G, *z = w + L.z, *H = w + L.H, *Y = w + L.Y, *y_lat = w + L.y_lat;
   const bool keep = ctx->cfg.keep_preact != 0;
@@ -443,7 +450,8 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
     // dispatch X[r] = z[perm_src[r]] happens inside expert_up's operand load
     MOE_RUN(MOE_K_EXPERT_UP, launch_expert_up(D, z, p.perm_src, p.tile_info, n_mtiles, t, ctx->w.W_g, ctx->w.W_u, H,
                                               s, keep ? w + L.A : nullptr, keep ? w + L.U : nullptr));
-    MOE_RUN(MOE_K_EXPERT_DOWN, launch_expert_down(D, H, p.tile_info, n_mtiles, t, ctx->w.W_d, Y, s));
+    MOE_RUN(MOE_K_EXPERT_DOWN,
+            launch_expert_down(D, H, p.tile_info2, p.tile_offsets2 + D.E, t, ctx->w.W_d, Y, s));
   }
   MOE_RUN(MOE_K_COMBINE, launch_combine(D, Y, p.gates, p.inv, t, y_lat, s));
   MOE_RUN(MOE_K_GEMM_OUT, launch_gemm_out(D, G, y_lat, t, ctx->w.W_sd, ctx->w.W_up, out, s));
@@ -503,7 +511,7 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   moe_ws_layout L;
   ws_layout(&c, T, &L);
   char* fw = static_cast<char*>(const_cast<void*>(fwd_ws));
-  const RoutePtrs p = route_ptrs(L, fw, r);
+  const RoutePtrs p = route_ptrs(ctx->cfg, T, L, fw, r);
   const void *h = fw + L.h, *G = fw + L.G, *z = fw + L.z, *H = fw + L.H, *Y = fw + L.Y, *y_lat = fw + L.y_lat;
   const int32_t* n_mtiles = p.tile_offsets + E;
   char* w = static_cast<char*>(ws);

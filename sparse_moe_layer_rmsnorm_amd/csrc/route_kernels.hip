@@ -350,10 +350,16 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
                                                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ tile_offsets, int2* __restrict__ tile_info,
                                                       uint32_t* __restrict__ load, unsigned long long* __restrict__ count,
-                                                      int T) {
-  __shared__ int wsum_r[16], wsum_t[16];
+                                                      int T, int k, int32_t* __restrict__ tile_offsets2,
+                                                      int2* __restrict__ tile_info2) {
+  __shared__ int wsum_r[16], wsum_t[16], wsum_u[16];
+  // per expert (E <= 1024): first row, count, inclusive tile prefixes of both tables
+  __shared__ int s_row0[1024], s_cnt[1024], s_t[1024], s_u[1024];
   constexpr int kReg = 16;  // up to this many super-chunk totals stay in registers
   const int i = threadIdx.x, lane = i & 63, w = i >> 6;
+  // at most 8 tiles of kExpertBM rows per expert on average: one thread per
+  // expert writes its tiles (cheaper than a block-wide pass at these sizes)
+  const bool few = (long long)T * k <= 8LL * kExpertBM * E;
   int c = 0;
   int v[kReg];
   if (i < E) {
@@ -368,24 +374,27 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
       for (int sc = 0; sc < nsuper; ++sc) c += sbase[(size_t)sc * E + i];
     }
   }
-  const int tl = (c + kExpertBM - 1) / kExpertBM;
-  int r = c, t = tl;  // inclusive wave scans
+  const int tl = (c + kExpertBM - 1) / kExpertBM, tl2 = (c + kExpertBM2 - 1) / kExpertBM2;
+  int r = c, t = tl, u = tl2;  // inclusive wave scans
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int ro = __shfl_up(r, o, 64), to = __shfl_up(t, o, 64);
+    const int ro = __shfl_up(r, o, 64), to = __shfl_up(t, o, 64), uo = __shfl_up(u, o, 64);
     if (lane >= o) {
       r += ro;
       t += to;
+      u += uo;
     }
   }
   if (lane == 63) {
     wsum_r[w] = r;
     wsum_t[w] = t;
+    wsum_u[w] = u;
   }
   __syncthreads();
   for (int j = 0; j < w; ++j) {
     r += wsum_r[j];
     t += wsum_t[j];
+    u += wsum_u[j];
   }
   if (i < E) {
     counts[i] = c;
@@ -408,20 +417,51 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
         run += x;
       }
     }
-    const int row0 = r - c, tile0 = t - tl;
-    for (int j = 0; j < tl; ++j)
-      tile_info[tile0 + j] = make_int2(row0 + j * kExpertBM, (i << 8) | min(kExpertBM, c - j * kExpertBM));
+    s_row0[i] = r - c;
+    s_cnt[i] = c;
+    s_t[i] = t;
+    s_u[i] = u;
+    if (tile_offsets2) tile_offsets2[i + 1] = u;
+    if (few) {  // each expert thread writes its own few tiles
+      for (int j = 0, t0 = t - tl; j < tl; ++j)
+        tile_info[t0 + j] = make_int2(r - c + j * kExpertBM, (i << 8) | min(kExpertBM, c - j * kExpertBM));
+      if (tile_info2)
+        for (int j = 0, u0 = u - tl2; j < tl2; ++j)
+          tile_info2[u0 + j] = make_int2(r - c + j * kExpertBM2, (i << 8) | min(kExpertBM2, c - j * kExpertBM2));
+    }
   }
   if (i == 0) {
     offsets[0] = 0;
     tile_offsets[0] = 0;
+    if (tile_offsets2) tile_offsets2[0] = 0;
     if (load) *count += (unsigned long long)T;
   }
+  if (few) return;
+  __syncthreads();
+  // Many tiles per expert: the tile tables are spread over the whole block;
+  // tile g belongs to the expert whose tile range holds it (binary search
+  // over the inclusive prefixes).
+  auto fill = [&](const int* pre, int bm, int2* info) {
+    const int total = pre[E - 1];
+    for (int g = i; g < total; g += 1024) {
+      int lo = 0, hi = E - 1;  // first e with pre[e] > g
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] > g) hi = mid;
+        else lo = mid + 1;
+      }
+      const int j = g - (lo > 0 ? pre[lo - 1] : 0);
+      info[g] = make_int2(s_row0[lo] + j * bm, (lo << 8) | min(bm, s_cnt[lo] - j * bm));
+    }
+  };
+  fill(s_t, kExpertBM, tile_info);
+  if (tile_info2) fill(s_u, kExpertBM2, tile_info2);
 }
 
 hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cbase, int32_t* sbase, int32_t* counts,
                        int32_t* offsets, int32_t* tile_offsets, int2* tile_info, uint32_t* load,
-                       unsigned long long* count, hipStream_t s) {
+                       unsigned long long* count, hipStream_t s, int32_t* tile_offsets2, int2* tile_info2) {
+  if ((tile_offsets2 == nullptr) != (tile_info2 == nullptr)) return hipErrorInvalidValue;
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int nsuper = (nchunks + kSuper - 1) / kSuper;
   dim3 g1((D.E + 63) / 64, (nsuper + 3) / 4);
@@ -429,7 +469,7 @@ hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cb
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan_global, dim3(1), dim3(1024), 0, s, sbase, nsuper, D.E, counts, offsets, tile_offsets,
-                     tile_info, load, load ? count : nullptr, T);
+                     tile_info, load, load ? count : nullptr, T, D.k, tile_offsets2, tile_info2);
   return hipGetLastError();
 }
 
