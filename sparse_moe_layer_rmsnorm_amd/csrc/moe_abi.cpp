@@ -169,6 +169,10 @@ struct moe_ctx {
   int prof_max = 0, prof_n = 0;
   std::vector<hipEvent_t> ev;
   std::vector<int> ev_kernel;
+  // backward: an internal stream for the weight-gradient products, forked
+  // from and joined back to the caller's stream with these events
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev[4] = {}, join_ev = nullptr;
 };
 
 namespace {
@@ -386,6 +390,13 @@ moe_status moe_init(const moe_config* cfg, const moe_weights* w, void* state, vo
     delete c;
     return fail(MOE_ERR_HIP, "clearing the state failed: %s", hipGetErrorString(e));
   }
+  e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);  // default priority
+  for (int i = 0; i < 4 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->fork_ev[i], hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->join_ev, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    moe_destroy(c);
+    return fail(MOE_ERR_HIP, "creating the backward stream failed: %s", hipGetErrorString(e));
+  }
   *out = c;
   return MOE_OK;
 }
@@ -526,86 +537,37 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   auto elw = [&](void* base, size_t elems) { return static_cast<char*>(base) + elems * es; };
   const moe_weights& W = ctx->w;
 
-  // Data-gradient products read the weights as stored (K-major B operands).
-  // output projections: [dG | dy_lat] = dout [W_sd | W_up]
-  {
-    DgradSegSpec sg[2] = {};
-    int n = 0;
-    if (fs > 0) sg[n++] = {{{W.W_sd, fs, d, d}}, fs, 1, dG, fs};
-    sg[n++] = {{{W.W_up, l, d, d}}, l, 1, dy, l};
-    MOE_RUN(MOE_K_BWD_GEMM, launch_dgrad_dense(D, 4, dout, d * es, t, sg, n, 1, s));
-  }
+  // With kept pre-activations the weight-gradient products run on an
+  // internal stream, each forked off the caller's stream once its operands
+  // are written there (the side stream's work stays in order: the dense ones
+  // share the split-K partials), and joined back before returning; they then
+  // overlap the chain of data gradients, much of which is bound by memory or
+  // latency.  When the pre-activations are recomputed, those GEMMs already
+  // fill the GPU beside the chain and everything stays on the caller's
+  // stream (the overlap measured slower there).
   const bool kept = c.keep_preact != 0;  // pre-activations stored by the forward
-  if (kept) {
-    P = fw + L.P;
-    Q = fw + L.Q;
-    Apre = fw + L.A;
-    U = fw + L.U;
-  }
-  if (fs > 0) {  // shared GLU: P, Q (recomputed unless kept); dP, dQ into the first 2 f_s columns of dAcat
-    if (!kept) {
-      DenseSegSpec sg[2] = {{W.W_sg, fs, 1, P, fs}, {W.W_su, fs, 1, Q, fs}};
-      MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 3, h, d * es, t, d * es, sg, 2, d * es, s));
-    }
-    MOE_RUN(MOE_K_BWD_ELTWISE, launch_glu_bwd(D, P, Q, dG, t, fs, dAcat, elw(dAcat, fs), Kc, s));
-  }
-  // combine transpose: dY rows and gate gradients
-  MOE_RUN(MOE_K_BWD_ELTWISE, launch_combine_bwd(D, dy, Y, p.gates, p.inv, t, dY, dg, s));
-  // experts: dH = dY W_d; recompute A = X W_g^T, U = X W_u^T; GLU derivative; dX = [dA|dU] [W_g; W_u]
-  const size_t wfl = (size_t)f * l * es;
+  hipStream_t s2 = kept ? ctx->side : s;
+  int nfork = 0;
+  auto fork = [&]() -> moe_status {
+    if (s2 == s) return MOE_OK;
+    hipEvent_t ev = ctx->fork_ev[nfork++];
+    hipError_t e = hipEventRecord(ev, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s2, ev, 0);
+    return e == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "forking the backward stream failed: %s", hipGetErrorString(e));
+  };
+  const int u = Tp / 64;
+  auto slices = [&](int want, int* step) {
+    const int c = (u + want - 1) / want;  // 64-token stages per slice
+    *step = 64 * c;
+    return (u + c - 1) / c;               // every slice non-empty
+  };
+  int step_o, step_c;
+  const int S_o = slices(kSplitOut, &step_o), S_c = slices(kSplitCat, &step_c);
+  // [dW_sd | dW_up] = dout^T [G | y_lat]: forward values and dout only
+  if ((st = fork()) != MOE_OK) return st;
   {
-    const KPiece wd[1] = {{W.W_d, f, l, l}};  // W_d[e] [l, f]: K = l
-    MOE_RUN(MOE_K_BWD_EXPERT,
-            launch_dgrad_expert(D, 8, dY, l * es, wd, 1, wfl, f, p.tile_info, n_mtiles, t, dH, f, s));
-  }
-  if (!kept) {
-    MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, z, l * es, p.perm_src, W.W_g, wfl, l * es, f, l * es, p.tile_info,
-                                               n_mtiles, t, Apre, f, s));
-    MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, z, l * es, p.perm_src, W.W_u, wfl, l * es, f, l * es, p.tile_info,
-                                               n_mtiles, t, U, f, s));
-  }
-  MOE_RUN(MOE_K_BWD_ELTWISE, launch_glu_bwd(D, Apre, U, dH, Tk, f, dAU, elw(dAU, f), 2 * f, s));
-  {
-    const KPiece wgu[2] = {{W.W_g, l, f, f}, {W.W_u, l, f, f}};  // [W_g[e]; W_u[e]] [2f, l]: K = 2f
-    MOE_RUN(MOE_K_BWD_EXPERT,
-            launch_dgrad_expert(D, 9, dAU, 2 * f * es, wgu, 2, wfl, l, p.tile_info, n_mtiles, t, dX, l, s));
-  }
-  // dispatch transpose and router: dz and dl into their columns of dAcat
-  MOE_RUN(MOE_K_BWD_ELTWISE, launch_dispatch_bwd(D, dX, p.inv, t, elw(dAcat, 2 * fs), Kc, s));
-  MOE_RUN(MOE_K_BWD_ELTWISE, launch_gates_bwd(D, p.logits, p.idx, dg, t, Epad, elw(dAcat, 2 * fs + l), Kc, s));
-  // dh = [dP | dQ | dz | dl] [W_sg; W_su; W_dn; W_r], then RMSNorm
-  {
-    DgradSegSpec sg = {};
-    int np = 0;
-    if (fs > 0) {
-      sg.piece[np++] = {W.W_sg, d, fs, fs};
-      sg.piece[np++] = {W.W_su, d, fs, fs};
-    }
-    sg.piece[np++] = {W.W_dn, d, l, l};
-    sg.piece[np++] = {W.W_r, d, Epad, E};  // pad rows of W_r count as zero
-    sg.N = d;
-    sg.kind = 0;
-    sg.out = dh;
-    sg.ldo = d;
-    MOE_RUN(MOE_K_BWD_GEMM, launch_dgrad_dense(D, 5, dAcat, Kc * es, t, &sg, 1, np, s));
-  }
-  MOE_RUN(MOE_K_BWD_ELTWISE, launch_rmsnorm_bwd(D, x, W.gamma, dh, t, dx, static_cast<float*>(at(B.rstd)),
-                                                static_cast<float*>(at(B.gpart)), kGammaSlices, g->gamma, s));
-  // Dense weight gradients, K = tokens split in slices (few output tiles:
-  // d x (f_s + l) and (2 f_s + l + Epad) x d), partials summed into the
-  // outputs.  All weight-gradient products read their token-major operands
-  // as stored (K-major tiles), so nothing is transposed.
-  {
-    const int u = Tp / 64;
-    auto slices = [&](int want, int* step) {
-      const int c = (u + want - 1) / want;  // 64-token stages per slice
-      *step = 64 * c;
-      return (u + c - 1) / c;               // every slice non-empty
-    };
-    int step_o, step_c;
-    const int S_o = slices(kSplitOut, &step_o), S_c = slices(kSplitCat, &step_c);
-    auto dense_wgrad = [&]() -> hipError_t {
-      // [dW_sd | dW_up] = dout^T [G | y_lat]
+    hipStream_t s = s2;
+    auto wgrad_out = [&]() -> hipError_t {
       WgradKmSpec wo{dout, d, G, fs, y_lat, l, fs, nullptr, step_o, t, nullptr, 0, d, fs + l, S_o, dWcat};
       hipError_t e = launch_wgrad_km(D, wo, s);
       SplitOut o{};
@@ -620,9 +582,83 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
       if (fs > 0) addc(0, fs, g->W_sd);
       addc(fs, l, g->W_up);
       if (e == hipSuccess) e = launch_reduce_split(dWcat, S_o, d, fs + l, o, s);
-      // [dW_sg; dW_su; dW_dn; dW_r] = dA_cat^T h
+      return e;
+    };
+    MOE_RUN(MOE_K_BWD_WGRAD, wgrad_out());
+  }
+  // Data-gradient products read the weights as stored (K-major B operands).
+  // output projections: [dG | dy_lat] = dout [W_sd | W_up]
+  {
+    DgradSegSpec sg[2] = {};
+    int n = 0;
+    if (fs > 0) sg[n++] = {{{W.W_sd, fs, d, d}}, fs, 1, dG, fs};
+    sg[n++] = {{{W.W_up, l, d, d}}, l, 1, dy, l};
+    MOE_RUN(MOE_K_BWD_GEMM, launch_dgrad_dense(D, 4, dout, d * es, t, sg, n, 1, s));
+  }
+  if (kept) {
+    P = fw + L.P;
+    Q = fw + L.Q;
+    Apre = fw + L.A;
+    U = fw + L.U;
+  }
+  if (fs > 0) {  // shared GLU: P, Q (recomputed unless kept); dP, dQ into the first 2 f_s columns of dAcat
+    if (!kept) {
+      DenseSegSpec sg[2] = {{W.W_sg, fs, 1, P, fs}, {W.W_su, fs, 1, Q, fs}};
+      MOE_RUN(MOE_K_BWD_GEMM, launch_dense_nt(D, 3, h, d * es, t, d * es, sg, 2, d * es, s));
+    }
+    MOE_RUN(MOE_K_BWD_ELTWISE, launch_glu_bwd(D, P, Q, dG, t, fs, dAcat, elw(dAcat, fs), Kc, s));
+  }
+  // expert pre-activations A = X W_g^T, U = X W_u^T (recomputed unless kept),
+  // before the next fork so that they do not share the GPU with its products
+  const size_t wfl = (size_t)f * l * es;
+  if (!kept) {
+    MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, z, l * es, p.perm_src, W.W_g, wfl, l * es, f, l * es, p.tile_info,
+                                               n_mtiles, t, Apre, f, s));
+    MOE_RUN(MOE_K_BWD_EXPERT, launch_expert_nt(D, z, l * es, p.perm_src, W.W_u, wfl, l * es, f, l * es, p.tile_info,
+                                               n_mtiles, t, U, f, s));
+  }
+  // combine transpose: dY rows and gate gradients
+  MOE_RUN(MOE_K_BWD_ELTWISE, launch_combine_bwd(D, dy, Y, p.gates, p.inv, t, dY, dg, s));
+  // dW_d[e] = dY_e^T H_e (K = the expert's rows of the dispatch order)
+  if ((st = fork()) != MOE_OK) return st;
+  {
+    hipStream_t s = s2;
+    const WgradKmSpec wd{dY, l, nullptr, 0, H, f, 0, p.offsets, 0, Tk, nullptr, 0, l, f, E, g->W_d};
+    MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad_km(D, wd, s));
+  }
+  // experts: dH = dY W_d; GLU derivative; dX = [dA|dU] [W_g; W_u]
+  {
+    const KPiece wd[1] = {{W.W_d, f, l, l}};  // W_d[e] [l, f]: K = l
+    MOE_RUN(MOE_K_BWD_EXPERT,
+            launch_dgrad_expert(D, 8, dY, l * es, wd, 1, wfl, f, p.tile_info, n_mtiles, t, dH, f, s));
+  }
+  MOE_RUN(MOE_K_BWD_ELTWISE, launch_glu_bwd(D, Apre, U, dH, Tk, f, dAU, elw(dAU, f), 2 * f, s));
+  // dW_g[e] = dA_e^T X_e and dW_u[e] = dU_e^T X_e, X_e's rows gathered from z
+  if ((st = fork()) != MOE_OK) return st;
+  {
+    hipStream_t s = s2;
+    const WgradKmSpec wg{dAU, 2 * f, nullptr, 0, z, l, 0, p.offsets, 0, Tk, p.perm_src, Tk, f, l, E, g->W_g};
+    MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad_km(D, wg, s));
+    WgradKmSpec wu = wg;
+    wu.A = el(dAU, f);
+    wu.out = g->W_u;
+    MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad_km(D, wu, s));
+  }
+  {
+    const KPiece wgu[2] = {{W.W_g, l, f, f}, {W.W_u, l, f, f}};  // [W_g[e]; W_u[e]] [2f, l]: K = 2f
+    MOE_RUN(MOE_K_BWD_EXPERT,
+            launch_dgrad_expert(D, 9, dAU, 2 * f * es, wgu, 2, wfl, l, p.tile_info, n_mtiles, t, dX, l, s));
+  }
+  // dispatch transpose and router: dz and dl into their columns of dAcat
+  MOE_RUN(MOE_K_BWD_ELTWISE, launch_dispatch_bwd(D, dX, p.inv, t, elw(dAcat, 2 * fs), Kc, s));
+  MOE_RUN(MOE_K_BWD_ELTWISE, launch_gates_bwd(D, p.logits, p.idx, dg, t, Epad, elw(dAcat, 2 * fs + l), Kc, s));
+  // [dW_sg; dW_su; dW_dn; dW_r] = dA_cat^T h, K = tokens in slices, partials summed into the outputs
+  if ((st = fork()) != MOE_OK) return st;
+  {
+    hipStream_t s = s2;
+    auto wgrad_cat = [&]() -> hipError_t {
       WgradKmSpec wc{dAcat, Kc, nullptr, 0, h, d, 0, nullptr, step_c, t, nullptr, 0, Kc, d, S_c, dWcat};
-      if (e == hipSuccess) e = launch_wgrad_km(D, wc, s);
+      hipError_t e = launch_wgrad_km(D, wc, s);
       SplitOut c{};
       c.by_rows = 1;
       auto add = [&](int start, int len, float* out) {
@@ -641,19 +677,32 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
       if (e == hipSuccess) e = launch_reduce_split(dWcat, S_c, Kc, d, c, s);
       return e;
     };
-    MOE_RUN(MOE_K_BWD_WGRAD, dense_wgrad());
+    MOE_RUN(MOE_K_BWD_WGRAD, wgrad_cat());
   }
-  // per-expert weight gradients, K = the expert's rows of the dispatch order
-  // dW_d[e] = dY_e^T H_e
-  const WgradKmSpec wd{dY, l, nullptr, 0, H, f, 0, p.offsets, 0, Tk, nullptr, 0, l, f, E, g->W_d};
-  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad_km(D, wd, s));
-  // dW_g[e] = dA_e^T X_e and dW_u[e] = dU_e^T X_e, X_e's rows gathered from z
-  const WgradKmSpec wg{dAU, 2 * f, nullptr, 0, z, l, 0, p.offsets, 0, Tk, p.perm_src, Tk, f, l, E, g->W_g};
-  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad_km(D, wg, s));
-  WgradKmSpec wu = wg;
-  wu.A = el(dAU, f);
-  wu.out = g->W_u;
-  MOE_RUN(MOE_K_BWD_WGRAD, launch_wgrad_km(D, wu, s));
+  // dh = [dP | dQ | dz | dl] [W_sg; W_su; W_dn; W_r], then RMSNorm
+  {
+    DgradSegSpec sg = {};
+    int np = 0;
+    if (fs > 0) {
+      sg.piece[np++] = {W.W_sg, d, fs, fs};
+      sg.piece[np++] = {W.W_su, d, fs, fs};
+    }
+    sg.piece[np++] = {W.W_dn, d, l, l};
+    sg.piece[np++] = {W.W_r, d, Epad, E};  // pad rows of W_r count as zero
+    sg.N = d;
+    sg.kind = 0;
+    sg.out = dh;
+    sg.ldo = d;
+    MOE_RUN(MOE_K_BWD_GEMM, launch_dgrad_dense(D, 5, dAcat, Kc * es, t, &sg, 1, np, s));
+  }
+  MOE_RUN(MOE_K_BWD_ELTWISE, launch_rmsnorm_bwd(D, x, W.gamma, dh, t, dx, static_cast<float*>(at(B.rstd)),
+                                                static_cast<float*>(at(B.gpart)), kGammaSlices, g->gamma, s));
+  // join: the caller's stream waits for the weight gradients
+  if (s2 != s) {
+    hipError_t e = hipEventRecord(ctx->join_ev, s2);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, ctx->join_ev, 0);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "joining the backward stream failed: %s", hipGetErrorString(e));
+  }
   return MOE_OK;
 }
 
@@ -687,6 +736,10 @@ moe_status moe_set_qb_mode(moe_ctx* ctx, moe_qb_mode mode) {
 void moe_destroy(moe_ctx* ctx) {
   if (!ctx) return;
   for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : ctx->fork_ev)
+    if (e) (void)hipEventDestroy(e);
+  if (ctx->join_ev) (void)hipEventDestroy(ctx->join_ev);
+  if (ctx->side) (void)hipStreamDestroy(ctx->side);
   delete ctx;
 }
 
