@@ -208,8 +208,11 @@ moe_status moe_workspace_layout(const moe_config* cfg, int64_t T, moe_ws_layout*
 /*
  * Create a context for `cfg` over the caller's weights and QB state buffer
  * (moe_state_bytes(cfg) bytes of device memory, 256-byte aligned).  Enqueues
- * on `stream` the clearing of the state: bias 0, histogram 0, count 0.
- * *out receives a host object freed by moe_destroy().
+ * on `stream` the clearing of the state: bias 0, histogram 0, count 0
+ * (and, for block-scaled experts, the quantisation of the expert weights).
+ * *out receives a host object freed by moe_destroy(); it owns one internal
+ * stream (default priority) and five timing-free events on the current
+ * device, used by moe_backward and released by moe_destroy().
  */
 moe_status moe_init(const moe_config* cfg, const moe_weights* w, void* state, void* stream, moe_ctx** out);
 
@@ -278,7 +281,12 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg, int64_t T);
  * h, RMSNorm.  Weight gradients of the experts take each expert's own tokens
  * as the K range of one grouped product.  `ws` holds
  * moe_backward_workspace_bytes(cfg, T) bytes (256-byte aligned).  QB state
- * is neither read nor changed.  T = 0 enqueues nothing.
+ * is neither read nor changed.  T = 0 enqueues nothing.  With keep_preact
+ * the weight-gradient products run on the context's internal stream, forked
+ * from `stream` by events after their operands are written and joined back
+ * before the call returns, so every result is still ordered on `stream`
+ * (and the call can still be captured in a graph on `stream`); concurrent
+ * moe_backward calls on one context are not allowed.
  */
 moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T, const moe_route_out* r,
                         const void* fwd_ws, size_t fwd_ws_bytes, void* dx, const moe_grads* g, void* ws,
