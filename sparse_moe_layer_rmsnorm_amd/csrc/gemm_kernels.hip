@@ -1461,8 +1461,11 @@ using ExpertPipe = Pipe<MOE_EXPERT_CFG, BF16>;
 #endif
 template <bool BF16>
 using ExpertDownPipe = Pipe<MOE_EXPERT_DOWN_CFG, BF16>;
+#ifndef MOE_WGRAD_CFG
+#define MOE_WGRAD_CFG MOE_DENSE_CFG
+#endif
 template <bool BF16>
-using WgradKmPipe = Pipe<MOE_DENSE_CFG, BF16, 3>;
+using WgradKmPipe = Pipe<MOE_WGRAD_CFG, BF16, 3>;
 template <bool BF16>
 using DgradPipe = Pipe<MOE_DENSE_CFG, BF16, 2>;
 template <bool BF16>
