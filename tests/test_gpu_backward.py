@@ -25,6 +25,8 @@ CASES = [  # name, dtype, T, d, l, E, k, f, f_s
     ("single-expert", "bf16", 130, 128, 64, 1, 1, 64, 64),
     ("k32", "bf16", 70, 128, 64, 64, 32, 64, 128),
     ("replica", "bf16", 8192, 1024, 256, 256, 6, 512, 2048),   # the benchmarked size
+    ("wide", "bf16", 300, 128, 64, 1024, 32, 64, 64),          # most experts and slots: router rows up to Epad
+    ("deep", "bf16", 4096, 256, 128, 8, 2, 256, 256),          # 1024 rows per expert: block-wide tile tables
 ]
 
 

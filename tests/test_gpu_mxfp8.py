@@ -70,6 +70,7 @@ SHAPES = [  # name, T, d, l, E, k, f, f_s
     ("small", 300, 256, 128, 16, 2, 128, 256),
     ("ragged", 203, 192, 256, 24, 5, 384, 0),
     ("replica-widths", 1000, 1024, 256, 256, 6, 512, 2048),
+    ("deep", 4096, 256, 128, 8, 2, 128, 0),          # 1024 rows per expert: block-wide tile tables
 ]
 
 
