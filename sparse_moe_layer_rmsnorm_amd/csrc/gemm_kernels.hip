@@ -1461,6 +1461,9 @@ using ExpertPipe = Pipe<MOE_EXPERT_CFG, BF16>;
 #endif
 template <bool BF16>
 using ExpertDownPipe = Pipe<MOE_EXPERT_DOWN_CFG, BF16>;
+// expert_up over the kExpertBM2-row table, for many rows per expert
+template <bool BF16>
+using ExpertUpPipe2 = Pipe<MOE_EXPERT_DOWN_CFG, BF16>;
 #ifndef MOE_WGRAD_CFG
 #define MOE_WGRAD_CFG MOE_DENSE_CFG
 #endif
@@ -1622,9 +1625,11 @@ static hipError_t launch_expert(const Dims& D, const ExpertArgs& a, int T, hipSt
 
 hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_src, const int2* tile_info,
                             const int32_t* n_mtiles, int T, const void* W_g, const void* W_u, void* H, hipStream_t s,
-                            void* A, void* U) {
+                            void* A, void* U, bool tall) {
   if ((A == nullptr) != (U == nullptr)) return hipErrorInvalidValue;
-  constexpr int BN = ExpertPipe<true>::BN, RB = ExpertPipe<true>::RB;
+  static_assert(ExpertUpPipe2<true>::BN == ExpertPipe<true>::BN, "one column tiling for both tile heights");
+  constexpr int BN = ExpertPipe<true>::BN;
+  const int RB = tall ? ExpertUpPipe2<true>::RB : ExpertPipe<true>::RB;  // the launched pipeline's stage rows
   const int es = esz(D);
   ExpertArgs a{};
   a.A = static_cast<const char*>(z);
@@ -1643,6 +1648,7 @@ hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_sr
   a.keep[1] = U;
   a.out = H;
   a.ldo = D.f;
+  if (tall) return launch_expert<EPI_GLU, ExpertUpPipe2>(D, a, T, s);
   return launch_expert<EPI_GLU>(D, a, T, s);
 }
 

@@ -82,9 +82,10 @@ int expert_max_mtiles(int T, int k, int E, int bm = kExpertBM);
 // Expert GEMM 1 + GLU; its A rows are z[perm_src[r]] (the dispatch is part
 // of the operand load, no dispatch buffer is written).  A, U (both or
 // neither): the pre-activations X W_g^T, X W_u^T are stored there as well.
+// tall: the tile table is the kExpertBM2-row one (many rows per expert).
 hipError_t launch_expert_up(const Dims& D, const void* z, const int32_t* perm_src, const int2* tile_info,
                             const int32_t* n_mtiles, int T, const void* W_g, const void* W_u, void* H, hipStream_t s,
-                            void* A = nullptr, void* U = nullptr);
+                            void* A = nullptr, void* U = nullptr, bool tall = false);
 // Expert GEMM 2 over the kExpertBM2-row tile table (tile_info2, n_mtiles2).
 hipError_t launch_expert_down(const Dims& D, const void* H, const int2* tile_info, const int32_t* n_mtiles, int T,
                               const void* W_d, void* Y, hipStream_t s);

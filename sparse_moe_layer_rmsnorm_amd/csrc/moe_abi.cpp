@@ -459,8 +459,12 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
     st = route_tail(ctx, p, t, s);
     if (st != MOE_OK) return st;
     // dispatch X[r] = z[perm_src[r]] happens inside expert_up's operand load
-    MOE_RUN(MOE_K_EXPERT_UP, launch_expert_up(D, z, p.perm_src, p.tile_info, n_mtiles, t, ctx->w.W_g, ctx->w.W_u, H,
-                                              s, keep ? w + L.A : nullptr, keep ? w + L.U : nullptr));
+    // Many rows per expert (T k / E >= 512): 128-row tiles (better operand reuse); fewer: 64-row tiles
+    // (128-row ones measured slower at 192 and 293 rows per expert, 8-14% faster at 768 and 3072).
+    const bool tall = (long long)t * D.k >= 512LL * D.E;
+    MOE_RUN(MOE_K_EXPERT_UP, launch_expert_up(D, z, p.perm_src, tall ? p.tile_info2 : p.tile_info,
+                                              tall ? p.tile_offsets2 + D.E : n_mtiles, t, ctx->w.W_g, ctx->w.W_u, H,
+                                              s, keep ? w + L.A : nullptr, keep ? w + L.U : nullptr, tall));
     MOE_RUN(MOE_K_EXPERT_DOWN,
             launch_expert_down(D, H, p.tile_info2, p.tile_offsets2 + D.E, t, ctx->w.W_d, Y, s));
   }
