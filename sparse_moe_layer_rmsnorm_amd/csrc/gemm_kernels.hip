@@ -1,20 +1,35 @@
 // MFMA GEMMs of the LatentMoE layer on gfx950 (CDNA4).
 //
-// All products here are y = a W^T with both operands K-contiguous (activation
+// Forward products, y = a W^T with both operands K-contiguous (activation
 // rows and PyTorch-layout [out, in] weight rows), fp32 accumulation:
 //   * gemm_h:      h [T,d] against [W_r | W_sg,W_su | W_dn] -> fp32 router
 //                  logits, the shared GLU hidden G = silu(h W_sg^T)*(h W_su^T)
 //                  and the latent z = h W_dn^T in one launch (one pass of h);
 //   * expert_up:   per expert, its dispatched rows X against W_g[e], W_u[e]
-//                  with the GLU in the epilogue -> H;
+//                  with the GLU in the epilogue -> H (optionally also the
+//                  pre-activations, or H quantised to MXFP8);
 //   * expert_down: per expert, H rows against W_d[e] -> Y;
 //   * gemm_out:    [G | y_lat] against [W_sd | W_up] (one K loop over both
 //                  parts) -> out, so the shared and routed paths are summed in
-//                  the fp32 accumulators.
+//                  the fp32 accumulators;
+//   * expert_mx / expert_mx4: expert_up / expert_down with MXFP8 activations
+//                  against MXFP8 or MXFP4 weights (v_mfma_scale f8f6f4), and
+//                  mx_quant, the per-32-column quantiser that feeds them.
+// Backward products:
+//   * dense_nt / expert_nt: the forward layout with a plain store epilogue,
+//                  recomputing the GLU pre-activations h W_sg^T, h W_su^T and
+//                  X W_g[e]^T, X W_u[e]^T when they were not kept;
+// and, with K-major operands (see Pipe):
+//   * dgrad:       dX = dY W with W K-major ([out, in] read along out), dense
+//                  or per expert, several operands concatenated along K;
+//   * wgrad_km:    dW = dY^T X, contracting over tokens, both operands
+//                  token-major, per expert segment of the dispatch order.
 // (Width separation and the shared/routed dual path: architecture paragraph
 // and Tab 1 of the "Kimi K3 MoE lightweight replica demo" article; the expert
 // GLUs as batched matmuls per expert group: capsule 20 of the "Pretraining a
-// Mini Kimi K3" review.)
+// Mini Kimi K3" review; 4-bit expert weights against 8-bit activations:
+// fourth-waste section of the "K3 tops open source" blog, read as the OCP
+// MXFP4 / MXFP8 block formats.)
 //
 // Execution: persistent blocks of 4 wavefronts.  Block b runs on XCD b%8 and
 // walks a contiguous range of the logical tile order that belongs to its XCD,

@@ -10,8 +10,8 @@ what it reads for the plain 256 MiB device copy that `bench.py
 --copy-calibration` runs first, and prints a markdown table plus the JSON
 record (HBM bytes per launch per kernel) that bench.py reports as
 `roofline.traffic`; with a fifth argument it also writes that record, keyed
-by a hash of the kernel sources, to the given JSON file (bench.py reports the
-figure only while the sources still hash the same).
+by a hash of the kernel sources' code, comments excluded, to the given JSON
+file (bench.py reports the figure only while the sources still hash the same).
 
 The dense GEMM launches carry a tag template argument: 0 the h GEMM of a
 forward (gemm_h), 1 router logits alone (gemm_rz, routing-only pass), 2 the
@@ -37,12 +37,38 @@ COPY_BYTES = 256 << 20
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
-def source_hash() -> str:
-    """Hash of the HIP/C++ sources: counter figures are valid for one hash."""
+def strip_comments(text: str) -> str:
+    """C/C++ source with // and /* */ comments, trailing blanks and empty lines
+    removed (string and character literals are kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).split("\n"))
+    return "\n".join(line for line in lines if line)
+
+
+def source_hash(csrc: str = CSRC) -> str:
+    """Hash of the HIP/C++ sources' code (comments and blank lines excluded):
+    counter figures are valid for one hash."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + f.read())
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -164,3 +164,21 @@ def test_python_wrappers_raise_with_message():
     cfg.k = 0
     with pytest.raises(B.MoeError, match="MOE_ERR_SHAPE"):
         B.moe_state_layout_of(cfg)
+
+
+def test_counter_hash_follows_code_not_comments(tmp_path):
+    """The HBM-traffic figures are keyed by a hash of the kernel sources: a
+    comment or blank-line edit keeps it, any code edit changes it."""
+    import shutil
+    from sparse_moe_layer_rmsnorm_amd import profsum
+    src = tmp_path / "csrc"
+    shutil.copytree(profsum.CSRC, src)
+    h0 = profsum.source_hash(str(src))
+    assert h0 == profsum.source_hash()
+    f = src / "gemm_kernels.hip"
+    text = f.read_text()
+    f.write_text("// a new header line\n\n" + text.replace("\n", "  /* x */\n", 1))
+    assert profsum.source_hash(str(src)) == h0
+    f.write_text(text.replace("BM = BM_", "BM = BM_ + 0", 1))
+    assert profsum.source_hash(str(src)) != h0
+    assert profsum.strip_comments('s = "a//b"; c = \'/\'; // note\n/* x\n y */ t;') == 's = "a//b"; c = \'/\';\n t;'
