@@ -284,9 +284,10 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg, int64_t T);
  * is neither read nor changed.  T = 0 enqueues nothing.  With keep_preact
  * the weight-gradient products run on the context's internal stream, forked
  * from `stream` by events after their operands are written and joined back
- * before the call returns, so every result is still ordered on `stream`
- * (and the call can still be captured in a graph on `stream`); concurrent
- * moe_backward calls on one context are not allowed.
+ * before the call returns (also when it returns an error after the fork),
+ * so every result is still ordered on `stream` (and the call can still be
+ * captured in a graph on `stream`); concurrent moe_backward calls on one
+ * context are not allowed.
  */
 moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T, const moe_route_out* r,
                         const void* fwd_ws, size_t fwd_ws_bytes, void* dx, const moe_grads* g, void* ws,

@@ -551,13 +551,28 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   // stream (the overlap measured slower there).
   const bool kept = c.keep_preact != 0;  // pre-activations stored by the forward
   hipStream_t s2 = kept ? ctx->side : s;
+  // Once forked, every return (an error included) leaves the caller's stream
+  // waiting for the internal one, so no work of this call outlives it there.
+  struct Join {
+    hipStream_t s, s2;
+    hipEvent_t ev;
+    bool armed = false;
+    ~Join() {
+      if (armed) {
+        (void)hipEventRecord(ev, s2);
+        (void)hipStreamWaitEvent(s, ev, 0);
+      }
+    }
+  } join{s, s2, ctx->join_ev};
   int nfork = 0;
   auto fork = [&]() -> moe_status {
     if (s2 == s) return MOE_OK;
     hipEvent_t ev = ctx->fork_ev[nfork++];
     hipError_t e = hipEventRecord(ev, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s2, ev, 0);
-    return e == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "forking the backward stream failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "forking the backward stream failed: %s", hipGetErrorString(e));
+    join.armed = true;
+    return MOE_OK;
   };
   const int u = Tp / 64;
   auto slices = [&](int want, int* step) {
@@ -702,7 +717,8 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   MOE_RUN(MOE_K_BWD_ELTWISE, launch_rmsnorm_bwd(D, x, W.gamma, dh, t, dx, static_cast<float*>(at(B.rstd)),
                                                 static_cast<float*>(at(B.gpart)), kGammaSlices, g->gamma, s));
   // join: the caller's stream waits for the weight gradients
-  if (s2 != s) {
+  if (join.armed) {
+    join.armed = false;
     hipError_t e = hipEventRecord(ctx->join_ev, s2);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, ctx->join_ev, 0);
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "joining the backward stream failed: %s", hipGetErrorString(e));
