@@ -103,6 +103,10 @@ MOE_DEV void wait_vmcnt() {
 
 MOE_DEV void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// s_waitcnt immediate (gfx9 encoding) for lgkmcnt(0) with vmcnt and expcnt
+// left at their maxima, i.e. no wait on them.
+constexpr int kLgkmcnt0 = 0xC07F;
+
 // Scalar (SMEM) load of wave-uniform tile metadata written by an earlier kernel.
 MOE_DEV int2 scalar_load2(const int2* p, int i) {
   const unsigned long long v = *((const __attribute__((address_space(4))) unsigned long long*)p + i);
@@ -526,6 +530,14 @@ MOE_DEV void stream(const Prob& prob, char* smem) {
     Pp::wait_stage(issued - g - 1);
     block_barrier();
     if (issued < total) issue();
+    // Prob::kSettleScalar: wait for any scalar load still in flight before
+    // the fragment reads.  Scalar loads share lgkmcnt with LDS reads and
+    // return out of order, so while one may be pending the compiler waits for
+    // all 16 fragment reads before the first MFMA; with none pending it waits
+    // for just the fragments each MFMA group needs, and the later reads land
+    // under the first MFMAs (the dense GEMMs gain 2-3%; the grouped ones,
+    // whose gather indices come by scalar loads just before, lose).
+    if constexpr (Prob::kSettleScalar) __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
     Pp::compute(smem + (g % Pp::NS) * Pp::STAGE, acc);
     if (++cks == KT) {
       prob.epilogue(ct, acc);
@@ -614,6 +626,7 @@ MOE_DEV Tile dense_tile(int L, int m_tiles, int total_ntiles, int M, int nseg, i
 template <class Pp>
 struct DenseProb {
   static constexpr int PARTS = 2;
+  static constexpr bool kSettleScalar = true;  // operand addresses come from kernel arguments
   template <int L>
   struct SrcT {
     const char* p[2][L];
@@ -737,6 +750,7 @@ struct ExpertArgs {
 template <class Pp, int KIND>
 struct ExpertProb {
   static constexpr int PARTS = 1;
+  static constexpr bool kSettleScalar = false;
   template <int L>
   struct SrcT {
     const char* p[L];
@@ -860,6 +874,7 @@ struct DgradArgs {
 template <class Pp, bool EXPERT>
 struct DgradProb {
   static constexpr int PARTS = 1;
+  static constexpr bool kSettleScalar = false;
   static constexpr int LA = Pp::LA, KR = Pp::KR;
   template <int L>
   struct SrcT {
