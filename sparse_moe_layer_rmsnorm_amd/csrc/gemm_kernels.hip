@@ -273,10 +273,15 @@ struct Pipe {
       for (int kk = 0; kk < KK; ++kk) {
         const int ch = kk * 4 + (lane >> 4);
         uint4 af[MI], wf[NI];
+        // read in first-use order (row fragment 0, every weight fragment, the
+        // other row fragments) so each MFMA group waits only for its own reads
+        af[0] = frag_a(cur, wm * WTM, ch, kk);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) wf[ni] = frag_b(cur, wn * WTN + ni * 16, ch, kk);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) af[mi] = frag_a(cur, wm * WTM + mi * 16, ch, kk);
+        for (int mi = 1; mi < MI; ++mi) af[mi] = frag_a(cur, wm * WTM + mi * 16, ch, kk);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
@@ -287,12 +292,15 @@ struct Pipe {
     }
     uint4 af[KK][MI], wf[KK][NI];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {  // in first-use order, as above
       const int ch = kk * 4 + (lane >> 4);
+      af[kk][0] = frag_a(cur, wm * WTM, ch, kk);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) wf[kk][ni] = frag_b(cur, wn * WTN + ni * 16, ch, kk);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) af[kk][mi] = frag_a(cur, wm * WTM + mi * 16, ch, kk);
+      for (int mi = 1; mi < MI; ++mi) af[kk][mi] = frag_a(cur, wm * WTM + mi * 16, ch, kk);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
