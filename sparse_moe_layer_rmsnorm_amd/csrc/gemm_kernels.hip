@@ -1191,9 +1191,22 @@ __global__ __launch_bounds__(Pp::THREADS, Pp::BPC * Pp::NW / 4) void k_gemm_wgra
 // DMA ring, LDS layout and epilogues are those of the bf16 expert GEMM.
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 
+// Byte g (the lane's 32-element block) of the current stage's scale word,
+// which is always w[0]: the words then move down one place for the next
+// stage (the tile's stages run in order from 0 and the next tile reloads
+// them).  Indexing the words by the stage number instead made the compiler
+// branch on it between MFMAs, or keep the words in scratch memory.
+MOE_DEV int mx_take(uint32_t (&w)[4], int g) {
+  const int v = (int)((w[0] >> (8 * g)) & 0xFFu);
+  w[0] = w[1];
+  w[1] = w[2];
+  w[2] = w[3];
+  return v;
+}
+
 template <class Pp>
-MOE_DEV void mx_compute(const char* cur, typename Pp::Acc& acc, const uint32_t (&sa)[Pp::MI][4],
-                        const uint32_t (&sb)[Pp::NI][4], int s) {
+MOE_DEV void mx_compute(const char* cur, typename Pp::Acc& acc, uint32_t (&sa)[Pp::MI][4],
+                        uint32_t (&sb)[Pp::NI][4]) {
   const int lane = threadIdx.x & 63, wave = Pp::wave_id();
   const int wm = wave / Pp::WN, wn = wave % Pp::WN, g = lane >> 4;
   v8i_t af[Pp::MI], wf[Pp::NI];
@@ -1211,20 +1224,20 @@ MOE_DEV void mx_compute(const char* cur, typename Pp::Acc& acc, const uint32_t (
     const uint4 hi = *reinterpret_cast<const uint4*>(cur + Pp::lds_off(row, 4 + g));
     af[mi] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
-  const int sh = 8 * g;
-  auto pick = [&](const uint32_t (&w)[4]) -> int {
-    const uint32_t v = s == 0 ? w[0] : (s == 1 ? w[1] : (s == 2 ? w[2] : w[3]));
-    return (int)((v >> sh) & 0xFFu);
-  };
+  // the stage's scale byte of every row and weight fragment, taken once
+  // before the MFMAs
+  int scA[Pp::MI], scB[Pp::NI];
+#pragma unroll
+  for (int mi = 0; mi < Pp::MI; ++mi) scA[mi] = mx_take(sa[mi], g);
+#pragma unroll
+  for (int ni = 0; ni < Pp::NI; ++ni) scB[ni] = mx_take(sb[ni], g);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int mi = 0; mi < Pp::MI; ++mi) {
-    const int sA = pick(sa[mi]);
+  for (int mi = 0; mi < Pp::MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < Pp::NI; ++ni)
-      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[ni], af[mi], acc[mi][ni], 0, 0, 0, pick(sb[ni]),
-                                                                     0, sA);
-  }
+      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[ni], af[mi], acc[mi][ni], 0, 0, 0, scB[ni],
+                                                                     0, scA[mi]);
 }
 
 template <class Pp, int KIND>
@@ -1293,8 +1306,8 @@ struct Mx4Pipe : Pipe<BM_, BN_, WM_, WN_, NS_, 128, BPC_, true> {
 };
 
 template <class Pp>
-MOE_DEV void mx4_compute(const char* cur, typename Pp::Acc& acc, const uint32_t (&sa)[Pp::MI][4],
-                         const uint32_t (&sb)[Pp::NI][4], int s) {
+MOE_DEV void mx4_compute(const char* cur, typename Pp::Acc& acc, uint32_t (&sa)[Pp::MI][4],
+                         uint32_t (&sb)[Pp::NI][4]) {
   const int lane = threadIdx.x & 63, wave = Pp::wave_id();
   const int wm = wave / Pp::WN, wn = wave % Pp::WN, g = lane >> 4;
   v8i_t af[Pp::MI], wf[Pp::NI];
@@ -1310,20 +1323,20 @@ MOE_DEV void mx4_compute(const char* cur, typename Pp::Acc& acc, const uint32_t 
     const uint4 hi = *reinterpret_cast<const uint4*>(cur + Pp::lds_off(row, 4 + g));
     af[mi] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
-  const int sh = 8 * g;
-  auto pick = [&](const uint32_t (&w)[4]) -> int {
-    const uint32_t v = s == 0 ? w[0] : (s == 1 ? w[1] : (s == 2 ? w[2] : w[3]));
-    return (int)((v >> sh) & 0xFFu);
-  };
+  // the stage's scale byte of every row and weight fragment, taken once
+  // before the MFMAs
+  int scA[Pp::MI], scB[Pp::NI];
+#pragma unroll
+  for (int mi = 0; mi < Pp::MI; ++mi) scA[mi] = mx_take(sa[mi], g);
+#pragma unroll
+  for (int ni = 0; ni < Pp::NI; ++ni) scB[ni] = mx_take(sb[ni], g);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int mi = 0; mi < Pp::MI; ++mi) {
-    const int sA = pick(sa[mi]);
+  for (int mi = 0; mi < Pp::MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < Pp::NI; ++ni)
-      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[ni], af[mi], acc[mi][ni], 4, 0, 0,
-                                                                     pick(sb[ni]), 0, sA);
-  }
+      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[ni], af[mi], acc[mi][ni], 4, 0, 0, scB[ni],
+                                                                     0, scA[mi]);
 }
 
 template <class Pp, int KIND>
@@ -1401,8 +1414,8 @@ MOE_DEV void expert_mx_stream(const ExpertArgs& args, char* smem) {
 #pragma unroll
     for (int i = 0; i < Pp::NI; ++i) asm volatile("" ::"v"(sb[i][0]), "v"(sb[i][1]), "v"(sb[i][2]), "v"(sb[i][3]));
     if (issued < total) issue();
-    if constexpr (W4) mx4_compute<Pp>(smem + (g % Pp::NS) * Pp::STAGE, acc, sa, sb, cks);
-    else mx_compute<Pp>(smem + (g % Pp::NS) * Pp::STAGE, acc, sa, sb, cks);
+    if constexpr (W4) mx4_compute<Pp>(smem + (g % Pp::NS) * Pp::STAGE, acc, sa, sb);
+    else mx_compute<Pp>(smem + (g % Pp::NS) * Pp::STAGE, acc, sa, sb);
     if (++cks == KT) {
       prob.epilogue(ct, acc);
       Pp::zero(acc);
