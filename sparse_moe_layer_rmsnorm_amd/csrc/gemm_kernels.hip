@@ -290,6 +290,40 @@ struct Pipe {
       }
       return;
     }
+    if constexpr (BF16 && KM == 3) {
+      // Both operands K-major: two transposed reads per fragment, 2 (MI+NI)
+      // reads per K step, more than lgkmcnt can count at once.  The next K
+      // step's reads are interleaved with this step's MFMAs (two reads per
+      // MFMA) instead of all being issued up front.
+      uint4 af[KK][MI], wf[KK][NI];
+      auto load = [&](int kk) {
+        const int ch = kk * 4 + (lane >> 4);
+        af[kk][0] = frag_a(cur, wm * WTM, ch, kk);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) wf[kk][ni] = frag_b(cur, wn * WTN + ni * 16, ch, kk);
+#pragma unroll
+        for (int mi = 1; mi < MI; ++mi) af[kk][mi] = frag_a(cur, wm * WTM + mi * 16, ch, kk);
+      };
+      load(0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) load(kk + 1);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) mfma_chunk<BF16>(acc[mi][ni], wf[kk][ni], af[kk][mi]);
+        if (kk + 1 < KK) {
+#pragma unroll
+          for (int i = 0; i < MI * NI; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
     uint4 af[KK][MI], wf[KK][NI];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {  // in first-use order, as above
