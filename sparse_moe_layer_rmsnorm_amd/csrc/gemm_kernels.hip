@@ -721,11 +721,16 @@ struct DenseProb {
 
   template <int L>
   MOE_DEV void issue(const SrcT<L>& src, int ks, uint32_t lds) const {
-    const bool second = ks >= a.kt[0];
-    const int off = (second ? ks - a.kt[0] : ks) * Pp::RB;
+    // the K part is wave-uniform: one scalar branch, not a per-slot select
+    if (ks >= uniform_int(a.kt[0])) {
+      const int off = (ks - uniform_int(a.kt[0])) * Pp::RB;
 #pragma unroll
-    for (int i = 0; i < L; ++i)
-      lds_dma16((second ? src.p[1][i] : src.p[0][i]) + off, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
+      for (int i = 0; i < L; ++i) lds_dma16(src.p[1][i] + off, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
+    } else {
+      const int off = ks * Pp::RB;
+#pragma unroll
+      for (int i = 0; i < L; ++i) lds_dma16(src.p[0][i] + off, __builtin_amdgcn_readfirstlane(lds + i * Pp::NW * 1024));
+    }
   }
 
 
