@@ -684,37 +684,60 @@ struct DenseProb {
     return dense_tile<Pp::BM>(L, a.m_tiles, a.total_ntiles, a.M, a.nseg, a.seg[0].ntiles, a.seg[1].ntiles);
   }
 
-  // Start of stage row `row` (A rows first, then weight rows) of K part `part`.
-  MOE_DEV const char* row_ptr(const Tile& t, const DenseSeg& S, int part, int row) const {
+  // Wave-uniform operand fields of one K part of the tile's segment, read
+  // once per tile (readfirstlane is not merged across calls, so reading them
+  // per slot put a chain of dependent scalar loads at every tile switch).
+  struct PartSrc {
+    const char *A, *gate, *up;
+    int lda, ldb, N;
+    bool glu;
+  };
+
+  // Start of stage row `row` (A rows first, then weight rows).
+  MOE_DEV static const char* row_ptr(const Tile& t, const PartSrc& P, int row) {
     if (row < Pp::BM) {  // A row (rows past the end read row0: their results are not stored)
       const int r = row < t.rows ? row : 0;
-      return uniform_ptr(a.A[part]) + (size_t)(t.row0 + r) * uniform_int(a.lda_bytes[part]);
+      return P.A + (size_t)(t.row0 + r) * P.lda;
     }
     const int c = row - Pp::BM;  // weight row of tile column c (columns past N read row 0)
-    const char* gate = uniform_ptr(S.B[part]);
     int wrow;
     const char* base;
-    if (S.kind == EPI_GLU) {
+    if (P.glu) {
       wrow = t.nt * (Pp::BN / 2) + (c >> 5) * 16 + (c & 15);
-      base = ((c & 31) >= 16) ? uniform_ptr(S.Bu[part]) : gate;
+      base = ((c & 31) >= 16) ? P.up : P.gate;
     } else {
       wrow = t.nt * Pp::BN + c;
-      base = gate;
+      base = P.gate;
     }
-    if (wrow >= uniform_int(S.N)) wrow = 0;
-    return base + (size_t)wrow * uniform_int(a.ldb_bytes[part]);
+    if (wrow >= P.N) wrow = 0;
+    return base + (size_t)wrow * P.ldb;
   }
 
   template <int L>
   MOE_DEV void sources(const Tile& t, SrcT<L>& src) const {
     const int lane = threadIdx.x & 63, wave = Pp::wave_id();
     const DenseSeg& S = seg(t.sel);
+    const bool glu = S.kind == EPI_GLU;
+    const int N = uniform_int(S.N);
 #pragma unroll
     for (int part = 0; part < 2; ++part) {
+      if (a.kt[part] <= 0) {
+#pragma unroll
+        for (int i = 0; i < L; ++i) src.p[part][i] = nullptr;
+        continue;
+      }
+      PartSrc P;
+      P.A = uniform_ptr(a.A[part]);
+      P.lda = uniform_int(a.lda_bytes[part]);
+      P.gate = uniform_ptr(S.B[part]);
+      P.up = glu ? uniform_ptr(S.Bu[part]) : P.gate;
+      P.ldb = uniform_int(a.ldb_bytes[part]);
+      P.N = N;
+      P.glu = glu;
 #pragma unroll
       for (int i = 0; i < L; ++i) {
         const int row = Pp::slot_row(i, wave, lane);
-        src.p[part][i] = a.kt[part] > 0 ? row_ptr(t, S, part, row) + Pp::slot_chunk(row, lane) * 16 : nullptr;
+        src.p[part][i] = row_ptr(t, P, row) + Pp::slot_chunk(row, lane) * 16;
       }
     }
   }
