@@ -107,9 +107,22 @@ typedef enum moe_expert_format {
 } moe_expert_format;
 
 /*
- * Layer sizes.  d, l, f must be multiples of 64 and f_s a multiple of 64 or 0
- * (0 = no shared expert; several shared experts of hidden f are one of hidden
- * n*f).  1 <= E <= 1024, 1 <= k <= min(E, 32), 2 <= qb_bins <= 256.
+ * Layer sizes.  d, l, f must be multiples of 64 and f_s a multiple of 64 or 0.
+ * n_shared shared experts (>= 0), each a GLU of hidden f_s at width d (the
+ * shared path of the demo article's architecture paragraph); their outputs
+ * add, so they are held as one GLU of hidden n_shared*f_s: W_sg, W_su are
+ * [n_shared*f_s, d] (expert i's hidden units at rows i*f_s ..) and W_sd is
+ * [d, n_shared*f_s].  No shared path when n_shared*f_s == 0.
+ * 1 <= E <= 1024, 1 <= k <= min(E, 32), 2 <= qb_bins <= 256.
+ * qb_lo < qb_hi (finite): the QB histogram has qb_bins equal bins over the
+ * score range [qb_lo, qb_hi] (Tab 2 Fig. 2(b) of the demo article: a
+ * histogram estimate of each expert's score quantile); a score s falls in bin
+ * clamp(floor(fp32(fp32(s - qb_lo) * scale)), 0, qb_bins - 1) with scale =
+ * fp32(qb_bins / (qb_hi - qb_lo)) (quotient in fp64), so scores beyond the
+ * range count in the end bins, and the quantile estimate is mapped back as
+ * qb_lo + (qb_hi - qb_lo) * u (fp64).  Sigmoid scores lie in (0, 1): the
+ * range [0, 1] covers them all; a narrower range that still holds every
+ * expert's target quantile gives narrower bins.
  * max_tokens bounds T for every call (1 <= max_tokens, max_tokens*k < 2^31).
  * rms_eps > 0.  routed_scale multiplies every gate (1 = plain renormalised).
  * balancer picks the update rule; sign_gamma (finite, > 0) is read only for
@@ -122,10 +135,11 @@ typedef enum moe_expert_format {
  * 2 (T f_s + T k f) more stored elements per forward).
  */
 typedef struct moe_config {
-  int32_t d, l, E, k, f, f_s;
+  int32_t d, l, E, k, f, f_s, n_shared;
   moe_dtype dtype;
   float rms_eps;
   int32_t qb_bins;
+  float qb_lo, qb_hi;
   moe_qb_mode qb_mode;
   int64_t max_tokens;
   float routed_scale;
@@ -139,10 +153,12 @@ typedef struct moe_config {
 typedef struct moe_weights {
   const float* gamma;        /* [d]     fp32 RMSNorm scale                 */
   const void* W_r;           /* [E,d]   router                             */
-  const float* logit_offset; /* [E]     fp32 added to the logits, or NULL  */
-  const void* W_sg;          /* [f_s,d] shared gate   (NULL when f_s == 0) */
-  const void* W_su;          /* [f_s,d] shared up     (NULL when f_s == 0) */
-  const void* W_sd;          /* [d,f_s] shared down   (NULL when f_s == 0) */
+  const float* logit_offset; /* [E]     fp32 added to the logits, or NULL: a
+                                learned router logit bias, which (unlike the
+                                QB bias) also moves the scores and gates   */
+  const void* W_sg;          /* [n_shared*f_s,d] shared gate (NULL: no shared path) */
+  const void* W_su;          /* [n_shared*f_s,d] shared up                       */
+  const void* W_sd;          /* [d,n_shared*f_s] shared down                     */
   const void* W_dn;          /* [l,d]   down-projection d -> l             */
   const void* W_g;           /* [E,f,l] expert gate                        */
   const void* W_u;           /* [E,f,l] expert up                          */
@@ -190,7 +206,7 @@ typedef struct moe_ws_layout {
                                   E4M3 bytes and E8M0 scales; Xs the scale rows of
                                   the grouped rows */
   size_t P, Q, A, U;            /* keep_preact only (else zero bytes): the GLU
-                                  pre-activations, P, Q [T, f_s], A, U [T k, f]
+                                  pre-activations, P, Q [T, n_shared f_s], A, U [T k, f]
                                   (grouped rows, as H) */
   size_t total;
 } moe_ws_layout;
@@ -231,6 +247,18 @@ moe_status moe_route(moe_ctx* ctx, const void* x, const float* logits, int64_t T
  * enqueues nothing).  In training mode also adds the tokens' scores to the QB
  * histogram.  `r` (may be NULL) receives the routing.  `ws` must hold
  * moe_workspace_bytes(cfg, T) bytes of device memory (256-byte aligned).
+ *
+ * Statistics window.  The histogram bins and loads are 32-bit counters, so
+ * one window (the training tokens between two qb_update calls) holds at
+ * most 2^32 - 1 tokens.  A forward or routing call that would pass that
+ * returns MOE_ERR_STATE before enqueueing anything; the host counts the
+ * tokens of the calls it sees.  Replays of a captured graph are not calls:
+ * a graph that holds training forwards should hold qb_update too (or be
+ * replayed fewer than (2^32 - 1) / T times between updates).  If a replayed
+ * window does pass the limit, the device's own 64-bit token count catches
+ * it: that qb_update leaves the bias unchanged, writes NaN to every q_e of
+ * the state (moe_state_layout.q) and clears the window.  Nothing is ever
+ * silently wrapped.
  */
 moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_route_out* r, void* ws,
                        size_t ws_bytes, void* stream);
@@ -249,15 +277,16 @@ moe_status qb_update(moe_ctx* ctx, void* stream);
 /*
  * Gradients of the layer (fp32, the shapes of moe_weights; every pointer is
  * device memory, overwritten, not accumulated).  W_sg, W_su, W_sd may be NULL
- * when f_s == 0.  The router bias gets no gradient: it only reroutes (Tab 8-10
- * of the demo article), so a routing decision is a constant of the backward.
+ * when there is no shared path (n_shared * f_s == 0).  The router bias gets
+ * no gradient: it only reroutes (Tab 8-10 of the demo article), so a routing
+ * decision is a constant of the backward.
  */
 typedef struct moe_grads {
   float* gamma; /* [d]     */
   float* W_r;   /* [E,d]   */
-  float* W_sg;  /* [f_s,d] */
-  float* W_su;  /* [f_s,d] */
-  float* W_sd;  /* [d,f_s] */
+  float* W_sg;  /* [n_shared*f_s,d] */
+  float* W_su;  /* [n_shared*f_s,d] */
+  float* W_sd;  /* [d,n_shared*f_s] */
   float* W_dn;  /* [l,d]   */
   float* W_g;   /* [E,f,l] */
   float* W_u;   /* [E,f,l] */

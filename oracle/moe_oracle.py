@@ -193,31 +193,43 @@ def permutation(idx: np.ndarray, E: int):
 # --------------------------------------------------------------------------
 
 
-def score_bins(s: np.ndarray, B: int) -> np.ndarray:
-    """bin = min(B-1, floor(s*B)), s*B an fp32 product."""
-    sb = (np.asarray(s, dtype=F32) * F32(B)).astype(F32)
-    return np.minimum(np.floor(sb).astype(np.int64), B - 1)
+def bin_scale(B: int, lo: float = 0.0, hi: float = 1.0) -> np.float32:
+    """Bins per unit of score, fp32(B / (hi - lo)) with the quotient taken in
+    fp64 on the fp32 range ends (exactly B on [0, 1])."""
+    return F32(float(B) / (float(F32(hi)) - float(F32(lo))))
 
 
-def histogram(s: np.ndarray, B: int) -> np.ndarray:
+def score_bins(s: np.ndarray, B: int, lo: float = 0.0, hi: float = 1.0) -> np.ndarray:
+    """B equal bins over the score range [lo, hi]:
+    bin = clamp(floor(fp32(fp32(s - lo) * scale)), 0, B-1), scale from
+    ``bin_scale``; scores outside the range land in the end bins.  On [0, 1]
+    this is min(B-1, floor(s*B)) with s*B an fp32 product."""
+    t = (np.asarray(s, dtype=F32) - F32(lo)).astype(F32)
+    sb = (t * bin_scale(B, lo, hi)).astype(F32)
+    return np.clip(np.floor(sb).astype(np.int64), 0, B - 1)
+
+
+def histogram(s: np.ndarray, B: int, lo: float = 0.0, hi: float = 1.0) -> np.ndarray:
     """hist[E,B] (int64): per expert, the number of tokens whose score falls
-    in each of B equal bins of [0, 1]."""
+    in each of B equal bins of [lo, hi] (end bins also take what lies beyond)."""
     T, E = s.shape
-    bins = score_bins(s, B)
+    bins = score_bins(s, B, lo, hi)
     flat = (np.arange(E)[None, :] * B + bins).reshape(-1)
     return np.bincount(flat, minlength=E * B).reshape(E, B).astype(np.int64)
 
 
-def qb_quantiles(hist: np.ndarray, N: int, k: int) -> np.ndarray:
+def qb_quantiles(hist: np.ndarray, N: int, k: int, lo: float = 0.0, hi: float = 1.0) -> np.ndarray:
     """Histogram estimate q_e of the score each expert must exceed to receive
     its target load m = N*k/E.
 
     Scanning bins from the top, j is the bin with A_j*E < N*k <= (A_j+c_j)*E
     (A_j = count above bin j, integer comparisons); inside it the estimate is
-    linear: q = (j+1)/B - ((N*k - A_j*E) / (E*c_j)) / B   (fp64).
+    linear, as a fraction u of the range: u = (j+1)/B - ((N*k - A_j*E) /
+    (E*c_j)) / B, and q = lo + (hi - lo) * u (fp64; q = u on [0, 1]).
     """
     E, B = hist.shape
     target = N * k
+    lo64, w64 = float(F32(lo)), float(F32(hi)) - float(F32(lo))
     q = np.zeros(E, dtype=np.float64)
     for e in range(E):
         above = 0
@@ -225,7 +237,7 @@ def qb_quantiles(hist: np.ndarray, N: int, k: int) -> np.ndarray:
             c = int(hist[e, j])
             if above * E < target <= (above + c) * E:
                 frac = float(target - above * E) / float(E * c)
-                q[e] = (j + 1) / B - frac / B
+                q[e] = lo64 + w64 * ((j + 1) / B - frac / B)
                 break
             above += c
         else:                                   # unreachable for N > 0
@@ -242,12 +254,13 @@ def qb_bias(q: np.ndarray) -> np.ndarray:
     return np.array([mu - float(v) for v in q], dtype=np.float64).astype(F32)
 
 
-def qb_update(hist: np.ndarray, N: int, k: int, bias: np.ndarray) -> np.ndarray:
-    """New bias from the accumulated histogram; the old bias is kept when no
-    token was seen.  The caller applies it to the next forward (one step late)."""
+def qb_update(hist: np.ndarray, N: int, k: int, bias: np.ndarray, lo: float = 0.0, hi: float = 1.0) -> np.ndarray:
+    """New bias from the accumulated histogram over [lo, hi]; the old bias is
+    kept when no token was seen.  The caller applies it to the next forward
+    (one step late)."""
     if N == 0:
         return np.asarray(bias, dtype=F32).copy()
-    return qb_bias(qb_quantiles(hist, N, k))
+    return qb_bias(qb_quantiles(hist, N, k, lo, hi))
 
 
 def sign_update(load: np.ndarray, bias: np.ndarray, gamma: float) -> np.ndarray:
@@ -437,7 +450,7 @@ def expert_outputs(X: np.ndarray, offsets: np.ndarray, W: Dict[str, np.ndarray],
 def forward(x: np.ndarray, W: Dict[str, np.ndarray], bias: np.ndarray, *, k: int, dtype: str,
             eps: float = 1e-6, B: int = 256, routed_scale: float = 1.0,
             logits: Optional[np.ndarray] = None, with_hist: bool = True,
-            experts: str = "bf16") -> Dict[str, np.ndarray]:
+            experts: str = "bf16", qb_lo: float = 0.0, qb_hi: float = 1.0) -> Dict[str, np.ndarray]:
     """One training (or frozen) forward of the layer on x[T,d].
 
     ``logits`` (fp32 [T,E]) replaces the router output when given, so that the
@@ -458,7 +471,7 @@ def forward(x: np.ndarray, W: Dict[str, np.ndarray], bias: np.ndarray, *, k: int
     s = sigmoid_r(lg)                                                  # S3
     r["s"] = s
     if with_hist:
-        r["hist"] = histogram(s, B)                                    # S4
+        r["hist"] = histogram(s, B, qb_lo, qb_hi)                      # S4
     idx = topk_select(s, bias, k)                                      # S5
     g = gates_from(s, idx, routed_scale)                               # S6
     r["idx"], r["gates"] = idx, g

@@ -30,9 +30,10 @@ MOE_NUM_KERNELS = len(KERNELS)
 
 class moe_config(ctypes.Structure):
     _fields_ = [("d", c_int32), ("l", c_int32), ("E", c_int32), ("k", c_int32), ("f", c_int32), ("f_s", c_int32),
-                ("dtype", c_int), ("rms_eps", c_float), ("qb_bins", c_int32), ("qb_mode", c_int),
-                ("max_tokens", c_int64), ("routed_scale", c_float), ("balancer", c_int), ("sign_gamma", c_float),
-                ("experts", c_int), ("keep_preact", c_int32)]
+                ("n_shared", c_int32), ("dtype", c_int), ("rms_eps", c_float), ("qb_bins", c_int32),
+                ("qb_lo", c_float), ("qb_hi", c_float), ("qb_mode", c_int), ("max_tokens", c_int64),
+                ("routed_scale", c_float), ("balancer", c_int), ("sign_gamma", c_float), ("experts", c_int),
+                ("keep_preact", c_int32)]
 
 
 class moe_weights(ctypes.Structure):
@@ -214,12 +215,14 @@ def moe_profile_end(ctx: int) -> Dict[str, tuple]:
     return {KERNELS[i]: (ms[i], n[i]) for i in range(MOE_NUM_KERNELS)}
 
 
-def make_config(d: int, l: int, E: int, k: int, f: int, f_s: int, *, dtype: str = "bf16", rms_eps: float = 1e-6,
-                qb_bins: int = 256, frozen: bool = False, max_tokens: int = 1, routed_scale: float = 1.0,
-                balancer: str = "qb", sign_gamma: float = 1e-2, experts: str = "bf16",
-                keep_preact: bool = False) -> moe_config:
-    return moe_config(d=d, l=l, E=E, k=k, f=f, f_s=f_s, dtype=MOE_BF16 if dtype == "bf16" else MOE_F32,
-                      rms_eps=rms_eps, qb_bins=qb_bins, qb_mode=MOE_QB_FROZEN if frozen else MOE_QB_TRAIN,
+def make_config(d: int, l: int, E: int, k: int, f: int, f_s: int, *, n_shared: int = 1, dtype: str = "bf16",
+                rms_eps: float = 1e-6, qb_bins: int = 256, qb_lo: float = 0.0, qb_hi: float = 1.0,
+                frozen: bool = False, max_tokens: int = 1, routed_scale: float = 1.0, balancer: str = "qb",
+                sign_gamma: float = 1e-2, experts: str = "bf16", keep_preact: bool = False) -> moe_config:
+    """f_s is the hidden width of each of the n_shared shared experts."""
+    return moe_config(d=d, l=l, E=E, k=k, f=f, f_s=f_s, n_shared=n_shared,
+                      dtype=MOE_BF16 if dtype == "bf16" else MOE_F32, rms_eps=rms_eps, qb_bins=qb_bins,
+                      qb_lo=qb_lo, qb_hi=qb_hi, qb_mode=MOE_QB_FROZEN if frozen else MOE_QB_TRAIN,
                       max_tokens=max_tokens, routed_scale=routed_scale,
                       balancer=MOE_BALANCE_SIGN if balancer == "sign" else MOE_BALANCE_QB, sign_gamma=sign_gamma,
                       experts=_EXPERT_FORMATS[experts],

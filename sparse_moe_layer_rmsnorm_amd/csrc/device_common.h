@@ -57,12 +57,16 @@ MOE_DEV float router_sigmoid(float logit) {
   return 1.0f / (1.0f + e);
 }
 
-// Histogram bin of a score in [0, 1]: min(B - 1, floor(s * B)), s*B in fp32.
-MOE_DEV int score_bin(float s, int B) {
+// Histogram bin of a score over the range [lo, lo + B / scale]:
+// clamp(floor(fp32(fp32(s - lo) * scale)), 0, B - 1), scale = fp32(B / (hi -
+// lo)); on [0, 1] this is min(B - 1, floor(s * B)) with s*B in fp32.  Scores
+// beyond the range fall in the end bins (the clamp is done in fp32 first, so
+// no out-of-range float reaches the integer conversion).
+MOE_DEV int score_bin(float s, int B, float lo, float scale) {
 #pragma clang fp contract(off)
-  int b = (int)floorf(s * (float)B);
-  b = b > 0 ? b : 0;
-  return b < B - 1 ? b : B - 1;
+  const float t = floorf((s - lo) * scale);
+  const float c = fminf(fmaxf(t, 0.0f), (float)(B - 1));
+  return (int)c;
 }
 
 // Orderable key of an fp32 value: a larger float gives a larger key; -0 and

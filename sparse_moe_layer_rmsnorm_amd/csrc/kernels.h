@@ -26,9 +26,10 @@ constexpr int kExpertBM2 = 2 * kExpertBM;
 constexpr int kHistExperts = 16;
 
 struct Dims {
-  int d, l, E, k, f, f_s, B;
+  int d, l, E, k, f, f_s, B;  // f_s: hidden of the whole shared path (n_shared GLUs as one)
   bool bf16;
   float eps, routed_scale;
+  float qb_lo, qb_hi, qb_scale;  // histogram score range and fp32(B / (qb_hi - qb_lo))
 };
 
 hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s);

@@ -32,6 +32,14 @@ moe_status fail(moe_status st, const char* fmt, ...) {
 constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Hidden width of the shared path: n_shared GLUs of hidden f_s held as one.
+int32_t shared_hidden(const moe_config* c) { return c->n_shared * c->f_s; }
+
+// Bins per unit of score: fp32(B / (hi - lo)), the quotient in fp64.
+float qb_scale(const moe_config* c) {
+  return (float)((double)c->qb_bins / ((double)c->qb_hi - (double)c->qb_lo));
+}
+
 moe_status check_config(const moe_config* c) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return fail(MOE_ERR_DTYPE, "unknown dtype %d", (int)c->dtype);
@@ -57,8 +65,14 @@ moe_status check_config(const moe_config* c) {
   if (!m64(c->d) || !m64(c->l) || !m64(c->f))
     return fail(MOE_ERR_SHAPE, "d, l, f must be positive multiples of 64 (d=%d l=%d f=%d)", c->d, c->l, c->f);
   if (c->f_s < 0 || c->f_s % 64 != 0) return fail(MOE_ERR_SHAPE, "f_s must be 0 or a multiple of 64 (f_s=%d)", c->f_s);
-  if (c->d > (1 << 20) || c->l > (1 << 20) || c->f > (1 << 20) || c->f_s > (1 << 20))
-    return fail(MOE_ERR_SHAPE, "a width exceeds 2^20");
+  if (c->n_shared < 0) return fail(MOE_ERR_SHAPE, "n_shared must be >= 0 (n_shared=%d)", c->n_shared);
+  if (c->d > (1 << 20) || c->l > (1 << 20) || c->f > (1 << 20) || (int64_t)c->n_shared * c->f_s > (1 << 20))
+    return fail(MOE_ERR_SHAPE, "a width (or n_shared*f_s) exceeds 2^20");
+  if (!std::isfinite(c->qb_lo) || !std::isfinite(c->qb_hi) || !(c->qb_lo < c->qb_hi))
+    return fail(MOE_ERR_INVALID_ARG, "the histogram range needs finite qb_lo < qb_hi (%g, %g)", (double)c->qb_lo,
+                (double)c->qb_hi);
+  if (!std::isfinite(qb_scale(c)))
+    return fail(MOE_ERR_INVALID_ARG, "qb_bins / (qb_hi - qb_lo) overflows fp32");
   if (c->E < 1 || c->E > 1024) return fail(MOE_ERR_SHAPE, "E must be in [1, 1024] (E=%d)", c->E);
   if (c->k < 1 || c->k > 32 || c->k > c->E) return fail(MOE_ERR_SHAPE, "k must be in [1, min(E, 32)] (k=%d)", c->k);
   if (c->qb_bins < 2 || c->qb_bins > 256) return fail(MOE_ERR_SHAPE, "qb_bins must be in [2, 256] (%d)", c->qb_bins);
@@ -76,11 +90,14 @@ Dims dims_of(const moe_config* c) {
   D.E = c->E;
   D.k = c->k;
   D.f = c->f;
-  D.f_s = c->f_s;
+  D.f_s = shared_hidden(c);
   D.B = c->qb_bins;
   D.bf16 = c->dtype == MOE_BF16;
   D.eps = c->rms_eps;
   D.routed_scale = c->routed_scale;
+  D.qb_lo = c->qb_lo;
+  D.qb_hi = c->qb_hi;
+  D.qb_scale = qb_scale(c);
   return D;
 }
 
@@ -132,7 +149,8 @@ void ws_layout(const moe_config* c, int64_t T, moe_ws_layout* L) {
   L->tile_info = take(T > 0 ? ((size_t)expert_max_mtiles((int)T, c->k, c->E) +
                                 (size_t)expert_max_mtiles((int)T, c->k, c->E, kExpertBM2)) * 8
                              : 0);  // both tile tables
-  L->G = take(t * c->f_s * es);
+  const size_t fs = (size_t)shared_hidden(c);
+  L->G = take(t * fs * es);
   L->z = take(t * c->l * es);
   L->X = take(0);  // no dispatch buffer: expert_up gathers z rows itself
   L->H = take(t * k * c->f * es);
@@ -145,8 +163,8 @@ void ws_layout(const moe_config* c, int64_t T, moe_ws_layout* L) {
   L->H8 = take(mx ? t * k * c->f : 0);
   L->Hs = take(mx ? t * k * c->f / 32 : 0);
   const bool keep = c->keep_preact != 0;
-  L->P = take(keep ? t * c->f_s * es : 0);
-  L->Q = take(keep ? t * c->f_s * es : 0);
+  L->P = take(keep ? t * fs * es : 0);
+  L->Q = take(keep ? t * fs * es : 0);
   L->A = take(keep ? t * k * c->f * es : 0);
   L->U = take(keep ? t * k * c->f * es : 0);
   L->total = o;
@@ -226,7 +244,11 @@ RoutePtrs route_ptrs(const moe_config& c, int64_t T, const moe_ws_layout& L, cha
   return p;
 }
 
-moe_status check_call(moe_ctx* ctx, int64_t T, void* ws, size_t ws_bytes) {
+// Checks of a call on T tokens with a workspace.  `accumulates`: the call
+// adds T tokens to the training statistics (a forward or routing pass in
+// training mode), so the window limit applies; the host counts the tokens of
+// the calls it sees (a replayed graph is checked by the update kernels).
+moe_status check_call(moe_ctx* ctx, int64_t T, void* ws, size_t ws_bytes, bool accumulates = true) {
   if (!ctx) return fail(MOE_ERR_INVALID_ARG, "context is NULL");
   if (T < 0 || T > ctx->cfg.max_tokens)
     return fail(MOE_ERR_SHAPE, "T=%lld outside [0, max_tokens=%lld]", (long long)T, (long long)ctx->cfg.max_tokens);
@@ -235,7 +257,7 @@ moe_status check_call(moe_ctx* ctx, int64_t T, void* ws, size_t ws_bytes) {
   if (!ws || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : (size_t)0, need);
   if (!aligned(ws, kAlign)) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (ctx->cfg.qb_mode == MOE_QB_TRAIN && ctx->pending_tokens + (uint64_t)T >= (uint64_t(1) << 32))
+  if (accumulates && ctx->cfg.qb_mode == MOE_QB_TRAIN && ctx->pending_tokens + (uint64_t)T >= (uint64_t(1) << 32))
     return fail(MOE_ERR_STATE, "more than 2^32-1 tokens accumulated without qb_update");
   return MOE_OK;
 }
@@ -272,7 +294,8 @@ constexpr int kSplitOut = 3, kSplitCat = 3;  // K slices of the two dense weight
 
 void bwd_layout(const moe_config* c, int64_t T, BwdLayout* L) {
   const size_t es = c->dtype == MOE_BF16 ? 2 : 4;
-  const size_t t = (size_t)T, E = (size_t)c->E, k = (size_t)c->k, d = c->d, l = c->l, f = c->f, fs = c->f_s;
+  const size_t t = (size_t)T, E = (size_t)c->E, k = (size_t)c->k, d = c->d, l = c->l, f = c->f,
+               fs = (size_t)shared_hidden(c);
   const size_t Tk = t * k;
   L->Tp = (int)((t + 63) / 64 * 64);
   L->Epad = (int)((E + 63) / 64 * 64);
@@ -372,8 +395,8 @@ moe_status moe_init(const moe_config* cfg, const moe_weights* w, void* state, vo
   if (!w || !out) return fail(MOE_ERR_INVALID_ARG, "weights or output pointer is NULL");
   if (!w->gamma || !w->W_r || !w->W_dn || !w->W_g || !w->W_u || !w->W_d || !w->W_up)
     return fail(MOE_ERR_INVALID_ARG, "a required weight pointer is NULL");
-  if (cfg->f_s > 0 && (!w->W_sg || !w->W_su || !w->W_sd))
-    return fail(MOE_ERR_INVALID_ARG, "shared-expert weights are NULL while f_s > 0");
+  if (shared_hidden(cfg) > 0 && (!w->W_sg || !w->W_su || !w->W_sd))
+    return fail(MOE_ERR_INVALID_ARG, "shared-expert weights are NULL while n_shared * f_s > 0");
   if (!state) return fail(MOE_ERR_INVALID_ARG, "state buffer is NULL");
   if (!aligned(state, kAlign)) return fail(MOE_ERR_INVALID_ARG, "state buffer must be 256-byte aligned");
   moe_ctx* c = new (std::nothrow) moe_ctx();
@@ -504,13 +527,14 @@ size_t moe_backward_workspace_bytes(const moe_config* cfg, int64_t T) {
 moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T, const moe_route_out* r,
                         const void* fwd_ws, size_t fwd_ws_bytes, void* dx, const moe_grads* g, void* ws,
                         size_t ws_bytes, void* stream) {
-  moe_status st = check_call(ctx, T, const_cast<void*>(fwd_ws), fwd_ws_bytes);
+  // a backward adds nothing to the training statistics
+  moe_status st = check_call(ctx, T, const_cast<void*>(fwd_ws), fwd_ws_bytes, /*accumulates=*/false);
   if (st != MOE_OK || T == 0) return st;
   if (!x || !dout || !dx || !g) return fail(MOE_ERR_INVALID_ARG, "x, dout, dx or grads is NULL");
   if (ctx->cfg.experts != MOE_EXPERTS_BF16) return fail(MOE_ERR_STATE, "the backward pass needs bf16 experts");
   const moe_config& c = ctx->cfg;
   if (!g->gamma || !g->W_r || !g->W_dn || !g->W_g || !g->W_u || !g->W_d || !g->W_up ||
-      (c.f_s > 0 && (!g->W_sg || !g->W_su || !g->W_sd)))
+      (shared_hidden(&c) > 0 && (!g->W_sg || !g->W_su || !g->W_sd)))
     return fail(MOE_ERR_INVALID_ARG, "a required gradient pointer is NULL");
   BwdLayout B;
   bwd_layout(&c, T, &B);
@@ -520,7 +544,7 @@ moe_status moe_backward(moe_ctx* ctx, const void* x, const void* dout, int64_t T
   if (!aligned(ws, kAlign)) return fail(MOE_ERR_WORKSPACE, "backward workspace must be 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Dims& D = ctx->D;
-  const int t = (int)T, E = c.E, k = c.k, d = c.d, l = c.l, f = c.f, fs = c.f_s;
+  const int t = (int)T, E = c.E, k = c.k, d = c.d, l = c.l, f = c.f, fs = shared_hidden(&c);
   const int es = c.dtype == MOE_BF16 ? 2 : 4;
   const int Tk = t * k, Tp = B.Tp, Kc = B.Kc, Epad = B.Epad;
   moe_ws_layout L;

@@ -243,7 +243,8 @@ MOE_DEV void topk_block(int chunk, uint32_t* mask, const float* __restrict__ log
 // (no other block of the launch writes them), so no reduction pass is needed
 // per forward; qb_update sums the slices.
 MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict__ logits, int T, int E, int B,
-                        int tps, uint32_t* __restrict__ hist, unsigned long long* __restrict__ count) {
+                        float lo, float scale, int tps, uint32_t* __restrict__ hist,
+                        unsigned long long* __restrict__ count) {
   constexpr int TR = kTopkThreads / kHistExperts;  // token rows in flight per step
   const int e0 = group * kHistExperts;
   const int ne = min(kHistExperts, E - e0);
@@ -260,10 +261,11 @@ MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict
     int t = tb + tl;
     for (; t + TR < te; t += 2 * TR) {
       const float l0 = logits[(size_t)t * E + e], l1 = logits[(size_t)(t + TR) * E + e];
-      atomicAdd(&row[score_bin(router_sigmoid(l0), B)], 1u);
-      atomicAdd(&row[score_bin(router_sigmoid(l1), B)], 1u);
+      atomicAdd(&row[score_bin(router_sigmoid(l0), B, lo, scale)], 1u);
+      atomicAdd(&row[score_bin(router_sigmoid(l1), B, lo, scale)], 1u);
     }
-    for (; t < te; t += TR) atomicAdd(&row[score_bin(router_sigmoid(logits[(size_t)t * E + e]), B)], 1u);
+    for (; t < te; t += TR)
+      atomicAdd(&row[score_bin(router_sigmoid(logits[(size_t)t * E + e]), B, lo, scale)], 1u);
   }
   __syncthreads();
   if (tb < T) {
@@ -284,7 +286,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
                                                        const float* __restrict__ bias, int T, int E, int k,
                                                        float scale, int32_t* __restrict__ idx,
                                                        float* __restrict__ gates, uint32_t* __restrict__ bitmap,
-                                                       int nchunks, int B, int tps, uint32_t* __restrict__ hist,
+                                                       int nchunks, int B, float lo, float bscale, int tps,
+                                                       uint32_t* __restrict__ hist,
                                                        unsigned long long* __restrict__ count) {
   __shared__ uint32_t smem[kHistExperts * 256];
   static_assert(kHistExperts * 256 >= 1024, "the top-k masks fit");
@@ -292,7 +295,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
     topk_block<CPL>(blockIdx.x, smem, logits, bias, T, E, k, scale, idx, gates, bitmap);
   } else {
     const int hb = blockIdx.x - nchunks, groups = (E + kHistExperts - 1) / kHistExperts;
-    hist_block(hb % groups, hb / groups, smem, logits, T, E, B, tps, hist, count);
+    hist_block(hb % groups, hb / groups, smem, logits, T, E, B, lo, bscale, tps, hist, count);
   }
 }
 
@@ -305,7 +308,7 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
   dim3 grid(nchunks + hblocks), block(kTopkThreads);
 #define MOE_TOPK(C)                                                                                                 \
   hipLaunchKernelGGL(k_topk<C>, grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, bitmap, \
-                     nchunks, D.B, tps, hist, count)
+                     nchunks, D.B, D.qb_lo, D.qb_scale, tps, hist, count)
   if (cpl <= 1) MOE_TOPK(1);
   else if (cpl <= 2) MOE_TOPK(2);
   else if (cpl <= 4) MOE_TOPK(4);
@@ -568,20 +571,32 @@ hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, cons
 }
 
 // ------------------------------------------------------------ QB update ----
+// Largest token count one statistics window may hold: each histogram bin (and
+// each sign-rule load) is a 32-bit counter that never exceeds the window's
+// token count.  The host refuses an eager call that would pass it
+// (MOE_ERR_STATE); replays of a captured graph are not seen by the host, so
+// the update kernels check the device's own 64-bit count as well: a window
+// past the limit leaves the bias unchanged, writes NaN to every q_e (QB) and
+// is cleared.
+constexpr unsigned long long kMaxWindowTokens = 0xFFFFFFFFull;
+
 // Per expert (one block each, one thread per bin): sum the bin over the
 // histogram slices and clear it; with A_j = tokens above bin j (a suffix sum:
 // wave shuffles, then the wave totals), the one bin with
 // A_j*E < N*k <= (A_j + c_j)*E (exact integer tests) holds the score the
-// expert must beat to receive N*k/E tokens; inside it the estimate is linear:
-// q = (j+1)/B - ((N*k - A_j*E) / (E*c_j)) / B, fp64.
+// expert must beat to receive N*k/E tokens; inside it the estimate is linear
+// in the bin, as a fraction of the histogram range [lo, hi]:
+// u = (j+1)/B - ((N*k - A_j*E) / (E*c_j)) / B and q = lo + (hi - lo) * u,
+// fp64 (q = u on [0, 1]).
 __global__ __launch_bounds__(256) void k_qb_quantile(uint32_t* __restrict__ hist,
                                                      const unsigned long long* __restrict__ count, int E, int B,
-                                                     int k, double* __restrict__ q) {
+                                                     int k, double lo, double width, double* __restrict__ q) {
 #pragma clang fp contract(off)
   __shared__ unsigned long long wtot[4];
   const unsigned long long N = *count;
   if (N == 0) return;
   const int e = blockIdx.x, j = threadIdx.x, lane = j & 63, w = j >> 6;
+  const bool overflow = N > kMaxWindowTokens;  // block-uniform
   unsigned long long c = 0;
   if (j < B) {
     uint32_t v[kHistSlices];
@@ -592,6 +607,10 @@ __global__ __launch_bounds__(256) void k_qb_quantile(uint32_t* __restrict__ hist
       c += v[sl];
       hist[((size_t)sl * E + e) * B + j] = 0u;
     }
+  }
+  if (overflow) {
+    if (j == 0) q[e] = __builtin_nan("");
+    return;
   }
   unsigned long long incl = c;  // inclusive suffix sum inside the wavefront
 #pragma unroll
@@ -607,20 +626,27 @@ __global__ __launch_bounds__(256) void k_qb_quantile(uint32_t* __restrict__ hist
     const unsigned long long target = N * (unsigned long long)k, EE = (unsigned long long)E;
     if (above * EE < target && target <= incl * EE) {
       const double frac = (double)(target - above * EE) / (double)(EE * c);
-      q[e] = (double)(j + 1) / (double)B - frac / (double)B;
+      q[e] = lo + width * ((double)(j + 1) / (double)B - frac / (double)B);
     }
   }
 }
 
 // b_e = fp32(mu - q_e), mu the fp64 mean of q summed in expert order (the q
 // are staged in LDS by all threads, the sum is one thread's); then the token
-// count is cleared.  Keeps the bias when no token was accumulated.
+// count is cleared.  Keeps the bias when no token was accumulated, or when
+// the window passed kMaxWindowTokens (then only the count is cleared).
 __global__ __launch_bounds__(1024) void k_qb_bias(const double* __restrict__ q, unsigned long long* __restrict__ count,
                                                   int E, float* __restrict__ bias) {
 #pragma clang fp contract(off)
   __shared__ double qs[1024];
   __shared__ double mu_s;
-  if (*count == 0) return;
+  const unsigned long long N = *count;
+  if (N == 0) return;
+  if (N > kMaxWindowTokens) {
+    __syncthreads();  // every thread has read the count before it is cleared
+    if (threadIdx.x == 0) *count = 0ull;
+    return;
+  }
   for (int e = threadIdx.x; e < E; e += 1024) qs[e] = q[e];
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -637,7 +663,8 @@ __global__ __launch_bounds__(1024) void k_qb_bias(const double* __restrict__ q, 
 
 hipError_t launch_qb_quantile(const Dims& D, uint32_t* hist, const unsigned long long* count, double* q,
                               hipStream_t s) {
-  hipLaunchKernelGGL(k_qb_quantile, dim3(D.E), dim3(256), 0, s, hist, count, D.E, D.B, D.k, q);
+  const double lo = (double)D.qb_lo, width = (double)D.qb_hi - (double)D.qb_lo;
+  hipLaunchKernelGGL(k_qb_quantile, dim3(D.E), dim3(256), 0, s, hist, count, D.E, D.B, D.k, lo, width, q);
   return hipGetLastError();
 }
 
@@ -656,6 +683,12 @@ __global__ __launch_bounds__(1024) void k_sign_bias(uint32_t* __restrict__ load,
                                                     int E, float gamma, float* __restrict__ bias) {
   __shared__ unsigned long long part[16];
   const int i = threadIdx.x, lane = i & 63, w = i >> 6;
+  if (*count > kMaxWindowTokens) {  // loads may have wrapped: keep the bias, clear the window
+    __syncthreads();
+    if (i < E) load[i] = 0u;
+    if (i == 0) *count = 0ull;
+    return;
+  }
   const uint32_t n = i < E ? load[i] : 0u;
   unsigned long long v = n;
 #pragma unroll

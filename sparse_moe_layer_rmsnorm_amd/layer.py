@@ -23,24 +23,39 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _sync(stream) -> None:
+    """Wait for the stream a call was enqueued on (torch stream, raw handle or None)."""
+    if stream is None:
+        torch.cuda.current_stream().synchronize()
+    elif hasattr(stream, "synchronize"):
+        stream.synchronize()
+    else:
+        torch.cuda.ExternalStream(int(stream)).synchronize()
+
+
 class MoeLayer:
     """One Stable LatentMoE layer on a GPU.
 
     ``weights`` maps the names of ``moe_weights`` to numpy arrays (or torch
     tensors) holding values of the storage dtype; ``logit_offset`` is the
-    optional per-expert router offset.
+    optional per-expert router offset.  ``f_s`` is the hidden width of each
+    of the ``n_shared`` shared experts, whose weights are stacked along the
+    hidden axis (W_sg, W_su [n_shared*f_s, d], W_sd [d, n_shared*f_s]).
     """
 
     def __init__(self, *, d: int, l: int, E: int, k: int, f: int, f_s: int, dtype: str, weights: Dict,
                  max_tokens: int, qb_bins: int = 256, rms_eps: float = 1e-6, frozen: bool = False,
                  routed_scale: float = 1.0, logit_offset=None, device: str = "cuda", stream=None,
-                 balancer: str = "qb", sign_gamma: float = 1e-2, experts: str = "bf16", keep_preact: bool = False):
+                 balancer: str = "qb", sign_gamma: float = 1e-2, experts: str = "bf16", keep_preact: bool = False,
+                 n_shared: int = 1, qb_lo: float = 0.0, qb_hi: float = 1.0):
         self.dtype = dtype
         self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.device = torch.device(device)
-        self.cfg = B.make_config(d, l, E, k, f, f_s, dtype=dtype, rms_eps=rms_eps, qb_bins=qb_bins, frozen=frozen,
-                                 max_tokens=max_tokens, routed_scale=routed_scale, balancer=balancer,
-                                 sign_gamma=sign_gamma, experts=experts, keep_preact=keep_preact)
+        self.cfg = B.make_config(d, l, E, k, f, f_s, n_shared=n_shared, dtype=dtype, rms_eps=rms_eps,
+                                 qb_bins=qb_bins, qb_lo=qb_lo, qb_hi=qb_hi, frozen=frozen, max_tokens=max_tokens,
+                                 routed_scale=routed_scale, balancer=balancer, sign_gamma=sign_gamma,
+                                 experts=experts, keep_preact=keep_preact)
+        f_s = n_shared * f_s                              # hidden width of the whole shared path
         self.dims = dict(d=d, l=l, E=E, k=k, f=f, f_s=f_s, B=qb_bins)
         self.w: Dict[str, torch.Tensor] = {}
         for name in _WEIGHT_NAMES:
@@ -180,9 +195,10 @@ class MoeLayer:
         return out
 
     def set_bias(self, b, stream=None) -> None:
-        t = self._dev(b, torch.float32)
+        t = self._dev(b, torch.float32)                  # written on the current stream
+        torch.cuda.current_stream().synchronize()         # ... and complete before another stream reads it
         B.moe_set_bias(self.ctx, t.data_ptr(), _stream(stream))
-        torch.cuda.current_stream().synchronize()
+        _sync(stream)                                     # the copy has read t before t is freed
 
     def set_qb_mode(self, frozen: bool) -> None:
         B.moe_set_qb_mode(self.ctx, B.MOE_QB_FROZEN if frozen else B.MOE_QB_TRAIN)
@@ -201,10 +217,14 @@ class MoeLayer:
 
 def layer_from_shape(shape, weights: Dict, *, max_tokens: Optional[int] = None, frozen: Optional[bool] = None,
                      logit_offset=None, device: str = "cuda", balancer: str = "qb",
-                     sign_gamma: float = 1e-2, experts: str = "bf16", keep_preact: bool = False) -> MoeLayer:
-    """MoeLayer for a workloads.LayerShape."""
-    return MoeLayer(d=shape.d, l=shape.l, E=shape.E, k=shape.k, f=shape.f, f_s=shape.f_s, dtype=shape.dtype,
+                     sign_gamma: float = 1e-2, experts: str = "bf16", keep_preact: bool = False,
+                     n_shared: int = 1, qb_lo: float = 0.0, qb_hi: float = 1.0) -> MoeLayer:
+    """MoeLayer for a workloads.LayerShape (shape.f_s: the whole shared hidden,
+    split over n_shared experts of shape.f_s / n_shared each)."""
+    assert shape.f_s % max(n_shared, 1) == 0
+    return MoeLayer(d=shape.d, l=shape.l, E=shape.E, k=shape.k, f=shape.f,
+                    f_s=shape.f_s // n_shared if n_shared > 0 else 0, n_shared=n_shared, dtype=shape.dtype,
                     weights=weights, max_tokens=max_tokens or shape.T, qb_bins=shape.B, rms_eps=shape.rms_eps,
                     frozen=shape.qb_frozen if frozen is None else frozen, logit_offset=logit_offset,
                     device=device, balancer=balancer, sign_gamma=sign_gamma, experts=experts,
-                    keep_preact=keep_preact)
+                    keep_preact=keep_preact, qb_lo=qb_lo, qb_hi=qb_hi)

@@ -61,3 +61,31 @@ def oracle_routing(logits: np.ndarray, bias: np.ndarray, k: int, E: int, B: int,
     counts, offsets, perm_src, inv = o.permutation(idx, E)
     return {"s": s, "idx": idx, "gates": g, "counts": counts, "offsets": offsets, "perm_src": perm_src,
             "inv": inv, "hist": o.histogram(s, B)}
+
+
+def compare_full(shape, W, x, lg, r_gpu, out_gpu, views, bias, *, experts="bf16", with_hist=False,
+                 out_tol=None, names=None):
+    """Whole-batch parity: the oracle's full forward with the GPU's logits
+    injected.  The GPU logits are checked against the oracle's own router
+    output on its own h (tolerance); routing is compared bit for bit; every
+    element of the stored intermediates (h, z, G, H, Y, y_lat) and of out is
+    compared within the layer tolerance.  Returns the oracle's forward and the
+    errors."""
+    T = x.shape[0]
+    ref = o.forward(x, W, np.asarray(bias, F32), k=shape.k, dtype=shape.dtype, eps=shape.rms_eps, B=shape.B,
+                    logits=lg, with_hist=with_hist, experts=experts)
+    errs = {"logits": rel_err(lg, o.router_logits(ref["h"], W["W_r"], W.get("c")))}
+    say(f"  logits rel err {errs['logits']:.3e}")
+    assert errs["logits"] <= LOGIT_TOL[shape.dtype]
+    assert_routing_equal(r_gpu, ref, T)
+    tol = OUT_TOL[shape.dtype]
+    if names is None:
+        names = ("h", "z") + (("G",) if shape.f_s else ()) + ("H", "Y", "y_lat")
+    for name in names:  # intermediates first: a failure names the first wrong step
+        errs[name] = rel_err(to_np(views[name]), ref[name])
+        say(f"  {name} rel err {errs[name]:.3e} ({ref[name].size} elements)")
+        assert errs[name] <= tol, name
+    errs["out"] = rel_err(to_np(out_gpu), ref["out"])
+    say(f"  out rel err {errs['out']:.3e} ({ref['out'].size} elements)")
+    assert errs["out"] <= (tol if out_tol is None else out_tol)
+    return ref, errs

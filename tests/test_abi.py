@@ -62,6 +62,10 @@ def test_sizes_and_layouts():
     ("qb_mode", 5, B.MOE_ERR_INVALID_ARG), ("rms_eps", 0.0, B.MOE_ERR_INVALID_ARG),
     ("max_tokens", 0, B.MOE_ERR_SHAPE), ("max_tokens", 2 ** 30, B.MOE_ERR_SHAPE),
     ("balancer", 2, B.MOE_ERR_INVALID_ARG), ("balancer", -1, B.MOE_ERR_INVALID_ARG),
+    ("n_shared", -1, B.MOE_ERR_SHAPE), ("n_shared", 1024, B.MOE_ERR_SHAPE),
+    ("qb_lo", 1.0, B.MOE_ERR_INVALID_ARG), ("qb_lo", 2.0, B.MOE_ERR_INVALID_ARG),
+    ("qb_hi", float("inf"), B.MOE_ERR_INVALID_ARG), ("qb_lo", float("nan"), B.MOE_ERR_INVALID_ARG),
+    ("qb_hi", 1e-42, B.MOE_ERR_INVALID_ARG),
 ])
 def test_bad_config_rejected_before_any_device_call(L, field, value, status):
     cfg = B.make_config(**REPLICA, max_tokens=64)
@@ -133,6 +137,24 @@ def test_keep_preact_config_and_workspaces(L):
         cfg.keep_preact = bad["keep_preact"]
         assert B.moe_state_bytes(cfg) == 0
     assert B.moe_state_bytes(B.make_config(**REPLICA, max_tokens=T, keep_preact=True, experts="mxfp8")) == 0
+
+
+def test_shared_experts_and_histogram_range_fields():
+    """n_shared shared experts of hidden f_s are one GLU of hidden
+    n_shared*f_s (the workspace's shared hidden grows with it; n_shared = 0 or
+    f_s = 0 means no shared path); the QB score range is any finite
+    qb_lo < qb_hi whose bins per unit of score fit fp32."""
+    T = 1000
+    ws1 = B.moe_workspace_layout(B.make_config(**REPLICA, max_tokens=T), T)
+    ws3 = B.moe_workspace_layout(B.make_config(**REPLICA, max_tokens=T, n_shared=3), T)
+    ws0 = B.moe_workspace_layout(B.make_config(**REPLICA, max_tokens=T, n_shared=0), T)
+    assert ws1.z - ws1.G >= T * 2048 * 2 and ws3.z - ws3.G >= T * 3 * 2048 * 2 and ws0.z - ws0.G == 0
+    args = dict(REPLICA, f_s=0)
+    assert B.moe_workspace_layout(B.make_config(**args, max_tokens=T, n_shared=4), T).z == \
+        B.moe_workspace_layout(B.make_config(**args, max_tokens=T, n_shared=0), T).z
+    for lo, hi in ((0.0, 1.0), (0.25, 0.75), (-3.0, 3.0), (0.5, 0.5000001)):
+        assert B.moe_state_bytes(B.make_config(**REPLICA, max_tokens=T, qb_lo=lo, qb_hi=hi)) > 0
+    assert B.moe_state_bytes(B.make_config(**REPLICA, max_tokens=T, qb_lo=0.5, qb_hi=0.5)) == 0
 
 
 def test_null_arguments_rejected(L):

@@ -11,7 +11,8 @@ import torch
 from oracle import moe_oracle as o
 from sparse_moe_layer_rmsnorm_amd import workloads as wl
 
-from gpu_util import (LOGIT_TOL, OUT_TOL, assert_routing_equal, make_layer, rel_err, say, to_np, x_on_gpu)
+from gpu_util import (LOGIT_TOL, OUT_TOL, assert_routing_equal, compare_full, make_layer, rel_err, say, to_np,
+                      x_on_gpu)
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32
@@ -90,10 +91,12 @@ def test_replica_shape_ragged():
     _run(shape, 1000, bias=(np.random.default_rng(5).standard_normal(shape.E) * 0.02).astype(F32))
 
 
-def test_replica_full_size_sampled():
+def test_replica_full_size_all_elements():
     """The replica workload at full size (T=8192), as the benchmark runs it:
-    logits by tolerance, routing bit-exact from the GPU logits, outputs on
-    sampled tokens through the oracle's per-token path."""
+    the oracle's whole forward with the GPU logits injected; routing and the
+    QB histogram bit-exact; every element of h, z, G, H, Y, y_lat and out
+    compared (64 m-tiles x 36 n-tiles of the h GEMM: the persistent blocks'
+    cross-tile DMA ring and tile switches are all in play)."""
     shape = wl.workload("replica")
     T = shape.T
     say(f"replica full T={T}")
@@ -101,21 +104,24 @@ def test_replica_full_size_sampled():
     x = wl.make_x(shape)
     layer = make_layer(shape, W, max_tokens=T)
     r = layer.route_buffers(T)
-    out = to_np(layer.forward(x_on_gpu(x, layer), route=r))
+    out = layer.forward(x_on_gpu(x, layer), route=r)
     torch.cuda.synchronize()
-    lg = to_np(r["logits"])
-    pick = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(0).integers(0, T, 61)]))
-    h = o.bf16_round(o.rmsnorm(x[pick], W["gamma"], shape.rms_eps))
-    assert rel_err(lg[pick], o.router_logits(h, W["W_r"])) <= LOGIT_TOL["bf16"]
-    from gpu_util import oracle_routing
-    ref = oracle_routing(lg, np.zeros(shape.E, F32), shape.k, shape.E, shape.B)
-    assert_routing_equal(r, ref, T)
+    ref, _ = compare_full(shape, W, x, to_np(r["logits"]), r, out, layer.ws_views(T), np.zeros(shape.E, F32),
+                          with_hist=True)
     np.testing.assert_array_equal(to_np(layer.state_views()["hist"]), ref["hist"])
-    want = o.forward_tokens(x[pick], W, ref["idx"][pick], ref["gates"][pick], dtype="bf16", eps=shape.rms_eps)
-    err = rel_err(out[pick], want)
-    say(f"  sampled out rel err {err:.3e}")
-    assert err <= OUT_TOL["bf16"]
     layer.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_tall_expert_tiles(dtype):
+    """T*k/E = 1024 rows per expert (>= 512): expert_up takes the 128-row
+    tile table and pipeline (the path of the load-skew and decode-like
+    workloads); every element of z, G, H, Y, y_lat and out compared.  With
+    f_s = 1024 the h GEMM has 32 x 18 tiles, more than its 512 block slots, so
+    the fp32 persistent loop crosses tiles as well."""
+    say(f"forward tall expert tiles {dtype}")
+    shape = wl.LayerShape("tall", 15, dtype, T=1, d=256, l=128, E=8, k=2, f=256, f_s=1024)
+    _run(shape, 4096, bias=(np.random.default_rng(15).standard_normal(8) * 0.02).astype(F32))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -176,4 +182,22 @@ def test_route_from_x_odd_shape(dtype):
     assert rel_err(lg, ref_own["logits"]) <= LOGIT_TOL[dtype]
     ref = o.forward(x, W, np.zeros(96, F32), k=shape.k, dtype=dtype, eps=shape.rms_eps, B=shape.B, logits=lg)
     assert_routing_equal(r, ref, T)
+    layer.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_two_shared_experts(dtype):
+    """n_shared = 2 shared experts of hidden 64 each, their weights stacked
+    along the hidden axis: the layer equals the oracle's single shared GLU of
+    hidden 128 (the stacking identity is pinned on the CPU)."""
+    say(f"forward two shared experts {dtype}")
+    shape = _small(dtype, f_s=128)
+    T = 150
+    W = wl.make_weights(shape)
+    x = wl.make_x(shape.with_tokens(T))
+    layer = make_layer(shape, W, max_tokens=T, n_shared=2)
+    r = layer.route_buffers(T)
+    out = layer.forward(x_on_gpu(x, layer), route=r)
+    torch.cuda.synchronize()
+    compare_full(shape, W, x, to_np(r["logits"]), r, out, layer.ws_views(T), np.zeros(shape.E, F32))
     layer.close()

@@ -124,3 +124,64 @@ def test_qb_frozen_and_empty():
     assert int(st["count"].item()) == 0 and int(st["hist"].abs().sum().item()) == 0
     np.testing.assert_array_equal(to_np(layer.get_bias()), b0)
     layer.close()
+
+
+@pytest.mark.parametrize("lo,hi,B", [(0.25, 0.75, 256), (0.3, 0.9, 100), (-1.0, 2.0, 7)])
+def test_qb_histogram_over_a_score_range(lo, hi, B):
+    """The histogram over [qb_lo, qb_hi] (scores beyond it in the end bins)
+    and the quantile mapped back onto that range: bit-exact with the oracle."""
+    say(f"qb range [{lo}, {hi}] B={B}")
+    E, k, T = 40, 4, 3000
+    rng = np.random.default_rng(B)
+    shape = _shape(E, k, B=B)
+    layer = make_layer(shape, wl.make_weights(shape), max_tokens=T, qb_lo=lo, qb_hi=hi)
+    logits = (rng.standard_normal((T, E)) * 0.6 + rng.standard_normal(E)[None, :] * 0.3).astype(F32)
+    r = layer.route(T, logits=torch.from_numpy(logits).cuda())
+    torch.cuda.synchronize()
+    ref = oracle_routing(logits, np.zeros(E, F32), k, E, B)
+    assert_routing_equal(r, ref, T)
+    want = o.histogram(ref["s"], B, lo, hi)
+    np.testing.assert_array_equal(to_np(layer.state_views()["hist"]), want)
+    layer.qb_update()
+    torch.cuda.synchronize()
+    b = o.qb_update(want, T, k, np.zeros(E, F32), lo, hi)
+    np.testing.assert_array_equal(to_np(layer.get_bias()).view(np.uint32), b.view(np.uint32))
+    layer.close()
+
+
+@pytest.mark.parametrize("balancer", ["qb", "sign"])
+def test_window_overflow_guard_on_the_device(balancer):
+    """A statistics window past 2^32 - 1 tokens that the host did not see (as
+    under graph replay, emulated by writing the device count directly): the
+    update keeps the bias, marks every q_e NaN (QB) and clears the window."""
+    say(f"window overflow guard ({balancer})")
+    E, k, T = 32, 4, 256
+    shape = _shape(E, k)
+    layer = make_layer(shape, wl.make_weights(shape), max_tokens=T, balancer=balancer)
+    b0 = (np.random.default_rng(2).standard_normal(E) * 0.1).astype(F32)
+    layer.set_bias(b0)
+    st = layer.state_views()
+    st["count"].fill_(2 ** 32 - 100)                # tokens the host mirror never counted
+    logits = np.random.default_rng(4).standard_normal((T, E)).astype(F32)
+    layer.route(T, logits=torch.from_numpy(logits).cuda())
+    torch.cuda.synchronize()
+    assert int(st["count"].item()) == 2 ** 32 - 100 + T
+    layer.qb_update()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(layer.get_bias()).view(np.uint32), b0.view(np.uint32))
+    assert int(st["count"].item()) == 0
+    assert int(st["hist_slices"].abs().sum().item()) == 0 and int(st["load"].abs().sum().item()) == 0
+    if balancer == "qb":
+        assert np.all(np.isnan(to_np(st["q"])))
+    # the next window starts clean: an ordinary update works again
+    r = layer.route(T, logits=torch.from_numpy(logits).cuda())
+    layer.qb_update()
+    torch.cuda.synchronize()
+    ref = oracle_routing(logits, b0, k, E, shape.B)
+    assert_routing_equal(r, ref, T)
+    if balancer == "qb":
+        want = o.qb_update(ref["hist"], T, k, b0)
+    else:
+        want = o.sign_update(ref["counts"], b0, 1e-2)
+    np.testing.assert_array_equal(to_np(layer.get_bias()).view(np.uint32), want.view(np.uint32))
+    layer.close()

@@ -32,8 +32,11 @@ def _setup(shape, seed=0, bias_scale=0.1):
     return W, x, bias, dout
 
 
-def _torch_grads(shape, W, x, idx, dout, eps, rs=1.0):
-    """Gradients of sum(out * dout) by torch.autograd (fp64), dense form."""
+def _torch_grads(shape, W, x, idx, dout, eps, rs=1.0, gates=None):
+    """Gradients of sum(out * dout) by torch.autograd (fp64), dense form;
+    res["out"] is torch's forward output.  ``gates`` (fp32 [T,k]) replaces
+    the gates computed from torch's sigmoid (the forward check then isolates
+    the assembly of the output from the score function)."""
     t = {n: torch.tensor(np.asarray(v, np.float64), requires_grad=True) for n, v in W.items() if v is not None}
     xt = torch.tensor(np.asarray(x, np.float64), requires_grad=True)
     it = torch.tensor(idx.astype(np.int64))
@@ -43,6 +46,8 @@ def _torch_grads(shape, W, x, idx, dout, eps, rs=1.0):
     s = torch.sigmoid(lg)
     s_sel = s.gather(1, it)
     g = rs * s_sel / s_sel.sum(1, keepdim=True)
+    if gates is not None:
+        g = torch.tensor(np.asarray(gates, np.float64))
     z = h @ t["W_dn"].T
     y_lat = torch.zeros(shape.T, shape.l, dtype=torch.float64)
     for j in range(shape.k):
@@ -59,6 +64,7 @@ def _torch_grads(shape, W, x, idx, dout, eps, rs=1.0):
     (out * torch.tensor(np.asarray(dout, np.float64))).sum().backward()
     res = {n: v.grad.numpy() for n, v in t.items() if v.grad is not None}
     res["x"] = xt.grad.numpy()
+    res["out"] = out.detach().numpy()
     return res
 
 
@@ -83,12 +89,37 @@ def test_backward_matches_autograd(dims):
     fwd = o.forward(x, W, bias, k=k, dtype="f32", eps=shape.rms_eps)
     got = o.backward(x, W, dout, fwd, dtype="f32", eps=shape.rms_eps)
     want = _torch_grads(shape, W, x, fwd["idx"], dout, shape.rms_eps)
+    # the forward output itself: torch's dense formulation (its own sigmoid,
+    # SiLU and per-token expert evaluation, no permutation) against the
+    # oracle's dispatch path in f32 mode (nothing rounded)
+    assert _rel(fwd["out"], want["out"]) < 1e-6
     for n in NAMES:
         if n in ("W_sg", "W_su", "W_sd") and f_s == 0:
             continue
         # the oracle's scores come from the fp32-specified sigmoid, torch's from
         # its fp64 one: agreement to ~1e-7 relative, far below any dropped term
         assert _rel(got[n], want[n]) < 1e-5, n
+
+
+@pytest.mark.parametrize("dims", [
+    (64, 64, 32, 8, 2, 32, 64),      # T, d, l, E, k, f, f_s
+    (37, 64, 64, 5, 3, 64, 0),       # no shared expert, ragged T
+    (50, 32, 16, 16, 16, 16, 32),    # k = E
+    (96, 128, 64, 1, 1, 64, 0),      # E = k = 1: a dense GLU at width l
+])
+def test_forward_output_matches_torch(dims):
+    """out = shared GLU + up-projection of the gate-weighted combine, with
+    the oracle's own gates fed to torch: the two fp64 evaluations (dispatch
+    through the permutation against every token's experts in place) agree
+    to rounding, 1e-12 relative, which a dropped term, a wrong gate or a
+    transposed weight would break by many orders of magnitude."""
+    T, d, l, E, k, f, f_s = dims
+    shape = _shape(T, d, l, E, k, f, f_s)
+    W, x, bias, dout = _setup(shape, seed=T + 1)
+    fwd = o.forward(x, W, bias, k=k, dtype="f32", eps=shape.rms_eps)
+    want = _torch_grads(shape, W, x, fwd["idx"], dout, shape.rms_eps, gates=fwd["gates"])
+    assert _rel(fwd["out"], want["out"]) < 1e-12
+    assert _rel(fwd["y_r"] + fwd["sh"], want["out"]) < 1e-12
 
 
 def test_backward_routed_scale_matches_autograd():

@@ -121,3 +121,20 @@ def test_replica_parameter_count():
     t = wl.workload("tiny")
     assert sum(v.size for v in W.values()) == (t.d + t.E * t.d + 3 * t.d * t.f_s + 2 * t.d * t.l
                                                + 3 * t.E * t.f * t.l)
+
+
+def test_shared_experts_stack_into_one_glu():
+    """n shared experts of hidden f_s, each evaluated on its own and summed,
+    equal the oracle's one shared GLU over the weights stacked along the
+    hidden axis (the layout the library takes for n_shared > 1)."""
+    s = _small(f_s=96)
+    W = wl.make_weights(s)
+    x = wl.make_x(s)
+    r = o.forward(x, W, np.zeros(s.E, F32), k=s.k, dtype="f32")
+    h = r["h"]
+    parts = 0.0
+    for i in range(3):                                   # three experts of hidden 32
+        rows = slice(32 * i, 32 * (i + 1))
+        Gi = o.silu(h @ W["W_sg"][rows].astype(np.float64).T) * (h @ W["W_su"][rows].astype(np.float64).T)
+        parts = parts + Gi @ W["W_sd"][:, rows].astype(np.float64).T
+    np.testing.assert_allclose(r["sh"], parts, rtol=1e-12, atol=1e-12)

@@ -28,6 +28,49 @@ def test_histogram_matches_numpy_histogram(B):
     assert h.sum() == s.size
 
 
+@pytest.mark.parametrize("lo,hi,B", [(0.25, 0.75, 256), (0.125, 0.625, 64), (0.0, 0.5, 8)])
+def test_histogram_over_a_score_range_matches_numpy(lo, hi, B):
+    """Bins over [lo, hi]: numpy's histogram of the scores clipped to the
+    range (what lies beyond counts in the end bins).  These ranges keep
+    s - lo and its product with B / (hi - lo) exact in fp32, so numpy's fp64
+    bin edges and the fp32 rule agree bin for bin."""
+    rng = np.random.default_rng(B + 7)
+    s = o.sigmoid_r((rng.standard_normal((4000, 9)) * 2).astype(F32))
+    s[:4] = F32(lo)
+    s[4:8] = F32(hi)
+    h = o.histogram(s, B, lo, hi)
+    for e in range(9):
+        clipped = np.clip(s[:, e].astype(np.float64), lo, hi)
+        want, _ = np.histogram(clipped, bins=B, range=(lo, hi))
+        np.testing.assert_array_equal(h[e], want)
+    np.testing.assert_array_equal(o.histogram(s, B, 0.0, 1.0), o.histogram(s, B))
+
+
+@pytest.mark.parametrize("lo,hi,B", [(0.5, 0.75, 256), (0.3, 0.9, 100), (0.0, 1.0, 256)])
+def test_qb_quantile_over_a_range_within_one_bin(lo, hi, B):
+    """With the target quantile inside [lo, hi], the estimate is within one
+    bin width (hi - lo) / B of the sort-based exact quantile; a narrower
+    range has narrower bins, so a tighter bound."""
+    T, E, k = 3000, 40, 4
+    rng = np.random.default_rng(int(hi * 100) + B)
+    s = o.sigmoid_r((0.4 * rng.standard_normal((T, E))).astype(F32))
+    exact = np.array([o.exact_quantile(s[:, e], T, k, E) for e in range(E)])
+    assert np.all((exact > lo) & (exact < hi))
+    q = o.qb_quantiles(o.histogram(s, B, lo, hi), T, k, lo, hi)
+    assert np.max(np.abs(q - exact)) <= (hi - lo) / B * (1 + 1e-6)
+    b = o.qb_update(o.histogram(s, B, lo, hi), T, k, np.zeros(E, F32), lo, hi)
+    assert abs(b.astype(np.float64).sum()) <= E * 2.0 ** -24 * np.abs(b).max()
+
+
+def test_qb_default_range_is_unit_interval_bit_for_bit():
+    rng = np.random.default_rng(3)
+    s = o.sigmoid_r(rng.standard_normal((500, 16)).astype(F32))
+    h = o.histogram(s, 256)
+    np.testing.assert_array_equal(o.qb_quantiles(h, 500, 2, 0.0, 1.0).view(np.uint64),
+                                  o.qb_quantiles(h, 500, 2).view(np.uint64))
+    assert o.bin_scale(256) == F32(256.0)
+
+
 def test_qb_worked_example():
     g = json.load(open(os.path.join(GOLDEN, "qb_worked_example.json")))
     s = np.array(g["scores"], F32)
