@@ -36,11 +36,16 @@ METRIC_BWD = "MoE-layer fwd+bwd tokens/sec on 1 MI355X (training step: forward, 
 
 
 def kernel_work(s, T: int) -> dict:
-    """Algorithmic work per launch: FLOPs of the GEMMs, bytes of the
-    memory-bound kernels (each operand read once, each result written once)."""
+    """Algorithmic work per launch: FLOPs of the GEMMs, and bytes of the
+    memory-bound kernels counted as the layer's own data (each operand read
+    once, each result written once), not as the buffers an implementation
+    chooses to keep.  Routing bytes follow the per-token figures of the
+    routing, permutation and combine steps (scores and top-k read the fp32
+    logits and write indices and gates, 4E + 8k per token, plus the E x B
+    histogram once; counts, offsets and the stable permutation 16k per token;
+    combine 2kl + 8k + 2l per token in bf16)."""
     es = 2 if s.dtype == "bf16" else 4
     Tk = T * s.k
-    nchunks = (T + 31) // 32
     flops = {
         "gemm_h": 2.0 * T * s.d * (s.E + 2 * s.f_s + s.l),
         "gemm_rz": 2.0 * T * s.d * s.E,
@@ -50,20 +55,54 @@ def kernel_work(s, T: int) -> dict:
     }
     bytes_ = {
         "rmsnorm": 2.0 * T * s.d * es + 4 * s.d,
-        # scores, top-k, gates, masks; in training the same launch also adds
-        # the score histogram into its 16 token slices (read + write)
-        "topk": 4.0 * T * s.E + 8.0 * Tk + 4.0 * nchunks * s.E + 4 * s.E + 8.0 * 16 * s.E * s.B,
-        "scan": 12.0 * nchunks * s.E + 16.0 * s.E,
-        # stable rows and inverse rows (the dispatch copy is in expert_up's operand load)
-        "scatter": 4.0 * Tk + 8.0 * Tk + 8.0 * nchunks * s.E,
+        "topk": 4.0 * T * s.E + 8.0 * Tk + 4.0 * s.E * s.B,
+        # count + prefix sum + stable scatter: 16 bytes per (token, slot) in all
+        "scan": 4.0 * Tk,
+        "scatter": 12.0 * Tk,
         "combine": 1.0 * Tk * s.l * es + 8.0 * Tk + 1.0 * T * s.l * es,
-        "qb_quantile": 8.0 * 16 * s.E * s.B,
+        "qb_quantile": 4.0 * s.E * s.B + 8.0 * s.E,
         "qb_bias": 20.0 * s.E,
         # MXFP8 quantisation of z and H (one launch each): read bf16, write bytes + scales
         "mx_quant": 0.5 * (2.0 + 1.0 + 1.0 / 32) * (T * s.l + Tk * s.f),
         "sign_bias": 16.0 * s.E,
     }
-    return {"flops": flops, "bytes": bytes_}
+    # bytes the implementation moves beyond those: the histogram kept as 16
+    # token slices (read-modify-write by the training forward, read and
+    # cleared by the update), the per-chunk selection masks
+    nchunks = (T + 31) // 32
+    impl_extra = {
+        "topk": 8.0 * 16 * s.E * s.B + 4.0 * nchunks * s.E,
+        "scan": 12.0 * nchunks * s.E,
+        "scatter": 8.0 * nchunks * s.E,
+        "qb_quantile": 8.0 * 16 * s.E * s.B - 4.0 * s.E * s.B,
+    }
+    return {"flops": flops, "bytes": bytes_, "impl_extra": impl_extra}
+
+
+def gemm_groups(s, T: int) -> dict:
+    """FLOPs and minimum HBM bytes of each GEMM group (weights, inputs and
+    outputs once): the h GEMM, the routed experts (with the expert hidden H
+    kept on chip: weights, dispatched rows in, expert rows out) and the output
+    GEMM."""
+    es = 2 if s.dtype == "bf16" else 4
+    Tk = T * s.k
+    return {
+        "gemm_h": (2.0 * T * s.d * (s.E + 2 * s.f_s + s.l),
+                   es * (T * s.d + s.d * (s.E + 2 * s.f_s + s.l) + T * (s.f_s + s.l)) + 4.0 * T * s.E),
+        "experts": (2.0 * Tk * s.l * 3 * s.f, es * (3.0 * s.E * s.f * s.l + 2.0 * Tk * s.l)),
+        "gemm_out": (2.0 * T * s.d * (s.f_s + s.l), es * (T * (s.f_s + s.l) + s.d * (s.f_s + s.l) + T * s.d)),
+    }
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def backward_flops(s, T: int, keep: bool = False) -> dict:
@@ -116,7 +155,8 @@ def cpu_baseline(shape, W, x, seconds: float = 12.0) -> dict:
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 50:
             break
-    res = {"value": reps * Ts / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    res = {"value": reps * Ts / el, "unit": "tokens/s", "cores": int(cores), "cpu_model": host_cpu_model(),
+           "kind": "oracle",
            "sample": f"{reps} x full training forward + QB update of the first {Ts} tokens of the {shape.name} "
                      f"workload (numpy fp64, {el:.1f} s)"}
     # the same sample on one host thread, about a third of the time budget
@@ -159,6 +199,31 @@ def cold_forward(layer, x, out, stream, n: int) -> dict:
             "forwards": n, "flush": "512 MB device write before each forward"}
 
 
+def balance_record(layer, shape, steps: int) -> list:
+    """Per-step expert load balance of a training loop (fresh x each step,
+    the bias of each step set by the previous step's update): max/min and
+    max/mean of the tokens per expert and the number of experts with none.
+    Runs outside the timed region; the layer's bias and statistics are
+    restored afterwards."""
+    import torch
+    from sparse_moe_layer_rmsnorm_amd import workloads as wl
+    bias0 = layer.get_bias().clone()
+    T = shape.T
+    r = layer.route_buffers(T)
+    out = torch.empty(T, shape.d, dtype=layer.tdtype, device="cuda")
+    rows = []
+    for step in range(steps):
+        x = torch.from_numpy(wl.make_x(shape, step)).cuda().to(layer.tdtype)
+        layer.forward(x, out=out, route=r)
+        layer.qb_update()
+        n = r["counts"].double()
+        rows.append({"step": step, "max_over_min": round(float(n.max() / n.min()), 3) if n.min() > 0 else None,
+                     "max_over_mean": round(float(n.max() / n.mean()), 3), "dead": int((n == 0).sum())})
+    layer.set_bias(bias0)
+    torch.cuda.synchronize()
+    return rows
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +250,9 @@ def main() -> int:
                          "instead of recomputing them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain device copy of 256 MiB (the reference for HBM byte counters)")
+    ap.add_argument("--balance-steps", type=int, default=None,
+                    help="training steps of the per-step load-balance record (default: 20 for the load-skew "
+                         "workload, 3 for the other training workloads)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the layer is built and measured per GPU); --gpus {args.gpus} "
@@ -304,11 +372,29 @@ def main() -> int:
                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom,
                     "avg_us": round(dom_us, 3), "algorithmic": f"{work['bytes'][dom]:.6g} bytes per launch"}
     # expert GEMMs together, and routing + permutation + combine together
-    ex_us = sum(kernels[n]["avg_us"] for n in ("expert_up", "expert_down") if n in kernels)
+    ex_names = [n for n in ("expert_up", "expert_down", "expert_fused") if n in kernels]
+    ex_us = sum(kernels[n]["avg_us"] for n in ex_names)
     ex_tf = (work["flops"]["expert_up"] + work["flops"]["expert_down"]) / (ex_us * 1e-6) / 1e12
     rt_names = [n for n in ("topk", "scan", "scatter", "combine") if n in kernels]
     rt_us = sum(kernels[n]["avg_us"] for n in rt_names)
     rt_bytes = sum(work["bytes"].get(n, 0.0) for n in rt_names)
+    rt_impl = sum(work["impl_extra"].get(n, 0.0) for n in rt_names)
+    # each GEMM group against the roof that applies to it: the larger of its
+    # time at the MFMA peak and its time at the HBM peak, over its time
+    groups = gemm_groups(shape, T)
+    group_us = {"gemm_h": kernels.get("gemm_h", {}).get("avg_us"), "experts": ex_us or None,
+                "gemm_out": kernels.get("gemm_out", {}).get("avg_us")}
+    roofs = {}
+    for g, (fl, by) in groups.items():
+        us = group_us[g]
+        if not us:
+            continue
+        t_mm, t_hbm = fl / (peak_mm * 1e12), by / (PEAK_HBM_GBS * 1e9)
+        roofs[g] = {"us": round(us, 3), "gflop": round(fl / 1e9, 2), "min_mbytes": round(by / 1e6, 1),
+                    "bound": "mfma" if t_mm >= t_hbm else "hbm",
+                    "roof_us": round(max(t_mm, t_hbm) * 1e6, 2),
+                    "frac_of_roof": round(max(t_mm, t_hbm) / (us * 1e-6), 4),
+                    "mfma_frac": round(fl / (us * 1e-6) / 1e12 / peak_mm, 4)}
     # GEMM FLOPs of one step: the launched forward GEMMs (plus the backward's)
     layer_flops = sum(work["flops"][n] * kernels[n]["launches"] / args.steps for n in kernels if n in work["flops"])
     if args.backward:
@@ -354,15 +440,23 @@ def main() -> int:
         "roofline": roofline,
         "layer_mfma_frac": round(layer_flops / (ms_step * 1e-3) / 1e12 / peak_mm, 4),
         "expert_gemm": {"tflops": round(ex_tf, 1), "mfma_frac": round(ex_tf / peak_mm, 4)},
+        "gemm_roofs": roofs,
         "routing_permute_combine": {"gbs": round(rt_bytes / (rt_us * 1e-6) / 1e9, 1),
                                     "hbm_frac": round(rt_bytes / (rt_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                                    "us": round(rt_us, 2)},
+                                    "us": round(rt_us, 2), "kernels": rt_names,
+                                    "algorithmic_mbytes": round(rt_bytes / 1e6, 2),
+                                    "implementation_extra_mbytes": round(rt_impl / 1e6, 2)},
         "kernels": kernels,
     }
     if cold is not None:
         res["cold_mall"] = cold
     if bwd is not None:
         res["backward"] = bwd
+    nbal = args.balance_steps if args.balance_steps is not None else (20 if shape.name == "skew" else 3)
+    if not frozen and not args.backward and nbal > 0:
+        res["balance"] = {"steps": balance_record(layer, shape, nbal),
+                          "note": "fresh x per step (seeded by step), each step's bias from the previous step's "
+                                  "update; tokens per expert"}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(shape, dict(W, c=c) if c is not None else W, x_np, args.cpu_seconds)
     layer.close()
