@@ -264,6 +264,26 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
                        size_t ws_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation): moe_forward with the workspace
+ * taken from a fixed array of MOE_NOALLOC_SCRATCH_BYTES (160 MiB: one
+ * forward of the replica-shaped layer, d=1024, l=256, E=256, k=6, f=512,
+ * f_s=2048, at 8192 tokens) that the library holds on each GPU it runs on
+ * until the process ends.  Same arguments and results as moe_forward; the
+ * caller still provides x, out and (optionally) r.  A T whose
+ * moe_workspace_bytes(cfg, T) exceeds MOE_NOALLOC_SCRATCH_BYTES returns
+ * MOE_ERR_WORKSPACE before anything is enqueued.  The call allocates
+ * nothing; the array's device address is looked up by moe_init (and on the
+ * first call on any other device).  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (different streams, threads or
+ * contexts without ordering between them) race, so order them.  The array
+ * keeps the last call's intermediates; nothing a call reads from it has to
+ * start at zero.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)160 << 20)
+moe_status moe_forward_noalloc(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_route_out* r, void* stream);
+
+/*
  * Bias update from the statistics accumulated since the last update, then
  * those statistics and the token count are cleared; the new bias is used by
  * the next forward.  MOE_BALANCE_QB: from the histogram, b_e = mean(q) - q_e;

@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
                                   c_void_p]),
             "moe_forward": (c_int, [c_void_p, c_void_p, c_int64, c_void_p, POINTER(moe_route_out), c_void_p,
                                     c_size_t, c_void_p]),
+            "moe_forward_noalloc": (c_int, [c_void_p, c_void_p, c_int64, c_void_p, POINTER(moe_route_out),
+                                            c_void_p]),
             "moe_backward_workspace_bytes": (c_size_t, [cfgp, c_int64]),
             "moe_backward": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, POINTER(moe_route_out), c_void_p,
                                      c_size_t, c_void_p, POINTER(moe_grads), c_void_p, c_size_t, c_void_p]),
@@ -165,6 +167,14 @@ def moe_forward(ctx: int, x: int, T: int, out: int, r: Optional[moe_route_out], 
                 stream: int) -> None:
     check(lib().moe_forward(ctx, x, T, out, ctypes.byref(r) if r is not None else None, ws, ws_bytes, stream),
           "moe_forward")
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 160 << 20
+
+
+def moe_forward_noalloc(ctx: int, x: int, T: int, out: int, r: Optional[moe_route_out], stream: int) -> None:
+    check(lib().moe_forward_noalloc(ctx, x, T, out, ctypes.byref(r) if r is not None else None, stream),
+          "moe_forward_noalloc")
 
 
 def moe_backward_workspace_bytes(cfg: moe_config, T: int) -> int:

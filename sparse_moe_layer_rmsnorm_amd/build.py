@@ -41,7 +41,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".", "_") + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        lang = ["-x", "hip"]  # moe_abi.cpp holds the no-alloc forward's device scratch array
         cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -10,12 +10,20 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "kernels.h"
 
 using namespace moe;
+
+// Workspace of moe_forward_noalloc: one array per GPU, in the library's code
+// object, so that forward needs no allocation.  Each GPU the library's kernels
+// are loaded on holds it until the process ends.  In host code the name is a
+// host-side stand-in, never the device memory: kernels and copies only ever
+// get the device address that hipGetSymbolAddress returns for it.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -171,6 +179,29 @@ void ws_layout(const moe_config* c, int64_t T, moe_ws_layout* L) {
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Device address of `scratch` on each GPU, looked up once per device (with
+// that device current) and kept for the life of the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_HIP, "device %d: only %d devices are tracked", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress of the no-alloc scratch failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -413,6 +444,11 @@ moe_status moe_init(const moe_config* cfg, const moe_weights* w, void* state, vo
     delete c;
     return fail(MOE_ERR_HIP, "clearing the state failed: %s", hipGetErrorString(e));
   }
+  void* scratch_dev = nullptr;  // set up the no-alloc forward's scratch on this device
+  if (scratch_of_current_device(&scratch_dev) != MOE_OK) {
+    delete c;
+    return MOE_ERR_HIP;
+  }
   e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);  // default priority
   for (int i = 0; i < 4 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&c->fork_ev[i], hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->join_ev, hipEventDisableTiming);
@@ -494,6 +530,25 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
   MOE_RUN(MOE_K_COMBINE, launch_combine(D, Y, p.gates, p.inv, t, y_lat, s));
   MOE_RUN(MOE_K_GEMM_OUT, launch_gemm_out(D, G, y_lat, t, ctx->w.W_sd, ctx->w.W_up, out, s));
   return MOE_OK;
+}
+
+moe_status moe_forward_noalloc(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_route_out* r, void* stream) {
+  if (!ctx) return fail(MOE_ERR_INVALID_ARG, "context is NULL");
+  if (T < 0 || T > ctx->cfg.max_tokens)
+    return fail(MOE_ERR_SHAPE, "T=%lld outside [0, max_tokens=%lld]", (long long)T, (long long)ctx->cfg.max_tokens);
+  const size_t need = moe_workspace_bytes(&ctx->cfg, T);
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "T=%lld needs %zu bytes of workspace; the no-alloc forward has %zu (MOE_NOALLOC_SCRATCH_BYTES): "
+                "call moe_forward with a workspace, or split the batch",
+                (long long)T, need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  if (T == 0) return MOE_OK;
+  void* ws = nullptr;
+  moe_status st = scratch_of_current_device(&ws);
+  if (st != MOE_OK) return st;
+  // nothing in the workspace has to start at zero: every piece a forward
+  // reads is written earlier in the same forward
+  return moe_forward(ctx, x, T, out, r, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 moe_status qb_update(moe_ctx* ctx, void* stream) {

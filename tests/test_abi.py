@@ -204,3 +204,14 @@ def test_counter_hash_follows_code_not_comments(tmp_path):
     f.write_text(text.replace("BM = BM_", "BM = BM_ + 0", 1))
     assert profsum.source_hash(str(src)) != h0
     assert profsum.strip_comments('s = "a//b"; c = \'/\'; // note\n/* x\n y */ t;') == 's = "a//b"; c = \'/\';\n t;'
+
+
+def test_noalloc_scratch_size_matches_header():
+    """The binding's copy of MOE_NOALLOC_SCRATCH_BYTES is the header's, and
+    the array holds one replica-shaped forward of 8192 tokens."""
+    import re
+    text = open(B.HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.MOE_NOALLOC_SCRATCH_BYTES
+    cfg = B.make_config(**REPLICA, max_tokens=16384)
+    assert B.moe_workspace_bytes(cfg, 8192) <= B.MOE_NOALLOC_SCRATCH_BYTES < B.moe_workspace_bytes(cfg, 16384)
