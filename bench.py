@@ -372,7 +372,7 @@ def main() -> int:
                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom,
                     "avg_us": round(dom_us, 3), "algorithmic": f"{work['bytes'][dom]:.6g} bytes per launch"}
     # expert GEMMs together, and routing + permutation + combine together
-    ex_names = [n for n in ("expert_up", "expert_down", "expert_fused") if n in kernels]
+    ex_names = [n for n in ("expert_up", "expert_down") if n in kernels]
     ex_us = sum(kernels[n]["avg_us"] for n in ex_names)
     ex_tf = (work["flops"]["expert_up"] + work["flops"]["expert_down"]) / (ex_us * 1e-6) / 1e12
     rt_names = [n for n in ("topk", "scan", "scatter", "combine") if n in kernels]

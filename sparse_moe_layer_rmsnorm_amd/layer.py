@@ -100,7 +100,8 @@ class MoeLayer:
             "logits": view(L.logits, T * dm["E"], torch.float32, (T, dm["E"])),
             "G": view(L.G, T * dm["f_s"], es, (T, dm["f_s"])),
             "z": view(L.z, T * dm["l"], es, (T, dm["l"])),
-            "H": view(L.H, T * dm["k"] * dm["f"], es, (T * dm["k"], dm["f"])),
+            # H: empty when the experts ran fused (the hidden never left the chip)
+            "H": view(L.H, T * dm["k"] * dm["f"] if L.Y > L.H else 0, es, (-1, dm["f"])),
             "Y": view(L.Y, T * dm["k"] * dm["l"], es, (T * dm["k"], dm["l"])),
             "y_lat": view(L.y_lat, T * dm["l"], es, (T, dm["l"])),
             "tile_offsets": view(L.tile_offsets, dm["E"] + 1, torch.int32, (dm["E"] + 1,)),

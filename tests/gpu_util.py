@@ -63,6 +63,13 @@ def oracle_routing(logits: np.ndarray, bias: np.ndarray, k: int, E: int, B: int,
             "inv": inv, "hist": o.histogram(s, B)}
 
 
+def stored_intermediates(shape, views):
+    """The intermediates a forward left in its workspace: h, z, G (with a
+    shared expert), H (unless the experts ran fused, keeping H on chip), Y,
+    y_lat."""
+    return ("h", "z") + (("G",) if shape.f_s else ()) + (("H",) if views["H"].numel() else ()) + ("Y", "y_lat")
+
+
 def compare_full(shape, W, x, lg, r_gpu, out_gpu, views, bias, *, experts="bf16", with_hist=False,
                  out_tol=None, names=None):
     """Whole-batch parity: the oracle's full forward with the GPU's logits
@@ -80,7 +87,7 @@ def compare_full(shape, W, x, lg, r_gpu, out_gpu, views, bias, *, experts="bf16"
     assert_routing_equal(r_gpu, ref, T)
     tol = OUT_TOL[shape.dtype]
     if names is None:
-        names = ("h", "z") + (("G",) if shape.f_s else ()) + ("H", "Y", "y_lat")
+        names = stored_intermediates(shape, views)
     for name in names:  # intermediates first: a failure names the first wrong step
         errs[name] = rel_err(to_np(views[name]), ref[name])
         say(f"  {name} rel err {errs[name]:.3e} ({ref[name].size} elements)")

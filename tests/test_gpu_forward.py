@@ -11,8 +11,8 @@ import torch
 from oracle import moe_oracle as o
 from sparse_moe_layer_rmsnorm_amd import workloads as wl
 
-from gpu_util import (LOGIT_TOL, OUT_TOL, assert_routing_equal, compare_full, make_layer, rel_err, say, to_np,
-                      x_on_gpu)
+from gpu_util import (LOGIT_TOL, OUT_TOL, assert_routing_equal, compare_full, make_layer, rel_err, say,
+                      stored_intermediates, to_np, x_on_gpu)
 
 pytestmark = pytest.mark.gpu
 F32 = np.float32
@@ -39,7 +39,7 @@ def _run(shape, T, *, bias=None, c=None, step=0, compare_inner=True, layer=None,
     assert_routing_equal(r, ref, T)
     if compare_inner:  # intermediates first: a failure then names the first wrong step
         v = layer.ws_views(T)
-        for name in ("h", "z") + (("G",) if shape.f_s else ()) + ("H", "Y", "y_lat"):
+        for name in stored_intermediates(shape, v):
             e = rel_err(to_np(v[name]), ref[name])
             say(f"  {name} rel err {e:.3e}")
             assert e <= OUT_TOL[shape.dtype], name
