@@ -60,21 +60,21 @@ def kernel_work(s, T: int) -> dict:
         "scan": 4.0 * Tk,
         "scatter": 12.0 * Tk,
         "combine": 1.0 * Tk * s.l * es + 8.0 * Tk + 1.0 * T * s.l * es,
-        "qb_quantile": 4.0 * s.E * s.B + 8.0 * s.E,
-        "qb_bias": 20.0 * s.E,
+        # read and clear the histogram, write q and the bias
+        "qb_update": 8.0 * s.E * s.B + 12.0 * s.E,
         # MXFP8 quantisation of z and H (one launch each): read bf16, write bytes + scales
         "mx_quant": 0.5 * (2.0 + 1.0 + 1.0 / 32) * (T * s.l + Tk * s.f),
         "sign_bias": 16.0 * s.E,
     }
-    # bytes the implementation moves beyond those: the histogram kept as 16
-    # token slices (read-modify-write by the training forward, read and
-    # cleared by the update), the per-chunk selection masks
+    # bytes the implementation moves beyond those: the histogram's atomic
+    # adds from 16 token parts, the per-chunk selection masks and the
+    # per-super-chunk counts
     nchunks = (T + 31) // 32
+    nsuper = (nchunks + 15) // 16
     impl_extra = {
-        "topk": 8.0 * 16 * s.E * s.B + 4.0 * nchunks * s.E,
-        "scan": 12.0 * nchunks * s.E,
-        "scatter": 8.0 * nchunks * s.E,
-        "qb_quantile": 8.0 * 16 * s.E * s.B - 4.0 * s.E * s.B,
+        "topk": 8.0 * 16 * s.E * s.B + 4.0 * nchunks * s.E + 8.0 * nsuper * s.E,
+        "scan": 8.0 * nsuper * s.E,
+        "scatter": 4.0 * 8 * Tk,
     }
     return {"flops": flops, "bytes": bytes_, "impl_extra": impl_extra}
 

@@ -186,8 +186,8 @@ typedef struct moe_state_layout {
   size_t bias;  /* [E] fp32 router bias                                   */
   size_t count; /* uint64 tokens accumulated since the last qb_update     */
   size_t q;     /* [E] fp64 quantiles of the last qb_update               */
-  size_t hist;  /* [hist_slices, E, qb_bins] uint32 score histogram; the
-                   histogram is the sum over the slices                   */
+  size_t hist;  /* [hist_slices, E, qb_bins] uint32 score histogram (one
+                   slice; the histogram is the sum over the slices)       */
   size_t hist_slices;
   size_t load;  /* [E] uint32 tokens routed to each expert since the last
                    update (sign-rule balancer only)                       */
@@ -363,15 +363,19 @@ const char* moe_last_error(void);
  * to n launches, is bracketed by HIP events on its stream.  moe_profile_end()
  * waits for those events and fills, for each kernel id 0..n_ids-1, the summed
  * milliseconds and the launch count; then profiling stops.  Host-side event
- * objects only; no device memory.  MOE_K_HIST and MOE_K_BWD_TRANSPOSE are
- * kept for numbering only and record no launches: in training mode the QB
- * histogram is built inside the MOE_K_TOPK launch, and the backward's GEMMs
- * read their operands as stored (K-major tiles), with no transposed copies.
+ * objects only; no device memory.  MOE_K_HIST, MOE_K_QB_BIAS and
+ * MOE_K_BWD_TRANSPOSE are kept for numbering only and record no launches: in
+ * training mode the QB histogram is built inside the MOE_K_TOPK launch, the
+ * bias launch is timed with the quantile launch under MOE_K_QB_UPDATE, and
+ * the backward's GEMMs read their operands as stored (K-major tiles), with
+ * no transposed copies.
  */
 enum {
   MOE_K_RMSNORM = 0, MOE_K_GEMM_H, MOE_K_TOPK, MOE_K_HIST, MOE_K_SCAN, MOE_K_SCATTER,
-  MOE_K_EXPERT_UP, MOE_K_EXPERT_DOWN, MOE_K_COMBINE, MOE_K_GEMM_OUT, MOE_K_QB_QUANTILE,
-  MOE_K_QB_BIAS, MOE_K_GEMM_RZ, MOE_K_SIGN_BIAS,
+  MOE_K_EXPERT_UP, MOE_K_EXPERT_DOWN, MOE_K_COMBINE, MOE_K_GEMM_OUT,
+  MOE_K_QB_UPDATE, /* the update's two launches: quantiles per expert, then mean and bias */
+  MOE_K_QB_BIAS,   /* (numbering only: both launches are timed under MOE_K_QB_UPDATE) */
+  MOE_K_GEMM_RZ, MOE_K_SIGN_BIAS,
   /* backward: dense products, grouped expert products, weight gradients,
      elementwise transposes and derivatives, (unused) */
   MOE_K_BWD_GEMM, MOE_K_BWD_EXPERT, MOE_K_BWD_WGRAD, MOE_K_BWD_ELTWISE, MOE_K_BWD_TRANSPOSE,

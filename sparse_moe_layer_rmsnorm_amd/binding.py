@@ -23,7 +23,7 @@ MOE_BALANCE_QB, MOE_BALANCE_SIGN = 0, 1
 MOE_EXPERTS_BF16, MOE_EXPERTS_MXFP8, MOE_EXPERTS_MXFP4 = 0, 1, 2
 _EXPERT_FORMATS = {"bf16": MOE_EXPERTS_BF16, "mxfp8": MOE_EXPERTS_MXFP8, "mxfp4": MOE_EXPERTS_MXFP4}
 KERNELS = ["rmsnorm", "gemm_h", "topk", "hist", "scan", "scatter", "expert_up", "expert_down", "combine",
-           "gemm_out", "qb_quantile", "qb_bias", "gemm_rz", "sign_bias", "bwd_gemm", "bwd_expert", "bwd_wgrad",
+           "gemm_out", "qb_update", "qb_bias", "gemm_rz", "sign_bias", "bwd_gemm", "bwd_expert", "bwd_wgrad",
            "bwd_eltwise", "bwd_transpose", "mx_quant"]
 MOE_NUM_KERNELS = len(KERNELS)
 

@@ -10,8 +10,9 @@ namespace moe {
 constexpr int kChunk = 32;
 // Chunks per super-chunk of the two-level prefix sum.
 constexpr int kSuper = 16;
-// Token slices of the QB histogram kept in the state ([slice][E][B]).
-constexpr int kHistSlices = 16;
+// Token parts of one training pass whose score histograms are built by
+// separate blocks (each adds its counts into the one histogram of the state).
+constexpr int kHistParts = 16;
 // Rows per tile of the grouped expert GEMMs (also the granularity of the
 // per-expert tile offsets computed by the scan).
 #ifndef MOE_EXPERT_BM
@@ -32,32 +33,38 @@ struct Dims {
   float qb_lo, qb_hi, qb_scale;  // histogram score range and fp32(B / (qb_hi - qb_lo))
 };
 
-hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s);
-// Scores, biased top-k, gates and selection masks; with `hist` non-NULL
-// (training) the same launch adds the score histogram and the token count.
+// RMSNorm; the launch also clears zero[0 .. nzero) (the super-chunk
+// selection counts the top-k launch of the same pass adds into).
+hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s,
+                          int32_t* zero = nullptr, int nzero = 0);
+// Scores, biased top-k, gates and selection masks, and each super-chunk's
+// selection count per expert added to ssum[T / (kChunk kSuper)][E] (cleared
+// beforehand); with `hist` non-NULL (training) the same launch adds the
+// score histogram and the token count.
 hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, int T, int32_t* idx, float* gates,
-                       uint32_t* bitmap, uint32_t* hist, unsigned long long* count, hipStream_t s);
-// Two launches: per-super-chunk prefix, then the global prefix, the row and
-// m-tile offsets and the m-tile table tile_info[g] = {first row, expert << 8 |
-// rows in use} of the grouped GEMMs.  With `load` non-NULL (sign-rule training) the
-// counts are also added to load[E] and T to *count.
+                       uint32_t* bitmap, uint32_t* hist, unsigned long long* count, int32_t* ssum, hipStream_t s);
+// The global prefix over the super-chunk totals sbase (which become each
+// super-chunk's first row per expert), the row and m-tile offsets and the
+// m-tile table tile_info[g] = {first row, expert << 8 | rows in use} of the
+// grouped GEMMs.  With `load` non-NULL (sign-rule training) the counts are
+// also added to load[E] and T to *count.
 // tile_offsets / tile_info: the kExpertBM table; tile_offsets2 / tile_info2
 // (nullable): the kExpertBM2 table.
-hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cbase, int32_t* sbase, int32_t* counts,
-                       int32_t* offsets, int32_t* tile_offsets, int2* tile_info, uint32_t* load,
-                       unsigned long long* count, hipStream_t s, int32_t* tile_offsets2 = nullptr,
-                       int2* tile_info2 = nullptr);
-// Rows of the permutation, and the dispatch buffer X[row] = z[token].
-// With zs non-NULL (MXFP8 experts) also copies each token's z scale row
-// (s_ld bytes, a multiple of 4) to Xs at each of its grouped rows.
-hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* cbase,
-                          const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s,
-                          const uint8_t* zs = nullptr, uint8_t* Xs = nullptr, int s_ld = 0);
+hipError_t launch_scan(const Dims& D, int T, int32_t* sbase, int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
+                       int2* tile_info, uint32_t* load, unsigned long long* count, hipStream_t s,
+                       int32_t* tile_offsets2 = nullptr, int2* tile_info2 = nullptr);
+// Rows of the permutation (perm_src, inv).  With zs non-NULL (MXFP8 experts)
+// also copies each token's z scale row (s_ld bytes, a multiple of 4) to Xs at
+// each of its grouped rows.
+hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* sbase, int T,
+                          int32_t* perm_src, int32_t* inv, hipStream_t s, const uint8_t* zs = nullptr,
+                          uint8_t* Xs = nullptr, int s_ld = 0);
 hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, const int32_t* inv, int T,
                           void* y_lat, hipStream_t s);
-hipError_t launch_qb_quantile(const Dims& D, uint32_t* hist, const unsigned long long* count, double* q,
-                              hipStream_t s);
-hipError_t launch_qb_bias(const Dims& D, const double* q, unsigned long long* count, float* bias, hipStream_t s);
+// QB update: quantiles from the histogram [E][B] (cleared; one block per
+// expert), then b = mean(q) - q and the token count cleared (one block).
+hipError_t launch_qb_update(const Dims& D, uint32_t* hist, unsigned long long* count, double* q, float* bias,
+                            hipStream_t s);
 // Sign-rule bias update from the accumulated loads; clears loads and count.
 hipError_t launch_sign_bias(const Dims& D, uint32_t* load, unsigned long long* count, float gamma, float* bias,
                             hipStream_t s);

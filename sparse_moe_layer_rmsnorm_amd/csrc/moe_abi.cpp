@@ -118,8 +118,8 @@ void state_layout(const moe_config* c, moe_state_layout* L) {
   L->q = o;
   o = up(o + (size_t)c->E * 8);
   L->hist = o;
-  L->hist_slices = kHistSlices;
-  o = up(o + (size_t)kHistSlices * c->E * c->qb_bins * 4);
+  L->hist_slices = 1;
+  o = up(o + (size_t)c->E * c->qb_bins * 4);
   L->load = o;
   o = up(o + (size_t)c->E * 4);
   L->mx = o;
@@ -147,7 +147,7 @@ void ws_layout(const moe_config* c, int64_t T, moe_ws_layout* L) {
   L->idx = take(t * k * 4);
   L->gates = take(t * k * 4);
   L->bitmap = take(nchunks * E * 4);
-  L->cbase = take(nchunks * E * 4);
+  L->cbase = take(0);  // kept in the layout, no longer used (the scatter sums chunk bases from the masks)
   L->sbase = take(nsuper * E * 4);
   L->counts = take(E * 4);
   L->offsets = take((E + 1) * 4);
@@ -248,7 +248,8 @@ moe_status run(moe_ctx* c, int kid, hipStream_t s, F&& f) {
 
 struct RoutePtrs {
   float* logits;
-  int32_t *idx, *cbase, *sbase, *counts, *offsets, *tile_offsets, *perm_src, *inv;
+  int32_t *idx, *sbase, *counts, *offsets, *tile_offsets, *perm_src, *inv;
+  int nsbase;  // ints in sbase
   uint32_t* bitmap;
   int2* tile_info;
   int32_t* tile_offsets2;  // the kExpertBM2 tile table (expert down-projection)
@@ -266,8 +267,8 @@ RoutePtrs route_ptrs(const moe_config& c, int64_t T, const moe_ws_layout& L, cha
   p.perm_src = (r && r->perm_src) ? r->perm_src : reinterpret_cast<int32_t*>(ws + L.perm_src);
   p.inv = (r && r->inv) ? r->inv : reinterpret_cast<int32_t*>(ws + L.inv);
   p.bitmap = reinterpret_cast<uint32_t*>(ws + L.bitmap);
-  p.cbase = reinterpret_cast<int32_t*>(ws + L.cbase);
   p.sbase = reinterpret_cast<int32_t*>(ws + L.sbase);
+  p.nsbase = (int)((((T + kChunk - 1) / kChunk + kSuper - 1) / kSuper) * c.E);
   p.tile_offsets = reinterpret_cast<int32_t*>(ws + L.tile_offsets);
   p.tile_info = reinterpret_cast<int2*>(ws + L.tile_info);
   p.tile_offsets2 = p.tile_offsets + (c.E + 1);
@@ -305,12 +306,12 @@ moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s, co
   uint32_t* hist = train && !sign ? reinterpret_cast<uint32_t*>(ctx->state + ctx->sl.hist) : nullptr;
   uint32_t* load = train && sign ? reinterpret_cast<uint32_t*>(ctx->state + ctx->sl.load) : nullptr;
   unsigned long long* cnt = reinterpret_cast<unsigned long long*>(ctx->state + ctx->sl.count);
-  MOE_RUN(MOE_K_TOPK, launch_topk(D, p.logits, bias, T, p.idx, p.gates, p.bitmap, hist, cnt, s));
+  MOE_RUN(MOE_K_TOPK, launch_topk(D, p.logits, bias, T, p.idx, p.gates, p.bitmap, hist, cnt, p.sbase, s));
   if (train) ctx->pending_tokens += (uint64_t)T;
-  MOE_RUN(MOE_K_SCAN, launch_scan(D, p.bitmap, T, p.cbase, p.sbase, p.counts, p.offsets, p.tile_offsets,
+  MOE_RUN(MOE_K_SCAN, launch_scan(D, T, p.sbase, p.counts, p.offsets, p.tile_offsets,
                                   p.tile_info, load, train && sign ? cnt : nullptr, s, p.tile_offsets2,
                                   p.tile_info2));
-  MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.bitmap, p.cbase, p.sbase, T, p.perm_src, p.inv, s, zs, Xs, D.l / 32));
+  MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.bitmap, p.sbase, T, p.perm_src, p.inv, s, zs, Xs, D.l / 32));
   return MOE_OK;
 }
 
@@ -473,10 +474,12 @@ moe_status moe_route(moe_ctx* ctx, const void* x, const float* logits, int64_t T
   const int t = (int)T;
   if (logits) {
     p.logits = const_cast<float*>(logits);
+    // no RMSNorm launch to clear the super-chunk counts in: a fill launch
+    MOE_RUN(MOE_K_SCAN, launch_zero(p.sbase, ((size_t)p.nsbase * 4 + 15) / 16 * 16, s));  // in the 256-byte padding
   } else {
     const Dims& D = ctx->D;
     void* h = w + L.h;
-    MOE_RUN(MOE_K_RMSNORM, launch_rmsnorm(D, x, ctx->w.gamma, h, t, s));
+    MOE_RUN(MOE_K_RMSNORM, launch_rmsnorm(D, x, ctx->w.gamma, h, t, s, p.sbase, p.nsbase));
     MOE_RUN(MOE_K_GEMM_RZ, launch_gemm_rz(D, h, t, ctx->w.W_r, ctx->w.logit_offset, p.logits, s));
   }
   return route_tail(ctx, p, t, s);
@@ -496,7 +499,7 @@ moe_status moe_forward(moe_ctx* ctx, const void* x, int64_t T, void* out, moe_ro
   const int t = (int)T;
   void *h = w + L.h, *G = w + L.G, *z = w + L.z, *H = w + L.H, *Y = w + L.Y, *y_lat = w + L.y_lat;
   const bool keep = ctx->cfg.keep_preact != 0;
-  MOE_RUN(MOE_K_RMSNORM, launch_rmsnorm(D, x, ctx->w.gamma, h, t, s));
+  MOE_RUN(MOE_K_RMSNORM, launch_rmsnorm(D, x, ctx->w.gamma, h, t, s, p.sbase, p.nsbase));
   MOE_RUN(MOE_K_GEMM_H, launch_gemm_h(D, h, t, ctx->w.W_r, ctx->w.logit_offset, ctx->w.W_sg, ctx->w.W_su,
                                       ctx->w.W_dn, p.logits, D.f_s > 0 ? G : nullptr, z, s,
                                       keep && D.f_s > 0 ? w + L.P : nullptr, keep && D.f_s > 0 ? w + L.Q : nullptr));
@@ -566,8 +569,7 @@ moe_status qb_update(moe_ctx* ctx, void* stream) {
     ctx->pending_tokens = 0;
     return MOE_OK;
   }
-  MOE_RUN(MOE_K_QB_QUANTILE, launch_qb_quantile(D, hist, cnt, q, s));
-  MOE_RUN(MOE_K_QB_BIAS, launch_qb_bias(D, q, cnt, bias, s));
+  MOE_RUN(MOE_K_QB_UPDATE, launch_qb_update(D, hist, cnt, q, bias, s));
   ctx->pending_tokens = 0;
   return MOE_OK;
 }
@@ -860,7 +862,7 @@ const char* moe_last_error(void) { return g_err; }
 const char* moe_kernel_name(int id) {
   static const char* names[MOE_NUM_KERNELS] = {"rmsnorm",     "gemm_h",  "topk",     "hist",
                                                 "scan",        "scatter", "expert_up", "expert_down",
-                                                "combine",     "gemm_out", "qb_quantile", "qb_bias", "gemm_rz",
+                                                "combine",     "gemm_out", "qb_update", "qb_bias", "gemm_rz",
                                                 "sign_bias",   "bwd_gemm", "bwd_expert", "bwd_wgrad",
                                                 "bwd_eltwise", "bwd_transpose", "mx_quant"};
   return (id >= 0 && id < MOE_NUM_KERNELS) ? names[id] : "unknown";

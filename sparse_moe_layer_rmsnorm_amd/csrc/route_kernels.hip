@@ -60,7 +60,11 @@ MOE_DEV uint4 chunk_scale(const uint4& v, float rstd, const float* g) {
 
 template <bool BF16, int CPL>
 __global__ __launch_bounds__(256) void k_rmsnorm(const void* __restrict__ x, const float* __restrict__ gamma,
-                                                 void* __restrict__ h, int T, int d, float eps) {
+                                                 void* __restrict__ h, int T, int d, float eps,
+                                                 int32_t* __restrict__ zero, int nzero) {
+  // the top-k launch of the same pass accumulates into `zero` (per super-chunk
+  // selection counts): cleared here, the pass's first launch
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < nzero; i += gridDim.x * 256) zero[i] = 0;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= T) return;
@@ -92,21 +96,27 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const void* __restrict__ x, con
 }
 
 template <bool BF16>
-static void rmsnorm_dispatch(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s) {
+static void rmsnorm_dispatch(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s,
+                             int32_t* zero, int nzero) {
   const int per_lane = (D.d / (BF16 ? 8 : 4) + 63) / 64;
   dim3 grid((T + 3) / 4), block(256);
-  if (per_lane <= 1) hipLaunchKernelGGL((k_rmsnorm<BF16, 1>), grid, block, 0, s, x, gamma, h, T, D.d, D.eps);
-  else if (per_lane <= 2) hipLaunchKernelGGL((k_rmsnorm<BF16, 2>), grid, block, 0, s, x, gamma, h, T, D.d, D.eps);
-  else if (per_lane <= 4) hipLaunchKernelGGL((k_rmsnorm<BF16, 4>), grid, block, 0, s, x, gamma, h, T, D.d, D.eps);
-  else if (per_lane <= 8) hipLaunchKernelGGL((k_rmsnorm<BF16, 8>), grid, block, 0, s, x, gamma, h, T, D.d, D.eps);
-  else hipLaunchKernelGGL((k_rmsnorm<BF16, 0>), grid, block, 0, s, x, gamma, h, T, D.d, D.eps);
+#define MOE_RMS(C) \
+  hipLaunchKernelGGL((k_rmsnorm<BF16, C>), grid, block, 0, s, x, gamma, h, T, D.d, D.eps, zero, nzero)
+  if (per_lane <= 1) MOE_RMS(1);
+  else if (per_lane <= 2) MOE_RMS(2);
+  else if (per_lane <= 4) MOE_RMS(4);
+  else if (per_lane <= 8) MOE_RMS(8);
+  else MOE_RMS(0);
+#undef MOE_RMS
 }
 
-hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s) {
+hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s,
+                          int32_t* zero, int nzero) {
+  if (T <= 0) return hipSuccess;
   if (D.bf16)
-    rmsnorm_dispatch<true>(D, x, gamma, h, T, s);
+    rmsnorm_dispatch<true>(D, x, gamma, h, T, s, zero, nzero);
   else
-    rmsnorm_dispatch<false>(D, x, gamma, h, T, s);
+    rmsnorm_dispatch<false>(D, x, gamma, h, T, s, zero, nzero);
   return hipGetLastError();
 }
 
@@ -206,7 +216,7 @@ constexpr int kTopkThreads = kChunk / kTopkNT * 64;      // one token group per 
 template <int CPL>
 MOE_DEV void topk_block(int chunk, uint32_t* mask, const float* __restrict__ logits, const float* __restrict__ bias,
                         int T, int E, int k, float scale, int32_t* __restrict__ idx, float* __restrict__ gates,
-                        uint32_t* __restrict__ bitmap) {
+                        uint32_t* __restrict__ bitmap, int32_t* __restrict__ ssum) {
   constexpr int NW = kChunk / kTopkNT;
   for (int i = threadIdx.x; i < E; i += kTopkThreads) mask[i] = 0u;
   __syncthreads();
@@ -233,15 +243,21 @@ MOE_DEV void topk_block(int chunk, uint32_t* mask, const float* __restrict__ log
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < E; i += kTopkThreads) bitmap[(size_t)chunk * E + i] = mask[i];
+  // the chunk's masks, and its counts added to its super-chunk's totals
+  // (integer atomics: the sums do not depend on the order of the chunks)
+  int32_t* sdst = ssum + (size_t)(chunk / kSuper) * E;
+  for (int i = threadIdx.x; i < E; i += kTopkThreads) {
+    const uint32_t m = mask[i];
+    bitmap[(size_t)chunk * E + i] = m;
+    if (m) atomicAdd(&sdst[i], __popc(m));
+  }
 }
 
 // ---------------------------------------------------------- QB histogram ----
-// The state keeps the histogram as kHistSlices token slices [slice][E][B].
-// Block (16-expert group, slice) counts its tokens' score bins in LDS with
-// integer atomics (order-free) and adds them to its own rows of its own slice
-// (no other block of the launch writes them), so no reduction pass is needed
-// per forward; qb_update sums the slices.
+// The state keeps one histogram [E][B].  Block (16-expert group, token part)
+// counts its part's score bins in LDS with integer atomics and adds them to
+// the histogram rows with global integer atomics: both are order-free, so the
+// histogram is the same whatever order the blocks run in.
 MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict__ logits, int T, int E, int B,
                         float lo, float scale, int tps, uint32_t* __restrict__ hist,
                         unsigned long long* __restrict__ count) {
@@ -268,11 +284,11 @@ MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict
       atomicAdd(&row[score_bin(router_sigmoid(logits[(size_t)t * E + e]), B, lo, scale)], 1u);
   }
   __syncthreads();
-  if (tb < T) {
-    uint32_t* dst = hist + ((size_t)ts * E + e0) * B;
+  if (tb < T) {  // integer atomics: the sums do not depend on the order of the token parts
+    uint32_t* dst = hist + (size_t)e0 * B;
     for (int i = threadIdx.x; i < ne * B; i += kTopkThreads) {
       const uint32_t v = lh[i];
-      if (v) dst[i] += v;
+      if (v) atomicAdd(&dst[i], v);
     }
   }
   if (group == 0 && ts == 0 && threadIdx.x == 0) *count += (unsigned long long)T;
@@ -288,11 +304,12 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
                                                        float* __restrict__ gates, uint32_t* __restrict__ bitmap,
                                                        int nchunks, int B, float lo, float bscale, int tps,
                                                        uint32_t* __restrict__ hist,
-                                                       unsigned long long* __restrict__ count) {
+                                                       unsigned long long* __restrict__ count,
+                                                       int32_t* __restrict__ ssum) {
   __shared__ uint32_t smem[kHistExperts * 256];
   static_assert(kHistExperts * 256 >= 1024, "the top-k masks fit");
   if ((int)blockIdx.x < nchunks) {
-    topk_block<CPL>(blockIdx.x, smem, logits, bias, T, E, k, scale, idx, gates, bitmap);
+    topk_block<CPL>(blockIdx.x, smem, logits, bias, T, E, k, scale, idx, gates, bitmap, ssum);
   } else {
     const int hb = blockIdx.x - nchunks, groups = (E + kHistExperts - 1) / kHistExperts;
     hist_block(hb % groups, hb / groups, smem, logits, T, E, B, lo, bscale, tps, hist, count);
@@ -300,15 +317,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
 }
 
 hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, int T, int32_t* idx, float* gates,
-                       uint32_t* bitmap, uint32_t* hist, unsigned long long* count, hipStream_t s) {
+                       uint32_t* bitmap, uint32_t* hist, unsigned long long* count, int32_t* ssum, hipStream_t s) {
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int cpl = (D.E + 63) / 64;
-  const int tps = (T + kHistSlices - 1) / kHistSlices;
-  const int hblocks = hist ? (D.E + kHistExperts - 1) / kHistExperts * kHistSlices : 0;
+  const int tps = (T + kHistParts - 1) / kHistParts;
+  const int hblocks = hist ? (D.E + kHistExperts - 1) / kHistExperts * kHistParts : 0;
   dim3 grid(nchunks + hblocks), block(kTopkThreads);
 #define MOE_TOPK(C)                                                                                                 \
   hipLaunchKernelGGL(k_topk<C>, grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, bitmap, \
-                     nchunks, D.B, D.qb_lo, D.qb_scale, tps, hist, count)
+                     nchunks, D.B, D.qb_lo, D.qb_scale, tps, hist, count, ssum)
   if (cpl <= 1) MOE_TOPK(1);
   else if (cpl <= 2) MOE_TOPK(2);
   else if (cpl <= 4) MOE_TOPK(4);
@@ -320,28 +337,10 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
 
 // ------------------------------------------------------- counts / scan ----
 // Two-level exclusive prefix sums of the per-(chunk, expert) selection counts
-// popcount(bitmap[c][e]).  Local: per super-chunk of kSuper chunks, one lane
-// per expert walks its chunks: cbase[c][e] = count of expert e in the earlier
-// chunks of the super-chunk; sbase[sc][e] = the super-chunk's total.
-__global__ __launch_bounds__(256) void k_scan_local(const uint32_t* __restrict__ bitmap, int nchunks, int E,
-                                                    int32_t* __restrict__ cbase, int32_t* __restrict__ sbase) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = blockIdx.x * 64 + lane;
-  const int sc = blockIdx.y * 4 + wave;
-  const int c0 = sc * kSuper;
-  if (e >= E || c0 >= nchunks) return;
-  uint32_t m[kSuper];  // all loads of the super-chunk in flight together
-#pragma unroll
-  for (int j = 0; j < kSuper; ++j) m[j] = c0 + j < nchunks ? bitmap[(size_t)(c0 + j) * E + e] : 0u;
-  int run = 0;
-#pragma unroll
-  for (int j = 0; j < kSuper; ++j) {
-    if (c0 + j < nchunks) cbase[(size_t)(c0 + j) * E + e] = run;
-    run += __popc(m[j]);
-  }
-  sbase[(size_t)sc * E + e] = run;
-}
-
+// popcount(bitmap[c][e]).  The top-k launch leaves each super-chunk's (kSuper
+// chunks') total per expert in sbase; the global scan below turns those into
+// first rows; the base of a chunk inside its super-chunk is summed by the
+// scatter from the masks themselves.
 // Global (one block of 1024 threads, one expert per thread): per expert, the
 // total and the exclusive prefix over super-chunks (sbase becomes the
 // absolute first row of each super-chunk's part of the expert's group); over
@@ -461,16 +460,12 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
   if (tile_info2) fill(s_u, kExpertBM2, tile_info2);
 }
 
-hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cbase, int32_t* sbase, int32_t* counts,
-                       int32_t* offsets, int32_t* tile_offsets, int2* tile_info, uint32_t* load,
-                       unsigned long long* count, hipStream_t s, int32_t* tile_offsets2, int2* tile_info2) {
+hipError_t launch_scan(const Dims& D, int T, int32_t* sbase, int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
+                       int2* tile_info, uint32_t* load, unsigned long long* count, hipStream_t s,
+                       int32_t* tile_offsets2, int2* tile_info2) {
   if ((tile_offsets2 == nullptr) != (tile_info2 == nullptr)) return hipErrorInvalidValue;
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int nsuper = (nchunks + kSuper - 1) / kSuper;
-  dim3 g1((D.E + 63) / 64, (nsuper + 3) / 4);
-  hipLaunchKernelGGL(k_scan_local, g1, dim3(256), 0, s, bitmap, nchunks, D.E, cbase, sbase);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan_global, dim3(1), dim3(1024), 0, s, sbase, nsuper, D.E, counts, offsets, tile_offsets,
                      tile_info, load, load ? count : nullptr, T, D.k, tile_offsets2, tile_info2);
   return hipGetLastError();
@@ -478,22 +473,28 @@ hipError_t launch_scan(const Dims& D, const uint32_t* bitmap, int T, int32_t* cb
 
 // -------------------------------------------------------------- scatter ----
 // Stable rows without order-dependent atomics, one thread per (t, j): the row
-// of (t, j) in expert e's group is the super-chunk base + the chunk base +
-// the number of earlier tokens of the chunk in the chunk's mask for e.
+// of (t, j) in expert e's group is the super-chunk's first row (global scan)
+// + the tokens of e in the earlier chunks of the super-chunk (their masks'
+// popcounts, at most kSuper - 1 loads, all in flight together) + the earlier
+// tokens of the chunk in the chunk's mask for e.
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, const uint32_t* __restrict__ bitmap,
-                                                 const int32_t* __restrict__ cbase, const int32_t* __restrict__ sbase,
-                                                 int T, int E, int k, int32_t* __restrict__ perm_src,
-                                                 int32_t* __restrict__ inv, const uint32_t* __restrict__ zs,
-                                                 uint32_t* __restrict__ Xs, int s4) {
+                                                 const int32_t* __restrict__ sbase, int T, int E, int k,
+                                                 int32_t* __restrict__ perm_src, int32_t* __restrict__ inv,
+                                                 const uint32_t* __restrict__ zs, uint32_t* __restrict__ Xs, int s4) {
   const int Tk = T * k;
   const int p = blockIdx.x * 256 + threadIdx.x;
   if (p >= Tk) return;
   const int t = p / k;
   const int e = idx[p];
-  const int c = t / kChunk;
-  const size_t ce = (size_t)c * E + e;
-  const uint32_t below = bitmap[ce] & ((1u << (t % kChunk)) - 1u);
-  const int row = sbase[(size_t)(c / kSuper) * E + e] + cbase[ce] + __popc(below);
+  const int c = t / kChunk, c0 = c - c % kSuper;
+  uint32_t m[kSuper - 1];
+#pragma unroll
+  for (int j = 0; j < kSuper - 1; ++j) m[j] = c0 + j < c ? bitmap[(size_t)(c0 + j) * E + e] : 0u;
+  int cb = 0;
+#pragma unroll
+  for (int j = 0; j < kSuper - 1; ++j) cb += __popc(m[j]);
+  const uint32_t below = bitmap[(size_t)c * E + e] & ((1u << (t % kChunk)) - 1u);
+  const int row = sbase[(size_t)(c / kSuper) * E + e] + cb + __popc(below);
   inv[p] = row;
   if ((unsigned)row < (unsigned)Tk) {  // always true for a consistent permutation
     perm_src[row] = t;
@@ -501,12 +502,11 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
   }
 }
 
-hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* cbase,
-                          const int32_t* sbase, int T, int32_t* perm_src, int32_t* inv, hipStream_t s,
-                          const uint8_t* zs, uint8_t* Xs, int s_ld) {
+hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* sbase, int T,
+                          int32_t* perm_src, int32_t* inv, hipStream_t s, const uint8_t* zs, uint8_t* Xs, int s_ld) {
   const long long Tk = (long long)T * D.k;
   if (zs && s_ld % 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_scatter, dim3((unsigned)((Tk + 255) / 256)), dim3(256), 0, s, idx, bitmap, cbase, sbase, T,
+  hipLaunchKernelGGL(k_scatter, dim3((unsigned)((Tk + 255) / 256)), dim3(256), 0, s, idx, bitmap, sbase, T,
                      D.E, D.k, perm_src, inv, reinterpret_cast<const uint32_t*>(zs), reinterpret_cast<uint32_t*>(Xs),
                      zs ? s_ld / 4 : 0);
   return hipGetLastError();
@@ -580,14 +580,13 @@ hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, cons
 // is cleared.
 constexpr unsigned long long kMaxWindowTokens = 0xFFFFFFFFull;
 
-// Per expert (one block each, one thread per bin): sum the bin over the
-// histogram slices and clear it; with A_j = tokens above bin j (a suffix sum:
-// wave shuffles, then the wave totals), the one bin with
-// A_j*E < N*k <= (A_j + c_j)*E (exact integer tests) holds the score the
-// expert must beat to receive N*k/E tokens; inside it the estimate is linear
-// in the bin, as a fraction of the histogram range [lo, hi]:
-// u = (j+1)/B - ((N*k - A_j*E) / (E*c_j)) / B and q = lo + (hi - lo) * u,
-// fp64 (q = u on [0, 1]).
+// Per expert (one block each, one thread per bin): read the bin and clear
+// it; with A_j = tokens above bin j (a suffix sum: wave shuffles, then the
+// wave totals), the one bin with A_j*E < N*k <= (A_j + c_j)*E (exact integer
+// tests) holds the score the expert must beat to receive N*k/E tokens; inside
+// it the estimate is linear in the bin, as a fraction of the histogram range
+// [lo, hi]: u = (j+1)/B - ((N*k - A_j*E) / (E*c_j)) / B and q = lo + (hi - lo)
+// * u, fp64 (q = u on [0, 1]).  A window past kMaxWindowTokens marks q NaN.
 __global__ __launch_bounds__(256) void k_qb_quantile(uint32_t* __restrict__ hist,
                                                      const unsigned long long* __restrict__ count, int E, int B,
                                                      int k, double lo, double width, double* __restrict__ q) {
@@ -596,19 +595,12 @@ __global__ __launch_bounds__(256) void k_qb_quantile(uint32_t* __restrict__ hist
   const unsigned long long N = *count;
   if (N == 0) return;
   const int e = blockIdx.x, j = threadIdx.x, lane = j & 63, w = j >> 6;
-  const bool overflow = N > kMaxWindowTokens;  // block-uniform
   unsigned long long c = 0;
   if (j < B) {
-    uint32_t v[kHistSlices];
-#pragma unroll
-    for (int sl = 0; sl < kHistSlices; ++sl) v[sl] = hist[((size_t)sl * E + e) * B + j];
-#pragma unroll
-    for (int sl = 0; sl < kHistSlices; ++sl) {
-      c += v[sl];
-      hist[((size_t)sl * E + e) * B + j] = 0u;
-    }
+    c = hist[(size_t)e * B + j];
+    hist[(size_t)e * B + j] = 0u;
   }
-  if (overflow) {
+  if (N > kMaxWindowTokens) {  // block-uniform
     if (j == 0) q[e] = __builtin_nan("");
     return;
   }
@@ -661,14 +653,12 @@ __global__ __launch_bounds__(1024) void k_qb_bias(const double* __restrict__ q, 
   if (threadIdx.x == 0) *count = 0ull;
 }
 
-hipError_t launch_qb_quantile(const Dims& D, uint32_t* hist, const unsigned long long* count, double* q,
-                              hipStream_t s) {
+hipError_t launch_qb_update(const Dims& D, uint32_t* hist, unsigned long long* count, double* q, float* bias,
+                            hipStream_t s) {
   const double lo = (double)D.qb_lo, width = (double)D.qb_hi - (double)D.qb_lo;
   hipLaunchKernelGGL(k_qb_quantile, dim3(D.E), dim3(256), 0, s, hist, count, D.E, D.B, D.k, lo, width, q);
-  return hipGetLastError();
-}
-
-hipError_t launch_qb_bias(const Dims& D, const double* q, unsigned long long* count, float* bias, hipStream_t s) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_qb_bias, dim3(1), dim3(1024), 0, s, q, count, D.E, bias);
   return hipGetLastError();
 }
