@@ -200,14 +200,15 @@ def cold_forward(layer, x, out, stream, n: int) -> dict:
 
 
 def balance_record(layer, shape, steps: int) -> list:
-    """Per-step expert load balance of a training loop (fresh x each step,
-    the bias of each step set by the previous step's update): max/min and
-    max/mean of the tokens per expert and the number of experts with none.
-    Runs outside the timed region; the layer's bias and statistics are
-    restored afterwards."""
+    """Per-step expert load balance of a training loop that starts from a
+    zero bias (fresh x each step, the bias of each step set by the previous
+    step's update): max/min and max/mean of the tokens per expert and the
+    number of experts with none.  Runs outside the timed region; the layer's
+    bias is restored afterwards."""
     import torch
     from sparse_moe_layer_rmsnorm_amd import workloads as wl
     bias0 = layer.get_bias().clone()
+    layer.set_bias(torch.zeros_like(bias0))
     T = shape.T
     r = layer.route_buffers(T)
     out = torch.empty(T, shape.d, dtype=layer.tdtype, device="cuda")
@@ -455,8 +456,8 @@ def main() -> int:
     nbal = args.balance_steps if args.balance_steps is not None else (20 if shape.name == "skew" else 3)
     if not frozen and not args.backward and nbal > 0:
         res["balance"] = {"steps": balance_record(layer, shape, nbal),
-                          "note": "fresh x per step (seeded by step), each step's bias from the previous step's "
-                                  "update; tokens per expert"}
+                          "note": "starts from a zero bias; fresh x per step (seeded by step), each step's bias "
+                                  "from the previous step's update; tokens per expert"}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(shape, dict(W, c=c) if c is not None else W, x_np, args.cpu_seconds)
     layer.close()

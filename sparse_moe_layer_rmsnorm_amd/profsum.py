@@ -3,6 +3,8 @@
     python -m sparse_moe_layer_rmsnorm_amd.profsum trace <kernel_trace.csv> <workload> "<command>"
     python -m sparse_moe_layer_rmsnorm_amd.profsum traffic <fetch.csv> <write.csv> <workload> "<command>" [json]
 
+    python -m sparse_moe_layer_rmsnorm_amd.profsum counters <workload> "<commands>" <pmc.csv> [<pmc.csv> ...]
+
 `trace` prints a markdown table of per-kernel launch counts and durations
 from a `--kernel-trace` CSV.  `traffic` reads two `--pmc FETCH_SIZE` and
 `--pmc WRITE_SIZE` counter CSVs of the same command, scales each counter by
@@ -12,6 +14,11 @@ record (HBM bytes per launch per kernel) that bench.py reports as
 `roofline.traffic`; with a fifth argument it also writes that record, keyed
 by a hash of the kernel sources' code, comments excluded, to the given JSON
 file (bench.py reports the figure only while the sources still hash the same).
+
+`counters` sums each hardware counter of each kernel's launches (the first
+launch of a kernel skipped when it has more), over the counter's hardware
+instances, from one or more `--pmc` CSVs, and prints them per launch with the
+ratios derived from them (each ratio states its counters).
 
 The dense GEMM launches carry a tag template argument: 0 the h GEMM of a
 forward (gemm_h), 1 router logits alone (gemm_rz, routing-only pass), 2 the
@@ -161,6 +168,35 @@ def traffic_table(fetch_csv: str, write_csv: str):
     return per, factors
 
 
+def counters_table(paths: list) -> OrderedDict:
+    """{kernel: {counter: mean per launch}} over the given --pmc CSVs."""
+    out: OrderedDict = OrderedDict()
+    for path in paths:
+        acc: OrderedDict = OrderedDict()  # dispatch -> [symbol, {counter: value}]
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                did = int(r["Dispatch_Id"])
+                e = acc.setdefault(did, [r["Kernel_Name"], defaultdict(float)])
+                e[1][r["Counter_Name"]] += float(r["Counter_Value"])
+        rows = sorted((did, sym, vals) for did, (sym, vals) in acc.items())
+        per = defaultdict(list)
+        for (did, sym, vals), name in zip(rows, _label(rows)):
+            if name and name != "copy":
+                per[name].append(vals)
+        for name, launches in per.items():
+            use = launches[1:] if len(launches) > 1 else launches
+            d = out.setdefault(name, OrderedDict())
+            for c in use[0]:
+                d[c] = sum(v.get(c, 0.0) for v in use) / len(use)
+    return out
+
+
+def _ratio(d, num, den, scale=1.0):
+    if num in d and den in d and d[den] > 0:
+        return d[num] / (d[den] * scale)
+    return None
+
+
 def main(argv) -> int:
     if len(argv) >= 4 and argv[0] == "trace":
         path, workload, cmd = argv[1], argv[2], argv[3]
@@ -199,6 +235,31 @@ def main(argv) -> int:
             with open(argv[5], "w") as f:
                 json.dump(doc, f, indent=1)
                 f.write("\n")
+        return 0
+    if len(argv) >= 4 and argv[0] == "counters":
+        workload, cmd, paths = argv[1], argv[2], argv[3:]
+        tab = counters_table(paths)
+        print(f"# Hardware counters per launch, {workload} workload\n")
+        print(f"Commands (one run per counter group): `{cmd}`\n")
+        print("Counter values are summed over their hardware instances and averaged over a kernel's launches (its "
+              "first launch skipped). GRBM_GUI_ACTIVE sums 8 XCD instances, so cycles = GRBM_GUI_ACTIVE / 8.\n")
+        print("| kernel | cycles | MFMA busy | TA busy | L2 hit | L2 read latency (cycles) | "
+              "TCP stalled on L2 |")
+        print("|---|---:|---:|---:|---:|---:|---:|")
+        for n, d in tab.items():
+            cyc = d.get("GRBM_GUI_ACTIVE", 0.0) / 8
+            mf = _ratio(d, "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", 1024 / 8)
+            ta = _ratio(d, "TA_TA_BUSY_sum", "GRBM_GUI_ACTIVE", 256 / 8)
+            hits, miss = d.get("TCC_HIT_sum"), d.get("TCC_MISS_sum")
+            hit = hits / (hits + miss) if hits is not None and miss is not None and hits + miss > 0 else None
+            lat = _ratio(d, "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum")
+            st = _ratio(d, "TCP_PENDING_STALL_CYCLES_sum", "GRBM_GUI_ACTIVE", 256 / 8)
+            f = lambda v, pct=True: "—" if v is None else (f"{100 * v:.0f}%" if pct else f"{v:.0f}")  # noqa: E731
+            print(f"| {n} | {cyc:.0f} | {f(mf)} | {f(ta)} | {f(hit)} | {f(lat, False)} | {f(st)} |")
+        print("\nRatios: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles); TA busy = TA_TA_BUSY_sum / "
+              "(256 x cycles); L2 hit = TCC_HIT / (TCC_HIT + TCC_MISS); L2 read latency = "
+              "TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum; TCP stalled on L2 = TCP_PENDING_STALL_CYCLES_sum "
+              "/ (256 x cycles).")
         return 0
     print(__doc__)
     return 2
