@@ -109,6 +109,16 @@ def test_replica_full_size_all_elements():
     ref, _ = compare_full(shape, W, x, to_np(r["logits"]), r, out, layer.ws_views(T), np.zeros(shape.E, F32),
                           with_hist=True)
     np.testing.assert_array_equal(to_np(layer.state_views()["hist"]), ref["hist"])
+    # the update's histogram quantiles (the state's q) against the exact,
+    # sort-based quantiles of the same scores: within one bin width
+    layer.qb_update()
+    torch.cuda.synchronize()
+    q = to_np(layer.state_views()["q"])
+    np.testing.assert_array_equal(q, o.qb_quantiles(ref["hist"], T, shape.k))
+    exact = np.array([o.exact_quantile(ref["s"][:, e], T, shape.k, shape.E) for e in range(shape.E)])
+    qerr = float(np.abs(q - exact).max())
+    say(f"  histogram quantile vs exact: max |q - q*| = {qerr:.5f} (bin width {1 / shape.B:.5f})")
+    assert qerr <= 1.0 / shape.B
     layer.close()
 
 
