@@ -349,6 +349,23 @@ moe_status moe_requantize_experts(moe_ctx* ctx, void* stream);
 moe_status moe_get_bias(moe_ctx* ctx, float* dst, void* stream);
 moe_status moe_set_bias(moe_ctx* ctx, const float* src, void* stream);
 
+/*
+ * Self-check of the routing kernels' shortcut.  To skip work, the top-k and
+ * histogram kernels first evaluate a fast router score (the same clamp, then
+ * the hardware exp2 and reciprocal) and compute the exact score of the
+ * "Stable LatentMoE" routing section (the specified sigmoid above) only where
+ * a decision could depend on it; each such decision keeps at least twice
+ * MOE_FAST_SCORE_ERR of room, so routing and histogram stay bit-identical to
+ * the exact definition while every fp32 logit gives |fast - exact| <=
+ * MOE_FAST_SCORE_ERR.  This call measures that difference on the device over
+ * all 2^32 fp32 bit patterns and writes the largest one to err[0] (one float
+ * of caller-owned device memory, overwritten).  Two launches on `stream`,
+ * about 10 ms; nothing is allocated.  MOE_ERR_INVALID_ARG for a NULL err,
+ * MOE_ERR_HIP if a launch fails.
+ */
+#define MOE_FAST_SCORE_ERR 0x1p-20f
+moe_status moe_fast_score_error(float* err, void* stream);
+
 /* Switch between training and frozen QB; the accumulated statistics are kept. */
 moe_status moe_set_qb_mode(moe_ctx* ctx, moe_qb_mode mode);
 

@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
             "qb_update": (c_int, [c_void_p, c_void_p]),
             "moe_requantize_experts": (c_int, [c_void_p, c_void_p]),
             "moe_get_bias": (c_int, [c_void_p, c_void_p, c_void_p]),
+            "moe_fast_score_error": (c_int, [c_void_p, c_void_p]),
             "moe_set_bias": (c_int, [c_void_p, c_void_p, c_void_p]),
             "moe_set_qb_mode": (c_int, [c_void_p, c_int]),
             "moe_destroy": (None, [c_void_p]),
@@ -170,6 +171,7 @@ def moe_forward(ctx: int, x: int, T: int, out: int, r: Optional[moe_route_out], 
 
 
 MOE_NOALLOC_SCRATCH_BYTES = 160 << 20
+MOE_FAST_SCORE_ERR = 2.0 ** -20  # bound on |fast - exact| router score that the routing kernels rely on
 
 
 def moe_forward_noalloc(ctx: int, x: int, T: int, out: int, r: Optional[moe_route_out], stream: int) -> None:
@@ -193,6 +195,10 @@ def moe_requantize_experts(ctx: int, stream: int) -> None:
 
 def qb_update(ctx: int, stream: int) -> None:
     check(lib().qb_update(ctx, stream), "qb_update")
+
+
+def moe_fast_score_error(err: int, stream: int) -> None:
+    check(lib().moe_fast_score_error(err, stream), "moe_fast_score_error")
 
 
 def moe_get_bias(ctx: int, dst: int, stream: int) -> None:

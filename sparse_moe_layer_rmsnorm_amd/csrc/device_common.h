@@ -57,6 +57,21 @@ MOE_DEV float router_sigmoid(float logit) {
   return 1.0f / (1.0f + e);
 }
 
+// Fast router score: the same clamp, then the hardware base-2 exponential
+// and reciprocal (v_exp_f32, v_rcp_f32).  It only decides where exact scores
+// are needed: every fp32 logit gives |fast_sigmoid - router_sigmoid| <=
+// kFastScoreErr (the library's moe_fast_score_error measures the largest
+// difference over all 2^32 inputs on the device), and each decision taken
+// from a fast score keeps a distance of at least twice that bound from the
+// point where the exact score could decide otherwise.
+constexpr float kFastScoreErr = 0x1p-20f;
+MOE_DEV float fast_sigmoid(float logit) {
+#pragma clang fp contract(off)
+  const float kLog2e = 0x1.715476p+0f;
+  const float y = -fminf(fmaxf(logit, -30.0f), 30.0f);
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y * kLog2e));
+}
+
 // Histogram bin of a score over the range [lo, lo + B / scale]:
 // clamp(floor(fp32(fp32(s - lo) * scale)), 0, B - 1), scale = fp32(B / (hi -
 // lo)); on [0, 1] this is min(B - 1, floor(s * B)) with s*B in fp32.  Scores
@@ -69,6 +84,23 @@ MOE_DEV int score_bin(float s, int B, float lo, float scale) {
   return (int)c;
 }
 
+// score_bin(router_sigmoid(logit), ...) computed from the fast score: when
+// no bin boundary (nor clamp edge) lies within dlt of the fast position x',
+// the exact position x = fp32(fp32(s - lo) * scale) falls in the same bin,
+// since |x' - x| <= kFastScoreErr * scale + 2^-22 |x| (the roundings of the
+// subtraction and the product); dlt keeps four times the first term and
+// eight times the second.  Otherwise the exact score decides.
+MOE_DEV int score_bin_fast(float logit, int B, float lo, float scale) {
+#pragma clang fp contract(off)
+  const float x = (fast_sigmoid(logit) - lo) * scale;
+  const float dlt = 4.0f * kFastScoreErr * scale + fabsf(x) * 0x1p-19f + 0x1p-19f;
+  const float top = (float)(B - 1);
+  const float a = fminf(fmaxf(floorf(x - dlt), 0.0f), top);
+  const float c = fminf(fmaxf(floorf(x + dlt), 0.0f), top);
+  if (a == c) return (int)a;
+  return score_bin(router_sigmoid(logit), B, lo, scale);
+}
+
 // Orderable key of an fp32 value: a larger float gives a larger key; -0 and
 // +0 give the same key.
 MOE_DEV uint32_t float_order_key(float v) {
@@ -76,6 +108,14 @@ MOE_DEV uint32_t float_order_key(float v) {
   if ((u << 1) == 0) u = 0;  // canonical +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+// Signed-integer order key of an fp32 value (a larger float gives a larger
+// int; -0 sorts just below +0), and its inverse (the map is an involution).
+MOE_DEV int32_t float_skey(float v) {
+  const int32_t u = __float_as_int(v);
+  return u ^ ((u >> 31) & 0x7FFFFFFF);
+}
+MOE_DEV float skey_float(int32_t k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
 
 // --------------------------------------------------------- wave helpers ----
 MOE_DEV float wave_sum(float v) {
@@ -129,6 +169,26 @@ MOE_DEV uint32_t wave_max_u32(uint32_t v) {
   const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 15), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
   const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 47), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
   return max(max(a, b), max(c, d));
+}
+
+// Minimum of a signed 32-bit value over the 64 lanes, wave-uniform.
+MOE_DEV int32_t wave_min_i32(int32_t v) {
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x111, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x112, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x114, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x118, 0xF, 0xF, false));
+  const int32_t a = __builtin_amdgcn_readlane(v, 15), b = __builtin_amdgcn_readlane(v, 31);
+  const int32_t c = __builtin_amdgcn_readlane(v, 47), d = __builtin_amdgcn_readlane(v, 63);
+  return min(min(a, b), min(c, d));
+}
+
+// Orders the LDS accesses of one wavefront around an exchange between its
+// lanes (a wavefront's LDS instructions execute in issue order, so only the
+// compiler has to be kept from moving them).
+MOE_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Blocks are handed to the 8 XCDs of the chip round-robin.  Map the

@@ -33,6 +33,9 @@ struct Dims {
   float qb_lo, qb_hi, qb_scale;  // histogram score range and fp32(B / (qb_hi - qb_lo))
 };
 
+// The largest |fast - exact| router score difference over all 2^32 fp32
+// logits, written (as a float) to out[0] on the device.
+hipError_t launch_fast_score_error(float* out, hipStream_t s);
 // RMSNorm; the launch also clears zero[0 .. nzero) (the super-chunk
 // selection counts the top-k launch of the same pass adds into).
 hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void* h, int T, hipStream_t s,

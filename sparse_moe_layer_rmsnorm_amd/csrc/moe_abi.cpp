@@ -827,6 +827,11 @@ moe_status moe_set_bias(moe_ctx* ctx, const float* src, void* stream) {
   return e == hipSuccess ? MOE_OK : fail(MOE_ERR_HIP, "bias copy failed: %s", hipGetErrorString(e));
 }
 
+moe_status moe_fast_score_error(float* err, void* stream) {
+  if (!err) return fail(MOE_ERR_INVALID_ARG, "destination is NULL");
+  return hip_ok(launch_fast_score_error(err, static_cast<hipStream_t>(stream)), "fast score check");
+}
+
 moe_status moe_set_qb_mode(moe_ctx* ctx, moe_qb_mode mode) {
   if (!ctx) return fail(MOE_ERR_INVALID_ARG, "context is NULL");
   if (mode != MOE_QB_TRAIN && mode != MOE_QB_FROZEN) return fail(MOE_ERR_INVALID_ARG, "unknown qb_mode");

@@ -13,8 +13,11 @@
 // raise their threshold).
 #include "device_common.h"
 #include "kernels.h"
+#include "moe.h"
 
 namespace moe {
+
+static_assert(kFastScoreErr == MOE_FAST_SCORE_ERR, "the documented fast-score bound is the kernels' bound");
 
 // ------------------------------------------------------------- RMSNorm ----
 // One wavefront per token row; h = (x * rstd) * gamma, rstd = 1/sqrt(mean(x^2)
@@ -130,7 +133,7 @@ hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void
 // selections leave as one 32-bit token mask per expert: bitmap[chunk][e] bit
 // t%32 is set iff token t picked e.
 template <int CPL, int NT>
-MOE_DEV void topk_tokens(const float* __restrict__ logits, const float (&b)[CPL], const int (&t)[NT], int E, int k,
+MOE_DEV void topk_tokens(const float* __restrict__ logits, const float* sb, const int (&t)[NT], int E, int k,
                          float scale, int32_t* __restrict__ idx, float* __restrict__ gates, uint32_t* mask) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
@@ -152,7 +155,7 @@ MOE_DEV void topk_tokens(const float* __restrict__ logits, const float (&b)[CPL]
       const int e = lane + 64 * c;
       if (e < E) {
         s[n][c] = router_sigmoid(s[n][c]);
-        key[n][c] = float_order_key(s[n][c] + b[c]);  // > 0 for any finite v
+        key[n][c] = float_order_key(s[n][c] + sb[e]);  // > 0 for any finite v
       } else {
         s[n][c] = 0.f;
         key[n][c] = 0u;
@@ -207,26 +210,169 @@ MOE_DEV void topk_tokens(const float* __restrict__ logits, const float (&b)[CPL]
     }
 }
 
+// Candidate filter in front of the exact ranking (same result as
+// topk_tokens, bit for bit).  With fast scores v' = fast_sigmoid(l) + b, let
+// tau be the k-th largest of the maxima of v' over G groups of 64/G lanes
+// (G >= 2k, fewer groups make tau cheaper to find): at least k experts have
+// v' >= tau, so the exact k-th largest v is >= tau - eps and every expert of
+// the exact top-k has v' >= tau - 2 eps (eps bounds |v' - v|).
+// The experts with v' >= tau - margin (margin >= 2 eps) are compacted into
+// the wavefront's LDS, one per lane, and only they get the exact score; each
+// candidate's slot is its rank among them by (exact key, lowest expert).
+// A token with more than 64 candidates (many equal scores) or fewer than k
+// (impossible while the error bound holds) takes the k-round path instead.
+struct TopkScratch {            // one token's exchange area in LDS
+  int32_t m[64];                // lane maxima of the fast keys; then the chosen scores in slot order
+  float cl[64];                 // candidates: logit
+  int32_t ce[64];               // candidates: expert
+  unsigned long long r[64];     // candidates: (exact key << 32) | ~expert
+};
+
+template <int CPL, int NT>
+MOE_DEV void topk_filter_tokens(const float* __restrict__ logits, const float* sb, const int (&t)[NT], int E,
+                                int k, float scale, int32_t* __restrict__ idx, float* __restrict__ gates,
+                                uint32_t* mask, TopkScratch* ts, bool (&fallback)[NT]) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  float l[NT][CPL];
+  int32_t q[NT][CPL];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const float* lr = logits + (size_t)t[n] * E;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int e = lane + 64 * c;
+      l[n][c] = e < E ? lr[e] : 0.f;
+    }
+  }
+  int32_t mx[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) mx[n] = INT32_MIN;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int e = lane + 64 * c;
+    const float bc = e < E ? sb[e] : 0.f;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      q[n][c] = e < E ? float_skey(fast_sigmoid(l[n][c]) + bc) : INT32_MIN;
+      mx[n] = max(mx[n], q[n][c]);
+    }
+  }
+  // group maxima: lanes 4g .. 4g+3 (G = 16), 2g, 2g+1 (G = 32) or each lane
+  const int G = k <= 8 ? 16 : k <= 16 ? 32 : 64;
+  const int gs = 64 / G;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    if (gs >= 2) mx[n] = max(mx[n], __builtin_amdgcn_update_dpp(mx[n], mx[n], 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    if (gs >= 4) mx[n] = max(mx[n], __builtin_amdgcn_update_dpp(mx[n], mx[n], 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    if ((lane & (gs - 1)) == 0) ts[n].m[lane / gs] = mx[n];
+  }
+  wave_lds_sync();
+  // tau: the smallest group maximum with fewer than k larger ones
+  int32_t thr[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    int cnt = 0;
+    for (int i = 0; i < G; i += 4) {
+      const int4 w = *reinterpret_cast<const int4*>(&ts[n].m[i]);
+      cnt += (w.x > mx[n]) + (w.y > mx[n]) + (w.z > mx[n]) + (w.w > mx[n]);
+    }
+    const int32_t tau = wave_min_i32(cnt < k ? mx[n] : INT32_MAX);
+    const float vt = skey_float(tau);
+    // margin: 2^-12 + 2^-16 |tau| >> 2 kFastScoreErr plus the roundings of v' and v
+    thr[n] = __builtin_isfinite(vt) ? float_skey(vt - (0x1p-12f + fabsf(vt) * 0x1p-16f)) : INT32_MIN + 1;
+  }
+  int C[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    int base = 0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const bool p = q[n][c] >= thr[n];
+      const unsigned long long bm = __ballot(p);
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+      if (p && pos < 64) {
+        ts[n].cl[pos] = l[n][c];
+        ts[n].ce[pos] = lane + 64 * c;
+      }
+      base += __popcll(bm);
+    }
+    C[n] = base;
+    fallback[n] = base < k || base > 64;
+  }
+  wave_lds_sync();
+  float s[NT];
+  int e[NT];
+  unsigned long long R[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    s[n] = 0.f;
+    e[n] = 0;
+    R[n] = 0ull;
+    if (!fallback[n] && lane < C[n]) {
+      e[n] = ts[n].ce[lane];
+      s[n] = router_sigmoid(ts[n].cl[lane]);
+      R[n] = ((unsigned long long)float_order_key(s[n] + sb[e[n]]) << 32) | (uint32_t)~e[n];
+    }
+    ts[n].r[lane] = R[n];  // lanes past the candidates write 0, below every real key
+  }
+  wave_lds_sync();
+  int rank[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    rank[n] = 0;
+    if (!fallback[n])
+      for (int i = 0; i < C[n]; i += 2) {
+        const ulonglong2 w = *reinterpret_cast<const ulonglong2*>(&ts[n].r[i]);
+        rank[n] += (w.x > R[n]) + (w.y > R[n]);
+      }
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+    if (!fallback[n] && lane < C[n] && rank[n] < k) ts[n].m[rank[n]] = __float_as_int(s[n]);
+  wave_lds_sync();
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    if (fallback[n]) continue;
+    float S = __int_as_float(ts[n].m[0]);  // the gates' denominator: fp32 sum in slot order
+    for (int j = 1; j < k; ++j) S = S + __int_as_float(ts[n].m[j]);
+    if (lane < C[n] && rank[n] < k) {
+      const size_t o = (size_t)t[n] * k + rank[n];
+      idx[o] = e[n];
+      gates[o] = (s[n] / S) * scale;
+      atomicOr(&mask[e[n]], 1u << (t[n] & 31));
+    }
+  }
+  wave_lds_sync();
+}
+
 #ifndef MOE_TOPK_NT
 #define MOE_TOPK_NT 2
 #endif
 constexpr int kTopkNT = MOE_TOPK_NT;                    // tokens ranked side by side per wavefront
 constexpr int kTopkThreads = kChunk / kTopkNT * 64;      // one token group per wavefront
 
+// Tokens a wavefront ranks side by side in the filter: two while their
+// registers leave room for two blocks per CU, else one after the other.
 template <int CPL>
-MOE_DEV void topk_block(int chunk, uint32_t* mask, const float* __restrict__ logits, const float* __restrict__ bias,
-                        int T, int E, int k, float scale, int32_t* __restrict__ idx, float* __restrict__ gates,
-                        uint32_t* __restrict__ bitmap, int32_t* __restrict__ ssum) {
+constexpr int topk_filter_nt() { return CPL >= 16 ? 1 : 2; }
+
+template <int CPL>
+MOE_DEV void topk_block(int chunk, uint32_t* mask, float* sb, TopkScratch* scratch, const float* __restrict__ logits,
+                        const float* __restrict__ bias, int T, int E, int k, float scale, int32_t* __restrict__ idx,
+                        float* __restrict__ gates, uint32_t* __restrict__ bitmap, int32_t* __restrict__ ssum) {
   constexpr int NW = kChunk / kTopkNT;
-  for (int i = threadIdx.x; i < E; i += kTopkThreads) mask[i] = 0u;
+  constexpr int NF = topk_filter_nt<CPL>();
+  static_assert(kTopkNT % NF == 0, "filter groups tile a wavefront's tokens");
+  for (int i = threadIdx.x; i < E; i += kTopkThreads) {
+    mask[i] = 0u;
+    sb[i] = bias[i];
+  }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float b[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int e = lane + 64 * c;
-    b[c] = e < E ? bias[e] : 0.f;
-  }
+  TopkScratch* ts = scratch + wave * kTopkNT;
   int t[kTopkNT];
   int n = 0;
 #pragma unroll
@@ -234,13 +380,36 @@ MOE_DEV void topk_block(int chunk, uint32_t* mask, const float* __restrict__ log
     t[u] = chunk * kChunk + wave + NW * u;
     n += t[u] < T;
   }
+  bool fb[kTopkNT];
   if (n == kTopkNT) {
-    topk_tokens<CPL, kTopkNT>(logits, b, t, E, k, scale, idx, gates, mask);
+#pragma unroll
+    for (int u0 = 0; u0 < kTopkNT; u0 += NF) {
+      int tg[NF];
+      bool fg[NF];
+#pragma unroll
+      for (int u = 0; u < NF; ++u) tg[u] = t[u0 + u];
+      topk_filter_tokens<CPL, NF>(logits, sb, tg, E, k, scale, idx, gates, mask, ts + u0, fg);
+#pragma unroll
+      for (int u = 0; u < NF; ++u) fb[u0 + u] = fg[u];
+    }
   } else {
+    for (int u = 0; u < kTopkNT; ++u) fb[u] = false;
     for (int u = 0; u < n; ++u) {  // ragged last chunk: one at a time
       const int t1[1] = {t[u]};
-      topk_tokens<CPL, 1>(logits, b, t1, E, k, scale, idx, gates, mask);
+      bool f1[1];
+      topk_filter_tokens<CPL, 1>(logits, sb, t1, E, k, scale, idx, gates, mask, ts, f1);
+      fb[u] = f1[0];
     }
+  }
+  bool any = false;
+#pragma unroll
+  for (int u = 0; u < kTopkNT; ++u) any |= fb[u];
+  if (any) {  // tokens with too many candidates: the k-round selection
+    for (int u = 0; u < kTopkNT; ++u)
+      if (fb[u]) {
+        const int t1[1] = {t[u]};
+        topk_tokens<CPL, 1>(logits, sb, t1, E, k, scale, idx, gates, mask);
+      }
   }
   __syncthreads();
   // the chunk's masks, and its counts added to its super-chunk's totals
@@ -277,11 +446,11 @@ MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict
     int t = tb + tl;
     for (; t + TR < te; t += 2 * TR) {
       const float l0 = logits[(size_t)t * E + e], l1 = logits[(size_t)(t + TR) * E + e];
-      atomicAdd(&row[score_bin(router_sigmoid(l0), B, lo, scale)], 1u);
-      atomicAdd(&row[score_bin(router_sigmoid(l1), B, lo, scale)], 1u);
+      atomicAdd(&row[score_bin_fast(l0, B, lo, scale)], 1u);
+      atomicAdd(&row[score_bin_fast(l1, B, lo, scale)], 1u);
     }
     for (; t < te; t += TR)
-      atomicAdd(&row[score_bin(router_sigmoid(logits[(size_t)t * E + e]), B, lo, scale)], 1u);
+      atomicAdd(&row[score_bin_fast(logits[(size_t)t * E + e], B, lo, scale)], 1u);
   }
   __syncthreads();
   if (tb < T) {  // integer atomics: the sums do not depend on the order of the token parts
@@ -298,7 +467,7 @@ MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict
 // training mode blocks past them build the QB histogram from the same
 // logits (independent work side by side instead of two launches).
 template <int CPL>
-__global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__ logits,
+__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_topk(const float* __restrict__ logits,
                                                        const float* __restrict__ bias, int T, int E, int k,
                                                        float scale, int32_t* __restrict__ idx,
                                                        float* __restrict__ gates, uint32_t* __restrict__ bitmap,
@@ -306,10 +475,13 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(const float* __restrict__
                                                        uint32_t* __restrict__ hist,
                                                        unsigned long long* __restrict__ count,
                                                        int32_t* __restrict__ ssum) {
-  __shared__ uint32_t smem[kHistExperts * 256];
-  static_assert(kHistExperts * 256 >= 1024, "the top-k masks fit");
+  constexpr int kTopkBytes = 2 * 1024 * 4 + kChunk * (int)sizeof(TopkScratch);  // masks, bias, exchange
+  constexpr int kHistBytes = kHistExperts * 256 * 4;
+  __shared__ __align__(16) uint32_t smem[(kTopkBytes > kHistBytes ? kTopkBytes : kHistBytes) / 4];
   if ((int)blockIdx.x < nchunks) {
-    topk_block<CPL>(blockIdx.x, smem, logits, bias, T, E, k, scale, idx, gates, bitmap, ssum);
+    topk_block<CPL>(blockIdx.x, smem, reinterpret_cast<float*>(smem + 1024),
+                    reinterpret_cast<TopkScratch*>(smem + 2048), logits, bias, T, E, k, scale, idx, gates, bitmap,
+                    ssum);
   } else {
     const int hb = blockIdx.x - nchunks, groups = (E + kHistExperts - 1) / kHistExperts;
     hist_block(hb % groups, hb / groups, smem, logits, T, E, B, lo, bscale, tps, hist, count);
@@ -341,7 +513,26 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
 // chunks') total per expert in sbase; the global scan below turns those into
 // first rows; the base of a chunk inside its super-chunk is summed by the
 // scatter from the masks themselves.
-// Global (one block of 1024 threads, one expert per thread): per expert, the
+// Super-chunks [s0, s1) of expert e: each total in sbase becomes the first
+// row of its part of the expert's group, counting on from `run` (16 loads
+// issued before their stores: the compiler cannot tell that the stores do
+// not alias the next loads).
+MOE_DEV void prefix_rows(int32_t* __restrict__ sbase, int E, int e, int s0, int s1, int run) {
+  for (int sc0 = s0; sc0 < s1; sc0 += 16) {
+    int x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) x[u] = sc0 + u < s1 ? sbase[(size_t)(sc0 + u) * E + e] : 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (sc0 + u < s1) {
+        sbase[(size_t)(sc0 + u) * E + e] = run;
+        run += x[u];
+      }
+  }
+}
+
+// Global (one block of 1024 threads, one expert per thread, or several when
+// there are more super-chunks than registers and few experts): per expert, the
 // total and the exclusive prefix over super-chunks (sbase becomes the
 // absolute first row of each super-chunk's part of the expert's group); over
 // experts, the row offsets and the first m-tile of each expert for the grouped
@@ -357,24 +548,45 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
   __shared__ int wsum_r[16], wsum_t[16], wsum_u[16];
   // per expert (E <= 1024): first row, count, inclusive tile prefixes of both tables
   __shared__ int s_row0[1024], s_cnt[1024], s_t[1024], s_u[1024];
+  __shared__ int s_part[1024];  // many super-chunks: each thread's partial sum
   constexpr int kReg = 16;  // up to this many super-chunk totals stay in registers
   const int i = threadIdx.x, lane = i & 63, w = i >> 6;
   // at most 8 tiles of kExpertBM rows per expert on average: one thread per
   // expert writes its tiles (cheaper than a block-wide pass at these sizes)
   const bool few = (long long)T * k <= 8LL * kExpertBM * E;
+  // More super-chunks than registers and E <= 512: P threads per expert
+  // (P E <= 1024), thread i takes expert i % E and the P-th part i / E of its
+  // super-chunks, so that P times more loads are in flight.
+  int P = 1;
+  while (2 * P * E <= 1024) P *= 2;
+  const bool split = nsuper > kReg && P > 1;
+  const int part = i / E, pe = i - part * E;
+  const int pm = (nsuper + P - 1) / P, ps0 = min(nsuper, part * pm), ps1 = min(nsuper, ps0 + pm);
   int c = 0;
   int v[kReg];
-  if (i < E) {
-    if (nsuper <= kReg) {
+  if (!split) {
+    if (i < E) {
+      if (nsuper <= kReg) {
 #pragma unroll
-      for (int sc = 0; sc < kReg; ++sc) {
-        v[sc] = sc < nsuper ? sbase[(size_t)sc * E + i] : 0;
-        c += v[sc];
-      }
-    } else {
+        for (int sc = 0; sc < kReg; ++sc) {
+          v[sc] = sc < nsuper ? sbase[(size_t)sc * E + i] : 0;
+          c += v[sc];
+        }
+      } else {
 #pragma unroll 16
-      for (int sc = 0; sc < nsuper; ++sc) c += sbase[(size_t)sc * E + i];
+        for (int sc = 0; sc < nsuper; ++sc) c += sbase[(size_t)sc * E + i];
+      }
     }
+  } else {
+    int ps = 0;
+    if (part < P) {
+#pragma unroll 16
+      for (int sc = ps0; sc < ps1; ++sc) ps += sbase[(size_t)sc * E + pe];
+    }
+    s_part[i] = ps;
+    __syncthreads();
+    if (i < E)
+      for (int q = 0; q < P; ++q) c += s_part[q * E + i];
   }
   const int tl = (c + kExpertBM - 1) / kExpertBM, tl2 = (c + kExpertBM2 - 1) / kExpertBM2;
   int r = c, t = tl, u = tl2;  // inclusive wave scans
@@ -410,14 +622,8 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
         if (sc < nsuper) sbase[(size_t)sc * E + i] = run;
         run += v[sc];
       }
-    } else {
-#pragma unroll 16
-      for (int sc = 0; sc < nsuper; ++sc) {
-        const size_t j = (size_t)sc * E + i;
-        const int x = sbase[j];
-        sbase[j] = run;
-        run += x;
-      }
+    } else if (!split) {
+      prefix_rows(sbase, E, i, 0, nsuper, run);
     }
     s_row0[i] = r - c;
     s_cnt[i] = c;
@@ -437,6 +643,14 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
     tile_offsets[0] = 0;
     if (tile_offsets2) tile_offsets2[0] = 0;
     if (load) *count += (unsigned long long)T;
+  }
+  if (split) {
+    __syncthreads();
+    if (part < P) {  // each part's super-chunks become first rows, from its base
+      int run = s_row0[pe];
+      for (int q = 0; q < part; ++q) run += s_part[q * E + pe];
+      prefix_rows(sbase, E, pe, ps0, ps1, run);
+    }
   }
   if (few) return;
   __syncthreads();
@@ -706,6 +920,29 @@ hipError_t launch_sign_bias(const Dims& D, uint32_t* load, unsigned long long* c
 // ----------------------------------------------------------------- fill ----
 // Zero a 16-byte-aligned region whose size is a multiple of 16 (a kernel
 // rather than a memset node, so that the call is safe under graph capture).
+// Largest |fast_sigmoid - router_sigmoid| over every fp32 bit pattern,
+// kept as the bits of a non-negative float (their integer order is the
+// float order), so the maximum does not depend on the order of the blocks.
+__global__ __launch_bounds__(256) void k_fast_score_error(uint32_t* __restrict__ out) {
+  uint32_t m = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * 256u;
+  for (uint64_t u = (uint64_t)blockIdx.x * 256u + threadIdx.x; u < (1ull << 32); u += stride) {
+    const float l = __uint_as_float((uint32_t)u);
+    m = max(m, __float_as_uint(fabsf(fast_sigmoid(l) - router_sigmoid(l))));
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(out, m);
+}
+
+__global__ void k_set_u32(uint32_t* __restrict__ p, uint32_t v) { *p = v; }
+
+hipError_t launch_fast_score_error(float* out, hipStream_t s) {
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);
+  hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(1), 0, s, o, 0u);
+  hipLaunchKernelGGL(k_fast_score_error, dim3(8192), dim3(256), 0, s, o);
+  return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void k_zero(uint4* __restrict__ p, size_t n16) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
     p[i] = make_uint4(0, 0, 0, 0);

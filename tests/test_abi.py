@@ -215,3 +215,12 @@ def test_noalloc_scratch_size_matches_header():
     assert m and int(m.group(1)) << int(m.group(2)) == B.MOE_NOALLOC_SCRATCH_BYTES
     cfg = B.make_config(**REPLICA, max_tokens=16384)
     assert B.moe_workspace_bytes(cfg, 8192) <= B.MOE_NOALLOC_SCRATCH_BYTES < B.moe_workspace_bytes(cfg, 16384)
+
+
+def test_fast_score_bound_constant():
+    """The binding's copy of MOE_FAST_SCORE_ERR is the header's."""
+    import re
+    text = open(B.HEADER).read()
+    m = re.search(r"#define MOE_FAST_SCORE_ERR 0x1p-(\d+)f", text)
+    assert m and 2.0 ** -int(m.group(1)) == B.MOE_FAST_SCORE_ERR
+

@@ -27,9 +27,12 @@ CASES = [  # (E, k, T, logit scale, bias scale)
     (256, 6, 4097, 3.0, 0.05),     # ragged tail
     (896, 16, 2048, 1.0, 0.05),    # K3 routing shape
     (100, 7, 333, 2.0, 0.2),       # E not a multiple of 64
+    (384, 8, 1500, 1.0, 0.05),     # 8 columns per lane
     (8, 8, 130, 1.0, 0.0),         # k = E
     (64, 1, 1, 1.0, 0.0),          # one token
     (1024, 32, 700, 1.0, 0.01),    # largest E and k
+    (256, 6, 16384, 1.0, 0.05),    # 32 super-chunks: the scan splits each expert's over 4 threads
+    (48, 3, 30000, 1.5, 0.1),      # 59 super-chunks over 16 threads per expert, one part empty
 ]
 
 
@@ -69,6 +72,97 @@ def test_sigmoid_bitexact_sweep():
     ref = oracle_routing(logits, np.zeros(E, F32), k, E, shape.B)
     assert_routing_equal(r, ref, T)
     np.testing.assert_array_equal(to_np(layer.state_views()["hist"]), ref["hist"])
+    layer.close()
+
+
+def test_fast_score_error_bound():
+    """The routing kernels filter with a fast router score (hardware exp2 and
+    reciprocal) and compute the exact one only where a decision could depend
+    on it; that is exact only while |fast - exact| <= MOE_FAST_SCORE_ERR for
+    every fp32 logit, which the library measures over all 2^32 of them."""
+    say("fast score error over all fp32 logits")
+    from sparse_moe_layer_rmsnorm_amd import binding as B
+    err = torch.full((4,), -1.0, dtype=torch.float32, device="cuda")
+    B.moe_fast_score_error(err.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    e = float(err[0].item())
+    say(f"  max |fast - exact| = {e:.3e} (bound {B.MOE_FAST_SCORE_ERR:.3e})")
+    assert 0.0 <= e <= B.MOE_FAST_SCORE_ERR
+
+
+NEAR_TIE_CASES = [  # (E, k, T, kind)
+    (896, 16, 512, "cluster"),   # K3 routing shape
+    (256, 6, 1024, "cluster"),   # replica shape
+    (100, 7, 257, "cluster"),    # E not a multiple of 64, ragged chunk
+    (500, 12, 700, "cluster"),   # 8 columns per lane
+    (256, 6, 300, "equal"),      # every expert a candidate: more than 64
+    (896, 16, 65, "equal"),
+    (64, 8, 256, "equal"),       # 64 candidates, all tied
+    (256, 6, 512, "coarse"),     # logits on a grid of 1/4: many exact ties
+]
+
+
+@pytest.mark.parametrize("E,k,T,kind", NEAR_TIE_CASES)
+def test_route_near_ties_bitexact(E, k, T, kind):
+    """Scores closer together than the fast score resolves.  "cluster": per
+    token 2k + 8 random experts get logits within 3 fp32 ulps of 2.0, above
+    the rest, so the top-k cut falls inside the cluster and only the exact
+    scores (and the lower index on exact ties) order it; "equal": half the
+    rows hold one logit everywhere (the exact ranking sees every expert);
+    "coarse": logits rounded to quarters.  Routing must still equal the
+    oracle's bit for bit."""
+    say(f"near ties E={E} k={k} T={T} {kind}")
+    rng = np.random.default_rng(E * 3 + T)
+    logits = (rng.standard_normal((T, E)) * 0.5).astype(F32)
+    bias = np.zeros(E, F32)
+    if kind == "cluster":
+        n = min(E, 2 * k + 8)
+        base = np.array([2.0], F32).view(np.int32)[0]
+        for t in range(T):
+            sel = rng.choice(E, size=n, replace=False)
+            logits[t, sel] = (base + rng.integers(-3, 4, n).astype(np.int32)).view(F32)
+    elif kind == "equal":
+        logits[::2] = F32(0.75)
+        bias = (rng.standard_normal(E) * 0.05).astype(F32)
+        bias[:] = bias[0]                      # equal biases keep the rows tied
+    else:
+        logits = (np.round(logits * 4) / 4).astype(F32)
+    shape = _shape(E, k)
+    layer = make_layer(shape, wl.make_weights(shape), max_tokens=T)
+    layer.set_bias(bias)
+    r = layer.route(T, logits=torch.from_numpy(logits).cuda())
+    torch.cuda.synchronize()
+    ref = oracle_routing(logits, bias, k, E, shape.B)
+    assert_routing_equal(r, ref, T)
+    np.testing.assert_array_equal(to_np(layer.state_views()["hist"]), ref["hist"])
+    layer.close()
+
+
+@pytest.mark.parametrize("lo,hi,B", [(0.0, 1.0, 256), (0.3, 0.9, 100)])
+def test_histogram_at_bin_edges_bitexact(lo, hi, B):
+    """Scores within a few ulps of every bin edge, where the fast score cannot
+    place them and the exact score must decide: the histogram must equal the
+    oracle's bit for bit."""
+    say(f"histogram bin edges [{lo}, {hi}] B={B}")
+    E, k = 64, 2
+    p = lo + (hi - lo) * np.arange(1, B) / B
+    p = p[(p > 0) & (p < 1)]
+    l0 = np.log(p / (1 - p)).astype(F32)
+    cols, up, down = [l0], l0, l0
+    for _ in range(6):                         # the 6 fp32 neighbours on each side
+        up, down = np.nextafter(up, F32(np.inf)), np.nextafter(down, F32(-np.inf))
+        cols += [up, down]
+    vals = np.stack(cols, axis=1).ravel()
+    T = -(-vals.size // E)
+    rng = np.random.default_rng(B)
+    logits = rng.permutation(np.resize(vals, T * E)).reshape(T, E).astype(F32)
+    shape = _shape(E, k, B=B)
+    layer = make_layer(shape, wl.make_weights(shape), max_tokens=T, qb_lo=lo, qb_hi=hi)
+    r = layer.route(T, logits=torch.from_numpy(logits).cuda())
+    torch.cuda.synchronize()
+    ref = oracle_routing(logits, np.zeros(E, F32), k, E, B)
+    assert_routing_equal(r, ref, T)
+    np.testing.assert_array_equal(to_np(layer.state_views()["hist"]), o.histogram(ref["s"], B, lo, hi))
     layer.close()
 
 
