@@ -422,6 +422,153 @@ MOE_DEV void topk_block(int chunk, uint32_t* mask, float* sb, TopkScratch* scrat
   }
 }
 
+// Row layout for E <= 256 and k <= 8: a token per row of 16 lanes (a DPP
+// row), so one wavefront runs the filter for four tokens at once and the
+// per-token steps (threshold, exact scores, ranking, gates) are shared four
+// ways.  Lane li of row r holds experts li + 16 c; the groups of the
+// threshold are the 16 lanes of the row (16 >= 2k); at most 16 candidates
+// per token (the lanes of its row), else that token takes the k-round path.
+// Same result as topk_tokens, bit for bit.
+constexpr int kRowMaxK = 8;
+
+MOE_DEV int32_t row_bcast15(int32_t v) { return __shfl(v, (threadIdx.x & 48) | 15, 64); }
+
+template <int CPR>
+MOE_DEV bool topk_row_tokens(const float* __restrict__ logits, const float* sb, int t, bool valid, int E, int k,
+                             float scale, int32_t* __restrict__ idx, float* __restrict__ gates, uint32_t* mask,
+                             TopkScratch* ws) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63, li = lane & 15, rb = lane & 48;
+  float l[CPR];
+  int32_t q[CPR];
+  int32_t mx = INT32_MIN;
+#pragma unroll
+  for (int c = 0; c < CPR; ++c) {
+    const int e = li + 16 * c;
+    const bool ok = valid && e < E;
+    l[c] = ok ? logits[(size_t)t * E + e] : 0.f;
+  }
+#pragma unroll
+  for (int c = 0; c < CPR; ++c) {
+    const int e = li + 16 * c;
+    q[c] = (valid && e < E) ? float_skey(fast_sigmoid(l[c]) + sb[e]) : INT32_MIN;
+    mx = max(mx, q[c]);
+  }
+  ws->m[lane] = mx;
+  wave_lds_sync();
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 16; i += 4) {
+    const int4 w = *reinterpret_cast<const int4*>(&ws->m[rb + i]);
+    cnt += (w.x > mx) + (w.y > mx) + (w.z > mx) + (w.w > mx);
+  }
+  // the row's smallest lane maximum with fewer than k larger ones (prefix
+  // minimum over the row by DPP row shifts, then lane 15 of the row)
+  int32_t tau = cnt < k ? mx : INT32_MAX;
+  tau = min(tau, __builtin_amdgcn_update_dpp(tau, tau, 0x111, 0xF, 0xF, false));
+  tau = min(tau, __builtin_amdgcn_update_dpp(tau, tau, 0x112, 0xF, 0xF, false));
+  tau = min(tau, __builtin_amdgcn_update_dpp(tau, tau, 0x114, 0xF, 0xF, false));
+  tau = min(tau, __builtin_amdgcn_update_dpp(tau, tau, 0x118, 0xF, 0xF, false));
+  tau = row_bcast15(tau);
+  const float vt = skey_float(tau);
+  const int32_t thr = __builtin_isfinite(vt) ? float_skey(vt - (0x1p-12f + fabsf(vt) * 0x1p-16f)) : INT32_MIN + 1;
+  // compaction: each lane's candidates after those of the lanes before it in the row
+  int n = 0;
+#pragma unroll
+  for (int c = 0; c < CPR; ++c) n += q[c] >= thr;
+  int incl = n;
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, false);
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, false);
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, false);
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, false);
+  const int C = row_bcast15(incl);
+  const bool fb = valid && (C < k || C > 16);
+  const bool act = valid && !fb;
+  if (act) {
+    int pos = rb + incl - n;
+#pragma unroll
+    for (int c = 0; c < CPR; ++c)
+      if (q[c] >= thr) {
+        ws->cl[pos] = l[c];
+        ws->ce[pos] = li + 16 * c;
+        ++pos;
+      }
+  }
+  wave_lds_sync();
+  const bool mine = act && li < C;  // this lane scores candidate li of its row
+  float sv = 0.f;
+  int ev = 0;
+  unsigned long long R = 0ull;
+  if (mine) {
+    ev = ws->ce[lane];
+    sv = router_sigmoid(ws->cl[lane]);
+    R = ((unsigned long long)float_order_key(sv + sb[ev]) << 32) | (uint32_t)~ev;
+  }
+  ws->r[lane] = R;  // zero past the candidates: below every real key
+  wave_lds_sync();
+  const int cw = act ? C : 0;
+  const int cmax = max(max(__builtin_amdgcn_readlane(cw, 15), __builtin_amdgcn_readlane(cw, 31)),
+                       max(__builtin_amdgcn_readlane(cw, 47), __builtin_amdgcn_readlane(cw, 63)));
+  int rank = 0;
+  for (int i = 0; i < cmax; i += 2) {
+    const ulonglong2 w = *reinterpret_cast<const ulonglong2*>(&ws->r[rb + i]);
+    rank += (w.x > R) + (w.y > R);
+  }
+  wave_lds_sync();
+  if (mine && rank < k) ws->m[rb + rank] = __float_as_int(sv);
+  wave_lds_sync();
+  if (mine && rank < k) {
+    float S = __int_as_float(ws->m[rb]);  // the gates' denominator: fp32 sum in slot order
+    for (int j = 1; j < k; ++j) S = S + __int_as_float(ws->m[rb + j]);
+    const size_t o = (size_t)t * k + rank;
+    idx[o] = ev;
+    gates[o] = (sv / S) * scale;
+    atomicOr(&mask[ev], 1u << (t & 31));
+  }
+  wave_lds_sync();
+  return fb;
+}
+
+// Block of the row layout: two chunks, eight wavefronts each, four tokens
+// per wavefront.
+template <int CPL>
+MOE_DEV void topk_row_block(int pair, uint32_t* mask2, float* sb, TopkScratch* scratch,
+                            const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
+                            float scale, int32_t* __restrict__ idx, float* __restrict__ gates,
+                            uint32_t* __restrict__ bitmap, int32_t* __restrict__ ssum, int nchunks) {
+  constexpr int CPR = 4 * CPL;
+  for (int i = threadIdx.x; i < E; i += kTopkThreads) {
+    mask2[i] = 0u;
+    mask2[E + i] = 0u;
+    sb[i] = bias[i];
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = wave >> 3;                    // which chunk of the pair
+  const int chunk = 2 * pair + half;
+  uint32_t* mask = mask2 + half * E;
+  const int t = chunk * kChunk + (wave & 7) * 4 + (lane >> 4);
+  const bool valid = chunk < nchunks && t < T;
+  const bool fb = topk_row_tokens<CPR>(logits, sb, t, valid, E, k, scale, idx, gates, mask, scratch + wave);
+  const unsigned long long fbm = __ballot(fb && (lane & 15) == 0);
+  for (int r = 0; r < 4; ++r)  // tokens with more than 16 candidates: the k-round selection
+    if ((fbm >> (16 * r)) & 1ull) {
+      const int t1[1] = {chunk * kChunk + (wave & 7) * 4 + r};
+      topk_tokens<CPL, 1>(logits, sb, t1, E, k, scale, idx, gates, mask);
+    }
+  __syncthreads();
+  for (int hh = 0; hh < 2; ++hh) {
+    const int c = 2 * pair + hh;
+    if (c >= nchunks) break;
+    int32_t* sdst = ssum + (size_t)(c / kSuper) * E;
+    for (int i = threadIdx.x; i < E; i += kTopkThreads) {
+      const uint32_t m = mask2[hh * E + i];
+      bitmap[(size_t)c * E + i] = m;
+      if (m) atomicAdd(&sdst[i], __popc(m));
+    }
+  }
+}
+
 // ---------------------------------------------------------- QB histogram ----
 // The state keeps one histogram [E][B].  Block (16-expert group, token part)
 // counts its part's score bins in LDS with integer atomics and adds them to
@@ -463,10 +610,12 @@ MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict
   if (group == 0 && ts == 0 && threadIdx.x == 0) *count += (unsigned long long)T;
 }
 
-// One launch for the scores: blocks [0, nchunks) rank the chunks; in
-// training mode blocks past them build the QB histogram from the same
-// logits (independent work side by side instead of two launches).
-template <int CPL>
+// One launch for the scores: the last nchunks blocks rank the chunks; in
+// training mode the blocks before them build the QB histogram from the same
+// logits (independent work side by side instead of two launches; the fewer,
+// longer histogram blocks are dispatched first so that they overlap the
+// ranking instead of trailing it).
+template <int CPL, bool ROW>
 __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_topk(const float* __restrict__ logits,
                                                        const float* __restrict__ bias, int T, int E, int k,
                                                        float scale, int32_t* __restrict__ idx,
@@ -478,13 +627,20 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8)
   constexpr int kTopkBytes = 2 * 1024 * 4 + kChunk * (int)sizeof(TopkScratch);  // masks, bias, exchange
   constexpr int kHistBytes = kHistExperts * 256 * 4;
   __shared__ __align__(16) uint32_t smem[(kTopkBytes > kHistBytes ? kTopkBytes : kHistBytes) / 4];
-  if ((int)blockIdx.x < nchunks) {
-    topk_block<CPL>(blockIdx.x, smem, reinterpret_cast<float*>(smem + 1024),
-                    reinterpret_cast<TopkScratch*>(smem + 2048), logits, bias, T, E, k, scale, idx, gates, bitmap,
-                    ssum);
+  const int nrank = ROW ? (nchunks + 1) / 2 : nchunks;
+  const int nhist = (int)gridDim.x - nrank;
+  if ((int)blockIdx.x >= nhist) {
+    if (ROW)
+      topk_row_block<CPL>(blockIdx.x - nhist, smem, reinterpret_cast<float*>(smem + 1024),
+                          reinterpret_cast<TopkScratch*>(smem + 2048), logits, bias, T, E, k, scale, idx, gates,
+                          bitmap, ssum, nchunks);
+    else
+      topk_block<CPL>(blockIdx.x - nhist, smem, reinterpret_cast<float*>(smem + 1024),
+                      reinterpret_cast<TopkScratch*>(smem + 2048), logits, bias, T, E, k, scale, idx, gates, bitmap,
+                      ssum);
   } else {
-    const int hb = blockIdx.x - nchunks, groups = (E + kHistExperts - 1) / kHistExperts;
-    hist_block(hb % groups, hb / groups, smem, logits, T, E, B, lo, bscale, tps, hist, count);
+    const int groups = (E + kHistExperts - 1) / kHistExperts;
+    hist_block(blockIdx.x % groups, blockIdx.x / groups, smem, logits, T, E, B, lo, bscale, tps, hist, count);
   }
 }
 
@@ -494,15 +650,16 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
   const int cpl = (D.E + 63) / 64;
   const int tps = (T + kHistParts - 1) / kHistParts;
   const int hblocks = hist ? (D.E + kHistExperts - 1) / kHistExperts * kHistParts : 0;
-  dim3 grid(nchunks + hblocks), block(kTopkThreads);
-#define MOE_TOPK(C)                                                                                                 \
-  hipLaunchKernelGGL(k_topk<C>, grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, bitmap, \
-                     nchunks, D.B, D.qb_lo, D.qb_scale, tps, hist, count, ssum)
-  if (cpl <= 1) MOE_TOPK(1);
-  else if (cpl <= 2) MOE_TOPK(2);
-  else if (cpl <= 4) MOE_TOPK(4);
-  else if (cpl <= 8) MOE_TOPK(8);
-  else MOE_TOPK(16);
+  const bool row = cpl <= 4 && D.k <= kRowMaxK;  // E <= 256: four tokens per wavefront
+  dim3 grid((row ? (nchunks + 1) / 2 : nchunks) + hblocks), block(kTopkThreads);
+#define MOE_TOPK(C, R)                                                                                          \
+  hipLaunchKernelGGL((k_topk<C, R>), grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, \
+                     bitmap, nchunks, D.B, D.qb_lo, D.qb_scale, tps, hist, count, ssum)
+  if (cpl <= 1) { if (row) MOE_TOPK(1, true); else MOE_TOPK(1, false); }
+  else if (cpl <= 2) { if (row) MOE_TOPK(2, true); else MOE_TOPK(2, false); }
+  else if (cpl <= 4) { if (row) MOE_TOPK(4, true); else MOE_TOPK(4, false); }
+  else if (cpl <= 8) MOE_TOPK(8, false);
+  else MOE_TOPK(16, false);
 #undef MOE_TOPK
   return hipGetLastError();
 }
@@ -729,7 +886,8 @@ hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bit
 // -------------------------------------------------------------- combine ----
 // y_lat[t] = sum_j g[t,j] Y[inv[t,j]] in slot order, fp32, stored in the
 // activation dtype.  One wavefront per token; lane c handles 4 latent
-// columns per 4*64-column stripe.
+// columns per 4*64-column stripe, with the row loads of up to 8 slots in
+// flight before they are summed (in slot order).
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ Y, const float* __restrict__ gates,
                                                  const int32_t* __restrict__ inv, int T, int l, int k,
@@ -745,24 +903,45 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ Y, con
     if ((unsigned)my_row >= (unsigned)(T * k)) my_row = 0;  // never taken for a consistent permutation
   }
   const int nq = l / 4;  // groups of 4 columns
+  constexpr int J = 8;   // slots whose row loads are in flight together
   for (int q = lane; q < nq; q += 64) {
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int j = 0; j < k; ++j) {
+    for (int j0 = 0; j0 < k; j0 += J) {
       // readlane, not a shuffle: lanes past l/4 are inactive in this loop
-      const int row = __builtin_amdgcn_readlane(my_row, j);
-      const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), j));
       if (BF16) {
-        const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(Y) + (size_t)row * l + 4 * q);
-        a0 += g * bf16_bits_to_f32(v.x & 0xFFFFu);
-        a1 += g * bf16_bits_to_f32(v.x >> 16);
-        a2 += g * bf16_bits_to_f32(v.y & 0xFFFFu);
-        a3 += g * bf16_bits_to_f32(v.y >> 16);
+        uint2 v[J];
+#pragma unroll
+        for (int u = 0; u < J; ++u)
+          if (j0 + u < k) {
+            const int row = __builtin_amdgcn_readlane(my_row, j0 + u);
+            v[u] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(Y) + (size_t)row * l + 4 * q);
+          }
+#pragma unroll
+        for (int u = 0; u < J; ++u)
+          if (j0 + u < k) {
+            const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), j0 + u));
+            a0 += g * bf16_bits_to_f32(v[u].x & 0xFFFFu);
+            a1 += g * bf16_bits_to_f32(v[u].x >> 16);
+            a2 += g * bf16_bits_to_f32(v[u].y & 0xFFFFu);
+            a3 += g * bf16_bits_to_f32(v[u].y >> 16);
+          }
       } else {
-        const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(Y) + (size_t)row * l + 4 * q);
-        a0 += g * v.x;
-        a1 += g * v.y;
-        a2 += g * v.z;
-        a3 += g * v.w;
+        float4 v[J];
+#pragma unroll
+        for (int u = 0; u < J; ++u)
+          if (j0 + u < k) {
+            const int row = __builtin_amdgcn_readlane(my_row, j0 + u);
+            v[u] = *reinterpret_cast<const float4*>(static_cast<const float*>(Y) + (size_t)row * l + 4 * q);
+          }
+#pragma unroll
+        for (int u = 0; u < J; ++u)
+          if (j0 + u < k) {
+            const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), j0 + u));
+            a0 += g * v[u].x;
+            a1 += g * v[u].y;
+            a2 += g * v[u].z;
+            a3 += g * v[u].w;
+          }
       }
     }
     if (BF16) {

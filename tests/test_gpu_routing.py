@@ -93,6 +93,8 @@ def test_fast_score_error_bound():
 NEAR_TIE_CASES = [  # (E, k, T, kind)
     (896, 16, 512, "cluster"),   # K3 routing shape
     (256, 6, 1024, "cluster"),   # replica shape
+    (256, 6, 1024, "tight"),     # replica shape, cluster of k + 4: ranked among at most 16 candidates
+    (128, 8, 700, "tight"),
     (100, 7, 257, "cluster"),    # E not a multiple of 64, ragged chunk
     (500, 12, 700, "cluster"),   # 8 columns per lane
     (256, 6, 300, "equal"),      # every expert a candidate: more than 64
@@ -107,7 +109,8 @@ def test_route_near_ties_bitexact(E, k, T, kind):
     """Scores closer together than the fast score resolves.  "cluster": per
     token 2k + 8 random experts get logits within 3 fp32 ulps of 2.0, above
     the rest, so the top-k cut falls inside the cluster and only the exact
-    scores (and the lower index on exact ties) order it; "equal": half the
+    scores (and the lower index on exact ties) order it ("tight": k + 4 such
+    experts, few enough for the 16-lane row layout); "equal": half the
     rows hold one logit everywhere (the exact ranking sees every expert);
     "coarse": logits rounded to quarters.  Routing must still equal the
     oracle's bit for bit."""
@@ -115,8 +118,8 @@ def test_route_near_ties_bitexact(E, k, T, kind):
     rng = np.random.default_rng(E * 3 + T)
     logits = (rng.standard_normal((T, E)) * 0.5).astype(F32)
     bias = np.zeros(E, F32)
-    if kind == "cluster":
-        n = min(E, 2 * k + 8)
+    if kind in ("cluster", "tight"):
+        n = min(E, 2 * k + 8 if kind == "cluster" else k + 4)
         base = np.array([2.0], F32).view(np.int32)[0]
         for t in range(T):
             sel = rng.choice(E, size=n, replace=False)
