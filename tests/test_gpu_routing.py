@@ -33,6 +33,8 @@ CASES = [  # (E, k, T, logit scale, bias scale)
     (1024, 32, 700, 1.0, 0.01),    # largest E and k
     (256, 6, 16384, 1.0, 0.05),    # 32 super-chunks: the scan splits each expert's over 4 threads
     (48, 3, 30000, 1.5, 0.1),      # 59 super-chunks over 16 threads per expert, one part empty
+    (256, 6, 2000, 1.0, 300.0),    # |b| >> s: v = s + b spaced by ulps of a few hundred, many negative
+    (896, 16, 1000, 1.0, 40.0),
 ]
 
 
