@@ -422,35 +422,56 @@ MOE_DEV void topk_block(int chunk, uint32_t* mask, float* sb, TopkScratch* scrat
   }
 }
 
-// Row layout for E <= 256 and k <= 8: a token per row of 16 lanes (a DPP
-// row), so one wavefront runs the filter for four tokens at once and the
-// per-token steps (threshold, exact scores, ranking, gates) are shared four
-// ways.  Lane li of row r holds experts li + 16 c; the groups of the
-// threshold are the 16 lanes of the row (16 >= 2k); at most 16 candidates
-// per token (the lanes of its row), else that token takes the k-round path.
-// Same result as topk_tokens, bit for bit.
-constexpr int kRowMaxK = 8;
+// Group layout for E <= 16 GL and k <= GL / 2: a token per group of GL = 16
+// lanes (a DPP row; four tokens per wavefront) or 32 lanes (two per
+// wavefront), so the per-token steps (threshold, exact scores, ranking,
+// gates) are shared by the wavefront's tokens.  Lane li of a group holds
+// experts li + GL c; the groups of the threshold are the GL lanes of the
+// token (GL >= 2k); at most GL candidates per token (one per lane of its
+// group), else that token takes the k-round path.  Same result as
+// topk_tokens, bit for bit.
+template <int GL>
+constexpr int group_max_k() { return GL / 2; }
 
-MOE_DEV int32_t row_bcast15(int32_t v) { return __shfl(v, (threadIdx.x & 48) | 15, 64); }
+// Inclusive prefix (sum, or minimum with MIN) over the GL lanes of each group:
+// DPP row shifts within 16-lane rows, then one shuffle across the two rows of
+// a 32-lane group.
+template <int GL, bool MIN>
+MOE_DEV int32_t group_scan(int32_t v) {
+  const int32_t id = MIN ? INT32_MAX : 0;
+  auto op = [](int32_t a, int32_t b) { return MIN ? min(a, b) : a + b; };
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x111, 0xF, 0xF, false));
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x112, 0xF, 0xF, false));
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x114, 0xF, 0xF, false));
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x118, 0xF, 0xF, false));
+  if constexpr (GL == 32) {
+    const int32_t u = __shfl(v, (threadIdx.x & 32) | 15, 64);  // the lower row's last value
+    if (threadIdx.x & 16) v = op(v, u);
+  }
+  return v;
+}
 
-template <int CPR>
-MOE_DEV bool topk_row_tokens(const float* __restrict__ logits, const float* sb, int t, bool valid, int E, int k,
-                             float scale, int32_t* __restrict__ idx, float* __restrict__ gates, uint32_t* mask,
-                             TopkScratch* ws) {
+template <int GL>
+MOE_DEV int32_t group_last(int32_t v) { return __shfl(v, (threadIdx.x & (64 - GL)) | (GL - 1), 64); }
+
+template <int CPR, int GL>
+MOE_DEV bool topk_group_tokens(const float* __restrict__ logits, const float* sb, int t, bool valid, int E, int k,
+                               float scale, int32_t* __restrict__ idx, float* __restrict__ gates, uint32_t* mask,
+                               TopkScratch* ws) {
 #pragma clang fp contract(off)
-  const int lane = threadIdx.x & 63, li = lane & 15, rb = lane & 48;
+  const int lane = threadIdx.x & 63, li = lane & (GL - 1), rb = lane & (64 - GL);
   float l[CPR];
   int32_t q[CPR];
   int32_t mx = INT32_MIN;
 #pragma unroll
   for (int c = 0; c < CPR; ++c) {
-    const int e = li + 16 * c;
+    const int e = li + GL * c;
     const bool ok = valid && e < E;
     l[c] = ok ? logits[(size_t)t * E + e] : 0.f;
   }
 #pragma unroll
   for (int c = 0; c < CPR; ++c) {
-    const int e = li + 16 * c;
+    const int e = li + GL * c;
     q[c] = (valid && e < E) ? float_skey(fast_sigmoid(l[c]) + sb[e]) : INT32_MIN;
     mx = max(mx, q[c]);
   }
@@ -458,31 +479,21 @@ MOE_DEV bool topk_row_tokens(const float* __restrict__ logits, const float* sb, 
   wave_lds_sync();
   int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < 16; i += 4) {
+  for (int i = 0; i < GL; i += 4) {
     const int4 w = *reinterpret_cast<const int4*>(&ws->m[rb + i]);
     cnt += (w.x > mx) + (w.y > mx) + (w.z > mx) + (w.w > mx);
   }
-  // the row's smallest lane maximum with fewer than k larger ones (prefix
-  // minimum over the row by DPP row shifts, then lane 15 of the row)
-  int32_t tau = cnt < k ? mx : INT32_MAX;
-  tau = min(tau, __builtin_amdgcn_update_dpp(tau, tau, 0x111, 0xF, 0xF, false));
-  tau = min(tau, __builtin_amdgcn_update_dpp(tau, tau, 0x112, 0xF, 0xF, false));
-  tau = min(tau, __builtin_amdgcn_update_dpp(tau, tau, 0x114, 0xF, 0xF, false));
-  tau = min(tau, __builtin_amdgcn_update_dpp(tau, tau, 0x118, 0xF, 0xF, false));
-  tau = row_bcast15(tau);
+  // the group's smallest lane maximum with fewer than k larger ones
+  const int32_t tau = group_last<GL>(group_scan<GL, true>(cnt < k ? mx : INT32_MAX));
   const float vt = skey_float(tau);
   const int32_t thr = __builtin_isfinite(vt) ? float_skey(vt - (0x1p-12f + fabsf(vt) * 0x1p-16f)) : INT32_MIN + 1;
-  // compaction: each lane's candidates after those of the lanes before it in the row
+  // compaction: each lane's candidates after those of the lanes before it in the group
   int n = 0;
 #pragma unroll
   for (int c = 0; c < CPR; ++c) n += q[c] >= thr;
-  int incl = n;
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, false);
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, false);
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, false);
-  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, false);
-  const int C = row_bcast15(incl);
-  const bool fb = valid && (C < k || C > 16);
+  const int incl = group_scan<GL, false>(n);
+  const int C = group_last<GL>(incl);
+  const bool fb = valid && (C < k || C > GL);
   const bool act = valid && !fb;
   if (act) {
     int pos = rb + incl - n;
@@ -490,12 +501,12 @@ MOE_DEV bool topk_row_tokens(const float* __restrict__ logits, const float* sb, 
     for (int c = 0; c < CPR; ++c)
       if (q[c] >= thr) {
         ws->cl[pos] = l[c];
-        ws->ce[pos] = li + 16 * c;
+        ws->ce[pos] = li + GL * c;
         ++pos;
       }
   }
   wave_lds_sync();
-  const bool mine = act && li < C;  // this lane scores candidate li of its row
+  const bool mine = act && li < C;  // this lane scores candidate li of its group
   float sv = 0.f;
   int ev = 0;
   unsigned long long R = 0ull;
@@ -507,8 +518,9 @@ MOE_DEV bool topk_row_tokens(const float* __restrict__ logits, const float* sb, 
   ws->r[lane] = R;  // zero past the candidates: below every real key
   wave_lds_sync();
   const int cw = act ? C : 0;
-  const int cmax = max(max(__builtin_amdgcn_readlane(cw, 15), __builtin_amdgcn_readlane(cw, 31)),
-                       max(__builtin_amdgcn_readlane(cw, 47), __builtin_amdgcn_readlane(cw, 63)));
+  int cmax = 0;
+#pragma unroll
+  for (int g = 0; g < 64 / GL; ++g) cmax = max(cmax, __builtin_amdgcn_readlane(cw, g * GL + GL - 1));
   int rank = 0;
   for (int i = 0; i < cmax; i += 2) {
     const ulonglong2 w = *reinterpret_cast<const ulonglong2*>(&ws->r[rb + i]);
@@ -529,40 +541,41 @@ MOE_DEV bool topk_row_tokens(const float* __restrict__ logits, const float* sb, 
   return fb;
 }
 
-// Block of the row layout: two chunks, eight wavefronts each, four tokens
-// per wavefront.
-template <int CPL>
-MOE_DEV void topk_row_block(int pair, uint32_t* mask2, float* sb, TopkScratch* scratch,
-                            const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
-                            float scale, int32_t* __restrict__ idx, float* __restrict__ gates,
-                            uint32_t* __restrict__ bitmap, int32_t* __restrict__ ssum, int nchunks) {
-  constexpr int CPR = 4 * CPL;
+// Block of the group layout: 32 / GL chunks (two for GL = 16, one for
+// GL = 32), GL / 2 wavefronts per chunk, 64 / GL tokens per wavefront.
+template <int CPL, int GL>
+MOE_DEV void topk_group_block(int blk, uint32_t* maskc, float* sb, TopkScratch* scratch,
+                              const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
+                              float scale, int32_t* __restrict__ idx, float* __restrict__ gates,
+                              uint32_t* __restrict__ bitmap, int32_t* __restrict__ ssum, int nchunks) {
+  constexpr int CPR = 64 * CPL / GL, NCH = 32 / GL, WPC = GL / 2, TPW = 64 / GL;
   for (int i = threadIdx.x; i < E; i += kTopkThreads) {
-    mask2[i] = 0u;
-    mask2[E + i] = 0u;
+#pragma unroll
+    for (int h = 0; h < NCH; ++h) maskc[h * E + i] = 0u;
     sb[i] = bias[i];
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = wave >> 3;                    // which chunk of the pair
-  const int chunk = 2 * pair + half;
-  uint32_t* mask = mask2 + half * E;
-  const int t = chunk * kChunk + (wave & 7) * 4 + (lane >> 4);
+  const int half = wave / WPC;                   // which chunk of the block
+  const int chunk = NCH * blk + half;
+  uint32_t* mask = maskc + half * E;
+  const int t0 = chunk * kChunk + (wave % WPC) * TPW;
+  const int t = t0 + lane / GL;
   const bool valid = chunk < nchunks && t < T;
-  const bool fb = topk_row_tokens<CPR>(logits, sb, t, valid, E, k, scale, idx, gates, mask, scratch + wave);
-  const unsigned long long fbm = __ballot(fb && (lane & 15) == 0);
-  for (int r = 0; r < 4; ++r)  // tokens with more than 16 candidates: the k-round selection
-    if ((fbm >> (16 * r)) & 1ull) {
-      const int t1[1] = {chunk * kChunk + (wave & 7) * 4 + r};
+  const bool fb = topk_group_tokens<CPR, GL>(logits, sb, t, valid, E, k, scale, idx, gates, mask, scratch + wave);
+  const unsigned long long fbm = __ballot(fb && (lane & (GL - 1)) == 0);
+  for (int r = 0; r < TPW; ++r)  // tokens with more than GL candidates: the k-round selection
+    if ((fbm >> (GL * r)) & 1ull) {
+      const int t1[1] = {t0 + r};
       topk_tokens<CPL, 1>(logits, sb, t1, E, k, scale, idx, gates, mask);
     }
   __syncthreads();
-  for (int hh = 0; hh < 2; ++hh) {
-    const int c = 2 * pair + hh;
+  for (int hh = 0; hh < NCH; ++hh) {
+    const int c = NCH * blk + hh;
     if (c >= nchunks) break;
     int32_t* sdst = ssum + (size_t)(c / kSuper) * E;
     for (int i = threadIdx.x; i < E; i += kTopkThreads) {
-      const uint32_t m = mask2[hh * E + i];
+      const uint32_t m = maskc[hh * E + i];
       bitmap[(size_t)c * E + i] = m;
       if (m) atomicAdd(&sdst[i], __popc(m));
     }
@@ -615,7 +628,7 @@ MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict
 // logits (independent work side by side instead of two launches; the fewer,
 // longer histogram blocks are dispatched first so that they overlap the
 // ranking instead of trailing it).
-template <int CPL, bool ROW>
+template <int CPL, int GL>
 __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_topk(const float* __restrict__ logits,
                                                        const float* __restrict__ bias, int T, int E, int k,
                                                        float scale, int32_t* __restrict__ idx,
@@ -627,13 +640,13 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8)
   constexpr int kTopkBytes = 2 * 1024 * 4 + kChunk * (int)sizeof(TopkScratch);  // masks, bias, exchange
   constexpr int kHistBytes = kHistExperts * 256 * 4;
   __shared__ __align__(16) uint32_t smem[(kTopkBytes > kHistBytes ? kTopkBytes : kHistBytes) / 4];
-  const int nrank = ROW ? (nchunks + 1) / 2 : nchunks;
+  const int nrank = GL ? (nchunks + 32 / GL - 1) / (32 / GL) : nchunks;
   const int nhist = (int)gridDim.x - nrank;
   if ((int)blockIdx.x >= nhist) {
-    if (ROW)
-      topk_row_block<CPL>(blockIdx.x - nhist, smem, reinterpret_cast<float*>(smem + 1024),
-                          reinterpret_cast<TopkScratch*>(smem + 2048), logits, bias, T, E, k, scale, idx, gates,
-                          bitmap, ssum, nchunks);
+    if constexpr (GL != 0)
+      topk_group_block<CPL, GL>(blockIdx.x - nhist, smem, reinterpret_cast<float*>(smem + 1024),
+                                reinterpret_cast<TopkScratch*>(smem + 2048), logits, bias, T, E, k, scale, idx,
+                                gates, bitmap, ssum, nchunks);
     else
       topk_block<CPL>(blockIdx.x - nhist, smem, reinterpret_cast<float*>(smem + 1024),
                       reinterpret_cast<TopkScratch*>(smem + 2048), logits, bias, T, E, k, scale, idx, gates, bitmap,
@@ -644,22 +657,35 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8)
   }
 }
 
+// Lanes per token of the group layout (0: the 64-lane layout).  A group of
+// GL lanes holds 64 CPL / GL <= 16 columns and ranks up to GL / 2 experts.
+// Up to 512 chunks (16384 tokens) 32 lanes per token and one chunk per block
+// give twice the blocks and half the columns per lane (replica, T = 8192:
+// 11.3 -> 9.6 us); beyond that the launch is bound by instruction issue and
+// 16 lanes, sharing the per-token steps four ways, are faster (decode,
+// T = 131072: 49 against 59 us).
+static int topk_group_lanes(int cpl, int k, int nchunks) {
+  const bool g16 = cpl <= 4 && k <= group_max_k<16>(), g32 = cpl <= 8 && k <= group_max_k<32>();
+  if (g16 && nchunks > 512) return 16;
+  return g32 ? 32 : g16 ? 16 : 0;
+}
+
 hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, int T, int32_t* idx, float* gates,
                        uint32_t* bitmap, uint32_t* hist, unsigned long long* count, int32_t* ssum, hipStream_t s) {
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int cpl = (D.E + 63) / 64;
   const int tps = (T + kHistParts - 1) / kHistParts;
   const int hblocks = hist ? (D.E + kHistExperts - 1) / kHistExperts * kHistParts : 0;
-  const bool row = cpl <= 4 && D.k <= kRowMaxK;  // E <= 256: four tokens per wavefront
-  dim3 grid((row ? (nchunks + 1) / 2 : nchunks) + hblocks), block(kTopkThreads);
-#define MOE_TOPK(C, R)                                                                                          \
-  hipLaunchKernelGGL((k_topk<C, R>), grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, \
+  const int gl = topk_group_lanes(cpl, D.k, nchunks);
+  dim3 grid((gl ? (nchunks + 32 / gl - 1) / (32 / gl) : nchunks) + hblocks), block(kTopkThreads);
+#define MOE_TOPK(C, G)                                                                                          \
+  hipLaunchKernelGGL((k_topk<C, G>), grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, \
                      bitmap, nchunks, D.B, D.qb_lo, D.qb_scale, tps, hist, count, ssum)
-  if (cpl <= 1) { if (row) MOE_TOPK(1, true); else MOE_TOPK(1, false); }
-  else if (cpl <= 2) { if (row) MOE_TOPK(2, true); else MOE_TOPK(2, false); }
-  else if (cpl <= 4) { if (row) MOE_TOPK(4, true); else MOE_TOPK(4, false); }
-  else if (cpl <= 8) MOE_TOPK(8, false);
-  else MOE_TOPK(16, false);
+  if (cpl <= 1) { if (gl == 16) MOE_TOPK(1, 16); else if (gl == 32) MOE_TOPK(1, 32); else MOE_TOPK(1, 0); }
+  else if (cpl <= 2) { if (gl == 16) MOE_TOPK(2, 16); else if (gl == 32) MOE_TOPK(2, 32); else MOE_TOPK(2, 0); }
+  else if (cpl <= 4) { if (gl == 16) MOE_TOPK(4, 16); else if (gl == 32) MOE_TOPK(4, 32); else MOE_TOPK(4, 0); }
+  else if (cpl <= 8) { if (gl == 32) MOE_TOPK(8, 32); else MOE_TOPK(8, 0); }
+  else MOE_TOPK(16, 0);
 #undef MOE_TOPK
   return hipGetLastError();
 }

@@ -97,6 +97,8 @@ NEAR_TIE_CASES = [  # (E, k, T, kind)
     (256, 6, 1024, "cluster"),   # replica shape
     (256, 6, 1024, "tight"),     # replica shape, cluster of k + 4: ranked among at most 16 candidates
     (128, 8, 700, "tight"),
+    (256, 6, 20000, "tight"),    # more than 512 chunks: 16 lanes per token
+    (128, 8, 17000, "equal"),
     (100, 7, 257, "cluster"),    # E not a multiple of 64, ragged chunk
     (500, 12, 700, "cluster"),   # 8 columns per lane
     (256, 6, 300, "equal"),      # every expert a candidate: more than 64
