@@ -124,14 +124,16 @@ hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void
 }
 
 // -------------------------------------------------- scores + top-k ----
-// One block per chunk of kChunk = 32 tokens, kTopkNT tokens per wavefront
-// ranked side by side (independent chains hide each other's latency).  Lane i holds experts i, i+64, ... .  Each of the k rounds takes
-// the wave-wide maximum (DPP, no LDS) of the order key of v = s + b; among
-// equal keys the lowest expert index wins (first the lowest column c of any
-// lane holding the key, then the lowest such lane, by ballots).  Gates are
-// the chosen unbiased scores over their fp32 sum in slot order.  The chunk's
-// selections leave as one 32-bit token mask per expert: bitmap[chunk][e] bit
-// t%32 is set iff token t picked e.
+// Tokens are ranked in chunks of kChunk = 32 (one or two chunks per block).
+// The selection is the candidate filter below (topk_filter_tokens, or
+// topk_group_tokens with 16 or 32 lanes per token); tokens it cannot settle
+// take the k-round path here: lane i holds experts i, i+64, ...; each of the
+// k rounds takes the wave-wide maximum (DPP, no LDS) of the order key of
+// v = s + b; among equal keys the lowest expert index wins (first the lowest
+// column c of any lane holding the key, then the lowest such lane, by
+// ballots).  Gates are the chosen unbiased scores over their fp32 sum in
+// slot order.  The chunk's selections leave as one 32-bit token mask per
+// expert: bitmap[chunk][e] bit t%32 is set iff token t picked e.
 template <int CPL, int NT>
 MOE_DEV void topk_tokens(const float* __restrict__ logits, const float* sb, const int (&t)[NT], int E, int k,
                          float scale, int32_t* __restrict__ idx, float* __restrict__ gates, uint32_t* mask) {
@@ -623,7 +625,7 @@ MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict
   if (group == 0 && ts == 0 && threadIdx.x == 0) *count += (unsigned long long)T;
 }
 
-// One launch for the scores: the last nchunks blocks rank the chunks; in
+// One launch for the scores: the last blocks rank the chunks; in
 // training mode the blocks before them build the QB histogram from the same
 // logits (independent work side by side instead of two launches; the fewer,
 // longer histogram blocks are dispatched first so that they overlap the
