@@ -41,19 +41,32 @@ MOE_DEV float chunk_sumsq(const uint4& v) {
   return ss;
 }
 
+// gamma of one 16-byte chunk of the row (8 bf16 or 4 fp32 elements)
 template <bool BF16>
-MOE_DEV uint4 chunk_scale(const uint4& v, float rstd, const float* g) {
+struct ChunkGamma {
+  float4 g0, g1;
+};
+template <bool BF16>
+MOE_DEV ChunkGamma<BF16> chunk_gamma(const float* g) {
+  ChunkGamma<BF16> r;
+  r.g0 = *reinterpret_cast<const float4*>(g);
+  r.g1 = BF16 ? *reinterpret_cast<const float4*>(g + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  return r;
+}
+
+template <bool BF16>
+MOE_DEV uint4 chunk_scale(const uint4& v, float rstd, const ChunkGamma<BF16>& cg) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[4];
   if (BF16) {
-    const float4 g0 = *reinterpret_cast<const float4*>(g), g1 = *reinterpret_cast<const float4*>(g + 4);
+    const float4 g0 = cg.g0, g1 = cg.g1;
     const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       o[i] = pack_bf16x2(bf16_bits_to_f32(w[i] & 0xFFFFu) * rstd * gg[2 * i],
                          bf16_bits_to_f32(w[i] >> 16) * rstd * gg[2 * i + 1]);
   } else {
-    const float4 g0 = *reinterpret_cast<const float4*>(g);
+    const float4 g0 = cg.g0;
     const float gg[4] = {g0.x, g0.y, g0.z, g0.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(__uint_as_float(w[i]) * rstd * gg[i]);
@@ -79,8 +92,13 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const void* __restrict__ x, con
   float ss = 0.f;
   if constexpr (CPL > 0) {
     uint4 v[CPL];
+    ChunkGamma<BF16> g[CPL];  // gamma read with the row, not after its reduction
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) v[i] = lane + 64 * i < nch ? xr[lane + 64 * i] : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < CPL; ++i) {
+      const int c = lane + 64 * i;
+      v[i] = c < nch ? xr[c] : make_uint4(0, 0, 0, 0);
+      if (c < nch) g[i] = chunk_gamma<BF16>(gamma + c * EPC);
+    }
 #pragma unroll
     for (int i = 0; i < CPL; ++i) ss += chunk_sumsq<BF16>(v[i]);
     ss = wave_sum(ss);
@@ -88,13 +106,14 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const void* __restrict__ x, con
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = lane + 64 * i;
-      if (c < nch) hr[c] = chunk_scale<BF16>(v[i], rstd, gamma + c * EPC);
+      if (c < nch) hr[c] = chunk_scale<BF16>(v[i], rstd, g[i]);
     }
   } else {
     for (int c = lane; c < nch; c += 64) ss += chunk_sumsq<BF16>(xr[c]);
     ss = wave_sum(ss);
     const float rstd = 1.0f / sqrtf(ss / (float)d + eps);
-    for (int c = lane; c < nch; c += 64) hr[c] = chunk_scale<BF16>(xr[c], rstd, gamma + c * EPC);
+    for (int c = lane; c < nch; c += 64)
+      hr[c] = chunk_scale<BF16>(xr[c], rstd, chunk_gamma<BF16>(gamma + c * EPC));
   }
 }
 
