@@ -52,16 +52,21 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
 // grouped GEMMs.  With `load` non-NULL (sign-rule training) the counts are
 // also added to load[E] and T to *count.
 // tile_offsets / tile_info: the kExpertBM table; tile_offsets2 / tile_info2
-// (nullable): the kExpertBM2 table.
+// (nullable): the kExpertBM2 table.  The scan writes the tile tables only with
+// at most 8 tiles per expert on average; otherwise the scatter launch does.
 hipError_t launch_scan(const Dims& D, int T, int32_t* sbase, int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
                        int2* tile_info, uint32_t* load, unsigned long long* count, hipStream_t s,
                        int32_t* tile_offsets2 = nullptr, int2* tile_info2 = nullptr);
 // Rows of the permutation (perm_src, inv).  With zs non-NULL (MXFP8 experts)
 // also copies each token's z scale row (s_ld bytes, a multiple of 4) to Xs at
-// each of its grouped rows.
+// each of its grouped rows.  With many tiles per expert (more than 8 on
+// average) the same launch writes the grouped GEMMs' tile tables from the
+// scan's counts, offsets and tile offsets (tile_offsets2 / tile_info2 may be
+// NULL); otherwise the scan has written them.
 hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* sbase, int T,
-                          int32_t* perm_src, int32_t* inv, hipStream_t s, const uint8_t* zs = nullptr,
-                          uint8_t* Xs = nullptr, int s_ld = 0);
+                          int32_t* perm_src, int32_t* inv, hipStream_t s, const uint8_t* zs, uint8_t* Xs, int s_ld,
+                          const int32_t* counts, const int32_t* offsets, const int32_t* tile_offsets,
+                          int2* tile_info, const int32_t* tile_offsets2, int2* tile_info2);
 hipError_t launch_combine(const Dims& D, const void* Y, const float* gates, const int32_t* inv, int T,
                           void* y_lat, hipStream_t s);
 // QB update: quantiles from the histogram [E][B] (cleared; one block per

@@ -311,7 +311,9 @@ moe_status route_tail(moe_ctx* ctx, const RoutePtrs& p, int T, hipStream_t s, co
   MOE_RUN(MOE_K_SCAN, launch_scan(D, T, p.sbase, p.counts, p.offsets, p.tile_offsets,
                                   p.tile_info, load, train && sign ? cnt : nullptr, s, p.tile_offsets2,
                                   p.tile_info2));
-  MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.bitmap, p.sbase, T, p.perm_src, p.inv, s, zs, Xs, D.l / 32));
+  MOE_RUN(MOE_K_SCATTER, launch_scatter(D, p.idx, p.bitmap, p.sbase, T, p.perm_src, p.inv, s, zs, Xs, D.l / 32,
+                                        p.counts, p.offsets, p.tile_offsets, p.tile_info, p.tile_offsets2,
+                                        p.tile_info2));
   return MOE_OK;
 }
 

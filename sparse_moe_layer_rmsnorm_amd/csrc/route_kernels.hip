@@ -717,6 +717,13 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
 // chunks') total per expert in sbase; the global scan below turns those into
 // first rows; the base of a chunk inside its super-chunk is summed by the
 // scatter from the masks themselves.
+// At most 8 tiles of kExpertBM rows per expert on average: the scan's one
+// thread per expert writes that expert's tiles; otherwise the scatter launch
+// writes the tile tables, spread over its blocks.
+__host__ __device__ inline bool scan_writes_tiles(int T, int k, int E) {
+  return (long long)T * k <= 8LL * kExpertBM * E;
+}
+
 // Super-chunks [s0, s1) of expert e: each total in sbase becomes the first
 // row of its part of the expert's group, counting on from `run` (16 loads
 // issued before their stores: the compiler cannot tell that the stores do
@@ -750,14 +757,11 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
                                                       int T, int k, int32_t* __restrict__ tile_offsets2,
                                                       int2* __restrict__ tile_info2) {
   __shared__ int wsum_r[16], wsum_t[16], wsum_u[16];
-  // per expert (E <= 1024): first row, count, inclusive tile prefixes of both tables
-  __shared__ int s_row0[1024], s_cnt[1024], s_t[1024], s_u[1024];
+  __shared__ int s_row0[1024];  // per expert (E <= 1024): first row
   __shared__ int s_part[1024];  // many super-chunks: each thread's partial sum
   constexpr int kReg = 16;  // up to this many super-chunk totals stay in registers
   const int i = threadIdx.x, lane = i & 63, w = i >> 6;
-  // at most 8 tiles of kExpertBM rows per expert on average: one thread per
-  // expert writes its tiles (cheaper than a block-wide pass at these sizes)
-  const bool few = (long long)T * k <= 8LL * kExpertBM * E;
+  const bool few = scan_writes_tiles(T, k, E);
   // More super-chunks than registers and E <= 512: P threads per expert
   // (P E <= 1024), thread i takes expert i % E and the P-th part i / E of its
   // super-chunks, so that P times more loads are in flight.
@@ -830,9 +834,6 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
       prefix_rows(sbase, E, i, 0, nsuper, run);
     }
     s_row0[i] = r - c;
-    s_cnt[i] = c;
-    s_t[i] = t;
-    s_u[i] = u;
     if (tile_offsets2) tile_offsets2[i + 1] = u;
     if (few) {  // each expert thread writes its own few tiles
       for (int j = 0, t0 = t - tl; j < tl; ++j)
@@ -856,26 +857,7 @@ __global__ __launch_bounds__(1024) void k_scan_global(int32_t* __restrict__ sbas
       prefix_rows(sbase, E, pe, ps0, ps1, run);
     }
   }
-  if (few) return;
-  __syncthreads();
-  // Many tiles per expert: the tile tables are spread over the whole block;
-  // tile g belongs to the expert whose tile range holds it (binary search
-  // over the inclusive prefixes).
-  auto fill = [&](const int* pre, int bm, int2* info) {
-    const int total = pre[E - 1];
-    for (int g = i; g < total; g += 1024) {
-      int lo = 0, hi = E - 1;  // first e with pre[e] > g
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (pre[mid] > g) hi = mid;
-        else lo = mid + 1;
-      }
-      const int j = g - (lo > 0 ? pre[lo - 1] : 0);
-      info[g] = make_int2(s_row0[lo] + j * bm, (lo << 8) | min(bm, s_cnt[lo] - j * bm));
-    }
-  };
-  fill(s_t, kExpertBM, tile_info);
-  if (tile_info2) fill(s_u, kExpertBM2, tile_info2);
+  // many tiles per expert: the scatter launch writes the tile tables
 }
 
 hipError_t launch_scan(const Dims& D, int T, int32_t* sbase, int32_t* counts, int32_t* offsets, int32_t* tile_offsets,
@@ -895,10 +877,47 @@ hipError_t launch_scan(const Dims& D, int T, int32_t* sbase, int32_t* counts, in
 // + the tokens of e in the earlier chunks of the super-chunk (their masks'
 // popcounts, at most kSuper - 1 loads, all in flight together) + the earlier
 // tokens of the chunk in the chunk's mask for e.
+// Tile table entries g = this block's threads (many tiles per expert): tile g
+// belongs to the first expert e with pre[e] > g, pre the inclusive tile
+// prefix (tile_offsets[1 .. E]), found by a binary search over a copy of pre
+// in LDS; consecutive entries per wavefront, so the stores coalesce.  Every
+// table has at most T k tiles (each holds at least one row), so the scatter's
+// grid covers it.
+MOE_DEV void fill_tiles(int* s_pre, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+                        const int32_t* __restrict__ tile_offsets, int2* __restrict__ info, int bm, int E) {
+  const int total = tile_offsets[E];
+  if ((int)blockIdx.x * 256 >= total) return;  // block-uniform
+  for (int i = threadIdx.x; i < E; i += 256) s_pre[i] = tile_offsets[i + 1];
+  __syncthreads();
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g < total) {
+    int lo = 0, hi = E - 1;  // first e with pre[e] > g
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pre[mid] > g) hi = mid;
+      else lo = mid + 1;
+    }
+    const int j = g - (lo > 0 ? s_pre[lo - 1] : 0), c = counts[lo];
+    info[g] = make_int2(offsets[lo] + j * bm, (lo << 8) | min(bm, c - j * bm));
+  }
+  __syncthreads();  // s_pre is reused by the next table
+}
+
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, const uint32_t* __restrict__ bitmap,
                                                  const int32_t* __restrict__ sbase, int T, int E, int k,
                                                  int32_t* __restrict__ perm_src, int32_t* __restrict__ inv,
-                                                 const uint32_t* __restrict__ zs, uint32_t* __restrict__ Xs, int s4) {
+                                                 const uint32_t* __restrict__ zs, uint32_t* __restrict__ Xs, int s4,
+                                                 const int32_t* __restrict__ counts,
+                                                 const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ tile_offsets,
+                                                 int2* __restrict__ tile_info,
+                                                 const int32_t* __restrict__ tile_offsets2,
+                                                 int2* __restrict__ tile_info2) {
+  __shared__ int s_pre[1024];
+  if (tile_info) {  // many tiles per expert: the tile tables are written here
+    fill_tiles(s_pre, counts, offsets, tile_offsets, tile_info, kExpertBM, E);
+    if (tile_info2) fill_tiles(s_pre, counts, offsets, tile_offsets2, tile_info2, kExpertBM2, E);
+  }
   const int Tk = T * k;
   const int p = blockIdx.x * 256 + threadIdx.x;
   if (p >= Tk) return;
@@ -921,12 +940,18 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
 }
 
 hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bitmap, const int32_t* sbase, int T,
-                          int32_t* perm_src, int32_t* inv, hipStream_t s, const uint8_t* zs, uint8_t* Xs, int s_ld) {
+                          int32_t* perm_src, int32_t* inv, hipStream_t s, const uint8_t* zs, uint8_t* Xs, int s_ld,
+                          const int32_t* counts, const int32_t* offsets, const int32_t* tile_offsets,
+                          int2* tile_info, const int32_t* tile_offsets2, int2* tile_info2) {
   const long long Tk = (long long)T * D.k;
   if (zs && s_ld % 4) return hipErrorInvalidValue;
+  if ((tile_offsets2 == nullptr) != (tile_info2 == nullptr)) return hipErrorInvalidValue;
+  const bool fill = !scan_writes_tiles(T, D.k, D.E);  // else the scan wrote them
+  if (fill && (!counts || !offsets || !tile_offsets || !tile_info)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_scatter, dim3((unsigned)((Tk + 255) / 256)), dim3(256), 0, s, idx, bitmap, sbase, T,
                      D.E, D.k, perm_src, inv, reinterpret_cast<const uint32_t*>(zs), reinterpret_cast<uint32_t*>(Xs),
-                     zs ? s_ld / 4 : 0);
+                     zs ? s_ld / 4 : 0, counts, offsets, tile_offsets, fill ? tile_info : nullptr, tile_offsets2,
+                     fill ? tile_info2 : nullptr);
   return hipGetLastError();
 }
 
