@@ -476,25 +476,40 @@ template <int GL>
 MOE_DEV int32_t group_last(int32_t v) { return __shfl(v, (threadIdx.x & (64 - GL)) | (GL - 1), 64); }
 
 template <int CPR, int GL>
-MOE_DEV bool topk_group_tokens(const float* __restrict__ logits, const float* sb, int t, bool valid, int E, int k,
-                               float scale, int32_t* __restrict__ idx, float* __restrict__ gates, uint32_t* mask,
-                               TopkScratch* ws) {
+MOE_DEV bool topk_group_tokens(const float* __restrict__ logits, const float* sb, const float* sbt, int t,
+                               bool valid, int E, int k, float scale, int32_t* __restrict__ idx,
+                               float* __restrict__ gates, uint32_t* mask, TopkScratch* ws) {
 #pragma clang fp contract(off)
+  constexpr int BV = CPR % 4 == 0 ? 4 : CPR % 2 == 0 ? 2 : 1;  // bias columns per LDS read
   const int lane = threadIdx.x & 63, li = lane & (GL - 1), rb = lane & (64 - GL);
   float l[CPR];
   int32_t q[CPR];
   int32_t mx = INT32_MIN;
+  // branch-free loads: rows past T and columns past E read a valid element,
+  // whose key is replaced below
+  const float* lr = logits + (size_t)(valid ? t : 0) * E;
 #pragma unroll
-  for (int c = 0; c < CPR; ++c) {
-    const int e = li + GL * c;
-    const bool ok = valid && e < E;
-    l[c] = ok ? logits[(size_t)t * E + e] : 0.f;
-  }
+  for (int c = 0; c < CPR; ++c) l[c] = lr[min(li + GL * c, E - 1)];
 #pragma unroll
-  for (int c = 0; c < CPR; ++c) {
-    const int e = li + GL * c;
-    q[c] = (valid && e < E) ? float_skey(fast_sigmoid(l[c]) + sb[e]) : INT32_MIN;
-    mx = max(mx, q[c]);
+  for (int c0 = 0; c0 < CPR; c0 += BV) {
+    // the lane's bias columns, BV per LDS read (sbt[li][c] = b[li + GL c])
+    float bc[BV];
+    if constexpr (BV == 4) {
+      const float4 b4 = *reinterpret_cast<const float4*>(sbt + li * CPR + c0);
+      bc[0] = b4.x, bc[1] = b4.y, bc[2] = b4.z, bc[3] = b4.w;
+    } else if constexpr (BV == 2) {
+      const float2 b2 = *reinterpret_cast<const float2*>(sbt + li * CPR + c0);
+      bc[0] = b2.x, bc[1] = b2.y;
+    } else {
+      bc[0] = sbt[li * CPR + c0];
+    }
+#pragma unroll
+    for (int u = 0; u < BV; ++u) {
+      const int c = c0 + u, e = li + GL * c;
+      const int32_t key = float_skey(fast_sigmoid(l[c]) + bc[u]);
+      q[c] = (valid && e < E) ? key : INT32_MIN;
+      mx = max(mx, q[c]);
+    }
   }
   ws->m[lane] = mx;
   wave_lds_sync();
@@ -570,11 +585,14 @@ MOE_DEV void topk_group_block(int blk, uint32_t* maskc, float* sb, TopkScratch* 
                               float scale, int32_t* __restrict__ idx, float* __restrict__ gates,
                               uint32_t* __restrict__ bitmap, int32_t* __restrict__ ssum, int nchunks) {
   constexpr int CPR = 64 * CPL / GL, NCH = 32 / GL, WPC = GL / 2, TPW = 64 / GL;
+  static_assert(GL * CPR <= 512, "the lane-major bias copy fits beside the bias");
+  float* sbt = sb + 512;  // sbt[li * CPR + c] = bias[li + GL c] (0 past E)
   for (int i = threadIdx.x; i < E; i += kTopkThreads) {
 #pragma unroll
     for (int h = 0; h < NCH; ++h) maskc[h * E + i] = 0u;
     sb[i] = bias[i];
   }
+  for (int i = threadIdx.x; i < GL * CPR; i += kTopkThreads) sbt[(i % GL) * CPR + i / GL] = i < E ? bias[i] : 0.f;
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = wave / WPC;                   // which chunk of the block
@@ -583,7 +601,7 @@ MOE_DEV void topk_group_block(int blk, uint32_t* maskc, float* sb, TopkScratch* 
   const int t0 = chunk * kChunk + (wave % WPC) * TPW;
   const int t = t0 + lane / GL;
   const bool valid = chunk < nchunks && t < T;
-  const bool fb = topk_group_tokens<CPR, GL>(logits, sb, t, valid, E, k, scale, idx, gates, mask, scratch + wave);
+  const bool fb = topk_group_tokens<CPR, GL>(logits, sb, sbt, t, valid, E, k, scale, idx, gates, mask, scratch + wave);
   const unsigned long long fbm = __ballot(fb && (lane & (GL - 1)) == 0);
   for (int r = 0; r < TPW; ++r)  // tokens with more than GL candidates: the k-round selection
     if ((fbm >> (GL * r)) & 1ull) {
