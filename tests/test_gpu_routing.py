@@ -35,6 +35,8 @@ CASES = [  # (E, k, T, logit scale, bias scale)
     (48, 3, 30000, 1.5, 0.1),      # 59 super-chunks over 16 threads per expert, one part empty
     (256, 6, 2000, 1.0, 300.0),    # |b| >> s: v = s + b spaced by ulps of a few hundred, many negative
     (896, 16, 1000, 1.0, 40.0),
+    (256, 6, 65569, 1.0, 0.05),    # 2050 chunks: the per-block scatter, its last block 2 chunks, a 1-token chunk
+    (100, 4, 70001, 1.0, 0.1),     # the per-block scatter with E < 256 (threads without an expert)
 ]
 
 
