@@ -67,12 +67,14 @@ def kernel_work(s, T: int) -> dict:
         "sign_bias": 16.0 * s.E,
     }
     # bytes the implementation moves beyond those: the histogram's atomic
-    # adds from 16 token parts, the per-chunk selection masks and the
-    # per-super-chunk counts
+    # adds from its token parts (16, or 32 where the top-k runs 512-thread
+    # blocks: a token per 16 lanes, E <= 256, k <= 8, more than 512 chunks),
+    # the per-chunk selection masks and the per-super-chunk counts
     nchunks = (T + 31) // 32
     nsuper = (nchunks + 15) // 16
+    parts = 32 if (s.E <= 256 and s.k <= 8 and nchunks > 512) else 16
     impl_extra = {
-        "topk": 8.0 * 16 * s.E * s.B + 4.0 * nchunks * s.E + 8.0 * nsuper * s.E,
+        "topk": 8.0 * parts * s.E * s.B + 4.0 * nchunks * s.E + 8.0 * nsuper * s.E,
         "scan": 8.0 * nsuper * s.E,
         "scatter": 4.0 * 8 * Tk,
     }

@@ -11,7 +11,8 @@ constexpr int kChunk = 32;
 // Chunks per super-chunk of the two-level prefix sum.
 constexpr int kSuper = 16;
 // Token parts of one training pass whose score histograms are built by
-// separate blocks (each adds its counts into the one histogram of the state).
+// separate blocks (each adds its counts into the one histogram of the state),
+// per 1024 threads of a top-k block (twice as many with 512-thread blocks).
 constexpr int kHistParts = 16;
 // Rows per tile of the grouped expert GEMMs (also the granularity of the
 // per-expert tile offsets computed by the scan).

@@ -374,6 +374,9 @@ MOE_DEV void topk_filter_tokens(const float* __restrict__ logits, const float* s
 #endif
 constexpr int kTopkNT = MOE_TOPK_NT;                    // tokens ranked side by side per wavefront
 constexpr int kTopkThreads = kChunk / kTopkNT * 64;      // one token group per wavefront
+// Threads of a top-k block: the 16-lane group layout holds one chunk in 8
+// wavefronts; the other layouts one chunk in 16.
+constexpr int topk_threads(int GL) { return GL == 16 ? 512 : kTopkThreads; }
 
 // Tokens a wavefront ranks side by side in the filter: two while their
 // registers leave room for two blocks per CU, else one after the other.
@@ -577,22 +580,28 @@ MOE_DEV bool topk_group_tokens(const float* __restrict__ logits, const float* sb
   return fb;
 }
 
-// Block of the group layout: 32 / GL chunks (two for GL = 16, one for
-// GL = 32), GL / 2 wavefronts per chunk, 64 / GL tokens per wavefront.
+// Block of the group layout: one chunk, GL / 2 wavefronts (8 for GL = 16,
+// 16 for GL = 32) of 64 / GL tokens each.  One chunk per block keeps the
+// block barriers to the wavefronts of one chunk and, for GL = 16, gives four
+// resident blocks per CU instead of two (decode shape, T = 131072: 44.8 ->
+// 42.1 us frozen, 80.0 -> 73.5 us in training with twice the histogram
+// parts).
 template <int CPL, int GL>
 MOE_DEV void topk_group_block(int blk, uint32_t* maskc, float* sb, TopkScratch* scratch,
                               const float* __restrict__ logits, const float* __restrict__ bias, int T, int E, int k,
                               float scale, int32_t* __restrict__ idx, float* __restrict__ gates,
                               uint32_t* __restrict__ bitmap, int32_t* __restrict__ ssum, int nchunks) {
-  constexpr int CPR = 64 * CPL / GL, NCH = 32 / GL, WPC = GL / 2, TPW = 64 / GL;
+  constexpr int CPR = 64 * CPL / GL, WPC = GL / 2, TPW = 64 / GL, NTHR = topk_threads(GL);
+  constexpr int NCH = NTHR / 64 / WPC;  // chunks per block
+  static_assert(NCH >= 1 && NTHR == NCH * WPC * 64, "whole chunks per block");
   static_assert(GL * CPR <= 512, "the lane-major bias copy fits beside the bias");
   float* sbt = sb + 512;  // sbt[li * CPR + c] = bias[li + GL c] (0 past E)
-  for (int i = threadIdx.x; i < E; i += kTopkThreads) {
+  for (int i = threadIdx.x; i < E; i += NTHR) {
 #pragma unroll
     for (int h = 0; h < NCH; ++h) maskc[h * E + i] = 0u;
     sb[i] = bias[i];
   }
-  for (int i = threadIdx.x; i < GL * CPR; i += kTopkThreads) sbt[(i % GL) * CPR + i / GL] = i < E ? bias[i] : 0.f;
+  for (int i = threadIdx.x; i < GL * CPR; i += NTHR) sbt[(i % GL) * CPR + i / GL] = i < E ? bias[i] : 0.f;
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = wave / WPC;                   // which chunk of the block
@@ -613,7 +622,7 @@ MOE_DEV void topk_group_block(int blk, uint32_t* maskc, float* sb, TopkScratch* 
     const int c = NCH * blk + hh;
     if (c >= nchunks) break;
     int32_t* sdst = ssum + (size_t)(c / kSuper) * E;
-    for (int i = threadIdx.x; i < E; i += kTopkThreads) {
+    for (int i = threadIdx.x; i < E; i += NTHR) {
       const uint32_t m = maskc[hh * E + i];
       bitmap[(size_t)c * E + i] = m;
       if (m) atomicAdd(&sdst[i], __popc(m));
@@ -626,14 +635,15 @@ MOE_DEV void topk_group_block(int blk, uint32_t* maskc, float* sb, TopkScratch* 
 // counts its part's score bins in LDS with integer atomics and adds them to
 // the histogram rows with global integer atomics: both are order-free, so the
 // histogram is the same whatever order the blocks run in.
+template <int NTHR>
 MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict__ logits, int T, int E, int B,
                         float lo, float scale, int tps, uint32_t* __restrict__ hist,
                         unsigned long long* __restrict__ count) {
-  constexpr int TR = kTopkThreads / kHistExperts;  // token rows in flight per step
+  constexpr int TR = NTHR / kHistExperts;  // token rows in flight per step
   const int e0 = group * kHistExperts;
   const int ne = min(kHistExperts, E - e0);
   const int nb = kHistExperts * B;
-  for (int i = threadIdx.x; i < nb; i += kTopkThreads) lh[i] = 0;
+  for (int i = threadIdx.x; i < nb; i += NTHR) lh[i] = 0;
   __syncthreads();
   // thread -> expert e0 + (i % 16), tokens (i / 16) + TR m: each wavefront
   // reads four 64-byte row pieces per step
@@ -654,7 +664,7 @@ MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict
   __syncthreads();
   if (tb < T) {  // integer atomics: the sums do not depend on the order of the token parts
     uint32_t* dst = hist + (size_t)e0 * B;
-    for (int i = threadIdx.x; i < ne * B; i += kTopkThreads) {
+    for (int i = threadIdx.x; i < ne * B; i += NTHR) {
       const uint32_t v = lh[i];
       if (v) atomicAdd(&dst[i], v);
     }
@@ -668,7 +678,7 @@ MOE_DEV void hist_block(int group, int ts, uint32_t* lh, const float* __restrict
 // longer histogram blocks are dispatched first so that they overlap the
 // ranking instead of trailing it).
 template <int CPL, int GL>
-__global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_topk(const float* __restrict__ logits,
+__global__ __launch_bounds__(topk_threads(GL)) __attribute__((amdgpu_waves_per_eu(8))) void k_topk(const float* __restrict__ logits,
                                                        const float* __restrict__ bias, int T, int E, int k,
                                                        float scale, int32_t* __restrict__ idx,
                                                        float* __restrict__ gates, uint32_t* __restrict__ bitmap,
@@ -676,10 +686,13 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8)
                                                        uint32_t* __restrict__ hist,
                                                        unsigned long long* __restrict__ count,
                                                        int32_t* __restrict__ ssum) {
-  constexpr int kTopkBytes = 2 * 1024 * 4 + kChunk * (int)sizeof(TopkScratch);  // masks, bias, exchange
+  // masks, bias, exchange (one TopkScratch per token group: per wavefront in
+  // the group layout, kTopkNT per wavefront in the 64-lane one)
+  constexpr int kScratches = GL ? topk_threads(GL) / 64 : kChunk;
+  constexpr int kTopkBytes = 2 * 1024 * 4 + kScratches * (int)sizeof(TopkScratch);
   constexpr int kHistBytes = kHistExperts * 256 * 4;
   __shared__ __align__(16) uint32_t smem[(kTopkBytes > kHistBytes ? kTopkBytes : kHistBytes) / 4];
-  const int nrank = GL ? (nchunks + 32 / GL - 1) / (32 / GL) : nchunks;
+  const int nrank = nchunks;  // one chunk per ranking block
   const int nhist = (int)gridDim.x - nrank;
   if ((int)blockIdx.x >= nhist) {
     if constexpr (GL != 0)
@@ -692,17 +705,18 @@ __global__ __launch_bounds__(kTopkThreads) __attribute__((amdgpu_waves_per_eu(8)
                       ssum);
   } else {
     const int groups = (E + kHistExperts - 1) / kHistExperts;
-    hist_block(blockIdx.x % groups, blockIdx.x / groups, smem, logits, T, E, B, lo, bscale, tps, hist, count);
+    hist_block<topk_threads(GL)>(blockIdx.x % groups, blockIdx.x / groups, smem, logits, T, E, B, lo, bscale, tps,
+                                 hist, count);
   }
 }
 
 // Lanes per token of the group layout (0: the 64-lane layout).  A group of
 // GL lanes holds 64 CPL / GL <= 16 columns and ranks up to GL / 2 experts.
-// Up to 512 chunks (16384 tokens) 32 lanes per token and one chunk per block
-// give twice the blocks and half the columns per lane (replica, T = 8192:
-// 11.3 -> 9.6 us); beyond that the launch is bound by instruction issue and
-// 16 lanes, sharing the per-token steps four ways, are faster (decode,
-// T = 131072: 49 against 59 us).
+// Up to 512 chunks (16384 tokens) 32 lanes per token give half the columns
+// per lane and, with a chunk per block either way, twice the lanes per block
+// (replica, T = 8192: 11.3 -> 9.6 us against 16 lanes); beyond that 16 lanes,
+// sharing the per-token steps four ways, are faster (decode, T = 131072: 49
+// against 59 us when measured).
 static int topk_group_lanes(int cpl, int k, int nchunks) {
   const bool g16 = cpl <= 4 && k <= group_max_k<16>(), g32 = cpl <= 8 && k <= group_max_k<32>();
   if (g16 && nchunks > 512) return 16;
@@ -713,10 +727,13 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
                        uint32_t* bitmap, uint32_t* hist, unsigned long long* count, int32_t* ssum, hipStream_t s) {
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int cpl = (D.E + 63) / 64;
-  const int tps = (T + kHistParts - 1) / kHistParts;
-  const int hblocks = hist ? (D.E + kHistExperts - 1) / kHistExperts * kHistParts : 0;
   const int gl = topk_group_lanes(cpl, D.k, nchunks);
-  dim3 grid((gl ? (nchunks + 32 / gl - 1) / (32 / gl) : nchunks) + hblocks), block(kTopkThreads);
+  // token parts of the histogram: kHistParts per 1024 threads a block has, so
+  // smaller blocks keep the same threads on it
+  const int parts = kHistParts * kTopkThreads / topk_threads(gl);
+  const int tps = (T + parts - 1) / parts;
+  const int hblocks = hist ? (D.E + kHistExperts - 1) / kHistExperts * parts : 0;
+  dim3 grid(nchunks + hblocks), block(topk_threads(gl));
 #define MOE_TOPK(C, G)                                                                                          \
   hipLaunchKernelGGL((k_topk<C, G>), grid, block, 0, s, logits, bias, T, D.E, D.k, D.routed_scale, idx, gates, \
                      bitmap, nchunks, D.B, D.qb_lo, D.qb_scale, tps, hist, count, ssum)

@@ -71,6 +71,7 @@ SHAPES = [  # name, T, d, l, E, k, f, f_s
     ("ragged", 203, 192, 256, 24, 5, 384, 0),
     ("replica-widths", 1000, 1024, 256, 256, 6, 512, 2048),
     ("deep", 4096, 256, 128, 8, 2, 128, 0),          # 1024 rows per expert: block-wide tile tables
+    ("long", 65600, 128, 128, 16, 2, 128, 0),        # 2050 chunks: the per-block scatter copies the scale rows
 ]
 
 
