@@ -67,12 +67,18 @@ def kernel_work(s, T: int) -> dict:
         "sign_bias": 16.0 * s.E,
     }
     # bytes the implementation moves beyond those: the histogram's atomic
-    # adds from its token parts (16, or 32 where the top-k runs 512-thread
-    # blocks: a token per 16 lanes, E <= 256, k <= 8, more than 512 chunks),
-    # the per-chunk selection masks and the per-super-chunk counts
+    # adds from its token parts (32 where the top-k runs 512-thread blocks: a
+    # token per 16 lanes, E <= 256, k <= 8, more than 512 chunks; 16 with a
+    # token per 32 lanes, E <= 512, k <= 16; else 8), the per-chunk selection
+    # masks and the per-super-chunk counts
     nchunks = (T + 31) // 32
     nsuper = (nchunks + 15) // 16
-    parts = 32 if (s.E <= 256 and s.k <= 8 and nchunks > 512) else 16
+    if s.E <= 256 and s.k <= 8 and nchunks > 512:
+        parts = 32
+    elif s.E <= 512 and s.k <= 16:
+        parts = 16
+    else:
+        parts = 8
     impl_extra = {
         "topk": 8.0 * parts * s.E * s.B + 4.0 * nchunks * s.E + 8.0 * nsuper * s.E,
         "scan": 8.0 * nsuper * s.E,

@@ -12,7 +12,8 @@ constexpr int kChunk = 32;
 constexpr int kSuper = 16;
 // Token parts of one training pass whose score histograms are built by
 // separate blocks (each adds its counts into the one histogram of the state),
-// per 1024 threads of a top-k block (twice as many with 512-thread blocks).
+// per 1024 threads of a top-k block (twice as many with 512-thread blocks,
+// half as many in the 64-lane layout).
 constexpr int kHistParts = 16;
 // Rows per tile of the grouped expert GEMMs (also the granularity of the
 // per-expert tile offsets computed by the scan).

@@ -729,8 +729,11 @@ hipError_t launch_topk(const Dims& D, const float* logits, const float* bias, in
   const int cpl = (D.E + 63) / 64;
   const int gl = topk_group_lanes(cpl, D.k, nchunks);
   // token parts of the histogram: kHistParts per 1024 threads a block has, so
-  // smaller blocks keep the same threads on it
-  const int parts = kHistParts * kTopkThreads / topk_threads(gl);
+  // smaller blocks keep the same threads on it; half as many in the 64-lane
+  // layout (large E), whose many expert groups otherwise outnumber the ranking
+  // blocks (k3 shape: 48.4 -> 43.9 us in training; a quarter, or half at the
+  // replica shape, were slower)
+  const int parts = gl ? kHistParts * kTopkThreads / topk_threads(gl) : kHistParts / 2;
   const int tps = (T + parts - 1) / parts;
   const int hblocks = hist ? (D.E + kHistExperts - 1) / kHistExperts * parts : 0;
   dim3 grid(nchunks + hblocks), block(topk_threads(gl));
