@@ -927,12 +927,13 @@ hipError_t launch_scan(const Dims& D, int T, int32_t* sbase, int32_t* counts, in
 // entries per wavefront, so the stores coalesce (a grid-stride loop: every
 // table has at most T k tiles, each holding at least one row).
 MOE_DEV void fill_tiles(int* s_pre, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-                        const int32_t* __restrict__ tile_offsets, int2* __restrict__ info, int bm, int E) {
+                        const int32_t* __restrict__ tile_offsets, int2* __restrict__ info, int bm, int E,
+                        int grid_threads) {
   const int total = tile_offsets[E];
   if ((int)blockIdx.x * 256 >= total) return;  // block-uniform
   for (int i = threadIdx.x; i < E; i += 256) s_pre[i] = tile_offsets[i + 1];
   __syncthreads();
-  for (int g = blockIdx.x * 256 + threadIdx.x; g < total; g += gridDim.x * 256) {
+  for (int g = blockIdx.x * 256 + threadIdx.x; g < total; g += grid_threads) {
     int lo = 0, hi = E - 1;  // first e with pre[e] > g
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -962,10 +963,11 @@ struct ScatterArgs {
   int2* tile_info2;
 };
 
-MOE_DEV void fill_tables(int* s_pre, const ScatterArgs& a, int E) {
+MOE_DEV void fill_tables(int* s_pre, const ScatterArgs& a, int E, int grid_threads) {
   if (a.tile_info) {
-    fill_tiles(s_pre, a.counts, a.offsets, a.tile_offsets, a.tile_info, kExpertBM, E);
-    if (a.tile_info2) fill_tiles(s_pre, a.counts, a.offsets, a.tile_offsets2, a.tile_info2, kExpertBM2, E);
+    fill_tiles(s_pre, a.counts, a.offsets, a.tile_offsets, a.tile_info, kExpertBM, E, grid_threads);
+    if (a.tile_info2)
+      fill_tiles(s_pre, a.counts, a.offsets, a.tile_offsets2, a.tile_info2, kExpertBM2, E, grid_threads);
   }
 }
 
@@ -977,9 +979,9 @@ MOE_DEV void place(const ScatterArgs& a, int p, int t, int row, int Tk) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_scatter(ScatterArgs a, int T, int E, int k) {
+__global__ __launch_bounds__(256) void k_scatter(ScatterArgs a, int T, int E, int k, int grid_threads) {
   __shared__ int s_pre[1024];
-  fill_tables(s_pre, a, E);
+  fill_tables(s_pre, a, E, grid_threads);
   const int Tk = T * k;
   const int p = blockIdx.x * 256 + threadIdx.x;
   if (p >= Tk) return;
@@ -1000,10 +1002,10 @@ constexpr int kWideG = 8;  // chunks per block of the wide form (divides kSuper)
 constexpr int kWidePre = 8;  // expert indices per thread loaded before the masks
 static_assert(kSuper % kWideG == 0 && kSuper - kWideG <= 8, "one batch of earlier mask rows");
 
-__global__ __launch_bounds__(256) void k_scatter_wide(ScatterArgs a, int T, int E, int k) {
+__global__ __launch_bounds__(256) void k_scatter_wide(ScatterArgs a, int T, int E, int k, int grid_threads) {
   __shared__ int s_row[kWideG * 256];        // [chunk][expert] first rows
   __shared__ uint32_t s_mask[kWideG * 256];  // [chunk][expert] masks
-  fill_tables(s_row, a, E);
+  fill_tables(s_row, a, E, grid_threads);
   const int nchunks = (T + kChunk - 1) / kChunk;
   const int cb = blockIdx.x * kWideG, c0 = cb - cb % kSuper, cn = min(kWideG, nchunks - cb);
   const int Tk = T * k, pb = cb * kChunk * k, p1 = min(T, (cb + cn) * kChunk) * k;
@@ -1060,11 +1062,14 @@ hipError_t launch_scatter(const Dims& D, const int32_t* idx, const uint32_t* bit
                       reinterpret_cast<uint32_t*>(Xs), zs ? s_ld / 4 : 0, counts, offsets, tile_offsets,
                       fill ? tile_info : nullptr, tile_offsets2, fill ? tile_info2 : nullptr};
   const int nchunks = (T + kChunk - 1) / kChunk;
-  if (nchunks > 2048 && D.E <= 256)
-    hipLaunchKernelGGL(k_scatter_wide, dim3((unsigned)((nchunks + kWideG - 1) / kWideG)), dim3(256), 0, s, a, T,
-                       D.E, D.k);
-  else
-    hipLaunchKernelGGL(k_scatter, dim3((unsigned)((Tk + 255) / 256)), dim3(256), 0, s, a, T, D.E, D.k);
+  // the fill's stride, the grid's thread count, comes as an argument
+  if (nchunks > 2048 && D.E <= 256) {
+    const unsigned blocks = (unsigned)((nchunks + kWideG - 1) / kWideG);
+    hipLaunchKernelGGL(k_scatter_wide, dim3(blocks), dim3(256), 0, s, a, T, D.E, D.k, (int)blocks * 256);
+  } else {
+    const unsigned blocks = (unsigned)((Tk + 255) / 256);
+    hipLaunchKernelGGL(k_scatter, dim3(blocks), dim3(256), 0, s, a, T, D.E, D.k, (int)blocks * 256);
+  }
   return hipGetLastError();
 }
 
