@@ -144,6 +144,16 @@ def test_forward_odd_widths(dtype):
     _run(shape, 203, bias=(np.random.default_rng(3).standard_normal(96) * 0.03).astype(F32))
 
 
+@pytest.mark.parametrize("l,k", [(512, 6), (1024, 16), (1024, 3)])
+def test_forward_wide_latent_rows(l, k):
+    """Latent widths 512 and 1024 in bf16, whose combine reads whole rows per
+    wavefront load (k = 16 in four batches of four slots; k = 3 leaves a
+    partial batch), with a ragged T."""
+    say(f"forward wide latent l={l} k={k}")
+    shape = wl.LayerShape("wide", 11, "bf16", T=1, d=256, l=l, E=32, k=k, f=128, f_s=256)
+    _run(shape, 301, bias=(np.random.default_rng(l + k).standard_normal(32) * 0.05).astype(F32))
+
+
 def test_forward_k_max_and_single_expert():
     """k = 32 of E = 64 (the largest k), then E = k = 1 (one expert takes every token)."""
     say("forward k=32 of 64")
