@@ -143,7 +143,7 @@ hipError_t launch_rmsnorm(const Dims& D, const void* x, const float* gamma, void
 }
 
 // -------------------------------------------------- scores + top-k ----
-// Tokens are ranked in chunks of kChunk = 32 (one or two chunks per block).
+// Tokens are ranked in chunks of kChunk = 32, one chunk per block.
 // The selection is the candidate filter below (topk_filter_tokens, or
 // topk_group_tokens with 16 or 32 lanes per token); tokens it cannot settle
 // take the k-round path here: lane i holds experts i, i+64, ...; each of the
