@@ -37,6 +37,7 @@ CASES = [  # (E, k, T, logit scale, bias scale)
     (896, 16, 1000, 1.0, 40.0),
     (256, 6, 65569, 1.0, 0.05),    # 2050 chunks: the per-block scatter, its last block 2 chunks, a 1-token chunk
     (100, 4, 70001, 1.0, 0.1),     # the per-block scatter with E < 256 (threads without an expert)
+    (128, 12, 65601, 1.0, 0.05),   # the per-block scatter with more slots than its prefetched indices
 ]
 
 
